@@ -1,0 +1,291 @@
+"""fp64 CPU oracle for the TTR hybrid-attention forward and the causal elu+1 variant.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it. It shares no code with the HIP library and imports
+nothing from it.
+
+Sources (page titles and sections of the method's web pages):
+
+* "Flux2TTRTrainer", section "How the distillation works": the TTR layer
+  fuses a linear-time kernel branch with a small exact-softmax branch over
+  landmark tokens, blended by a bounded weight. Section "Why this exists":
+  the branch is a kernel-regression replacement for attention. Section
+  "Inputs worth setting": feature_dim defaults to 256 and is a multiple of 256.
+* "NNT Define Linear Attention", section "The inputs": the elu feature map is
+  elu(x) + 1; eps (default 1e-6) sits in the denominator; causal masks so a
+  token attends only to earlier tokens. Section "How it works": compute
+  K'^T V first, normalise with 1 / (Q' . sum(K') + eps), never form the
+  N x N map.
+
+Every function computes the plain definition in float64 with numpy, one
+(batch, head) slice at a time. Readings taken where the pages are silent:
+
+* elu uses alpha = 1 (the standard elu).
+* The same W_h, b_h map both Q and K; W is [H, D, F], b is [H, F], g is [H].
+* Landmarks are idx_j = floor(j * N / L), j = 0..L-1 (strided from token 0;
+  with N = 256, L = 16 this is every 16th token).
+* The landmark branch is softmax(Q K_L^T / sqrt(D)) V_L on the raw Q, K, V.
+* alpha_h = sigmoid(g_h) weights the linear branch:
+  out = alpha * out_lin + (1 - alpha) * out_lm.
+* L = 0 means no landmark branch: out = out_lin.
+* The causal mask includes the diagonal (key index <= query index).
+* Without W the feature map is the identity projection: phi(x) = elu(x + b) + 1
+  with F = D (b optional).
+
+Pins (tests/test_oracle.py): brute-force N x N row-normalised attention,
+torch's elu and scaled_dot_product_attention in fp64, closed forms
+(W = 0, L = 1, Q = 0, first causal token), invariants (phi > 0, permutation,
+linearity, convex hull, alpha limits, last causal token equals the non-causal
+result), and a hand-worked example under tests/golden/.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "elu_plus_one", "feature_map", "kv_reduce", "apply", "landmark_indices",
+    "landmark_attn", "blend", "hybrid_forward", "causal_forward",
+    "hybrid_rows", "causal_rows", "normwise_err",
+]
+
+
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def elu_plus_one(z: np.ndarray) -> np.ndarray:
+    """elu(z) + 1 with alpha = 1: z + 1 for z > 0, exp(z) otherwise.
+
+    "NNT Define Linear Attention", section "The inputs" (elu mapped as elu(x)+1).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    # elu(z) = z for z > 0 and exp(z) - 1 otherwise; adding 1 gives the two
+    # branches below exactly (written this way so that exp(z) is not lost to
+    # cancellation against 1 for very negative z).
+    return np.where(z > 0.0, z + 1.0, np.exp(np.minimum(z, 0.0)))
+
+
+def _phi_slice(x: np.ndarray, W: Optional[np.ndarray], b: Optional[np.ndarray]) -> np.ndarray:
+    # x [N, D] -> phi [N, F]; one head's map.
+    z = x @ W if W is not None else x.copy()
+    if b is not None:
+        z = z + b[None, :]
+    return elu_plus_one(z)
+
+
+def feature_map(X, W=None, b=None) -> np.ndarray:
+    """phi(X) = elu(X W_h + b_h) + 1 per (batch, head).  X [B,H,N,D] -> [B,H,N,F].
+
+    North-star feature map; "Flux2TTRTrainer" section "Inputs worth setting"
+    (feature_dim F); "NNT Define Linear Attention" section "The inputs" (elu+1).
+    """
+    X, W, b = _f64(X), _f64(W), _f64(b)
+    B, H, N, D = X.shape
+    F = W.shape[2] if W is not None else D
+    out = np.empty((B, H, N, F))
+    for bi in range(B):
+        for h in range(H):
+            out[bi, h] = _phi_slice(X[bi, h], None if W is None else W[h], None if b is None else b[h])
+    return out
+
+
+def kv_reduce(K, V, W=None, b=None):
+    """KV_h = phi(K)^T V  [B,H,F,D] and ksum_h = sum_n phi(K)_n  [B,H,F].
+
+    "NNT Define Linear Attention", section "How it works" (accumulate kv = K^T V,
+    the sum of K' for the normaliser).
+    """
+    K, V = _f64(K), _f64(V)
+    phik = feature_map(K, W, b)
+    B, H, N, F = phik.shape
+    D = V.shape[3]
+    KV = np.empty((B, H, F, D))
+    ksum = np.empty((B, H, F))
+    for bi in range(B):
+        for h in range(H):
+            KV[bi, h] = phik[bi, h].T @ V[bi, h]
+            ksum[bi, h] = phik[bi, h].sum(axis=0)
+    return KV, ksum
+
+
+def apply(Q, W, b, KV, ksum, eps) -> np.ndarray:
+    """out_lin = (phi(Q) KV) / (phi(Q) . ksum + eps)  [B,H,N,D].
+
+    "NNT Define Linear Attention", section "How it works" (Q'(K'^T V), normalised by
+    1 / (Q' . sum(K') + eps)); eps from section "The inputs".
+    """
+    phiq = feature_map(Q, W, b)
+    KV, ksum = _f64(KV), _f64(ksum)
+    eps = float(eps)
+    B, H, N, F = phiq.shape
+    D = KV.shape[3]
+    out = np.empty((B, H, N, D))
+    for bi in range(B):
+        for h in range(H):
+            num = phiq[bi, h] @ KV[bi, h]
+            den = phiq[bi, h] @ ksum[bi, h] + eps
+            out[bi, h] = num / den[:, None]
+    return out
+
+
+def landmark_indices(N: int, L: int) -> np.ndarray:
+    """Strided landmark tokens idx_j = floor(j N / L), integer arithmetic.
+
+    "Flux2TTRTrainer", section "How the distillation works" (landmark tokens);
+    strided placement from token 0 is the reading taken (with N = 256, L = 16 it
+    gives every 16th token).
+    """
+    if not (0 < L <= N):
+        raise ValueError("need 0 < L <= N")
+    return np.array([(j * N) // L for j in range(L)], dtype=np.int64)
+
+
+def landmark_attn(Q, K, V, L: int) -> np.ndarray:
+    """Exact softmax attention of every query over the L landmark tokens.
+
+    S = Q K_L^T / sqrt(D); P = softmax over landmarks (max-subtracted);
+    out_lm = P V_L.  "Flux2TTRTrainer", section "How the distillation works"
+    (small exact-softmax branch over landmark tokens).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    B, H, N, D = Q.shape
+    idx = landmark_indices(N, L)
+    out = np.empty((B, H, N, D))
+    scale = 1.0 / math.sqrt(D)
+    for bi in range(B):
+        for h in range(H):
+            kl = K[bi, h][idx]
+            vl = V[bi, h][idx]
+            s = (Q[bi, h] @ kl.T) * scale
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            out[bi, h] = (p @ vl) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def _sigmoid(g: np.ndarray) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-g))
+
+
+def blend(out_lin, out_lm, g) -> np.ndarray:
+    """out = alpha_h out_lin + (1 - alpha_h) out_lm with alpha_h = sigmoid(g_h).
+
+    "Flux2TTRTrainer", section "How the distillation works" (blended by a
+    bounded weight).
+    """
+    out_lin, out_lm = _f64(out_lin), _f64(out_lm)
+    a = _sigmoid(g)[None, :, None, None]
+    return a * out_lin + (1.0 - a) * out_lm
+
+
+def hybrid_forward(Q, K, V, W, b, g, eps, L: int) -> np.ndarray:
+    """The TTR hybrid forward: linear kernel branch, landmark softmax branch, blend.
+
+    With L = 0 the landmark branch is absent and the result is out_lin.
+    """
+    KV, ksum = kv_reduce(K, V, W, b)
+    lin = apply(Q, W, b, KV, ksum, eps)
+    if L == 0:
+        return lin
+    lm = landmark_attn(Q, K, V, L)
+    return blend(lin, lm, g)
+
+
+def causal_forward(Q, K, V, W, b, eps) -> np.ndarray:
+    """Causal elu+1 linear attention as the running prefix over tokens.
+
+    For n = 0..N-1:  S += phi(k_n) v_n^T,  z += phi(k_n),
+    out_n = phi(q_n) S / (phi(q_n) . z + eps).
+    "NNT Define Linear Attention", section "The inputs" (causal: tokens attend
+    only to earlier tokens, here including themselves) and section "How it works".
+    Vectorised over the (batch, head) slices; the loop runs over tokens.
+    """
+    phiq = feature_map(Q, W, b)
+    phik = feature_map(K, W, b)
+    V = _f64(V)
+    eps = float(eps)
+    B, H, N, F = phiq.shape
+    D = V.shape[3]
+    S = np.zeros((B, H, F, D))
+    z = np.zeros((B, H, F))
+    out = np.empty((B, H, N, D))
+    for n in range(N):
+        kn = phik[:, :, n, :]
+        S += kn[..., :, None] * V[:, :, n, None, :]
+        z += kn
+        qn = phiq[:, :, n, :]
+        num = np.einsum("bhf,bhfd->bhd", qn, S)
+        den = np.einsum("bhf,bhf->bh", qn, z) + eps
+        out[:, :, n, :] = num / den[..., None]
+    return out
+
+
+def hybrid_rows(Q, K, V, W, b, g, eps, L: int, rows: Sequence[tuple]) -> np.ndarray:
+    """hybrid_forward evaluated only at the listed (batch, head, token) rows.
+
+    The linear branch uses the kernel-regression form of the same definition
+    (weights phi(q_n) . phi(k_m), normalised by their sum plus eps), which needs
+    one pass over the slice per row; the landmark branch and blend are as in
+    ``landmark_attn`` and ``blend``.  Returns [len(rows), D].
+    """
+    Q, K, V, W, b = _f64(Q), _f64(K), _f64(V), _f64(W), _f64(b)
+    _, _, N, D = Q.shape
+    res = np.empty((len(rows), D))
+    cache = {}
+    for i, (bi, h, n) in enumerate(rows):
+        key = (bi, h)
+        if key not in cache:
+            Wh = None if W is None else W[h]
+            bh = None if b is None else b[h]
+            cache[key] = _phi_slice(K[bi, h], Wh, bh)
+        phik = cache[key]
+        Wh = None if W is None else W[h]
+        bh = None if b is None else b[h]
+        phiq = _phi_slice(Q[bi, h][n:n + 1], Wh, bh)[0]
+        wts = phik @ phiq
+        lin = (wts @ V[bi, h]) / (wts.sum() + float(eps))
+        if L == 0:
+            res[i] = lin
+            continue
+        idx = landmark_indices(N, L)
+        s = (K[bi, h][idx] @ Q[bi, h][n]) / math.sqrt(D)
+        p = np.exp(s - s.max())
+        lm = (p @ V[bi, h][idx]) / p.sum()
+        a = float(_sigmoid(np.asarray(g, dtype=np.float64)[h]))
+        res[i] = a * lin + (1.0 - a) * lm
+    return res
+
+
+def causal_rows(Q, K, V, W, b, eps, rows: Sequence[tuple]) -> np.ndarray:
+    """causal_forward evaluated only at the listed (batch, head, token) rows.
+
+    Direct masked sum for row n: weights phi(q_n) . phi(k_m) for m <= n,
+    out_n = sum_m w_m v_m / (sum_m w_m + eps).  Returns [len(rows), D].
+    """
+    Q, K, V, W, b = _f64(Q), _f64(K), _f64(V), _f64(W), _f64(b)
+    D = V.shape[3]
+    res = np.empty((len(rows), D))
+    for i, (bi, h, n) in enumerate(rows):
+        Wh = None if W is None else W[h]
+        bh = None if b is None else b[h]
+        phik = _phi_slice(K[bi, h][: n + 1], Wh, bh)
+        phiq = _phi_slice(Q[bi, h][n:n + 1], Wh, bh)[0]
+        wts = phik @ phiq
+        res[i] = (wts @ V[bi, h][: n + 1]) / (wts.sum() + float(eps))
+    return res
+
+
+def normwise_err(got, ref, axes=(-2, -1)) -> float:
+    """max over slices of max|got - ref| / max|ref| (slices reduce over ``axes``)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.abs(got - ref).max(axis=axes)
+    den = np.abs(ref).max(axis=axes)
+    den = np.where(den == 0.0, 1.0, den)
+    return float((num / den).max())

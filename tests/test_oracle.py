@@ -1,0 +1,451 @@
+"""Pins for the fp64 oracle: checks against facts other than the oracle itself.
+
+Each check is something the pages or the mathematics fix independently of
+the oracle's own formulas: hand-worked values (tests/golden), brute-force
+N x N attention, torch library routines in fp64, closed forms and
+invariants. The mutation tests at the end plant plausible mistakes into the
+oracle (on the CPU) and confirm some pin fails.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.ttr_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EPS = float(np.float32(1e-6))
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _small(seed=0, B=1, H=2, N=40, D=8, F=16, proj=True, bscale=0.1):
+    r = np.random.default_rng(seed)
+    Q = r.standard_normal((B, H, N, D))
+    K = r.standard_normal((B, H, N, D))
+    V = r.standard_normal((B, H, N, D))
+    W = r.standard_normal((H, D, F)) / math.sqrt(D) if proj else None
+    b = r.standard_normal((H, F if proj else D)) * bscale
+    g = r.standard_normal(H)
+    return Q, K, V, W, b, g
+
+
+def _eval(expr):
+    return float(eval(expr, {"e": math.e, "__builtins__": {}}))
+
+
+def _golden_hand():
+    rows = {}
+    with open(os.path.join(GOLDEN, "hand_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, n, num, den = line.split()
+            rows.setdefault(name, {})[int(n)] = _eval(num) / _eval(den)
+    return {k: np.array([v[i] for i in sorted(v)]) for k, v in rows.items()}
+
+
+HAND_X = np.array([0.0, 1.0, 3.0]).reshape(1, 1, 3, 1)
+HAND_V = np.array([3.0, 6.0, -3.0]).reshape(1, 1, 3, 1)
+
+
+def brute_linear(Q, K, V, W, b, eps, causal=False):
+    """Row-normalised N x N form: A = phi(Q) phi(K)^T, out = A V / (A 1 + eps)."""
+    B, H, N, D = Q.shape
+    out = np.empty((B, H, N, V.shape[3]))
+    for bi in range(B):
+        for h in range(H):
+            Wh = None if W is None else torch.from_numpy(W[h])
+            def phi(x):
+                t = torch.from_numpy(x)
+                z = t @ Wh if Wh is not None else t
+                if b is not None:
+                    z = z + torch.from_numpy(b[h])
+                return (torch.nn.functional.elu(z, alpha=1.0) + 1.0).numpy()
+            A = phi(Q[bi, h]) @ phi(K[bi, h]).T
+            if causal:
+                A = A * np.tril(np.ones((N, N)))
+            out[bi, h] = (A @ V[bi, h]) / (A.sum(axis=1, keepdims=True) + eps)
+    return out
+
+
+def sdpa(q, k, v):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+
+
+# ---------------------------------------------------------------- feature map
+
+def test_elu_plus_one_matches_torch_elu():
+    z = np.linspace(-40.0, 40.0, 20001)
+    ref = (torch.nn.functional.elu(torch.from_numpy(z), alpha=1.0) + 1.0).numpy()
+    np.testing.assert_allclose(O.elu_plus_one(z), ref, rtol=1e-14, atol=2e-16)
+
+
+def test_elu_plus_one_special_values():
+    assert O.elu_plus_one(np.array([0.0]))[0] == 1.0
+    z = np.linspace(-700, 700, 10001)
+    p = O.elu_plus_one(z)
+    assert (p > 0).all()
+    assert (p[z >= 0] >= 1.0).all()
+    assert (p[z < 0] < 1.0).all()
+    np.testing.assert_allclose(p[z > 0], z[z > 0] + 1.0, rtol=0, atol=0)
+
+
+def test_feature_map_hand_worked():
+    xs, want = [], []
+    with open(os.path.join(GOLDEN, "feature_map_hand.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, c = line.split("|")
+            xs.append([float(t) for t in a.split()])
+            want.append([_eval(t) for t in c.split()])
+    X = np.array(xs).reshape(1, 1, -1, 2)
+    W = np.array([[[1.0, 0.0], [0.0, -1.0]]])
+    b = np.array([[0.0, 1.0]])
+    np.testing.assert_allclose(O.feature_map(X, W, b)[0, 0], np.array(want), rtol=1e-15)
+
+
+def test_feature_map_zero_projection_is_constant():
+    Q, _, _, W, b, _ = _small(1)
+    phi = O.feature_map(Q, np.zeros_like(W), b)
+    want = (torch.nn.functional.elu(torch.from_numpy(b), alpha=1.0) + 1.0).numpy()
+    np.testing.assert_allclose(phi[0], np.broadcast_to(want[:, None, :], phi[0].shape), rtol=1e-15)
+
+
+def test_feature_map_identity_projection_equals_no_projection():
+    Q, _, _, _, b, _ = _small(2, proj=False)
+    D = Q.shape[3]
+    eye = np.broadcast_to(np.eye(D), (Q.shape[1], D, D)).copy()
+    np.testing.assert_allclose(O.feature_map(Q, eye, b), O.feature_map(Q, None, b), rtol=1e-15)
+
+
+def test_feature_map_positive_on_config_scale():
+    Q, _, _, W, b, _ = _small(3, N=512, D=64, F=256)
+    assert (O.feature_map(Q, W, b) > 0).all()
+
+
+# ---------------------------------------------------------------- linear branch
+
+def test_linear_branch_matches_bruteforce_nxn():
+    for seed, proj in ((4, True), (5, False)):
+        Q, K, V, W, b, _ = _small(seed, proj=proj)
+        KV, ksum = O.kv_reduce(K, V, W, b)
+        got = O.apply(Q, W, b, KV, ksum, EPS)
+        ref = brute_linear(Q, K, V, W, b, EPS)
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_linear_branch_hand_worked():
+    want = _golden_hand()
+    KV, ksum = O.kv_reduce(HAND_X, HAND_V, None, None)
+    assert KV.shape == (1, 1, 1, 1) and KV[0, 0, 0, 0] == 3.0 and ksum[0, 0, 0] == 7.0
+    got = O.apply(HAND_X, None, None, KV, ksum, 1e-6)[0, 0, :, 0]
+    np.testing.assert_allclose(got, want["lin"], rtol=1e-14)
+
+
+def test_linear_branch_closed_form_constant_phi():
+    # W = 0, b = 0 -> phi == 1 on all F features: out_n = F sum(V) / (F N + eps)
+    Q, K, V, W, _, _ = _small(6)
+    F = W.shape[2]
+    N = Q.shape[2]
+    KV, ksum = O.kv_reduce(K, V, np.zeros_like(W), None)
+    got = O.apply(Q, np.zeros_like(W), None, KV, ksum, EPS)
+    want = F * V.sum(axis=2, keepdims=True) / (F * N + EPS)
+    np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=1e-13)
+
+
+def test_linear_branch_constant_values():
+    # V == c -> out = c * den / (den + eps) with den = phi(q) . ksum
+    Q, K, V, W, b, _ = _small(7)
+    c = 1.75
+    Vc = np.full_like(V, c)
+    KV, ksum = O.kv_reduce(K, Vc, W, b)
+    got = O.apply(Q, W, b, KV, ksum, 0.5)
+    den = np.einsum("bhnf,bhf->bhn", O.feature_map(Q, W, b), ksum)
+    np.testing.assert_allclose(got, np.broadcast_to((c * den / (den + 0.5))[..., None], got.shape), rtol=1e-13)
+
+
+def test_linear_branch_invariants():
+    Q, K, V, W, b, _ = _small(8)
+    KV, ksum = O.kv_reduce(K, V, W, b)
+    base = O.apply(Q, W, b, KV, ksum, EPS)
+    perm = np.random.default_rng(0).permutation(K.shape[2])
+    KV2, ks2 = O.kv_reduce(K[:, :, perm], V[:, :, perm], W, b)
+    np.testing.assert_allclose(O.apply(Q, W, b, KV2, ks2, EPS), base, rtol=1e-12)
+    # linear in V
+    V2 = _rand(V.shape, 9)
+    KVa, _ = O.kv_reduce(K, 2.0 * V - 3.0 * V2, W, b)
+    KVb, _ = O.kv_reduce(K, V2, W, b)
+    lhs = O.apply(Q, W, b, KVa, ksum, EPS)
+    rhs = 2.0 * base - 3.0 * O.apply(Q, W, b, KVb, ksum, EPS)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-10, atol=1e-12)
+    # convex hull of {0} and the values (weights are positive and sum below 1)
+    lo = np.minimum(0.0, V.min(axis=2, keepdims=True))
+    hi = np.maximum(0.0, V.max(axis=2, keepdims=True))
+    assert (base >= lo - 1e-12).all() and (base <= hi + 1e-12).all()
+
+
+def test_kv_reduce_shapes_and_ksum():
+    Q, K, V, W, b, _ = _small(10, F=32)
+    KV, ksum = O.kv_reduce(K, V, W, b)
+    assert KV.shape == (1, 2, 32, 8) and ksum.shape == (1, 2, 32)
+    # ksum equals KV against an all-ones value column
+    ones = np.ones(V.shape[:3] + (1,))
+    KV1, _ = O.kv_reduce(K, ones, W, b)
+    np.testing.assert_allclose(KV1[..., 0], ksum, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- landmarks
+
+def test_landmark_indices_golden():
+    with open(os.path.join(GOLDEN, "landmarks_tiny.txt")) as f:
+        lines = [l for l in f.read().splitlines() if l and not l.startswith("#")]
+    N, L = map(int, lines[0].split())
+    want = [int(t) for t in lines[1].split()]
+    assert O.landmark_indices(N, L).tolist() == want
+
+
+@pytest.mark.parametrize("N,L", [(1536, 64), (4608, 128), (16896, 256), (257, 16), (1000, 7), (5, 5), (9, 1)])
+def test_landmark_indices_properties(N, L):
+    idx = O.landmark_indices(N, L)
+    assert idx[0] == 0 and len(idx) == L
+    assert (np.diff(idx) > 0).all() and idx[-1] < N
+    if N % L == 0:
+        assert (np.diff(idx) == N // L).all()
+    if L == N:
+        assert idx.tolist() == list(range(N))
+
+
+def test_landmark_single_landmark_returns_first_value():
+    Q, K, V, _, _, _ = _small(11)
+    got = O.landmark_attn(Q, K, V, 1)
+    np.testing.assert_allclose(got, np.broadcast_to(V[:, :, :1, :], got.shape), rtol=1e-15)
+
+
+def test_landmark_zero_query_is_mean():
+    Q, K, V, _, _, _ = _small(12)
+    L = 8
+    idx = O.landmark_indices(Q.shape[2], L)
+    got = O.landmark_attn(np.zeros_like(Q), K, V, L)
+    want = V[:, :, idx, :].mean(axis=2, keepdims=True)
+    np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=1e-13)
+
+
+def test_landmark_matches_torch_sdpa_on_gathered():
+    Q, K, V, _, _, _ = _small(13, D=16)
+    Q = Q * 3.0  # spread the scores so the softmax is far from uniform
+    L = 10
+    idx = O.landmark_indices(Q.shape[2], L)
+    ref = sdpa(Q, K[:, :, idx], V[:, :, idx])
+    np.testing.assert_allclose(O.landmark_attn(Q, K, V, L), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_landmark_hand_worked():
+    want = _golden_hand()
+    np.testing.assert_allclose(O.landmark_attn(HAND_X, HAND_X, HAND_V, 1)[0, 0, :, 0], want["lm1"], rtol=1e-15)
+    np.testing.assert_allclose(O.landmark_attn(HAND_X, HAND_X, HAND_V, 3)[0, 0, :, 0], want["lm3"], rtol=1e-13)
+
+
+def test_landmark_shift_invariance():
+    Q, K, V, _, _, _ = _small(14)
+    base = O.landmark_attn(Q, K, V, 8)
+    # adding a vector orthogonal... use a per-query constant: scores shift by q . c for all landmarks
+    # when every landmark key moves by the same c, the softmax is unchanged
+    c = _rand((1, 1, 1, Q.shape[3]), 15)
+    np.testing.assert_allclose(O.landmark_attn(Q, K + c, V, 8), base, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- blend and hybrid
+
+def test_blend_limits_and_direction():
+    Q, K, V, W, b, _ = _small(16)
+    KV, ksum = O.kv_reduce(K, V, W, b)
+    lin = O.apply(Q, W, b, KV, ksum, EPS)
+    lm = O.landmark_attn(Q, K, V, 8)
+    H = Q.shape[1]
+    np.testing.assert_array_equal(O.blend(lin, lm, np.full(H, np.inf)), lin)
+    np.testing.assert_array_equal(O.blend(lin, lm, np.full(H, -np.inf)), lm)
+    np.testing.assert_allclose(O.blend(lin, lm, np.zeros(H)), 0.5 * (lin + lm), rtol=1e-15)
+    # g = ln 3 -> alpha = 3/4 on the linear branch
+    np.testing.assert_allclose(O.blend(lin, lm, np.full(H, math.log(3.0))), 0.75 * lin + 0.25 * lm, rtol=1e-14)
+
+
+def test_hybrid_hand_worked():
+    want = _golden_hand()
+    g = np.array([math.log(3.0)])
+    got = O.hybrid_forward(HAND_X, HAND_X, HAND_V, None, None, g, 1e-6, 3)[0, 0, :, 0]
+    np.testing.assert_allclose(got, 0.75 * want["lin"] + 0.25 * want["lm3"], rtol=1e-13)
+
+
+def test_hybrid_alpha_zero_all_landmarks_is_full_softmax():
+    Q, K, V, W, b, _ = _small(17, N=48, D=16)
+    H = Q.shape[1]
+    got = O.hybrid_forward(Q, K, V, W, b, np.full(H, -np.inf), EPS, Q.shape[2])
+    np.testing.assert_allclose(got, sdpa(Q, K, V), rtol=1e-12, atol=1e-14)
+
+
+def test_hybrid_alpha_zero_is_landmark_softmax():
+    Q, K, V, W, b, _ = _small(18, N=64, D=16)
+    H = Q.shape[1]
+    idx = O.landmark_indices(64, 16)
+    got = O.hybrid_forward(Q, K, V, W, b, np.full(H, -np.inf), EPS, 16)
+    np.testing.assert_allclose(got, sdpa(Q, K[:, :, idx], V[:, :, idx]), rtol=1e-12, atol=1e-14)
+
+
+def test_hybrid_no_landmarks_is_linear():
+    Q, K, V, W, b, g = _small(19)
+    got = O.hybrid_forward(Q, K, V, W, b, g, EPS, 0)
+    np.testing.assert_allclose(got, brute_linear(Q, K, V, W, b, EPS), rtol=1e-11, atol=1e-13)
+
+
+def test_hybrid_rows_match_full():
+    Q, K, V, W, b, g = _small(20, B=2, N=50)
+    full = O.hybrid_forward(Q, K, V, W, b, g, EPS, 5)
+    rows = [(0, 0, 0), (1, 1, 49), (0, 1, 17), (1, 0, 33)]
+    got = O.hybrid_rows(Q, K, V, W, b, g, EPS, 5, rows)
+    np.testing.assert_allclose(got, np.stack([full[r] for r in rows]), rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- causal
+
+def test_causal_hand_worked():
+    want = _golden_hand()
+    got = O.causal_forward(HAND_X, HAND_X, HAND_V, None, None, 1e-6)[0, 0, :, 0]
+    np.testing.assert_allclose(got, want["causal"], rtol=1e-14)
+
+
+def test_causal_matches_masked_bruteforce():
+    for seed, proj in ((21, False), (22, True)):
+        Q, K, V, W, b, _ = _small(seed, B=2, N=33, proj=proj)
+        got = O.causal_forward(Q, K, V, W, b, EPS)
+        ref = brute_linear(Q, K, V, W, b, EPS, causal=True)
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_causal_first_token_closed_form():
+    Q, K, V, _, b, _ = _small(23, proj=False)
+    got = O.causal_forward(Q, K, V, None, b, EPS)[:, :, 0, :]
+    phiq = O.elu_plus_one(Q[:, :, 0, :] + b[None])
+    phik = O.elu_plus_one(K[:, :, 0, :] + b[None])
+    a = (phiq * phik).sum(-1, keepdims=True)
+    np.testing.assert_allclose(got, V[:, :, 0, :] * a / (a + EPS), rtol=1e-13)
+
+
+def test_causal_last_token_equals_noncausal():
+    Q, K, V, _, b, _ = _small(24, N=70, proj=False)
+    c = O.causal_forward(Q, K, V, None, b, EPS)
+    KV, ksum = O.kv_reduce(K, V, None, b)
+    nc = O.apply(Q, None, b, KV, ksum, EPS)
+    np.testing.assert_allclose(c[:, :, -1], nc[:, :, -1], rtol=1e-12)
+
+
+def test_causal_rows_match_full():
+    Q, K, V, _, _, _ = _small(25, B=2, N=40, proj=False)
+    full = O.causal_forward(Q, K, V, None, None, EPS)
+    rows = [(0, 0, 0), (1, 1, 39), (0, 1, 20)]
+    np.testing.assert_allclose(O.causal_rows(Q, K, V, None, None, EPS, rows),
+                               np.stack([full[r] for r in rows]), rtol=1e-11)
+
+
+def test_normwise_err():
+    ref = np.zeros((2, 3, 4, 5))
+    ref[0, 0] = 2.0
+    ref[1, 2] = 4.0
+    got = ref.copy()
+    got[1, 2, 0, 0] += 0.4
+    assert O.normwise_err(got, ref) == pytest.approx(0.1)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _pins_linear():
+    test_linear_branch_hand_worked()
+    test_linear_branch_matches_bruteforce_nxn()
+    test_linear_branch_closed_form_constant_phi()
+
+
+def _pins_landmark():
+    test_landmark_hand_worked()
+    test_landmark_matches_torch_sdpa_on_gathered()
+    test_hybrid_alpha_zero_all_landmarks_is_full_softmax()
+
+
+def _pins_causal():
+    test_causal_hand_worked()
+    test_causal_matches_masked_bruteforce()
+
+
+def _mut_apply_no_eps(Q, W, b, KV, ksum, eps):
+    phiq = O.feature_map(Q, W, b)
+    return np.einsum("bhnf,bhfd->bhnd", phiq, KV) / np.einsum("bhnf,bhf->bhn", phiq, ksum)[..., None]
+
+
+def _mut_apply_eps_outside(Q, W, b, KV, ksum, eps):
+    phiq = O.feature_map(Q, W, b)
+    return np.einsum("bhnf,bhfd->bhnd", phiq, KV) / np.einsum("bhnf,bhf->bhn", phiq, ksum)[..., None] + eps
+
+
+def _mut_elu_no_plus_one(z):
+    z = np.asarray(z, dtype=np.float64)
+    return np.where(z > 0.0, z, np.expm1(np.minimum(z, 0.0)))
+
+
+def _mut_elu_relu(z):
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0) + 1.0
+
+
+def _mut_landmark_no_scale(Q, K, V, L):
+    Q = np.asarray(Q, dtype=np.float64)
+    return _orig_landmark(Q * math.sqrt(Q.shape[3]), K, V, L)
+
+
+def _mut_landmark_idx_offset(N, L):
+    return np.array([min(N - 1, (j * N) // L + 1) for j in range(L)], dtype=np.int64)
+
+
+def _mut_blend_swapped(out_lin, out_lm, g):
+    return _orig_blend(out_lm, out_lin, g)
+
+
+def _mut_causal_exclusive(Q, K, V, W, b, eps):
+    phiq = O.feature_map(Q, W, b)
+    phik = O.feature_map(K, W, b)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, N, F = phiq.shape
+    S = np.zeros((B, H, F, V.shape[3]))
+    z = np.zeros((B, H, F))
+    out = np.empty((B, H, N, V.shape[3]))
+    for n in range(N):
+        qn = phiq[:, :, n, :]
+        out[:, :, n, :] = np.einsum("bhf,bhfd->bhd", qn, S) / (np.einsum("bhf,bhf->bh", qn, z) + eps)[..., None]
+        S += phik[:, :, n, :, None] * V[:, :, n, None, :]
+        z += phik[:, :, n, :]
+    return out
+
+
+_orig_landmark = O.landmark_attn
+_orig_blend = O.blend
+
+
+@pytest.mark.parametrize("attr,mutant,pins", [
+    ("apply", _mut_apply_no_eps, _pins_linear),
+    ("apply", _mut_apply_eps_outside, _pins_linear),
+    ("elu_plus_one", _mut_elu_no_plus_one, _pins_linear),
+    ("elu_plus_one", _mut_elu_relu, _pins_linear),
+    ("landmark_attn", _mut_landmark_no_scale, _pins_landmark),
+    ("landmark_indices", _mut_landmark_idx_offset, _pins_landmark),
+    ("blend", _mut_blend_swapped, test_hybrid_hand_worked),
+    ("causal_forward", _mut_causal_exclusive, _pins_causal),
+])
+def test_planted_mistake_is_caught(monkeypatch, attr, mutant, pins):
+    monkeypatch.setattr(O, attr, mutant)
+    with pytest.raises(AssertionError):
+        pins()
