@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the TTR hybrid-attention forward on one MI355X.
+
+One step = one ttr_hybrid_forward over the whole workload (key/value
+reduction, then the fused apply + landmark softmax + blend kernel) with the
+inputs already resident in HBM. Prints one JSON line:
+  metric/value  hybrid-attention tokens/s (B*N / forward time, all heads)
+  roofline      the dominant kernel's algorithmic TFLOP/s (per-launch flops /
+                its average duration from HIP events recorded inside the timed
+                forwards) against the dense bf16 MFMA peak
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_1024]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "linear_hybrid_attention_amd", "csrc")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="flux_1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(KERNEL_SRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def flops_per_launch(w):
+    """Algorithmic flops of each kernel stage for one forward of workload w."""
+    BH, N, D, F, L = w.B * w.H, w.N, w.D, w.F, w.L
+    if w.causal:
+        # chunked scan with causal tile skipping: intra-chunk (masked blocks),
+        # inter-chunk phi(Q) P, state update phi(K)^T V (segment pass + walk)
+        C = w.chunk
+        nb = C // 32
+        blocks = nb * (nb + 1) // 2
+        per_chunk = blocks * 32 * 32 * (2 * D + 2 * D) + 2 * C * D * D + 2 * C * D * D
+        chunks = -(-N // C)
+        return {"walk": BH * chunks * per_chunk, "segment_totals": BH * chunks * 2 * C * D * D}
+    proj = 2 * N * D * F  # X W_h
+    kv = 2 * N * F * D + N * F  # phi(K)^T V and ksum
+    apply = 2 * N * F * D + 2 * N * F  # phi(Q) KV and phi(Q) . ksum
+    lm = 4 * N * L * D  # Q K_L^T and P V_L
+    return {"kv_reduce": BH * (proj + kv), "fused_apply_landmark_blend": BH * (proj + apply + lm)}
+
+
+def algorithmic_bytes(w):
+    io = 2 if w.dtype == "bf16" else 4
+    return 4 * w.B * w.H * w.N * w.D * io  # Q, K, V read once, out written once
+
+
+def cpu_baseline(w, x, target_s):
+    """Time the fp64 oracle on a bounded sample of heads; scale to the workload's tokens/s."""
+    import numpy as np
+    import oracle.ttr_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+
+    def run(hs):
+        sl = slice(0, hs)
+        W = None if x["W"] is None else x["W"][sl]
+        b = None if x["b"] is None else x["b"][sl]
+        t0 = time.perf_counter()
+        if w.causal:
+            O.causal_forward(x["Q"][:1, sl], x["K"][:1, sl], x["V"][:1, sl], W, b, x["eps"])
+        else:
+            O.hybrid_forward(x["Q"][:, sl], x["K"][:, sl], x["V"][:, sl], W, b, x["g"][sl], x["eps"], w.L)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    heads = int(max(1, min(w.H, target_s / max(t1, 1e-3))))
+    t = run(heads) if heads > 1 else t1
+    seqs = heads if not w.causal else heads  # (batch, head) slices timed
+    total_seqs = w.B * w.H
+    sec_full = t * total_seqs / seqs
+    sample = (f"{seqs} of {total_seqs} (batch, head) slices of the {w.name} workload "
+              f"(N={w.N}), fp64 numpy oracle, {t:.2f} s, scaled to all slices")
+    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds_full_estimate": sec_full}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (every (batch, head) "
+              "slice is independent; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import linear_hybrid_attention_amd as ttr
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def io(name):
+        if x[name] is None:
+            return None
+        if w.dtype == "bf16":
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x[name]).to(dev)
+
+    Q, K, V, W = io("Q"), io("K"), io("V"), io("W")
+    b = None if x["b"] is None else torch.from_numpy(x["b"]).to(dev)
+    g = torch.from_numpy(x["g"]).to(dev)
+    eps = float(x["eps"])
+    out = torch.empty_like(Q)
+    lib = ttr.load_library()
+    F = w.F
+    nbytes = ttr.workspace_bytes(w.B, w.H, w.N, w.D, F, 1 if w.dtype == "bf16" else 0, w.L, w.causal, 0)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        if events is not None:
+            lib.ttr_set_stage_events(events, 3)
+        ttr.hybrid_forward(Q, K, V, W, b, g, eps, w.L, causal=w.causal, out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # stage events: three per step, created (recorded once) before the timed region
+    import ctypes
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for trio in ev:
+        for e in trio:
+            e.record(stream)
+    handles = [(ctypes.c_void_p * 3)(*[e.cuda_event for e in trio]) for trio in ev]
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(handles[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    stage1 = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    stage2 = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+
+    fl = flops_per_launch(w)
+    names = list(fl.keys())
+    stage_ms = {names[0]: float(np.mean(stage1)), names[1]: float(np.mean(stage2))}
+    dom = max(stage_ms, key=stage_ms.get)
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    achieved = fl[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    kernel_names = {"kv_reduce": "kv_partial_kernel + kv_finalize_kernel",
+                    "fused_apply_landmark_blend": "hybrid_kernel (M_LIN|M_LM)",
+                    "walk": "causal_scan_kernel", "segment_totals": "causal_segsum_kernel"}
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(w.name, {}).get(dom)
+        if ent and ent.get("source_hash") == source_hash(ent["sources"]):
+            traffic = ent["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+    total_flops = sum(fl.values())
+    res = {
+        "metric": "hybrid-attention tokens/sec at Flux 1024^2 (24 heads) + % bf16 MFMA peak",
+        "value": w.B * w.N / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F, "L": w.L,
+                   "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
+        "roofline": {"kernel": kernel_names[dom], "bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
+                     "flops_per_launch": fl[dom], "avg_launch_ms": stage_ms[dom]},
+        "forward": {"tflops": total_flops / (ms * 1e-3) / 1e12,
+                    "frac_mfma_peak": total_flops / (ms * 1e-3) / 1e12 / peak,
+                    "algorithmic_bytes": algorithmic_bytes(w),
+                    "frac_hbm_peak": algorithmic_bytes(w) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "stage_ms": stage_ms, "wall_s": wall},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

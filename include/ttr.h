@@ -1,0 +1,153 @@
+/*
+ * ttr.h -- C ABI of the MI355X (gfx950) TTR hybrid-attention library (libttr.so).
+ *
+ * The method (web pages it is described on, by title and section):
+ *   "Flux2TTRTrainer", "How the distillation works": a TTR layer fuses a
+ *     linear-time kernel branch with a small exact-softmax branch over
+ *     landmark tokens, blended by a bounded weight; "Inputs worth setting":
+ *     feature_dim F defaults to 256 and must be a multiple of 256.
+ *   "NNT Define Linear Attention", "The inputs": feature map elu(x) + 1,
+ *     eps = 1e-6 in the denominator, causal flag; "How it works":
+ *     Q'(K'^T V) normalised by 1 / (Q' . sum(K') + eps).
+ *
+ * Computed per (batch b, head h), with x a row of Q or K:
+ *   phi(x)  = elu(x W_h + b_h) + 1           (W == NULL: elu(x + b_h) + 1, F = D)
+ *   KV      = phi(K)^T V           [F, D]    ksum = sum_n phi(K)_n   [F]
+ *   out_lin = phi(Q) KV / (phi(Q) . ksum + eps)
+ *   idx_j   = floor(j N / L), j = 0..L-1     (strided landmarks from token 0)
+ *   out_lm  = softmax(Q K[idx]^T / sqrt(D)) V[idx]
+ *   out     = alpha_h out_lin + (1 - alpha_h) out_lm,  alpha_h = sigmoid(g_h)
+ *   causal:  out_n = phi(q_n) S_n / (phi(q_n) . z_n + eps),
+ *            S_n = sum_{m<=n} phi(k_m) v_m^T,  z_n = sum_{m<=n} phi(k_m)
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays:
+ *     Q, K, V, out_* [B,H,N,D]; W [H,D,F]; b [H,F] (or [H,D] when W is NULL);
+ *     g [H]; KV [B,H,F,D]; ksum [B,H,F]; phi [B,H,N,F].
+ *   - Q, K, V, W, phi and `out` of ttr_blend / ttr_hybrid_forward /
+ *     ttr_causal_scan use the IO dtype (dims.dtype). b, g, KV, ksum, out_lin
+ *     and out_lm are always fp32.
+ *   - Every pointer must be 16-byte aligned. Outputs must not overlap inputs.
+ *   - The caller owns all memory, including the workspace; the library never
+ *     allocates, frees, synchronises or keeps a pointer after returning.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream). Calls are stateless and thread-safe.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     validation failure the call returns a non-zero status and enqueues
+ *     nothing. A failed launch returns TTR_ERR_HIP; ttr_last_hip_error()
+ *     gives the hipError_t (per calling thread).
+ *   - Results are bitwise deterministic run to run (no floating-point atomics).
+ *   - Shape rules: B, H, N >= 1; D in {64, 128}; with W, F == 256; without W,
+ *     F == D. fp32 IO needs D == 64. 0 <= L <= N. Ragged N (not a multiple of
+ *     any tile size) is supported.
+ */
+#ifndef TTR_H
+#define TTR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TTR_OK = 0,
+  TTR_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  TTR_ERR_SHAPE = 2,       /* B/H/N/D/F/L/chunk outside the rules above          */
+  TTR_ERR_DTYPE = 3,       /* unknown dims.dtype                                 */
+  TTR_ERR_UNSUPPORTED = 4, /* a valid request this library does not implement    */
+  TTR_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than ttr_workspace_bytes */
+  TTR_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                   */
+  TTR_ERR_HIP = 7,         /* a HIP launch failed, see ttr_last_hip_error()      */
+  TTR_ERR_ALIAS = 8        /* an output overlaps an input                        */
+} ttr_status;
+
+typedef enum { TTR_FP32 = 0, TTR_BF16 = 1 } ttr_dtype;
+
+/* Problem sizes. F is the feature dimension (256 with a projection W, D without). */
+typedef struct {
+  int32_t B, H, N, D, F;
+  int32_t dtype; /* ttr_dtype of the IO tensors */
+} ttr_dims;
+
+/* Feature map: phi = elu(X W_h + b_h) + 1 written as [B,H,N,F] in the IO dtype.
+ * "Flux2TTRTrainer", "Inputs worth setting" (feature_dim);
+ * "NNT Define Linear Attention", "The inputs" (elu(x) + 1).
+ * X [B,H,N,D]; W [H,D,F] or NULL (identity, F == D); b [H,F] fp32 or NULL. */
+ttr_status ttr_feature_map(ttr_dims d, const void* X, const void* W, const float* b,
+                           void* phi, void* stream);
+
+/* Key/value reduction with the feature map fused: KV = phi(K)^T V (fp32
+ * [B,H,F,D]) and ksum = sum_n phi(K)_n (fp32 [B,H,F]).
+ * "NNT Define Linear Attention", "How it works" (kv = K^T V, sum(K)).
+ * ws: device workspace of at least ttr_workspace_bytes(d, 0, 0, 0) bytes
+ * (split-N partial sums; its contents on entry do not matter). */
+ttr_status ttr_kv_reduce(ttr_dims d, const void* K, const void* V, const void* W,
+                         const float* b, float* KV, float* ksum, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Apply and normalise with the feature map of Q fused:
+ * out_lin = phi(Q) KV / (phi(Q) . ksum + eps), fp32 [B,H,N,D].
+ * "NNT Define Linear Attention", "How it works" and "The inputs" (eps). */
+ttr_status ttr_apply(ttr_dims d, const void* Q, const void* W, const float* b,
+                     const float* KV, const float* ksum, float eps, float* out_lin,
+                     void* stream);
+
+/* Exact softmax over L strided landmarks (1 <= L <= N):
+ * out_lm = softmax(Q K[idx]^T / sqrt(D)) V[idx], idx_j = floor(j N / L); fp32 [B,H,N,D].
+ * "Flux2TTRTrainer", "How the distillation works" (exact-softmax branch). */
+ttr_status ttr_landmark_attn(ttr_dims d, const void* Q, const void* K, const void* V,
+                             int32_t L, float* out_lm, void* stream);
+
+/* Bounded blend: out = sigmoid(g_h) out_lin + (1 - sigmoid(g_h)) out_lm, out in
+ * the IO dtype (round to nearest even for bf16). g [H] fp32 (+-inf allowed).
+ * "Flux2TTRTrainer", "How the distillation works" (bounded weight). */
+ttr_status ttr_blend(ttr_dims d, const float* out_lin, const float* out_lm, const float* g,
+                     void* out, void* stream);
+
+/* Causal elu+1 linear attention as a chunked prefix scan (chunk in {64,128,256};
+ * the chunk changes the schedule, not the result). Identity feature map only
+ * (W must be NULL, F == D); b [H,D] fp32 or NULL.
+ * out [B,H,N,D] in the IO dtype. ws: at least ttr_workspace_bytes(d, 0, 1, chunk) bytes.
+ * "NNT Define Linear Attention", "The inputs" (causal) and "How it works". */
+ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void* V,
+                           const void* W, const float* b, float eps, int32_t chunk,
+                           void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole hybrid forward (kv_reduce, then apply + landmark + blend in one
+ * fused kernel), out [B,H,N,D] in the IO dtype. L == 0: out = out_lin.
+ * causal != 0 routes to ttr_causal_scan with the largest supported chunk
+ * <= 256 (256 for bf16 with D = 64, else 128) and needs L == 0 and W == NULL
+ * (the pages define no causal landmark branch: TTR_ERR_UNSUPPORTED otherwise).
+ * ws: at least ttr_workspace_bytes(d, L, causal, 0) bytes. */
+ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const void* V,
+                              const void* W, const float* b, const float* g, float eps,
+                              int32_t L, int32_t causal, void* out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Workspace size in bytes for the given call shape (0 if the shape is invalid). */
+size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk);
+
+/* Static, never-NULL description of a status code. */
+const char* ttr_status_string(ttr_status st);
+
+/* hipError_t of the last TTR_ERR_HIP returned on the calling thread (0 if none). */
+int ttr_last_hip_error(void);
+
+/* Stage timing for profilers and benchmarks. After this call, the calling
+ * thread's next ttr_hybrid_forward records events[0] on its stream before its
+ * first kernel, events[1] after the key/value reduction (or, causal, after the
+ * segment-total pass) and events[2] after the last kernel; the registration
+ * is consumed by that one call. events holds n >= 3 hipEvent_t handles created
+ * by the caller; NULL clears the registration. The events only observe: the
+ * enqueued kernels and results are the same with or without them. */
+void ttr_set_stage_events(void* const* events, int32_t n);
+
+/* Library version string, e.g. "ttr 0.1.0 gfx950". */
+const char* ttr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTR_H */

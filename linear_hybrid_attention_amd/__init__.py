@@ -1,0 +1,269 @@
+"""Python binding of libttr.so, the MI355X (gfx950) TTR hybrid-attention library.
+
+Argument marshalling only: every function checks tensor placement, dtype and
+contiguity, allocates outputs/workspace with torch, and calls the C ABI of
+include/ttr.h with raw device pointers on torch's current HIP stream. All
+arithmetic runs in the library's HIP kernels; nothing falls back to the CPU.
+
+The method (web pages, by title and section): "Flux2TTRTrainer", "How the
+distillation works" (linear kernel branch + exact softmax over landmark tokens,
+blended by a bounded weight); "NNT Define Linear Attention", "The inputs" and
+"How it works" (elu(x) + 1 feature map, eps, causal variant, K'^T V first).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "TTRError", "load_library", "library_path", "exported_symbols", "Dims",
+    "feature_map", "kv_reduce", "apply", "landmark_attn", "blend", "causal_scan",
+    "hybrid_forward", "workspace_bytes", "status_string", "version",
+    "TTR_FP32", "TTR_BF16",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+HEADER = os.path.join(ROOT, "include", "ttr.h")
+TTR_FP32, TTR_BF16 = 0, 1
+
+
+def library_path() -> str:
+    return os.path.join(HERE, "libttr.so")
+
+
+class TTRError(RuntimeError):
+    """A non-zero ttr_status returned by the library."""
+
+    def __init__(self, status: int, where: str, msg: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        extra = f" (hipError {hip_error})" if status == 7 else ""
+        super().__init__(f"{where}: status {status}: {msg}{extra}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "ttr_feature_map": [Dims, _P, _P, _P, _P, _P],
+    "ttr_kv_reduce": [Dims, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "ttr_apply": [Dims, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P],
+    "ttr_landmark_attn": [Dims, _P, _P, _P, ctypes.c_int32, _P, _P],
+    "ttr_blend": [Dims, _P, _P, _P, _P, _P],
+    "ttr_causal_scan": [Dims, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
+    "ttr_hybrid_forward": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                           _P, _P, ctypes.c_size_t, _P],
+}
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libttr.so once; raise loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m linear_hybrid_attention_amd.build` "
+                          "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ttr_workspace_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.ttr_workspace_bytes.restype = ctypes.c_size_t
+    lib.ttr_status_string.argtypes = [ctypes.c_int]
+    lib.ttr_status_string.restype = ctypes.c_char_p
+    lib.ttr_last_hip_error.argtypes = []
+    lib.ttr_last_hip_error.restype = ctypes.c_int
+    lib.ttr_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.ttr_set_stage_events.restype = None
+    lib.ttr_version.argtypes = []
+    lib.ttr_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> list:
+    """Function names declared in include/ttr.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(ttr_\w+)\s*\(", text, flags=re.M)))
+
+
+def status_string(st: int) -> str:
+    return load_library().ttr_status_string(st).decode()
+
+
+def version() -> str:
+    return load_library().ttr_version().decode()
+
+
+def _check(st: int, where: str) -> None:
+    if st != 0:
+        lib = load_library()
+        raise TTRError(st, where, status_string(st), lib.ttr_last_hip_error())
+
+
+_IO = {torch.float32: TTR_FP32, torch.bfloat16: TTR_BF16}
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _IO:
+        raise TypeError(f"IO tensors must be float32 or bfloat16, got {t.dtype}")
+    return _IO[t.dtype]
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dims(X: torch.Tensor, F: int) -> Dims:
+    if X.dim() != 4:
+        raise ValueError("Q/K/V must be [B, H, N, D]")
+    B, H, N, D = X.shape
+    return Dims(B, H, N, D, F, _io_dtype(X))
+
+
+def _feat_dim(X: torch.Tensor, W: Optional[torch.Tensor]) -> int:
+    return int(W.shape[2]) if W is not None else int(X.shape[3])
+
+
+def workspace_bytes(B: int, H: int, N: int, D: int, F: int, dtype: int, L: int = 0, causal: bool = False,
+                    chunk: int = 0) -> int:
+    return int(load_library().ttr_workspace_bytes(Dims(B, H, N, D, F, dtype), L, int(causal), chunk))
+
+
+def _workspace(d: Dims, nbytes: int, like: torch.Tensor, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def feature_map(X: torch.Tensor, W: Optional[torch.Tensor] = None, b: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """phi(X) = elu(X W_h + b_h) + 1, [B,H,N,F] in X's dtype (ttr_feature_map)."""
+    lib = load_library()
+    F = _feat_dim(X, W)
+    d = _dims(X, F)
+    if out is None:
+        out = torch.empty((d.B, d.H, d.N, F), dtype=X.dtype, device=X.device)
+    st = lib.ttr_feature_map(d, _dev(X, "X"), _dev(W, "W", X.dtype), _dev(b, "b", torch.float32),
+                             _dev(out, "phi", X.dtype), _stream(X))
+    _check(st, "ttr_feature_map")
+    return out
+
+
+def kv_reduce(K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor] = None,
+              b: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """KV = phi(K)^T V [B,H,F,D] and ksum [B,H,F], both fp32 (ttr_kv_reduce)."""
+    lib = load_library()
+    F = _feat_dim(K, W)
+    d = _dims(K, F)
+    KV = torch.empty((d.B, d.H, F, d.D), dtype=torch.float32, device=K.device)
+    ksum = torch.empty((d.B, d.H, F), dtype=torch.float32, device=K.device)
+    need = lib.ttr_workspace_bytes(d, 0, 0, 0) - KV.numel() * 4 - ksum.numel() * 4
+    ws, wsb = _workspace(d, max(0, need), K, ws)
+    st = lib.ttr_kv_reduce(d, _dev(K, "K"), _dev(V, "V", K.dtype), _dev(W, "W", K.dtype),
+                           _dev(b, "b", torch.float32), KV.data_ptr(), ksum.data_ptr(),
+                           None if ws is None else ws.data_ptr(), wsb, _stream(K))
+    _check(st, "ttr_kv_reduce")
+    return KV, ksum
+
+
+def apply(Q: torch.Tensor, W: Optional[torch.Tensor], b: Optional[torch.Tensor], KV: torch.Tensor,
+          ksum: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    """out_lin = phi(Q) KV / (phi(Q) . ksum + eps), fp32 [B,H,N,D] (ttr_apply)."""
+    lib = load_library()
+    d = _dims(Q, _feat_dim(Q, W))
+    out = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
+    st = lib.ttr_apply(d, _dev(Q, "Q"), _dev(W, "W", Q.dtype), _dev(b, "b", torch.float32),
+                       _dev(KV, "KV", torch.float32), _dev(ksum, "ksum", torch.float32), float(eps),
+                       out.data_ptr(), _stream(Q))
+    _check(st, "ttr_apply")
+    return out
+
+
+def landmark_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, L: int) -> torch.Tensor:
+    """Exact softmax over L strided landmarks, fp32 [B,H,N,D] (ttr_landmark_attn)."""
+    lib = load_library()
+    d = _dims(Q, Q.shape[3])
+    out = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
+    st = lib.ttr_landmark_attn(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype), int(L),
+                               out.data_ptr(), _stream(Q))
+    _check(st, "ttr_landmark_attn")
+    return out
+
+
+def blend(out_lin: torch.Tensor, out_lm: torch.Tensor, g: torch.Tensor, dtype=torch.bfloat16) -> torch.Tensor:
+    """out = sigmoid(g_h) out_lin + (1 - sigmoid(g_h)) out_lm in `dtype` (ttr_blend)."""
+    lib = load_library()
+    B, H, N, D = out_lin.shape
+    d = Dims(B, H, N, D, D, _IO[dtype])
+    out = torch.empty(out_lin.shape, dtype=dtype, device=out_lin.device)
+    st = lib.ttr_blend(d, _dev(out_lin, "out_lin", torch.float32), _dev(out_lm, "out_lm", torch.float32),
+                       _dev(g, "g", torch.float32), out.data_ptr(), _stream(out_lin))
+    _check(st, "ttr_blend")
+    return out
+
+
+def causal_scan(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, b: Optional[torch.Tensor] = None,
+                eps: float = 1e-6, chunk: int = 256, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal elu+1 linear attention, chunked prefix scan, [B,H,N,D] in Q's dtype (ttr_causal_scan)."""
+    lib = load_library()
+    d = _dims(Q, Q.shape[3])
+    if out is None:
+        out = torch.empty_like(Q)
+    need = lib.ttr_workspace_bytes(d, 0, 1, int(chunk))
+    ws, wsb = _workspace(d, need, Q, ws)
+    st = lib.ttr_causal_scan(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype), None,
+                             _dev(b, "b", torch.float32), float(eps), int(chunk), _dev(out, "out", Q.dtype),
+                             None if ws is None else ws.data_ptr(), wsb, _stream(Q))
+    _check(st, "ttr_causal_scan")
+    return out
+
+
+def hybrid_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor],
+                   b: Optional[torch.Tensor], g: Optional[torch.Tensor], eps: float = 1e-6, L: int = 0,
+                   causal: bool = False, out: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole TTR forward, [B,H,N,D] in Q's dtype (ttr_hybrid_forward)."""
+    lib = load_library()
+    d = _dims(Q, _feat_dim(Q, W))
+    if out is None:
+        out = torch.empty_like(Q)
+    need = lib.ttr_workspace_bytes(d, int(L), int(causal), 0)
+    ws, wsb = _workspace(d, need, Q, ws)
+    st = lib.ttr_hybrid_forward(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype),
+                                _dev(W, "W", Q.dtype), _dev(b, "b", torch.float32), _dev(g, "g", torch.float32),
+                                float(eps), int(L), int(causal), _dev(out, "out", Q.dtype),
+                                None if ws is None else ws.data_ptr(), wsb, _stream(Q))
+    _check(st, "ttr_hybrid_forward")
+    return out

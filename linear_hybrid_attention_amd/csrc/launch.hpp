@@ -1,0 +1,54 @@
+// Internal launch interface between the C-ABI layer (ttr_api.cpp) and the
+// kernel translation units. Shapes reaching these functions are validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ttr {
+
+struct Problem {
+  int B, H, N, D, F;
+  int dtype;  // 0 = fp32, 1 = bf16
+  bool proj;  // W present (F == 256) or identity map (F == D)
+};
+
+enum { M_PHI = 1, M_LIN = 2, M_LM = 4 };
+
+struct HybridArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* W;
+  const float* bias;
+  const float* KV;    // fp32 [B,H,F,D]
+  const float* ksum;  // fp32 [B,H,F]
+  const float* g;     // fp32 [H]
+  float eps;
+  int H, N, L;
+  void* out;
+};
+
+// k_hybrid.hip: feature map / apply / landmark / fused apply+landmark+blend.
+// out_io selects the IO dtype (instead of fp32) for the M_LIN output.
+hipError_t launch_hybrid(const Problem& p, int mode, bool out_io, const HybridArgs& a, hipStream_t s);
+
+// k_kv.hip: KV = phi(K)^T V and ksum over split token ranges, then a
+// fixed-order sum of the partials.
+int kv_nsplit(const Problem& p);
+size_t kv_workspace_bytes(const Problem& p);
+hipError_t launch_kv_reduce(const Problem& p, const void* K, const void* V, const void* W,
+                            const float* bias, float* KV, float* ksum, void* ws, hipStream_t s);
+
+// k_blend.hip
+hipError_t launch_blend(const Problem& p, const float* lin, const float* lm, const float* g, void* out,
+                        hipStream_t s);
+
+// k_causal.hip: chunked prefix scan (segment totals, then an in-order chunk walk).
+void causal_plan(const Problem& p, int chunk, int* nseg, int* chunks_per_seg);
+size_t causal_workspace_bytes(const Problem& p, int chunk);
+hipError_t launch_causal(const Problem& p, const void* Q, const void* K, const void* V, const float* bias,
+                         float eps, int chunk, void* out, void* ws, hipStream_t s,
+                         void* const* stage_events);
+
+}  // namespace ttr

@@ -1,0 +1,294 @@
+// C ABI of libttr.so: validation on the host, then kernel launches on the
+// caller's stream. Declarations and conventions: include/ttr.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ttr.h"
+#include "launch.hpp"
+#include "validate.hpp"
+
+using namespace ttr;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+thread_local void* const* g_stage_events = nullptr;
+
+// Record stage event i of the registered set (if any) on stream s.
+void stage_event(void* const* ev, int i, hipStream_t s) {
+  if (ev != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+}
+
+// Take (and clear) the calling thread's registered stage events.
+void* const* take_stage_events() {
+  void* const* ev = g_stage_events;
+  g_stage_events = nullptr;
+  return ev;
+}
+
+ttr_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return TTR_OK;
+  g_last_hip_error = (int)e;
+  return TTR_ERR_HIP;
+}
+
+Problem make_problem(const ttr_dims& d, bool proj) {
+  Problem p;
+  p.B = d.B;
+  p.H = d.H;
+  p.N = d.N;
+  p.D = d.D;
+  p.F = d.F;
+  p.dtype = d.dtype;
+  p.proj = proj;
+  return p;
+}
+
+size_t io(const ttr_dims& d) { return dtype_bytes(d.dtype); }
+size_t qkv_bytes(const ttr_dims& d) { return (size_t)d.B * d.H * d.N * d.D * io(d); }
+size_t w_bytes(const ttr_dims& d) { return (size_t)d.H * d.D * d.F * io(d); }
+size_t b_bytes(const ttr_dims& d) { return (size_t)d.H * d.F * sizeof(float); }
+size_t kv_bytes(const ttr_dims& d) { return (size_t)d.B * d.H * d.F * d.D * sizeof(float); }
+size_t ks_bytes(const ttr_dims& d) { return (size_t)d.B * d.H * d.F * sizeof(float); }
+size_t f32_out_bytes(const ttr_dims& d) { return (size_t)d.B * d.H * d.N * d.D * sizeof(float); }
+
+#define TTR_TRY(expr)                    \
+  do {                                   \
+    const ttr_status st_ = (expr);       \
+    if (st_ != TTR_OK) return st_;       \
+  } while (0)
+
+// Bytes the fused hybrid path needs: KV/ksum (fp32) plus the split partials.
+size_t hybrid_ws(const ttr_dims& d, bool proj) {
+  const Problem p = make_problem(d, proj);
+  return kv_bytes(d) + ks_bytes(d) + kv_workspace_bytes(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttr_status_string(ttr_status st) {
+  switch (st) {
+    case TTR_OK: return "ok";
+    case TTR_ERR_NULL: return "a required pointer is NULL";
+    case TTR_ERR_SHAPE: return "invalid shape (B, H, N, D, F, L or chunk)";
+    case TTR_ERR_DTYPE: return "unknown dtype";
+    case TTR_ERR_UNSUPPORTED: return "valid request not supported by this library";
+    case TTR_ERR_WORKSPACE: return "workspace missing or too small";
+    case TTR_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case TTR_ERR_HIP: return "HIP launch failed";
+    case TTR_ERR_ALIAS: return "an output overlaps an input";
+  }
+  return "unknown status";
+}
+
+int ttr_last_hip_error(void) { return g_last_hip_error; }
+
+const char* ttr_version(void) { return "ttr 0.1.0 gfx950"; }
+
+void ttr_set_stage_events(void* const* events, int32_t n) { g_stage_events = (events != nullptr && n >= 3) ? events : nullptr; }
+
+size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk) {
+  if (causal) {
+    if (d.F != d.D || check_dims(d, false) != TTR_OK) return 0;
+    if (chunk == 0) chunk = causal_default_chunk(d.dtype, d.D);
+    if (!causal_chunk_ok(d.dtype, d.D, chunk)) return 0;
+    return causal_workspace_bytes(make_problem(d, false), chunk);
+  }
+  const bool proj = d.F != d.D;
+  if (check_dims(d, proj) != TTR_OK || L < 0 || L > d.N) return 0;
+  return hybrid_ws(d, proj);
+}
+
+ttr_status ttr_feature_map(ttr_dims d, const void* X, const void* W, const float* b, void* phi,
+                           void* stream) {
+  const bool proj = W != nullptr;
+  TTR_TRY(check_dims(d, proj));
+  TTR_TRY(check_ptr(X));
+  TTR_TRY(check_ptr(phi));
+  TTR_TRY(check_opt_ptr(W));
+  TTR_TRY(check_opt_ptr(b));
+  const Range outs[] = {{phi, (size_t)d.B * d.H * d.N * d.F * io(d)}};
+  const Range ins[] = {{X, qkv_bytes(d)}, {W, proj ? w_bytes(d) : 0}, {b, b ? b_bytes(d) : 0}};
+  TTR_TRY(check_no_alias(outs, 1, ins, 3));
+  HybridArgs a = {};
+  a.Q = X;
+  a.W = W;
+  a.bias = b;
+  a.H = d.H;
+  a.N = d.N;
+  a.out = phi;
+  return hip_status(launch_hybrid(make_problem(d, proj), M_PHI, true, a, (hipStream_t)stream));
+}
+
+ttr_status ttr_kv_reduce(ttr_dims d, const void* K, const void* V, const void* W, const float* b, float* KV,
+                         float* ksum, void* ws, size_t ws_bytes, void* stream) {
+  const bool proj = W != nullptr;
+  TTR_TRY(check_dims(d, proj));
+  TTR_TRY(check_ptr(K));
+  TTR_TRY(check_ptr(V));
+  TTR_TRY(check_ptr(KV));
+  TTR_TRY(check_ptr(ksum));
+  TTR_TRY(check_opt_ptr(W));
+  TTR_TRY(check_opt_ptr(b));
+  const Problem p = make_problem(d, proj);
+  const size_t need = kv_workspace_bytes(p);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
+    TTR_TRY(check_ptr(ws));
+  }
+  const Range outs[] = {{KV, kv_bytes(d)}, {ksum, ks_bytes(d)}, {ws, need}};
+  const Range ins[] = {{K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {W, proj ? w_bytes(d) : 0}, {b, b ? b_bytes(d) : 0}};
+  TTR_TRY(check_no_alias(outs, 3, ins, 4));
+  return hip_status(launch_kv_reduce(p, K, V, W, b, KV, ksum, ws, (hipStream_t)stream));
+}
+
+ttr_status ttr_apply(ttr_dims d, const void* Q, const void* W, const float* b, const float* KV,
+                     const float* ksum, float eps, float* out_lin, void* stream) {
+  const bool proj = W != nullptr;
+  TTR_TRY(check_dims(d, proj));
+  TTR_TRY(check_ptr(Q));
+  TTR_TRY(check_ptr(KV));
+  TTR_TRY(check_ptr(ksum));
+  TTR_TRY(check_ptr(out_lin));
+  TTR_TRY(check_opt_ptr(W));
+  TTR_TRY(check_opt_ptr(b));
+  const Range outs[] = {{out_lin, f32_out_bytes(d)}};
+  const Range ins[] = {{Q, qkv_bytes(d)}, {W, proj ? w_bytes(d) : 0}, {b, b ? b_bytes(d) : 0},
+                       {KV, kv_bytes(d)}, {ksum, ks_bytes(d)}};
+  TTR_TRY(check_no_alias(outs, 1, ins, 5));
+  HybridArgs a = {};
+  a.Q = Q;
+  a.W = W;
+  a.bias = b;
+  a.KV = KV;
+  a.ksum = ksum;
+  a.eps = eps;
+  a.H = d.H;
+  a.N = d.N;
+  a.out = out_lin;
+  return hip_status(launch_hybrid(make_problem(d, proj), M_LIN, false, a, (hipStream_t)stream));
+}
+
+ttr_status ttr_landmark_attn(ttr_dims d, const void* Q, const void* K, const void* V, int32_t L, float* out_lm,
+                             void* stream) {
+  TTR_TRY(check_dims(d, d.F != d.D));
+  if (L < 1 || L > d.N) return TTR_ERR_SHAPE;
+  TTR_TRY(check_ptr(Q));
+  TTR_TRY(check_ptr(K));
+  TTR_TRY(check_ptr(V));
+  TTR_TRY(check_ptr(out_lm));
+  const Range outs[] = {{out_lm, f32_out_bytes(d)}};
+  const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}};
+  TTR_TRY(check_no_alias(outs, 1, ins, 3));
+  HybridArgs a = {};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.H = d.H;
+  a.N = d.N;
+  a.L = L;
+  a.out = out_lm;
+  return hip_status(launch_hybrid(make_problem(d, false), M_LM, false, a, (hipStream_t)stream));
+}
+
+ttr_status ttr_blend(ttr_dims d, const float* out_lin, const float* out_lm, const float* g, void* out,
+                     void* stream) {
+  TTR_TRY(check_dims(d, d.F != d.D));
+  TTR_TRY(check_ptr(out_lin));
+  TTR_TRY(check_ptr(out_lm));
+  TTR_TRY(check_ptr(g));
+  TTR_TRY(check_ptr(out));
+  const Range outs[] = {{out, qkv_bytes(d)}};
+  const Range ins[] = {{out_lin, f32_out_bytes(d)}, {out_lm, f32_out_bytes(d)}, {g, (size_t)d.H * sizeof(float)}};
+  TTR_TRY(check_no_alias(outs, 1, ins, 3));
+  return hip_status(launch_blend(make_problem(d, false), out_lin, out_lm, g, out, (hipStream_t)stream));
+}
+
+ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void* V, const void* W, const float* b,
+                           float eps, int32_t chunk, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
+  if (W != nullptr) return TTR_ERR_UNSUPPORTED;  // the causal variant has no projection
+  TTR_TRY(check_dims(d, false));
+  TTR_TRY(check_causal(d, W, 0, chunk));
+  TTR_TRY(check_ptr(Q));
+  TTR_TRY(check_ptr(K));
+  TTR_TRY(check_ptr(V));
+  TTR_TRY(check_ptr(out));
+  TTR_TRY(check_opt_ptr(b));
+  const Problem p = make_problem(d, false);
+  const size_t need = causal_workspace_bytes(p, chunk);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
+    TTR_TRY(check_ptr(ws));
+  }
+  const Range outs[] = {{out, qkv_bytes(d)}, {ws, need}};
+  const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {b, b ? b_bytes(d) : 0}};
+  TTR_TRY(check_no_alias(outs, 2, ins, 4));
+  void* const* ev = take_stage_events();
+  hipStream_t s = (hipStream_t)stream;
+  stage_event(ev, 0, s);
+  const ttr_status st = hip_status(launch_causal(p, Q, K, V, b, eps, chunk, out, ws, s, ev));
+  stage_event(ev, 2, s);
+  return st;
+}
+
+ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const void* V, const void* W,
+                              const float* b, const float* g, float eps, int32_t L, int32_t causal, void* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (causal) {
+    if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
+    if (W != nullptr || L != 0) return TTR_ERR_UNSUPPORTED;
+    TTR_TRY(check_dims(d, false));
+    const int32_t chunk = causal_default_chunk(d.dtype, d.D);
+    if (chunk == 0) return TTR_ERR_UNSUPPORTED;
+    return ttr_causal_scan(d, Q, K, V, W, b, eps, chunk, out, ws, ws_bytes, stream);
+  }
+  const bool proj = W != nullptr;
+  TTR_TRY(check_dims(d, proj));
+  if (L < 0 || L > d.N) return TTR_ERR_SHAPE;
+  TTR_TRY(check_ptr(Q));
+  TTR_TRY(check_ptr(K));
+  TTR_TRY(check_ptr(V));
+  TTR_TRY(check_ptr(out));
+  TTR_TRY(check_opt_ptr(W));
+  TTR_TRY(check_opt_ptr(b));
+  if (L > 0) TTR_TRY(check_ptr(g));
+  const Problem p = make_problem(d, proj);
+  const size_t need = hybrid_ws(d, proj);
+  if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
+  TTR_TRY(check_ptr(ws));
+  const Range outs[] = {{out, qkv_bytes(d)}, {ws, need}};
+  const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {W, proj ? w_bytes(d) : 0},
+                       {b, b ? b_bytes(d) : 0}, {g, (L > 0) ? (size_t)d.H * sizeof(float) : 0}};
+  TTR_TRY(check_no_alias(outs, 2, ins, 6));
+
+  // workspace: KV [B,H,F,D] fp32 | ksum [B,H,F] fp32 | split partials
+  float* KV = static_cast<float*>(ws);
+  float* ksum = KV + (size_t)d.B * d.H * d.F * d.D;
+  void* part = ksum + (size_t)d.B * d.H * d.F;
+  hipStream_t s = (hipStream_t)stream;
+  void* const* ev = take_stage_events();
+  stage_event(ev, 0, s);
+  TTR_TRY(hip_status(launch_kv_reduce(p, K, V, W, b, KV, ksum, part, s)));
+  stage_event(ev, 1, s);
+  HybridArgs a = {};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.W = W;
+  a.bias = b;
+  a.KV = KV;
+  a.ksum = ksum;
+  a.g = g;
+  a.eps = eps;
+  a.H = d.H;
+  a.N = d.N;
+  a.L = L;
+  a.out = out;
+  const ttr_status st = hip_status(launch_hybrid(p, L > 0 ? (M_LIN | M_LM) : M_LIN, true, a, s));
+  stage_event(ev, 2, s);
+  return st;
+}
+
+}  // extern "C"

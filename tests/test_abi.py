@@ -1,0 +1,150 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any launch.
+No compute call is made here (there is no GPU in this suite)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_hybrid_attention_amd as ttr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 1 << 20  # a 16-byte-aligned fake device address; never dereferenced on these paths
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, ALIGN, HIP, ALIAS = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ttr.load_library()
+
+
+def test_header_declarations_are_exported(lib):
+    names = ttr.exported_symbols()
+    assert {"ttr_feature_map", "ttr_kv_reduce", "ttr_apply", "ttr_landmark_attn", "ttr_blend",
+            "ttr_causal_scan", "ttr_hybrid_forward", "ttr_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_dynamic_symbol_table_matches_header():
+    # every extern "C" function in the header is a dynamic symbol of the .so
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", ttr.library_path()], capture_output=True, text=True).stdout
+    syms = set(re.findall(r"\bT (ttr_\w+)", out))
+    assert set(ttr.exported_symbols()) <= syms
+
+
+def test_status_strings(lib):
+    for st in range(9):
+        s = ttr.status_string(st)
+        assert isinstance(s, str) and s
+    assert ttr.status_string(0) == "ok"
+    assert lib.ttr_last_hip_error() == 0
+    assert ttr.version().startswith("ttr ")
+
+
+def D(B=1, H=2, N=256, Dm=64, F=256, dt=0):
+    return ttr.Dims(B, H, N, Dm, F, dt)
+
+
+def hyb(lib, d, Q=P, K=2 * P, V=3 * P, W=4 * P, b=None, g=5 * P, L=16, causal=0, out=6 * P, ws=7 * P,
+        wsb=1 << 30):
+    return lib.ttr_hybrid_forward(d, Q, K, V, W, b, g, 1e-6, L, causal, out, ws, wsb, None)
+
+
+def test_hybrid_forward_validation(lib):
+    big = 1 << 40
+    kw = dict(Q=big, K=2 * big, V=3 * big, W=4 * big, g=5 * big, out=6 * big, ws=7 * big)
+    assert hyb(lib, D(dt=5), **kw) == DTYPE
+    assert hyb(lib, D(B=0), **kw) == SHAPE
+    assert hyb(lib, D(N=0), **kw) == SHAPE
+    assert hyb(lib, D(Dm=96), **kw) == SHAPE
+    assert hyb(lib, D(F=200), **kw) == SHAPE          # feature_dim must be a multiple of 256
+    assert hyb(lib, D(F=512), **kw) == UNSUP          # a multiple of 256 other than 256
+    assert hyb(lib, D(Dm=128, F=256, dt=0), **kw) == UNSUP  # fp32 IO needs D == 64
+    assert hyb(lib, D(), L=257, **kw) == SHAPE
+    assert hyb(lib, D(), L=-1, **kw) == SHAPE
+    kw2 = dict(kw)
+    kw2["Q"] = None
+    assert hyb(lib, D(), **kw2) == NULL
+    kw2 = dict(kw)
+    kw2["g"] = None
+    assert hyb(lib, D(), **kw2) == NULL
+    assert hyb(lib, D(), L=0, **kw2) != NULL          # g unused without landmarks
+    kw2 = dict(kw)
+    kw2["V"] = 3 * big + 4
+    assert hyb(lib, D(), **kw2) == ALIGN
+    kw2 = dict(kw)
+    kw2["ws"] = None
+    assert hyb(lib, D(), **kw2) == WS
+    assert hyb(lib, D(), wsb=16, **kw) == WS
+    kw2 = dict(kw)
+    kw2["out"] = kw["Q"]
+    assert hyb(lib, D(), **kw2) == ALIAS
+    kw2 = dict(kw)
+    kw2["out"] = kw["Q"] + 64                          # partial overlap
+    assert hyb(lib, D(), **kw2) == ALIAS
+    # identity map: F must equal D
+    kw2 = dict(kw)
+    kw2["W"] = None
+    assert hyb(lib, D(F=256), **kw2) == SHAPE
+    # causal: landmarks and projections are not defined for it
+    assert hyb(lib, D(F=64, dt=1), causal=1, L=16, **kw2) == UNSUP
+    assert hyb(lib, D(F=256, dt=1), causal=1, L=0, **kw) == UNSUP
+
+
+def test_causal_scan_validation(lib):
+    big = 1 << 40
+    d = D(B=8, H=8, N=32768, Dm=64, F=64, dt=1)
+    need = lib.ttr_workspace_bytes(d, 0, 1, 256)
+    assert need > 0
+
+    def cs(dd, chunk=256, W=None, ws=7 * big, wsb=need):
+        return lib.ttr_causal_scan(dd, big, 2 * big, 3 * big, W, None, 1e-6, chunk, 6 * big, ws, wsb, None)
+
+    assert cs(d, chunk=100) == SHAPE
+    assert cs(d, chunk=512) == SHAPE
+    assert cs(d, W=4 * big) == UNSUP
+    assert cs(D(Dm=128, F=128, dt=1), chunk=256) == UNSUP   # LDS budget of the D=128 chunk walk
+    assert cs(D(Dm=64, F=64, dt=0), chunk=256) == UNSUP     # fp32 walks chunks of at most 128
+    assert cs(d, wsb=need - 1) == WS
+    assert cs(d, ws=None) == WS
+
+
+def test_staged_validation(lib):
+    big = 1 << 40
+    d = D()
+    assert lib.ttr_feature_map(d, None, big, None, 2 * big, None) == NULL
+    assert lib.ttr_feature_map(d, big, big + 8, None, 2 * big, None) == ALIGN
+    assert lib.ttr_feature_map(d, big, 2 * big, None, big, None) == ALIAS
+    assert lib.ttr_landmark_attn(d, big, 2 * big, 3 * big, 0, 4 * big, None) == SHAPE
+    assert lib.ttr_landmark_attn(d, big, 2 * big, 3 * big, 257, 4 * big, None) == SHAPE
+    assert lib.ttr_apply(d, big, 2 * big, None, None, 3 * big, 1e-6, 4 * big, None) == NULL
+    assert lib.ttr_blend(D(F=64), big, 2 * big, None, 3 * big, None) == NULL
+    assert lib.ttr_kv_reduce(D(N=4096), big, 2 * big, 3 * big, None, 4 * big, 5 * big, None, 0, None) == WS
+
+
+def test_workspace_bytes(lib):
+    assert lib.ttr_workspace_bytes(D(Dm=96), 0, 0, 0) == 0
+    assert lib.ttr_workspace_bytes(D(), 300, 0, 0) == 0
+    c2 = lib.ttr_workspace_bytes(ttr.Dims(1, 24, 4608, 128, 256, 1), 128, 0, 0)
+    # at least KV and ksum in fp32
+    assert c2 >= 24 * (256 * 128 + 256) * 4
+    assert lib.ttr_workspace_bytes(ttr.Dims(8, 8, 32768, 64, 64, 1), 0, 1, 256) > 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(ttr, "_lib", None)
+    monkeypatch.setattr(ttr, "library_path", lambda: str(tmp_path / "libttr.so"))
+    with pytest.raises(ImportError):
+        ttr.load_library()
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "linear_hybrid_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("oracle-free", ""), f
