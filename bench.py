@@ -61,7 +61,8 @@ def flops_per_launch(w):
         blocks = nb * (nb + 1) // 2
         per_chunk = blocks * 32 * 32 * (2 * D + 2 * D) + 2 * C * D * D + 2 * C * D * D
         chunks = -(-N // C)
-        return {"walk": BH * chunks * per_chunk, "segment_totals": BH * chunks * 2 * C * D * D}
+        # stage order matches the stage events: segment totals first, then the walk
+        return {"segment_totals": BH * chunks * 2 * C * D * D, "walk": BH * chunks * per_chunk}
     proj = 2 * N * D * F  # X W_h
     kv = 2 * N * F * D + N * F  # phi(K)^T V and ksum
     apply = 2 * N * F * D + 2 * N * F  # phi(Q) KV and phi(Q) . ksum
