@@ -40,6 +40,20 @@ size_t kv_workspace_bytes(const Problem& p);
 hipError_t launch_kv_reduce(const Problem& p, const void* K, const void* V, const void* W,
                             const float* bias, float* KV, float* ksum, void* ws, hipStream_t s);
 
+// k_kv2.hip + k_fused.hip: the bf16 hot path. launch_kv2 runs the split-N
+// key/value reduction and writes the per-head operand pack into ws; then
+// launch_fused_query runs apply + landmark softmax + blend over Q.
+struct FusedPack {
+  const unsigned char* pack_bh;  // [B*H][bh_bytes]
+  const unsigned char* pack_w;   // [H][w_bytes]
+  size_t bh_bytes, w_bytes;
+};
+size_t fused_workspace_bytes(const Problem& p, int L);
+hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void* W, const float* bias, int L,
+                      void* ws, FusedPack* pk, hipStream_t s);
+hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& pk, const float* g, float eps,
+                              int L, void* out, hipStream_t s);
+
 // k_blend.hip
 hipError_t launch_blend(const Problem& p, const float* lin, const float* lm, const float* g, void* out,
                         hipStream_t s);

@@ -1,0 +1,77 @@
+// LDS tile layouts shared by the bf16 hot-path kernels (the key/value stage
+// writes operand packs in exactly these layouts; the query kernel copies them
+// into LDS verbatim), plus the asynchronous-copy and wait helpers.
+//
+// All tiles are row-major bf16 with 16-byte pieces permuted within a row
+// (XOR swizzle) so that the MFMA operand reads hit disjoint LDS banks:
+//   kRowRead:  rows read as MFMA A/B fragments with ds_read_b128 by 32
+//              consecutive rows at one column (phys = piece ^ (row & 15) for
+//              rows of >= 256 bytes, piece ^ ((row >> 1) & 7) for 128 bytes).
+//   kTrRead:   rows read column-wise with ds_read_b64_tr_b16 (the tile holds
+//              [k][n]; the read yields a fragment with k in registers):
+//              phys = piece ^ ((row & 3) << 2) for >= 256-byte rows,
+//              piece ^ (((row >> 1) & 3) << 1) for 128-byte rows.
+#pragma once
+#include "common.hpp"
+
+namespace ttr {
+
+enum TileKind { kRowRead = 0, kTrRead = 1 };
+
+template <int COLS, int KIND>
+__host__ __device__ __forceinline__ constexpr int tswz(int row) {
+  static_assert(COLS * 2 == 128 || COLS * 2 >= 256, "row size");
+  if constexpr (KIND == kRowRead) return (COLS * 2 == 128) ? ((row >> 1) & 7) : (row & 15);
+  else return (COLS * 2 == 128) ? (((row >> 1) & 3) << 1) : ((row & 3) << 2);
+}
+// element offset of (row, col) in a bf16 tile with COLS columns
+template <int COLS, int KIND>
+__host__ __device__ __forceinline__ constexpr int toff(int row, int col) {
+  return row * COLS + (((col >> 3) ^ tswz<COLS, KIND>(row)) << 3) + (col & 7);
+}
+
+// Fragment (8 k-values of one lane) of a tile stored [k rows][n cols] (kTrRead
+// layout), for the 16 k-rows starting at k0 and the 32 n-columns starting at
+// n0. Slot 8g + i of lane l (g = l / 32) holds k = k0 + crow(l, i): the same
+// k order as a 32x32 MFMA C tile reused as an operand (see common.hpp).
+// Within each 16-lane group the hardware hands lane l element (l % 4) of the
+// 8 bytes addressed by lane 4 e + (l % 16) / 4 of the group as its element e.
+template <int COLS>
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int k0, int n0, int lane) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const int G = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+  const int row = k0 + 4 * (G >> 1) + e;
+  const int col = n0 + 16 * (G & 1) + 4 * q;
+  const uint16_t* p0 = tile + toff<COLS, kTrRead>(row, col);
+  const uint16_t* p1 = tile + toff<COLS, kTrRead>(row + 8, col);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Asynchronous global -> LDS copy of one 16-byte piece per lane: lane l of
+// the wave writes lds_wave_base + 16 l (the LDS address must be wave-uniform).
+__device__ __forceinline__ void copy16_async(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads (which
+// would wait for every outstanding global load, including prefetches). The
+// memory clobber keeps the compiler from moving LDS accesses across it; the
+// callers wait for the asynchronous copies they need before calling it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads/writes are done
+  asm volatile("s_barrier" ::: "memory");
+}
+
+}  // namespace ttr

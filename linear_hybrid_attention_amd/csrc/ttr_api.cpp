@@ -57,9 +57,11 @@ size_t f32_out_bytes(const ttr_dims& d) { return (size_t)d.B * d.H * d.N * d.D *
     if (st_ != TTR_OK) return st_;       \
   } while (0)
 
-// Bytes the fused hybrid path needs: KV/ksum (fp32) plus the split partials.
-size_t hybrid_ws(const ttr_dims& d, bool proj) {
+// Bytes the hybrid forward needs. bf16: split partials + operand pack of the
+// fused query kernel; fp32: KV/ksum (fp32) plus the split partials.
+size_t hybrid_ws(const ttr_dims& d, bool proj, int32_t L) {
   const Problem p = make_problem(d, proj);
+  if (d.dtype == TTR_BF16) return fused_workspace_bytes(p, L);
   return kv_bytes(d) + ks_bytes(d) + kv_workspace_bytes(p);
 }
 
@@ -97,7 +99,7 @@ size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk)
   }
   const bool proj = d.F != d.D;
   if (check_dims(d, proj) != TTR_OK || L < 0 || L > d.N) return 0;
-  return hybrid_ws(d, proj);
+  return hybrid_ws(d, proj, L);
 }
 
 ttr_status ttr_feature_map(ttr_dims d, const void* X, const void* W, const float* b, void* phi,
@@ -255,7 +257,7 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
   TTR_TRY(check_opt_ptr(b));
   if (L > 0) TTR_TRY(check_ptr(g));
   const Problem p = make_problem(d, proj);
-  const size_t need = hybrid_ws(d, proj);
+  const size_t need = hybrid_ws(d, proj, L);
   if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
   TTR_TRY(check_ptr(ws));
   const Range outs[] = {{out, qkv_bytes(d)}, {ws, need}};
@@ -263,12 +265,22 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
                        {b, b ? b_bytes(d) : 0}, {g, (L > 0) ? (size_t)d.H * sizeof(float) : 0}};
   TTR_TRY(check_no_alias(outs, 2, ins, 6));
 
-  // workspace: KV [B,H,F,D] fp32 | ksum [B,H,F] fp32 | split partials
+  hipStream_t s = (hipStream_t)stream;
+  void* const* ev = take_stage_events();
+  if (d.dtype == TTR_BF16) {
+    // split-N key/value reduction + operand pack, then the fused query kernel
+    FusedPack pk;
+    stage_event(ev, 0, s);
+    TTR_TRY(hip_status(launch_kv2(p, K, V, W, b, L, ws, &pk, s)));
+    stage_event(ev, 1, s);
+    const ttr_status st = hip_status(launch_fused_query(p, Q, pk, g, eps, L, out, s));
+    stage_event(ev, 2, s);
+    return st;
+  }
+  // fp32: KV [B,H,F,D] fp32 | ksum [B,H,F] fp32 | split partials, then the generic query kernel
   float* KV = static_cast<float*>(ws);
   float* ksum = KV + (size_t)d.B * d.H * d.F * d.D;
   void* part = ksum + (size_t)d.B * d.H * d.F;
-  hipStream_t s = (hipStream_t)stream;
-  void* const* ev = take_stage_events();
   stage_event(ev, 0, s);
   TTR_TRY(hip_status(launch_kv_reduce(p, K, V, W, b, KV, ksum, part, s)));
   stage_event(ev, 1, s);
