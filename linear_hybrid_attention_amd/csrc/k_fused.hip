@@ -111,23 +111,31 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   for (int fc = 0; fc < NFC; ++fc) {
     load_chunk(2 * fc + 1);
     Frag<uint16_t> pb[4];  // phi^T of these 64 features, 4 k-blocks of 16
+    {
+      // two independent accumulation chains (feature blocks 0 and 1), interleaved
+      f32x16 acc[2];
 #pragma unroll
-    for (int fb = 0; fb < 2; ++fb) {
-      f32x16 acc;
-      const float* bp = vecS + fc * 64 + fb * 32 + 8 * g;
-      const float* kp = vecS + F + fc * 64 + fb * 32 + 8 * g;
+      for (int fb = 0; fb < 2; ++fb) {
+        const float* bp = vecS + fc * 64 + fb * 32 + 8 * g;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) { acc[r] = bp[r]; acc[8 + r] = bp[16 + r]; }
+        for (int r = 0; r < 8; ++r) { acc[fb][r] = bp[r]; acc[fb][8 + r] = bp[16 + r]; }
+      }
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb)
-        mma(acc, ld_frag<uint16_t>(slot0 + toff<D, kRowRead>(fb * 32 + c, kb * 16 + 8 * g)), qf[kb]);
-      float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = elu1(acc[r]);
+        for (int fb = 0; fb < 2; ++fb)
+          mma(acc[fb], ld_frag<uint16_t>(slot0 + toff<D, kRowRead>(fb * 32 + c, kb * 16 + 8 * g)), qf[kb]);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) den += p[r] * kp[r] + p[8 + r] * kp[16 + r];
-      pb[2 * fb] = to_frag<uint16_t>(p);
-      pb[2 * fb + 1] = to_frag<uint16_t>(p + 8);
+      for (int fb = 0; fb < 2; ++fb) {
+        const float* kp = vecS + F + fc * 64 + fb * 32 + 8 * g;
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = elu1(acc[fb][r]);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) den += p[r] * kp[r] + p[8 + r] * kp[16 + r];
+        pb[2 * fb] = to_frag<uint16_t>(p);
+        pb[2 * fb + 1] = to_frag<uint16_t>(p + 8);
+      }
     }
     store_chunk(slot1);
     barrier_lds();
@@ -165,18 +173,30 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
     const uint16_t* sl = (lc & 1) ? slot1 : slot0;
     const uint16_t* vl = sl + 32 * D;
     const int j0 = lc * 32;
-    f32x16 s = f32x16{};
+    // scores: two independent half-depth chains, added at the end
+    f32x16 s = f32x16{}, s2 = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb)
+    for (int kb = 0; kb < D / 16; kb += 2) {
       mma(s, ld_frag<uint16_t>(sl + toff<D, kRowRead>(c, kb * 16 + 8 * g)), qf[kb]);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = j0 + crow(lane, r) < L ? s[r] * sl2 : -INFINITY;
-      mx = fmaxf(mx, s[r]);
+      mma(s2, ld_frag<uint16_t>(sl + toff<D, kRowRead>(c, kb * 16 + 16 + 8 * g)), qf[kb + 1]);
     }
-    mx = fmaxf(mx, shfl_xor32(mx));  // finite: landmark j0 is valid
-    if (__any(mx > m + 8.f)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += s2[r];
+    // row max of the raw scores (landmarks past L masked to -inf; only the last
+    // chunk can hold such landmarks)
+    float mx = -INFINITY;
+    if (j0 + 32 <= L) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (j0 + crow(lane, r) >= L) s[r] = -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor32(mx)) * sl2;  // base-2 scaled; finite: landmark j0 is valid
+    if (__builtin_expect(__any(mx > m + 8.f), 0)) {
       const float mn = fmaxf(m, mx);
       const float corr = fast_exp2(m - mn);
       l *= corr;
@@ -186,9 +206,10 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
         for (int r = 0; r < 16; ++r) o[db][r] *= corr;
       m = mn;
     }
+    const float nm = -m;
     float p[16], ls = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { p[r] = fast_exp2(s[r] - m); ls += p[r]; }
+    for (int r = 0; r < 16; ++r) { p[r] = fast_exp2(fmaf(s[r], sl2, nm)); ls += p[r]; }
     l += ls + shfl_xor32(ls);
     const Frag<uint16_t> p0 = to_frag<uint16_t>(p), p1 = to_frag<uint16_t>(p + 8);
 #pragma unroll
@@ -200,18 +221,28 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
     barrier_lds();
   }
 
+  // Epilogue: the wave's 32 x D output tile goes through LDS (the ring is free
+  // after the last barrier) so that the global stores are whole 16-byte pieces,
+  // four full rows per store instruction.
   const float cb = L > 0 ? (1.f - 1.f / (1.f + expf(-a.g[h]))) / l : 0.f;
-  if (tok_ok) {
-    uint16_t* op = a.out + ((size_t)bh * N + tok) * D + 4 * g;
+  uint16_t* ot = slot0 + w * 32 * D;  // [32 tokens][D], kRowRead swizzle
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
+    for (int q = 0; q < 4; ++q) {
+      float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = num[db][4 * q + j] + cb * o[db][4 * q + j];
-        st4(op + db * 32 + 8 * q, v[0], v[1], v[2], v[3]);
-      }
+      for (int j = 0; j < 4; ++j) v[j] = num[db][4 * q + j] + cb * o[db][4 * q + j];
+      st4(ot + toff<D, kRowRead>(c, db * 32 + 8 * q + 4 * g), v[0], v[1], v[2], v[3]);
+    }
+  constexpr int PIECES_PER_ROW = D / 8;
+  uint16_t* obase = a.out + ((size_t)bh * N + tile * 128 + 32 * w) * D;
+#pragma unroll
+  for (int i = 0; i < 32 * PIECES_PER_ROW / 64; ++i) {
+    const int P = 64 * i + lane;
+    const int row = P / PIECES_PER_ROW, pc = P % PIECES_PER_ROW;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ot + toff<D, kRowRead>(row, pc * 8));
+    if (tile * 128 + 32 * w + row < N) *reinterpret_cast<u32x4*>(obase + (size_t)row * D + pc * 8) = v;
   }
 }
 
