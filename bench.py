@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="flux_1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     return ap.parse_args()
 
 
@@ -50,24 +50,44 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def flops_per_launch(w):
-    """Algorithmic flops of each kernel stage for one forward of workload w."""
+def kernel_plan(w):
+    """Kernels of one forward in launch order: (name, bound, algorithmic work per launch).
+
+    Work is flops for MFMA-bound kernels and bytes for HBM-bound ones; it counts
+    what the method must compute or move, not what a kernel happens to do.
+    """
     BH, N, D, F, L = w.B * w.H, w.N, w.D, w.F, w.L
+    io = 2 if w.dtype == "bf16" else 4
     if w.causal:
-        # chunked scan with causal tile skipping: intra-chunk (masked blocks),
-        # inter-chunk phi(Q) P, state update phi(K)^T V (segment pass + walk)
-        C = w.chunk
-        nb = C // 32
-        blocks = nb * (nb + 1) // 2
-        per_chunk = blocks * 32 * 32 * (2 * D + 2 * D) + 2 * C * D * D + 2 * C * D * D
-        chunks = -(-N // C)
-        # stage order matches the stage events: segment totals first, then the walk
-        return {"segment_totals": BH * chunks * 2 * C * D * D, "walk": BH * chunks * per_chunk}
+        chunk = 128  # the chunk the hybrid entry point uses for the causal route
+        nseg, cps = causal_plan(w, chunk)
+        qkvo = BH * N * D * io
+        # segment totals read K and V of every segment but the last; the walk
+        # reads Q, K, V and writes out once
+        seg_tokens = min(N, (nseg - 1) * cps * chunk)
+        plan = []
+        if nseg > 1:
+            plan.append((f"causal2_kernel<{chunk}, false>", "hbm", 2 * BH * seg_tokens * D * io))
+        plan.append((f"causal2_kernel<{chunk}, true>", "hbm", 4 * qkvo))
+        return plan
     proj = 2 * N * D * F  # X W_h
     kv = 2 * N * F * D + N * F  # phi(K)^T V and ksum
     apply = 2 * N * F * D + 2 * N * F  # phi(Q) KV and phi(Q) . ksum
     lm = 4 * N * L * D  # Q K_L^T and P V_L
-    return {"kv_reduce": BH * (proj + kv), "fused_apply_landmark_blend": BH * (proj + apply + lm)}
+    if w.dtype == "bf16":
+        return [("kv2_partial_kernel", "mfma", BH * (proj + kv)),
+                ("kv2_pack_kernel", "hbm", 0),
+                ("fused_query_kernel", "mfma", BH * (proj + apply + lm))]
+    return [("kv_partial_kernel (+ kv_finalize_kernel)", "mfma", BH * (proj + kv)),
+            ("hybrid_kernel", "mfma", BH * (proj + apply + lm))]
+
+
+def causal_plan(w, chunk):
+    """Segments of the chunked scan: about 1024 workgroups over the (batch, head) slices."""
+    nchunks = -(-w.N // chunk)
+    want = min(max(-(-1024 // (w.B * w.H)), 1), nchunks)
+    cps = -(-nchunks // want)
+    return -(-nchunks // cps), cps
 
 
 def algorithmic_bytes(w):
@@ -76,7 +96,12 @@ def algorithmic_bytes(w):
 
 
 def cpu_baseline(w, x, target_s):
-    """Time the fp64 oracle on a bounded sample of heads; scale to the workload's tokens/s."""
+    """Time the fp64 oracle on a bounded sample; scale to the workload's tokens/s.
+
+    The sample is the first few (batch, head) slices of the same inputs (all of
+    them when one pass is quick), repeated until about target_s seconds of CPU
+    work have been timed.
+    """
     import numpy as np
     import oracle.ttr_oracle as O
     try:
@@ -99,11 +124,16 @@ def cpu_baseline(w, x, target_s):
     t1 = run(1)
     heads = int(max(1, min(w.H, target_s / max(t1, 1e-3))))
     t = run(heads) if heads > 1 else t1
-    seqs = heads if not w.causal else heads  # (batch, head) slices timed
+    reps, total = 1, t
+    while total < target_s and reps < 64:
+        total += run(heads)
+        reps += 1
+    t = total / reps
+    seqs = heads * (1 if w.causal else w.B)  # (batch, head) slices in one pass
     total_seqs = w.B * w.H
     sec_full = t * total_seqs / seqs
-    sample = (f"{seqs} of {total_seqs} (batch, head) slices of the {w.name} workload "
-              f"(N={w.N}), fp64 numpy oracle, {t:.2f} s, scaled to all slices")
+    sample = (f"{seqs} of {total_seqs} (batch, head) slices of the {w.name} workload (N={w.N}), fp64 numpy "
+              f"oracle, {reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all slices")
     return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": sample, "seconds_full_estimate": sec_full}
 
@@ -145,57 +175,67 @@ def main():
 
     def step(events=None):
         if events is not None:
-            lib.ttr_set_stage_events(events, 3)
+            lib.ttr_set_stage_events(events, len(plan) + 1)
         ttr.hybrid_forward(Q, K, V, W, b, g, eps, w.L, causal=w.causal, out=out, ws=ws)
 
+    plan = kernel_plan(w)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # stage events: three per step, created (recorded once) before the timed region
+    # per-kernel events: len(plan) + 1 per step, created (recorded once) before the timed region
     import ctypes
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for trio in ev:
-        for e in trio:
+    nev = len(plan) + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
             e.record(stream)
-    handles = [(ctypes.c_void_p * 3)(*[e.cuda_event for e in trio]) for trio in ev]
+    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in ev]
     torch.cuda.synchronize()
 
+    # Headline: K forwards back to back, nothing recorded between kernels.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(handles[i])
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    stage1 = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
-    stage2 = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
-
-    fl = flops_per_launch(w)
-    names = list(fl.keys())
-    stage_ms = {names[0]: float(np.mean(stage1)), names[1]: float(np.mean(stage2))}
-    dom = max(stage_ms, key=stage_ms.get)
-    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-    achieved = fl[dom] / (stage_ms[dom] * 1e-3) / 1e12
-    kernel_names = {"kv_reduce": "kv_partial_kernel + kv_finalize_kernel",
-                    "fused_apply_landmark_blend": "hybrid_kernel (M_LIN|M_LM)",
-                    "walk": "causal_scan_kernel", "segment_totals": "causal_segsum_kernel"}
+    # Per-kernel durations: another K forwards with an event between kernels.
+    for i in range(args.steps):
+        step(handles[i])
+    torch.cuda.synchronize()
+    kern_ms = {}
+    for k, (name, _, _) in enumerate(plan):
+        kern_ms[name] = float(np.mean([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)]))
+    dom = max(plan, key=lambda p: kern_ms[p[0]])
+    name, bound, work = dom
+    if bound == "mfma":
+        peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+        achieved, unit = work / (kern_ms[name] * 1e-3) / 1e12, "TFLOP/s"
+    else:
+        peak, achieved, unit = HBM_PEAK_GBS, work / (kern_ms[name] * 1e-3) / 1e9, "GB/s"
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        ent = tr.get(w.name, {}).get(dom)
+        ent = tr.get(w.name, {}).get(name)
         if ent and ent.get("source_hash") == source_hash(ent["sources"]):
             traffic = ent["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
-    total_flops = sum(fl.values())
+    total_flops = sum(p[2] for p in plan if p[1] == "mfma")
+    peak_fwd = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    if w.causal:
+        metric = f"causal linear-attention tokens/sec (B={w.B}, H={w.H}, N={w.N}, D={w.D})"
+    else:
+        metric = "hybrid-attention tokens/sec at Flux 1024^2 (24 heads) + % bf16 MFMA peak"
     res = {
-        "metric": "hybrid-attention tokens/sec at Flux 1024^2 (24 heads) + % bf16 MFMA peak",
+        "metric": metric,
         "value": w.B * w.N / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -209,14 +249,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F, "L": w.L,
                    "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
-        "roofline": {"kernel": kernel_names[dom], "bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
-                     "flops_per_launch": fl[dom], "avg_launch_ms": stage_ms[dom]},
+        "roofline": {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic,
+                     ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"): work,
+                     "avg_launch_ms": kern_ms[name]},
         "forward": {"tflops": total_flops / (ms * 1e-3) / 1e12,
-                    "frac_mfma_peak": total_flops / (ms * 1e-3) / 1e12 / peak,
+                    "frac_mfma_peak": total_flops / (ms * 1e-3) / 1e12 / peak_fwd,
                     "algorithmic_bytes": algorithmic_bytes(w),
                     "frac_hbm_peak": algorithmic_bytes(w) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "stage_ms": stage_ms, "wall_s": wall},
+                    "kernel_ms": kern_ms, "wall_s": wall},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -117,8 +117,8 @@ ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void*
 
 /* The whole hybrid forward (kv_reduce, then apply + landmark + blend in one
  * fused kernel), out [B,H,N,D] in the IO dtype. L == 0: out = out_lin.
- * causal != 0 routes to ttr_causal_scan with the largest supported chunk
- * <= 256 (256 for bf16 with D = 64, else 128) and needs L == 0 and W == NULL
+ * causal != 0 routes to ttr_causal_scan with chunk 128 (the largest supported
+ * chunk <= 128 for the dtype and D) and needs L == 0 and W == NULL
  * (the pages define no causal landmark branch: TTR_ERR_UNSUPPORTED otherwise).
  * ws: at least ttr_workspace_bytes(d, L, causal, 0) bytes. */
 ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const void* V,
@@ -135,13 +135,17 @@ const char* ttr_status_string(ttr_status st);
 /* hipError_t of the last TTR_ERR_HIP returned on the calling thread (0 if none). */
 int ttr_last_hip_error(void);
 
-/* Stage timing for profilers and benchmarks. After this call, the calling
- * thread's next ttr_hybrid_forward records events[0] on its stream before its
- * first kernel, events[1] after the key/value reduction (or, causal, after the
- * segment-total pass) and events[2] after the last kernel; the registration
- * is consumed by that one call. events holds n >= 3 hipEvent_t handles created
- * by the caller; NULL clears the registration. The events only observe: the
- * enqueued kernels and results are the same with or without them. */
+/* Per-kernel timing for profilers and benchmarks. After this call, the
+ * calling thread's next ttr_hybrid_forward or ttr_causal_scan records
+ * events[0] on its stream before its first kernel and events[1], events[2],
+ * ... after each kernel it launches, as long as events remain (bf16 hybrid:
+ * key/value partial sums, operand pack, fused query kernel; fp32 hybrid:
+ * key/value reduction, query kernel; causal: segment totals (when the
+ * sequence has several segments), chunk walk); events left over are recorded
+ * after the last kernel. The registration is consumed
+ * by that one call. events holds n hipEvent_t handles created by the caller;
+ * NULL clears the registration. The events only observe: the enqueued
+ * kernels and results are the same with or without them. */
 void ttr_set_stage_events(void* const* events, int32_t n);
 
 /* Library version string, e.g. "ttr 0.1.0 gfx950". */

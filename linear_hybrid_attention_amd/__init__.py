@@ -234,7 +234,7 @@ def blend(out_lin: torch.Tensor, out_lm: torch.Tensor, g: torch.Tensor, dtype=to
 
 
 def causal_scan(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, b: Optional[torch.Tensor] = None,
-                eps: float = 1e-6, chunk: int = 256, out: Optional[torch.Tensor] = None,
+                eps: float = 1e-6, chunk: int = 128, out: Optional[torch.Tensor] = None,
                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal elu+1 linear attention, chunked prefix scan, [B,H,N,D] in Q's dtype (ttr_causal_scan)."""
     lib = load_library()

@@ -303,29 +303,35 @@ void causal_plan(const Problem& p, int chunk, int* nseg, int* cps) {
   *nseg = (nchunks + *cps - 1) / *cps;
 }
 
-size_t causal_workspace_bytes(const Problem& p, int chunk) {
+size_t causal_seg_bytes(const Problem& p, int chunk) {
   int nseg, cps;
   causal_plan(p, chunk, &nseg, &cps);
   if (nseg <= 1) return 0;
   return (size_t)p.B * p.H * nseg * (size_t)(p.D * p.D + p.D) * sizeof(float);
 }
 
+size_t causal_workspace_bytes(const Problem& p, int chunk) {
+  // segment totals, then (streamed kernel only) the store sink
+  return causal_seg_bytes(p, chunk) + (causal2_supported(p, chunk) ? CAUSAL2_SINK_BYTES : 0);
+}
+
 template <typename T, int D, int C>
-static hipError_t launch_causal_t(const CausalArgs& a, int B, hipStream_t s, void* const* ev) {
+static hipError_t launch_causal_t(const CausalArgs& a, int B, hipStream_t s, StageTimer* t) {
   const dim3 grid(a.nseg, B * a.H), block(256);
   if (a.nseg > 1) {
     hipLaunchKernelGGL((causal_segsum_kernel<T, D, C>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    t->mark();
   }
-  if (ev != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[1]), s);
   hipLaunchKernelGGL((causal_scan_kernel<T, D, C>), grid, block, 0, s, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  t->mark();
+  return e;
 }
 
 hipError_t launch_causal(const Problem& p, const void* Q, const void* K, const void* V, const float* bias,
-                         float eps, int chunk, void* out, void* ws, hipStream_t s,
-                         void* const* ev) {
+                         float eps, int chunk, void* out, void* ws, hipStream_t s, StageTimer* t) {
   CausalArgs a;
   a.Q = Q;
   a.K = K;
@@ -338,15 +344,15 @@ hipError_t launch_causal(const Problem& p, const void* Q, const void* K, const v
   a.seg = static_cast<float*>(ws);
   a.out = out;
   if (p.dtype == 1 && p.D == 64) {
-    if (chunk == 64) return launch_causal_t<uint16_t, 64, 64>(a, p.B, s, ev);
-    if (chunk == 128) return launch_causal_t<uint16_t, 64, 128>(a, p.B, s, ev);
-    if (chunk == 256) return launch_causal_t<uint16_t, 64, 256>(a, p.B, s, ev);
+    if (chunk == 64) return launch_causal_t<uint16_t, 64, 64>(a, p.B, s, t);
+    if (chunk == 128) return launch_causal_t<uint16_t, 64, 128>(a, p.B, s, t);
+    if (chunk == 256) return launch_causal_t<uint16_t, 64, 256>(a, p.B, s, t);
   } else if (p.dtype == 1 && p.D == 128) {
-    if (chunk == 64) return launch_causal_t<uint16_t, 128, 64>(a, p.B, s, ev);
-    if (chunk == 128) return launch_causal_t<uint16_t, 128, 128>(a, p.B, s, ev);
+    if (chunk == 64) return launch_causal_t<uint16_t, 128, 64>(a, p.B, s, t);
+    if (chunk == 128) return launch_causal_t<uint16_t, 128, 128>(a, p.B, s, t);
   } else if (p.dtype == 0 && p.D == 64) {
-    if (chunk == 64) return launch_causal_t<float, 64, 64>(a, p.B, s, ev);
-    if (chunk == 128) return launch_causal_t<float, 64, 128>(a, p.B, s, ev);
+    if (chunk == 64) return launch_causal_t<float, 64, 64>(a, p.B, s, t);
+    if (chunk == 128) return launch_causal_t<float, 64, 128>(a, p.B, s, t);
   }
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,343 @@
+// Causal elu+1 linear attention, bf16 with D = 64: chunked prefix scan with
+// register-staged chunk prefetch. Same computation and segment structure as
+// the generic kernels in k_causal.hip ("NNT Define Linear Attention", sections
+// "The inputs" (causal, elu(x) + 1, eps) and "How it works"):
+//   chunk c:  num = tril(phi(Q_c) phi(K_c)^T) V_c + phi(Q_c) P,
+//             den = rowsum(tril(.)) + phi(Q_c) . z,  out = num / (den + eps),
+//             P += phi(K_c)^T V_c,  z += colsum(phi(K_c))
+// What differs from the generic kernels (all about keeping HBM busy):
+//  * the K and V rows of chunk c + 2 are loaded into registers while chunk c
+//    is processed; chunk c + 1 is written to LDS at the end of chunk c, with
+//    phi applied to K on the way, so one K/V buffer and two barriers per
+//    chunk suffice and two workgroups fit on a CU at C = 128;
+//  * phi(K) and V are read as transposed MFMA operands with
+//    ds_read_b64_tr_b16 (no transposed copies). These reads are not mixed
+//    with asynchronous global->LDS copies: the compiler waits for every such
+//    copy in flight before a transposed read, which would serialise the
+//    prefetch;
+//  * the next chunk's query rows are loaded during the current chunk;
+//  * each wave's 32 x 64 output block goes through LDS so the global stores
+//    are whole 16-byte pieces.
+// Pass 1 (segment totals) and pass 2 (walk) are the same kernel, WALK = false / true.
+#include "common.hpp"
+#include "launch.hpp"
+#include "tiles.hpp"
+
+namespace ttr {
+
+struct Causal2Args {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const float* bias;  // [H][64] or NULL
+  float eps;
+  int H, N, cps, nseg;
+  float* seg;  // [BH][nseg][64*64 + 64]: segment totals P^T (row d, column f), then z
+  uint16_t* sink;  // CAUSAL2_SINK_BYTES of workspace that absorb the stores of rows past N
+  uint16_t* out;
+};
+
+template <int C, bool WALK>
+struct Causal2Shape {
+  static constexpr int D = 64;
+  static constexpr int TILE = C * D;               // elements of the K (or V) tile
+  static constexpr int PER_T = 2 * TILE / 8 / 256;  // 16-byte pieces per thread per chunk (K then V)
+  static_assert(PER_T * 256 * 8 == 2 * TILE && (TILE / 8) % 256 == 0, "whole pieces, K/V split per piece index");
+  static constexpr int kv_bytes = 2 * TILE * 2;
+  static constexpr int pt_bytes = WALK ? D * D * 2 : 0;  // P^T as MFMA operand, [d][f] kRowRead
+  static constexpr int zb_bytes = 2 * D * 4;             // z, then the bias (zeros without one)
+  static constexpr int NB = C / 32;                // 32-token blocks per chunk
+  static constexpr int QB = (NB + 3) / 4;          // query blocks per wave
+  static constexpr int o_bytes = WALK ? 4 * QB * 32 * D * 2 : 0;  // per-wave output staging
+  static constexpr int bytes = kv_bytes + pt_bytes + zb_bytes + o_bytes;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static constexpr int WG_PER_CU = (160 * 1024) / bytes >= 2 ? 2 : 1;
+};
+
+template <int C, bool WALK>
+__global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causal2_kernel(Causal2Args a) {
+  using S = Causal2Shape<C, WALK>;
+  constexpr int D = 64, NB = S::NB, QB = S::QB, PER_T = S::PER_T;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
+  uint16_t* kt = reinterpret_cast<uint16_t*>(smem);  // phi(K) rows, kRowRead
+  uint16_t* vt = kt + S::TILE;                        // V rows, kTrRead
+  float* zS = reinterpret_cast<float*>(smem + S::kv_bytes + S::pt_bytes);
+  float* bS = zS + D;
+  uint16_t* Pt = reinterpret_cast<uint16_t*>(smem + S::kv_bytes);
+  uint16_t* ostage = reinterpret_cast<uint16_t*>(smem + S::kv_bytes + S::pt_bytes + S::zb_bytes);
+
+  const int s = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
+  if (!WALK && s >= a.nseg - 1) return;  // the last segment's total is never read
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;  // wave-uniform, kept in a scalar register
+  const int N = a.N;
+  const size_t base = (size_t)bh * N * D;
+  const uint16_t* Qg = a.Q + base;
+  const uint16_t* Kg = a.K + base;
+  const uint16_t* Vg = a.V + base;
+  const int nchunks = (N + C - 1) / C;
+  const int cbeg = s * a.cps, cend = min(nchunks, cbeg + a.cps);
+  if (cbeg >= cend) return;
+
+  // P^T tile owned by this wave: rows dt*32.., columns ft*32.. (dt = w >> 1, ft = w & 1).
+  const int dt = w >> 1, ft = w & 1;
+  f32x16 P = f32x16{};
+  float zr = 0.f;  // z[ft*32 + c], kept by the waves with dt == 0
+  if constexpr (WALK) {
+    for (int s2 = 0; s2 < s; ++s2) {
+      const float* sp = a.seg + ((size_t)bh * a.nseg + s2) * (size_t)(D * D + D);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) P[r] += sp[(dt * 32 + crow(lane, r)) * D + ft * 32 + c];
+      zr += sp[D * D + ft * 32 + c];
+    }
+  }
+  // A thread's K pieces are all logical piece tid % 8 of their rows: 8 fixed columns.
+  const int kcol = (tid & 7) * 8;
+  float kb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kb[j] = a.bias ? a.bias[(size_t)h * D + kcol + j] : 0.f;
+  if (tid < D) bS[tid] = a.bias ? a.bias[(size_t)h * D + tid] : 0.f;
+
+  // K/V staging: piece i of thread tid is piece tid + 256 i of the chunk
+  // (K pieces first); rows past N repeat row N - 1 and are zeroed (K) when
+  // stored, so they contribute nothing.
+  u32x4 stg[PER_T];
+  auto load_stg = [&](int ch) {
+    const int c0 = ch * C;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const bool isv = i >= PER_T / 2;
+      const int Pl = tid + 256 * (isv ? i - PER_T / 2 : i);
+      const int row = Pl / (D / 8), p = Pl % (D / 8);
+      const int t = min(c0 + row, N - 1);
+      stg[i] = *reinterpret_cast<const u32x4*>((isv ? Vg : Kg) + (size_t)t * D + p * 8);
+    }
+  };
+  auto store_stg = [&](int ch) {
+    const int c0 = ch * C;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const bool isv = i >= PER_T / 2;
+      const int Pl = tid + 256 * (isv ? i - PER_T / 2 : i);
+      const int row = Pl / (D / 8), p = Pl % (D / 8);
+      if (isv) {
+        *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = stg[i];
+      } else {
+        const float keep = c0 + row < N ? 1.f : 0.f;
+        Vec8<uint16_t> v = __builtin_bit_cast(Vec8<uint16_t>, stg[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = f2bf(elu1(bf2f(v.v[j]) + kb[j]) * keep);
+        *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = __builtin_bit_cast(u32x4, v);
+      }
+    }
+  };
+  auto write_state = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Pt[toff<D, kRowRead>(dt * 32 + crow(lane, r), ft * 32 + c)] = f2bf(P[r]);
+    if (dt == 0 && g == 0) zS[ft * 32 + c] = zr;
+  };
+
+  // Raw query fragments (B operand: column = token, k = feature) of this
+  // wave's query blocks of chunk ch.
+  Frag<uint16_t> qraw[QB][D / 16];
+  auto load_q = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      const int qb = (i & 1) ? (4 * i + 3 - w) : (4 * i + w);
+      // Rows past N repeat row N - 1 and blocks past the chunk (waves without
+      // a block when C = 64) load the last block: their outputs are not stored.
+      const int q = min(ch * C + min(qb, NB - 1) * 32 + c, N - 1);
+#pragma unroll
+      for (int kb2 = 0; kb2 < D / 16; ++kb2) qraw[i][kb2] = ld_frag<uint16_t>(Qg + (size_t)q * D + kb2 * 16 + 8 * g);
+    }
+  };
+
+  // Every iteration issues the same global loads and stores whatever the
+  // chunk (indexes are clamped, rows past N are stored to the sink): with no
+  // data-dependent branch around them the compiler's count of memory
+  // operations in flight is exact, and each wait below covers only what it
+  // needs (the prologue issues the same sequence as an iteration).
+  auto store_out = [&](int ch) {
+    wave_lds_order();
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      const int qb = (i & 1) ? (4 * i + 3 - w) : (4 * i + w);
+      const uint16_t* ot = ostage + (w * QB + i) * 32 * D;
+      const int t0 = max(ch, 0) * C + qb * 32;
+      uint16_t* og = a.out + base + (size_t)t0 * D;
+#pragma unroll
+      for (int k = 0; k < 32 * D / 8 / 64; ++k) {
+        const int P8 = 64 * k + lane;
+        const int row = P8 / (D / 8), pc = P8 % (D / 8);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ot + toff<D, kRowRead>(row, pc * 8));
+        const bool ok = qb < NB && ch >= 0 && t0 + row < N;
+        // one sink slot per store, so that none of them is merged away
+        uint16_t* sk = a.sink + ((i * (32 * D / 8 / 64) + k) * 64 + lane) * 8;
+        *reinterpret_cast<u32x4*>(ok ? og + (size_t)row * D + pc * 8 : sk) = v;
+      }
+    }
+  };
+
+  load_stg(cbeg);
+  if constexpr (WALK) {
+    write_state();
+    load_q(cbeg);
+  }
+  store_stg(cbeg);
+  load_stg(min(cbeg + 1, cend - 1));
+  if constexpr (WALK) store_out(-1);  // sink only (stands in for the previous chunk's stores)
+
+  for (int ch = cbeg; ch < cend; ++ch) {
+    const int c0 = ch * C;
+    barrier_lds();  // chunk ch (phi(K), V), P^T and z are in LDS
+
+    // phi(Q) fragments of this wave's query blocks and their inter-chunk
+    // normaliser phi(q) . z; the raw rows are then free for the next chunk's
+    // (no register copy, which would have to wait for the loads).
+    Frag<uint16_t> qf[QB][D / 16];
+    float den0[QB];
+    if constexpr (WALK) {
+#pragma unroll
+      for (int i = 0; i < QB; ++i) {
+        den0[i] = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < D / 16; ++kb2) {
+          float v[8];
+          frag_to_f32(qraw[i][kb2], v);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = elu1(v[j] + bS[kb2 * 16 + 8 * g + j]);
+          qf[i][kb2] = to_frag<uint16_t>(v);
+          float vr[8];
+          frag_to_f32(qf[i][kb2], vr);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) den0[i] += vr[j] * zS[kb2 * 16 + 8 * g + j];
+        }
+      }
+      load_q(min(ch + 1, cend - 1));
+    }
+
+    // Next state: P^T[dt block][ft block] += V^T phi(K) over the chunk and
+    // z += column sums of phi(K), in registers (the LDS copy is updated after
+    // every wave has read the current one).
+    {
+      float zp = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < C / 16; ++kk) {
+        const Frag<uint16_t> av = tr_frag<D>(vt, kk * 16, dt * 32, lane);
+        const Frag<uint16_t> bk = tr_frag<D, kRowRead>(kt, kk * 16, ft * 32, lane);
+        float bv[8];
+        frag_to_f32(bk, bv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zp += bv[j];
+        mma(P, av, bk);
+      }
+      zr += zp + shfl_xor32(zp);
+    }
+
+    if constexpr (WALK) {
+#pragma unroll
+      for (int i = 0; i < QB; ++i) {
+        const int qb = (i & 1) ? (4 * i + 3 - w) : (4 * i + w);
+        if (qb >= NB) continue;  // wave-uniform (C = 64 only)
+        float den = den0[i];
+        f32x16 num[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          num[db] = f32x16{};
+#pragma unroll
+          for (int kb2 = 0; kb2 < D / 16; ++kb2)
+            mma(num[db], ld_frag<uint16_t>(Pt + toff<D, kRowRead>(db * 32 + c, kb2 * 16 + 8 * g)), qf[i][kb2]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          if (kb > qb) break;
+          f32x16 sc = f32x16{};
+#pragma unroll
+          for (int kb2 = 0; kb2 < D / 16; ++kb2)
+            mma(sc, ld_frag<uint16_t>(kt + toff<D, kRowRead>(kb * 32 + c, kb2 * 16 + 8 * g)), qf[i][kb2]);
+          float sv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = (kb == qb && crow(lane, r) > c) ? 0.f : sc[r];
+          const Frag<uint16_t> sb0 = to_frag<uint16_t>(sv), sb1 = to_frag<uint16_t>(sv + 8);
+          float sr[16];
+          frag_to_f32(sb0, sr);
+          frag_to_f32(sb1, sr + 8);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) den += sr[r];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            mma(num[db], tr_frag<D>(vt, kb * 32, db * 32, lane), sb0);
+            mma(num[db], tr_frag<D>(vt, kb * 32 + 16, db * 32, lane), sb1);
+          }
+        }
+        den += shfl_xor32(den);
+        const float inv = 1.f / (den + a.eps);
+        // 32 x 64 output block -> this wave's LDS staging (swizzled rows)
+        uint16_t* ot = ostage + (w * QB + i) * 32 * D;
+        wave_lds_order();  // the previous chunk's reads of ot are done
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            st4(ot + toff<D, kRowRead>(c, db * 32 + 8 * qq + 4 * g), num[db][4 * qq] * inv,
+                num[db][4 * qq + 1] * inv, num[db][4 * qq + 2] * inv, num[db][4 * qq + 3] * inv);
+      }
+    }
+    barrier_lds();  // every wave is done reading chunk ch, P^T and z
+    if constexpr (WALK) write_state();
+    store_stg(min(ch + 1, cend - 1));
+    load_stg(min(ch + 2, cend - 1));
+    // Global stores after the staging loads are issued: the wait for the
+    // staged chunk in the next iteration never covers these stores.
+    if constexpr (WALK) store_out(ch);
+  }
+
+  if constexpr (!WALK) {
+    float* o = a.seg + ((size_t)bh * a.nseg + s) * (size_t)(D * D + D);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[(dt * 32 + crow(lane, r)) * D + ft * 32 + c] = P[r];
+    if (dt == 0 && lane < 32) o[D * D + ft * 32 + c] = zr;
+  }
+}
+
+template <int C>
+static hipError_t launch_causal2_t(const Causal2Args& a, int B, hipStream_t s, StageTimer* t) {
+  const dim3 grid(a.nseg, B * a.H), block(256);
+  if (a.nseg > 1) {
+    hipLaunchKernelGGL((causal2_kernel<C, false>), grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    t->mark();
+  }
+  hipLaunchKernelGGL((causal2_kernel<C, true>), grid, block, 0, s, a);
+  const hipError_t e = hipGetLastError();
+  t->mark();
+  return e;
+}
+
+bool causal2_supported(const Problem& p, int chunk) {
+  return p.dtype == 1 && p.D == 64 && (chunk == 64 || chunk == 128 || chunk == 256);
+}
+
+hipError_t launch_causal2(const Problem& p, const void* Q, const void* K, const void* V, const float* bias,
+                          float eps, int chunk, void* out, void* ws, hipStream_t s, StageTimer* t) {
+  Causal2Args a;
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.bias = bias;
+  a.eps = eps;
+  a.H = p.H;
+  a.N = p.N;
+  causal_plan(p, chunk, &a.nseg, &a.cps);
+  a.seg = static_cast<float*>(ws);
+  a.sink = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + causal_seg_bytes(p, chunk));
+  static_assert(CAUSAL2_SINK_BYTES >= 2 * 4 * 64 * 16, "one 16-byte slot per store of a wave (QB <= 2)");
+  a.out = static_cast<uint16_t*>(out);
+  if (chunk == 64) return launch_causal2_t<64>(a, p.B, s, t);
+  if (chunk == 128) return launch_causal2_t<128>(a, p.B, s, t);
+  if (chunk == 256) return launch_causal2_t<256>(a, p.B, s, t);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ttr

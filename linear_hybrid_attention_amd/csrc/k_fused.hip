@@ -235,6 +235,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       for (int j = 0; j < 4; ++j) v[j] = num[db][4 * q + j] + cb * o[db][4 * q + j];
       st4(ot + toff<D, kRowRead>(c, db * 32 + 8 * q + 4 * g), v[0], v[1], v[2], v[3]);
     }
+  wave_lds_order();
   constexpr int PIECES_PER_ROW = D / 8;
   uint16_t* obase = a.out + ((size_t)bh * N + tile * 128 + 32 * w) * D;
 #pragma unroll

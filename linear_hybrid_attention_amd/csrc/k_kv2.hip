@@ -346,17 +346,21 @@ size_t fused_workspace_bytes(const Problem& p, int L) {
 }
 
 template <int D, int F, bool PROJ>
-static hipError_t launch_kv2_t(const Problem& p, const Kv2Args& ka, const PackArgs& pa, hipStream_t s) {
+static hipError_t launch_kv2_t(const Problem& p, const Kv2Args& ka, const PackArgs& pa, hipStream_t s,
+                               StageTimer* t) {
   hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ>), dim3(ka.nsplit, p.B * p.H), dim3(512), 0, s, ka);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  t->mark();
   const int jobs = F / 4 + (pa.L + 31) / 32;
   hipLaunchKernelGGL((kv2_pack_kernel<D, F, PROJ>), dim3(jobs, p.B * p.H), dim3(256), 0, s, pa);
-  return hipGetLastError();
+  e = hipGetLastError();
+  t->mark();
+  return e;
 }
 
 hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void* W, const float* bias, int L,
-                      void* ws, FusedPack* pk, hipStream_t s) {
+                      void* ws, FusedPack* pk, hipStream_t s, StageTimer* t) {
   int nsplit, chunk;
   kv2_plan(p, &nsplit, &chunk);
   const PackLayout pl = pack_layout(p, L);
@@ -393,12 +397,12 @@ hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void
   pa.pack_w = pw;
   if (p.dtype != 1) return hipErrorInvalidValue;
   if (p.D == 128) {
-    if (p.proj) return launch_kv2_t<128, 256, true>(p, ka, pa, s);
-    return launch_kv2_t<128, 128, false>(p, ka, pa, s);
+    if (p.proj) return launch_kv2_t<128, 256, true>(p, ka, pa, s, t);
+    return launch_kv2_t<128, 128, false>(p, ka, pa, s, t);
   }
   if (p.D == 64) {
-    if (p.proj) return launch_kv2_t<64, 256, true>(p, ka, pa, s);
-    return launch_kv2_t<64, 64, false>(p, ka, pa, s);
+    if (p.proj) return launch_kv2_t<64, 256, true>(p, ka, pa, s, t);
+    return launch_kv2_t<64, 64, false>(p, ka, pa, s, t);
   }
   return hipErrorInvalidValue;
 }

@@ -15,6 +15,20 @@ struct Problem {
 
 enum { M_PHI = 1, M_LIN = 2, M_LM = 4 };
 
+// Optional per-kernel timing: records the next caller-provided event on the
+// stream after each kernel launch (no-op without events).
+struct StageTimer {
+  void* const* ev = nullptr;
+  int n = 0, i = 0;
+  hipStream_t s = nullptr;
+  void mark() {
+    if (ev != nullptr && i < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i++]), s);
+  }
+  void finish() {  // events not used by a kernel are recorded at the end
+    while (ev != nullptr && i < n) mark();
+  }
+};
+
 struct HybridArgs {
   const void* Q;
   const void* K;
@@ -50,7 +64,7 @@ struct FusedPack {
 };
 size_t fused_workspace_bytes(const Problem& p, int L);
 hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void* W, const float* bias, int L,
-                      void* ws, FusedPack* pk, hipStream_t s);
+                      void* ws, FusedPack* pk, hipStream_t s, StageTimer* t);
 hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& pk, const float* g, float eps,
                               int L, void* out, hipStream_t s);
 
@@ -61,8 +75,14 @@ hipError_t launch_blend(const Problem& p, const float* lin, const float* lm, con
 // k_causal.hip: chunked prefix scan (segment totals, then an in-order chunk walk).
 void causal_plan(const Problem& p, int chunk, int* nseg, int* chunks_per_seg);
 size_t causal_workspace_bytes(const Problem& p, int chunk);
+size_t causal_seg_bytes(const Problem& p, int chunk);  // the segment-totals part of the workspace
+// k_causal2.hip: the bf16, D = 64 scan with streamed chunk tiles (same plan; the
+// workspace adds a sink for the stores of rows past N after the segment totals).
+constexpr size_t CAUSAL2_SINK_BYTES = 8192;
+bool causal2_supported(const Problem& p, int chunk);
+hipError_t launch_causal2(const Problem& p, const void* Q, const void* K, const void* V, const float* bias,
+                          float eps, int chunk, void* out, void* ws, hipStream_t s, StageTimer* t);
 hipError_t launch_causal(const Problem& p, const void* Q, const void* K, const void* V, const float* bias,
-                         float eps, int chunk, void* out, void* ws, hipStream_t s,
-                         void* const* stage_events);
+                         float eps, int chunk, void* out, void* ws, hipStream_t s, StageTimer* t);
 
 }  // namespace ttr

@@ -36,14 +36,14 @@ __host__ __device__ __forceinline__ constexpr int toff(int row, int col) {
 // k order as a 32x32 MFMA C tile reused as an operand (see common.hpp).
 // Within each 16-lane group the hardware hands lane l element (l % 4) of the
 // 8 bytes addressed by lane 4 e + (l % 16) / 4 of the group as its element e.
-template <int COLS>
+template <int COLS, int KIND = kTrRead>
 __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int k0, int n0, int lane) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   const int G = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
   const int row = k0 + 4 * (G >> 1) + e;
   const int col = n0 + 16 * (G & 1) + 4 * q;
-  const uint16_t* p0 = tile + toff<COLS, kTrRead>(row, col);
-  const uint16_t* p1 = tile + toff<COLS, kTrRead>(row + 8, col);
+  const uint16_t* p0 = tile + toff<COLS, KIND>(row, col);
+  const uint16_t* p1 = tile + toff<COLS, KIND>(row + 8, col);
   const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
   const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
   typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -73,5 +73,11 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads/writes are done
   asm volatile("s_barrier" ::: "memory");
 }
+
+// Orders this wave's LDS accesses across lanes (lane i writes what lane j
+// then reads). The hardware executes one wave's LDS instructions in order, so
+// this emits no instruction; it only keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 }  // namespace ttr

@@ -12,17 +12,18 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 thread_local void* const* g_stage_events = nullptr;
+thread_local int g_stage_n = 0;
 
-// Record stage event i of the registered set (if any) on stream s.
-void stage_event(void* const* ev, int i, hipStream_t s) {
-  if (ev != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
-}
-
-// Take (and clear) the calling thread's registered stage events.
-void* const* take_stage_events() {
-  void* const* ev = g_stage_events;
+// Take (and clear) the calling thread's registered stage events; record the first.
+StageTimer take_stage_timer(hipStream_t s) {
+  StageTimer t;
+  t.ev = g_stage_events;
+  t.n = g_stage_n;
+  t.s = s;
   g_stage_events = nullptr;
-  return ev;
+  g_stage_n = 0;
+  t.mark();
+  return t;
 }
 
 ttr_status hip_status(hipError_t e) {
@@ -88,7 +89,10 @@ int ttr_last_hip_error(void) { return g_last_hip_error; }
 
 const char* ttr_version(void) { return "ttr 0.1.0 gfx950"; }
 
-void ttr_set_stage_events(void* const* events, int32_t n) { g_stage_events = (events != nullptr && n >= 3) ? events : nullptr; }
+void ttr_set_stage_events(void* const* events, int32_t n) {
+  g_stage_events = (events != nullptr && n >= 1) ? events : nullptr;
+  g_stage_n = g_stage_events ? n : 0;
+}
 
 size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk) {
   if (causal) {
@@ -227,11 +231,12 @@ ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void*
   const Range outs[] = {{out, qkv_bytes(d)}, {ws, need}};
   const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {b, b ? b_bytes(d) : 0}};
   TTR_TRY(check_no_alias(outs, 2, ins, 4));
-  void* const* ev = take_stage_events();
   hipStream_t s = (hipStream_t)stream;
-  stage_event(ev, 0, s);
-  const ttr_status st = hip_status(launch_causal(p, Q, K, V, b, eps, chunk, out, ws, s, ev));
-  stage_event(ev, 2, s);
+  StageTimer t = take_stage_timer(s);
+  const ttr_status st = hip_status(causal2_supported(p, chunk)
+                                       ? launch_causal2(p, Q, K, V, b, eps, chunk, out, ws, s, &t)
+                                       : launch_causal(p, Q, K, V, b, eps, chunk, out, ws, s, &t));
+  t.finish();
   return st;
 }
 
@@ -266,24 +271,21 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
   TTR_TRY(check_no_alias(outs, 2, ins, 6));
 
   hipStream_t s = (hipStream_t)stream;
-  void* const* ev = take_stage_events();
+  StageTimer t = take_stage_timer(s);
   if (d.dtype == TTR_BF16) {
     // split-N key/value reduction + operand pack, then the fused query kernel
     FusedPack pk;
-    stage_event(ev, 0, s);
-    TTR_TRY(hip_status(launch_kv2(p, K, V, W, b, L, ws, &pk, s)));
-    stage_event(ev, 1, s);
+    TTR_TRY(hip_status(launch_kv2(p, K, V, W, b, L, ws, &pk, s, &t)));
     const ttr_status st = hip_status(launch_fused_query(p, Q, pk, g, eps, L, out, s));
-    stage_event(ev, 2, s);
+    t.finish();
     return st;
   }
   // fp32: KV [B,H,F,D] fp32 | ksum [B,H,F] fp32 | split partials, then the generic query kernel
   float* KV = static_cast<float*>(ws);
   float* ksum = KV + (size_t)d.B * d.H * d.F * d.D;
   void* part = ksum + (size_t)d.B * d.H * d.F;
-  stage_event(ev, 0, s);
   TTR_TRY(hip_status(launch_kv_reduce(p, K, V, W, b, KV, ksum, part, s)));
-  stage_event(ev, 1, s);
+  t.mark();
   HybridArgs a = {};
   a.Q = Q;
   a.K = K;
@@ -299,7 +301,7 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
   a.L = L;
   a.out = out;
   const ttr_status st = hip_status(launch_hybrid(p, L > 0 ? (M_LIN | M_LM) : M_LIN, true, a, s));
-  stage_event(ev, 2, s);
+  t.finish();
   return st;
 }
 

@@ -68,7 +68,8 @@ bool causal_chunk_ok(int32_t dtype, int32_t D, int32_t chunk) {
 }
 
 int32_t causal_default_chunk(int32_t dtype, int32_t D) {
-  for (int32_t c = 256; c >= 64; c /= 2)
+  // 128 where it fits: two workgroups of the streamed bf16 kernel share a CU
+  for (int32_t c = 128; c >= 64; c /= 2)
     if (causal_chunk_ok(dtype, D, c)) return c;
   return 0;
 }

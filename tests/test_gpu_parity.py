@@ -87,6 +87,26 @@ def test_causal_chunk_invariance_and_bias():
     assert normwise(outs[0], outs[2]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("B,H,N", [(4, 256, 333), (2, 260, 1100)])
+def test_causal_segments_of_several_chunks(B, H, N, chunk):
+    # Enough (batch, head) slices that each segment walks several chunks
+    # (one segment per slice for B*H >= 1024, two for B*H = 520): every slice
+    # is independent, so a few of them are checked against the oracle.
+    w = small("causal", B=B, H=H, N=N, seed=15)
+    x = workloads.make_inputs(w)
+    d = to_device(w, x)
+    b = np.random.default_rng(4).standard_normal((w.H, w.D)).astype(np.float32) * 0.1
+    print(f"[causal-segments] B={B} H={H} N={N} chunk={chunk}", flush=True)
+    out = ttr.causal_scan(d["Q"], d["K"], d["V"], b=dev_f32(b), chunk=chunk)
+    torch.cuda.synchronize()
+    for bi, hi in [(0, 0), (0, 1), (B - 1, H - 1), (B // 2, H // 2)]:
+        sl = (slice(bi, bi + 1), slice(hi, hi + 1))
+        ref = O.causal_forward(x["Q"][sl], x["K"][sl], x["V"][sl], None, b[hi:hi + 1], x["eps"])
+        err = normwise(host(out[sl]), ref)
+        assert err <= TOL["bf16"], (bi, hi, err)
+
+
 def test_causal_last_token_equals_noncausal():
     # identity feature map on both sides; the last causal row sees every token
     w = small("causal", B=1, H=2, N=500, seed=13)

@@ -49,7 +49,7 @@ class Workload:
     w_std: float
     b_std: float
     seed: int
-    chunk: int = 256
+    chunk: int = 128
     eps: float = 1e-6
 
     def with_(self, **kw) -> "Workload":
