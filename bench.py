@@ -39,7 +39,88 @@ def parse():
     ap.add_argument("--workload", default="flux_1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
+    ap.add_argument("--write-traffic", default=None, metavar="DIR",
+                    help="only turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv runs under DIR (fetch/, write/, "
+                         "copy_fetch/, copy_write/) into profiles/traffic_counters.json")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
+def _pmc_means(run_dir, counter):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    sums = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = sums.setdefault(r["Kernel_Name"], {})
+                k[r["Dispatch_Id"]] = k.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {name: sum(d.values()) / len(d) for name, d in sums.items()}
+
+
+def write_traffic(run_dir):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for a plain copy of known size."""
+    import workloads
+    fetch, write = _pmc_means(os.path.join(run_dir, "fetch"), "FETCH_SIZE"), \
+        _pmc_means(os.path.join(run_dir, "write"), "WRITE_SIZE")
+    cf = _pmc_means(os.path.join(run_dir, "copy_fetch"), "FETCH_SIZE")
+    cw = _pmc_means(os.path.join(run_dir, "copy_write"), "WRITE_SIZE")
+    copy_name = max(cf, key=cf.get)  # the copy kernel is the only large dispatch of that run
+    with open(os.path.join(run_dir, "copy_bytes.txt")) as f:
+        copy_bytes = int(f.read().split()[0])
+    f_scale = copy_bytes / (cf[copy_name] * 1024.0)
+    w_scale = copy_bytes / (cw[copy_name] * 1024.0)
+    with open(os.path.join(run_dir, "workload.txt")) as f:
+        wl = f.read().split()[0]
+    w = workloads.WORKLOADS[wl]
+    out = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            out = json.load(f)
+    ent = {}
+    for name, _, _ in kernel_plan(w):
+        full = [k for k in fetch if k.split("(")[0].replace("void ttr::", "") in (name, name + "<")
+                or k.split("(")[0].replace("void ttr::", "").split("<")[0] == name]
+        if not full or full[0] not in write:
+            continue
+        kname = full[0]
+        srcs = kernel_sources(name)
+        ent[name] = {"bytes_per_launch": fetch[kname] * 1024.0 * f_scale + write[kname] * 1024.0 * w_scale,
+                     "fetch_bytes": fetch[kname] * 1024.0 * f_scale, "write_bytes": write[kname] * 1024.0 * w_scale,
+                     "fetch_scale": f_scale, "write_scale": w_scale, "copy_kernel": copy_name,
+                     "sources": srcs, "source_hash": source_hash(srcs)}
+    out[w.name] = ent
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out[w.name], indent=1))
+
+
+def kernel_sources(name):
+    """Source files a kernel is built from (a change to any of them voids stored counters)."""
+    common = ["common.hpp", "tiles.hpp", "launch.hpp"]
+    if name.startswith("kv2_"):
+        return ["k_kv2.hip"] + common
+    if name.startswith("fused_"):
+        return ["k_fused.hip"] + common
+    if name.startswith("causal2_"):
+        return ["k_causal2.hip"] + common
+    return ["k_hybrid.hip", "k_kv.hip", "k_causal.hip"] + common
 
 
 def source_hash(files) -> str:
@@ -51,35 +132,50 @@ def source_hash(files) -> str:
 
 
 def kernel_plan(w):
-    """Kernels of one forward in launch order: (name, bound, algorithmic work per launch).
+    """Kernels of one forward in launch order: (name, algorithmic flops, algorithmic bytes) per launch.
 
-    Work is flops for MFMA-bound kernels and bytes for HBM-bound ones; it counts
-    what the method must compute or move, not what a kernel happens to do.
+    Both count what the method must compute or move (Q, K, V read once, out
+    written once, the products of the method), not what a kernel happens to do:
+    workspace traffic of the split reduction is the design's, not the method's.
     """
     BH, N, D, F, L = w.B * w.H, w.N, w.D, w.F, w.L
     io = 2 if w.dtype == "bf16" else 4
+    tok = BH * N * D * io  # one [B, H, N, D] tensor
     if w.causal:
         chunk = 128  # the chunk the hybrid entry point uses for the causal route
         nseg, cps = causal_plan(w, chunk)
-        qkvo = BH * N * D * io
         # segment totals read K and V of every segment but the last; the walk
         # reads Q, K, V and writes out once
         seg_tokens = min(N, (nseg - 1) * cps * chunk)
+        state = 2 * D * D + D  # P += phi(k)^T v, z += phi(k) per token
         plan = []
         if nseg > 1:
-            plan.append((f"causal2_kernel<{chunk}, false>", "hbm", 2 * BH * seg_tokens * D * io))
-        plan.append((f"causal2_kernel<{chunk}, true>", "hbm", 4 * qkvo))
+            plan.append((f"causal2_kernel<{chunk}, false>", BH * seg_tokens * state, 2 * BH * seg_tokens * D * io))
+        # per token: its share of the causal score and value tiles (C/2 keys on
+        # average, plus the diagonal), the inter-chunk product and the state update
+        walk = BH * N * (2 * 2 * D * (chunk // 2 + 16) + 2 * D * D + state)
+        plan.append((f"causal2_kernel<{chunk}, true>", walk, 4 * tok))
         return plan
     proj = 2 * N * D * F  # X W_h
     kv = 2 * N * F * D + N * F  # phi(K)^T V and ksum
     apply = 2 * N * F * D + 2 * N * F  # phi(Q) KV and phi(Q) . ksum
     lm = 4 * N * L * D  # Q K_L^T and P V_L
     if w.dtype == "bf16":
-        return [("kv2_partial_kernel", "mfma", BH * (proj + kv)),
-                ("kv2_pack_kernel", "hbm", 0),
-                ("fused_query_kernel", "mfma", BH * (proj + apply + lm))]
-    return [("kv_partial_kernel (+ kv_finalize_kernel)", "mfma", BH * (proj + kv)),
-            ("hybrid_kernel", "mfma", BH * (proj + apply + lm))]
+        return [("kv2_partial_kernel", BH * (proj + kv), 2 * tok),
+                ("kv2_pack_kernel", 0, 0),
+                ("fused_query_kernel", BH * (proj + apply + lm), 2 * tok)]
+    return [("kv_partial_kernel (+ kv_finalize_kernel)", BH * (proj + kv), 2 * tok),
+            ("hybrid_kernel", BH * (proj + apply + lm), 2 * tok)]
+
+
+def roofline(w, flops, nbytes, ms):
+    """The binding roofline of one kernel: whichever of MFMA and HBM time is longer at peak."""
+    peak_f = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    if flops / (peak_f * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9):
+        a = flops / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+        return {"bound": "mfma", "achieved": a, "peak": peak_f, "unit": "TFLOP/s", "frac": a / peak_f}
+    a = nbytes / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
 
 
 def causal_plan(w, chunk):
@@ -140,6 +236,12 @@ def cpu_baseline(w, x, target_s):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (every (batch, head) "
               "slice is independent; see the sharding notes)", file=sys.stderr)
@@ -212,13 +314,8 @@ def main():
     kern_ms = {}
     for k, (name, _, _) in enumerate(plan):
         kern_ms[name] = float(np.mean([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)]))
-    dom = max(plan, key=lambda p: kern_ms[p[0]])
-    name, bound, work = dom
-    if bound == "mfma":
-        peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-        achieved, unit = work / (kern_ms[name] * 1e-3) / 1e12, "TFLOP/s"
-    else:
-        peak, achieved, unit = HBM_PEAK_GBS, work / (kern_ms[name] * 1e-3) / 1e9, "GB/s"
+    name, flops, nbytes = max(plan, key=lambda p: kern_ms[p[0]])
+    rl = roofline(w, flops, nbytes, kern_ms[name])
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
@@ -228,7 +325,11 @@ def main():
             traffic = ent["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
-    total_flops = sum(p[2] for p in plan if p[1] == "mfma")
+    kernels = {}
+    for kn, kf, kb in plan:
+        r = roofline(w, kf, kb, kern_ms[kn]) if (kf or kb) else {"bound": None, "frac": None}
+        kernels[kn] = {"ms": kern_ms[kn], "flops": kf, "bytes": kb, "bound": r["bound"], "frac": r["frac"]}
+    total_flops = sum(p[1] for p in plan)
     peak_fwd = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     if w.causal:
         metric = f"causal linear-attention tokens/sec (B={w.B}, H={w.H}, N={w.N}, D={w.D})"
@@ -249,15 +350,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F, "L": w.L,
                    "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
-        "roofline": {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": traffic,
-                     ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"): work,
+        "roofline": {"kernel": name, "bound": rl["bound"], "achieved": rl["achieved"], "peak": rl["peak"],
+                     "unit": rl["unit"], "frac": rl["frac"], "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_ms": kern_ms[name]},
         "forward": {"tflops": total_flops / (ms * 1e-3) / 1e12,
                     "frac_mfma_peak": total_flops / (ms * 1e-3) / 1e12 / peak_fwd,
                     "algorithmic_bytes": algorithmic_bytes(w),
                     "frac_hbm_peak": algorithmic_bytes(w) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "kernel_ms": kern_ms, "wall_s": wall},
+                    "kernels": kernels, "wall_s": wall},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -47,11 +47,15 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// elu(x) + 1 with alpha = 1: x + 1 for x > 0 and exp(x) for x <= 0, written
-// as max(x, 0) + exp(min(x, 0)) so that it needs no branch. exp uses the
-// hardware base-2 exponential: exp(x) = 2^(x log2 e).
+// elu(x) + 1 with alpha = 1: x + 1 for x > 0 and exp(x) for x <= 0. Written
+// without a branch as max(x + 1, min(exp(x), 1)): for x > 0 the clamped
+// exponential is 1 <= x + 1, and for x <= 0 exp(x) >= x + 1 (the tangent line
+// at 0 lies below the exponential). exp uses the hardware base-2 exponential,
+// exp(x) = 2^(x log2 e), and the clamp to [0, 1] folds into its output
+// modifier where NaN semantics are not required (four instructions).
 __device__ __forceinline__ float elu1(float x) {
-  return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * kLog2e);
+  const float e = __builtin_amdgcn_exp2f(x * kLog2e);
+  return fmaxf(x + 1.f, fminf(fmaxf(e, 0.f), 1.f));
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -65,6 +69,10 @@ template <typename T> using Frag = typename FragOf<T>::type;
 
 __device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// a . b + c into a new accumulator (c is only read: no copy of it is needed).
+__device__ __forceinline__ f32x16 mma_from(const f32x16& c, const bf16x8& a, const bf16x8& b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
 #pragma unroll

@@ -10,9 +10,9 @@
 //     phi[tok x 32]  = K[tok x D] . W[:, slice]     (A = K rows from LDS)
 //     KV[32 x D]    += phi^T . V                    (B = V read transposed
 //                                                    from LDS, ds_read_b64_tr_b16)
-//   K and V tiles are copied global -> LDS asynchronously into a 4-step
-//   ring: three steps are in flight while one is consumed; one barrier per
-//   step.
+//   K and V rows of 128-token super-steps are loaded into registers one
+//   super-step ahead and written to a double LDS buffer; one barrier per
+//   super-step.
 //
 // kv2_pack_kernel: adds the split partials in split order (deterministic) and
 // writes the operands of the fused query kernel as bf16 "chunks" that are
@@ -61,15 +61,16 @@ struct Kv2Shape {
   static constexpr int NW = 8;
   static constexpr int NFS = F / 32;
   static constexpr int NTW = NW / NFS;
-  static constexpr int STEP = 32 * NTW;
-  static constexpr int NS = 4;                   // ring depth (steps)
-  static constexpr int TILE = STEP * D;          // elements of the K (or V) tile of one step
-  static constexpr int SLOT = 2 * TILE;          // K tile, then V tile
-  static constexpr int PER_T = SLOT * 2 / 16 / 512;  // 16-byte pieces per thread per step
-  static_assert(PER_T * 512 * 16 == SLOT * 2, "whole pieces");
-  using WR = LdsRow<uint16_t, D>;                // W^T [F][D] staging (prologue)
+  static constexpr int STEP = 32 * NTW;           // tokens all waves consume per MFMA step
+  static constexpr int SS = 128;                  // tokens per staged super-step
+  static_assert(SS % STEP == 0, "whole steps per super-step");
+  static constexpr int TILE = SS * D;             // elements of the K (or V) tile of a super-step
+  static constexpr int BUF = 2 * TILE;            // K tile, then V tile
+  static constexpr int PER_T = BUF / 8 / 512;     // 16-byte pieces per thread per super-step
+  static_assert(PER_T * 512 * 8 == BUF && (TILE / 8) % 512 == 0, "whole pieces, K/V split per piece index");
+  using WR = LdsRow<uint16_t, D>;                 // W^T [F][D] staging (prologue)
   static constexpr int w_bytes = F * WR::bytes_per_row;
-  static constexpr int ring_bytes = NS * SLOT * 2;
+  static constexpr int ring_bytes = 2 * BUF * 2;
   static constexpr int red_floats = (D / 32) * 16 * 64 + 64;  // one wave's KV slice + ksum
   static constexpr int r_bytes = (NTW - 1) * NFS * red_floats * 4;
   static constexpr int m1 = w_bytes > ring_bytes ? w_bytes : ring_bytes;
@@ -80,7 +81,7 @@ struct Kv2Shape {
 template <int D, int F, bool PROJ>
 __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
   using S = Kv2Shape<D, F>;
-  constexpr int NFS = S::NFS, NTW = S::NTW, STEP = S::STEP, NS = S::NS, PER_T = S::PER_T;
+  constexpr int NFS = S::NFS, NTW = S::NTW, STEP = S::STEP, SS = S::SS, PER_T = S::PER_T;
   using WR = typename S::WR;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
 
@@ -91,6 +92,41 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
   const int N = a.N;
   const int t_begin = split * a.chunk;
   const int t_end = min(N, t_begin + a.chunk);
+  const int nss = (t_end - t_begin + SS - 1) / SS;
+  const uint16_t* K = a.K + (size_t)bh * N * D;
+  const uint16_t* V = a.V + (size_t)bh * N * D;
+
+  // K/V staging through registers: piece i of thread tid is piece tid + 512 i
+  // of the super-step (K pieces first). Rows past the range repeat the last
+  // valid token; their phi is masked to zero below, so they add nothing.
+  // (Direct global -> LDS copies are not used: the compiler waits for every
+  // such copy in flight before a transposed LDS read, which would serialise
+  // the prefetch.)
+  u32x4 stg[PER_T];
+  auto load_stg = [&](int ss) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const bool isv = i >= PER_T / 2;
+      const int Pl = tid + 512 * (isv ? i - PER_T / 2 : i);
+      const int row = Pl / (D / 8), p = Pl % (D / 8);
+      const int t = min(t_begin + ss * SS + row, t_end - 1);
+      stg[i] = *reinterpret_cast<const u32x4*>((isv ? V : K) + (size_t)t * D + p * 8);
+    }
+  };
+  uint16_t* const ring = reinterpret_cast<uint16_t*>(smem);
+  auto store_stg = [&](int buf) {
+    uint16_t* kt = ring + buf * S::BUF;
+    uint16_t* vt = kt + S::TILE;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const bool isv = i >= PER_T / 2;
+      const int Pl = tid + 512 * (isv ? i - PER_T / 2 : i);
+      const int row = Pl / (D / 8), p = Pl % (D / 8);
+      if (isv) *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = stg[i];
+      else *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = stg[i];
+    }
+  };
+  load_stg(0);  // in flight during the W staging below
 
   // W slice as B operand (lane = feature column f0 + c, k = D), via a transposed LDS image.
   Frag<uint16_t> wf[D / 16];
@@ -98,6 +134,8 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
     uint16_t* Wt = reinterpret_cast<uint16_t*>(smem);
     if constexpr (PROJ) {
       const uint16_t* W = a.W + (size_t)h * D * F;
+      static_assert((D / 2) * (F / 8) % 512 == 0, "whole rounds");
+#pragma unroll
       for (int u = tid; u < (D / 2) * (F / 8); u += 512) {
         const int d = 2 * (u % (D / 2)), fo = (u / (D / 2)) * 8;
         const Vec8<uint16_t> w0 = ld8(W + (size_t)d * F + fo);
@@ -114,77 +152,59 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
     __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) wf[kb] = ld_frag<uint16_t>(Wt + (f0 + c) * WR::stride + kb * 16 + 8 * g);
-    __syncthreads();  // the region becomes the step ring
+    __syncthreads();  // the region becomes the K/V double buffer
   }
   const float bcol = a.bias ? a.bias[(size_t)h * F + f0 + c] : 0.f;
-  wait_vmcnt<0>();  // bias is in a register before the asynchronous copies start
-
-  const uint16_t* K = a.K + (size_t)bh * N * D;
-  const uint16_t* V = a.V + (size_t)bh * N * D;
-  uint16_t* const ring = reinterpret_cast<uint16_t*>(smem);
-
-  // Async copy of step st into its ring slot. Piece P of the slot (16 bytes)
-  // is row (P % TILE8) / (D/8) of the K (P < TILE8) or V tile at physical
-  // piece p = P % (D/8), i.e. logical piece p ^ swizzle(row). Rows past the
-  // range repeat the last valid token: their phi is masked to zero below, so
-  // they add nothing.
-  constexpr int TILE8 = S::TILE / 8;
-  auto issue_step = [&](int st) {
-    const int t_step = t_begin + st * STEP;
-    uint16_t* slot = ring + (st % NS) * S::SLOT;
+  f32x16 bias16;  // GEMM1 starts from the bias (MFMA C operand, only read)
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int P = tid + 512 * i;
-      const int isv = P >= TILE8;
-      const int Pl = P - isv * TILE8;
-      const int row = Pl / (D / 8), p = Pl % (D / 8);
-      const int lp = isv ? (p ^ tswz<D, kTrRead>(row)) : (p ^ tswz<D, kRowRead>(row));
-      const int t = min(t_step + row, t_end - 1);
-      const uint16_t* src = (isv ? V : K) + (size_t)t * D + lp * 8;
-      copy16_async(src, slot + (512 * i + 64 * w) * 8);
-    }
-  };
+  for (int r = 0; r < 16; ++r) bias16[r] = bcol;
 
   f32x16 kv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) kv[db] = f32x16{};
   float ks = 0.f;
 
-  const int nsteps = (t_end - t_begin + STEP - 1) / STEP;
-  for (int st = 0; st < NS - 1 && st < nsteps; ++st) issue_step(st);
-  for (int st = 0; st < nsteps; ++st) {
-    // this wave's pieces of step st have landed once at most (later issued steps) x PER_T remain
-    const int later = min(NS - 2, nsteps - 1 - st);
-    if (later >= 2) wait_vmcnt<2 * PER_T>();
-    else if (later == 1) wait_vmcnt<PER_T>();
-    else wait_vmcnt<0>();
-    barrier_lds();  // step st visible to all waves; all waves are done with step st - 1
-    if (st + NS - 1 < nsteps) issue_step(st + NS - 1);
-
-    const uint16_t* kt = ring + (st % NS) * S::SLOT;
+  store_stg(0);
+  if (nss > 1) load_stg(1);
+  for (int ss = 0; ss < nss; ++ss) {
+    barrier_lds();  // super-step ss is in buffer ss & 1; every wave is done with the other buffer
+    const uint16_t* kt = ring + (ss & 1) * S::BUF;
     const uint16_t* vt = kt + S::TILE;
-    const int t0 = t_begin + st * STEP + 32 * tw;
-    f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = bcol;
+    for (int j = 0; j < SS / STEP; ++j) {
+      const int r0 = j * STEP + 32 * tw;  // this wave's 32 rows of the super-step
+      const int t0 = t_begin + ss * SS + r0;
+      if (t0 >= t_end) break;  // wave-uniform
+      f32x16 acc = mma_from(bias16, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, 8 * g)), wf[0]);
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb)
-      mma(acc, ld_frag<uint16_t>(kt + toff<D, kRowRead>(32 * tw + c, kb * 16 + 8 * g)), wf[kb]);
-    float p[16];
+      for (int kb = 1; kb < D / 16; ++kb)
+        mma(acc, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, kb * 16 + 8 * g)), wf[kb]);
+      float p[16];
+      if (t0 + 32 <= t_end) {  // wave-uniform: only the range's last step has rows past it
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = t0 + crow(lane, r) < t_end ? elu1(acc[r]) : 0.f;
-      ks += p[r];
+        for (int r = 0; r < 16; ++r) p[r] = elu1(acc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = t0 + crow(lane, r) < t_end ? elu1(acc[r]) : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ks += p[r];
+      const Frag<uint16_t> pa0 = to_frag<uint16_t>(p), pa1 = to_frag<uint16_t>(p + 8);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        mma(kv[db], pa0, tr_frag<D>(vt, r0, 32 * db, lane));
+        mma(kv[db], pa1, tr_frag<D>(vt, r0 + 16, 32 * db, lane));
+      }
     }
-    const Frag<uint16_t> pa0 = to_frag<uint16_t>(p), pa1 = to_frag<uint16_t>(p + 8);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      mma(kv[db], pa0, tr_frag<D>(vt, 32 * tw, 32 * db, lane));
-      mma(kv[db], pa1, tr_frag<D>(vt, 32 * tw + 16, 32 * db, lane));
+    // The only global loads in flight are the staged super-step's, so this
+    // wait (issued one super-step ago) is the full count.
+    if (ss + 1 < nss) {
+      store_stg((ss + 1) & 1);
+      if (ss + 2 < nss) load_stg(ss + 2);
     }
   }
   ks += shfl_xor32(ks);
-  __syncthreads();  // ring no longer read
+  __syncthreads();  // K/V buffers no longer read
 
   if constexpr (NTW > 1) {
     float* red = reinterpret_cast<float*>(smem);
@@ -234,11 +254,13 @@ struct PackArgs {
 };
 
 // Jobs of one (batch, head), by blockIdx.x:
-//   [0, F/8)            KV^T rows: 8 features x D (sum of partials), ksum, bias
-//   [F/8, F/8 + F/8)    W^T rows for 8 features (batch 0 only)
+//   [0, KVJ)            KV^T rows: FJ features x D (sum of partials), ksum, bias
+//   [KVJ, KVJ + F/8)    W^T rows for 8 features (batch 0 only)
 //   then one per 32-landmark chunk (K_L and V_L^T)
 template <int D, int F, bool PROJ>
 __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
+  constexpr int FJ = 2048 / D > F ? F : 2048 / D;  // features per KV job: (FJ/2)*(D/4) = 256 threads
+  constexpr int KVJ = F / FJ;
   const int tid = threadIdx.x;
   const int bh = blockIdx.y, h = bh % a.H, b = bh / a.H;
   const int nlb = (a.L + 31) / 32;
@@ -250,18 +272,29 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
   uint16_t* lmc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes() + pl.kv_bytes());
   const int job = blockIdx.x;
 
-  if (job < F / 8) {
-    // 8 features f0..f0+7 x D values: thread -> (feature pair, 4 consecutive d)
-    const int f0 = job * 8;
+  if (job < KVJ) {
+    // FJ features f0.. x D values: thread -> (feature pair, 4 consecutive d).
+    // Partials are loaded 8 splits at a time and added in split order.
+    const int f0 = job * FJ;
     const size_t stride = (size_t)F * D + F;
     const float* p0 = a.part + (size_t)bh * a.nsplit * stride;
-    for (int u = tid; u < 4 * (D / 4); u += 256) {
+    for (int u = tid; u < (FJ / 2) * (D / 4); u += 256) {
       const int fp = u / (D / 4), d0 = (u % (D / 4)) * 4, f = f0 + 2 * fp;
-      f32x4 s0 = *reinterpret_cast<const f32x4*>(p0 + (size_t)f * D + d0);
-      f32x4 s1 = *reinterpret_cast<const f32x4*>(p0 + (size_t)(f + 1) * D + d0);
-      for (int s = 1; s < a.nsplit; ++s) {
-        s0 += *reinterpret_cast<const f32x4*>(p0 + s * stride + (size_t)f * D + d0);
-        s1 += *reinterpret_cast<const f32x4*>(p0 + s * stride + (size_t)(f + 1) * D + d0);
+      f32x4 s0 = f32x4{}, s1 = f32x4{};
+      for (int s = 0; s < a.nsplit; s += 8) {
+        f32x4 v0[8], v1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int sk = min(s + k, a.nsplit - 1);
+          v0[k] = *reinterpret_cast<const f32x4*>(p0 + sk * stride + (size_t)f * D + d0);
+          v1[k] = *reinterpret_cast<const f32x4*>(p0 + sk * stride + (size_t)(f + 1) * D + d0);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (s + k < a.nsplit) {
+            s0 += v0[k];
+            s1 += v1[k];
+          }
       }
       // KV^T chunk f / 64, column q = (f & 32) + kperm(f & 31); f even so q + 1 holds f + 1
       uint16_t* ch = kvc + (size_t)(f / 64) * 64 * D;
@@ -272,18 +305,25 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
         *reinterpret_cast<uint32_t*>(ch + toff<64, kRowRead>(d, q)) = pack_bf16x2(s0[j], s1[j]);
       }
     }
-    if (tid < 8) {
+    if (tid < FJ) {
       const int f = f0 + tid;
-      float s = p0[(size_t)F * D + f];
-      for (int sp = 1; sp < a.nsplit; ++sp) s += p0[sp * stride + (size_t)F * D + f];
+      float s = 0.f;
+      for (int sp = 0; sp < a.nsplit; sp += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = p0[min(sp + k, a.nsplit - 1) * stride + (size_t)F * D + f];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (sp + k < a.nsplit) s += v[k];
+      }
       ksumP[kperm(f)] = s;
       biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
     }
     return;
   }
-  if (job < F / 4) {
+  if (job < KVJ + F / 8) {
     if (b != 0) return;  // W^T is per head
-    const int f0 = (job - F / 8) * 8;
+    const int f0 = (job - KVJ) * 8;
     uint16_t* wc = reinterpret_cast<uint16_t*>(a.pack_w + (size_t)h * pl.w_bytes());
     for (int u = tid; u < 8 * (D / 8); u += 256) {
       const int f = f0 + u / (D / 8), d0 = (u % (D / 8)) * 8;
@@ -298,7 +338,7 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
     }
     return;
   }
-  const int jb = job - F / 4;  // landmark chunk of 32
+  const int jb = job - KVJ - F / 8;  // landmark chunk of 32
   if (jb >= nlb) return;
   const uint16_t* K = a.K + (size_t)bh * a.N * D;
   const uint16_t* V = a.V + (size_t)bh * a.N * D;
@@ -352,7 +392,8 @@ static hipError_t launch_kv2_t(const Problem& p, const Kv2Args& ka, const PackAr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   t->mark();
-  const int jobs = F / 4 + (pa.L + 31) / 32;
+  constexpr int FJ = 2048 / D > F ? F : 2048 / D;
+  const int jobs = F / FJ + F / 8 + (pa.L + 31) / 32;
   hipLaunchKernelGGL((kv2_pack_kernel<D, F, PROJ>), dim3(jobs, p.B * p.H), dim3(256), 0, s, pa);
   e = hipGetLastError();
   t->mark();
