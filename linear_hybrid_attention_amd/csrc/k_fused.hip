@@ -9,17 +9,16 @@
 // waves per SIMD, so one wave's exp/elu work overlaps the other's MFMAs).
 // The per-head operands come from the pack written by the key/value stage as
 // a sequence of equal-size chunks (W^T, KV^T alternately per 64 features,
-// then one K_L + V_L chunk per 32 landmarks). They stream through two LDS
-// slots: the global loads of the next chunk are issued into registers before
-// the current chunk is consumed and written to the free slot after it, one
-// barrier per chunk. (Direct global -> LDS copies are avoided here: while one
-// is in flight the compiler drains every LDS read with lgkmcnt(0), which
-// stalls each MFMA on the prefetch.) Q stays in registers as the B operand of every product:
+// then one K_L + V_L^T chunk per 32 landmarks). They stream global ->
+// registers -> three LDS slots, two chunks ahead of the one being consumed in
+// the linear branch and one ahead in the landmark branch (whose accumulators
+// leave room for one register set only), one barrier per chunk. Q stays in registers as the B operand of every
+// product, and every operand read from LDS is a plain 16-byte row read:
 //   W^T chunk:   phi^T [64 f x tok]  = W^T . Q^T (+ bias, then elu + 1; phi . ksum)
 //   KV^T chunk:  num^T [D x tok]    += KV^T . phi^T
-//   landmark chunk (32 landmarks: K_L then V_L):
+//   landmark chunk (32 landmarks: K_L then V_L^T):
 //                S^T  [32 j x tok]   = K_L . Q^T  (scaled to base 2, online max)
-//                o^T  [D x tok]     += V_L^T . P^T  (V_L read transposed)
+//                o^T  [D x tok]     += V_L^T . P^T
 // The online softmax keeps a running row max m and only rescales o and the
 // row sum when a new score exceeds m by more than 8 (base 2), so the exp
 // arguments stay below 2^8 and most chunks skip the rescale.
@@ -48,10 +47,9 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   constexpr int NFC = F / 64;
   constexpr int PER_T = CH * 2 / 16 / 256;  // 16-byte pieces per thread per chunk
   static_assert(PER_T * 256 * 16 == CH * 2, "whole pieces");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * F * 4 + 2 * CH * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * F * 4 + 3 * CH * 2];
   float* vecS = reinterpret_cast<float*>(smem);  // biasP [F] | ksumP [F]
-  uint16_t* slot0 = reinterpret_cast<uint16_t*>(smem + 2 * F * 4);
-  uint16_t* slot1 = slot0 + CH;
+  uint16_t* const slots = reinterpret_cast<uint16_t*>(smem + 2 * F * 4);  // 3 chunk slots
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
@@ -72,46 +70,60 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   const int nlc = (L + 31) / 32;  // landmark chunks
   const int nch = 2 * NFC + nlc;
 
-  // Register-staged chunk copies: the global loads of chunk ci + 1 are issued
-  // before chunk ci is consumed and written to the other LDS slot after it.
-  u32x4 stg[PER_T];
-  auto load_chunk = [&](int ci) {
-    const uint16_t* src = ci < 2 * NFC ? ((ci & 1) ? kvpk : wpk) + (ci >> 1) * CH : lmpk + (ci - 2 * NFC) * CH;
-    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) stg[i] = s4[tid + 256 * i];
+  // Chunk ci streams global -> registers -> LDS slot ci % 3. Its loads are
+  // issued two chunks ahead (at the start of step ci - 2, into register set
+  // ci & 1) and it is written to LDS at the end of step ci - 1, so each load
+  // has two steps of compute to land. The sets are named statically (the
+  // loops below take chunks in pairs of even and odd index), and loads are
+  // issued on every step (indexes clamped) so the compiler's count of loads
+  // in flight, and with it every wait, is exact.
+  auto chunk_src = [&](int ci) {
+    ci = min(ci, nch - 1);
+    return reinterpret_cast<const u32x4*>(ci < 2 * NFC ? ((ci & 1) ? kvpk : wpk) + (ci >> 1) * CH
+                                                       : lmpk + (ci - 2 * NFC) * CH);
   };
-  auto store_chunk = [&](uint16_t* slot) {
-    u32x4* d4 = reinterpret_cast<u32x4*>(slot);
+  u32x4 sa[PER_T], sb[PER_T];  // register sets for even / odd chunks
+  auto load_to = [&](u32x4 (&st)[PER_T], int ci) {
+    const u32x4* s4 = chunk_src(ci);
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) d4[tid + 256 * i] = stg[i];
+    for (int i = 0; i < PER_T; ++i) st[i] = s4[tid + 256 * i];
   };
+  auto store_from = [&](const u32x4 (&st)[PER_T], int ci) {
+    u32x4* d4 = reinterpret_cast<u32x4*>(slots + (ci % 3) * CH);
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) d4[tid + 256 * i] = st[i];
+  };
+  auto slot_of = [&](int ci) -> const uint16_t* { return slots + (ci % 3) * CH; };
 
-  // prologue: bias/ksum vectors, chunk 0, Q fragments
+  // prologue: query fragments, then chunks 0 and 1; chunk 0 to LDS
+  Frag<uint16_t> qf[D / 16];
+  const uint16_t* Qp = a.Q + ((size_t)bh * N + (tok_ok ? tok : 0)) * D + 8 * g;
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) qf[kb] = ld_frag<uint16_t>(Qp + kb * 16);  // rows past N: row 0, not stored
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(pbh);
     u32x4* dst = reinterpret_cast<u32x4*>(smem);
     for (int i = tid; i < 2 * F * 4 / 16; i += 256) dst[i] = src[i];
   }
-  load_chunk(0);
-  store_chunk(slot0);
-  Frag<uint16_t> qf[D / 16];
-  const uint16_t* Qp = a.Q + ((size_t)bh * N + (tok_ok ? tok : 0)) * D + 8 * g;
-#pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) qf[kb] = tok_ok ? ld_frag<uint16_t>(Qp + kb * 16) : zero_frag<uint16_t>();
-  barrier_lds();
+  const float gh = L > 0 ? a.g[h] : 0.f;
+  load_to(sa, 0);
+  load_to(sb, 1);
+  store_from(sa, 0);
 
   f32x16 num[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) num[db] = f32x16{};
   float den = 0.f;
 
-  // ---- linear branch: per 64 features, a W^T chunk (slot 0) then a KV^T chunk (slot 1)
+  // ---- linear branch: per 64 features, a W^T chunk (even) then a KV^T chunk (odd)
 #pragma clang loop unroll(disable)
   for (int fc = 0; fc < NFC; ++fc) {
-    load_chunk(2 * fc + 1);
+    const int ci = 2 * fc;
+    barrier_lds();  // chunk ci in LDS; every wave is done with step ci - 1
+    load_to(sa, ci + 2);
     Frag<uint16_t> pb[4];  // phi^T of these 64 features, 4 k-blocks of 16
     {
+      const uint16_t* wt = slot_of(ci);
       // two independent accumulation chains (feature blocks 0 and 1), interleaved
       f32x16 acc[2];
 #pragma unroll
@@ -124,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       for (int kb = 0; kb < D / 16; ++kb)
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
-          mma(acc[fb], ld_frag<uint16_t>(slot0 + toff<D, kRowRead>(fb * 32 + c, kb * 16 + 8 * g)), qf[kb]);
+          mma(acc[fb], ld_frag<uint16_t>(wt + toff<D, kRowRead>(fb * 32 + c, kb * 16 + 8 * g)), qf[kb]);
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) {
         const float* kp = vecS + F + fc * 64 + fb * 32 + 8 * g;
@@ -137,21 +149,23 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
         pb[2 * fb + 1] = to_frag<uint16_t>(p + 8);
       }
     }
-    store_chunk(slot1);
-    barrier_lds();
-    if (2 * fc + 2 < nch) load_chunk(2 * fc + 2);
+    store_from(sb, ci + 1);
+    barrier_lds();  // chunk ci + 1 in LDS
+    load_to(sb, ci + 3);
+    {
+      const uint16_t* kvt = slot_of(ci + 1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        mma(num[db], ld_frag<uint16_t>(slot1 + toff<64, kRowRead>(db * 32 + c, kk * 16 + 8 * g)), pb[kk]);
-    if (2 * fc + 2 < nch) store_chunk(slot0);
-    barrier_lds();
+        for (int kk = 0; kk < 4; ++kk)
+          mma(num[db], ld_frag<uint16_t>(kvt + toff<64, kRowRead>(db * 32 + c, kk * 16 + 8 * g)), pb[kk]);
+    }
+    if (ci + 2 < nch) store_from(sa, ci + 2);
   }
   den += shfl_xor32(den);
   {
     const float inv = 1.f / (den + a.eps);
-    const float alpha = L > 0 ? 1.f / (1.f + expf(-a.g[h])) : 1.f;  // g = +inf -> 1, g = -inf -> 0
+    const float alpha = L > 0 ? 1.f / (1.f + expf(-gh)) : 1.f;  // g = +inf -> 1, g = -inf -> 0
     const float ca = alpha * inv;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -159,29 +173,19 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       for (int r = 0; r < 16; ++r) num[db][r] *= ca;  // alpha * out_lin
   }
 
-  // ---- landmark branch: one chunk per 32 landmarks, K_L [32 j][D] then V_L [32 j][D];
-  // chunk lc sits in slot lc % 2 (the linear branch used an even number of chunks)
+  // ---- landmark branch: one chunk per 32 landmarks, K_L [32 j][D] then V_L^T [D][32 j]
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
   const float sl2 = kLog2e * rsqrtf((float)D);
-#pragma clang loop unroll(disable)
-  for (int lc = 0; lc < nlc; ++lc) {
-    const int ci = 2 * NFC + lc;
-    if (ci + 1 < nch) load_chunk(ci + 1);
-    const uint16_t* sl = (lc & 1) ? slot1 : slot0;
-    const uint16_t* vl = sl + 32 * D;
+  auto lm_step = [&](int lc) {
+    const uint16_t* kl = slot_of(2 * NFC + lc);
+    const uint16_t* vlt = kl + 32 * D;
     const int j0 = lc * 32;
-    // scores: two independent half-depth chains, added at the end
-    f32x16 s = f32x16{}, s2 = f32x16{};
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < D / 16; kb += 2) {
-      mma(s, ld_frag<uint16_t>(sl + toff<D, kRowRead>(c, kb * 16 + 8 * g)), qf[kb]);
-      mma(s2, ld_frag<uint16_t>(sl + toff<D, kRowRead>(c, kb * 16 + 16 + 8 * g)), qf[kb + 1]);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += s2[r];
+    for (int kb = 0; kb < D / 16; ++kb) mma(s, ld_frag<uint16_t>(kl + toff<D, kRowRead>(c, kb * 16 + 8 * g)), qf[kb]);
     // row max of the raw scores (landmarks past L masked to -inf; only the last
     // chunk can hold such landmarks)
     float mx = -INFINITY;
@@ -214,18 +218,32 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
     const Frag<uint16_t> p0 = to_frag<uint16_t>(p), p1 = to_frag<uint16_t>(p + 8);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      mma(o[db], tr_frag<D>(vl, 0, 32 * db, lane), p0);
-      mma(o[db], tr_frag<D>(vl, 16, 32 * db, lane), p1);
+      mma(o[db], ld_frag<uint16_t>(vlt + toff32(db * 32 + c, 8 * g)), p0);
+      mma(o[db], ld_frag<uint16_t>(vlt + toff32(db * 32 + c, 16 + 8 * g)), p1);
     }
-    if (ci + 1 < nch) store_chunk((lc & 1) ? slot0 : slot1);
+  };
+  // The first landmark chunk's successor is already in set b (loaded by the
+  // last linear step); after it, one register set suffices: each step loads
+  // its successor and writes it to LDS at its end.
+  if (nlc > 0) {  // workgroup-uniform
     barrier_lds();
+    lm_step(0);
+    if (2 * NFC + 1 < nch) store_from(sb, 2 * NFC + 1);
   }
+#pragma clang loop unroll(disable)
+  for (int lc = 1; lc < nlc; ++lc) {
+    const int ci = 2 * NFC + lc;
+    barrier_lds();
+    load_to(sa, ci + 1);
+    lm_step(lc);
+    if (ci + 1 < nch) store_from(sa, ci + 1);
+  }
+  barrier_lds();  // the slots are free for the output staging
 
-  // Epilogue: the wave's 32 x D output tile goes through LDS (the ring is free
-  // after the last barrier) so that the global stores are whole 16-byte pieces,
-  // four full rows per store instruction.
-  const float cb = L > 0 ? (1.f - 1.f / (1.f + expf(-a.g[h]))) / l : 0.f;
-  uint16_t* ot = slot0 + w * 32 * D;  // [32 tokens][D], kRowRead swizzle
+  // Epilogue: the wave's 32 x D output tile goes through LDS so that the
+  // global stores are whole 16-byte pieces, four full rows per store instruction.
+  const float cb = L > 0 ? (1.f - 1.f / (1.f + expf(-gh))) / l : 0.f;
+  uint16_t* ot = slots + w * 32 * D;  // [32 tokens][D], kRowRead swizzle
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll

@@ -21,7 +21,7 @@
 //   per head h:         W^T chunks  [64 f][D]        (F / 64 of them)
 //   per (batch, head):  bias, ksum  [F] fp32 each, in kperm order
 //                       KV^T chunks [D][64 f]        (F / 64)
-//                       per 32 landmarks: K_L [32 j][D], V_L [32 j][D]
+//                       per 32 landmarks: K_L [32 j][D], V_L^T [D][32 j]
 //   with landmarks idx_j = floor(j N / L) ("Flux2TTRTrainer", section "How the
 //   distillation works": exact softmax over strided landmark tokens).
 #include "common.hpp"
@@ -33,7 +33,8 @@ namespace ttr {
 // ---------------------------------------------------------------- pack layout
 // Every chunk holds 64 * D bf16 elements:
 //   W^T chunk   [64 f][D]   kRowRead      KV^T chunk [D][64 f]   kRowRead
-//   landmark chunk: K_L [32 j][D] kRowRead, then V_L [32 j][D] kTrRead
+//   landmark chunk: K_L [32 j][D] kRowRead, then V_L^T [D][32 j] (toff32),
+//   landmark j in column kperm(j)
 // Feature columns of a KV^T chunk are in MFMA C-row order: column
 // (f & 32) + kperm(f & 31) holds feature f of the chunk.
 struct PackLayout {
@@ -175,10 +176,16 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
       const int r0 = j * STEP + 32 * tw;  // this wave's 32 rows of the super-step
       const int t0 = t_begin + ss * SS + r0;
       if (t0 >= t_end) break;  // wave-uniform
+      // two independent chains over alternate k-blocks, added at the end
       f32x16 acc = mma_from(bias16, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, 8 * g)), wf[0]);
+      f32x16 acc2 = mma_from(f32x16{}, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, 16 + 8 * g)), wf[1]);
 #pragma unroll
-      for (int kb = 1; kb < D / 16; ++kb)
+      for (int kb = 2; kb < D / 16; kb += 2) {
         mma(acc, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, kb * 16 + 8 * g)), wf[kb]);
+        mma(acc2, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, kb * 16 + 16 + 8 * g)), wf[kb + 1]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
       float p[16];
       if (t0 + 32 <= t_end) {  // wave-uniform: only the range's last step has rows past it
 #pragma unroll
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
   const uint16_t* V = a.V + (size_t)bh * a.N * D;
   uint16_t* kl = lmc + (size_t)jb * pl.chunk_elems();
   uint16_t* vl = kl + 32 * D;
-  // K_L [32 j][D] (row reads) and V_L [32 j][D] (transposed reads); rows past L are zero
+  // K_L [32 j][D] and V_L^T [D][32 j] (both read as rows); landmarks past L are zero
   for (int u = tid; u < 2 * 32 * (D / 8); u += 256) {
     const int isv = u >= 32 * (D / 8);
     const int uu = u - isv * 32 * (D / 8);
@@ -352,8 +359,12 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
     const uint16_t* src = isv ? V : K;
     const Vec8<uint16_t> v =
         j < a.L ? ld8(src + (size_t)(((long long)j * a.N) / a.L) * D + d0) : zero8<uint16_t>();
-    if (isv) st8(vl + toff<D, kTrRead>(jl, d0), v);
-    else st8(kl + toff<D, kRowRead>(jl, d0), v);
+    if (isv) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vl[toff32(d0 + e, kperm(jl))] = v.v[e];
+    } else {
+      st8(kl + toff<D, kRowRead>(jl, d0), v);
+    }
   }
 }
 

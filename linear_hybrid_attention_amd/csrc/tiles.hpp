@@ -30,6 +30,14 @@ __host__ __device__ __forceinline__ constexpr int toff(int row, int col) {
   return row * COLS + (((col >> 3) ^ tswz<COLS, KIND>(row)) << 3) + (col & 7);
 }
 
+// Element offset of (row r, column j) in a bf16 tile with 32 columns (64-byte
+// rows), stored as rows of 128 bytes holding rows 2 i and 2 i + 1 with the
+// kRowRead swizzle, so that 16-byte row reads by 32 consecutive rows are
+// spread over the banks.
+__host__ __device__ __forceinline__ constexpr int toff32(int r, int j) {
+  return toff<64, kRowRead>(r >> 1, ((r & 1) << 5) + j);
+}
+
 // Fragment (8 k-values of one lane) of a tile stored [k rows][n cols] (kTrRead
 // layout), for the 16 k-rows starting at k0 and the 32 n-columns starting at
 // n0. Slot 8g + i of lane l (g = l / 32) holds k = k0 + crow(l, i): the same
