@@ -42,8 +42,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     ap.add_argument("--write-traffic", default=None, metavar="DIR",
-                    help="only turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv runs under DIR (fetch/, write/, "
-                         "copy_fetch/, copy_write/) into profiles/traffic_counters.json")
+                    help="only turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv runs under DIR (fetch/, write/ of "
+                         "--workload; copy_fetch/, copy_write/ of --copy-calibration --copy-mib) into "
+                         "profiles/traffic_counters.json")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy in the counter runs")
     return ap.parse_args()
 
 
@@ -74,7 +76,7 @@ def _pmc_means(run_dir, counter):
     return {name: sum(d.values()) / len(d) for name, d in sums.items()}
 
 
-def write_traffic(run_dir):
+def write_traffic(run_dir, wl, copy_mib):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for a plain copy of known size."""
     import workloads
     fetch, write = _pmc_means(os.path.join(run_dir, "fetch"), "FETCH_SIZE"), \
@@ -82,12 +84,9 @@ def write_traffic(run_dir):
     cf = _pmc_means(os.path.join(run_dir, "copy_fetch"), "FETCH_SIZE")
     cw = _pmc_means(os.path.join(run_dir, "copy_write"), "WRITE_SIZE")
     copy_name = max(cf, key=cf.get)  # the copy kernel is the only large dispatch of that run
-    with open(os.path.join(run_dir, "copy_bytes.txt")) as f:
-        copy_bytes = int(f.read().split()[0])
+    copy_bytes = copy_mib << 20
     f_scale = copy_bytes / (cf[copy_name] * 1024.0)
     w_scale = copy_bytes / (cw[copy_name] * 1024.0)
-    with open(os.path.join(run_dir, "workload.txt")) as f:
-        wl = f.read().split()[0]
     w = workloads.WORKLOADS[wl]
     out = {}
     if os.path.exists(TRAFFIC_FILE):
@@ -237,7 +236,7 @@ def cpu_baseline(w, x, target_s):
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(args.write_traffic)
+        write_traffic(args.write_traffic, args.workload, args.copy_mib)
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
