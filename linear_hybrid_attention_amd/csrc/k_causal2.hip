@@ -43,7 +43,10 @@ struct Causal2Shape {
   static constexpr int TILE = C * D;               // elements of the K (or V) tile
   static constexpr int PER_T = 2 * TILE / 8 / 256;  // 16-byte pieces per thread per chunk (K then V)
   static_assert(PER_T * 256 * 8 == 2 * TILE && (TILE / 8) % 256 == 0, "whole pieces, K/V split per piece index");
-  static constexpr int kv_bytes = 2 * TILE * 2;
+  // phi(K) is read transposed by the state update and, in the walk, also as
+  // rows by the score product: the walk keeps it twice, once per swizzle.
+  static constexpr int nk = WALK ? 2 : 1;
+  static constexpr int kv_bytes = (nk + 1) * TILE * 2;
   static constexpr int pt_bytes = WALK ? D * D * 2 : 0;  // P^T as MFMA operand, [d][f] kRowRead
   static constexpr int zb_bytes = 2 * D * 4;             // z, then the bias (zeros without one)
   static constexpr int NB = C / 32;                // 32-token blocks per chunk
@@ -59,8 +62,9 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
   using S = Causal2Shape<C, WALK>;
   constexpr int D = 64, NB = S::NB, QB = S::QB, PER_T = S::PER_T;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
-  uint16_t* kt = reinterpret_cast<uint16_t*>(smem);  // phi(K) rows, kRowRead
-  uint16_t* vt = kt + S::TILE;                        // V rows, kTrRead
+  uint16_t* ktt = reinterpret_cast<uint16_t*>(smem);  // phi(K) rows, kTrRead (state update)
+  uint16_t* vt = ktt + S::TILE;                        // V rows, kTrRead
+  uint16_t* kt = vt + S::TILE;                         // phi(K) rows, kRowRead (walk: scores)
   float* zS = reinterpret_cast<float*>(smem + S::kv_bytes + S::pt_bytes);
   float* bS = zS + D;
   uint16_t* Pt = reinterpret_cast<uint16_t*>(smem + S::kv_bytes);
@@ -79,6 +83,7 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
   const int cbeg = s * a.cps, cend = min(nchunks, cbeg + a.cps);
   if (cbeg >= cend) return;
 
+  const Frag<uint16_t> ones = __builtin_bit_cast(Frag<uint16_t>, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   // P^T tile owned by this wave: rows dt*32.., columns ft*32.. (dt = w >> 1, ft = w & 1).
   const int dt = w >> 1, ft = w & 1;
   f32x16 P = f32x16{};
@@ -127,7 +132,8 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
         Vec8<uint16_t> v = __builtin_bit_cast(Vec8<uint16_t>, stg[i]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v.v[j] = f2bf(elu1(bf2f(v.v[j]) + kb[j]) * keep);
-        *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = __builtin_bit_cast(u32x4, v);
+        *reinterpret_cast<u32x4*>(ktt + toff<D, kTrRead>(row, p * 8)) = __builtin_bit_cast(u32x4, v);
+        if constexpr (WALK) *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = __builtin_bit_cast(u32x4, v);
       }
     }
   };
@@ -207,24 +213,34 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] = elu1(v[j] + bS[kb2 * 16 + 8 * g + j]);
           qf[i][kb2] = to_frag<uint16_t>(v);
-          float vr[8];
-          frag_to_f32(qf[i][kb2], vr);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) den0[i] += vr[j] * zS[kb2 * 16 + 8 * g + j];
+          for (int j = 0; j < 8; ++j) den0[i] += v[j] * zS[kb2 * 16 + 8 * g + j];
         }
       }
       load_q(min(ch + 1, cend - 1));
     }
 
     // Next state: P^T[dt block][ft block] += V^T phi(K) over the chunk and
-    // z += column sums of phi(K), in registers (the LDS copy is updated after
+    // z += column sums of phi(K) (here an MFMA against an all-ones operand:
+    // every row of Z holds the sums), in registers (the LDS copy is updated after
     // every wave has read the current one).
-    {
+    // (The walk, short of registers, sums z on the VALU instead.)
+    if constexpr (!WALK) {
+      f32x16 Z = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < C / 16; ++kk) {
+        const Frag<uint16_t> av = tr_frag<D>(vt, kk * 16, dt * 32, lane);
+        const Frag<uint16_t> bk = tr_frag<D>(ktt, kk * 16, ft * 32, lane);
+        mma(P, av, bk);
+        mma(Z, ones, bk);
+      }
+      zr += Z[0];
+    } else {
       float zp = 0.f;
 #pragma unroll
       for (int kk = 0; kk < C / 16; ++kk) {
         const Frag<uint16_t> av = tr_frag<D>(vt, kk * 16, dt * 32, lane);
-        const Frag<uint16_t> bk = tr_frag<D, kRowRead>(kt, kk * 16, ft * 32, lane);
+        const Frag<uint16_t> bk = tr_frag<D>(ktt, kk * 16, ft * 32, lane);
         float bv[8];
         frag_to_f32(bk, bv);
 #pragma unroll
@@ -248,28 +264,37 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
           for (int kb2 = 0; kb2 < D / 16; ++kb2)
             mma(num[db], ld_frag<uint16_t>(Pt + toff<D, kRowRead>(db * 32 + c, kb2 * 16 + 8 * g)), qf[i][kb2]);
         }
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-          if (kb > qb) break;
+        // score blocks: kb < qb whole, then the diagonal block kb == qb with
+        // the keys after the query masked. The normaliser sums the fp32
+        // scores (the products use their bf16 rounding).
+        auto score_block = [&](int kb, bool diag) {
           f32x16 sc = f32x16{};
 #pragma unroll
           for (int kb2 = 0; kb2 < D / 16; ++kb2)
             mma(sc, ld_frag<uint16_t>(kt + toff<D, kRowRead>(kb * 32 + c, kb2 * 16 + 8 * g)), qf[i][kb2]);
+          if (diag) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[r] = crow(lane, r) > c ? 0.f : sc[r];
+          }
           float sv[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sv[r] = (kb == qb && crow(lane, r) > c) ? 0.f : sc[r];
+          for (int r = 0; r < 16; ++r) {
+            sv[r] = sc[r];
+            den += sv[r];
+          }
           const Frag<uint16_t> sb0 = to_frag<uint16_t>(sv), sb1 = to_frag<uint16_t>(sv + 8);
-          float sr[16];
-          frag_to_f32(sb0, sr);
-          frag_to_f32(sb1, sr + 8);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) den += sr[r];
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             mma(num[db], tr_frag<D>(vt, kb * 32, db * 32, lane), sb0);
             mma(num[db], tr_frag<D>(vt, kb * 32 + 16, db * 32, lane), sb1);
           }
+        };
+#pragma unroll
+        for (int kb = 0; kb < NB - 1; ++kb) {
+          if (kb >= qb) break;  // wave-uniform
+          score_block(kb, false);
         }
+        score_block(qb, true);
         den += shfl_xor32(den);
         const float inv = 1.f / (den + a.eps);
         // 32 x 64 output block -> this wave's LDS staging (swizzled rows)

@@ -8,9 +8,12 @@
 //              consecutive rows at one column (phys = piece ^ (row & 15) for
 //              rows of >= 256 bytes, piece ^ ((row >> 1) & 7) for 128 bytes).
 //   kTrRead:   rows read column-wise with ds_read_b64_tr_b16 (the tile holds
-//              [k][n]; the read yields a fragment with k in registers):
-//              phys = piece ^ ((row & 3) << 2) for >= 256-byte rows,
-//              piece ^ (((row >> 1) & 3) << 1) for 128-byte rows.
+//              [k][n]; the read yields a fragment with k in registers). Half a
+//              wave reads 4 consecutive rows x 64 bytes; rows whose addresses
+//              are a multiple of 256 bytes apart share banks, so their 64-byte
+//              windows are moved apart: phys = piece ^ ((row & 3) << 2) for
+//              >= 256-byte rows, piece ^ (((row >> 1) & 1) << 2) for 128-byte
+//              rows (rows r and r + 2 of a group of 4).
 #pragma once
 #include "common.hpp"
 
@@ -22,7 +25,7 @@ template <int COLS, int KIND>
 __host__ __device__ __forceinline__ constexpr int tswz(int row) {
   static_assert(COLS * 2 == 128 || COLS * 2 >= 256, "row size");
   if constexpr (KIND == kRowRead) return (COLS * 2 == 128) ? ((row >> 1) & 7) : (row & 15);
-  else return (COLS * 2 == 128) ? (((row >> 1) & 3) << 1) : ((row & 3) << 2);
+  else return (COLS * 2 == 128) ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
 }
 // element offset of (row, col) in a bf16 tile with COLS columns
 template <int COLS, int KIND>
