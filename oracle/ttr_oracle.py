@@ -32,6 +32,9 @@ Every function computes the plain definition in float64 with numpy, one
 * The causal mask includes the diagonal (key index <= query index).
 * Without W the feature map is the identity projection: phi(x) = elu(x + b) + 1
   with F = D (b optional).
+* The relu and softmax feature maps ("NNT Define Linear Attention", section
+  "The inputs") are max(z, 0) and the softmax over each token's features,
+  applied to z = x (+ b) like elu + 1.
 
 Pins (tests/test_oracle.py): brute-force N x N row-normalised attention,
 torch's elu and scaled_dot_product_attention in fp64, closed forms
@@ -47,7 +50,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "elu_plus_one", "feature_map", "kv_reduce", "apply", "landmark_indices",
+    "elu_plus_one", "relu_map", "softmax_map", "MAPS", "feature_map", "kv_reduce", "apply", "landmark_indices",
     "landmark_attn", "blend", "hybrid_forward", "causal_forward",
     "hybrid_rows", "causal_rows", "normwise_err",
 ]
@@ -69,19 +72,42 @@ def elu_plus_one(z: np.ndarray) -> np.ndarray:
     return np.where(z > 0.0, z + 1.0, np.exp(np.minimum(z, 0.0)))
 
 
-def _phi_slice(x: np.ndarray, W: Optional[np.ndarray], b: Optional[np.ndarray]) -> np.ndarray:
+def relu_map(z: np.ndarray) -> np.ndarray:
+    """max(z, 0): the relu feature map of "NNT Define Linear Attention", section
+    "The inputs" (named there beside elu as cheap and non-negative)."""
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0)
+
+
+def softmax_map(z: np.ndarray) -> np.ndarray:
+    """Softmax over the feature axis (the last one) of every token: the softmax
+    feature map of "NNT Define Linear Attention", section "The inputs". The
+    page names the option only; normalising each token's features (not the
+    tokens) is the reading taken, since the map replaces the similarity score
+    by a dot product of mapped features."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# map kind -> function name (looked up when called)
+MAPS = {"elu1": "elu_plus_one", "relu": "relu_map", "softmax": "softmax_map"}
+
+
+def _phi_slice(x: np.ndarray, W: Optional[np.ndarray], b: Optional[np.ndarray], kind: str = "elu1") -> np.ndarray:
     # x [N, D] -> phi [N, F]; one head's map.
     z = x @ W if W is not None else x.copy()
     if b is not None:
         z = z + b[None, :]
-    return elu_plus_one(z)
+    return globals()[MAPS[kind]](z)
 
 
-def feature_map(X, W=None, b=None) -> np.ndarray:
-    """phi(X) = elu(X W_h + b_h) + 1 per (batch, head).  X [B,H,N,D] -> [B,H,N,F].
+def feature_map(X, W=None, b=None, kind: str = "elu1") -> np.ndarray:
+    """phi(X) = map(X W_h + b_h) per (batch, head).  X [B,H,N,D] -> [B,H,N,F].
 
-    North-star feature map; "Flux2TTRTrainer" section "Inputs worth setting"
-    (feature_dim F); "NNT Define Linear Attention" section "The inputs" (elu+1).
+    map is elu(z) + 1 by default (north-star feature map; "Flux2TTRTrainer"
+    section "Inputs worth setting" for feature_dim F; "NNT Define Linear
+    Attention" section "The inputs" for elu + 1), or relu / softmax over the
+    features (the other options of that section).
     """
     X, W, b = _f64(X), _f64(W), _f64(b)
     B, H, N, D = X.shape
@@ -89,18 +115,18 @@ def feature_map(X, W=None, b=None) -> np.ndarray:
     out = np.empty((B, H, N, F))
     for bi in range(B):
         for h in range(H):
-            out[bi, h] = _phi_slice(X[bi, h], None if W is None else W[h], None if b is None else b[h])
+            out[bi, h] = _phi_slice(X[bi, h], None if W is None else W[h], None if b is None else b[h], kind)
     return out
 
 
-def kv_reduce(K, V, W=None, b=None):
+def kv_reduce(K, V, W=None, b=None, kind: str = "elu1"):
     """KV_h = phi(K)^T V  [B,H,F,D] and ksum_h = sum_n phi(K)_n  [B,H,F].
 
     "NNT Define Linear Attention", section "How it works" (accumulate kv = K^T V,
     the sum of K' for the normaliser).
     """
     K, V = _f64(K), _f64(V)
-    phik = feature_map(K, W, b)
+    phik = feature_map(K, W, b, kind)
     B, H, N, F = phik.shape
     D = V.shape[3]
     KV = np.empty((B, H, F, D))
@@ -112,13 +138,13 @@ def kv_reduce(K, V, W=None, b=None):
     return KV, ksum
 
 
-def apply(Q, W, b, KV, ksum, eps) -> np.ndarray:
+def apply(Q, W, b, KV, ksum, eps, kind: str = "elu1") -> np.ndarray:
     """out_lin = (phi(Q) KV) / (phi(Q) . ksum + eps)  [B,H,N,D].
 
     "NNT Define Linear Attention", section "How it works" (Q'(K'^T V), normalised by
     1 / (Q' . sum(K') + eps)); eps from section "The inputs".
     """
-    phiq = feature_map(Q, W, b)
+    phiq = feature_map(Q, W, b, kind)
     KV, ksum = _f64(KV), _f64(ksum)
     eps = float(eps)
     B, H, N, F = phiq.shape
@@ -184,21 +210,23 @@ def blend(out_lin, out_lm, g) -> np.ndarray:
     return a * out_lin + (1.0 - a) * out_lm
 
 
-def hybrid_forward(Q, K, V, W, b, g, eps, L: int) -> np.ndarray:
+def hybrid_forward(Q, K, V, W, b, g, eps, L: int, kind: str = "elu1") -> np.ndarray:
     """The TTR hybrid forward: linear kernel branch, landmark softmax branch, blend.
 
-    With L = 0 the landmark branch is absent and the result is out_lin.
+    With L = 0 the landmark branch is absent and the result is out_lin (the
+    plain linear attention of "NNT Define Linear Attention", with any of its
+    feature maps).
     """
-    KV, ksum = kv_reduce(K, V, W, b)
-    lin = apply(Q, W, b, KV, ksum, eps)
+    KV, ksum = kv_reduce(K, V, W, b, kind)
+    lin = apply(Q, W, b, KV, ksum, eps, kind)
     if L == 0:
         return lin
     lm = landmark_attn(Q, K, V, L)
     return blend(lin, lm, g)
 
 
-def causal_forward(Q, K, V, W, b, eps) -> np.ndarray:
-    """Causal elu+1 linear attention as the running prefix over tokens.
+def causal_forward(Q, K, V, W, b, eps, kind: str = "elu1") -> np.ndarray:
+    """Causal linear attention (elu+1 by default) as the running prefix over tokens.
 
     For n = 0..N-1:  S += phi(k_n) v_n^T,  z += phi(k_n),
     out_n = phi(q_n) S / (phi(q_n) . z + eps).
@@ -206,8 +234,8 @@ def causal_forward(Q, K, V, W, b, eps) -> np.ndarray:
     only to earlier tokens, here including themselves) and section "How it works".
     Vectorised over the (batch, head) slices; the loop runs over tokens.
     """
-    phiq = feature_map(Q, W, b)
-    phik = feature_map(K, W, b)
+    phiq = feature_map(Q, W, b, kind)
+    phik = feature_map(K, W, b, kind)
     V = _f64(V)
     eps = float(eps)
     B, H, N, F = phiq.shape
@@ -226,7 +254,7 @@ def causal_forward(Q, K, V, W, b, eps) -> np.ndarray:
     return out
 
 
-def hybrid_rows(Q, K, V, W, b, g, eps, L: int, rows: Sequence[tuple]) -> np.ndarray:
+def hybrid_rows(Q, K, V, W, b, g, eps, L: int, rows: Sequence[tuple], kind: str = "elu1") -> np.ndarray:
     """hybrid_forward evaluated only at the listed (batch, head, token) rows.
 
     The linear branch uses the kernel-regression form of the same definition
@@ -243,11 +271,11 @@ def hybrid_rows(Q, K, V, W, b, g, eps, L: int, rows: Sequence[tuple]) -> np.ndar
         if key not in cache:
             Wh = None if W is None else W[h]
             bh = None if b is None else b[h]
-            cache[key] = _phi_slice(K[bi, h], Wh, bh)
+            cache[key] = _phi_slice(K[bi, h], Wh, bh, kind)
         phik = cache[key]
         Wh = None if W is None else W[h]
         bh = None if b is None else b[h]
-        phiq = _phi_slice(Q[bi, h][n:n + 1], Wh, bh)[0]
+        phiq = _phi_slice(Q[bi, h][n:n + 1], Wh, bh, kind)[0]
         wts = phik @ phiq
         lin = (wts @ V[bi, h]) / (wts.sum() + float(eps))
         if L == 0:
@@ -262,7 +290,7 @@ def hybrid_rows(Q, K, V, W, b, g, eps, L: int, rows: Sequence[tuple]) -> np.ndar
     return res
 
 
-def causal_rows(Q, K, V, W, b, eps, rows: Sequence[tuple]) -> np.ndarray:
+def causal_rows(Q, K, V, W, b, eps, rows: Sequence[tuple], kind: str = "elu1") -> np.ndarray:
     """causal_forward evaluated only at the listed (batch, head, token) rows.
 
     Direct masked sum for row n: weights phi(q_n) . phi(k_m) for m <= n,
@@ -274,8 +302,8 @@ def causal_rows(Q, K, V, W, b, eps, rows: Sequence[tuple]) -> np.ndarray:
     for i, (bi, h, n) in enumerate(rows):
         Wh = None if W is None else W[h]
         bh = None if b is None else b[h]
-        phik = _phi_slice(K[bi, h][: n + 1], Wh, bh)
-        phiq = _phi_slice(Q[bi, h][n:n + 1], Wh, bh)[0]
+        phik = _phi_slice(K[bi, h][: n + 1], Wh, bh, kind)
+        phiq = _phi_slice(Q[bi, h][n:n + 1], Wh, bh, kind)[0]
         wts = phik @ phiq
         res[i] = (wts @ V[bi, h][: n + 1]) / (wts.sum() + float(eps))
     return res

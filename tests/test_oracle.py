@@ -54,8 +54,14 @@ HAND_X = np.array([0.0, 1.0, 3.0]).reshape(1, 1, 3, 1)
 HAND_V = np.array([3.0, 6.0, -3.0]).reshape(1, 1, 3, 1)
 
 
-def brute_linear(Q, K, V, W, b, eps, causal=False):
-    """Row-normalised N x N form: A = phi(Q) phi(K)^T, out = A V / (A 1 + eps)."""
+TORCH_MAPS = {"elu1": lambda z: torch.nn.functional.elu(z, alpha=1.0) + 1.0,
+              "relu": torch.relu,
+              "softmax": lambda z: torch.softmax(z, dim=-1)}
+
+
+def brute_linear(Q, K, V, W, b, eps, causal=False, kind="elu1"):
+    """Row-normalised N x N form: A = phi(Q) phi(K)^T, out = A V / (A 1 + eps),
+    with the feature maps taken from torch (fp64)."""
     B, H, N, D = Q.shape
     out = np.empty((B, H, N, V.shape[3]))
     for bi in range(B):
@@ -66,7 +72,7 @@ def brute_linear(Q, K, V, W, b, eps, causal=False):
                 z = t @ Wh if Wh is not None else t
                 if b is not None:
                     z = z + torch.from_numpy(b[h])
-                return (torch.nn.functional.elu(z, alpha=1.0) + 1.0).numpy()
+                return TORCH_MAPS[kind](z).numpy()
             A = phi(Q[bi, h]) @ phi(K[bi, h]).T
             if causal:
                 A = A * np.tril(np.ones((N, N)))
@@ -364,6 +370,69 @@ def test_normwise_err():
     assert O.normwise_err(got, ref) == pytest.approx(0.1)
 
 
+# ---------------------------------------------------------------- relu and softmax feature maps
+
+def test_relu_map_values():
+    z = np.array([-2.0, -0.0, 0.0, 1e-300, 3.5])
+    np.testing.assert_array_equal(O.relu_map(z), [0.0, 0.0, 0.0, 1e-300, 3.5])
+    Q, _, _, W, b, _ = _small(40)
+    assert (O.feature_map(Q, W, b, "relu") >= 0.0).all()
+
+
+def test_softmax_map_hand_worked_and_invariants():
+    # softmax([0, ln 3]) = [1/4, 3/4]; rows sum to 1; adding a constant to a
+    # token's features changes nothing
+    np.testing.assert_allclose(O.softmax_map(np.array([[0.0, math.log(3.0)]])), [[0.25, 0.75]], rtol=1e-15)
+    Q, _, _, _, b, _ = _small(41, proj=False)
+    phi = O.feature_map(Q, None, b, "softmax")
+    np.testing.assert_allclose(phi.sum(-1), 1.0, rtol=1e-14)
+    shifted = O.feature_map(Q + 7.25, None, b, "softmax")
+    np.testing.assert_allclose(shifted, phi, rtol=1e-12)
+    assert (phi > 0).all()
+
+
+def test_softmax_map_matches_torch():
+    Q, _, _, W, b, _ = _small(42)
+    got = O.feature_map(Q, W, b, "softmax")
+    z = torch.from_numpy(Q) @ torch.from_numpy(W)[None] + torch.from_numpy(b)[None, :, None, :]
+    np.testing.assert_allclose(got, torch.softmax(z, dim=-1).numpy(), rtol=1e-13, atol=1e-16)
+
+
+@pytest.mark.parametrize("kind", ["relu", "softmax"])
+def test_other_maps_linear_and_causal_match_bruteforce(kind):
+    for seed, proj in ((43, False), (44, True)):
+        Q, K, V, W, b, _ = _small(seed, B=2, N=33, proj=proj)
+        KV, ksum = O.kv_reduce(K, V, W, b, kind)
+        got = O.apply(Q, W, b, KV, ksum, EPS, kind)
+        np.testing.assert_allclose(got, brute_linear(Q, K, V, W, b, EPS, kind=kind), rtol=1e-10, atol=1e-12)
+        got = O.causal_forward(Q, K, V, W, b, EPS, kind)
+        np.testing.assert_allclose(got, brute_linear(Q, K, V, W, b, EPS, causal=True, kind=kind),
+                                   rtol=1e-10, atol=1e-12)
+        assert np.allclose(O.hybrid_forward(Q, K, V, W, b, None, EPS, 0, kind), O.apply(Q, W, b, KV, ksum, EPS, kind))
+
+
+@pytest.mark.parametrize("kind", ["relu", "softmax"])
+def test_other_maps_last_causal_token_and_rows(kind):
+    Q, K, V, _, b, _ = _small(45, N=50, proj=False)
+    c = O.causal_forward(Q, K, V, None, b, EPS, kind)
+    KV, ksum = O.kv_reduce(K, V, None, b, kind)
+    nc = O.apply(Q, None, b, KV, ksum, EPS, kind)
+    np.testing.assert_allclose(c[:, :, -1], nc[:, :, -1], rtol=1e-11)
+    rows = [(0, 0, 0), (0, 1, 17), (0, 1, 49)]
+    np.testing.assert_allclose(O.causal_rows(Q, K, V, None, b, EPS, rows, kind),
+                               np.stack([c[r] for r in rows]), rtol=1e-11)
+    np.testing.assert_allclose(O.hybrid_rows(Q, K, V, None, b, None, EPS, 0, rows, kind),
+                               np.stack([nc[r] for r in rows]), rtol=1e-11)
+
+
+def test_relu_map_all_negative_keys_give_zero():
+    # every key feature negative -> phi(K) = 0 -> KV = 0, ksum = 0 -> out = 0 / (0 + eps) = 0
+    Q, K, V, _, _, _ = _small(46, proj=False)
+    KV, ksum = O.kv_reduce(-np.abs(K) - 0.1, V, None, None, "relu")
+    assert not KV.any() and not ksum.any()
+    assert not O.apply(Q, None, None, KV, ksum, EPS, "relu").any()
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_linear():
@@ -431,6 +500,27 @@ def _mut_causal_exclusive(Q, K, V, W, b, eps):
     return out
 
 
+def _mut_softmax_token_axis(z):
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max(axis=-2, keepdims=True))
+    return e / e.sum(axis=-2, keepdims=True)
+
+
+def _mut_relu_plus_one(z):
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0) + 1.0
+
+
+def _pins_softmax():
+    test_softmax_map_hand_worked_and_invariants()
+    test_softmax_map_matches_torch()
+    test_other_maps_linear_and_causal_match_bruteforce("softmax")
+
+
+def _pins_relu():
+    test_relu_map_values()
+    test_other_maps_linear_and_causal_match_bruteforce("relu")
+
+
 _orig_landmark = O.landmark_attn
 _orig_blend = O.blend
 
@@ -444,6 +534,8 @@ _orig_blend = O.blend
     ("landmark_indices", _mut_landmark_idx_offset, _pins_landmark),
     ("blend", _mut_blend_swapped, test_hybrid_hand_worked),
     ("causal_forward", _mut_causal_exclusive, _pins_causal),
+    ("softmax_map", _mut_softmax_token_axis, _pins_softmax),
+    ("relu_map", _mut_relu_plus_one, _pins_relu),
 ])
 def test_planted_mistake_is_caught(monkeypatch, attr, mutant, pins):
     monkeypatch.setattr(O, attr, mutant)
