@@ -6,12 +6,15 @@
  *     linear-time kernel branch with a small exact-softmax branch over
  *     landmark tokens, blended by a bounded weight; "Inputs worth setting":
  *     feature_dim F defaults to 256 and must be a multiple of 256.
- *   "NNT Define Linear Attention", "The inputs": feature map elu(x) + 1,
- *     eps = 1e-6 in the denominator, causal flag; "How it works":
- *     Q'(K'^T V) normalised by 1 / (Q' . sum(K') + eps).
+ *   "NNT Define Linear Attention", "The inputs": feature map elu(x) + 1
+ *     (also relu or softmax), eps = 1e-6 in the denominator, causal flag;
+ *     "How it works": Q'(K'^T V) normalised by 1 / (Q' . sum(K') + eps).
  *
- * Computed per (batch b, head h), with x a row of Q or K:
- *   phi(x)  = elu(x W_h + b_h) + 1           (W == NULL: elu(x + b_h) + 1, F = D)
+ * Computed per (batch b, head h), with x a row of Q or K and z = x W_h + b_h
+ * (W == NULL: z = x + b_h, F = D):
+ *   phi(x)  = elu(z) + 1                     (dims.fmap == TTR_FMAP_ELU1, the default)
+ *           = max(z, 0)                      (TTR_FMAP_RELU)
+ *           = exp(z) / sum_f exp(z_f)        (TTR_FMAP_SOFTMAX, over the F features)
  *   KV      = phi(K)^T V           [F, D]    ksum = sum_n phi(K)_n   [F]
  *   out_lin = phi(Q) KV / (phi(Q) . ksum + eps)
  *   idx_j   = floor(j N / L), j = 0..L-1     (strided landmarks from token 0)
@@ -40,6 +43,9 @@
  *   - Shape rules: B, H, N >= 1; D in {64, 128}; with W, F == 256; without W,
  *     F == D. fp32 IO needs D == 64. 0 <= L <= N. Ragged N (not a multiple of
  *     any tile size) is supported.
+ *   - The relu and softmax feature maps are those of the NNT linear attention,
+ *     applied to already projected features: they need W == NULL and no
+ *     landmark branch (L == 0); otherwise TTR_ERR_UNSUPPORTED.
  */
 #ifndef TTR_H
 #define TTR_H
@@ -65,13 +71,16 @@ typedef enum {
 
 typedef enum { TTR_FP32 = 0, TTR_BF16 = 1 } ttr_dtype;
 
+typedef enum { TTR_FMAP_ELU1 = 0, TTR_FMAP_RELU = 1, TTR_FMAP_SOFTMAX = 2 } ttr_fmap;
+
 /* Problem sizes. F is the feature dimension (256 with a projection W, D without). */
 typedef struct {
   int32_t B, H, N, D, F;
   int32_t dtype; /* ttr_dtype of the IO tensors */
+  int32_t fmap;  /* ttr_fmap; 0 (elu + 1) when zero-initialised */
 } ttr_dims;
 
-/* Feature map: phi = elu(X W_h + b_h) + 1 written as [B,H,N,F] in the IO dtype.
+/* Feature map: phi = map(X W_h + b_h) (map per dims.fmap) written as [B,H,N,F] in the IO dtype.
  * "Flux2TTRTrainer", "Inputs worth setting" (feature_dim);
  * "NNT Define Linear Attention", "The inputs" (elu(x) + 1).
  * X [B,H,N,D]; W [H,D,F] or NULL (identity, F == D); b [H,F] fp32 or NULL. */
@@ -106,7 +115,7 @@ ttr_status ttr_landmark_attn(ttr_dims d, const void* Q, const void* K, const voi
 ttr_status ttr_blend(ttr_dims d, const float* out_lin, const float* out_lm, const float* g,
                      void* out, void* stream);
 
-/* Causal elu+1 linear attention as a chunked prefix scan (chunk in {64,128,256};
+/* Causal linear attention as a chunked prefix scan (chunk in {64,128,256};
  * the chunk changes the schedule, not the result). Identity feature map only
  * (W must be NULL, F == D); b [H,D] fp32 or NULL.
  * out [B,H,N,D] in the IO dtype. ws: at least ttr_workspace_bytes(d, 0, 1, chunk) bytes.

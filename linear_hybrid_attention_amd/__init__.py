@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "TTRError", "load_library", "library_path", "exported_symbols", "Dims",
+    "TTRError", "load_library", "library_path", "exported_symbols", "Dims", "FMAPS",
     "feature_map", "kv_reduce", "apply", "landmark_attn", "blend", "causal_scan",
     "hybrid_forward", "workspace_bytes", "status_string", "version",
     "TTR_FP32", "TTR_BF16",
@@ -48,7 +48,18 @@ class TTRError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("D", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("D", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("fmap", ctypes.c_int32)]
+
+
+# feature maps (ttr_fmap): elu(x) + 1, relu, softmax over the features
+FMAPS = {"elu1": 0, "relu": 1, "softmax": 2}
+
+
+def _fmap(name: str) -> int:
+    if name not in FMAPS:
+        raise ValueError(f"feature map must be one of {sorted(FMAPS)}")
+    return FMAPS[name]
 
 
 _P = ctypes.c_void_p
@@ -142,11 +153,11 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _dims(X: torch.Tensor, F: int) -> Dims:
+def _dims(X: torch.Tensor, F: int, fmap: str = "elu1") -> Dims:
     if X.dim() != 4:
         raise ValueError("Q/K/V must be [B, H, N, D]")
     B, H, N, D = X.shape
-    return Dims(B, H, N, D, F, _io_dtype(X))
+    return Dims(B, H, N, D, F, _io_dtype(X), _fmap(fmap))
 
 
 def _feat_dim(X: torch.Tensor, W: Optional[torch.Tensor]) -> int:
@@ -154,8 +165,8 @@ def _feat_dim(X: torch.Tensor, W: Optional[torch.Tensor]) -> int:
 
 
 def workspace_bytes(B: int, H: int, N: int, D: int, F: int, dtype: int, L: int = 0, causal: bool = False,
-                    chunk: int = 0) -> int:
-    return int(load_library().ttr_workspace_bytes(Dims(B, H, N, D, F, dtype), L, int(causal), chunk))
+                    chunk: int = 0, fmap: str = "elu1") -> int:
+    return int(load_library().ttr_workspace_bytes(Dims(B, H, N, D, F, dtype, _fmap(fmap)), L, int(causal), chunk))
 
 
 def _workspace(d: Dims, nbytes: int, like: torch.Tensor, ws: Optional[torch.Tensor]):
@@ -167,11 +178,11 @@ def _workspace(d: Dims, nbytes: int, like: torch.Tensor, ws: Optional[torch.Tens
 
 
 def feature_map(X: torch.Tensor, W: Optional[torch.Tensor] = None, b: Optional[torch.Tensor] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """phi(X) = elu(X W_h + b_h) + 1, [B,H,N,F] in X's dtype (ttr_feature_map)."""
+                out: Optional[torch.Tensor] = None, fmap: str = "elu1") -> torch.Tensor:
+    """phi(X) = map(X W_h + b_h) (elu + 1, relu or softmax), [B,H,N,F] in X's dtype (ttr_feature_map)."""
     lib = load_library()
     F = _feat_dim(X, W)
-    d = _dims(X, F)
+    d = _dims(X, F, fmap)
     if out is None:
         out = torch.empty((d.B, d.H, d.N, F), dtype=X.dtype, device=X.device)
     st = lib.ttr_feature_map(d, _dev(X, "X"), _dev(W, "W", X.dtype), _dev(b, "b", torch.float32),
@@ -181,11 +192,12 @@ def feature_map(X: torch.Tensor, W: Optional[torch.Tensor] = None, b: Optional[t
 
 
 def kv_reduce(K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor] = None,
-              b: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+              b: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+              fmap: str = "elu1") -> Tuple[torch.Tensor, torch.Tensor]:
     """KV = phi(K)^T V [B,H,F,D] and ksum [B,H,F], both fp32 (ttr_kv_reduce)."""
     lib = load_library()
     F = _feat_dim(K, W)
-    d = _dims(K, F)
+    d = _dims(K, F, fmap)
     KV = torch.empty((d.B, d.H, F, d.D), dtype=torch.float32, device=K.device)
     ksum = torch.empty((d.B, d.H, F), dtype=torch.float32, device=K.device)
     need = lib.ttr_workspace_bytes(d, 0, 0, 0) - KV.numel() * 4 - ksum.numel() * 4
@@ -198,10 +210,10 @@ def kv_reduce(K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor] = None
 
 
 def apply(Q: torch.Tensor, W: Optional[torch.Tensor], b: Optional[torch.Tensor], KV: torch.Tensor,
-          ksum: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+          ksum: torch.Tensor, eps: float = 1e-6, fmap: str = "elu1") -> torch.Tensor:
     """out_lin = phi(Q) KV / (phi(Q) . ksum + eps), fp32 [B,H,N,D] (ttr_apply)."""
     lib = load_library()
-    d = _dims(Q, _feat_dim(Q, W))
+    d = _dims(Q, _feat_dim(Q, W), fmap)
     out = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
     st = lib.ttr_apply(d, _dev(Q, "Q"), _dev(W, "W", Q.dtype), _dev(b, "b", torch.float32),
                        _dev(KV, "KV", torch.float32), _dev(ksum, "ksum", torch.float32), float(eps),
@@ -225,7 +237,7 @@ def blend(out_lin: torch.Tensor, out_lm: torch.Tensor, g: torch.Tensor, dtype=to
     """out = sigmoid(g_h) out_lin + (1 - sigmoid(g_h)) out_lm in `dtype` (ttr_blend)."""
     lib = load_library()
     B, H, N, D = out_lin.shape
-    d = Dims(B, H, N, D, D, _IO[dtype])
+    d = Dims(B, H, N, D, D, _IO[dtype], 0)
     out = torch.empty(out_lin.shape, dtype=dtype, device=out_lin.device)
     st = lib.ttr_blend(d, _dev(out_lin, "out_lin", torch.float32), _dev(out_lm, "out_lm", torch.float32),
                        _dev(g, "g", torch.float32), out.data_ptr(), _stream(out_lin))
@@ -235,10 +247,10 @@ def blend(out_lin: torch.Tensor, out_lm: torch.Tensor, g: torch.Tensor, dtype=to
 
 def causal_scan(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, b: Optional[torch.Tensor] = None,
                 eps: float = 1e-6, chunk: int = 128, out: Optional[torch.Tensor] = None,
-                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Causal elu+1 linear attention, chunked prefix scan, [B,H,N,D] in Q's dtype (ttr_causal_scan)."""
+                ws: Optional[torch.Tensor] = None, fmap: str = "elu1") -> torch.Tensor:
+    """Causal linear attention, chunked prefix scan, [B,H,N,D] in Q's dtype (ttr_causal_scan)."""
     lib = load_library()
-    d = _dims(Q, Q.shape[3])
+    d = _dims(Q, Q.shape[3], fmap)
     if out is None:
         out = torch.empty_like(Q)
     need = lib.ttr_workspace_bytes(d, 0, 1, int(chunk))
@@ -253,10 +265,10 @@ def causal_scan(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, b: Optional[t
 def hybrid_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor],
                    b: Optional[torch.Tensor], g: Optional[torch.Tensor], eps: float = 1e-6, L: int = 0,
                    causal: bool = False, out: Optional[torch.Tensor] = None,
-                   ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   ws: Optional[torch.Tensor] = None, fmap: str = "elu1") -> torch.Tensor:
     """The whole TTR forward, [B,H,N,D] in Q's dtype (ttr_hybrid_forward)."""
     lib = load_library()
-    d = _dims(Q, _feat_dim(Q, W))
+    d = _dims(Q, _feat_dim(Q, W), fmap)
     if out is None:
         out = torch.empty_like(Q)
     need = lib.ttr_workspace_bytes(d, int(L), int(causal), 0)

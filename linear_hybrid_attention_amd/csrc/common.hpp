@@ -59,6 +59,40 @@ __device__ __forceinline__ float elu1(float x) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Feature maps of the linear branch ("NNT Define Linear Attention", section
+// "The inputs": elu + 1 by default, also relu or softmax). The softmax runs
+// over each token's features: phi_f = exp(z_f - m) / sum_f' exp(z_f' - m), with
+// the token's feature maximum m and inverse sum inv_s found by the caller.
+enum FeatureMap { kElu1 = 0, kRelu = 1, kSoftmax = 2 };
+
+// Softmax statistics of one token whose features are spread over a group of
+// lanes: each lane holds NV of them in z, and the group is the lanes reached
+// by xor with the bits of XMASK (e.g. 7: 8 consecutive lanes; 32: the two
+// halves of the wave). Every lane of the group must be active. Returns the
+// group's maximum m and 1 / sum exp(z - m).
+template <int NV, int XMASK>
+__device__ __forceinline__ void softmax_stats(const float* z, float& m, float& inv_s) {
+  m = z[0];
+#pragma unroll
+  for (int j = 1; j < NV; ++j) m = fmaxf(m, z[j]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1)
+    if (XMASK & o) m = fmaxf(m, __shfl_xor(m, o));
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) s += __builtin_amdgcn_exp2f((z[j] - m) * kLog2e);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1)
+    if (XMASK & o) s += __shfl_xor(s, o);
+  inv_s = 1.f / s;
+}
+template <int MAP>
+__device__ __forceinline__ float phi_of(float z, float m, float inv_s) {
+  if constexpr (MAP == kElu1) return elu1(z);
+  else if constexpr (MAP == kRelu) return fmaxf(z, 0.f);
+  else return __builtin_amdgcn_exp2f((z - m) * kLog2e) * inv_s;
+}
+
 // ---------------------------------------------------------------- fragments
 // Eight k-consecutive operand values of one lane, in the element type T of
 // the MFMA (bf16: one 32x32x16 instruction; fp32: eight 32x32x2 instructions).

@@ -1,4 +1,4 @@
-// Causal elu+1 linear attention as a chunked prefix scan.
+// Causal linear attention (elu + 1, relu or softmax feature map) as a chunked prefix scan.
 // "NNT Define Linear Attention", section "The inputs" (causal: a token attends
 // only to earlier tokens; elu(x) + 1 map; eps) and section "How it works".
 //
@@ -59,12 +59,13 @@ struct CausalShape {
 // Stage one chunk: phi(K) rows (if ROWS), phi(K)^T and V^T (tokens in kperm
 // order). Tokens at or past N are zero. Consecutive threads read consecutive
 // 16-byte pieces of one row.
-template <typename T, int D, int C, bool ROWS>
+template <typename T, int D, int C, bool ROWS, int MAP>
 __device__ __forceinline__ void stage_chunk(const T* K, const T* V, const float* bias, int c0, int N, T* phiK,
                                             T* phiKt, T* Vt, int tid) {
   using S = CausalShape<T, D, C>;
   using KR = typename S::KR;
   using TR = typename S::TR;
+  static_assert(MAP != kSoftmax || (C / 2) * (D / 8) % 256 == 0, "every lane runs every round (row shuffles)");
   for (int u = tid; u < (C / 2) * (D / 8); u += 256) {
     const int d0 = (u % (D / 8)) * 8, tl = 2 * (u / (D / 8)), t = c0 + tl;
     const bool ok0 = t < N, ok1 = t + 1 < N;
@@ -73,11 +74,21 @@ __device__ __forceinline__ void stage_chunk(const T* K, const T* V, const float*
     const Vec8<T> v0 = ok0 ? ld8(V + (size_t)t * D + d0) : zero8<T>();
     const Vec8<T> v1 = ok1 ? ld8(V + (size_t)(t + 1) * D + d0) : zero8<T>();
     Vec8<T> p0, p1;
+    float z0[8], z1[8], m0 = 0.f, i0 = 1.f, m1 = 0.f, i1 = 1.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float bj = bias ? bias[d0 + j] : 0.f;
-      p0.v[j] = from_f32<T>(ok0 ? elu1(to_f32<T>(k0.v[j]) + bj) : 0.f);
-      p1.v[j] = from_f32<T>(ok1 ? elu1(to_f32<T>(k1.v[j]) + bj) : 0.f);
+      z0[j] = to_f32<T>(k0.v[j]) + bj;
+      z1[j] = to_f32<T>(k1.v[j]) + bj;
+    }
+    if constexpr (MAP == kSoftmax) {  // a row's D / 8 pieces sit in D / 8 consecutive lanes
+      softmax_stats<8, D / 8 - 1>(z0, m0, i0);
+      softmax_stats<8, D / 8 - 1>(z1, m1, i1);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p0.v[j] = from_f32<T>(ok0 ? phi_of<MAP>(z0[j], m0, i0) : 0.f);
+      p1.v[j] = from_f32<T>(ok1 ? phi_of<MAP>(z1[j], m1, i1) : 0.f);
     }
     if constexpr (ROWS) {
       st8(phiK + tl * KR::stride + d0, p0);
@@ -135,7 +146,7 @@ __device__ __forceinline__ void write_state(const f32x16* P, const float* zr, T*
   }
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, int MAP>
 __global__ __launch_bounds__(256, 1) void causal_segsum_kernel(CausalArgs a) {
   using S = CausalShape<T, D, C>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::seg_bytes];
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void causal_segsum_kernel(CausalArgs a) {
   for (int i = 0; i < S::NTPW; ++i) { P[i] = f32x16{}; zr[i] = 0.f; }
   for (int ch = cbeg; ch < cend; ++ch) {
     __syncthreads();
-    stage_chunk<T, D, C, false>(K, V, bias, ch * C, N, nullptr, phiKt, Vt, tid);
+    stage_chunk<T, D, C, false, MAP>(K, V, bias, ch * C, N, nullptr, phiKt, Vt, tid);
     __syncthreads();
     state_update<T, D, C>(P, zr, phiKt, Vt, w, lane);
   }
@@ -171,7 +182,7 @@ __global__ __launch_bounds__(256, 1) void causal_segsum_kernel(CausalArgs a) {
   }
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, int MAP>
 __global__ __launch_bounds__(256, 1) void causal_scan_kernel(CausalArgs a) {
   using S = CausalShape<T, D, C>;
   using KR = typename S::KR;
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void causal_scan_kernel(CausalArgs a) {
   for (int ch = cbeg; ch < cend; ++ch) {
     const int c0 = ch * C;
     __syncthreads();  // state written; previous chunk fully consumed
-    stage_chunk<T, D, C, true>(K, V, bias, c0, N, phiK, phiKt, Vt, tid);
+    stage_chunk<T, D, C, true, MAP>(K, V, bias, c0, N, phiK, phiKt, Vt, tid);
     __syncthreads();
 
     for (int i = 0; i < (NB + 3) / 4; ++i) {
@@ -227,15 +238,20 @@ __global__ __launch_bounds__(256, 1) void causal_scan_kernel(CausalArgs a) {
       const bool ok = q < N;
       Frag<T> qf[D / 16];
       float den = 0.f;
+      float zq[D / 16][8], m = 0.f, inv = 1.f;
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
         const Vec8<T> raw = ok ? ld8(Q + (size_t)q * D + kb * 16 + 8 * g) : zero8<T>();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zq[kb][j] = to_f32<T>(raw.v[j]) + (bias ? bias[kb * 16 + 8 * g + j] : 0.f);
+      }
+      // the query's features: half in this lane, half in lane ^ 32
+      if constexpr (MAP == kSoftmax) softmax_stats<D / 2, 32>(&zq[0][0], m, inv);
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int f = kb * 16 + 8 * g + j;
-          v[j] = ok ? elu1(to_f32<T>(raw.v[j]) + (bias ? bias[f] : 0.f)) : 0.f;
-        }
+        for (int j = 0; j < 8; ++j) v[j] = ok ? phi_of<MAP>(zq[kb][j], m, inv) : 0.f;
         qf[kb] = to_frag<T>(v);
         float vr[8];
         frag_to_f32(qf[kb], vr);  // the operand values the products see
@@ -315,19 +331,33 @@ size_t causal_workspace_bytes(const Problem& p, int chunk) {
   return causal_seg_bytes(p, chunk) + (causal2_supported(p, chunk) ? CAUSAL2_SINK_BYTES : 0);
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, int MAP>
 static hipError_t launch_causal_t(const CausalArgs& a, int B, hipStream_t s, StageTimer* t) {
   const dim3 grid(a.nseg, B * a.H), block(256);
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((causal_segsum_kernel<T, D, C>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((causal_segsum_kernel<T, D, C, MAP>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     t->mark();
   }
-  hipLaunchKernelGGL((causal_scan_kernel<T, D, C>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((causal_scan_kernel<T, D, C, MAP>), grid, block, 0, s, a);
   const hipError_t e = hipGetLastError();
   t->mark();
   return e;
+}
+
+// bf16 with D = 64 runs the streamed kernels of k_causal2.hip; these cover
+// fp32 (D = 64) and bf16 with D = 128.
+template <int MAP>
+static hipError_t launch_causal_m(const Problem& p, const CausalArgs& a, int chunk, hipStream_t s, StageTimer* t) {
+  if (p.dtype == 1 && p.D == 128) {
+    if (chunk == 64) return launch_causal_t<uint16_t, 128, 64, MAP>(a, p.B, s, t);
+    if (chunk == 128) return launch_causal_t<uint16_t, 128, 128, MAP>(a, p.B, s, t);
+  } else if (p.dtype == 0 && p.D == 64) {
+    if (chunk == 64) return launch_causal_t<float, 64, 64, MAP>(a, p.B, s, t);
+    if (chunk == 128) return launch_causal_t<float, 64, 128, MAP>(a, p.B, s, t);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_causal(const Problem& p, const void* Q, const void* K, const void* V, const float* bias,
@@ -343,18 +373,9 @@ hipError_t launch_causal(const Problem& p, const void* Q, const void* K, const v
   causal_plan(p, chunk, &a.nseg, &a.cps);
   a.seg = static_cast<float*>(ws);
   a.out = out;
-  if (p.dtype == 1 && p.D == 64) {
-    if (chunk == 64) return launch_causal_t<uint16_t, 64, 64>(a, p.B, s, t);
-    if (chunk == 128) return launch_causal_t<uint16_t, 64, 128>(a, p.B, s, t);
-    if (chunk == 256) return launch_causal_t<uint16_t, 64, 256>(a, p.B, s, t);
-  } else if (p.dtype == 1 && p.D == 128) {
-    if (chunk == 64) return launch_causal_t<uint16_t, 128, 64>(a, p.B, s, t);
-    if (chunk == 128) return launch_causal_t<uint16_t, 128, 128>(a, p.B, s, t);
-  } else if (p.dtype == 0 && p.D == 64) {
-    if (chunk == 64) return launch_causal_t<float, 64, 64>(a, p.B, s, t);
-    if (chunk == 128) return launch_causal_t<float, 64, 128>(a, p.B, s, t);
-  }
-  return hipErrorInvalidValue;
+  if (p.fmap == kRelu) return launch_causal_m<kRelu>(p, a, chunk, s, t);
+  if (p.fmap == kSoftmax) return launch_causal_m<kSoftmax>(p, a, chunk, s, t);
+  return launch_causal_m<kElu1>(p, a, chunk, s, t);
 }
 
 }  // namespace ttr

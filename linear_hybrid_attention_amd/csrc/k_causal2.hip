@@ -57,7 +57,7 @@ struct Causal2Shape {
   static constexpr int WG_PER_CU = (160 * 1024) / bytes >= 2 ? 2 : 1;
 };
 
-template <int C, bool WALK>
+template <int C, bool WALK, int MAP>
 __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causal2_kernel(Causal2Args a) {
   using S = Causal2Shape<C, WALK>;
   constexpr int D = 64, NB = S::NB, QB = S::QB, PER_T = S::PER_T;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
   // stored, so they contribute nothing.
   u32x4 stg[PER_T];
   auto load_stg = [&](int ch) {
-    const int c0 = ch * C;
+    [[maybe_unused]] const int c0 = ch * C;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const bool isv = i >= PER_T / 2;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
     }
   };
   auto store_stg = [&](int ch) {
-    const int c0 = ch * C;
+    [[maybe_unused]] const int c0 = ch * C;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const bool isv = i >= PER_T / 2;
@@ -130,8 +130,12 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
       } else {
         const float keep = c0 + row < N ? 1.f : 0.f;
         Vec8<uint16_t> v = __builtin_bit_cast(Vec8<uint16_t>, stg[i]);
+        float z[8], m = 0.f, inv = 1.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v.v[j] = f2bf(elu1(bf2f(v.v[j]) + kb[j]) * keep);
+        for (int j = 0; j < 8; ++j) z[j] = bf2f(v.v[j]) + kb[j];
+        if constexpr (MAP == kSoftmax) softmax_stats<8, 7>(z, m, inv);  // a row's 8 pieces: 8 consecutive lanes
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.v[j] = f2bf(phi_of<MAP>(z[j], m, inv) * keep);
         *reinterpret_cast<u32x4*>(ktt + toff<D, kTrRead>(row, p * 8)) = __builtin_bit_cast(u32x4, v);
         if constexpr (WALK) *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = __builtin_bit_cast(u32x4, v);
       }
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
   if constexpr (WALK) store_out(-1);  // sink only (stands in for the previous chunk's stores)
 
   for (int ch = cbeg; ch < cend; ++ch) {
-    const int c0 = ch * C;
+    [[maybe_unused]] const int c0 = ch * C;
     barrier_lds();  // chunk ch (phi(K), V), P^T and z are in LDS
 
     // phi(Q) fragments of this wave's query blocks and their inter-chunk
@@ -206,12 +210,20 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
 #pragma unroll
       for (int i = 0; i < QB; ++i) {
         den0[i] = 0.f;
+        float zq[D / 16][8], m = 0.f, inv = 1.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < D / 16; ++kb2) {
+          frag_to_f32(qraw[i][kb2], zq[kb2]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) zq[kb2][j] += bS[kb2 * 16 + 8 * g + j];
+        }
+        // the query's features: half in this lane, half in lane ^ 32
+        if constexpr (MAP == kSoftmax) softmax_stats<D / 2, 32>(&zq[0][0], m, inv);
 #pragma unroll
         for (int kb2 = 0; kb2 < D / 16; ++kb2) {
           float v[8];
-          frag_to_f32(qraw[i][kb2], v);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = elu1(v[j] + bS[kb2 * 16 + 8 * g + j]);
+          for (int j = 0; j < 8; ++j) v[j] = phi_of<MAP>(zq[kb2][j], m, inv);
           qf[i][kb2] = to_frag<uint16_t>(v);
 #pragma unroll
           for (int j = 0; j < 8; ++j) den0[i] += v[j] * zS[kb2 * 16 + 8 * g + j];
@@ -325,16 +337,16 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
   }
 }
 
-template <int C>
+template <int C, int MAP>
 static hipError_t launch_causal2_t(const Causal2Args& a, int B, hipStream_t s, StageTimer* t) {
   const dim3 grid(a.nseg, B * a.H), block(256);
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((causal2_kernel<C, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((causal2_kernel<C, false, MAP>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     t->mark();
   }
-  hipLaunchKernelGGL((causal2_kernel<C, true>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((causal2_kernel<C, true, MAP>), grid, block, 0, s, a);
   const hipError_t e = hipGetLastError();
   t->mark();
   return e;
@@ -342,6 +354,14 @@ static hipError_t launch_causal2_t(const Causal2Args& a, int B, hipStream_t s, S
 
 bool causal2_supported(const Problem& p, int chunk) {
   return p.dtype == 1 && p.D == 64 && (chunk == 64 || chunk == 128 || chunk == 256);
+}
+
+template <int MAP>
+static hipError_t launch_causal2_m(const Causal2Args& a, int B, int chunk, hipStream_t s, StageTimer* t) {
+  if (chunk == 64) return launch_causal2_t<64, MAP>(a, B, s, t);
+  if (chunk == 128) return launch_causal2_t<128, MAP>(a, B, s, t);
+  if (chunk == 256) return launch_causal2_t<256, MAP>(a, B, s, t);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_causal2(const Problem& p, const void* Q, const void* K, const void* V, const float* bias,
@@ -359,10 +379,9 @@ hipError_t launch_causal2(const Problem& p, const void* Q, const void* K, const 
   a.sink = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + causal_seg_bytes(p, chunk));
   static_assert(CAUSAL2_SINK_BYTES >= 2 * 4 * 64 * 16, "one 16-byte slot per store of a wave (QB <= 2)");
   a.out = static_cast<uint16_t*>(out);
-  if (chunk == 64) return launch_causal2_t<64>(a, p.B, s, t);
-  if (chunk == 128) return launch_causal2_t<128>(a, p.B, s, t);
-  if (chunk == 256) return launch_causal2_t<256>(a, p.B, s, t);
-  return hipErrorInvalidValue;
+  if (p.fmap == kRelu) return launch_causal2_m<kRelu>(a, p.B, chunk, s, t);
+  if (p.fmap == kSoftmax) return launch_causal2_m<kSoftmax>(a, p.B, chunk, s, t);
+  return launch_causal2_m<kElu1>(a, p.B, chunk, s, t);
 }
 
 }  // namespace ttr

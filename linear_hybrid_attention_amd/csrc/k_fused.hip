@@ -41,7 +41,7 @@ struct FusedArgs {
   uint16_t* out;
 };
 
-template <int D, int F>
+template <int D, int F, int MAP>
 __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   constexpr int CH = 64 * D;  // elements per chunk (every chunk kind)
   constexpr int NFC = F / 64;
@@ -115,6 +115,22 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   for (int db = 0; db < D / 32; ++db) num[db] = f32x16{};
   float den = 0.f;
 
+  // softmax map (identity projection, F == D): the token's feature maximum
+  // and inverse sum, from its Q row (half in this lane, half in lane ^ 32)
+  // plus the bias (stored in MFMA row order: feature f at kperm(f))
+  float qm = 0.f, qinv = 1.f;
+  if constexpr (MAP == kSoftmax) {
+    barrier_lds();  // bias in LDS
+    float z[D / 2];
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      frag_to_f32(qf[kb], z + 8 * kb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z[8 * kb + j] += vecS[kperm(kb * 16 + 8 * g + j)];
+    }
+    softmax_stats<D / 2, 32>(z, qm, qinv);
+  }
+
   // ---- linear branch: per 64 features, a W^T chunk (even) then a KV^T chunk (odd)
 #pragma clang loop unroll(disable)
   for (int fc = 0; fc < NFC; ++fc) {
@@ -142,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
         const float* kp = vecS + F + fc * 64 + fb * 32 + 8 * g;
         float p[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = elu1(acc[fb][r]);
+        for (int r = 0; r < 16; ++r) p[r] = phi_of<MAP>(acc[fb][r], qm, qinv);
 #pragma unroll
         for (int r = 0; r < 8; ++r) den += p[r] * kp[r] + p[8 + r] * kp[16 + r];
         pb[2 * fb] = to_frag<uint16_t>(p);
@@ -265,9 +281,9 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   }
 }
 
-template <int D, int F>
+template <int D, int F, int MAP>
 static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((fused_query_kernel<D, F>), dim3(a.nwg), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fused_query_kernel<D, F, MAP>), dim3(a.nwg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -288,8 +304,18 @@ hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& 
   a.nwg = a.ntiles * p.B * p.H;
   a.out = static_cast<uint16_t*>(out);
   if (p.dtype != 1) return hipErrorInvalidValue;
-  if (p.D == 128) return p.proj ? launch_fused_t<128, 256>(a, s) : launch_fused_t<128, 128>(a, s);
-  if (p.D == 64) return p.proj ? launch_fused_t<64, 256>(a, s) : launch_fused_t<64, 64>(a, s);
+  if (p.D == 128) {
+    if (p.proj) return launch_fused_t<128, 256, kElu1>(a, s);
+    if (p.fmap == kRelu) return launch_fused_t<128, 128, kRelu>(a, s);
+    if (p.fmap == kSoftmax) return launch_fused_t<128, 128, kSoftmax>(a, s);
+    return launch_fused_t<128, 128, kElu1>(a, s);
+  }
+  if (p.D == 64) {
+    if (p.proj) return launch_fused_t<64, 256, kElu1>(a, s);
+    if (p.fmap == kRelu) return launch_fused_t<64, 64, kRelu>(a, s);
+    if (p.fmap == kSoftmax) return launch_fused_t<64, 64, kSoftmax>(a, s);
+    return launch_fused_t<64, 64, kElu1>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -64,7 +64,7 @@ __device__ __forceinline__ void stage_wt(T* Wt, const T* W, int tid) {
   }
 }
 
-template <typename T, int D, int F, bool PROJ, int MODE, typename OutT>
+template <typename T, int D, int F, bool PROJ, int MODE, typename OutT, int MAP>
 __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
   using S = HybridSmem<T, D, F, MODE>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
@@ -112,6 +112,21 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
     }
     __syncthreads();
 
+    // softmax map (identity projection, F == D): the token's feature maximum
+    // and inverse sum, from its Q row (half in this lane, half in lane ^ 32)
+    float qm = 0.f, qinv = 1.f;
+    if constexpr (MAP == kSoftmax) {
+      static_assert(!PROJ, "the softmax map takes already projected features");
+      float z[D / 2];
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        frag_to_f32(qf[kb], z + 8 * kb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[8 * kb + j] += biasP[kperm(kb * 16 + 8 * g + j)];
+      }
+      softmax_stats<D / 2, 32>(z, qm, qinv);
+    }
+
     f32x16 num[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) num[db] = f32x16{};
@@ -130,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
         mma(acc, ld_frag<T>(Wt + (fc * 32 + c) * WR::stride + kb * 16 + 8 * g), qf[kb]);
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = elu1(acc[r]);
+      for (int r = 0; r < 16; ++r) p[r] = phi_of<MAP>(acc[r], qm, qinv);
 
       if constexpr ((MODE & M_PHI) != 0) {
         if (tok_ok) {
@@ -259,25 +274,27 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
   }
 }
 
-template <typename T, int D, bool PROJ>
+template <typename T, int D, bool PROJ, int MAP>
 static hipError_t launch_hybrid_t(int mode, bool out_io, const HybridArgs& a, int B, hipStream_t s) {
   constexpr int F = PROJ ? 256 : D;
   const dim3 grid((a.N + 127) / 128, B * a.H), block(256);
   switch (mode) {
     case M_PHI:
-      hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_PHI, T>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_PHI, T, MAP>), grid, block, 0, s, a);
       break;
     case M_LIN:
       if (out_io)
-        hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_LIN, T>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_LIN, T, MAP>), grid, block, 0, s, a);
       else
-        hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_LIN, float>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_LIN, float, MAP>), grid, block, 0, s, a);
       break;
     case M_LM:
-      hipLaunchKernelGGL((hybrid_kernel<T, D, D, false, M_LM, float>), grid, block, 0, s, a);
+      if constexpr (MAP != kElu1) return hipErrorInvalidValue;  // the landmark branch has no feature map
+      hipLaunchKernelGGL((hybrid_kernel<T, D, D, false, M_LM, float, kElu1>), grid, block, 0, s, a);
       break;
     case M_LIN | M_LM:
-      hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_LIN | M_LM, T>), grid, block, 0, s, a);
+      if constexpr (MAP != kElu1) return hipErrorInvalidValue;  // landmarks belong to the elu+1 layer
+      hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_LIN | M_LM, T, kElu1>), grid, block, 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;
@@ -285,15 +302,20 @@ static hipError_t launch_hybrid_t(int mode, bool out_io, const HybridArgs& a, in
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static hipError_t launch_hybrid_d(const Problem& p, int mode, bool out_io, const HybridArgs& a, hipStream_t s) {
+  if (p.proj || mode == M_LM) return launch_hybrid_t<T, D, true, kElu1>(mode, out_io, a, p.B, s);
+  if (p.fmap == kRelu) return launch_hybrid_t<T, D, false, kRelu>(mode, out_io, a, p.B, s);
+  if (p.fmap == kSoftmax) return launch_hybrid_t<T, D, false, kSoftmax>(mode, out_io, a, p.B, s);
+  return launch_hybrid_t<T, D, false, kElu1>(mode, out_io, a, p.B, s);
+}
+
 hipError_t launch_hybrid(const Problem& p, int mode, bool out_io, const HybridArgs& a, hipStream_t s) {
   if (p.dtype == 1) {
-    if (p.D == 64) return p.proj ? launch_hybrid_t<uint16_t, 64, true>(mode, out_io, a, p.B, s)
-                                 : launch_hybrid_t<uint16_t, 64, false>(mode, out_io, a, p.B, s);
-    if (p.D == 128) return p.proj ? launch_hybrid_t<uint16_t, 128, true>(mode, out_io, a, p.B, s)
-                                  : launch_hybrid_t<uint16_t, 128, false>(mode, out_io, a, p.B, s);
+    if (p.D == 64) return launch_hybrid_d<uint16_t, 64>(p, mode, out_io, a, s);
+    if (p.D == 128) return launch_hybrid_d<uint16_t, 128>(p, mode, out_io, a, s);
   } else if (p.dtype == 0 && p.D == 64) {
-    return p.proj ? launch_hybrid_t<float, 64, true>(mode, out_io, a, p.B, s)
-                  : launch_hybrid_t<float, 64, false>(mode, out_io, a, p.B, s);
+    return launch_hybrid_d<float, 64>(p, mode, out_io, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -44,7 +44,7 @@ struct KvShape {
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int D, int F, bool PROJ>
+template <typename T, int D, int F, bool PROJ, int MAP>
 __global__ __launch_bounds__(256, 1) void kv_partial_kernel(KvArgs a) {
   using S = KvShape<T, D, F>;
   constexpr int NFS = S::NFS, NTW = S::NTW, STEP = S::STEP;
@@ -91,6 +91,16 @@ __global__ __launch_bounds__(256, 1) void kv_partial_kernel(KvArgs a) {
   float bcol[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) bcol[cb] = a.bias ? a.bias[(size_t)h * F + f0 + cb * 32 + c] : 0.f;
+  // softmax map (identity projection, F == D): the bias of this lane's half
+  // of a key row's features
+  float brow[MAP == kSoftmax ? D / 2 : 1];
+  if constexpr (MAP == kSoftmax) {
+    static_assert(!PROJ, "the softmax map takes already projected features");
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) brow[8 * kb + j] = a.bias ? a.bias[(size_t)h * F + kb * 16 + 8 * g + j] : 0.f;
+  }
 
   const T* K = static_cast<const T*>(a.K) + (size_t)bh * N * D;
   const T* V = static_cast<const T*>(a.V) + (size_t)bh * N * D;
@@ -121,6 +131,19 @@ __global__ __launch_bounds__(256, 1) void kv_partial_kernel(KvArgs a) {
     for (int kb = 0; kb < D / 16; ++kb)
       kf[kb] = t0 + c < t_end ? ld_frag<T>(K + (size_t)(t0 + c) * D + kb * 16 + 8 * g) : zero_frag<T>();
 
+    // softmax: the feature maximum and inverse sum of this lane's key row
+    // (token t0 + c; half its features here, half in lane ^ 32)
+    float km = 0.f, kinv = 1.f;
+    if constexpr (MAP == kSoftmax) {
+      float z[D / 2];
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        frag_to_f32(kf[kb], z + 8 * kb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[8 * kb + j] += brow[8 * kb + j];
+      }
+      softmax_stats<D / 2, 32>(z, km, kinv);
+    }
     Frag<T> pa[2][2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -132,7 +155,11 @@ __global__ __launch_bounds__(256, 1) void kv_partial_kernel(KvArgs a) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = t0 + crow(lane, r) < t_end ? elu1(acc[r]) : 0.f;
+        // row r of the C tile is token t0 + crow(lane, r), whose statistics
+        // lane crow(lane, r) holds
+        const float mr = MAP == kSoftmax ? __shfl(km, crow(lane, r)) : 0.f;
+        const float ir = MAP == kSoftmax ? __shfl(kinv, crow(lane, r)) : 1.f;
+        p[r] = t0 + crow(lane, r) < t_end ? phi_of<MAP>(acc[r], mr, ir) : 0.f;
         ks[cb] += p[r];
       }
       pa[cb][0] = to_frag<T>(p);
@@ -253,9 +280,17 @@ size_t kv_workspace_bytes(const Problem& p) {
   return (size_t)p.B * p.H * ns * (size_t)(p.F * p.D + p.F) * sizeof(float);
 }
 
-template <typename T, int D, int F, bool PROJ>
+template <typename T, int D, int F, bool PROJ, int MAP>
 static void launch_kv_t(const KvArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((kv_partial_kernel<T, D, F, PROJ>), dim3(a.nsplit, B * a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((kv_partial_kernel<T, D, F, PROJ, MAP>), dim3(a.nsplit, B * a.H), dim3(256), 0, s, a);
+}
+
+template <typename T, int D>
+static void launch_kv_d(const Problem& p, const KvArgs& a, hipStream_t s) {
+  if (p.proj) launch_kv_t<T, D, 256, true, kElu1>(a, p.B, s);
+  else if (p.fmap == kRelu) launch_kv_t<T, D, D, false, kRelu>(a, p.B, s);
+  else if (p.fmap == kSoftmax) launch_kv_t<T, D, D, false, kSoftmax>(a, p.B, s);
+  else launch_kv_t<T, D, D, false, kElu1>(a, p.B, s);
 }
 
 hipError_t launch_kv_reduce(const Problem& p, const void* K, const void* V, const void* W,
@@ -274,14 +309,11 @@ hipError_t launch_kv_reduce(const Problem& p, const void* K, const void* V, cons
   a.kv_out = nsplit > 1 ? static_cast<float*>(ws) : KV;
   a.ks_out = ksum;
   if (p.dtype == 1 && p.D == 128) {
-    if (p.proj) launch_kv_t<uint16_t, 128, 256, true>(a, p.B, s);
-    else launch_kv_t<uint16_t, 128, 128, false>(a, p.B, s);
+    launch_kv_d<uint16_t, 128>(p, a, s);
   } else if (p.dtype == 1 && p.D == 64) {
-    if (p.proj) launch_kv_t<uint16_t, 64, 256, true>(a, p.B, s);
-    else launch_kv_t<uint16_t, 64, 64, false>(a, p.B, s);
+    launch_kv_d<uint16_t, 64>(p, a, s);
   } else if (p.dtype == 0 && p.D == 64) {
-    if (p.proj) launch_kv_t<float, 64, 256, true>(a, p.B, s);
-    else launch_kv_t<float, 64, 64, false>(a, p.B, s);
+    launch_kv_d<float, 64>(p, a, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -71,7 +71,7 @@ struct Kv2Shape {
   static_assert(PER_T * 512 * 8 == BUF && (TILE / 8) % 512 == 0, "whole pieces, K/V split per piece index");
   using WR = LdsRow<uint16_t, D>;                 // W^T [F][D] staging (prologue)
   static constexpr int w_bytes = F * WR::bytes_per_row;
-  static constexpr int ring_bytes = 2 * BUF * 2;
+  static constexpr int ring_bytes = 2 * BUF * 2 + 2 * SS * 8;  // K/V double buffer, then per-token softmax stats
   static constexpr int red_floats = (D / 32) * 16 * 64 + 64;  // one wave's KV slice + ksum
   static constexpr int r_bytes = (NTW - 1) * NFS * red_floats * 4;
   static constexpr int m1 = w_bytes > ring_bytes ? w_bytes : ring_bytes;
@@ -79,7 +79,7 @@ struct Kv2Shape {
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int F, bool PROJ>
+template <int D, int F, bool PROJ, int MAP>
 __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
   using S = Kv2Shape<D, F>;
   constexpr int NFS = S::NFS, NTW = S::NTW, STEP = S::STEP, SS = S::SS, PER_T = S::PER_T;
@@ -115,6 +115,14 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
     }
   };
   uint16_t* const ring = reinterpret_cast<uint16_t*>(smem);
+  float2* const stats = reinterpret_cast<float2*>(smem + 2 * S::BUF * 2);  // [2][SS] (max, 1 / sum)
+  // softmax map (identity projection, F == D): a thread's K pieces are all
+  // logical piece tid % (D / 8) of their rows, so its 8 bias values are fixed
+  float kbias[8];
+  if constexpr (MAP == kSoftmax) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kbias[j] = a.bias ? a.bias[(size_t)h * F + (tid % (D / 8)) * 8 + j] : 0.f;
+  }
   auto store_stg = [&](int buf) {
     uint16_t* kt = ring + buf * S::BUF;
     uint16_t* vt = kt + S::TILE;
@@ -123,8 +131,19 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
       const bool isv = i >= PER_T / 2;
       const int Pl = tid + 512 * (isv ? i - PER_T / 2 : i);
       const int row = Pl / (D / 8), p = Pl % (D / 8);
-      if (isv) *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = stg[i];
-      else *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = stg[i];
+      if (isv) {
+        *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = stg[i];
+      } else {
+        *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = stg[i];
+        if constexpr (MAP == kSoftmax) {  // the row's D / 8 pieces: D / 8 consecutive lanes
+          const Vec8<uint16_t> kv8 = __builtin_bit_cast(Vec8<uint16_t>, stg[i]);
+          float z[8], m, inv;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) z[j] = bf2f(kv8.v[j]) + kbias[j];
+          softmax_stats<8, D / 8 - 1>(z, m, inv);
+          if (p == 0) stats[buf * SS + row] = float2{m, inv};
+        }
+      }
     }
   };
   load_stg(0);  // in flight during the W staging below
@@ -187,12 +206,23 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
       float p[16];
+      // softmax: (max, 1 / sum) of the row's token, from the staging pass
+      auto st = [&](int r) {
+        if constexpr (MAP == kSoftmax) return stats[(ss & 1) * SS + r0 + crow(lane, r)];
+        else return float2{0.f, 1.f};
+      };
       if (t0 + 32 <= t_end) {  // wave-uniform: only the range's last step has rows past it
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = elu1(acc[r]);
+        for (int r = 0; r < 16; ++r) {
+          const float2 sr = st(r);
+          p[r] = phi_of<MAP>(acc[r], sr.x, sr.y);
+        }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = t0 + crow(lane, r) < t_end ? elu1(acc[r]) : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const float2 sr = st(r);
+          p[r] = t0 + crow(lane, r) < t_end ? phi_of<MAP>(acc[r], sr.x, sr.y) : 0.f;
+        }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) ks += p[r];
@@ -396,10 +426,10 @@ size_t fused_workspace_bytes(const Problem& p, int L) {
          (size_t)p.H * pl.w_bytes();
 }
 
-template <int D, int F, bool PROJ>
+template <int D, int F, bool PROJ, int MAP>
 static hipError_t launch_kv2_t(const Problem& p, const Kv2Args& ka, const PackArgs& pa, hipStream_t s,
                                StageTimer* t) {
-  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ>), dim3(ka.nsplit, p.B * p.H), dim3(512), 0, s, ka);
+  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit, p.B * p.H), dim3(512), 0, s, ka);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   t->mark();
@@ -449,12 +479,16 @@ hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void
   pa.pack_w = pw;
   if (p.dtype != 1) return hipErrorInvalidValue;
   if (p.D == 128) {
-    if (p.proj) return launch_kv2_t<128, 256, true>(p, ka, pa, s, t);
-    return launch_kv2_t<128, 128, false>(p, ka, pa, s, t);
+    if (p.proj) return launch_kv2_t<128, 256, true, kElu1>(p, ka, pa, s, t);
+    if (p.fmap == kRelu) return launch_kv2_t<128, 128, false, kRelu>(p, ka, pa, s, t);
+    if (p.fmap == kSoftmax) return launch_kv2_t<128, 128, false, kSoftmax>(p, ka, pa, s, t);
+    return launch_kv2_t<128, 128, false, kElu1>(p, ka, pa, s, t);
   }
   if (p.D == 64) {
-    if (p.proj) return launch_kv2_t<64, 256, true>(p, ka, pa, s, t);
-    return launch_kv2_t<64, 64, false>(p, ka, pa, s, t);
+    if (p.proj) return launch_kv2_t<64, 256, true, kElu1>(p, ka, pa, s, t);
+    if (p.fmap == kRelu) return launch_kv2_t<64, 64, false, kRelu>(p, ka, pa, s, t);
+    if (p.fmap == kSoftmax) return launch_kv2_t<64, 64, false, kSoftmax>(p, ka, pa, s, t);
+    return launch_kv2_t<64, 64, false, kElu1>(p, ka, pa, s, t);
   }
   return hipErrorInvalidValue;
 }

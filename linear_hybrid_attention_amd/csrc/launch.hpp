@@ -11,6 +11,7 @@ struct Problem {
   int B, H, N, D, F;
   int dtype;  // 0 = fp32, 1 = bf16
   bool proj;  // W present (F == 256) or identity map (F == D)
+  int fmap;   // feature map: kElu1, kRelu or kSoftmax (the last two only without W)
 };
 
 enum { M_PHI = 1, M_LIN = 2, M_LM = 4 };

@@ -41,6 +41,7 @@ Problem make_problem(const ttr_dims& d, bool proj) {
   p.F = d.F;
   p.dtype = d.dtype;
   p.proj = proj;
+  p.fmap = d.fmap;
   return p;
 }
 
@@ -254,6 +255,7 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
   const bool proj = W != nullptr;
   TTR_TRY(check_dims(d, proj));
   if (L < 0 || L > d.N) return TTR_ERR_SHAPE;
+  if (d.fmap != TTR_FMAP_ELU1 && L > 0) return TTR_ERR_UNSUPPORTED;  // landmarks belong to the elu+1 TTR layer
   TTR_TRY(check_ptr(Q));
   TTR_TRY(check_ptr(K));
   TTR_TRY(check_ptr(V));

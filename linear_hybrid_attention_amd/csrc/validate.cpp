@@ -16,6 +16,9 @@ size_t dtype_bytes(int32_t dtype) {
 
 ttr_status check_dims(const ttr_dims& d, bool has_w) {
   if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
+  if (d.fmap < TTR_FMAP_ELU1 || d.fmap > TTR_FMAP_SOFTMAX) return TTR_ERR_SHAPE;
+  // relu / softmax: the NNT linear attention's maps on projected features
+  if (d.fmap != TTR_FMAP_ELU1 && has_w) return TTR_ERR_UNSUPPORTED;
   if (d.B < 1 || d.H < 1 || d.N < 1) return TTR_ERR_SHAPE;
   if (d.D != 64 && d.D != 128) return TTR_ERR_SHAPE;
   if (has_w) {

@@ -94,6 +94,28 @@ def test_hybrid_forward_validation(lib):
     assert hyb(lib, D(F=256, dt=1), causal=1, L=0, **kw) == UNSUP
 
 
+def test_feature_map_kind_validation(lib):
+    big = 1 << 40
+    kw = dict(Q=big, K=2 * big, V=3 * big, W=4 * big, g=5 * big, out=6 * big, ws=7 * big)
+    nw = dict(kw)
+    nw["W"] = None
+
+    def Dm(fmap, F=256, dt=0):
+        d = D(F=F, dt=dt)
+        d.fmap = fmap
+        return d
+
+    assert hyb(lib, Dm(3), **kw) == SHAPE
+    assert hyb(lib, Dm(-1), **kw) == SHAPE
+    # relu / softmax are the NNT layer's maps on projected features: no W, no landmarks
+    assert hyb(lib, Dm(1), **kw) == UNSUP
+    assert hyb(lib, Dm(2, F=64), L=16, **nw) == UNSUP
+    assert hyb(lib, Dm(2, F=64), L=0, wsb=16, **nw) == WS      # otherwise valid: reaches the workspace check
+    assert lib.ttr_feature_map(Dm(1), big, 2 * big, None, 3 * big, None) == UNSUP
+    assert lib.ttr_workspace_bytes(Dm(2, F=64, dt=1), 0, 0, 0) > 0
+    assert lib.ttr_workspace_bytes(Dm(2, F=256, dt=1), 0, 0, 0) == 0
+
+
 def test_causal_scan_validation(lib):
     big = 1 << 40
     d = D(B=8, H=8, N=32768, Dm=64, F=64, dt=1)
