@@ -6,19 +6,20 @@
 // Linear Attention", sections "The inputs" and "How it works".)
 //
 // Workgroup: 4 waves x 32 query tokens, two workgroups per compute unit (two
-// waves per SIMD, so one wave's exp/elu work overlaps the other's MFMAs).
-// The per-head operands come from the pack written by the key/value stage as
-// a sequence of equal-size chunks (W^T, KV^T alternately per 64 features,
-// then one K_L + V_L^T chunk per 32 landmarks). They stream global ->
-// registers -> three LDS slots, two chunks ahead of the one being consumed in
-// the linear branch and one ahead in the landmark branch (whose accumulators
-// leave room for one register set only), one barrier per chunk. Q stays in registers as the B operand of every
-// product, and every operand read from LDS is a plain 16-byte row read:
-//   W^T chunk:   phi^T [64 f x tok]  = W^T . Q^T (+ bias, then elu + 1; phi . ksum)
+// waves per SIMD). The per-head operands come from the pack written by the
+// key/value stage as a sequence of equal-size chunks (W^T, KV^T alternately
+// per 64 features, then one K_L + V_L^T chunk per 32 landmarks), copied
+// global -> LDS asynchronously into a ring of four slots, one step ahead.
+// Q stays in registers as the B operand of every product, and every LDS
+// operand read is a plain 16-byte row read:
+//   W^T chunk:   phi^T [64 f x tok]  = W^T . Q^T (+ bias, then the map; phi . ksum)
 //   KV^T chunk:  num^T [D x tok]    += KV^T . phi^T
 //   landmark chunk (32 landmarks: K_L then V_L^T):
 //                S^T  [32 j x tok]   = K_L . Q^T  (scaled to base 2, online max)
 //                o^T  [D x tok]     += V_L^T . P^T
+// Both branches are software-pipelined so that each step issues two
+// independent MFMA products and overlaps the elementwise work (feature map,
+// softmax) of one with the execution of the other.
 // The online softmax keeps a running row max m and only rescales o and the
 // row sum when a new score exceeds m by more than 8 (base 2), so the exp
 // arguments stay below 2^8 and most chunks skip the rescale.
@@ -45,11 +46,12 @@ template <int D, int F, int MAP>
 __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   constexpr int CH = 64 * D;  // elements per chunk (every chunk kind)
   constexpr int NFC = F / 64;
-  constexpr int PER_T = CH * 2 / 16 / 256;  // 16-byte pieces per thread per chunk
+  constexpr int PER_T = CH * 2 / 16 / 256;  // 16-byte copies per thread per chunk
   static_assert(PER_T * 256 * 16 == CH * 2, "whole pieces");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * F * 4 + 3 * CH * 2];
+  constexpr int NSLOT = 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * F * 4 + NSLOT * CH * 2];
   float* vecS = reinterpret_cast<float*>(smem);  // biasP [F] | ksumP [F]
-  uint16_t* const slots = reinterpret_cast<uint16_t*>(smem + 2 * F * 4);  // 3 chunk slots
+  uint16_t* const slots = reinterpret_cast<uint16_t*>(smem + 2 * F * 4);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
@@ -66,61 +68,52 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   const unsigned char* pbh = a.pack_bh + (size_t)bh * a.bh_bytes;
   const uint16_t* wpk = reinterpret_cast<const uint16_t*>(a.pack_w + (size_t)h * a.w_bytes);
   const uint16_t* kvpk = reinterpret_cast<const uint16_t*>(pbh + 2 * F * 4);
-  const uint16_t* lmpk = kvpk + F * D;
   const int nlc = (L + 31) / 32;  // landmark chunks
   const int nch = 2 * NFC + nlc;
 
-  // Chunk ci streams global -> registers -> LDS slot ci % 3. Its loads are
-  // issued two chunks ahead (at the start of step ci - 2, into register set
-  // ci & 1) and it is written to LDS at the end of step ci - 1, so each load
-  // has two steps of compute to land. The sets are named statically (the
-  // loops below take chunks in pairs of even and odd index), and loads are
-  // issued on every step (indexes clamped) so the compiler's count of loads
-  // in flight, and with it every wait, is exact.
-  auto chunk_src = [&](int ci) {
-    ci = min(ci, nch - 1);
-    return reinterpret_cast<const u32x4*>(ci < 2 * NFC ? ((ci & 1) ? kvpk : wpk) + (ci >> 1) * CH
-                                                       : lmpk + (ci - 2 * NFC) * CH);
-  };
-  u32x4 sa[PER_T], sb[PER_T];  // register sets for even / odd chunks
-  auto load_to = [&](u32x4 (&st)[PER_T], int ci) {
-    const u32x4* s4 = chunk_src(ci);
+  // Chunk ci is copied global -> LDS slot ci % 4 asynchronously at the start
+  // of the step before the one that first reads it; every step ends by
+  // waiting for its copies and a barrier. A step reads at most two chunks
+  // (consecutive), so the two it reads and the two in flight never share a slot.
+  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wpk, (uint32_t)a.w_bytes);                     // W^T chunks
+  const __amdgpu_buffer_rsrc_t rkv = buffer_rsrc(kvpk, (uint32_t)(a.bh_bytes - 2 * F * 4));   // KV^T, then landmark chunks
+  auto issue = [&](int ci) {
+    if (ci >= nch) return;  // workgroup-uniform
+    const bool wchunk = ci < 2 * NFC && !(ci & 1);
+    const uint32_t soff = (uint32_t)(ci < 2 * NFC ? (ci >> 1) : NFC + ci - 2 * NFC) * (CH * 2);
+    uint16_t* dst = slots + (ci % NSLOT) * CH;
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) st[i] = s4[tid + 256 * i];
+    for (int i = 0; i < PER_T; ++i)
+      copy16_async(wchunk ? rw : rkv, (uint32_t)(tid + 256 * i) * 16, soff, dst + (256 * i + 64 * w) * 8);
   };
-  auto store_from = [&](const u32x4 (&st)[PER_T], int ci) {
-    u32x4* d4 = reinterpret_cast<u32x4*>(slots + (ci % 3) * CH);
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) d4[tid + 256 * i] = st[i];
+  auto end_step = [&]() {
+    wait_vmcnt<0>();
+    barrier_lds();
   };
-  auto slot_of = [&](int ci) -> const uint16_t* { return slots + (ci % 3) * CH; };
+  auto slot_of = [&](int ci) -> const uint16_t* { return slots + (ci % NSLOT) * CH; };
 
-  // prologue: query fragments, then chunks 0 and 1; chunk 0 to LDS
+  // Prologue: the copies of chunks 0..2 (read from L2 by every tile of the
+  // head) and of the bias/ksum vectors start first, then the query loads
+  // (from HBM), so that one wait covers all their latencies.
+  issue(0);
+  issue(1);
+  issue(2);
+  {
+    const __amdgpu_buffer_rsrc_t rvec = buffer_rsrc(pbh, 2 * F * 4);
+    if (tid < 2 * F * 4 / 16) copy16_async(rvec, (uint32_t)tid * 16, 0, smem + w * 64 * 16);
+  }
   Frag<uint16_t> qf[D / 16];
   const uint16_t* Qp = a.Q + ((size_t)bh * N + (tok_ok ? tok : 0)) * D + 8 * g;
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) qf[kb] = ld_frag<uint16_t>(Qp + kb * 16);  // rows past N: row 0, not stored
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(pbh);
-    u32x4* dst = reinterpret_cast<u32x4*>(smem);
-    for (int i = tid; i < 2 * F * 4 / 16; i += 256) dst[i] = src[i];
-  }
   const float gh = L > 0 ? a.g[h] : 0.f;
-  load_to(sa, 0);
-  load_to(sb, 1);
-  store_from(sa, 0);
-
-  f32x16 num[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) num[db] = f32x16{};
-  float den = 0.f;
+  end_step();  // chunks 0..2, bias and ksum in LDS; Q in registers
 
   // softmax map (identity projection, F == D): the token's feature maximum
   // and inverse sum, from its Q row (half in this lane, half in lane ^ 32)
   // plus the bias (stored in MFMA row order: feature f at kperm(f))
   float qm = 0.f, qinv = 1.f;
   if constexpr (MAP == kSoftmax) {
-    barrier_lds();  // bias in LDS
     float z[D / 2];
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) {
@@ -131,84 +124,171 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
     softmax_stats<D / 2, 32>(z, qm, qinv);
   }
 
-  // ---- linear branch: per 64 features, a W^T chunk (even) then a KV^T chunk (odd)
-#pragma clang loop unroll(disable)
-  for (int fc = 0; fc < NFC; ++fc) {
-    const int ci = 2 * fc;
-    barrier_lds();  // chunk ci in LDS; every wave is done with step ci - 1
-    load_to(sa, ci + 2);
-    Frag<uint16_t> pb[4];  // phi^T of these 64 features, 4 k-blocks of 16
-    {
-      const uint16_t* wt = slot_of(ci);
-      // two independent accumulation chains (feature blocks 0 and 1), interleaved
-      f32x16 acc[2];
+  f32x16 num[D / 32];
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb) {
-        const float* bp = vecS + fc * 64 + fb * 32 + 8 * g;
+  for (int db = 0; db < D / 32; ++db) num[db] = f32x16{};
+  float den = 0.f;
+
+  // ---- the products, one chunk each
+  // phi^T of features fc*64.. (two 32-row blocks) = W^T chunk . Q^T + bias
+  auto gemm1 = [&](int fc, f32x16 (&acc)[2]) {
+    const uint16_t* wt = slot_of(2 * fc);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) { acc[fb][r] = bp[r]; acc[fb][8 + r] = bp[16 + r]; }
-      }
+    for (int fb = 0; fb < 2; ++fb) {
+      const float* bp = vecS + fc * 64 + fb * 32 + 8 * g;
 #pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb)
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-          mma(acc[fb], ld_frag<uint16_t>(wt + toff<D, kRowRead>(fb * 32 + c, kb * 16 + 8 * g)), qf[kb]);
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb) {
-        const float* kp = vecS + F + fc * 64 + fb * 32 + 8 * g;
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = phi_of<MAP>(acc[fb][r], qm, qinv);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) den += p[r] * kp[r] + p[8 + r] * kp[16 + r];
-        pb[2 * fb] = to_frag<uint16_t>(p);
-        pb[2 * fb + 1] = to_frag<uint16_t>(p + 8);
-      }
+      for (int r = 0; r < 8; ++r) { acc[fb][r] = bp[r]; acc[fb][8 + r] = bp[16 + r]; }
     }
-    store_from(sb, ci + 1);
-    barrier_lds();  // chunk ci + 1 in LDS
-    load_to(sb, ci + 3);
-    {
-      const uint16_t* kvt = slot_of(ci + 1);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int kb = 0; kb < D / 16; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          mma(num[db], ld_frag<uint16_t>(kvt + toff<64, kRowRead>(db * 32 + c, kk * 16 + 8 * g)), pb[kk]);
+      for (int fb = 0; fb < 2; ++fb)
+        mma(acc[fb], ld_frag<uint16_t>(wt + toff<D, kRowRead>(fb * 32 + c, kb * 16 + 8 * g)), qf[kb]);
+  };
+  // phi = map(acc) as bf16 operands, and phi . ksum into den
+  auto map_den = [&](int fc, const f32x16 (&acc)[2], Frag<uint16_t> (&pb)[4]) {
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) {
+      const float* kp = vecS + F + fc * 64 + fb * 32 + 8 * g;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = phi_of<MAP>(acc[fb][r], qm, qinv);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) den += p[r] * kp[r] + p[8 + r] * kp[16 + r];
+      pb[2 * fb] = to_frag<uint16_t>(p);
+      pb[2 * fb + 1] = to_frag<uint16_t>(p + 8);
     }
-    if (ci + 2 < nch) store_from(sa, ci + 2);
-  }
-  den += shfl_xor32(den);
-  {
-    const float inv = 1.f / (den + a.eps);
-    const float alpha = L > 0 ? 1.f / (1.f + expf(-gh)) : 1.f;  // g = +inf -> 1, g = -inf -> 0
-    const float ca = alpha * inv;
+  };
+  // num^T += KV^T chunk . phi^T
+  auto gemm2 = [&](int fc, const Frag<uint16_t> (&pb)[4]) {
+    const uint16_t* kvt = slot_of(2 * fc + 1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) num[db][r] *= ca;  // alpha * out_lin
-  }
+      for (int kk = 0; kk < 4; ++kk)
+        mma(num[db], ld_frag<uint16_t>(kvt + toff<64, kRowRead>(db * 32 + c, kk * 16 + 8 * g)), pb[kk]);
+  };
 
-  // ---- landmark branch: one chunk per 32 landmarks, K_L [32 j][D] then V_L^T [D][32 j]
+  // ---- linear branch, software-pipelined: step k issues GEMM1 of feature
+  // chunk k and GEMM2 of chunk k - 1 (independent products), then maps the
+  // GEMM1 result while the GEMM2 MFMAs are still executing. Step k reads
+  // chunks 2k - 1 (KV^T) and 2k (W^T).
+  Frag<uint16_t> pb[4];
+  {  // (chunks 1 and 2 are already in flight)
+    f32x16 acc[2];
+    gemm1(0, acc);
+    map_den(0, acc, pb);
+    end_step();
+  }
+  // Steady linear step k (1 <= k < NFC): GEMM1 of feature chunk k (N1 MFMAs,
+  // two accumulator chains) then GEMM2 of chunk k - 1 (N2 MFMAs, four chains),
+  // one MFMA per slot in a fixed order. Each slot also issues the LDS reads of
+  // slot j + LEAD (operand, and for the map the matching ksum pair), and each
+  // GEMM2 slot maps PPS pairs of GEMM1's results, so the map's VALU work and
+  // the LDS latency both overlap the matrix core's execution.
+  constexpr int N1 = 2 * (D / 16), N2 = 4 * (D / 32), NJ = N1 + N2, LEAD = 4, PPS = 16 / N2;
+  static_assert(N1 >= LEAD && 16 % N2 == 0, "slot plan");
+  auto load_bias = [&](int fc, f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) {
+      const float* bp = vecS + fc * 64 + fb * 32 + 8 * g;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) { acc[fb][r] = bp[r]; acc[fb][8 + r] = bp[16 + r]; }
+    }
+  };
+  f32x16 accb[2];  // the next step's accumulators, holding its bias
+  if (NFC > 1) load_bias(1, accb);
+  pin_before(accb[0]);
+  pin_before(accb[1]);
+  // Step k reads KV^T chunk 2k - 1 and W^T chunk 2k: slots 1 and 2 for odd
+  // k, 3 and 0 for even k. Both call sites pass the parity as a literal and
+  // the step is inlined, so every operand address folds to a lane base plus
+  // an immediate offset.
+  auto lin_step = [&](int k, bool ODD) __attribute__((always_inline)) {
+    issue(2 * k + 1);
+    issue(2 * k + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* wt = slots + (ODD ? 2 : 0) * CH;
+    const uint16_t* kvt = slots + (ODD ? 1 : 3) * CH;
+    const float* kbase = vecS + F + k * 64 + 8 * g;
+    auto a_ptr = [&](int j) -> const uint16_t* {
+      if (j < N1) return wt + toff<D, kRowRead>((j & 1) * 32 + c, (j >> 1) * 16 + 8 * g);
+      const int jj = j - N1;
+      return kvt + toff<64, kRowRead>((jj % (D / 32)) * 32 + c, (jj / (D / 32)) * 16 + 8 * g);
+    };
+    // pair t (0..15) of the map: accumulator fb = t / 8, elements 2q, 2q + 1
+    // (q = t % 8), features fb * 32 + 8 g + {2q, 2q + 1} (+ 8 from q = 4 on)
+    auto k_quad = [&](int t) -> u32x4 {  // pairs t, t + 1 (t even)
+      const int fb = t >> 3, q = t & 7;
+      return *reinterpret_cast<const u32x4*>(kbase + fb * 32 + (q < 4 ? 2 * q : 16 + 2 * (q - 4)));
+    };
+    f32x16 acc[2] = {accb[0], accb[1]};
+    Frag<uint16_t> fa[NJ];
+    u32x4 kq[8];
+    u32x4 pw[4];
+#pragma unroll
+    for (int j = 0; j < LEAD; ++j) fa[j] = ld_frag<uint16_t>(a_ptr(j));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + LEAD < NJ) fa[j + LEAD] = ld_frag<uint16_t>(a_ptr(j + LEAD));
+      if (j + LEAD >= N1 && j + LEAD < NJ)
+#pragma unroll
+        for (int u = 0; u < PPS; ++u) {
+          const int t = (j + LEAD - N1) * PPS + u;
+          if ((t & 1) == 0) kq[t >> 1] = k_quad(t);
+        }
+      if (j < N1) mma(acc[j & 1], fa[j], qf[j >> 1]);
+      else mma(num[(j - N1) % (D / 32)], fa[j], pb[(j - N1) / (D / 32)]);
+      if (j >= N1) {
+#pragma unroll
+        for (int u = 0; u < PPS; ++u) {
+          const int t = (j - N1) * PPS + u, fb = t >> 3, q = t & 7;
+          const float p0 = phi_of<MAP>(acc[fb][2 * q], qm, qinv);
+          const float p1 = phi_of<MAP>(acc[fb][2 * q + 1], qm, qinv);
+          den = fmaf(p0, __uint_as_float(kq[t >> 1][2 * (t & 1)]), den);
+          den = fmaf(p1, __uint_as_float(kq[t >> 1][2 * (t & 1) + 1]), den);
+          pw[2 * fb + (q >> 2)][q & 3] = pack_bf16x2(p0, p1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(bf16x8, pw[i]);
+    load_bias(min(k + 1, NFC - 1), accb);  // unconditional: a branch here would let the map sink past the slots
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pin_before(pb[i]);
+    pin_before(den);
+    pin_before(accb[0]);
+    pin_before(accb[1]);
+    end_step();
+  };
+#pragma clang loop unroll(disable)
+  for (int k = 1; k < NFC; k += 2) {
+    lin_step(k, true);
+    if (k + 1 < NFC) lin_step(k + 1, false);  // workgroup-uniform
+  }
+  // landmark branch state
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
   const float sl2 = kLog2e * rsqrtf((float)D);
-  auto lm_step = [&](int lc) {
+  // S^T of landmark chunk lc = K_L . Q^T
+  auto scores = [&](int lc, f32x16& s) {
     const uint16_t* kl = slot_of(2 * NFC + lc);
-    const uint16_t* vlt = kl + 32 * D;
-    const int j0 = lc * 32;
-    f32x16 s = f32x16{};
+    s = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) mma(s, ld_frag<uint16_t>(kl + toff<D, kRowRead>(c, kb * 16 + 8 * g)), qf[kb]);
-    // row max of the raw scores (landmarks past L masked to -inf; only the last
-    // chunk can hold such landmarks)
+  };
+  // online softmax of chunk lc's scores: new running max (rescaling o and l
+  // only when it grows by more than 8 in base 2), probabilities as operands
+  auto softmax = [&](int lc, f32x16& s, Frag<uint16_t> (&pf)[2]) {
+    const int j0 = lc * 32;
     float mx = -INFINITY;
     if (j0 + 32 <= L) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    } else {
+    } else {  // only the last chunk can hold landmarks past L
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (j0 + crow(lane, r) >= L) s[r] = -INFINITY;
@@ -231,33 +311,57 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { p[r] = fast_exp2(fmaf(s[r], sl2, nm)); ls += p[r]; }
     l += ls + shfl_xor32(ls);
-    const Frag<uint16_t> p0 = to_frag<uint16_t>(p), p1 = to_frag<uint16_t>(p + 8);
+    pf[0] = to_frag<uint16_t>(p);
+    pf[1] = to_frag<uint16_t>(p + 8);
+  };
+  // o^T += V_L^T . P^T of chunk lc
+  auto pv = [&](int lc, const Frag<uint16_t> (&pf)[2]) {
+    const uint16_t* vlt = slot_of(2 * NFC + lc) + 32 * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      mma(o[db], ld_frag<uint16_t>(vlt + toff32(db * 32 + c, 8 * g)), p0);
-      mma(o[db], ld_frag<uint16_t>(vlt + toff32(db * 32 + c, 16 + 8 * g)), p1);
+      mma(o[db], ld_frag<uint16_t>(vlt + toff32(db * 32 + c, 8 * g)), pf[0]);
+      mma(o[db], ld_frag<uint16_t>(vlt + toff32(db * 32 + c, 16 + 8 * g)), pf[1]);
     }
   };
-  // The first landmark chunk's successor is already in set b (loaded by the
-  // last linear step); after it, one register set suffices: each step loads
-  // its successor and writes it to LDS at its end.
-  if (nlc > 0) {  // workgroup-uniform
-    barrier_lds();
-    lm_step(0);
-    if (2 * NFC + 1 < nch) store_from(sb, 2 * NFC + 1);
-  }
-#pragma clang loop unroll(disable)
-  for (int lc = 1; lc < nlc; ++lc) {
-    const int ci = 2 * NFC + lc;
-    barrier_lds();
-    load_to(sa, ci + 1);
-    lm_step(lc);
-    if (ci + 1 < nch) store_from(sa, ci + 1);
-  }
-  barrier_lds();  // the slots are free for the output staging
 
-  // Epilogue: the wave's 32 x D output tile goes through LDS so that the
-  // global stores are whole 16-byte pieces, four full rows per store instruction.
+  // last linear step: GEMM2 of the last feature chunk, with the scores of
+  // landmark chunk 0 (chunk 2 NFC) beside it
+  f32x16 s;
+  Frag<uint16_t> pf[2];
+  {
+    issue(2 * NFC + 1);
+    if (nlc > 0) scores(0, s);  // workgroup-uniform
+    gemm2(NFC - 1, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    den += shfl_xor32(den);
+    const float alpha = L > 0 ? 1.f / (1.f + expf(-gh)) : 1.f;  // g = +inf -> 1, g = -inf -> 0
+    const float ca = alpha / (den + a.eps);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) num[db][r] *= ca;  // alpha * out_lin
+    if (nlc > 0) softmax(0, s, pf);
+    end_step();
+  }
+
+  // ---- landmark branch, software-pipelined: step lc issues the scores of
+  // chunk lc + 1 and the PV product of chunk lc, then runs the softmax of
+  // chunk lc + 1 while the PV MFMAs execute. Step lc reads chunks 2 NFC + lc
+  // (V_L^T) and 2 NFC + lc + 1 (K_L).
+#pragma clang loop unroll(disable)
+  for (int lc = 0; lc < nlc; ++lc) {
+    issue(2 * NFC + lc + 2);
+    const bool more = lc + 1 < nlc;  // workgroup-uniform
+    if (more) scores(lc + 1, s);
+    pv(lc, pf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) softmax(lc + 1, s, pf);
+    end_step();
+  }
+
+  // Epilogue: the wave's 32 x D output tile goes through LDS (the slots are
+  // free after the last barrier) so that the global stores are whole 16-byte
+  // pieces, four full rows per store instruction.
   const float cb = L > 0 ? (1.f - 1.f / (1.f + expf(-gh))) / l : 0.f;
   uint16_t* ot = slots + w * 32 * D;  // [32 tokens][D], kRowRead swizzle
 #pragma unroll
@@ -270,14 +374,24 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       st4(ot + toff<D, kRowRead>(c, db * 32 + 8 * q + 4 * g), v[0], v[1], v[2], v[3]);
     }
   wave_lds_order();
-  constexpr int PIECES_PER_ROW = D / 8;
-  uint16_t* obase = a.out + ((size_t)bh * N + tile * 128 + 32 * w) * D;
+  // The stores go through a buffer resource over this (batch, head)'s output
+  // rows: a row past N gets offset N D 2 bytes, the resource's size, which
+  // the hardware drops. No branch, so all the LDS reads are in flight at once.
+  // (The validated N D < 2^31 keeps every offset within 32 bits.)
+  constexpr int PIECES_PER_ROW = D / 8, NP = 32 * PIECES_PER_ROW / 64;
+  const uint32_t out_bytes = (uint32_t)((size_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rout = buffer_rsrc(a.out + (size_t)bh * N * D, out_bytes);
+  u32x4 v[NP];
 #pragma unroll
-  for (int i = 0; i < 32 * PIECES_PER_ROW / 64; ++i) {
-    const int P = 64 * i + lane;
-    const int row = P / PIECES_PER_ROW, pc = P % PIECES_PER_ROW;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ot + toff<D, kRowRead>(row, pc * 8));
-    if (tile * 128 + 32 * w + row < N) *reinterpret_cast<u32x4*>(obase + (size_t)row * D + pc * 8) = v;
+  for (int i = 0; i < NP; ++i) {
+    const int P = 64 * i + lane, row = P / PIECES_PER_ROW, pc = P % PIECES_PER_ROW;
+    v[i] = *reinterpret_cast<const u32x4*>(ot + toff<D, kRowRead>(row, pc * 8));
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int P = 64 * i + lane, row = P / PIECES_PER_ROW, pc = P % PIECES_PER_ROW;
+    const int n = tile * 128 + 32 * w + row;
+    store16(rout, n < N ? (uint32_t)(n * D + pc * 8) * 2 : out_bytes, v[i]);
   }
 }
 

@@ -68,6 +68,27 @@ __device__ __forceinline__ void copy16_async(const void* gsrc, void* lds_wave_ba
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
+// Raw buffer resource over [base, base + bytes): 32-bit data format, no
+// stride or swizzle; an access at or past `bytes` reads zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The same asynchronous copy through a buffer resource: lane l copies the 16
+// bytes at soff + voff of r to lds_wave_base + 16 l. Unlike the global form,
+// this one is not a flat-segment access, so the compiler can still count the
+// wave's outstanding LDS reads in order while copies are in flight.
+__device__ __forceinline__ void copy16_async(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voff,
+                                           (int)soff, 0, 0);
+}
+
+// 16-byte store through a buffer resource at byte offset off (dropped by the
+// hardware when off is at or past the resource's size).
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
 template <int N>
@@ -83,6 +104,29 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads/writes are done
   asm volatile("s_barrier" ::: "memory");
+}
+
+// Instruction classes of the compiler's scheduling groups: sched_group<kind,
+// n>() asks the scheduler to place the next n instructions of that kind at
+// this point of the region's order (a hint; data dependences still hold).
+enum SchedKind : int { kSchedValu = 0x002, kSchedTrans = 0x400, kSchedAnyValu = 0x402, kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200 };
+template <int KIND, int N>
+__device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_barrier(KIND, N, 0); }
+
+// Makes v count as used at this point of the instruction stream: the
+// computation of v cannot then be moved past a later barrier or other
+// volatile asm (the compiler otherwise sinks pure register work towards its
+// first use).
+// (Device pass only: the host compiler has no "v" register class, and a
+// constraint it rejects inside a kernel template makes it drop that kernel's
+// launch stubs.)
+template <typename T>
+__device__ __forceinline__ void pin_before(const T& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(v));
+#else
+  (void)v;
+#endif
 }
 
 // Orders this wave's LDS accesses across lanes (lane i writes what lane j
