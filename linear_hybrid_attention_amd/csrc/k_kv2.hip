@@ -54,7 +54,8 @@ struct Kv2Args {
   const uint16_t* W;  // [H][D][F] or NULL (identity)
   const float* bias;  // [H][F] or NULL
   int H, N, chunk, nsplit;
-  float* part;  // [BH][nsplit][F*D + F]
+  float* part;             // [BH][nsplit][F*D + F]
+  unsigned char* pack_w;   // [H][F*D bf16]: W^T chunks, written by split 0 of batch 0
 };
 
 template <int D, int F>
@@ -173,6 +174,14 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) wf[kb] = ld_frag<uint16_t>(Wt + (f0 + c) * WR::stride + kb * 16 + 8 * g);
     __syncthreads();  // the region becomes the K/V double buffer
+    // The fused query kernel's W^T chunks [64 f][D] (kRowRead) are per head:
+    // one workgroup per head writes them, each lane its row f0 + c in 16-byte pieces.
+    if (split == 0 && bh < a.H && tw == 0) {
+      uint16_t* wc = reinterpret_cast<uint16_t*>(a.pack_w + (size_t)h * F * D * 2) + (size_t)((f0 + c) / 64) * 64 * D;
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb)
+        *reinterpret_cast<u32x4*>(wc + toff<D, kRowRead>((f0 + c) & 63, kb * 16 + 8 * g)) = __builtin_bit_cast(u32x4, wf[kb]);
+    }
   }
   const float bcol = a.bias ? a.bias[(size_t)h * F + f0 + c] : 0.f;
   f32x16 bias16;  // GEMM1 starts from the bias (MFMA C operand, only read)
@@ -292,14 +301,14 @@ struct PackArgs {
 
 // Jobs of one (batch, head), by blockIdx.x:
 //   [0, KVJ)            KV^T rows: FJ features x D (sum of partials), ksum, bias
-//   [KVJ, KVJ + F/8)    W^T rows for 8 features (batch 0 only)
 //   then one per 32-landmark chunk (K_L and V_L^T)
+// (The W^T chunks are written by the partial kernel, which holds W in registers.)
 template <int D, int F, bool PROJ>
 __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
   constexpr int FJ = 2048 / D > F ? F : 2048 / D;  // features per KV job: (FJ/2)*(D/4) = 256 threads
   constexpr int KVJ = F / FJ;
   const int tid = threadIdx.x;
-  const int bh = blockIdx.y, h = bh % a.H, b = bh / a.H;
+  const int bh = blockIdx.y, h = bh % a.H;
   const int nlb = (a.L + 31) / 32;
   PackLayout pl{D, F, a.L, nlb};
   unsigned char* base = a.pack_bh + (size_t)bh * pl.bh_bytes();
@@ -358,30 +367,16 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
     }
     return;
   }
-  if (job < KVJ + F / 8) {
-    if (b != 0) return;  // W^T is per head
-    const int f0 = (job - KVJ) * 8;
-    uint16_t* wc = reinterpret_cast<uint16_t*>(a.pack_w + (size_t)h * pl.w_bytes());
-    for (int u = tid; u < 8 * (D / 8); u += 256) {
-      const int f = f0 + u / (D / 8), d0 = (u % (D / 8)) * 8;
-      Vec8<uint16_t> v;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if constexpr (PROJ) v.v[j] = a.W[((size_t)h * D + d0 + j) * F + f];
-        else v.v[j] = (d0 + j == f) ? (uint16_t)0x3f80 : (uint16_t)0;
-      }
-      uint16_t* ch = wc + (size_t)(f / 64) * 64 * D;
-      st8(ch + toff<D, kRowRead>(f & 63, d0), v);
-    }
-    return;
-  }
-  const int jb = job - KVJ - F / 8;  // landmark chunk of 32
+  const int jb = job - KVJ;  // landmark chunk of 32
   if (jb >= nlb) return;
   const uint16_t* K = a.K + (size_t)bh * a.N * D;
   const uint16_t* V = a.V + (size_t)bh * a.N * D;
   uint16_t* kl = lmc + (size_t)jb * pl.chunk_elems();
   uint16_t* vl = kl + 32 * D;
-  // K_L [32 j][D] and V_L^T [D][32 j] (both read as rows); landmarks past L are zero
+  // K_L [32 j][D] straight to the chunk; V_L rows through LDS so that V_L^T
+  // [D][32 j] (landmark jl in column kperm(jl)) is written in 16-byte pieces.
+  // Landmarks past L are zero.
+  __shared__ uint16_t vrows[32][D + 8];
   for (int u = tid; u < 2 * 32 * (D / 8); u += 256) {
     const int isv = u >= 32 * (D / 8);
     const int uu = u - isv * 32 * (D / 8);
@@ -389,12 +384,16 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
     const uint16_t* src = isv ? V : K;
     const Vec8<uint16_t> v =
         j < a.L ? ld8(src + (size_t)(((long long)j * a.N) / a.L) * D + d0) : zero8<uint16_t>();
-    if (isv) {
+    if (isv) *reinterpret_cast<Vec8<uint16_t>*>(&vrows[jl][d0]) = v;
+    else st8(kl + toff<D, kRowRead>(jl, d0), v);
+  }
+  __syncthreads();
+  for (int u = tid; u < D * 4; u += 256) {  // piece (row d, columns 8q .. 8q + 7)
+    const int d = u / 4, q = u % 4;
+    Vec8<uint16_t> v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vl[toff32(d0 + e, kperm(jl))] = v.v[e];
-    } else {
-      st8(kl + toff<D, kRowRead>(jl, d0), v);
-    }
+    for (int e = 0; e < 8; ++e) v.v[e] = vrows[kperm(8 * q + e)][d];  // kperm is its own inverse
+    st8(vl + toff32(d, 8 * q), v);
   }
 }
 
@@ -434,7 +433,7 @@ static hipError_t launch_kv2_t(const Problem& p, const Kv2Args& ka, const PackAr
   if (e != hipSuccess) return e;
   t->mark();
   constexpr int FJ = 2048 / D > F ? F : 2048 / D;
-  const int jobs = F / FJ + F / 8 + (pa.L + 31) / 32;
+  const int jobs = F / FJ + (pa.L + 31) / 32;
   hipLaunchKernelGGL((kv2_pack_kernel<D, F, PROJ>), dim3(jobs, p.B * p.H), dim3(256), 0, s, pa);
   e = hipGetLastError();
   t->mark();
@@ -465,6 +464,7 @@ hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void
   ka.chunk = chunk;
   ka.nsplit = nsplit;
   ka.part = part;
+  ka.pack_w = pw;
   PackArgs pa;
   pa.part = part;
   pa.nsplit = nsplit;
