@@ -36,11 +36,21 @@ Every function computes the plain definition in float64 with numpy, one
   "The inputs") are max(z, 0) and the softmax over each token's features,
   applied to z = x (+ b) like elu + 1.
 
+The NNT linear-attention layer ("NNT Define Linear Attention", sections "The
+inputs" and "How it works": project Q/K/V, apply the feature map, K'^T V
+first, normalise, project back out; embed_dim divides by num_heads;
+batch_first) is read as: x [B, N, E]; each projection is x @ W + b with W
+[E, E] (input rows, output columns, the same row-vector convention as W_h)
+and b [E]; heads are consecutive D = E / H column blocks; dropout is the
+identity (an inference forward).
+
 Pins (tests/test_oracle.py): brute-force N x N row-normalised attention,
 torch's elu and scaled_dot_product_attention in fp64, closed forms
 (W = 0, L = 1, Q = 0, first causal token), invariants (phi > 0, permutation,
 linearity, convex hull, alpha limits, last causal token equals the non-causal
-result), and a hand-worked example under tests/golden/.
+result), and a hand-worked example under tests/golden/. The NNT layer is pinned by
+the layer restated in torch with heads as column slices and the N x N form,
+the zero query/key projection closed form, and head-permutation invariance.
 """
 from __future__ import annotations
 
@@ -52,7 +62,7 @@ import numpy as np
 __all__ = [
     "elu_plus_one", "relu_map", "softmax_map", "MAPS", "feature_map", "kv_reduce", "apply", "landmark_indices",
     "landmark_attn", "blend", "hybrid_forward", "causal_forward",
-    "hybrid_rows", "causal_rows", "normwise_err",
+    "hybrid_rows", "causal_rows", "normwise_err", "split_heads", "merge_heads", "nnt_layer_forward",
 ]
 
 
@@ -307,6 +317,46 @@ def causal_rows(Q, K, V, W, b, eps, rows: Sequence[tuple], kind: str = "elu1") -
         wts = phik @ phiq
         res[i] = (wts @ V[bi, h][: n + 1]) / (wts.sum() + float(eps))
     return res
+
+
+def split_heads(y: np.ndarray, H: int) -> np.ndarray:
+    """[B, N, E] -> [B, H, N, D]: head h takes columns h*D .. h*D + D - 1."""
+    B, N, E = y.shape
+    return y.reshape(B, N, H, E // H).transpose(0, 2, 1, 3)
+
+
+def merge_heads(a: np.ndarray) -> np.ndarray:
+    """[B, H, N, D] -> [B, N, H*D], the inverse of split_heads."""
+    B, H, N, D = a.shape
+    return a.transpose(0, 2, 1, 3).reshape(B, N, H * D)
+
+
+def nnt_layer_forward(x, Wq, bq, Wk, bk, Wv, bv, Wo, bo, H: int, eps, causal: bool = False,
+                      kind: str = "elu1") -> np.ndarray:
+    """NNT linear-attention layer, inference forward.
+
+    "NNT Define Linear Attention", section "How it works": Q, K, V are
+    projections of x; the feature map applies to Q and K; the attention is
+    phi(Q) (phi(K)^T V) / (phi(Q) . sum phi(K) + eps) per head (prefix sums
+    when causal, section "The inputs"); the heads are merged and projected
+    out. x [B, N, E]; W* [E, E] used as x @ W; b* [E] or None. Returns
+    [B, N, E] float64.
+    """
+    x = _f64(x)
+    B, N, E = x.shape
+    assert E % H == 0, "embed_dim must divide by num_heads"
+
+    def proj(inp, W, b):
+        y = inp @ _f64(W)
+        return y if b is None else y + _f64(b)
+
+    Q, K, V = (split_heads(proj(x, W, b), H) for W, b in ((Wq, bq), (Wk, bk), (Wv, bv)))
+    if causal:
+        A = causal_forward(Q, K, V, None, None, eps, kind)
+    else:
+        KV, ksum = kv_reduce(K, V, None, None, kind)
+        A = apply(Q, None, None, KV, ksum, eps, kind)
+    return proj(merge_heads(A), Wo, bo)
 
 
 def normwise_err(got, ref, axes=(-2, -1)) -> float:

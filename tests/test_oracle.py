@@ -433,6 +433,85 @@ def test_relu_map_all_negative_keys_give_zero():
     assert not O.apply(Q, None, None, KV, ksum, EPS, "relu").any()
 
 
+# ---------------------------------------------------------------- NNT layer (in/out projections)
+
+def _layer_params(seed, B=2, N=24, E=32, H=4, bias=True):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((B, N, E))
+    Ws = [r.standard_normal((E, E)) / math.sqrt(E) for _ in range(4)]
+    bs = [r.standard_normal(E) * 0.1 if bias else None for _ in range(4)]
+    return x, Ws, bs
+
+
+def brute_layer(x, Ws, bs, H, eps, causal=False, kind="elu1"):
+    """The layer restated in torch (fp64): heads as column slices of the
+    projections, attention in the N x N row-normalised form."""
+    X = torch.from_numpy(x)
+
+    def lin(inp, W, b):
+        y = inp @ torch.from_numpy(W)
+        return y if b is None else y + torch.from_numpy(b)
+
+    q, k, v = (lin(X, W, b) for W, b in zip(Ws[:3], bs[:3]))
+    B, N, E = x.shape
+    D = E // H
+    heads = torch.empty(B, N, E, dtype=torch.float64)
+    for h in range(H):
+        sl = slice(h * D, (h + 1) * D)
+        A = TORCH_MAPS[kind](q[..., sl]) @ TORCH_MAPS[kind](k[..., sl]).transpose(-1, -2)
+        if causal:
+            A = A * torch.tril(torch.ones(N, N, dtype=torch.float64))
+        heads[..., sl] = (A @ v[..., sl]) / (A.sum(-1, keepdim=True) + eps)
+    return lin(heads, Ws[3], bs[3]).numpy()
+
+
+def _layer(x, Ws, bs, H, causal=False, kind="elu1"):
+    return O.nnt_layer_forward(x, Ws[0], bs[0], Ws[1], bs[1], Ws[2], bs[2], Ws[3], bs[3], H, EPS, causal, kind)
+
+
+@pytest.mark.parametrize("kind", ["elu1", "relu", "softmax"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_nnt_layer_matches_bruteforce(kind, causal):
+    x, Ws, bs = _layer_params(70)
+    got = _layer(x, Ws, bs, 4, causal, kind)
+    ref = brute_layer(x, Ws, bs, 4, EPS, causal, kind)
+    assert got.shape == x.shape
+    assert np.abs(got - ref).max() < 1e-11 * max(1.0, np.abs(ref).max())
+
+
+def test_nnt_layer_no_bias_matches_bruteforce():
+    x, Ws, bs = _layer_params(71, B=1, N=17, E=48, H=3, bias=False)
+    assert np.abs(_layer(x, Ws, bs, 3) - brute_layer(x, Ws, bs, 3, EPS)).max() < 1e-11
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_nnt_layer_zero_query_key_projection_closed_form(causal):
+    # phi(0) = 1 for elu + 1, so every score is D: each head returns
+    # D * sum(v) / (D * count + eps) over the visible keys.
+    x, Ws, bs = _layer_params(72, B=1, N=9, E=16, H=2)
+    Ws[0] = np.zeros_like(Ws[0])
+    Ws[1] = np.zeros_like(Ws[1])
+    bs[0] = np.zeros_like(bs[0])
+    bs[1] = np.zeros_like(bs[1])
+    D = 8
+    v = x[0] @ Ws[2] + bs[2]
+    cnt = np.arange(1, 10)[:, None] if causal else np.full((9, 1), 9.0)
+    sums = np.cumsum(v, axis=0) if causal else np.repeat(v.sum(axis=0, keepdims=True), 9, axis=0)
+    heads = D * sums / (D * cnt + EPS)
+    want = heads @ Ws[3] + bs[3]
+    assert np.abs(_layer(x, Ws, bs, 2, causal)[0] - want).max() < 1e-12
+
+
+def test_nnt_layer_head_permutation_invariance():
+    x, Ws, bs = _layer_params(73, E=32, H=4)
+    perm = [2, 0, 3, 1]
+    D = 8
+    cols = np.concatenate([np.arange(h * D, (h + 1) * D) for h in perm])
+    Wp = [W[:, cols] for W in Ws[:3]] + [Ws[3][cols, :]]
+    bp = [b[cols] for b in bs[:3]] + [bs[3]]
+    assert np.abs(_layer(x, Ws, bs, 4) - _layer(x, Wp, bp, 4)).max() < 1e-12
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_linear():
@@ -521,8 +600,28 @@ def _pins_relu():
     test_other_maps_linear_and_causal_match_bruteforce("relu")
 
 
+def _mut_split_heads_interleaved(y, H):
+    B, N, E = y.shape
+    return y.reshape(B, N, E // H, H).transpose(0, 3, 1, 2)
+
+
+def _mut_merge_heads_interleaved(a):
+    B, H, N, D = a.shape
+    return a.transpose(0, 2, 3, 1).reshape(B, N, H * D)
+
+
+def _mut_layer_no_value_bias(x, Wq, bq, Wk, bk, Wv, bv, Wo, bo, H, eps, causal=False, kind="elu1"):
+    return _orig_layer(x, Wq, bq, Wk, bk, Wv, None, Wo, bo, H, eps, causal, kind)
+
+
+def _pins_layer():
+    test_nnt_layer_matches_bruteforce("elu1", False)
+    test_nnt_layer_matches_bruteforce("elu1", True)
+
+
 _orig_landmark = O.landmark_attn
 _orig_blend = O.blend
+_orig_layer = O.nnt_layer_forward
 
 
 @pytest.mark.parametrize("attr,mutant,pins", [
@@ -536,6 +635,9 @@ _orig_blend = O.blend
     ("causal_forward", _mut_causal_exclusive, _pins_causal),
     ("softmax_map", _mut_softmax_token_axis, _pins_softmax),
     ("relu_map", _mut_relu_plus_one, _pins_relu),
+    ("split_heads", _mut_split_heads_interleaved, _pins_layer),
+    ("merge_heads", _mut_merge_heads_interleaved, _pins_layer),
+    ("nnt_layer_forward", _mut_layer_no_value_bias, _pins_layer),
 ])
 def test_planted_mistake_is_caught(monkeypatch, attr, mutant, pins):
     monkeypatch.setattr(O, attr, mutant)
