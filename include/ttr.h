@@ -135,6 +135,36 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
                               int32_t L, int32_t causal, void* out, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* Sizes of the NNT linear-attention layer: x [B,N,E] (batch first), H heads of D = E / H. */
+typedef struct {
+  int32_t B, N, E, H;
+  int32_t dtype; /* ttr_dtype of x, the weights and out */
+  int32_t fmap;  /* ttr_fmap of the attention; 0 (elu + 1) when zero-initialised */
+} ttr_layer_dims;
+
+/* NNT linear-attention layer, inference forward (dropout is the identity):
+ *   Q = x Wq + bq, K = x Wk + bk, V = x Wv + bv    (W* [E,E] in the IO dtype,
+ *                                                   input rows, output columns; b* [E] fp32 or NULL)
+ *   head h takes columns h*D .. h*D + D - 1; per head the linear attention of
+ *   ttr_hybrid_forward with W == NULL, b == NULL, L == 0 (causal: that of
+ *   ttr_causal_scan), feature map d.fmap;
+ *   out = merged heads . Wo + bo                  ([B,N,E], IO dtype).
+ * "NNT Define Linear Attention", "The inputs" (embed_dim, num_heads,
+ * feature_map, eps, causal, batch_first) and "How it works" (project Q/K/V,
+ * feature map, K'^T V first, normalise, project back out).
+ * Shape rules: B, N, H >= 1; E % 128 == 0; E % H == 0; D = E / H in {64, 128}
+ * (64 for fp32); B*N*E < 2^31; B*H <= 65535.
+ * ws: at least ttr_nnt_layer_workspace_bytes(d, causal) bytes (transposed
+ * weights, Q/K/V and the attention output in [B,H,N,D], and the attention's
+ * own workspace); its contents on entry do not matter. */
+ttr_status ttr_nnt_layer_forward(ttr_layer_dims d, const void* x, const void* Wq, const float* bq,
+                                 const void* Wk, const float* bk, const void* Wv, const float* bv,
+                                 const void* Wo, const float* bo, float eps, int32_t causal, void* out,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace size in bytes of ttr_nnt_layer_forward (0 if the shape is invalid). */
+size_t ttr_nnt_layer_workspace_bytes(ttr_layer_dims d, int32_t causal);
+
 /* Workspace size in bytes for the given call shape (0 if the shape is invalid). */
 size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk);
 

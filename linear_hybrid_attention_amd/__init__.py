@@ -52,6 +52,11 @@ class Dims(ctypes.Structure):
                 ("fmap", ctypes.c_int32)]
 
 
+class LayerDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("dtype", ctypes.c_int32), ("fmap", ctypes.c_int32)]
+
+
 # feature maps (ttr_fmap): elu(x) + 1, relu, softmax over the features
 FMAPS = {"elu1": 0, "relu": 1, "softmax": 2}
 
@@ -72,6 +77,8 @@ _SIGS = {
     "ttr_causal_scan": [Dims, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
     "ttr_hybrid_forward": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                            _P, _P, ctypes.c_size_t, _P],
+    "ttr_nnt_layer_forward": [LayerDims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
+                              _P, _P, ctypes.c_size_t, _P],
 }
 
 _lib = None
@@ -93,6 +100,8 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.ttr_workspace_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.ttr_workspace_bytes.restype = ctypes.c_size_t
+    lib.ttr_nnt_layer_workspace_bytes.argtypes = [LayerDims, ctypes.c_int32]
+    lib.ttr_nnt_layer_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_status_string.argtypes = [ctypes.c_int]
     lib.ttr_status_string.restype = ctypes.c_char_p
     lib.ttr_last_hip_error.argtypes = []
@@ -278,4 +287,37 @@ def hybrid_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: Optiona
                                 float(eps), int(L), int(causal), _dev(out, "out", Q.dtype),
                                 None if ws is None else ws.data_ptr(), wsb, _stream(Q))
     _check(st, "ttr_hybrid_forward")
+    return out
+
+
+def nnt_layer_workspace_bytes(B: int, N: int, E: int, H: int, dtype: int, causal: bool = False,
+                              fmap: str = "elu1") -> int:
+    return int(load_library().ttr_nnt_layer_workspace_bytes(LayerDims(B, N, E, H, dtype, _fmap(fmap)), int(causal)))
+
+
+def nnt_layer_forward(x: torch.Tensor, Wq: torch.Tensor, bq: Optional[torch.Tensor], Wk: torch.Tensor,
+                      bk: Optional[torch.Tensor], Wv: torch.Tensor, bv: Optional[torch.Tensor], Wo: torch.Tensor,
+                      bo: Optional[torch.Tensor], H: int, eps: float = 1e-6, causal: bool = False,
+                      fmap: str = "elu1", out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """NNT linear-attention layer forward, x [B, N, E] -> [B, N, E] in x's dtype
+    (ttr_nnt_layer_forward). W* are [E, E] (x @ W), b* are [E] float32 or None."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, E]")
+    B, N, E = x.shape
+    d = LayerDims(B, N, E, int(H), _io_dtype(x), _fmap(fmap))
+    if out is None:
+        out = torch.empty_like(x)
+    need = lib.ttr_nnt_layer_workspace_bytes(d, int(causal))
+    if need == 0:
+        raise TTRError(2, "ttr_nnt_layer_forward", "invalid layer shape")
+    ws, wsb = _workspace(d, need, x, ws)
+    f32 = torch.float32
+    st = lib.ttr_nnt_layer_forward(d, _dev(x, "x"), _dev(Wq, "Wq", x.dtype), _dev(bq, "bq", f32),
+                                   _dev(Wk, "Wk", x.dtype), _dev(bk, "bk", f32), _dev(Wv, "Wv", x.dtype),
+                                   _dev(bv, "bv", f32), _dev(Wo, "Wo", x.dtype), _dev(bo, "bo", f32), float(eps),
+                                   int(causal), _dev(out, "out", x.dtype), None if ws is None else ws.data_ptr(), wsb,
+                                   _stream(x))
+    _check(st, "ttr_nnt_layer_forward")
     return out

@@ -307,4 +307,74 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
   return st;
 }
 
+// ---------------------------------------------------------------- NNT layer
+// Workspace: Wqkv^T [3E][E] | Wo^T [E][E] | Q | K | V | attention out (each
+// [B,H,N,D]) | the attention's workspace; regions 256-byte aligned.
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t ttr_nnt_layer_workspace_bytes(ttr_layer_dims d, int32_t causal) {
+  ttr_dims c;
+  if (check_layer(d, &c) != TTR_OK) return 0;
+  const size_t es = dtype_bytes(d.dtype), E = (size_t)d.E, act = (size_t)d.B * d.N * E * es;
+  return align256(3 * E * E * es) + align256(E * E * es) + 4 * align256(act) +
+         ttr_workspace_bytes(c, 0, causal ? 1 : 0, 0);
+}
+
+ttr_status ttr_nnt_layer_forward(ttr_layer_dims d, const void* x, const void* Wq, const float* bq, const void* Wk,
+                                 const float* bk, const void* Wv, const float* bv, const void* Wo, const float* bo,
+                                 float eps, int32_t causal, void* out, void* ws, size_t ws_bytes, void* stream) {
+  ttr_dims c;
+  TTR_TRY(check_layer(d, &c));
+  if (causal && causal_default_chunk(c.dtype, c.D) == 0) return TTR_ERR_UNSUPPORTED;
+  TTR_TRY(check_ptr(x));
+  TTR_TRY(check_ptr(Wq));
+  TTR_TRY(check_ptr(Wk));
+  TTR_TRY(check_ptr(Wv));
+  TTR_TRY(check_ptr(Wo));
+  TTR_TRY(check_ptr(out));
+  TTR_TRY(check_opt_ptr(bq));
+  TTR_TRY(check_opt_ptr(bk));
+  TTR_TRY(check_opt_ptr(bv));
+  TTR_TRY(check_opt_ptr(bo));
+  const size_t need = ttr_nnt_layer_workspace_bytes(d, causal);
+  if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
+  TTR_TRY(check_ptr(ws));
+  const size_t es = dtype_bytes(d.dtype), E = (size_t)d.E, act = (size_t)d.B * d.N * E * es;
+  const size_t wb = E * E * es, bb = E * sizeof(float);
+  const Range outs[] = {{out, act}, {ws, need}};
+  const Range ins[] = {{x, act}, {Wq, wb}, {Wk, wb}, {Wv, wb}, {Wo, wb},
+                       {bq, bq ? bb : 0}, {bk, bk ? bb : 0}, {bv, bv ? bb : 0}, {bo, bo ? bb : 0}};
+  TTR_TRY(check_no_alias(outs, 2, ins, 9));
+
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  void* wqkv_t = w8;
+  w8 += align256(3 * wb);
+  void* wo_t = w8;
+  w8 += align256(wb);
+  void* qkv[3];
+  for (int i = 0; i < 3; ++i) {
+    qkv[i] = w8;
+    w8 += align256(act);
+  }
+  void* attn = w8;
+  w8 += align256(act);
+  void* core_ws = w8;
+  const size_t core_bytes = need - (size_t)(w8 - static_cast<unsigned char*>(ws));
+
+  hipStream_t s = (hipStream_t)stream;
+  const int M = d.B * d.N, D = c.D;
+  const void* wqkv[3] = {Wq, Wk, Wv};
+  TTR_TRY(hip_status(launch_wt_transpose(d.dtype, wqkv, 3, d.E, d.E, wqkv_t, s)));
+  TTR_TRY(hip_status(launch_wt_transpose(d.dtype, &Wo, 1, d.E, d.E, wo_t, s)));
+  const float* bqkv[3] = {bq, bk, bv};
+  TTR_TRY(hip_status(launch_proj_gemm(d.dtype, false, true, x, wqkv_t, bqkv, qkv, M, d.E, 3 * d.E, d.N, d.H, D,
+                                      d.E, s)));
+  TTR_TRY(ttr_hybrid_forward(c, qkv[0], qkv[1], qkv[2], nullptr, nullptr, nullptr, eps, 0, causal ? 1 : 0, attn,
+                             core_ws, core_bytes, stream));
+  const float* bo3[3] = {bo, nullptr, nullptr};
+  void* out3[3] = {out, nullptr, nullptr};
+  return hip_status(
+      launch_proj_gemm(d.dtype, true, false, attn, wo_t, bo3, out3, M, d.E, d.E, d.N, d.H, D, d.E, s));
+}
+
 }  // extern "C"

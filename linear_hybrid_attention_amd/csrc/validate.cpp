@@ -85,4 +85,26 @@ ttr_status check_causal(const ttr_dims& d, const void* W, int32_t L, int32_t chu
   return TTR_OK;
 }
 
+ttr_status check_layer(const ttr_layer_dims& d, ttr_dims* core) {
+  if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
+  if (d.fmap < TTR_FMAP_ELU1 || d.fmap > TTR_FMAP_SOFTMAX) return TTR_ERR_SHAPE;
+  if (d.B < 1 || d.N < 1 || d.H < 1 || d.E < 1) return TTR_ERR_SHAPE;
+  if (d.E % d.H != 0) return TTR_ERR_SHAPE;  // embed_dim divides by num_heads
+  // projection tiles are 128 columns wide
+  if (d.E % 128 != 0) return TTR_ERR_UNSUPPORTED;
+  if ((int64_t)d.B * d.N * d.E >= ((int64_t)1 << 31)) return TTR_ERR_UNSUPPORTED;
+  ttr_dims c;
+  c.B = d.B;
+  c.H = d.H;
+  c.N = d.N;
+  c.D = d.E / d.H;
+  c.F = c.D;
+  c.dtype = d.dtype;
+  c.fmap = d.fmap;
+  const ttr_status st = check_dims(c, false);
+  if (st != TTR_OK) return st == TTR_ERR_SHAPE ? TTR_ERR_UNSUPPORTED : st;  // D outside {64, 128}: a valid layer not implemented
+  *core = c;
+  return TTR_OK;
+}
+
 }  // namespace ttr

@@ -33,6 +33,10 @@ ttr_status check_no_alias(const Range* outs, int nout, const Range* ins, int nin
 // Causal rules: identity map only, no landmarks, a supported chunk size.
 ttr_status check_causal(const ttr_dims& d, const void* W, int32_t L, int32_t chunk);
 
+// NNT layer shape rules (see ttr_nnt_layer_forward); on success *core holds
+// the per-head attention's dims (F = D, no projection).
+ttr_status check_layer(const ttr_layer_dims& d, ttr_dims* core);
+
 // Largest supported causal chunk <= 256 for this dtype and head dim (0 if none).
 int32_t causal_default_chunk(int32_t dtype, int32_t D);
 

@@ -116,6 +116,38 @@ def test_feature_map_kind_validation(lib):
     assert lib.ttr_workspace_bytes(Dm(2, F=256, dt=1), 0, 0, 0) == 0
 
 
+def test_nnt_layer_validation(lib):
+    big = 1 << 40
+
+    def LD(B=2, N=100, E=512, H=8, dt=1, fmap=0):
+        return ttr.LayerDims(B, N, E, H, dt, fmap)
+
+    def layer(d, x=big, Wq=2 * big, Wk=3 * big, Wv=4 * big, Wo=5 * big, bq=None, out=6 * big, ws=7 * big,
+              wsb=1 << 34, causal=0):
+        return lib.ttr_nnt_layer_forward(d, x, Wq, bq, Wk, None, Wv, None, Wo, None, 1e-6, causal, out, ws, wsb,
+                                         None)
+
+    assert layer(LD(dt=5)) == DTYPE
+    assert layer(LD(fmap=3)) == SHAPE
+    assert layer(LD(B=0)) == SHAPE
+    assert layer(LD(E=512, H=3)) == SHAPE          # embed_dim must divide by num_heads
+    assert layer(LD(E=192, H=3)) == UNSUP          # E not a multiple of 128
+    assert layer(LD(E=512, H=16)) == UNSUP         # D = 32
+    assert layer(LD(E=512, H=4, dt=0)) == UNSUP    # fp32 needs D = 64
+    assert layer(LD(), x=None) == NULL
+    assert layer(LD(), Wo=None) == NULL
+    assert layer(LD(), Wq=big + 8) == ALIGN
+    assert layer(LD(), bq=big + 4) == ALIGN
+    assert layer(LD(), wsb=16) == WS
+    assert layer(LD(), ws=None) == WS
+    assert layer(LD(), out=big + 64) == ALIAS        # out overlaps x
+    assert lib.ttr_nnt_layer_workspace_bytes(LD(), 0) > lib.ttr_nnt_layer_workspace_bytes(LD(N=10), 0)
+    assert lib.ttr_nnt_layer_workspace_bytes(LD(H=3), 0) == 0
+    # the layer's workspace holds the transposed weights, Q, K, V and the attention output
+    ws = lib.ttr_nnt_layer_workspace_bytes(LD(B=1, N=256, E=512, H=8), 1)
+    assert ws >= 4 * 512 * 512 * 2 + 4 * 256 * 512 * 2
+
+
 def test_causal_scan_validation(lib):
     big = 1 << 40
     d = D(B=8, H=8, N=32768, Dm=64, F=64, dt=1)

@@ -19,6 +19,15 @@ Distributions: Q, K, V ~ N(0, 1); W_h ~ N(0, 1/D) (variance notation, so the
 standard deviation is 1/sqrt(D)); b_h ~ N(0, 0.01) (std 0.1) except the tiny
 config where b_h = 0; g_h ~ N(0, 1); eps = 1e-6 (the fp32 value).
 
+NNT layer workloads ("NNT Define Linear Attention", section "The inputs":
+embed_dim 512, num_heads 8; the page fixes no sequence length, so N = 4096
+tokens, B = 8 are chosen): x ~ N(0, 1) [B, N, E]; Wq, Wk, Wv, Wo ~ N(0, 1/E)
+[E, E]; bq, bk, bv, bo ~ N(0, 0.01) [E]; drawn in that order; bf16 rounds x
+and the four W (the biases stay fp32).
+
+  nnt_layer         B=8 N=4096 E=512 H=8 bf16, elu + 1, not causal
+  nnt_layer_causal  the same, causal
+
 Draw order: Q, K, V, W, b, g from numpy's PCG64 ``default_rng(seed)`` with
 ``standard_normal(dtype=float32)`` scaled by the std. bf16 workloads round
 every IO tensor (Q, K, V, W) to bfloat16 with round-to-nearest-even; b and g
@@ -31,7 +40,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "bf16_round_bits", "bf16_bits_to_f32"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "bf16_round_bits", "bf16_bits_to_f32",
+           "LayerWorkload", "LAYER_WORKLOADS", "make_layer_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -114,6 +124,57 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
             if out[k] is None:
                 out[k + "_bits"] = None
                 continue
+            bits = bf16_round_bits(out[k])
+            out[k + "_bits"] = bits
+            out[k] = bf16_bits_to_f32(bits)
+    elif w.dtype != "fp32":
+        raise ValueError(f"unknown dtype {w.dtype!r}")
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerWorkload:
+    name: str
+    B: int
+    N: int
+    E: int
+    H: int
+    dtype: str  # "fp32" or "bf16"
+    causal: bool
+    fmap: str  # "elu1", "relu" or "softmax"
+    seed: int
+    b_std: float = 0.1
+    eps: float = 1e-6
+
+    def with_(self, **kw) -> "LayerWorkload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.N
+
+
+LAYER_WORKLOADS = {
+    "nnt_layer": LayerWorkload("nnt_layer", 8, 4096, 512, 8, "bf16", False, "elu1", 1005),
+    "nnt_layer_causal": LayerWorkload("nnt_layer_causal", 8, 4096, 512, 8, "bf16", True, "elu1", 1006),
+}
+
+
+def make_layer_inputs(w: LayerWorkload, seed: Optional[int] = None, bias: bool = True) -> dict:
+    """Draw one seeded input set for layer workload ``w``: fp32 arrays ``x``
+    [B,N,E], ``Wq Wk Wv Wo`` [E,E], ``bq bk bv bo`` [E] (None without bias),
+    ``eps`` and, for bf16, the uint16 bit patterns ``x_bits`` and ``W*_bits``.
+    The fp32 arrays hold the values after rounding to the IO dtype."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    out: dict = {"x": rng.standard_normal((w.B, w.N, w.E), dtype=np.float32)}
+    ws = np.float32(1.0 / np.sqrt(w.E))
+    for k in ("Wq", "Wk", "Wv", "Wo"):
+        out[k] = rng.standard_normal((w.E, w.E), dtype=np.float32) * ws
+    for k in ("bq", "bk", "bv", "bo"):
+        out[k] = rng.standard_normal((w.E,), dtype=np.float32) * np.float32(w.b_std) if bias else None
+    out["eps"] = np.float32(w.eps)
+    if w.dtype == "bf16":
+        for k in ("x", "Wq", "Wk", "Wv", "Wo"):
             bits = bf16_round_bits(out[k])
             out[k + "_bits"] = bits
             out[k] = bf16_bits_to_f32(bits)
