@@ -87,15 +87,15 @@ def write_traffic(run_dir, wl, copy_mib):
     copy_bytes = copy_mib << 20
     f_scale = copy_bytes / (cf[copy_name] * 1024.0)
     w_scale = copy_bytes / (cw[copy_name] * 1024.0)
-    w = workloads.WORKLOADS[wl]
+    layer = wl in workloads.LAYER_WORKLOADS
+    w = workloads.LAYER_WORKLOADS[wl] if layer else workloads.WORKLOADS[wl]
     out = {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             out = json.load(f)
     ent = {}
-    for name, _, _ in kernel_plan(w):
-        full = [k for k in fetch if k.split("(")[0].replace("void ttr::", "") in (name, name + "<")
-                or k.split("(")[0].replace("void ttr::", "").split("<")[0] == name]
+    for name, _, _ in (layer_plan(w) if layer else kernel_plan(w)):
+        full = [k for k in fetch if trace_name_matches(name, k)]
         if not full or full[0] not in write:
             continue
         kname = full[0]
@@ -110,9 +110,25 @@ def write_traffic(run_dir, wl, copy_mib):
     print(json.dumps(out[w.name], indent=1))
 
 
+def trace_name_matches(plan_name, trace_name):
+    """Whether a profiler's kernel name is the dispatch a plan entry names.
+
+    Plan entries name a kernel, a kernel with its template arguments, or a
+    projection by role ("proj_gemm_kernel (qkv)": A rows -> Q/K/V heads,
+    "(out)": A heads -> rows)."""
+    t = trace_name.split("(")[0].replace("void ttr::", "").strip()
+    roles = {" (qkv)": ", 0, 1>", " (out)": ", 1, 0>"}
+    for suffix, targs in roles.items():
+        if plan_name.endswith(suffix):
+            return t.startswith(plan_name[:-len(suffix)] + "<") and t.endswith(targs)
+    return t in (plan_name, plan_name + "<") or t.split("<")[0] == plan_name
+
+
 def kernel_sources(name):
     """Source files a kernel is built from (a change to any of them voids stored counters)."""
     common = ["common.hpp", "tiles.hpp", "launch.hpp"]
+    if name.startswith("proj_gemm") or name.startswith("wt_transpose"):
+        return ["k_proj.hip"] + common
     if name.startswith("kv2_"):
         return ["k_kv2.hip"] + common
     if name.startswith("fused_"):
@@ -233,6 +249,156 @@ def cpu_baseline(w, x, target_s):
             "sample": sample, "seconds_full_estimate": sec_full}
 
 
+def layer_plan(w):
+    """Kernels of one NNT layer forward in launch order (name, algorithmic flops, bytes).
+
+    The projections count their matrix products and the activations the method
+    must read or write (x in, out back); Q, K, V and the attention output in
+    between are the design's staging, as are the transposed weights."""
+    import workloads
+    io = 2 if w.dtype == "bf16" else 4
+    M, E = w.B * w.N, w.E
+    core = workloads.Workload(w.name, w.B, w.H, w.N, E // w.H, E // w.H, w.dtype, 0, w.causal, False, 0.0, 0.0, 0)
+    plan = [("wt_transpose_kernel", 0, 0),
+            ("proj_gemm_kernel (qkv)", 2 * M * E * 3 * E, M * E * io)]
+    for name, fl, by in kernel_plan(core):
+        if name.startswith("kv2_partial"):  # identity map: the method has no projection flops here
+            fl = core.B * core.H * (2 * core.N * core.D * core.D + core.N * core.D)
+        if name.startswith("fused_query"):
+            fl = core.B * core.H * (2 * core.N * core.D * core.D + 2 * core.N * core.D)
+        plan.append((name, fl, by))
+    plan.append(("proj_gemm_kernel (out)", 2 * M * E * E, M * E * io))
+    return plan
+
+
+def cpu_baseline_layer(w, x, target_s):
+    """The oracle layer on the first sequences of the same inputs, repeated to about target_s seconds."""
+    import oracle.ttr_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+
+    def run(nb):
+        t0 = time.perf_counter()
+        O.nnt_layer_forward(x["x"][:nb], x["Wq"], x["bq"], x["Wk"], x["bk"], x["Wv"], x["bv"], x["Wo"], x["bo"],
+                            w.H, x["eps"], w.causal, w.fmap)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nb = int(max(1, min(w.B, target_s / max(t1, 1e-3))))
+    t = run(nb) if nb > 1 else t1
+    reps, total = 1, t
+    while total < target_s and reps < 64:
+        total += run(nb)
+        reps += 1
+    t = total / reps
+    sec_full = t * w.B / nb
+    sample = (f"{nb} of {w.B} sequences of the {w.name} workload (N={w.N}, E={w.E}), fp64 numpy oracle, "
+              f"{reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all sequences")
+    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds_full_estimate": sec_full}
+
+
+def main_layer(args):
+    import ctypes
+    import numpy as np
+    import torch
+    import linear_hybrid_attention_amd as ttr
+    import workloads
+
+    w = workloads.LAYER_WORKLOADS[args.workload]
+    x = workloads.make_layer_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def io(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x[name]).to(dev)
+
+    X, Wq, Wk, Wv, Wo = (io(k) for k in ("x", "Wq", "Wk", "Wv", "Wo"))
+    bq, bk, bv, bo = (torch.from_numpy(x[k]).to(dev) for k in ("bq", "bk", "bv", "bo"))
+    out = torch.empty_like(X)
+    lib = ttr.load_library()
+    nbytes = ttr.nnt_layer_workspace_bytes(w.B, w.N, w.E, w.H, 1 if w.dtype == "bf16" else 0, w.causal, w.fmap)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = layer_plan(w)
+
+    def step(events=None):
+        if events is not None:
+            lib.ttr_set_stage_events(events, len(plan) + 1)
+        ttr.nnt_layer_forward(X, Wq, bq, Wk, bk, Wv, bv, Wo, bo, w.H, float(x["eps"]), w.causal, w.fmap,
+                              out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nev = len(plan) + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in ev]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    for i in range(args.steps):
+        step(handles[i])
+    torch.cuda.synchronize()
+    kern_ms = {name: float(np.mean([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)]))
+               for k, (name, _, _) in enumerate(plan)}
+    name, flops, nb = max(plan, key=lambda p: kern_ms[p[0]])
+    rl = roofline(w, flops, nb, kern_ms[name])
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            ent = json.load(f).get(w.name, {}).get(name)
+        if ent and ent.get("source_hash") == source_hash(ent["sources"]):
+            traffic = ent["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+    kernels = {}
+    for kn, kf, kb in plan:
+        r = roofline(w, kf, kb, kern_ms[kn]) if (kf or kb) else {"bound": None, "frac": None}
+        kernels[kn] = {"ms": kern_ms[kn], "flops": kf, "bytes": kb, "bound": r["bound"], "frac": r["frac"]}
+    total_flops = sum(p[1] for p in plan)
+    peak_fwd = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    io_b = 2 if w.dtype == "bf16" else 4
+    act_bytes = 2 * w.B * w.N * w.E * io_b  # x read, out written
+    res = {
+        "metric": f"NNT linear-attention layer tokens/sec (B={w.B}, N={w.N}, E={w.E}, {w.H} heads"
+                  f"{', causal' if w.causal else ''})",
+        "value": w.B * w.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "E": w.E, "H": w.H, "D": w.E // w.H,
+                   "feature_map": w.fmap, "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
+        "roofline": {"kernel": name, "bound": rl["bound"], "achieved": rl["achieved"], "peak": rl["peak"],
+                     "unit": rl["unit"], "frac": rl["frac"], "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nb,
+                     "avg_launch_ms": kern_ms[name]},
+        "forward": {"tflops": total_flops / (ms * 1e-3) / 1e12,
+                    "frac_mfma_peak": total_flops / (ms * 1e-3) / 1e12 / peak_fwd,
+                    "algorithmic_bytes": act_bytes,
+                    "frac_hbm_peak": act_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "kernels": kernels, "wall_s": wall},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_layer(w, x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -251,6 +417,9 @@ def main():
     import linear_hybrid_attention_amd as ttr
     import workloads
 
+    if args.workload in workloads.LAYER_WORKLOADS:
+        main_layer(args)
+        return
     w = workloads.WORKLOADS[args.workload]
     x = workloads.make_inputs(w)
     dev = torch.device("cuda:0")

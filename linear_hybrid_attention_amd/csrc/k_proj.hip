@@ -142,18 +142,25 @@ __global__ __launch_bounds__(256, 2) void proj_gemm_kernel(ProjArgs a) {
     if (ks + 1 < nks) issue(ks + 1);  // workgroup-uniform
     const T* wt_s = ring + (ks & 1) * 2 * ELEMS;
     const T* a_s = wt_s + ELEMS;
+    // Fixed order: four MFMA slots per k-block (Wt tile j, A tile i); each
+    // slot also reads one of the next k-block's four operands, so the LDS
+    // latency overlaps the matrix core.
+    constexpr int NKB = KT / 16;
+    auto ld = [&](int kb, int q) {  // q 0, 1: Wt tiles; 2, 3: A tiles
+      return q < 2 ? ld_tile_frag<T>(wt_s, wn * 64 + q * 32 + c, kb * 16 + 8 * g)
+                   : ld_tile_frag<T>(a_s, wm * 64 + (q - 2) * 32 + c, kb * 16 + 8 * g);
+    };
+    Frag<T> f[NKB][4];
 #pragma unroll
-    for (int kb = 0; kb < KT / 16; ++kb) {
-      Frag<T> fw[2], fa[2];
+    for (int q = 0; q < 4; ++q) f[0][q] = ld(0, q);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fw[j] = ld_tile_frag<T>(wt_s, wn * 64 + j * 32 + c, kb * 16 + 8 * g);
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = ld_tile_frag<T>(a_s, wm * 64 + i * 32 + c, kb * 16 + 8 * g);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) mma(acc[j][i], fw[j], fa[i]);
-    }
+      for (int sl = 0; sl < 4; ++sl) {
+        if (kb + 1 < NKB) f[kb + 1][sl] = ld(kb + 1, sl);
+        mma(acc[sl >> 1][sl & 1], f[kb][sl >> 1], f[kb][2 + (sl & 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
   barrier_lds();  // the ring becomes the output tile
 
@@ -200,25 +207,38 @@ __global__ __launch_bounds__(256, 2) void proj_gemm_kernel(ProjArgs a) {
   }
 }
 
-// Wt[n][k] = W[k][n] for one [rows x cols] matrix per blockIdx.z, written at
-// row offset z * cols of the output (so q, k, v stack into one [3E][E]).
+// Wt[n][k] = W[k][n] for up to four [E x E] matrices (blockIdx.z), 64 x 64
+// tiles through LDS, 16-byte loads and stores.
 struct TransposeArgs {
   const void* W[4];
-  void* Wt;
-  int rows, cols;  // of each W
+  void* Wt[4];
+  int E;
 };
 
 template <typename T>
 __global__ __launch_bounds__(256) void wt_transpose_kernel(TransposeArgs a) {
-  __shared__ T tile[32][33];
-  const int z = blockIdx.z;
+  constexpr int P = 16 / sizeof(T);  // elements per 16-byte piece
+  __shared__ T tile[64][64 + 1];
+  const int z = blockIdx.z, E = a.E;
   const T* W = static_cast<const T*>(a.W[z]);
-  T* Wt = static_cast<T*>(a.Wt) + (size_t)z * a.cols * a.rows;
-  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int y = ty; y < 32; y += 8) tile[y][tx] = W[(size_t)(r0 + y) * a.cols + c0 + tx];
+  T* Wt = static_cast<T*>(a.Wt[z]);
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int u = threadIdx.x; u < 64 * (64 / P); u += 256) {
+    const int r = u / (64 / P), pc = (u % (64 / P)) * P;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(W + (size_t)(r0 + r) * E + c0 + pc);
+    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int j = 0; j < P; ++j) tile[r][pc + j] = e[j];
+  }
   __syncthreads();
-  for (int y = ty; y < 32; y += 8) Wt[(size_t)(c0 + y) * a.rows + r0 + tx] = tile[tx][y];
+  for (int u = threadIdx.x; u < 64 * (64 / P); u += 256) {
+    const int cc = u / (64 / P), pr = (u % (64 / P)) * P;  // output row c0 + cc, columns r0 + pr ..
+    u32x4 v;
+    T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+    for (int j = 0; j < P; ++j) e[j] = tile[pr + j][cc];
+    *reinterpret_cast<u32x4*>(Wt + (size_t)(c0 + cc) * E + r0 + pr) = v;
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -228,14 +248,14 @@ static hipError_t launch_proj_t(ProjArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_wt_transpose(int dtype, const void* const* W, int nmat, int rows, int cols, void* Wt,
-                               hipStream_t s) {
+hipError_t launch_wt_transpose(int dtype, const void* const* W, void* const* Wt, int nmat, int E, hipStream_t s) {
   TransposeArgs a;
-  for (int i = 0; i < 4; ++i) a.W[i] = i < nmat ? W[i] : nullptr;
-  a.Wt = Wt;
-  a.rows = rows;
-  a.cols = cols;
-  const dim3 grid(cols / 32, rows / 32, nmat);
+  for (int i = 0; i < 4; ++i) {
+    a.W[i] = i < nmat ? W[i] : nullptr;
+    a.Wt[i] = i < nmat ? Wt[i] : nullptr;
+  }
+  a.E = E;
+  const dim3 grid(E / 64, E / 64, nmat);
   if (dtype == 1) hipLaunchKernelGGL((wt_transpose_kernel<uint16_t>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((wt_transpose_kernel<float>), grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -87,8 +87,7 @@ hipError_t launch_causal(const Problem& p, const void* Q, const void* K, const v
                          float eps, int chunk, void* out, void* ws, hipStream_t s, StageTimer* t);
 
 // NNT layer projections (k_proj.hip)
-hipError_t launch_wt_transpose(int dtype, const void* const* W, int nmat, int rows, int cols, void* Wt,
-                               hipStream_t s);
+hipError_t launch_wt_transpose(int dtype, const void* const* W, void* const* Wt, int nmat, int E, hipStream_t s);
 hipError_t launch_proj_gemm(int dtype, bool a_heads, bool c_qkv, const void* A, const void* Wt,
                             const float* const* bias, void* const* out, int M, int K, int Nc, int Ntok, int H,
                             int D, int E, hipStream_t s);

@@ -212,8 +212,12 @@ ttr_status ttr_blend(ttr_dims d, const float* out_lin, const float* out_lm, cons
   return hip_status(launch_blend(make_problem(d, false), out_lin, out_lm, g, out, (hipStream_t)stream));
 }
 
-ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void* V, const void* W, const float* b,
-                           float eps, int32_t chunk, void* out, void* ws, size_t ws_bytes, void* stream) {
+// The bodies of ttr_causal_scan and ttr_hybrid_forward. `outer` is the
+// stage timer of an enclosing entry point (the layer), or NULL: then the call
+// takes the thread's registration itself, after validation, and finishes it.
+static ttr_status causal_scan_impl(ttr_dims d, const void* Q, const void* K, const void* V, const void* W,
+                                   const float* b, float eps, int32_t chunk, void* out, void* ws, size_t ws_bytes,
+                                   hipStream_t s, StageTimer* outer) {
   if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
   if (W != nullptr) return TTR_ERR_UNSUPPORTED;  // the causal variant has no projection
   TTR_TRY(check_dims(d, false));
@@ -232,25 +236,29 @@ ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void*
   const Range outs[] = {{out, qkv_bytes(d)}, {ws, need}};
   const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {b, b ? b_bytes(d) : 0}};
   TTR_TRY(check_no_alias(outs, 2, ins, 4));
-  hipStream_t s = (hipStream_t)stream;
-  StageTimer t = take_stage_timer(s);
+  StageTimer own;
+  StageTimer* t = outer;
+  if (t == nullptr) {
+    own = take_stage_timer(s);
+    t = &own;
+  }
   const ttr_status st = hip_status(causal2_supported(p, chunk)
-                                       ? launch_causal2(p, Q, K, V, b, eps, chunk, out, ws, s, &t)
-                                       : launch_causal(p, Q, K, V, b, eps, chunk, out, ws, s, &t));
-  t.finish();
+                                       ? launch_causal2(p, Q, K, V, b, eps, chunk, out, ws, s, t)
+                                       : launch_causal(p, Q, K, V, b, eps, chunk, out, ws, s, t));
+  if (outer == nullptr) t->finish();
   return st;
 }
 
-ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const void* V, const void* W,
-                              const float* b, const float* g, float eps, int32_t L, int32_t causal, void* out,
-                              void* ws, size_t ws_bytes, void* stream) {
+static ttr_status hybrid_forward_impl(ttr_dims d, const void* Q, const void* K, const void* V, const void* W,
+                                      const float* b, const float* g, float eps, int32_t L, int32_t causal,
+                                      void* out, void* ws, size_t ws_bytes, hipStream_t s, StageTimer* outer) {
   if (causal) {
     if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
     if (W != nullptr || L != 0) return TTR_ERR_UNSUPPORTED;
     TTR_TRY(check_dims(d, false));
     const int32_t chunk = causal_default_chunk(d.dtype, d.D);
     if (chunk == 0) return TTR_ERR_UNSUPPORTED;
-    return ttr_causal_scan(d, Q, K, V, W, b, eps, chunk, out, ws, ws_bytes, stream);
+    return causal_scan_impl(d, Q, K, V, W, b, eps, chunk, out, ws, ws_bytes, s, outer);
   }
   const bool proj = W != nullptr;
   TTR_TRY(check_dims(d, proj));
@@ -272,14 +280,19 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
                        {b, b ? b_bytes(d) : 0}, {g, (L > 0) ? (size_t)d.H * sizeof(float) : 0}};
   TTR_TRY(check_no_alias(outs, 2, ins, 6));
 
-  hipStream_t s = (hipStream_t)stream;
-  StageTimer t = take_stage_timer(s);
+  StageTimer own;
+  StageTimer* t = outer;
+  if (t == nullptr) {
+    own = take_stage_timer(s);
+    t = &own;
+  }
   if (d.dtype == TTR_BF16) {
     // split-N key/value reduction + operand pack, then the fused query kernel
     FusedPack pk;
-    TTR_TRY(hip_status(launch_kv2(p, K, V, W, b, L, ws, &pk, s, &t)));
+    TTR_TRY(hip_status(launch_kv2(p, K, V, W, b, L, ws, &pk, s, t)));
     const ttr_status st = hip_status(launch_fused_query(p, Q, pk, g, eps, L, out, s));
-    t.finish();
+    t->mark();
+    if (outer == nullptr) t->finish();
     return st;
   }
   // fp32: KV [B,H,F,D] fp32 | ksum [B,H,F] fp32 | split partials, then the generic query kernel
@@ -287,7 +300,7 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
   float* ksum = KV + (size_t)d.B * d.H * d.F * d.D;
   void* part = ksum + (size_t)d.B * d.H * d.F;
   TTR_TRY(hip_status(launch_kv_reduce(p, K, V, W, b, KV, ksum, part, s)));
-  t.mark();
+  t->mark();
   HybridArgs a = {};
   a.Q = Q;
   a.K = K;
@@ -303,8 +316,20 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
   a.L = L;
   a.out = out;
   const ttr_status st = hip_status(launch_hybrid(p, L > 0 ? (M_LIN | M_LM) : M_LIN, true, a, s));
-  t.finish();
+  t->mark();
+  if (outer == nullptr) t->finish();
   return st;
+}
+
+ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void* V, const void* W, const float* b,
+                           float eps, int32_t chunk, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return causal_scan_impl(d, Q, K, V, W, b, eps, chunk, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const void* V, const void* W,
+                              const float* b, const float* g, float eps, int32_t L, int32_t causal, void* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return hybrid_forward_impl(d, Q, K, V, W, b, g, eps, L, causal, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 
 // ---------------------------------------------------------------- NNT layer
@@ -362,19 +387,25 @@ ttr_status ttr_nnt_layer_forward(ttr_layer_dims d, const void* x, const void* Wq
   const size_t core_bytes = need - (size_t)(w8 - static_cast<unsigned char*>(ws));
 
   hipStream_t s = (hipStream_t)stream;
+  StageTimer t = take_stage_timer(s);  // stages: transposes, QKV projection, attention kernels, out projection
   const int M = d.B * d.N, D = c.D;
-  const void* wqkv[3] = {Wq, Wk, Wv};
-  TTR_TRY(hip_status(launch_wt_transpose(d.dtype, wqkv, 3, d.E, d.E, wqkv_t, s)));
-  TTR_TRY(hip_status(launch_wt_transpose(d.dtype, &Wo, 1, d.E, d.E, wo_t, s)));
+  const void* wsrc[4] = {Wq, Wk, Wv, Wo};
+  void* wdst[4] = {wqkv_t, static_cast<unsigned char*>(wqkv_t) + wb, static_cast<unsigned char*>(wqkv_t) + 2 * wb,
+                   wo_t};
+  TTR_TRY(hip_status(launch_wt_transpose(d.dtype, wsrc, wdst, 4, d.E, s)));
+  t.mark();
   const float* bqkv[3] = {bq, bk, bv};
   TTR_TRY(hip_status(launch_proj_gemm(d.dtype, false, true, x, wqkv_t, bqkv, qkv, M, d.E, 3 * d.E, d.N, d.H, D,
                                       d.E, s)));
-  TTR_TRY(ttr_hybrid_forward(c, qkv[0], qkv[1], qkv[2], nullptr, nullptr, nullptr, eps, 0, causal ? 1 : 0, attn,
-                             core_ws, core_bytes, stream));
+  t.mark();
+  TTR_TRY(hybrid_forward_impl(c, qkv[0], qkv[1], qkv[2], nullptr, nullptr, nullptr, eps, 0, causal ? 1 : 0, attn,
+                              core_ws, core_bytes, s, &t));
   const float* bo3[3] = {bo, nullptr, nullptr};
   void* out3[3] = {out, nullptr, nullptr};
-  return hip_status(
+  const ttr_status st = hip_status(
       launch_proj_gemm(d.dtype, true, false, attn, wo_t, bo3, out3, M, d.E, d.E, d.N, d.H, D, d.E, s));
+  t.finish();
+  return st;
 }
 
 }  // extern "C"
