@@ -44,6 +44,19 @@ batch_first) is read as: x [B, N, E]; each projection is x @ W + b with W
 and b [E]; heads are consecutive D = E / H column blocks; dropout is the
 identity (an inference forward).
 
+The distillation step ("Flux2TTRTrainer", section "How the distillation
+works": the teacher is native softmax attention, the student is the TTR
+layer, the loss is a Kendall-style uncertainty-weighted blend of huber and
+cosine, optimizer state persists per layer) is read as: teacher =
+softmax(Q K^T / sqrt(D)) V on the same inputs; loss = exp(-s1) huber + s1 +
+exp(-s2) (1 - cos) + s2 with learnable log-variances s = (s1, s2) (Kendall,
+Gal and Cipolla's homoscedastic weighting), huber with delta = 1 averaged over
+every element, cos per (batch, head, token) row over D averaged over rows
+(cos = o.t / max(|o| |t|, 1e-8)); Adam (beta1 0.9, beta2 0.999, eps 1e-8,
+bias-corrected, no weight decay) updates W, b, g and s. The backward gives
+the gradients of the trainable parameters W, b, g (Q, K, V are the frozen
+model's activations).
+
 Pins (tests/test_oracle.py): brute-force N x N row-normalised attention,
 torch's elu and scaled_dot_product_attention in fp64, closed forms
 (W = 0, L = 1, Q = 0, first causal token), invariants (phi > 0, permutation,
@@ -63,6 +76,7 @@ __all__ = [
     "elu_plus_one", "relu_map", "softmax_map", "MAPS", "feature_map", "kv_reduce", "apply", "landmark_indices",
     "landmark_attn", "blend", "hybrid_forward", "causal_forward",
     "hybrid_rows", "causal_rows", "normwise_err", "split_heads", "merge_heads", "nnt_layer_forward",
+    "elu_plus_one_grad", "hybrid_backward", "full_softmax_attention", "distill_loss", "adam_update", "distill_step",
 ]
 
 
@@ -357,6 +371,135 @@ def nnt_layer_forward(x, Wq, bq, Wk, bk, Wv, bv, Wo, bo, H: int, eps, causal: bo
         KV, ksum = kv_reduce(K, V, None, None, kind)
         A = apply(Q, None, None, KV, ksum, eps, kind)
     return proj(merge_heads(A), Wo, bo)
+
+
+def elu_plus_one_grad(z: np.ndarray) -> np.ndarray:
+    """d(elu(z) + 1)/dz: 1 for z > 0, exp(z) otherwise (equal to the map itself there)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.where(z > 0.0, 1.0, np.exp(np.minimum(z, 0.0)))
+
+
+def hybrid_backward(Q, K, V, W, b, g, eps, L: int, dout):
+    """Gradients of sum(dout * hybrid_forward(...)) with respect to W [H,D,F],
+    b [H,F] and g [H] (elu + 1 map with a projection), by the chain rule through
+    the forward's definition:
+
+      z_q = Q W + b, z_k = K W + b, phi = elu(z) + 1
+      KV = phi_k^T V, ks = sum_n phi_k, num = phi_q KV, den = phi_q . ks + eps
+      lin = num / den, alpha = sigmoid(g), out = alpha lin + (1 - alpha) lm
+
+      dlin   = alpha dout;       dalpha = sum(dout * (lin - lm));  dg = dalpha alpha (1 - alpha)
+      dnum   = dlin / den;       dden = -sum_d(dlin * lin) / den
+      dphi_q = dnum KV^T + dden ks^T
+      dKV    = phi_q^T dnum;     dks = phi_q^T dden
+      dphi_k = V dKV^T + 1 dks^T
+      dz     = dphi * phi'(z);   dW = Q^T dz_q + K^T dz_k;   db = sum_n (dz_q + dz_k)
+
+    The landmark branch (raw Q, K, V) holds no parameter: it enters through
+    alpha only. Sums run over the batch for the per-head parameters.
+    """
+    Q, K, V, W, b, g, dout = (_f64(a) for a in (Q, K, V, W, b, g, dout))
+    B, H, N, D = Q.shape
+    F = W.shape[2]
+    dW = np.zeros((H, D, F))
+    db = np.zeros((H, F))
+    dg = np.zeros(H)
+    alpha = _sigmoid(g)
+    lm = landmark_attn(Q, K, V, L) if L > 0 else np.zeros_like(Q)
+    for bi in range(B):
+        for h in range(H):
+            bh = np.zeros(F) if b is None else b[h]
+            zq = Q[bi, h] @ W[h] + bh
+            zk = K[bi, h] @ W[h] + bh
+            pq, pk = elu_plus_one(zq), elu_plus_one(zk)
+            KV = pk.T @ V[bi, h]
+            ks = pk.sum(axis=0)
+            num = pq @ KV
+            den = pq @ ks + eps
+            lin = num / den[:, None]
+            G = dout[bi, h]
+            a = alpha[h] if L > 0 else 1.0
+            if L > 0:
+                dg[h] += (G * (lin - lm[bi, h])).sum() * alpha[h] * (1.0 - alpha[h])
+            dlin = a * G
+            dnum = dlin / den[:, None]
+            dden = -(dlin * lin).sum(axis=1) / den
+            dpq = dnum @ KV.T + np.outer(dden, ks)
+            dKV = pq.T @ dnum
+            dks = pq.T @ dden
+            dpk = V[bi, h] @ dKV.T + dks[None, :]
+            dzq = dpq * elu_plus_one_grad(zq)
+            dzk = dpk * elu_plus_one_grad(zk)
+            dW[h] += Q[bi, h].T @ dzq + K[bi, h].T @ dzk
+            db[h] += dzq.sum(axis=0) + dzk.sum(axis=0)
+    return dW, db, dg
+
+
+def full_softmax_attention(Q, K, V) -> np.ndarray:
+    """softmax(Q K^T / sqrt(D)) V per (batch, head): native attention, the teacher."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    S = np.einsum("bhnd,bhmd->bhnm", Q, K) / math.sqrt(Q.shape[3])
+    S -= S.max(axis=-1, keepdims=True)
+    P = np.exp(S)
+    return np.einsum("bhnm,bhmd->bhnd", P, V) / P.sum(axis=-1)[..., None]
+
+
+def distill_loss(out, teacher, s, delta: float = 1.0):
+    """Uncertainty-weighted huber + cosine distillation loss and its gradients.
+
+    loss = exp(-s1) H + s1 + exp(-s2) C + s2, H = mean over elements of
+    huber_delta(out - teacher), C = mean over rows of 1 - cos(out_row,
+    teacher_row). Returns (loss, dloss/dout, dloss/ds, H, C)."""
+    o, t, s = _f64(out), _f64(teacher), _f64(s)
+    r = o - t
+    ar = np.abs(r)
+    H = np.where(ar <= delta, 0.5 * r * r, delta * (ar - 0.5 * delta)).mean()
+    dH = np.clip(r, -delta, delta) / r.size
+    no = np.linalg.norm(o, axis=-1)
+    nt = np.linalg.norm(t, axis=-1)
+    dot = (o * t).sum(axis=-1)
+    den = np.maximum(no * nt, 1e-8)
+    cos = dot / den
+    rows = cos.size
+    C = (1.0 - cos).mean()
+    # d cos / d o = t / den - dot * o * nt / (no den^2) where no * nt > 1e-8 (else t / 1e-8)
+    live = (no * nt) > 1e-8
+    safe_no = np.where(no > 0, no, 1.0)
+    dcos = t / den[..., None] - np.where(live, dot * nt / (safe_no * den * den), 0.0)[..., None] * o
+    dC = -dcos / rows
+    w1, w2 = math.exp(-s[0]), math.exp(-s[1])
+    loss = w1 * H + s[0] + w2 * C + s[1]
+    dout = w1 * dH + w2 * dC
+    ds = np.array([1.0 - w1 * H, 1.0 - w2 * C])
+    return loss, dout, ds, H, C
+
+
+def adam_update(p, grad, m, v, step: int, lr: float, beta1=0.9, beta2=0.999, eps=1e-8):
+    """One Adam step (bias-corrected moments, step counted from 1). Returns (p, m, v)."""
+    p, grad, m, v = _f64(p), _f64(grad), _f64(m), _f64(v)
+    m = beta1 * m + (1.0 - beta1) * grad
+    v = beta2 * v + (1.0 - beta2) * grad * grad
+    mh = m / (1.0 - beta1 ** step)
+    vh = v / (1.0 - beta2 ** step)
+    return p - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
+def distill_step(Q, K, V, W, b, g, s, state, step: int, lr: float, eps, L: int, teacher=None):
+    """One Phase-1 distillation step: teacher (full softmax attention unless
+    given), student forward, loss, backward, Adam on W, b, g, s.
+
+    state: dict of Adam moments {"mW","vW","mb","vb","mg","vg","ms","vs"}.
+    Returns (W, b, g, s, state, loss)."""
+    T = full_softmax_attention(Q, K, V) if teacher is None else _f64(teacher)
+    out = hybrid_forward(Q, K, V, W, b, g, eps, L)
+    loss, dout, ds, _, _ = distill_loss(out, T, s)
+    dW, db, dg = hybrid_backward(Q, K, V, W, b, g, eps, L, dout)
+    new = {}
+    W2, new["mW"], new["vW"] = adam_update(W, dW, state["mW"], state["vW"], step, lr)
+    b2, new["mb"], new["vb"] = adam_update(b, db, state["mb"], state["vb"], step, lr)
+    g2, new["mg"], new["vg"] = adam_update(g, dg, state["mg"], state["vg"], step, lr)
+    s2, new["ms"], new["vs"] = adam_update(s, ds, state["ms"], state["vs"], step, lr)
+    return W2, b2, g2, s2, new, loss
 
 
 def normwise_err(got, ref, axes=(-2, -1)) -> float:

@@ -512,6 +512,144 @@ def test_nnt_layer_head_permutation_invariance():
     assert np.abs(_layer(x, Ws, bs, 4) - _layer(x, Wp, bp, 4)).max() < 1e-12
 
 
+# ---------------------------------------------------------------- backward and distillation
+
+def _bw_small(seed=80, B=2, H=2, N=24, D=4, F=8, L=6):
+    Q, K, V, W, b, g = _small(seed, B=B, H=H, N=N, D=D, F=F)
+    dout = np.random.default_rng(seed + 1).standard_normal(Q.shape)
+    return Q, K, V, W, b, g, L, dout
+
+
+def _fd(f, x, idx, h=1e-6):
+    xp, xm = x.copy(), x.copy()
+    xp[idx] += h
+    xm[idx] -= h
+    return (f(xp) - f(xm)) / (2 * h)
+
+
+def test_backward_matches_finite_differences():
+    Q, K, V, W, b, g, L, dout = _bw_small()
+    dW, db, dg = O.hybrid_backward(Q, K, V, W, b, g, EPS, L, dout)
+    obj = lambda W_, b_, g_: float((dout * O.hybrid_forward(Q, K, V, W_, b_, g_, EPS, L)).sum())
+    r = np.random.default_rng(3)
+    for _ in range(12):
+        idx = tuple(int(r.integers(n)) for n in W.shape)
+        assert abs(_fd(lambda x: obj(x, b, g), W, idx) - dW[idx]) < 1e-6 * max(1.0, abs(dW[idx]))
+    for h in range(b.shape[0]):
+        for f in (0, 3, 7):
+            assert abs(_fd(lambda x: obj(W, x, g), b, (h, f)) - db[h, f]) < 1e-6 * max(1.0, abs(db[h, f]))
+    for h in range(g.shape[0]):
+        assert abs(_fd(lambda x: obj(W, b, x), g, (h,)) - dg[h]) < 1e-6 * max(1.0, abs(dg[h]))
+
+
+def _torch_hybrid(Q, K, V, W, b, g, eps, L):
+    """The forward restated in torch (fp64, differentiable): N x N linear form,
+    softmax over the gathered landmarks, sigmoid blend."""
+    Qt, Kt, Vt = (torch.from_numpy(a) for a in (Q, K, V))
+    B, H, N, D = Q.shape
+    idx = torch.tensor([(j * N) // L for j in range(L)])
+    outs = []
+    for h in range(H):
+        pq = torch.nn.functional.elu(Qt[:, h] @ W[h] + b[h]) + 1
+        pk = torch.nn.functional.elu(Kt[:, h] @ W[h] + b[h]) + 1
+        A = pq @ pk.transpose(-1, -2)
+        lin = (A @ Vt[:, h]) / (A.sum(-1, keepdim=True) + eps)
+        S = (Qt[:, h] @ Kt[:, h, idx].transpose(-1, -2)) / math.sqrt(D)
+        lm = torch.softmax(S, dim=-1) @ Vt[:, h, idx]
+        a = torch.sigmoid(g[h])
+        outs.append(a * lin + (1 - a) * lm)
+    return torch.stack(outs, dim=1)
+
+
+def test_backward_matches_torch_autograd():
+    Q, K, V, W, b, g, L, dout = _bw_small(81, B=2, H=3, N=30, D=5, F=7, L=5)
+    Wt, bt, gt = (torch.tensor(a, requires_grad=True) for a in (W, b, g))
+    (torch.from_numpy(dout) * _torch_hybrid(Q, K, V, Wt, bt, gt, EPS, L)).sum().backward()
+    dW, db, dg = O.hybrid_backward(Q, K, V, W, b, g, EPS, L, dout)
+    for mine, ref in ((dW, Wt.grad), (db, bt.grad), (dg, gt.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-10 * max(1.0, np.abs(ref.numpy()).max())
+
+
+def test_backward_without_landmarks_has_no_g_gradient():
+    Q, K, V, W, b, g, _, dout = _bw_small(82)
+    dW, db, dg = O.hybrid_backward(Q, K, V, W, b, g, EPS, 0, dout)
+    assert not dg.any()
+    obj = lambda W_: float((dout * O.hybrid_forward(Q, K, V, W_, b, g, EPS, 0)).sum())
+    assert abs(_fd(obj, W, (1, 2, 3)) - dW[1, 2, 3]) < 1e-6 * max(1.0, abs(dW[1, 2, 3]))
+
+
+def test_elu_plus_one_grad():
+    z = np.array([-3.0, -1e-3, 0.0, 1e-3, 2.0])
+    want = np.array([math.exp(-3.0), math.exp(-1e-3), 1.0, 1.0, 1.0])
+    assert np.abs(O.elu_plus_one_grad(z) - want).max() < 1e-15
+
+
+def test_full_softmax_attention_matches_sdpa():
+    Q, K, V, _, _, _ = _small(83, B=2, H=2, N=33, D=8)
+    assert np.abs(O.full_softmax_attention(Q, K, V) - sdpa(Q, K, V)).max() < 1e-12
+
+
+def test_distill_loss_matches_torch():
+    r = np.random.default_rng(84)
+    o = r.standard_normal((2, 3, 10, 6)) * 1.5
+    t = r.standard_normal((2, 3, 10, 6))
+    o[0, 0, 0] = 0.0  # a zero row: cos is 0 there and its gradient is t / 1e-8 . 0
+    s = np.array([0.3, -0.2])
+    loss, dout, ds, H, C = O.distill_loss(o, t, s)
+    ot = torch.tensor(o, requires_grad=True)
+    st = torch.tensor(s, requires_grad=True)
+    Ht = torch.nn.functional.huber_loss(ot, torch.from_numpy(t), delta=1.0)
+    Ct = (1 - torch.nn.functional.cosine_similarity(ot, torch.from_numpy(t), dim=-1, eps=1e-8)).mean()
+    Lt = torch.exp(-st[0]) * Ht + st[0] + torch.exp(-st[1]) * Ct + st[1]
+    Lt.backward()
+    assert abs(H - Ht.item()) < 1e-12 and abs(C - Ct.item()) < 1e-12 and abs(loss - Lt.item()) < 1e-12
+    assert np.abs(dout[:, :, 1:] - ot.grad.numpy()[:, :, 1:]).max() < 1e-12
+    assert np.abs(ds - st.grad.numpy()).max() < 1e-12
+
+
+def test_adam_matches_torch_optim():
+    r = np.random.default_rng(85)
+    p0 = r.standard_normal(7)
+    grads = [r.standard_normal(7) for _ in range(5)]
+    pt = torch.tensor(p0, requires_grad=True)
+    opt = torch.optim.Adam([pt], lr=3e-3, betas=(0.9, 0.999), eps=1e-8)
+    p, m, v = p0.copy(), np.zeros(7), np.zeros(7)
+    for k, gr in enumerate(grads, start=1):
+        opt.zero_grad()
+        pt.grad = torch.from_numpy(gr.copy())
+        opt.step()
+        p, m, v = O.adam_update(p, gr, m, v, k, 3e-3)
+    assert np.abs(p - pt.detach().numpy()).max() < 1e-14
+
+
+def _adam_state(W, b, g, s):
+    z = np.zeros_like
+    return {"mW": z(W), "vW": z(W), "mb": z(b), "vb": z(b), "mg": z(g), "vg": z(g), "ms": z(s), "vs": z(s)}
+
+
+def test_distill_step_self_teacher_moves_only_log_variances():
+    Q, K, V, W, b, g, L, _ = _bw_small(86)
+    s = np.zeros(2)
+    T = O.hybrid_forward(Q, K, V, W, b, g, EPS, L)
+    W2, b2, g2, s2, _, loss = O.distill_step(Q, K, V, W, b, g, s, _adam_state(W, b, g, s), 1, 1e-2, EPS, L, T)
+    assert abs(loss) < 1e-12  # huber 0, cos 1 everywhere, s = 0
+    # the gradient is zero up to rounding (cos = 1 - ulp), which Adam's eps turns into < 1e-9 steps
+    assert np.abs(W2 - W).max() < 1e-9 and np.abs(b2 - b).max() < 1e-9 and np.abs(g2 - g).max() < 1e-9
+    assert np.all(s2 < 0)  # d loss / d s = 1 - exp(-s) * 0 = 1 > 0 pushes s down
+
+
+def test_distill_steps_reduce_the_loss():
+    Q, K, V, W, b, g, L, _ = _bw_small(87, B=1, H=2, N=32, D=8, F=16, L=8)
+    s = np.zeros(2)
+    st = _adam_state(W, b, g, s)
+    T = O.full_softmax_attention(Q, K, V)
+    losses = []
+    for k in range(1, 31):
+        W, b, g, s, st, loss = O.distill_step(Q, K, V, W, b, g, s, st, k, 1e-2, EPS, L, T)
+        losses.append(loss)
+    assert losses[-1] < losses[0] - 0.05
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_linear():
@@ -619,9 +757,57 @@ def _pins_layer():
     test_nnt_layer_matches_bruteforce("elu1", True)
 
 
+def _mut_elu_grad_one(z):
+    return np.ones_like(np.asarray(z, dtype=np.float64))
+
+
+def _mut_backward_no_den_term(Q, K, V, W, b, g, eps, L, dout):
+    # the chain rule without the normaliser's path (dden = 0): a plausible slip
+    Q, K, V, W, b, g, dout = (np.asarray(a, dtype=np.float64) for a in (Q, K, V, W, b, g, dout))
+    B, H, N, D = Q.shape
+    dW, db, dg = np.zeros_like(W), np.zeros_like(b), np.zeros_like(g)
+    alpha = 1 / (1 + np.exp(-g))
+    lm = O.landmark_attn(Q, K, V, L)
+    for bi in range(B):
+        for h in range(H):
+            zq, zk = Q[bi, h] @ W[h] + b[h], K[bi, h] @ W[h] + b[h]
+            pq, pk = O.elu_plus_one(zq), O.elu_plus_one(zk)
+            KV, ks = pk.T @ V[bi, h], pk.sum(axis=0)
+            den = pq @ ks + eps
+            lin = (pq @ KV) / den[:, None]
+            G = dout[bi, h]
+            dg[h] += (G * (lin - lm[bi, h])).sum() * alpha[h] * (1 - alpha[h])
+            dnum = alpha[h] * G / den[:, None]
+            dKV = pq.T @ dnum
+            dzq = (dnum @ KV.T) * O.elu_plus_one_grad(zq)
+            dzk = (V[bi, h] @ dKV.T) * O.elu_plus_one_grad(zk)
+            dW[h] += Q[bi, h].T @ dzq + K[bi, h].T @ dzk
+            db[h] += dzq.sum(axis=0) + dzk.sum(axis=0)
+    return dW, db, dg
+
+
+def _mut_loss_unweighted(out, teacher, s, delta=1.0):
+    loss, dout, ds, H, C = _orig_loss(out, teacher, np.zeros(2), delta)
+    return H + C + s[0] + s[1], dout, ds, H, C
+
+
+def _mut_adam_no_bias_correction(p, grad, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8):
+    p, grad, m, v = (np.asarray(a, dtype=np.float64) for a in (p, grad, m, v))
+    m = beta1 * m + (1 - beta1) * grad
+    v = beta2 * v + (1 - beta2) * grad * grad
+    return p - lr * m / (np.sqrt(v) + eps), m, v
+
+
+def _pins_backward():
+    test_backward_matches_finite_differences()
+    test_backward_matches_torch_autograd()
+
+
 _orig_landmark = O.landmark_attn
 _orig_blend = O.blend
 _orig_layer = O.nnt_layer_forward
+_orig_backward = O.hybrid_backward
+_orig_loss = O.distill_loss
 
 
 @pytest.mark.parametrize("attr,mutant,pins", [
@@ -638,6 +824,10 @@ _orig_layer = O.nnt_layer_forward
     ("split_heads", _mut_split_heads_interleaved, _pins_layer),
     ("merge_heads", _mut_merge_heads_interleaved, _pins_layer),
     ("nnt_layer_forward", _mut_layer_no_value_bias, _pins_layer),
+    ("elu_plus_one_grad", _mut_elu_grad_one, _pins_backward),
+    ("hybrid_backward", _mut_backward_no_den_term, _pins_backward),
+    ("distill_loss", _mut_loss_unweighted, test_distill_loss_matches_torch),
+    ("adam_update", _mut_adam_no_bias_correction, test_adam_matches_torch_optim),
 ])
 def test_planted_mistake_is_caught(monkeypatch, attr, mutant, pins):
     monkeypatch.setattr(O, attr, mutant)
