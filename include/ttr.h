@@ -135,6 +135,25 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
                               int32_t L, int32_t causal, void* out, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* Gradients of the hybrid forward (non-causal, elu + 1 map, projection W
+ * required, 0 <= L <= N) for its trainable parameters, given
+ * dout = dLoss/dout fp32 [B,H,N,D]:
+ *   dW [H,D,F], db [H,F], dg [H], all fp32, summed over the batch (overwritten).
+ * Chain rule through out = alpha lin + (1 - alpha) lm, alpha = sigmoid(g),
+ * lin = phi(Q) KV / (phi(Q) . ksum + eps), phi = elu(x W + b) + 1; the landmark
+ * branch holds no parameter and contributes through alpha only (dg = 0 when
+ * L == 0). Gradients for Q, K, V are not computed.
+ * "Flux2TTRTrainer", "How the distillation works" (the student layer that
+ * Phase 1 trains); "NNT Define Linear Attention", "How it works" (the linear branch).
+ * b may be NULL (zero bias; db is still written). g is needed when L > 0.
+ * ws: at least ttr_backward_workspace_bytes(d, L) bytes (fp32 intermediates). */
+ttr_status ttr_hybrid_backward(ttr_dims d, const void* Q, const void* K, const void* V, const void* W,
+                               const float* b, const float* g, float eps, int32_t L, const float* dout,
+                               float* dW, float* db, float* dg, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace size in bytes of ttr_hybrid_backward (0 if the shape is invalid). */
+size_t ttr_backward_workspace_bytes(ttr_dims d, int32_t L);
+
 /* Sizes of the NNT linear-attention layer: x [B,N,E] (batch first), H heads of D = E / H. */
 typedef struct {
   int32_t B, N, E, H;

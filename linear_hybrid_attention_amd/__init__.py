@@ -77,6 +77,8 @@ _SIGS = {
     "ttr_causal_scan": [Dims, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
     "ttr_hybrid_forward": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                            _P, _P, ctypes.c_size_t, _P],
+    "ttr_hybrid_backward": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P, _P, _P, _P, _P,
+                            ctypes.c_size_t, _P],
     "ttr_nnt_layer_forward": [LayerDims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
                               _P, _P, ctypes.c_size_t, _P],
 }
@@ -100,6 +102,8 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.ttr_workspace_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.ttr_workspace_bytes.restype = ctypes.c_size_t
+    lib.ttr_backward_workspace_bytes.argtypes = [Dims, ctypes.c_int32]
+    lib.ttr_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_nnt_layer_workspace_bytes.argtypes = [LayerDims, ctypes.c_int32]
     lib.ttr_nnt_layer_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_status_string.argtypes = [ctypes.c_int]
@@ -321,3 +325,27 @@ def nnt_layer_forward(x: torch.Tensor, Wq: torch.Tensor, bq: Optional[torch.Tens
                                    _stream(x))
     _check(st, "ttr_nnt_layer_forward")
     return out
+
+
+def hybrid_backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: torch.Tensor,
+                    b: Optional[torch.Tensor], g: Optional[torch.Tensor], eps: float, L: int, dout: torch.Tensor,
+                    ws: Optional[torch.Tensor] = None):
+    """Gradients (dW [H,D,F], db [H,F], dg [H], float32) of the hybrid forward for
+    dLoss/dout = dout (float32 [B,H,N,D]) (ttr_hybrid_backward)."""
+    lib = load_library()
+    d = _dims(Q, _feat_dim(Q, W))
+    B, H, N, D = Q.shape
+    F = d.F
+    dW = torch.empty((H, D, F), dtype=torch.float32, device=Q.device)
+    db = torch.empty((H, F), dtype=torch.float32, device=Q.device)
+    dg = torch.empty((H,), dtype=torch.float32, device=Q.device)
+    need = lib.ttr_backward_workspace_bytes(d, int(L))
+    if need == 0:
+        raise TTRError(2, "ttr_hybrid_backward", "invalid shape for the backward")
+    ws, wsb = _workspace(d, need, Q, ws)
+    st = lib.ttr_hybrid_backward(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype),
+                                 _dev(W, "W", Q.dtype), _dev(b, "b", torch.float32), _dev(g, "g", torch.float32),
+                                 float(eps), int(L), _dev(dout, "dout", torch.float32), _dev(dW, "dW"), _dev(db, "db"),
+                                 _dev(dg, "dg"), None if ws is None else ws.data_ptr(), wsb, _stream(Q))
+    _check(st, "ttr_hybrid_backward")
+    return dW, db, dg

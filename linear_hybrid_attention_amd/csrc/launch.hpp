@@ -92,4 +92,14 @@ hipError_t launch_proj_gemm(int dtype, bool a_heads, bool c_qkv, const void* A, 
                             const float* const* bias, void* const* out, int M, int K, int Nc, int Ntok, int H,
                             int D, int E, hipStream_t s);
 
+// k_backward.hip: gradients of the hybrid forward for W, b, g (fp32
+// intermediates in the workspace, byte offsets below).
+struct BackwardLayout {
+  size_t zq, zk, dzq, dzk, lin, lm, dnum, kv, dkv, ks, dks, den, dden, rpart, bytes;
+};
+BackwardLayout backward_layout(const Problem& p);
+hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
+                                  const float* bias, const float* g, float eps, int L, const float* dout, float* dW,
+                                  float* db, float* dg, void* ws, hipStream_t s);
+
 }  // namespace ttr

@@ -408,4 +408,43 @@ ttr_status ttr_nnt_layer_forward(ttr_layer_dims d, const void* x, const void* Wq
   return st;
 }
 
+// ---------------------------------------------------------------- backward
+static ttr_status check_backward(const ttr_dims& d, int32_t L) {
+  TTR_TRY(check_dims(d, true));
+  if (d.fmap != TTR_FMAP_ELU1) return TTR_ERR_UNSUPPORTED;
+  if (L < 0 || L > d.N) return TTR_ERR_SHAPE;
+  return TTR_OK;
+}
+
+size_t ttr_backward_workspace_bytes(ttr_dims d, int32_t L) {
+  if (check_backward(d, L) != TTR_OK) return 0;
+  return backward_layout(make_problem(d, true)).bytes;
+}
+
+ttr_status ttr_hybrid_backward(ttr_dims d, const void* Q, const void* K, const void* V, const void* W, const float* b,
+                               const float* g, float eps, int32_t L, const float* dout, float* dW, float* db,
+                               float* dg, void* ws, size_t ws_bytes, void* stream) {
+  TTR_TRY(check_backward(d, L));
+  TTR_TRY(check_ptr(Q));
+  TTR_TRY(check_ptr(K));
+  TTR_TRY(check_ptr(V));
+  TTR_TRY(check_ptr(W));
+  TTR_TRY(check_ptr(dout));
+  TTR_TRY(check_ptr(dW));
+  TTR_TRY(check_ptr(db));
+  TTR_TRY(check_ptr(dg));
+  TTR_TRY(check_opt_ptr(b));
+  if (L > 0) TTR_TRY(check_ptr(g));
+  const Problem p = make_problem(d, true);
+  const size_t need = backward_layout(p).bytes;
+  if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
+  TTR_TRY(check_ptr(ws));
+  const Range outs[] = {{dW, (size_t)d.H * d.D * d.F * 4}, {db, (size_t)d.H * d.F * 4}, {dg, (size_t)d.H * 4},
+                        {ws, need}};
+  const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {W, w_bytes(d)},
+                       {b, b ? b_bytes(d) : 0}, {g, g ? (size_t)d.H * 4 : 0}, {dout, f32_out_bytes(d)}};
+  TTR_TRY(check_no_alias(outs, 4, ins, 7));
+  return hip_status(launch_hybrid_backward(p, Q, K, V, W, b, g, eps, L, dout, dW, db, dg, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -41,7 +41,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "bf16_round_bits", "bf16_bits_to_f32",
-           "LayerWorkload", "LAYER_WORKLOADS", "make_layer_inputs"]
+           "LayerWorkload", "LAYER_WORKLOADS", "make_layer_inputs", "make_grad_output"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -181,3 +181,8 @@ def make_layer_inputs(w: LayerWorkload, seed: Optional[int] = None, bias: bool =
     elif w.dtype != "fp32":
         raise ValueError(f"unknown dtype {w.dtype!r}")
     return out
+
+
+def make_grad_output(w: Workload, seed: int) -> np.ndarray:
+    """A seeded upstream gradient dLoss/dout for workload ``w``: fp32 [B,H,N,D] ~ N(0, 1)."""
+    return np.random.default_rng(seed).standard_normal((w.B, w.H, w.N, w.D), dtype=np.float32)
