@@ -154,6 +154,32 @@ ttr_status ttr_hybrid_backward(ttr_dims d, const void* Q, const void* K, const v
 /* Workspace size in bytes of ttr_hybrid_backward (0 if the shape is invalid). */
 size_t ttr_backward_workspace_bytes(ttr_dims d, int32_t L);
 
+/* One Phase-1 distillation step of a TTR layer on one batch of Q, K, V
+ * ("Flux2TTRTrainer", "How the distillation works": the student TTR layer
+ * regresses native softmax attention; the loss is a Kendall-style
+ * uncertainty-weighted blend of huber and cosine; optimizer state persists):
+ *   teacher = softmax(Q K^T / sqrt(D)) V per (b, h) (computed when teacher is NULL)
+ *   out     = the hybrid forward with W, b, g (W rounded to the IO dtype for it)
+ *   loss    = exp(-s1) huber + s1 + exp(-s2) (1 - cos) + s2
+ *             (huber with delta 1 averaged over every element; cos per (b, h, n)
+ *             row over D, o.t / max(|o| |t|, 1e-8), averaged over rows)
+ *   then Adam (beta1 0.9, beta2 0.999, eps 1e-8, bias-corrected at `step`,
+ *   counted from 1, no weight decay) on W, b, g, s with the gradients of
+ *   ttr_hybrid_backward and dloss/ds.
+ * W [H,D,F], b [H,F], g [H], s [2]: fp32 master parameters, updated in place.
+ * moments: fp32 Adam moments, 2 (H D F + H F + H + 2) values laid out
+ * [mW vW mb vb mg vg ms vs], zero before step 1, updated in place.
+ * teacher: fp32 [B,H,N,D] or NULL. loss: fp32 [3] device output (loss,
+ * huber, 1 - cos) of the parameters before the update.
+ * Shape rules as ttr_hybrid_backward (F == 256 with the projection).
+ * ws: at least ttr_distill_workspace_bytes(d, L, teacher == NULL) bytes. */
+ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void* V, const float* teacher,
+                            float* W, float* b, float* g, float* s, float* moments, int32_t step, float lr,
+                            float eps, int32_t L, float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace size in bytes of ttr_distill_step (0 if the shape is invalid). */
+size_t ttr_distill_workspace_bytes(ttr_dims d, int32_t L, int32_t compute_teacher);
+
 /* Sizes of the NNT linear-attention layer: x [B,N,E] (batch first), H heads of D = E / H. */
 typedef struct {
   int32_t B, N, E, H;

@@ -79,6 +79,8 @@ _SIGS = {
                            _P, _P, ctypes.c_size_t, _P],
     "ttr_hybrid_backward": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P, _P, _P, _P, _P,
                             ctypes.c_size_t, _P],
+    "ttr_distill_step": [Dims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                         ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
     "ttr_nnt_layer_forward": [LayerDims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
                               _P, _P, ctypes.c_size_t, _P],
 }
@@ -102,6 +104,8 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.ttr_workspace_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.ttr_workspace_bytes.restype = ctypes.c_size_t
+    lib.ttr_distill_workspace_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32]
+    lib.ttr_distill_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_backward_workspace_bytes.argtypes = [Dims, ctypes.c_int32]
     lib.ttr_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_nnt_layer_workspace_bytes.argtypes = [LayerDims, ctypes.c_int32]
@@ -349,3 +353,40 @@ def hybrid_backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: torch.
                                  _dev(dg, "dg"), None if ws is None else ws.data_ptr(), wsb, _stream(Q))
     _check(st, "ttr_hybrid_backward")
     return dW, db, dg
+
+
+class DistillState:
+    """fp32 master parameters and Adam moments of one TTR layer for ttr_distill_step."""
+
+    def __init__(self, W: torch.Tensor, b: torch.Tensor, g: torch.Tensor, s: Optional[torch.Tensor] = None):
+        f32 = torch.float32
+        self.W = W.detach().to(f32).contiguous().clone()
+        self.b = b.detach().to(f32).contiguous().clone()
+        self.g = g.detach().to(f32).contiguous().clone()
+        self.s = torch.zeros(2, dtype=f32, device=W.device) if s is None else s.detach().to(f32).contiguous().clone()
+        n = self.W.numel() + self.b.numel() + self.g.numel() + 2
+        self.moments = torch.zeros(2 * n, dtype=f32, device=W.device)
+        self.step = 0
+
+
+def distill_step(state: DistillState, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, L: int, lr: float,
+                 eps: float = 1e-6, teacher: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """One distillation step (ttr_distill_step); updates ``state`` in place and
+    returns the device tensor [loss, huber, 1 - cos] before the update."""
+    lib = load_library()
+    d = _dims(Q, int(state.W.shape[2]))
+    need = lib.ttr_distill_workspace_bytes(d, int(L), int(teacher is None))
+    if need == 0:
+        raise TTRError(2, "ttr_distill_step", "invalid shape for the distillation step")
+    ws, wsb = _workspace(d, need, Q, ws)
+    loss = torch.empty(3, dtype=torch.float32, device=Q.device)
+    state.step += 1
+    st = lib.ttr_distill_step(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype),
+                              _dev(teacher, "teacher", torch.float32), _dev(state.W, "W"), _dev(state.b, "b"),
+                              _dev(state.g, "g"), _dev(state.s, "s"), _dev(state.moments, "moments"), state.step,
+                              float(lr), float(eps), int(L), _dev(loss, "loss"), None if ws is None else ws.data_ptr(),
+                              wsb, _stream(Q))
+    if st != 0:
+        state.step -= 1
+    _check(st, "ttr_distill_step")
+    return loss

@@ -352,24 +352,31 @@ BackwardLayout backward_layout(const Problem& p) {
   return l;
 }
 
-hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
-                                  const float* bias, const float* g, float eps, int L, const float* dout, float* dW,
-                                  float* db, float* dg, void* ws, hipStream_t s) {
+#define TTR_HIP(x)                 \
+  do {                             \
+    const hipError_t e_ = (x);     \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
+// Workspace views of the backward's fp32 intermediates.
+struct BwBufs {
+  float *zq, *zk, *dzq, *dzk, *lin, *lm, *dnum, *kv, *dkv, *ks, *dks, *den, *dden, *rpart;
+};
+static BwBufs bw_bufs(const Problem& p, void* ws) {
   const BackwardLayout l = backward_layout(p);
   unsigned char* w8 = static_cast<unsigned char*>(ws);
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w8 + off); };
-  float *zq = F32(l.zq), *zk = F32(l.zk), *dzq = F32(l.dzq), *dzk = F32(l.dzk), *lin = F32(l.lin), *lm = F32(l.lm);
-  float *dnum = F32(l.dnum), *kv = F32(l.kv), *dkv = F32(l.dkv), *ks = F32(l.ks), *dks = F32(l.dks);
-  float *den = F32(l.den), *dden = F32(l.dden), *rpart = F32(l.rpart);
+  return BwBufs{F32(l.zq),  F32(l.zk), F32(l.dzq), F32(l.dzk), F32(l.lin), F32(l.lm),  F32(l.dnum),
+                F32(l.kv),  F32(l.dkv), F32(l.ks), F32(l.dks), F32(l.den), F32(l.dden), F32(l.rpart)};
+}
+
+// Forward pass with the intermediates the gradients need: z_q, z_k (biased),
+// ks, KV, den, lin = num / den and (L > 0) the landmark output lm.
+static hipError_t backward_forward_pass(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
+                                        const float* bias, float eps, int L, const BwBufs& t, hipStream_t s) {
+  float *zq = t.zq, *zk = t.zk, *lin = t.lin, *lm = t.lm, *kv = t.kv, *ks = t.ks, *den = t.den;
   const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H, dt = p.dtype;
   const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
-  hipError_t e;
-#define TTR_HIP(x)             \
-  do {                         \
-    e = (x);                   \
-    if (e != hipSuccess) return e; \
-  } while (0)
-
   // z_q = Q W + b, z_k = K W + b: per (b, h), [N x D] . [D x F]; the bias in a second pass
   auto proj = [&](const void* X, float* Zout) {
     BgemmArgs a{};
@@ -462,6 +469,17 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
     pl.F = p.D;
     TTR_HIP(launch_hybrid(pl, M_LM, false, ha, s));
   }
+  return hipSuccess;
+}
+
+// Gradients from dout, after backward_forward_pass filled t.
+static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void* K, const void* V, const float* g,
+                                     int L, const float* dout, float* dW, float* db, float* dg, const BwBufs& t,
+                                     hipStream_t s) {
+  float *zq = t.zq, *zk = t.zk, *dzq = t.dzq, *dzk = t.dzk, *lin = t.lin, *lm = t.lm, *dnum = t.dnum, *kv = t.kv;
+  float *dkv = t.dkv, *ks = t.ks, *dks = t.dks, *den = t.den, *dden = t.dden, *rpart = t.rpart;
+  const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H, dt = p.dtype;
+  const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
   // dnum, dden, dalpha row shares
   TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, N, D, Z, L > 0, dnum, dden, rpart, s));
   // dphi_q = dnum KV^T (+ dden ks^T in dz): [N x D] . [D x F]
@@ -558,8 +576,230 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
   TTR_HIP(dw(Q, dzq, 0));
   TTR_HIP(dw(K, dzk, 1));
   TTR_HIP(launch_db_dg(dzq, dzk, rpart, g, B, H, N, F, L > 0, db, dg, s));
-#undef TTR_HIP
   return hipSuccess;
+}
+
+hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
+                                  const float* bias, const float* g, float eps, int L, const float* dout, float* dW,
+                                  float* db, float* dg, void* ws, hipStream_t s) {
+  const BwBufs t = bw_bufs(p, ws);
+  TTR_HIP(backward_forward_pass(p, Q, K, V, W, bias, eps, L, t, s));
+  return backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s);
+}
+
+// ---------------------------------------------------------------- distillation step
+// Per row (z, n), one wave: o = alpha lin + (1 - alpha) lm (lin alone when L == 0),
+// t = the teacher row; writes dout = w1 clip(o - t, -1, 1) / numel - w2 dcos / rows,
+// the row's huber sum and 1 - cos. w = exp(-s).
+__global__ void distill_loss_rows_kernel(const float* lin, const float* lm, const float* teacher, const float* g,
+                                         const float* sv, int H, int N, int D, int Z, int has_lm, float* dout,
+                                         float* hrow, float* crow_) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= Z * N) return;
+  const int h = (row / N) % H;
+  const float alpha = has_lm ? 1.f / (1.f + expf(-g[h])) : 1.f;
+  const float w1 = expf(-sv[0]), w2 = expf(-sv[1]);
+  const float inv_numel = 1.f / ((float)Z * N * D), inv_rows = 1.f / ((float)Z * N);
+  const float* li = lin + (size_t)row * D;
+  const float* lr = lm + (size_t)row * D;
+  const float* tr = teacher + (size_t)row * D;
+  float ov[4], tv[4];  // D <= 256: up to 4 elements per lane
+  float hs = 0.f, dot = 0.f, oo = 0.f, tt = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = lane + 64 * j;
+    float o = 0.f, t = 0.f;
+    if (d < D) {
+      o = has_lm ? alpha * li[d] + (1.f - alpha) * lr[d] : li[d];
+      t = tr[d];
+      const float r = o - t, ar = fabsf(r);
+      hs += ar <= 1.f ? 0.5f * r * r : ar - 0.5f;
+    }
+    ov[j] = o;
+    tv[j] = t;
+    dot += o * t;
+    oo += o * o;
+    tt += t * t;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    hs += __shfl_xor(hs, off);
+    dot += __shfl_xor(dot, off);
+    oo += __shfl_xor(oo, off);
+    tt += __shfl_xor(tt, off);
+  }
+  const float no = sqrtf(oo), nt = sqrtf(tt);
+  const float den = fmaxf(no * nt, 1e-8f);
+  const float cosv = dot / den;
+  const bool live = no * nt > 1e-8f;
+  const float co = live ? dot * nt / (no * den * den) : 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = lane + 64 * j;
+    if (d < D) {
+      const float r = ov[j] - tv[j];
+      const float dcos = tv[j] / den - co * ov[j];
+      dout[(size_t)row * D + d] = w1 * fminf(fmaxf(r, -1.f), 1.f) * inv_numel - w2 * dcos * inv_rows;
+    }
+  }
+  if (lane == 0) {
+    hrow[row] = hs;
+    crow_[row] = 1.f - cosv;
+  }
+}
+
+// One workgroup: H = sum hrow / numel, C = sum crow / rows (fixed order);
+// loss = w1 H + s1 + w2 C + s2; ds = (1 - w1 H, 1 - w2 C). out: loss, H, C.
+__global__ void distill_loss_total_kernel(const float* hrow, const float* crow_, int rows, int D, const float* sv,
+                                          float* loss_out, float* ds) {
+  __shared__ float sh[256], sc[256];
+  const int t = threadIdx.x;
+  float h = 0.f, c = 0.f;
+  for (int i = t; i < rows; i += 256) {
+    h += hrow[i];
+    c += crow_[i];
+  }
+  sh[t] = h;
+  sc[t] = c;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) {
+      sh[t] += sh[t + o];
+      sc[t] += sc[t + o];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    const float H = sh[0] / ((float)rows * D), C = sc[0] / (float)rows;
+    const float w1 = expf(-sv[0]), w2 = expf(-sv[1]);
+    loss_out[0] = w1 * H + sv[0] + w2 * C + sv[1];
+    loss_out[1] = H;
+    loss_out[2] = C;
+    ds[0] = 1.f - w1 * H;
+    ds[1] = 1.f - w2 * C;
+  }
+}
+
+// Adam over the parameter blocks (W, b, g, s) with their gradients; moments
+// [mW vW mb vb mg vg ms vs], bias-corrected at step `step` (from 1).
+struct AdamArgs {
+  float* p[4];
+  const float* grad[4];
+  float* moments;
+  long long n[4];
+  float lr, c1, c2;  // c1 = 1 - beta1^step, c2 = 1 - beta2^step
+};
+__global__ void adam_kernel(AdamArgs a) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  long long off = 0;
+  for (int k = 0; k < 4; ++k) {
+    if (i < a.n[k]) {
+      float* m = a.moments + 2 * off;
+      float* v = m + a.n[k];
+      const float gr = a.grad[k][i];
+      const float mi = 0.9f * m[i] + 0.1f * gr;
+      const float vi = 0.999f * v[i] + 0.001f * gr * gr;
+      m[i] = mi;
+      v[i] = vi;
+      a.p[k][i] -= a.lr * (mi / a.c1) / (sqrtf(vi / a.c2) + 1e-8f);
+      return;
+    }
+    i -= a.n[k];
+    off += a.n[k];
+  }
+}
+
+// fp32 -> bf16 (round to nearest even)
+__global__ void to_bf16_kernel(const float* x, uint16_t* y, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = f2bf(x[i]);
+}
+
+DistillLayout distill_layout(const Problem& p, bool need_teacher) {
+  DistillLayout l;
+  const size_t Z = (size_t)p.B * p.H, N = p.N, D = p.D, F = p.F, H = p.H;
+  auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  size_t o = al(backward_layout(p).bytes);
+  l.w_io = o;
+  o += al(p.dtype == 1 ? H * D * F * 2 : 0);
+  l.teacher = o;
+  o += al(need_teacher ? Z * N * D * 4 : 0);
+  l.dout = o;
+  o += al(Z * N * D * 4);
+  l.hrow = o;
+  o += al(Z * N * 4);
+  l.crow = o;
+  o += al(Z * N * 4);
+  l.grads = o;  // dW | db | dg | ds
+  o += al((H * D * F + H * F + H + 2) * 4);
+  l.bytes = o;
+  return l;
+}
+
+hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, const void* V, const float* teacher,
+                               float* W, float* bias, float* g, float* sv, float* moments, int step, float lr,
+                               float eps, int L, float* loss_out, void* ws, hipStream_t s) {
+  const DistillLayout l = distill_layout(p, teacher == nullptr);
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H;
+  const size_t nW = (size_t)H * D * F, nb = (size_t)H * F;
+  // weights in the IO dtype for the forward and backward
+  const void* Wio = W;
+  if (p.dtype == 1) {
+    uint16_t* wb = reinterpret_cast<uint16_t*>(w8 + l.w_io);
+    hipLaunchKernelGGL(to_bf16_kernel, dim3(blocks(nW, 256)), dim3(256), 0, s, W, wb, nW);
+    TTR_HIP(hipGetLastError());
+    Wio = wb;
+  }
+  // teacher: softmax over every token (the landmark branch with L = N)
+  const float* T = teacher;
+  if (T == nullptr) {
+    float* tw = reinterpret_cast<float*>(w8 + l.teacher);
+    HybridArgs ha = {};
+    ha.Q = Q;
+    ha.K = K;
+    ha.V = V;
+    ha.H = H;
+    ha.N = N;
+    ha.L = N;
+    ha.out = tw;
+    Problem pl = p;
+    pl.proj = false;
+    pl.F = p.D;
+    TTR_HIP(launch_hybrid(pl, M_LM, false, ha, s));
+    T = tw;
+  }
+  const BwBufs t = bw_bufs(p, ws);
+  TTR_HIP(backward_forward_pass(p, Q, K, V, Wio, bias, eps, L, t, s));
+  float* dout = reinterpret_cast<float*>(w8 + l.dout);
+  float* hrow = reinterpret_cast<float*>(w8 + l.hrow);
+  float* crw = reinterpret_cast<float*>(w8 + l.crow);
+  float* gr = reinterpret_cast<float*>(w8 + l.grads);
+  float *dW = gr, *db = gr + nW, *dg = db + nb, *ds = dg + H;
+  hipLaunchKernelGGL(distill_loss_rows_kernel, dim3(blocks((size_t)Z * N, 4)), dim3(256), 0, s, t.lin, t.lm, T, g,
+                     sv, H, N, D, Z, L > 0 ? 1 : 0, dout, hrow, crw);
+  TTR_HIP(hipGetLastError());
+  hipLaunchKernelGGL(distill_loss_total_kernel, dim3(1), dim3(256), 0, s, hrow, crw, Z * N, D, sv, loss_out, ds);
+  TTR_HIP(hipGetLastError());
+  TTR_HIP(backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s));
+  AdamArgs a;
+  a.p[0] = W;
+  a.p[1] = bias;
+  a.p[2] = g;
+  a.p[3] = sv;
+  a.grad[0] = dW;
+  a.grad[1] = db;
+  a.grad[2] = dg;
+  a.grad[3] = ds;
+  a.moments = moments;
+  a.n[0] = (long long)nW;
+  a.n[1] = (long long)nb;
+  a.n[2] = H;
+  a.n[3] = 2;
+  a.lr = lr;
+  a.c1 = 1.f - powf(0.9f, (float)step);
+  a.c2 = 1.f - powf(0.999f, (float)step);
+  hipLaunchKernelGGL(adam_kernel, dim3(blocks(nW + nb + H + 2, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace ttr

@@ -102,4 +102,13 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
                                   const float* bias, const float* g, float eps, int L, const float* dout, float* dW,
                                   float* db, float* dg, void* ws, hipStream_t s);
 
+// Phase-1 distillation step (k_backward.hip): workspace after the backward's
+struct DistillLayout {
+  size_t w_io, teacher, dout, hrow, crow, grads, bytes;
+};
+DistillLayout distill_layout(const Problem& p, bool need_teacher);
+hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, const void* V, const float* teacher,
+                               float* W, float* bias, float* g, float* sv, float* moments, int step, float lr,
+                               float eps, int L, float* loss_out, void* ws, hipStream_t s);
+
 }  // namespace ttr

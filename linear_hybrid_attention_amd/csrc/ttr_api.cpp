@@ -447,4 +447,35 @@ ttr_status ttr_hybrid_backward(ttr_dims d, const void* Q, const void* K, const v
   return hip_status(launch_hybrid_backward(p, Q, K, V, W, b, g, eps, L, dout, dW, db, dg, ws, (hipStream_t)stream));
 }
 
+size_t ttr_distill_workspace_bytes(ttr_dims d, int32_t L, int32_t compute_teacher) {
+  if (check_backward(d, L) != TTR_OK) return 0;
+  return distill_layout(make_problem(d, true), compute_teacher != 0).bytes;
+}
+
+ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void* V, const float* teacher, float* W,
+                            float* b, float* g, float* s, float* moments, int32_t step, float lr, float eps, int32_t L,
+                            float* loss, void* ws, size_t ws_bytes, void* stream) {
+  TTR_TRY(check_backward(d, L));
+  if (step < 1 || !(lr > 0.f) || !(lr < 1e30f)) return TTR_ERR_SHAPE;
+  TTR_TRY(check_ptr(Q));
+  TTR_TRY(check_ptr(K));
+  TTR_TRY(check_ptr(V));
+  TTR_TRY(check_opt_ptr(teacher));
+  for (const void* ptr : {(const void*)W, (const void*)b, (const void*)g, (const void*)s, (const void*)moments,
+                          (const void*)loss})
+    TTR_TRY(check_ptr(ptr));
+  const Problem p = make_problem(d, true);
+  const size_t need = distill_layout(p, teacher == nullptr).bytes;
+  if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
+  TTR_TRY(check_ptr(ws));
+  const size_t nW = (size_t)d.H * d.D * d.F * 4, nb = (size_t)d.H * d.F * 4, ng = (size_t)d.H * 4;
+  const size_t nm = 2 * (nW + nb + ng + 8);
+  const Range outs[] = {{W, nW}, {b, nb}, {g, ng}, {s, 8}, {moments, nm}, {loss, 12}, {ws, need}};
+  const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)},
+                       {teacher, teacher ? f32_out_bytes(d) : 0}};
+  TTR_TRY(check_no_alias(outs, 7, ins, 4));
+  return hip_status(
+      launch_distill_step(p, Q, K, V, teacher, W, b, g, s, moments, step, lr, eps, L, loss, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"
