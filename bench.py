@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="flux_1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--distill", action="store_true",
+                    help="time one Phase-1 distillation step (teacher, student, loss, backward, Adam) instead")
+    ap.add_argument("--lr", type=float, default=1e-4, help="Adam learning rate of the distillation step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
@@ -399,6 +402,155 @@ def main_layer(args):
     print(json.dumps(res), flush=True)
 
 
+def distill_plan(w):
+    """Launches of one distillation step (teacher computed, bias present), in
+    order: (name, algorithmic flops, algorithmic bytes)."""
+    Z, N, D, F, L, B, H = w.B * w.H, w.N, w.D, w.F, w.L, w.B, w.H
+    io = 2 if w.dtype == "bf16" else 4
+    gemm_nd = 2 * Z * N * D * F  # every product of the layer is N x D x F per (b, h)
+    plan = []
+    if w.dtype == "bf16":
+        plan.append(("to_bf16_kernel (W)", 0, 0))
+    plan.append(("teacher softmax attention (hybrid_kernel, L = N)", 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
+    plan += [("bgemm z_q = Q W + b", gemm_nd, 0), ("bgemm z_k = K W + b", gemm_nd, 0),
+             ("colsum ksum", 0, 0), ("bgemm KV = phi_k^T V", gemm_nd, 0), ("bgemm num = phi_q KV", gemm_nd, 0),
+             ("den_lin_kernel", 2 * Z * N * F, 0)]
+    if L > 0:
+        plan.append(("landmark branch (hybrid_kernel)", 4 * Z * N * L * D, 0))
+    plan += [("distill_loss_rows_kernel", 0, 0), ("distill_loss_total_kernel", 0, 0), ("dlin_kernel", 0, 0),
+             ("bgemm dphi_q = dnum KV^T", gemm_nd, 0), ("bgemm dKV = phi_q^T dnum", gemm_nd, 0),
+             ("colsum dks", 2 * Z * N * F, 0), ("dz_kernel (q)", 0, 0), ("bgemm dphi_k = V dKV^T", gemm_nd, 0),
+             ("dz_kernel (k)", 0, 0), ("bgemm dW += Q^T dz_q", gemm_nd, 0), ("bgemm dW += K^T dz_k", gemm_nd, 0),
+             ("colsum db, dg", 0, 0), ("adam_kernel", 0, 0)]
+    return plan
+
+
+def cpu_baseline_distill(w, x, target_s, lr):
+    """The oracle's distillation step on the first heads of the same inputs, scaled to all heads."""
+    import numpy as np
+    import oracle.ttr_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+
+    def run(hs):
+        sl = slice(0, hs)
+        W, b, g = x["W"][sl], x["b"][sl], x["g"][sl]
+        st = {k: np.zeros_like(v) for k, v in (("mW", W), ("vW", W), ("mb", b), ("vb", b), ("mg", g), ("vg", g))}
+        st["ms"] = np.zeros(2)
+        st["vs"] = np.zeros(2)
+        t0 = time.perf_counter()
+        O.distill_step(x["Q"][:, sl], x["K"][:, sl], x["V"][:, sl], W, b, g, np.zeros(2), st, 1, lr, x["eps"], w.L)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    heads = int(max(1, min(w.H, target_s / max(t1, 1e-3))))
+    t = run(heads) if heads > 1 else t1
+    reps, total = 1, t
+    while total < target_s and reps < 64:
+        total += run(heads)
+        reps += 1
+    t = total / reps
+    sec_full = t * w.H / heads
+    sample = (f"{heads} of {w.H} heads (all {w.B} batch rows) of the {w.name} workload (N={w.N}), fp64 numpy oracle "
+              f"distillation step, {reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all heads")
+    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds_full_estimate": sec_full}
+
+
+def main_distill(args):
+    import ctypes
+    import numpy as np
+    import torch
+    import linear_hybrid_attention_amd as ttr
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    if w.causal or not w.proj:
+        print("--distill needs a non-causal workload with a projection", file=sys.stderr)
+        sys.exit(2)
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def io(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x[name]).to(dev)
+
+    Q, K, V = io("Q"), io("K"), io("V")
+    b = x["b"] if x["b"] is not None else np.zeros((w.H, w.F), np.float32)
+    state = ttr.DistillState(torch.from_numpy(x["W"]).to(dev), torch.from_numpy(b).to(dev),
+                             torch.from_numpy(x["g"]).to(dev))
+    lib = ttr.load_library()
+    d = ttr.Dims(w.B, w.H, w.N, w.D, w.F, 1 if w.dtype == "bf16" else 0, 0)
+    ws = torch.empty(lib.ttr_distill_workspace_bytes(d, w.L, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = distill_plan(w)
+    eps = float(x["eps"])
+
+    def step(events=None):
+        if events is not None:
+            lib.ttr_set_stage_events(events, len(plan) + 1)
+        return ttr.distill_step(state, Q, K, V, w.L, args.lr, eps, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nev = len(plan) + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in ev]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        loss = step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    last_loss = loss.cpu().tolist()
+    for i in range(args.steps):
+        step(handles[i])
+    torch.cuda.synchronize()
+    kern_ms = {name: float(np.mean([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)]))
+               for k, (name, _, _) in enumerate(plan)}
+    name, flops, nb = max(plan, key=lambda p: kern_ms[p[0]])
+    rl = roofline(w, flops, nb, kern_ms[name])
+    kernels = {}
+    for kn, kf, kb in plan:
+        r = roofline(w, kf, kb, kern_ms[kn]) if (kf or kb) else {"bound": None, "frac": None}
+        kernels[kn] = {"ms": kern_ms[kn], "flops": kf, "bytes": kb, "bound": r["bound"], "frac": r["frac"]}
+    total_flops = sum(p[1] for p in plan)
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    res = {
+        "metric": f"TTR distillation step tokens/sec ({w.name}: B={w.B}, H={w.H}, N={w.N}, L={w.L}; teacher, "
+                  "student, loss, backward and Adam)",
+        "value": w.B * w.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "mode": "distill", "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F, "L": w.L,
+                   "lr": args.lr, "global_batch": w.B, "seq_len": w.N},
+        "roofline": {"kernel": name, "bound": rl["bound"], "achieved": rl["achieved"], "peak": rl["peak"],
+                     "unit": rl["unit"], "frac": rl["frac"], "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nb,
+                     "avg_launch_ms": kern_ms[name]},
+        "forward": {"tflops": total_flops / (ms * 1e-3) / 1e12,
+                    "frac_mfma_peak": total_flops / (ms * 1e-3) / 1e12 / peak,
+                    "kernels": kernels, "wall_s": wall, "last_loss": last_loss},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_distill(w, x, args.cpu_seconds, args.lr)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -419,6 +571,9 @@ def main():
 
     if args.workload in workloads.LAYER_WORKLOADS:
         main_layer(args)
+        return
+    if args.distill:
+        main_distill(args)
         return
     w = workloads.WORKLOADS[args.workload]
     x = workloads.make_inputs(w)

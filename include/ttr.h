@@ -220,17 +220,24 @@ const char* ttr_status_string(ttr_status st);
 int ttr_last_hip_error(void);
 
 /* Per-kernel timing for profilers and benchmarks. After this call, the
- * calling thread's next ttr_hybrid_forward, ttr_causal_scan or
- * ttr_nnt_layer_forward records events[0] on its stream before its first
- * kernel and events[1], events[2], ... after each kernel it launches, as
- * long as events remain (bf16 hybrid: key/value partial sums, operand pack,
- * fused query kernel; fp32 hybrid: key/value reduction, query kernel;
- * causal: segment totals (when the sequence has several segments), chunk
- * walk; layer: the weight transposes, Q/K/V projection, the
- * attention's stages as above, out projection); events left over are
- * recorded after the last kernel. The registration is consumed by that one
- * call. events holds n hipEvent_t handles created by the caller;
- * NULL clears the registration. The events only observe: the enqueued
+ * calling thread's next ttr_hybrid_forward, ttr_causal_scan,
+ * ttr_nnt_layer_forward, ttr_hybrid_backward or ttr_distill_step records
+ * events[0] on its stream before its first kernel and events[1], events[2],
+ * ... after each kernel (or stage) it launches, as long as events remain:
+ *   bf16 hybrid: key/value partial sums, operand pack, fused query kernel;
+ *   fp32 hybrid: key/value reduction, query kernel;
+ *   causal: segment totals (when the sequence has several segments), chunk walk;
+ *   layer: the weight transposes, Q/K/V projection, the attention's stages
+ *     as above, out projection;
+ *   backward: Q projection, K projection (one stage each, whatever the batch),
+ *     ksum, KV, num, normaliser, landmark branch (L > 0), then dnum/dden,
+ *     dphi_q, dKV, dks, dz_q, dphi_k, dz_k, dW from Q, dW from K, db/dg;
+ *   distillation step: W to bf16 (bf16 IO), teacher (when computed), the
+ *     backward's forward stages, loss rows, loss total, the backward's
+ *     gradient stages, Adam.
+ * Events left over are recorded after the last kernel. The registration is
+ * consumed by that one call. events holds n hipEvent_t handles created by the
+ * caller; NULL clears the registration. The events only observe: the enqueued
  * kernels and results are the same with or without them. */
 void ttr_set_stage_events(void* const* events, int32_t n);
 

@@ -33,11 +33,16 @@ struct BgemmArgs {
   long long sBz, sBkb, sBk, sBn;
   long long sCz, sCm, sCn;
   int beta;
+  const float* bias_n;  // optional: C(m, n) += bias_n[z * sbz + n]
+  long long sbz;
+  int ksplit;           // > 1: blockIdx.z = z * ksplit + split; partial sums go to part
+  float* part;          // [Z][ksplit][M][N]
 };
 
 template <typename CT> struct BgTile {
-  static constexpr int KT = 32;                  // K per step
-  static constexpr int LD = KT + 16 / (int)sizeof(CT);  // padded row (16-byte multiple)
+  static constexpr int TM = 128;                          // rows of each operand tile (m or n)
+  static constexpr int KT = 32;                           // K per step
+  static constexpr int LD = KT + 16 / (int)sizeof(CT);    // padded row (16-byte multiple)
 };
 
 template <typename T> __device__ __forceinline__ float ld_elem(const T* p, long long i);
@@ -48,71 +53,125 @@ template <typename CT> __device__ __forceinline__ CT to_ct(float x);
 template <> __device__ __forceinline__ float to_ct<float>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t to_ct<uint16_t>(float x) { return f2bf(x); }
 
-// Loads one operand tile [64 rows][KT] of step (kb, k0) into registers: 8
-// elements per thread. Along k when the k stride is 1 (8 consecutive k per
-// thread), else along the rows (consecutive threads, consecutive rows).
-template <typename T, bool ELU>
-__device__ __forceinline__ void bg_load(float (&v)[8], const T* base, long long s_row, long long s_k, int row0,
-                                        int nrows, int k0, int K, bool k_contig, int tid) {
+// 16 consecutive elements at p (16-byte aligned) as floats
+template <typename T> __device__ __forceinline__ void ld16(const T* p, float (&v)[16]);
+template <> __device__ __forceinline__ void ld16<float>(const float* p, float (&v)[16]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int r, k;
-    if (k_contig) {
-      r = tid / 4;
-      k = (tid % 4) * 8 + i;
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 x = reinterpret_cast<const f32x4*>(p)[q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * q + j] = x[j];
+  }
+}
+template <> __device__ __forceinline__ void ld16<uint16_t>(const uint16_t* p, float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const u32x4 x = reinterpret_cast<const u32x4*>(p)[q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * q + 2 * j] = __uint_as_float(x[j] << 16);
+      v[8 * q + 2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+    }
+  }
+}
+
+// One operand tile [128 rows][KT] of one K-step into registers: 16 elements
+// per thread along the operand's contiguous dimension. k_contig: thread t
+// takes row t / 2, k (t % 2) * 16 .. + 15; else k t / 8 and rows
+// (t % 8) * 16 .. + 15. Whole runs inside the matrix and 16-byte aligned use
+// vector loads; others load element by element with bounds (zeros outside).
+// phi = elu + 1 applies to loaded elements only (outside stays 0).
+template <typename T, bool ELU>
+__device__ __forceinline__ void bg_load(float (&v)[16], const T* base, long long s_row, long long s_k, int row0,
+                                        int nrows, int k0, int K, bool k_contig, bool vec, int tid) {
+  if (k_contig) {
+    const int gr = row0 + tid / 2, gk = k0 + (tid % 2) * 16;
+    if (vec && gr < nrows && gk + 16 <= K) {
+      ld16<T>(base + (long long)gr * s_row + gk, v);  // s_k == 1 here
+      if (ELU)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = elu1(v[i]);
     } else {
-      r = tid % 64;
-      k = (tid / 64) * 8 + i;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = 0.f;
+        if (gr < nrows && gk + i < K) {
+          x = ld_elem<T>(base, (long long)gr * s_row + (long long)(gk + i) * s_k);
+          if (ELU) x = elu1(x);
+        }
+        v[i] = x;
+      }
     }
-    const int gr = row0 + r, gk = k0 + k;
-    float x = 0.f;
-    if (gr < nrows && gk < K) {
-      x = ld_elem<T>(base, (long long)gr * s_row + (long long)gk * s_k);
-      if (ELU) x = elu1(x);
+  } else {
+    const int gk = k0 + tid / 8, gr = row0 + (tid % 8) * 16;
+    if (vec && gk < K && gr + 16 <= nrows) {
+      ld16<T>(base + (long long)gk * s_k + gr, v);  // s_row == 1 here
+      if (ELU)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = elu1(v[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = 0.f;
+        if (gr + i < nrows && gk < K) {
+          x = ld_elem<T>(base, (long long)(gr + i) * s_row + (long long)gk * s_k);
+          if (ELU) x = elu1(x);
+        }
+        v[i] = x;
+      }
     }
-    v[i] = x;
   }
 }
 template <typename CT>
-__device__ __forceinline__ void bg_store(CT* tile, const float (&v)[8], bool k_contig, int tid) {
+__device__ __forceinline__ void bg_store(CT* tile, const float (&v)[16], bool k_contig, int tid) {
   constexpr int LD = BgTile<CT>::LD;
+  if (k_contig) {
+    CT* p = tile + (tid / 2) * LD + (tid % 2) * 16;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int r, k;
-    if (k_contig) {
-      r = tid / 4;
-      k = (tid % 4) * 8 + i;
-    } else {
-      r = tid % 64;
-      k = (tid / 64) * 8 + i;
-    }
-    tile[r * LD + k] = to_ct<CT>(v[i]);
+    for (int i = 0; i < 16; ++i) p[i] = to_ct<CT>(v[i]);
+  } else {
+    CT* p = tile + ((tid % 8) * 16) * LD + tid / 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i * LD] = to_ct<CT>(v[i]);
   }
 }
 
+// 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (2 x 2 MFMA tiles).
 template <typename CT, typename TA, typename TB, bool A_ELU>
 __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
-  constexpr int KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
-  __shared__ __attribute__((aligned(16))) CT As[64 * LD];
-  __shared__ __attribute__((aligned(16))) CT Bs[64 * LD];  // B^T: [64 n][KT]
+  constexpr int TM = BgTile<CT>::TM, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
+  __shared__ __attribute__((aligned(16))) CT As[TM * LD];
+  __shared__ __attribute__((aligned(16))) CT Bs[TM * LD];  // B^T: [128 n][KT]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int wm = w & 1, wn = w >> 1;
-  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64, z = blockIdx.z;
+  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TM, z = blockIdx.z / a.ksplit, split = blockIdx.z % a.ksplit;
   const TA* A = static_cast<const TA*>(a.A) + z * a.sAz;
   const TB* B = static_cast<const TB*>(a.B) + z * a.sBz;
   const bool a_kc = a.sAk == 1, b_kc = a.sBk == 1;
+  // vector loads need 16-byte aligned runs: every stride of the operand a multiple of 16 bytes
+  constexpr int PA = 16 / sizeof(TA), PB = 16 / sizeof(TB);
+  // (the run's own stride must be 1: k for k_contig, else the rows)
+  const bool a_vec = (a_kc || a.sAm == 1) && ((a_kc ? a.sAm : a.sAk) % PA == 0) && (a.sAz % PA == 0) &&
+                     (a.sAkb % PA == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0);
+  const bool b_vec = (b_kc || a.sBn == 1) && ((b_kc ? a.sBn : a.sBk) % PB == 0) && (a.sBz % PB == 0) &&
+                     (a.sBkb % PB == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
 
-  f32x16 acc = f32x16{};
-  float va[8], vb[8];
-  const int nks = (a.K + KT - 1) / KT, total = a.KB * nks;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  float va[16], vb[16];
+  const int nks = (a.K + KT - 1) / KT, steps = a.KB * nks;
+  const int per = (steps + a.ksplit - 1) / a.ksplit, s_begin = split * per, total = min(steps, s_begin + per);
   auto load = [&](int s) {
     const int kb = s / nks, k0 = (s % nks) * KT;
-    bg_load<TA, A_ELU>(va, A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a.K, a_kc, tid);
-    bg_load<TB, false>(vb, B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, a.K, b_kc, tid);
+    bg_load<TA, A_ELU>(va, A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a.K, a_kc, a_vec, tid);
+    bg_load<TB, false>(vb, B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, a.K, b_kc, b_vec, tid);
   };
-  load(0);
-  for (int s = 0; s < total; ++s) {
+  if (s_begin < total) load(s_begin);
+  for (int s = s_begin; s < total; ++s) {
     __syncthreads();  // every wave is done with the previous tile
     bg_store<CT>(As, va, a_kc, tid);
     bg_store<CT>(Bs, vb, b_kc, tid);
@@ -120,36 +179,88 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
     if (s + 1 < total) load(s + 1);  // in flight during the products
 #pragma unroll
     for (int kb = 0; kb < KT / 16; ++kb) {
-      const Frag<CT> fa = ld_frag<CT>(As + (wm * 32 + c) * LD + kb * 16 + 8 * g);
-      const Frag<CT> fb = ld_frag<CT>(Bs + (wn * 32 + c) * LD + kb * 16 + 8 * g);
-      mma(acc, fa, fb);
-    }
-  }
-  // lane (c, g) holds column n0 + wn*32 + c and rows crow(lane, r)
-  const int n = n0 + wn * 32 + c;
-  if (n < a.N) {
-    float* C = a.C + z * a.sCz + n * a.sCn;
+      Frag<CT> fa[2], fb[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 32 + crow(lane, r);
-      if (m < a.M) {
-        float* p = C + m * a.sCm;
-        *p = a.beta ? *p + acc[r] : acc[r];
-      }
+      for (int i = 0; i < 2; ++i) fa[i] = ld_frag<CT>(As + (wm * 64 + i * 32 + c) * LD + kb * 16 + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = ld_frag<CT>(Bs + (wn * 64 + j * 32 + c) * LD + kb * 16 + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma(acc[i][j], fa[i], fb[j]);
     }
   }
+  // lane (c, g) holds, per tile (i, j), column n0 + wn*64 + j*32 + c and rows crow(lane, r)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + c;
+    if (n >= a.N) continue;
+    const float bn = (a.ksplit == 1 && a.bias_n) ? a.bias_n[z * a.sbz + n] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + crow(lane, r);
+        if (m >= a.M) continue;
+        if (a.ksplit > 1) {
+          a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[i][j][r];
+        } else {
+          float* p = a.C + z * a.sCz + (long long)m * a.sCm + (long long)n * a.sCn;
+          *p = (a.beta ? *p + acc[i][j][r] : acc[i][j][r]) + bn;
+        }
+      }
+  }
+}
+
+// C[z](m, n) = (beta ? C : 0) + bias + sum_split part[z][split](m, n), splits in order
+__global__ void bgemm_reduce_kernel(BgemmArgs a, int Z) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t mn = (size_t)a.M * a.N;
+  if (i >= (size_t)Z * mn) return;
+  const int z = (int)(i / mn), m = (int)((i % mn) / a.N), n = (int)(i % a.N);
+  float* p = a.C + z * a.sCz + (long long)m * a.sCm + (long long)n * a.sCn;
+  float v = a.beta ? *p : 0.f;
+  const float* P = a.part + (size_t)z * a.ksplit * mn + (size_t)m * a.N + n;
+  for (int sp = 0; sp < a.ksplit; ++sp) v += P[(size_t)sp * mn];
+  if (a.bias_n) v += a.bias_n[z * a.sbz + n];
+  *p = v;
 }
 
 template <typename CT, typename TA, typename TB, bool ELU>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
-  const dim3 grid((a.M + 63) / 64, (a.N + 63) / 64, Z);
+  const dim3 grid((a.M + 127) / 128, (a.N + 127) / 128, Z * a.ksplit);
   hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU>), grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  const size_t n = (size_t)Z * a.M * a.N;
+  hipLaunchKernelGGL(bgemm_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, Z);
   return hipGetLastError();
 }
 
 // dtype: 1 = bf16 IO (bf16 MFMA), 0 = fp32 IO (fp32 MFMA). a_io / b_io: the
 // operand is in the IO dtype (else fp32).
-static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, const BgemmArgs& a, int Z, hipStream_t s) {
+// Split-K scratch of the backward: enough for 16 partial products of F x D per slice.
+static size_t splitk_elems(const Problem& p) { return (size_t)16 * p.B * p.H * p.F * p.D; }
+
+// A grid of few tiles with a long reduction splits K (at most 16 ways, at
+// least 8 steps each, aiming at about 2048 workgroups), when `scratch` holds
+// the partial products.
+static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, const BgemmArgs& a0, int Z, hipStream_t s,
+                               float* scratch = nullptr, size_t scratch_elems = 0) {
+  BgemmArgs a = a0;
+  a.ksplit = 1;
+  a.part = nullptr;
+  const int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128) * Z;
+  const int steps = a.KB * ((a.K + 31) / 32);
+  if (scratch != nullptr && tiles < 512 && steps >= 32) {
+    int ks = min(16, max(1, 2048 / tiles));
+    ks = min(ks, steps / 8);
+    while (ks > 1 && (size_t)ks * Z * a.M * a.N > scratch_elems) --ks;
+    if (ks > 1) {
+      a.ksplit = ks;
+      a.part = scratch;
+    }
+  }
   if (dtype == 1) {
     if (a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false>(a, Z, s);
     if (a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false>(a, Z, s);
@@ -164,15 +275,45 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
 }
 
 // ---------------------------------------------------------------- small kernels
-// ks[z][f] = sum_n phi(z_k[z][n][f])
-__global__ void colsum_phi_kernel(const float* zk, float* ks, int Z, int N, int F) {
+// Column sums with a fixed order, in two passes:
+//   out[z][f] = sum_{r < R} val(z, r, f)
+// row r of slice z at src + z * sz + (r / rb) * sblk + (r % rb) * F;
+//   MODE 0: val = phi(x); 1: phi(x) * wv[z * R + r]; 2: x + src2[same]; 3: x.
+// Pass 1 (grid Z x F/64 x NSPLIT): 64 columns by 4 row groups per workgroup,
+// each group a strided run of its split's rows, combined in group order.
+// Pass 2 adds the splits in order.
+constexpr int kColSplit = 32;
+template <int MODE>
+__global__ __launch_bounds__(256) void colsum_part_kernel(const float* src, const float* src2, const float* wv,
+                                                          long long sz, int rb, long long sblk, int R, int F,
+                                                          float* part) {
+  __shared__ float sh[4][64];
+  const int z = blockIdx.x, f = blockIdx.y * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6, sp = blockIdx.z;
+  const int per = (R + kColSplit - 1) / kColSplit, r0 = sp * per, r1 = min(R, r0 + per);
+  float acc = 0.f;
+  if (f < F) {
+    for (int r = r0 + grp; r < r1; r += 4) {
+      const size_t off = (size_t)z * sz + (size_t)(r / rb) * sblk + (size_t)(r % rb) * F + f;
+      const float x = src[off];
+      if constexpr (MODE == 0) acc += elu1(x);
+      else if constexpr (MODE == 1) acc += elu1(x) * wv[(size_t)z * R + r];
+      else if constexpr (MODE == 2) acc += x + src2[off];
+      else acc += x;
+    }
+  }
+  sh[grp][threadIdx.x & 63] = acc;
+  __syncthreads();
+  if (grp == 0 && f < F)
+    part[((size_t)z * kColSplit + sp) * F + f] = ((sh[0][threadIdx.x] + sh[1][threadIdx.x]) + sh[2][threadIdx.x]) +
+                                                 sh[3][threadIdx.x];
+}
+__global__ void colsum_final_kernel(const float* part, int Z, int F, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= Z * F) return;
   const int z = i / F, f = i % F;
-  const float* p = zk + (size_t)z * N * F + f;
   float s = 0.f;
-  for (int n = 0; n < N; ++n) s += elu1(p[(size_t)n * F]);
-  ks[i] = s;
+  for (int sp = 0; sp < kColSplit; ++sp) s += part[((size_t)z * kColSplit + sp) * F + f];
+  out[i] = s;
 }
 
 // Per row (z, n), one wave: den = phi(z_q) . ks + eps; lin = num / den (in place).
@@ -233,66 +374,25 @@ __global__ void dz_kernel(float* dphi, const float* zv, const float* r, const fl
   dphi[i] = x > 0.f ? dp : dp * __expf(x);
 }
 
-// dks[z][f] = sum_n phi(z_q[z][n][f]) dden[z][n]
-__global__ void dks_kernel(const float* zq, const float* dden, float* dks, int Z, int N, int F) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= Z * F) return;
-  const int z = i / F, f = i % F;
-  const float* p = zq + (size_t)z * N * F + f;
-  const float* dd = dden + (size_t)z * N;
-  float s = 0.f;
-  for (int n = 0; n < N; ++n) s += elu1(p[(size_t)n * F]) * dd[n];
-  dks[i] = s;
-}
-
-// db[h][f] = sum_b sum_n dzq + dzk; dg[h] = alpha (1 - alpha) sum_b sum_n rpart
-__global__ void db_dg_kernel(const float* dzq, const float* dzk, const float* rpart, const float* g, int B, int H, int N,
-                             int F, int has_lm, float* db, float* dg) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < H * F) {
-    const int h = i / F, f = i % F;
-    float s = 0.f;
-    for (int b = 0; b < B; ++b) {
-      const size_t base = ((size_t)(b * H + h) * N) * F + f;
-      for (int n = 0; n < N; ++n) s += dzq[base + (size_t)n * F] + dzk[base + (size_t)n * F];
-    }
-    db[i] = s;
-  }
-  if (i < H) {
-    float s = 0.f;
-    if (has_lm) {
-      for (int b = 0; b < B; ++b) {
-        const float* rp = rpart + (size_t)(b * H + i) * N;
-        for (int n = 0; n < N; ++n) s += rp[n];
-      }
-      const float al = 1.f / (1.f + expf(-g[i]));
-      s *= al * (1.f - al);
-    }
-    dg[i] = s;
-  }
-}
-
-// z[b,h][n][f] += bias[h][f] for both projections
-__global__ void add_bias_kernel(float* zq, float* zk, const float* bias, int H, int N, int F, size_t total) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int f = (int)(i % F);
-  const int h = (int)((i / ((size_t)N * F)) % H);
-  const float bv = bias[(size_t)h * F + f];
-  zq[i] += bv;
-  zk[i] += bv;
+// dg[h] *= alpha (1 - alpha) (or 0 without the landmark branch)
+__global__ void dg_scale_kernel(float* dg, const float* g, int H, int has_lm) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  const float al = has_lm ? 1.f / (1.f + expf(-g[h])) : 0.f;
+  dg[h] = has_lm ? dg[h] * al * (1.f - al) : 0.f;
 }
 
 // ---------------------------------------------------------------- launches
 static unsigned blocks(size_t n, unsigned t) { return (unsigned)((n + t - 1) / t); }
 
-static hipError_t launch_add_bias(float* zq, float* zk, const float* bias, int B, int H, int N, int F, hipStream_t s) {
-  const size_t total = (size_t)B * H * N * F;
-  hipLaunchKernelGGL(add_bias_kernel, dim3(blocks(total, 256)), dim3(256), 0, s, zq, zk, bias, H, N, F, total);
-  return hipGetLastError();
-}
-static hipError_t launch_colsum_phi(const float* zk, float* ks, int Z, int N, int F, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_phi_kernel, dim3(blocks((size_t)Z * F, 256)), dim3(256), 0, s, zk, ks, Z, N, F);
+template <int MODE>
+static hipError_t launch_colsum(const float* src, const float* src2, const float* wv, long long sz, int rb,
+                                long long sblk, int R, int Z, int F, float* part, float* out, hipStream_t s) {
+  hipLaunchKernelGGL((colsum_part_kernel<MODE>), dim3(Z, (F + 63) / 64, kColSplit), dim3(256), 0, s, src, src2, wv, sz,
+                     rb, sblk, R, F, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3(blocks((size_t)Z * F, 256)), dim3(256), 0, s, part, Z, F, out);
   return hipGetLastError();
 }
 static hipError_t launch_den_lin(const float* zq, const float* ks, float* num, float* den, int Z, int N, int F, int D,
@@ -308,22 +408,11 @@ static hipError_t launch_dlin(const float* dout, const float* lin, const float* 
                      has_lm ? 1 : 0, dnum, dden, rpart);
   return hipGetLastError();
 }
-static hipError_t launch_dks(const float* zq, const float* dden, float* dks, int Z, int N, int F, hipStream_t s) {
-  hipLaunchKernelGGL(dks_kernel, dim3(blocks((size_t)Z * F, 256)), dim3(256), 0, s, zq, dden, dks, Z, N, F);
-  return hipGetLastError();
-}
 static hipError_t launch_dz(float* dphi, const float* zv, const float* r, const float* sv, int Z, int N, int F,
                             hipStream_t s) {
   hipLaunchKernelGGL(dz_kernel, dim3(blocks((size_t)Z * N * F, 256)), dim3(256), 0, s, dphi, zv, r, sv, Z, N, F);
   return hipGetLastError();
 }
-static hipError_t launch_db_dg(const float* dzq, const float* dzk, const float* rpart, const float* g, int B, int H,
-                               int N, int F, bool has_lm, float* db, float* dg, hipStream_t s) {
-  hipLaunchKernelGGL(db_dg_kernel, dim3(blocks((size_t)H * F, 256)), dim3(256), 0, s, dzq, dzk, rpart, g, B, H, N, F,
-                     has_lm ? 1 : 0, db, dg);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------- host side
 BackwardLayout backward_layout(const Problem& p) {
   BackwardLayout l;
@@ -348,6 +437,8 @@ BackwardLayout backward_layout(const Problem& p) {
   l.den = take(Z * N);
   l.dden = take(Z * N);
   l.rpart = take(Z * N);
+  l.colpart = take(Z * kColSplit * F);
+  l.splitk = take(splitk_elems(p));
   l.bytes = o;
   return l;
 }
@@ -360,20 +451,23 @@ BackwardLayout backward_layout(const Problem& p) {
 
 // Workspace views of the backward's fp32 intermediates.
 struct BwBufs {
-  float *zq, *zk, *dzq, *dzk, *lin, *lm, *dnum, *kv, *dkv, *ks, *dks, *den, *dden, *rpart;
+  float *zq, *zk, *dzq, *dzk, *lin, *lm, *dnum, *kv, *dkv, *ks, *dks, *den, *dden, *rpart, *colpart, *splitk;
+  size_t splitk_n;
 };
 static BwBufs bw_bufs(const Problem& p, void* ws) {
   const BackwardLayout l = backward_layout(p);
   unsigned char* w8 = static_cast<unsigned char*>(ws);
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w8 + off); };
-  return BwBufs{F32(l.zq),  F32(l.zk), F32(l.dzq), F32(l.dzk), F32(l.lin), F32(l.lm),  F32(l.dnum),
-                F32(l.kv),  F32(l.dkv), F32(l.ks), F32(l.dks), F32(l.den), F32(l.dden), F32(l.rpart)};
+  return BwBufs{F32(l.zq),  F32(l.zk),  F32(l.dzq),  F32(l.dzk),   F32(l.lin),     F32(l.lm),
+                F32(l.dnum), F32(l.kv),  F32(l.dkv),  F32(l.ks),    F32(l.dks),     F32(l.den),
+                F32(l.dden), F32(l.rpart), F32(l.colpart), F32(l.splitk), splitk_elems(p)};
 }
 
 // Forward pass with the intermediates the gradients need: z_q, z_k (biased),
 // ks, KV, den, lin = num / den and (L > 0) the landmark output lm.
 static hipError_t backward_forward_pass(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
-                                        const float* bias, float eps, int L, const BwBufs& t, hipStream_t s) {
+                                        const float* bias, float eps, int L, const BwBufs& t, hipStream_t s,
+                                        StageTimer* tm) {
   float *zq = t.zq, *zk = t.zk, *lin = t.lin, *lm = t.lm, *kv = t.kv, *ks = t.ks, *den = t.den;
   const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H, dt = p.dtype;
   const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
@@ -402,16 +496,20 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
       ab.C = Zout + (size_t)b * H * NF;
       ab.sBz = (long long)D * F;
       ab.sCz = NF;
+      ab.bias_n = bias;  // z = h within one batch row
+      ab.sbz = F;
       TTR_HIP(launch_bgemm(dt, true, true, false, ab, H, s));
     }
     return hipSuccess;
   };
   TTR_HIP(proj(Q, zq));
+  tm->mark();
   TTR_HIP(proj(K, zk));
-  if (bias != nullptr) TTR_HIP(launch_add_bias(zq, zk, bias, B, H, N, F, s));
+  tm->mark();
 
   // ks = sum_n phi(z_k); KV = phi(z_k)^T V
-  TTR_HIP(launch_colsum_phi(zk, ks, Z, N, F, s));
+  TTR_HIP(launch_colsum<0>(zk, nullptr, nullptr, NF, N, 0, N, Z, F, t.colpart, ks, s));
+  tm->mark();
   {
     BgemmArgs a{};
     a.A = zk;  // A(m = f, k = n) = phi(z_k[n][f])
@@ -430,7 +528,8 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     a.sCz = FD;
     a.sCm = D;
     a.sCn = 1;
-    TTR_HIP(launch_bgemm(dt, false, true, true, a, Z, s));
+    TTR_HIP(launch_bgemm(dt, false, true, true, a, Z, s, t.splitk, t.splitk_n));
+    tm->mark();
   }
   // num = phi(z_q) KV -> lin (in place after den)
   {
@@ -452,8 +551,10 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     a.sCm = D;
     a.sCn = 1;
     TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s));
+    tm->mark();
   }
   TTR_HIP(launch_den_lin(zq, ks, lin, den, Z, N, F, D, eps, s));
+  tm->mark();
   // landmark branch output (fp32), for dalpha
   if (L > 0) {
     HybridArgs ha = {};
@@ -468,6 +569,7 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     pl.proj = false;
     pl.F = p.D;
     TTR_HIP(launch_hybrid(pl, M_LM, false, ha, s));
+    tm->mark();
   }
   return hipSuccess;
 }
@@ -475,13 +577,14 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
 // Gradients from dout, after backward_forward_pass filled t.
 static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void* K, const void* V, const float* g,
                                      int L, const float* dout, float* dW, float* db, float* dg, const BwBufs& t,
-                                     hipStream_t s) {
+                                     hipStream_t s, StageTimer* tm) {
   float *zq = t.zq, *zk = t.zk, *dzq = t.dzq, *dzk = t.dzk, *lin = t.lin, *lm = t.lm, *dnum = t.dnum, *kv = t.kv;
   float *dkv = t.dkv, *ks = t.ks, *dks = t.dks, *den = t.den, *dden = t.dden, *rpart = t.rpart;
   const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H, dt = p.dtype;
   const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
   // dnum, dden, dalpha row shares
   TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, N, D, Z, L > 0, dnum, dden, rpart, s));
+  tm->mark();
   // dphi_q = dnum KV^T (+ dden ks^T in dz): [N x D] . [D x F]
   {
     BgemmArgs a{};
@@ -502,6 +605,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCm = F;
     a.sCn = 1;
     TTR_HIP(launch_bgemm(dt, false, false, false, a, Z, s));
+    tm->mark();
   }
   // dKV = phi(z_q)^T dnum: [F x N] . [N x D]; dks = phi(z_q)^T dden
   {
@@ -522,11 +626,14 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCz = FD;
     a.sCm = D;
     a.sCn = 1;
-    TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s));
+    TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s, t.splitk, t.splitk_n));
+    tm->mark();
   }
-  TTR_HIP(launch_dks(zq, dden, dks, Z, N, F, s));
+  TTR_HIP(launch_colsum<1>(zq, nullptr, dden, NF, N, 0, N, Z, F, t.colpart, dks, s));
+  tm->mark();
   // dz_q = (dphi_q + dden ks^T) phi'(z_q)
   TTR_HIP(launch_dz(dzq, zq, dden, ks, Z, N, F, s));
+  tm->mark();
   // dphi_k = V dKV^T (+ dks in dz): [N x D] . [D x F]
   {
     BgemmArgs a{};
@@ -547,8 +654,10 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCm = F;
     a.sCn = 1;
     TTR_HIP(launch_bgemm(dt, true, false, false, a, Z, s));
+    tm->mark();
   }
   TTR_HIP(launch_dz(dzk, zk, nullptr, dks, Z, N, F, s));
+  tm->mark();
   // dW[h] = sum_b Q[b,h]^T dz_q[b,h] + K[b,h]^T dz_k[b,h]: the batch is the outer K loop
   auto dw = [&](const void* X, const float* dzv, int beta) {
     BgemmArgs a{};
@@ -571,29 +680,36 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCm = F;
     a.sCn = 1;
     a.beta = beta;
-    return launch_bgemm(dt, true, false, false, a, H, s);
+    return launch_bgemm(dt, true, false, false, a, H, s, t.splitk, t.splitk_n);
   };
   TTR_HIP(dw(Q, dzq, 0));
+  tm->mark();
   TTR_HIP(dw(K, dzk, 1));
-  TTR_HIP(launch_db_dg(dzq, dzk, rpart, g, B, H, N, F, L > 0, db, dg, s));
+  tm->mark();
+  // db[h] over rows (b, n) of slice h; dg[h] from the row shares of dalpha
+  TTR_HIP(launch_colsum<2>(dzq, dzk, nullptr, NF, N, (long long)H * NF, B * N, H, F, t.colpart, db, s));
+  TTR_HIP(launch_colsum<3>(rpart, nullptr, nullptr, N, N, (long long)H * N, B * N, H, 1, t.colpart, dg, s));
+  hipLaunchKernelGGL(dg_scale_kernel, dim3(blocks(H, 64)), dim3(64), 0, s, dg, g, H, L > 0 ? 1 : 0);
+  TTR_HIP(hipGetLastError());
+  tm->mark();
   return hipSuccess;
 }
 
 hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
                                   const float* bias, const float* g, float eps, int L, const float* dout, float* dW,
-                                  float* db, float* dg, void* ws, hipStream_t s) {
+                                  float* db, float* dg, void* ws, hipStream_t s, StageTimer* tm) {
   const BwBufs t = bw_bufs(p, ws);
-  TTR_HIP(backward_forward_pass(p, Q, K, V, W, bias, eps, L, t, s));
-  return backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s);
+  TTR_HIP(backward_forward_pass(p, Q, K, V, W, bias, eps, L, t, s, tm));
+  return backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s, tm);
 }
 
 // ---------------------------------------------------------------- distillation step
 // Per row (z, n), one wave: o = alpha lin + (1 - alpha) lm (lin alone when L == 0),
 // t = the teacher row; writes dout = w1 clip(o - t, -1, 1) / numel - w2 dcos / rows,
 // the row's huber sum and 1 - cos. w = exp(-s).
-__global__ void distill_loss_rows_kernel(const float* lin, const float* lm, const float* teacher, const float* g,
-                                         const float* sv, int H, int N, int D, int Z, int has_lm, float* dout,
-                                         float* hrow, float* crow_) {
+__global__ void distill_loss_rows_kernel(const float* lin, const float* lm, const float* teacher,
+                                         const uint16_t* teacher_bf16, const float* g, const float* sv, int H, int N,
+                                         int D, int Z, int has_lm, float* dout, float* hrow, float* crow_) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= Z * N) return;
   const int h = (row / N) % H;
@@ -602,7 +718,7 @@ __global__ void distill_loss_rows_kernel(const float* lin, const float* lm, cons
   const float inv_numel = 1.f / ((float)Z * N * D), inv_rows = 1.f / ((float)Z * N);
   const float* li = lin + (size_t)row * D;
   const float* lr = lm + (size_t)row * D;
-  const float* tr = teacher + (size_t)row * D;
+  const size_t trow = (size_t)row * D;
   float ov[4], tv[4];  // D <= 256: up to 4 elements per lane
   float hs = 0.f, dot = 0.f, oo = 0.f, tt = 0.f;
 #pragma unroll
@@ -611,7 +727,7 @@ __global__ void distill_loss_rows_kernel(const float* lin, const float* lm, cons
     float o = 0.f, t = 0.f;
     if (d < D) {
       o = has_lm ? alpha * li[d] + (1.f - alpha) * lr[d] : li[d];
-      t = tr[d];
+      t = teacher_bf16 ? bf2f(teacher_bf16[trow + d]) : teacher[trow + d];
       const float r = o - t, ar = fabsf(r);
       hs += ar <= 1.f ? 0.5f * r * r : ar - 0.5f;
     }
@@ -647,14 +763,17 @@ __global__ void distill_loss_rows_kernel(const float* lin, const float* lm, cons
   }
 }
 
-// One workgroup: H = sum hrow / numel, C = sum crow / rows (fixed order);
-// loss = w1 H + s1 + w2 C + s2; ds = (1 - w1 H, 1 - w2 C). out: loss, H, C.
-__global__ void distill_loss_total_kernel(const float* hrow, const float* crow_, int rows, int D, const float* sv,
-                                          float* loss_out, float* ds) {
+// Loss totals in two fixed-order levels: workgroup k sums rows
+// [k * kLossRows, (k + 1) * kLossRows) into part[2k], part[2k + 1]; one
+// workgroup then adds the parts in order and forms
+// loss = w1 H + s1 + w2 C + s2, H = sum hrow / numel, C = sum crow / rows,
+// ds = (1 - w1 H, 1 - w2 C). out: loss, H, C.
+constexpr int kLossRows = 4096;
+__global__ void distill_loss_part_kernel(const float* hrow, const float* crow_, int rows, float* part) {
   __shared__ float sh[256], sc[256];
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, r0 = blockIdx.x * kLossRows, r1 = min(rows, r0 + kLossRows);
   float h = 0.f, c = 0.f;
-  for (int i = t; i < rows; i += 256) {
+  for (int i = r0 + t; i < r1; i += 256) {
     h += hrow[i];
     c += crow_[i];
   }
@@ -669,14 +788,25 @@ __global__ void distill_loss_total_kernel(const float* hrow, const float* crow_,
     __syncthreads();
   }
   if (t == 0) {
-    const float H = sh[0] / ((float)rows * D), C = sc[0] / (float)rows;
-    const float w1 = expf(-sv[0]), w2 = expf(-sv[1]);
-    loss_out[0] = w1 * H + sv[0] + w2 * C + sv[1];
-    loss_out[1] = H;
-    loss_out[2] = C;
-    ds[0] = 1.f - w1 * H;
-    ds[1] = 1.f - w2 * C;
+    part[2 * blockIdx.x] = sh[0];
+    part[2 * blockIdx.x + 1] = sc[0];
   }
+}
+__global__ void distill_loss_total_kernel(const float* part, int nparts, int rows, int D, const float* sv,
+                                          float* loss_out, float* ds) {
+  if (threadIdx.x != 0) return;
+  float hs = 0.f, cs = 0.f;
+  for (int k = 0; k < nparts; ++k) {
+    hs += part[2 * k];
+    cs += part[2 * k + 1];
+  }
+  const float H = hs / ((float)rows * D), C = cs / (float)rows;
+  const float w1 = expf(-sv[0]), w2 = expf(-sv[1]);
+  loss_out[0] = w1 * H + sv[0] + w2 * C + sv[1];
+  loss_out[1] = H;
+  loss_out[2] = C;
+  ds[0] = 1.f - w1 * H;
+  ds[1] = 1.f - w2 * C;
 }
 
 // Adam over the parameter blocks (W, b, g, s) with their gradients; moments
@@ -708,6 +838,11 @@ __global__ void adam_kernel(AdamArgs a) {
   }
 }
 
+__global__ void fill_kernel(float* x, float v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = v;
+}
+
 // fp32 -> bf16 (round to nearest even)
 __global__ void to_bf16_kernel(const float* x, uint16_t* y, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -721,8 +856,16 @@ DistillLayout distill_layout(const Problem& p, bool need_teacher) {
   size_t o = al(backward_layout(p).bytes);
   l.w_io = o;
   o += al(p.dtype == 1 ? H * D * F * 2 : 0);
-  l.teacher = o;
-  o += al(need_teacher ? Z * N * D * 4 : 0);
+  l.teacher = o;  // fp32 teacher (fp32 IO), or bf16 teacher, -inf gates and the fused path's workspace (bf16 IO)
+  if (need_teacher) {
+    if (p.dtype == 1) {
+      l.gneg = o + al(Z * N * D * 2);
+      l.tws = l.gneg + al(H * 4);
+      o = l.tws + al(fused_workspace_bytes(p, p.N));
+    } else {
+      o += al(Z * N * D * 4);
+    }
+  }
   l.dout = o;
   o += al(Z * N * D * 4);
   l.hrow = o;
@@ -731,13 +874,15 @@ DistillLayout distill_layout(const Problem& p, bool need_teacher) {
   o += al(Z * N * 4);
   l.grads = o;  // dW | db | dg | ds
   o += al((H * D * F + H * F + H + 2) * 4);
+  l.lpart = o;
+  o += al(2 * ((Z * N + kLossRows - 1) / kLossRows) * 4);
   l.bytes = o;
   return l;
 }
 
 hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, const void* V, const float* teacher,
                                float* W, float* bias, float* g, float* sv, float* moments, int step, float lr,
-                               float eps, int L, float* loss_out, void* ws, hipStream_t s) {
+                               float eps, int L, float* loss_out, void* ws, hipStream_t s, StageTimer* tm) {
   const DistillLayout l = distill_layout(p, teacher == nullptr);
   unsigned char* w8 = static_cast<unsigned char*>(ws);
   const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H;
@@ -748,39 +893,62 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
     uint16_t* wb = reinterpret_cast<uint16_t*>(w8 + l.w_io);
     hipLaunchKernelGGL(to_bf16_kernel, dim3(blocks(nW, 256)), dim3(256), 0, s, W, wb, nW);
     TTR_HIP(hipGetLastError());
+    tm->mark();
     Wio = wb;
   }
-  // teacher: softmax over every token (the landmark branch with L = N)
+  // Teacher: softmax over every token. bf16: the fused hybrid path with every
+  // token a landmark and alpha = sigmoid(-inf) = 0 exactly (the linear branch
+  // is multiplied by 0), output in bf16; fp32: the landmark branch with L = N.
   const float* T = teacher;
-  if (T == nullptr) {
-    float* tw = reinterpret_cast<float*>(w8 + l.teacher);
-    HybridArgs ha = {};
-    ha.Q = Q;
-    ha.K = K;
-    ha.V = V;
-    ha.H = H;
-    ha.N = N;
-    ha.L = N;
-    ha.out = tw;
-    Problem pl = p;
-    pl.proj = false;
-    pl.F = p.D;
-    TTR_HIP(launch_hybrid(pl, M_LM, false, ha, s));
-    T = tw;
+  const uint16_t* Tb = nullptr;
+  if (teacher == nullptr) {
+    if (p.dtype == 1) {
+      uint16_t* tb = reinterpret_cast<uint16_t*>(w8 + l.teacher);
+      float* gneg = reinterpret_cast<float*>(w8 + l.gneg);
+      hipLaunchKernelGGL(fill_kernel, dim3(blocks(H, 64)), dim3(64), 0, s, gneg, -INFINITY, H);
+      TTR_HIP(hipGetLastError());
+      FusedPack pk;
+      StageTimer none;
+      TTR_HIP(launch_kv2(p, K, V, Wio, bias, N, w8 + l.tws, &pk, s, &none));
+      TTR_HIP(launch_fused_query(p, Q, pk, gneg, eps, N, tb, s));
+      Tb = tb;
+    } else {
+      float* tw = reinterpret_cast<float*>(w8 + l.teacher);
+      HybridArgs ha = {};
+      ha.Q = Q;
+      ha.K = K;
+      ha.V = V;
+      ha.H = H;
+      ha.N = N;
+      ha.L = N;
+      ha.out = tw;
+      Problem pl = p;
+      pl.proj = false;
+      pl.F = p.D;
+      TTR_HIP(launch_hybrid(pl, M_LM, false, ha, s));
+      T = tw;
+    }
+    tm->mark();
   }
   const BwBufs t = bw_bufs(p, ws);
-  TTR_HIP(backward_forward_pass(p, Q, K, V, Wio, bias, eps, L, t, s));
+  TTR_HIP(backward_forward_pass(p, Q, K, V, Wio, bias, eps, L, t, s, tm));
   float* dout = reinterpret_cast<float*>(w8 + l.dout);
   float* hrow = reinterpret_cast<float*>(w8 + l.hrow);
   float* crw = reinterpret_cast<float*>(w8 + l.crow);
   float* gr = reinterpret_cast<float*>(w8 + l.grads);
   float *dW = gr, *db = gr + nW, *dg = db + nb, *ds = dg + H;
-  hipLaunchKernelGGL(distill_loss_rows_kernel, dim3(blocks((size_t)Z * N, 4)), dim3(256), 0, s, t.lin, t.lm, T, g,
-                     sv, H, N, D, Z, L > 0 ? 1 : 0, dout, hrow, crw);
+  hipLaunchKernelGGL(distill_loss_rows_kernel, dim3(blocks((size_t)Z * N, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
+                     g, sv, H, N, D, Z, L > 0 ? 1 : 0, dout, hrow, crw);
   TTR_HIP(hipGetLastError());
-  hipLaunchKernelGGL(distill_loss_total_kernel, dim3(1), dim3(256), 0, s, hrow, crw, Z * N, D, sv, loss_out, ds);
+  tm->mark();
+  float* lpart = reinterpret_cast<float*>(w8 + l.lpart);
+  const int nparts = (Z * N + kLossRows - 1) / kLossRows;
+  hipLaunchKernelGGL(distill_loss_part_kernel, dim3(nparts), dim3(256), 0, s, hrow, crw, Z * N, lpart);
   TTR_HIP(hipGetLastError());
-  TTR_HIP(backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s));
+  hipLaunchKernelGGL(distill_loss_total_kernel, dim3(1), dim3(64), 0, s, lpart, nparts, Z * N, D, sv, loss_out, ds);
+  TTR_HIP(hipGetLastError());
+  tm->mark();
+  TTR_HIP(backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s, tm));
   AdamArgs a;
   a.p[0] = W;
   a.p[1] = bias;
@@ -799,7 +967,9 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
   a.c1 = 1.f - powf(0.9f, (float)step);
   a.c2 = 1.f - powf(0.999f, (float)step);
   hipLaunchKernelGGL(adam_kernel, dim3(blocks(nW + nb + H + 2, 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  TTR_HIP(hipGetLastError());
+  tm->mark();
+  return hipSuccess;
 }
 
 }  // namespace ttr

@@ -95,20 +95,20 @@ hipError_t launch_proj_gemm(int dtype, bool a_heads, bool c_qkv, const void* A, 
 // k_backward.hip: gradients of the hybrid forward for W, b, g (fp32
 // intermediates in the workspace, byte offsets below).
 struct BackwardLayout {
-  size_t zq, zk, dzq, dzk, lin, lm, dnum, kv, dkv, ks, dks, den, dden, rpart, bytes;
+  size_t zq, zk, dzq, dzk, lin, lm, dnum, kv, dkv, ks, dks, den, dden, rpart, colpart, splitk, bytes;
 };
 BackwardLayout backward_layout(const Problem& p);
 hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
                                   const float* bias, const float* g, float eps, int L, const float* dout, float* dW,
-                                  float* db, float* dg, void* ws, hipStream_t s);
+                                  float* db, float* dg, void* ws, hipStream_t s, StageTimer* t);
 
 // Phase-1 distillation step (k_backward.hip): workspace after the backward's
 struct DistillLayout {
-  size_t w_io, teacher, dout, hrow, crow, grads, bytes;
+  size_t w_io, teacher, gneg, tws, dout, hrow, crow, grads, lpart, bytes;
 };
 DistillLayout distill_layout(const Problem& p, bool need_teacher);
 hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, const void* V, const float* teacher,
                                float* W, float* bias, float* g, float* sv, float* moments, int step, float lr,
-                               float eps, int L, float* loss_out, void* ws, hipStream_t s);
+                               float eps, int L, float* loss_out, void* ws, hipStream_t s, StageTimer* t);
 
 }  // namespace ttr

@@ -444,7 +444,11 @@ ttr_status ttr_hybrid_backward(ttr_dims d, const void* Q, const void* K, const v
   const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {W, w_bytes(d)},
                        {b, b ? b_bytes(d) : 0}, {g, g ? (size_t)d.H * 4 : 0}, {dout, f32_out_bytes(d)}};
   TTR_TRY(check_no_alias(outs, 4, ins, 7));
-  return hip_status(launch_hybrid_backward(p, Q, K, V, W, b, g, eps, L, dout, dW, db, dg, ws, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  StageTimer t = take_stage_timer(st);
+  const ttr_status r = hip_status(launch_hybrid_backward(p, Q, K, V, W, b, g, eps, L, dout, dW, db, dg, ws, st, &t));
+  t.finish();
+  return r;
 }
 
 size_t ttr_distill_workspace_bytes(ttr_dims d, int32_t L, int32_t compute_teacher) {
@@ -474,8 +478,12 @@ ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void
   const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)},
                        {teacher, teacher ? f32_out_bytes(d) : 0}};
   TTR_TRY(check_no_alias(outs, 7, ins, 4));
-  return hip_status(
-      launch_distill_step(p, Q, K, V, teacher, W, b, g, s, moments, step, lr, eps, L, loss, ws, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  StageTimer t = take_stage_timer(st);
+  const ttr_status r = hip_status(
+      launch_distill_step(p, Q, K, V, teacher, W, b, g, s, moments, step, lr, eps, L, loss, ws, st, &t));
+  t.finish();
+  return r;
 }
 
 }  // extern "C"
