@@ -57,6 +57,18 @@ bias-corrected, no weight decay) updates W, b, g and s. The backward gives
 the gradients of the trainable parameters W, b, g (Q, K, V are the frozen
 model's activations).
 
+Readiness gating and the landmark count ("Flux2TTRTrainer", section "How the
+distillation works": a layer serves the student only after enough updates and
+once its EMA cosine distance to the teacher is low, with hysteresis, failing
+closed to the teacher; section "Inputs worth setting": landmark
+fraction/min/max and a readiness threshold) are read as: distance = mean over
+(batch, head, token) rows of 1 - cos(student_row, teacher_row); ema = d on
+the first update, then rate * ema + (1 - rate) * d; a gate that is not ready
+becomes ready when updates >= min_updates and ema <= threshold_on, a ready
+gate drops when ema > threshold_off (threshold_off >= threshold_on); a
+non-finite distance drops it; L = clamp(round-half-up(fraction * N), lmin,
+lmax), at most N.
+
 Pins (tests/test_oracle.py): brute-force N x N row-normalised attention,
 torch's elu and scaled_dot_product_attention in fp64, closed forms
 (W = 0, L = 1, Q = 0, first causal token), invariants (phi > 0, permutation,
@@ -77,6 +89,7 @@ __all__ = [
     "landmark_attn", "blend", "hybrid_forward", "causal_forward",
     "hybrid_rows", "causal_rows", "normwise_err", "split_heads", "merge_heads", "nnt_layer_forward",
     "elu_plus_one_grad", "hybrid_backward", "full_softmax_attention", "distill_loss", "adam_update", "distill_step",
+    "cosine_distance", "landmark_count", "ReadinessGate",
 ]
 
 
@@ -500,6 +513,40 @@ def distill_step(Q, K, V, W, b, g, s, state, step: int, lr: float, eps, L: int, 
     g2, new["mg"], new["vg"] = adam_update(g, dg, state["mg"], state["vg"], step, lr)
     s2, new["ms"], new["vs"] = adam_update(s, ds, state["ms"], state["vs"], step, lr)
     return W2, b2, g2, s2, new, loss
+
+
+def cosine_distance(student, teacher) -> float:
+    """Mean over rows of 1 - o.t / max(|o| |t|, 1e-8), rows over the last axis."""
+    o, t = _f64(student), _f64(teacher)
+    cos = (o * t).sum(axis=-1) / np.maximum(np.linalg.norm(o, axis=-1) * np.linalg.norm(t, axis=-1), 1e-8)
+    return float((1.0 - cos).mean())
+
+
+def landmark_count(N: int, fraction: float, lmin: int, lmax: int) -> int:
+    """round-half-up(fraction * N) clamped to [lmin, lmax] and to N."""
+    L = int(math.floor(fraction * N + 0.5))
+    return min(N, max(lmin, min(lmax, L)))
+
+
+class ReadinessGate:
+    """Per-layer fail-closed readiness gate with an EMA of the cosine distance and hysteresis."""
+
+    def __init__(self, rate: float, threshold_on: float, threshold_off: float, min_updates: int):
+        self.rate, self.on, self.off, self.min_updates = rate, threshold_on, threshold_off, min_updates
+        self.ema, self.updates, self.ready = 0.0, 0, False
+
+    def update(self, d: float) -> bool:
+        if not math.isfinite(d):
+            self.ready = False
+            return self.ready
+        self.ema = d if self.updates == 0 else self.rate * self.ema + (1.0 - self.rate) * d
+        self.updates += 1
+        if self.ready:
+            if self.ema > self.off:
+                self.ready = False
+        elif self.updates >= self.min_updates and self.ema <= self.on:
+            self.ready = True
+        return self.ready
 
 
 def normwise_err(got, ref, axes=(-2, -1)) -> float:

@@ -650,6 +650,59 @@ def test_distill_steps_reduce_the_loss():
     assert losses[-1] < losses[0] - 0.05
 
 
+# ---------------------------------------------------------------- readiness gating
+
+def test_cosine_distance_matches_torch():
+    r = np.random.default_rng(90)
+    o, t = r.standard_normal((2, 3, 11, 8)), r.standard_normal((2, 3, 11, 8))
+    ref = (1 - torch.nn.functional.cosine_similarity(torch.from_numpy(o), torch.from_numpy(t), dim=-1,
+                                                     eps=1e-8)).mean().item()
+    assert abs(O.cosine_distance(o, t) - ref) < 1e-14
+    assert abs(O.cosine_distance(t, t)) < 1e-14 and abs(O.cosine_distance(-t, t) - 2.0) < 1e-14
+    assert abs(O.cosine_distance(3.0 * t, t)) < 1e-14  # scale invariant
+
+
+def test_landmark_count_hand_worked():
+    assert O.landmark_count(4608, 1 / 36, 16, 512) == 128
+    assert O.landmark_count(1536, 1 / 24, 16, 512) == 64
+    assert O.landmark_count(100, 0.005, 16, 512) == 16      # min clamp (0.5 rounds up to 1, then 16)
+    assert O.landmark_count(100000, 0.1, 16, 512) == 512    # max clamp
+    assert O.landmark_count(10, 0.5, 16, 512) == 10         # never more than N
+    assert O.landmark_count(30, 0.05, 0, 512) == 2          # 1.5 rounds half up
+
+
+def test_gate_fails_closed_until_min_updates():
+    g = O.ReadinessGate(0.9, 0.1, 0.2, 5)
+    assert [g.update(0.0) for _ in range(5)] == [False, False, False, False, True]
+
+
+def test_gate_ema_hand_worked():
+    g = O.ReadinessGate(0.5, 0.1, 0.2, 1)
+    g.update(0.4)
+    assert g.ema == 0.4 and not g.ready
+    g.update(0.0)                         # 0.5 * 0.4 + 0.5 * 0 = 0.2
+    assert abs(g.ema - 0.2) < 1e-15 and not g.ready
+    g.update(0.0)                         # 0.1 <= on: ready
+    assert abs(g.ema - 0.1) < 1e-15 and g.ready
+    g.update(0.3)                         # 0.2: inside the band, stays ready
+    assert abs(g.ema - 0.2) < 1e-15 and g.ready
+    g.update(0.3)                         # 0.25 > off: drops
+    assert abs(g.ema - 0.25) < 1e-15 and not g.ready
+    g.update(0.05)                        # 0.15: inside the band, stays down
+    assert not g.ready
+
+
+def test_gate_hysteresis_does_not_flap():
+    g = O.ReadinessGate(0.0, 0.1, 0.2, 1)  # rate 0: ema = the last distance
+    states = [g.update(d) for d in (0.05, 0.15, 0.12, 0.18, 0.21, 0.15, 0.11, 0.09)]
+    assert states == [True, True, True, True, False, False, False, True]
+
+
+def test_gate_non_finite_distance_fails_closed():
+    g = O.ReadinessGate(0.9, 0.1, 0.2, 1)
+    assert g.update(0.0) and not g.update(float("nan")) and g.updates == 1
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_linear():
@@ -798,6 +851,18 @@ def _mut_adam_no_bias_correction(p, grad, m, v, step, lr, beta1=0.9, beta2=0.999
     return p - lr * m / (np.sqrt(v) + eps), m, v
 
 
+def _mut_gate_no_hysteresis_update(self, d):
+    self.ema = d if self.updates == 0 else self.rate * self.ema + (1.0 - self.rate) * d
+    self.updates += 1
+    self.ready = self.updates >= self.min_updates and self.ema <= self.on
+    return self.ready
+
+
+def _pins_gate():
+    test_gate_ema_hand_worked()
+    test_gate_hysteresis_does_not_flap()
+
+
 def _pins_backward():
     test_backward_matches_finite_differences()
     test_backward_matches_torch_autograd()
@@ -833,3 +898,9 @@ def test_planted_mistake_is_caught(monkeypatch, attr, mutant, pins):
     monkeypatch.setattr(O, attr, mutant)
     with pytest.raises(AssertionError):
         pins()
+
+
+def test_planted_gate_without_hysteresis_is_caught(monkeypatch):
+    monkeypatch.setattr(O.ReadinessGate, "update", _mut_gate_no_hysteresis_update)
+    with pytest.raises(AssertionError):
+        _pins_gate()
