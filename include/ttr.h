@@ -180,6 +180,43 @@ ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void
 /* Workspace size in bytes of ttr_distill_step (0 if the shape is invalid). */
 size_t ttr_distill_workspace_bytes(ttr_dims d, int32_t L, int32_t compute_teacher);
 
+/* Cosine distance of a student's attention output to a teacher's: the mean
+ * over the B*H*N rows of 1 - o.t / max(|o| |t|, 1e-8) (rows of D values),
+ * written to out (one fp32 device value). student, teacher [B,H,N,D] in the
+ * IO dtype. The quantity the readiness gate tracks ("Flux2TTRTrainer", "How
+ * the distillation works": EMA cosine distance to the teacher).
+ * ws: at least ttr_cosine_workspace_bytes(d) bytes. */
+ttr_status ttr_cosine_distance(ttr_dims d, const void* student, const void* teacher, float* out, void* ws,
+                               size_t ws_bytes, void* stream);
+size_t ttr_cosine_workspace_bytes(ttr_dims d);
+
+/* Per-layer readiness gate, host only ("Flux2TTRTrainer", "How the
+ * distillation works": fail-closed until enough updates and a low EMA cosine
+ * distance, with hysteresis). A layer serves the student only while ready;
+ * otherwise it keeps the teacher's attention.
+ *   ema  = distance on the first update, then ema_rate ema + (1 - ema_rate) distance
+ *   not ready -> ready  when updates >= min_updates and ema <= threshold_on
+ *   ready -> not ready  when ema > threshold_off (threshold_off >= threshold_on)
+ * A zero-initialised state is a fresh, not-ready gate. A non-finite distance
+ * makes the gate not ready, leaves ema and updates unchanged and returns
+ * TTR_ERR_SHAPE; an invalid config (0 <= ema_rate < 1, 0 <= threshold_on <=
+ * threshold_off, min_updates >= 0) returns TTR_ERR_SHAPE and changes nothing. */
+typedef struct {
+  double ema_rate, threshold_on, threshold_off;
+  int32_t min_updates;
+} ttr_gate_config;
+typedef struct {
+  double ema;
+  int32_t updates;
+  int32_t ready;
+} ttr_gate_state;
+ttr_status ttr_gate_update(const ttr_gate_config* cfg, ttr_gate_state* st, double distance);
+
+/* Landmark count from the trainer's fraction/min/max knobs ("Flux2TTRTrainer",
+ * "Inputs worth setting"): round-half-up(fraction * N) clamped to [lmin, lmax]
+ * and to N. Returns -1 for N < 0, fraction < 0 or lmax < lmin (or lmin < 0). */
+int32_t ttr_landmark_count(int32_t N, double fraction, int32_t lmin, int32_t lmax);
+
 /* Sizes of the NNT linear-attention layer: x [B,N,E] (batch first), H heads of D = E / H. */
 typedef struct {
   int32_t B, N, E, H;

@@ -13,6 +13,7 @@ blended by a bounded weight); "NNT Define Linear Attention", "The inputs" and
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import re
 from typing import Optional, Tuple
@@ -57,6 +58,15 @@ class LayerDims(ctypes.Structure):
                 ("H", ctypes.c_int32), ("dtype", ctypes.c_int32), ("fmap", ctypes.c_int32)]
 
 
+class GateConfig(ctypes.Structure):
+    _fields_ = [("ema_rate", ctypes.c_double), ("threshold_on", ctypes.c_double),
+                ("threshold_off", ctypes.c_double), ("min_updates", ctypes.c_int32)]
+
+
+class GateState(ctypes.Structure):
+    _fields_ = [("ema", ctypes.c_double), ("updates", ctypes.c_int32), ("ready", ctypes.c_int32)]
+
+
 # feature maps (ttr_fmap): elu(x) + 1, relu, softmax over the features
 FMAPS = {"elu1": 0, "relu": 1, "softmax": 2}
 
@@ -81,6 +91,7 @@ _SIGS = {
                             ctypes.c_size_t, _P],
     "ttr_distill_step": [Dims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
                          ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
+    "ttr_cosine_distance": [Dims, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "ttr_nnt_layer_forward": [LayerDims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
                               _P, _P, ctypes.c_size_t, _P],
 }
@@ -110,6 +121,12 @@ def load_library() -> ctypes.CDLL:
     lib.ttr_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_nnt_layer_workspace_bytes.argtypes = [LayerDims, ctypes.c_int32]
     lib.ttr_nnt_layer_workspace_bytes.restype = ctypes.c_size_t
+    lib.ttr_cosine_workspace_bytes.argtypes = [Dims]
+    lib.ttr_cosine_workspace_bytes.restype = ctypes.c_size_t
+    lib.ttr_gate_update.argtypes = [ctypes.POINTER(GateConfig), ctypes.POINTER(GateState), ctypes.c_double]
+    lib.ttr_gate_update.restype = ctypes.c_int
+    lib.ttr_landmark_count.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_int32, ctypes.c_int32]
+    lib.ttr_landmark_count.restype = ctypes.c_int32
     lib.ttr_status_string.argtypes = [ctypes.c_int]
     lib.ttr_status_string.restype = ctypes.c_char_p
     lib.ttr_last_hip_error.argtypes = []
@@ -390,3 +407,53 @@ def distill_step(state: DistillState, Q: torch.Tensor, K: torch.Tensor, V: torch
         state.step -= 1
     _check(st, "ttr_distill_step")
     return loss
+
+
+def cosine_distance(student: torch.Tensor, teacher: torch.Tensor, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mean over rows of 1 - cos(student_row, teacher_row), [B,H,N,D] in the IO dtype
+    (ttr_cosine_distance); returns a one-element float32 device tensor."""
+    lib = load_library()
+    d = _dims(student, int(student.shape[3]))
+    out = torch.empty(1, dtype=torch.float32, device=student.device)
+    ws, wsb = _workspace(d, lib.ttr_cosine_workspace_bytes(d), student, ws)
+    st = lib.ttr_cosine_distance(d, _dev(student, "student"), _dev(teacher, "teacher", student.dtype),
+                                 _dev(out, "out"), None if ws is None else ws.data_ptr(), wsb, _stream(student))
+    _check(st, "ttr_cosine_distance")
+    return out
+
+
+class ReadinessGate:
+    """Per-layer fail-closed readiness gate (ttr_gate_update): serve the student only while ``ready``."""
+
+    def __init__(self, ema_rate: float = 0.9, threshold_on: float = 0.1, threshold_off: float = 0.15,
+                 min_updates: int = 50):
+        self.cfg = GateConfig(ema_rate, threshold_on, threshold_off, min_updates)
+        self.state = GateState(0.0, 0, 0)
+
+    def update(self, distance: float) -> bool:
+        st = load_library().ttr_gate_update(ctypes.byref(self.cfg), ctypes.byref(self.state), float(distance))
+        if st not in (0, 2):
+            _check(st, "ttr_gate_update")
+        if st == 2 and math.isfinite(distance):
+            _check(st, "ttr_gate_update")
+        return bool(self.state.ready)
+
+    @property
+    def ready(self) -> bool:
+        return bool(self.state.ready)
+
+    @property
+    def ema(self) -> float:
+        return float(self.state.ema)
+
+    @property
+    def updates(self) -> int:
+        return int(self.state.updates)
+
+
+def landmark_count(N: int, fraction: float, lmin: int, lmax: int) -> int:
+    """Landmarks from the fraction/min/max knobs (ttr_landmark_count)."""
+    L = load_library().ttr_landmark_count(int(N), float(fraction), int(lmin), int(lmax))
+    if L < 0:
+        raise ValueError("landmark_count: need N >= 0, fraction >= 0 and 0 <= lmin <= lmax")
+    return int(L)

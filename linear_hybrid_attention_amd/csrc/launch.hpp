@@ -111,4 +111,9 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
                                float* W, float* bias, float* g, float* sv, float* moments, int step, float lr,
                                float eps, int L, float* loss_out, void* ws, hipStream_t s, StageTimer* t);
 
+// k_gate.hip: cosine distance of two attention outputs
+size_t cosine_workspace_bytes(const Problem& p);
+hipError_t launch_cosine_distance(const Problem& p, const void* student, const void* teacher, float* out, void* ws,
+                                  hipStream_t s);
+
 }  // namespace ttr

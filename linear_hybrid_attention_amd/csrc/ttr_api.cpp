@@ -486,4 +486,26 @@ ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void
   return r;
 }
 
+size_t ttr_cosine_workspace_bytes(ttr_dims d) {
+  if (check_dims(d, false) != TTR_OK && check_dims(d, true) != TTR_OK) return 0;
+  return cosine_workspace_bytes(make_problem(d, d.F != d.D));
+}
+
+ttr_status ttr_cosine_distance(ttr_dims d, const void* student, const void* teacher, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
+  if (check_dims(d, false) != TTR_OK && check_dims(d, true) != TTR_OK) return TTR_ERR_SHAPE;
+  TTR_TRY(check_ptr(student));
+  TTR_TRY(check_ptr(teacher));
+  TTR_TRY(check_ptr(out));
+  const Problem p = make_problem(d, d.F != d.D);
+  const size_t need = cosine_workspace_bytes(p);
+  if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
+  TTR_TRY(check_ptr(ws));
+  const Range outs[] = {{out, 4}, {ws, need}};
+  const Range ins[] = {{student, qkv_bytes(d)}, {teacher, qkv_bytes(d)}};
+  TTR_TRY(check_no_alias(outs, 2, ins, 2));
+  return hip_status(launch_cosine_distance(p, student, teacher, out, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"
