@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--distill", action="store_true",
                     help="time one Phase-1 distillation step (teacher, student, loss, backward, Adam) instead")
     ap.add_argument("--lr", type=float, default=1e-4, help="Adam learning rate of the distillation step")
+    ap.add_argument("--cosine", action="store_true",
+                    help="time the student/teacher cosine distance of the readiness gate instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
@@ -551,6 +553,89 @@ def main_distill(args):
     print(json.dumps(res), flush=True)
 
 
+def main_cosine(args):
+    """The gate's cosine distance on [B,H,N,D] tensors of the workload: the
+    student is the hybrid forward's output, the teacher the softmax attention
+    over every token (both in the IO dtype). HBM-bound: both tensors read once."""
+    import ctypes
+    import numpy as np
+    import torch
+    import linear_hybrid_attention_amd as ttr
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    io_t = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def io(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x[name]).to(dev)
+
+    Q, K, V = io("Q"), io("K"), io("V")
+    W = None if x["W"] is None else io("W")
+    b = None if x["b"] is None else torch.from_numpy(x["b"]).to(dev)
+    g = torch.from_numpy(x["g"]).to(dev)
+    student = ttr.hybrid_forward(Q, K, V, W, b, g, float(x["eps"]), w.L)
+    gneg = torch.full_like(g, float("-inf"))
+    teacher = ttr.hybrid_forward(Q, K, V, W, b, gneg, float(x["eps"]), w.N)  # alpha = 0, every token a landmark
+    lib = ttr.load_library()
+    d = ttr.Dims(w.B, w.H, w.N, w.D, w.D, 1 if w.dtype == "bf16" else 0, 0)
+    ws = torch.empty(lib.ttr_cosine_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        out = ttr.cosine_distance(student, teacher, ws=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        out = ttr.cosine_distance(student, teacher, ws=ws)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    handles = [(ctypes.c_void_p * 3)(*[e.cuda_event for e in row]) for row in ev]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        lib.ttr_set_stage_events(handles[i], 3)
+        ttr.cosine_distance(student, teacher, ws=ws)
+    torch.cuda.synchronize()
+    part_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]))
+    total_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]))
+    io_b = 2 if w.dtype == "bf16" else 4
+    nbytes = 2 * w.B * w.H * w.N * w.D * io_b
+    rl = roofline(w, 0, nbytes, part_ms)
+    res = {"metric": f"readiness-gate cosine distance rows/sec ({w.name}: B={w.B}, H={w.H}, N={w.N}, D={w.D})",
+           "value": w.B * w.H * w.N / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+           "config": {"workload": w.name, "mode": "cosine", "B": w.B, "H": w.H, "N": w.N, "D": w.D},
+           "roofline": {"kernel": "cos_part_kernel", "bound": rl["bound"],
+                        "achieved": rl["achieved"], "peak": rl["peak"], "unit": rl["unit"], "frac": rl["frac"],
+                        "traffic": None, "algorithmic_flops_per_launch": 0, "algorithmic_bytes_per_launch": nbytes,
+                        "avg_launch_ms": part_ms},
+           "kernels": {"cos_part_kernel": {"ms": part_ms}, "cos_total_kernel": {"ms": total_ms}},
+           "distance": float(out.cpu()), "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        import oracle.ttr_oracle as O
+        s_np = student.float().cpu().numpy()
+        t_np = teacher.float().cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) or reps == 0:
+            O.cosine_distance(s_np, t_np)
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": w.B * w.H * w.N / sec, "unit": "rows/s", "cores": os.cpu_count() or 1,
+                               "kind": "oracle", "sample": f"the whole {w.name} pair, {reps} pass(es)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -574,6 +659,9 @@ def main():
         return
     if args.distill:
         main_distill(args)
+        return
+    if args.cosine:
+        main_cosine(args)
         return
     w = workloads.WORKLOADS[args.workload]
     x = workloads.make_inputs(w)

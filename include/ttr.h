@@ -258,7 +258,8 @@ int ttr_last_hip_error(void);
 
 /* Per-kernel timing for profilers and benchmarks. After this call, the
  * calling thread's next ttr_hybrid_forward, ttr_causal_scan,
- * ttr_nnt_layer_forward, ttr_hybrid_backward or ttr_distill_step records
+ * ttr_nnt_layer_forward, ttr_hybrid_backward, ttr_distill_step or
+ * ttr_cosine_distance records
  * events[0] on its stream before its first kernel and events[1], events[2],
  * ... after each kernel (or stage) it launches, as long as events remain:
  *   bf16 hybrid: key/value partial sums, operand pack, fused query kernel;
@@ -271,7 +272,8 @@ int ttr_last_hip_error(void);
  *     dphi_q, dKV, dks, dz_q, dphi_k, dz_k, dW from Q, dW from K, db/dg;
  *   distillation step: W to bf16 (bf16 IO), teacher (when computed), the
  *     backward's forward stages, loss rows, loss total, the backward's
- *     gradient stages, Adam.
+ *     gradient stages, Adam;
+ *   cosine distance: per-workgroup partial sums, total.
  * Events left over are recorded after the last kernel. The registration is
  * consumed by that one call. events holds n hipEvent_t handles created by the
  * caller; NULL clears the registration. The events only observe: the enqueued

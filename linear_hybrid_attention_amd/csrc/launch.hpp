@@ -114,6 +114,6 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
 // k_gate.hip: cosine distance of two attention outputs
 size_t cosine_workspace_bytes(const Problem& p);
 hipError_t launch_cosine_distance(const Problem& p, const void* student, const void* teacher, float* out, void* ws,
-                                  hipStream_t s);
+                                  hipStream_t s, StageTimer* t);
 
 }  // namespace ttr

@@ -505,7 +505,11 @@ ttr_status ttr_cosine_distance(ttr_dims d, const void* student, const void* teac
   const Range outs[] = {{out, 4}, {ws, need}};
   const Range ins[] = {{student, qkv_bytes(d)}, {teacher, qkv_bytes(d)}};
   TTR_TRY(check_no_alias(outs, 2, ins, 2));
-  return hip_status(launch_cosine_distance(p, student, teacher, out, ws, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  StageTimer t = take_stage_timer(st);
+  const ttr_status r = hip_status(launch_cosine_distance(p, student, teacher, out, ws, st, &t));
+  t.finish();
+  return r;
 }
 
 }  // extern "C"
