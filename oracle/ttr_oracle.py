@@ -69,6 +69,19 @@ gate drops when ema > threshold_off (threshold_off >= threshold_on); a
 non-finite distance drops it; L = clamp(round-half-up(fraction * N), lmin,
 lmax), at most N.
 
+The replay buffer ("Flux2TTRTrainer", section "How the distillation works":
+samples keep full keys and values but subsampled queries, offloaded to CPU
+memory with a 768 MB budget by default; section "The honest gotchas": replay
+offloads to the CPU by default) is read as: a sample of one layer call holds
+K and V [B, H, N, D] whole, the query rows Q[:, :, idx] [B, H, Nq, D] at a
+caller-given strictly increasing subset idx of the N tokens, optionally the
+teacher's fp32 output rows at the same idx, and idx itself (int32); each
+stored array counts toward the budget rounded up to 256 bytes; when a new
+sample would exceed the budget the oldest samples are evicted first (FIFO)
+until it fits, and a sample larger than the whole budget is refused without
+changing anything. Under FIFO the samples held are exactly the longest run of
+most recent pushes whose sizes fit the budget.
+
 Pins (tests/test_oracle.py): brute-force N x N row-normalised attention,
 torch's elu and scaled_dot_product_attention in fp64, closed forms
 (W = 0, L = 1, Q = 0, first causal token), invariants (phi > 0, permutation,
@@ -76,6 +89,9 @@ linearity, convex hull, alpha limits, last causal token equals the non-causal
 result), and a hand-worked example under tests/golden/. The NNT layer is pinned by
 the layer restated in torch with heads as column slices and the N x N form,
 the zero query/key projection closed form, and head-permutation invariance.
+The replay buffer is pinned by the brute-force longest-fitting-suffix rule over
+a random push sequence, hand-worked footprints, row-by-row gathering and the
+refusal of a sample larger than the budget.
 """
 from __future__ import annotations
 
@@ -89,7 +105,8 @@ __all__ = [
     "landmark_attn", "blend", "hybrid_forward", "causal_forward",
     "hybrid_rows", "causal_rows", "normwise_err", "split_heads", "merge_heads", "nnt_layer_forward",
     "elu_plus_one_grad", "hybrid_backward", "full_softmax_attention", "distill_loss", "adam_update", "distill_step",
-    "cosine_distance", "landmark_count", "ReadinessGate",
+    "cosine_distance", "landmark_count", "ReadinessGate", "replay_part_bytes", "replay_sample_bytes",
+    "ReplayBuffer",
 ]
 
 
@@ -547,6 +564,71 @@ class ReadinessGate:
         elif self.updates >= self.min_updates and self.ema <= self.on:
             self.ready = True
         return self.ready
+
+
+REPLAY_ALIGN = 256  # each stored array is counted (and placed) in whole 256-byte units
+
+
+def replay_part_bytes(nbytes: int) -> int:
+    """Bytes an array of ``nbytes`` takes from the replay budget."""
+    return -(-int(nbytes) // REPLAY_ALIGN) * REPLAY_ALIGN
+
+
+def replay_sample_bytes(B: int, H: int, N: int, D: int, io_bytes: int, Nq: int, teacher: bool) -> int:
+    """Budget footprint of one sample: K, V (IO dtype), the Nq query rows (IO
+    dtype), the teacher rows (fp32, when kept) and the int32 indices."""
+    kv = replay_part_bytes(B * H * N * D * io_bytes)
+    q = replay_part_bytes(B * H * Nq * D * io_bytes)
+    t = replay_part_bytes(B * H * Nq * D * 4) if teacher else 0
+    return 2 * kv + q + t + replay_part_bytes(Nq * 4)
+
+
+class ReplayBuffer:
+    """FIFO replay buffer of (K, V, subsampled Q, teacher rows, indices) under a byte budget.
+
+    Arrays are kept as given (IO-dtype values or bf16 bit patterns, fp32
+    teacher rows), copied at push time; ids count pushes from 0."""
+
+    def __init__(self, budget: int):
+        self.budget = int(budget)
+        self.samples = []  # (id, footprint, dict) oldest first
+        self.next_id = 0
+        self.evicted = 0
+
+    @property
+    def used(self) -> int:
+        return sum(f for _, f, _ in self.samples)
+
+    def ids(self):
+        return [i for i, _, _ in self.samples]
+
+    def push(self, Q, K, V, idx, teacher=None):
+        """Store one sample; return its id, or None (nothing changed) if it exceeds the budget."""
+        Q, K, V = np.asarray(Q), np.asarray(K), np.asarray(V)
+        idx = np.asarray(idx, dtype=np.int32)
+        B, H, N, D = K.shape
+        if Q.shape != K.shape or V.shape != K.shape or idx.ndim != 1 or idx.size < 1:
+            raise ValueError("Q, K, V must share [B, H, N, D]; idx must be a non-empty vector")
+        if idx[0] < 0 or idx[-1] >= N or np.any(np.diff(idx) <= 0):
+            raise ValueError("idx must be strictly increasing in [0, N)")
+        sample = {"K": K.copy(), "V": V.copy(), "Q": Q[:, :, idx, :].copy(), "idx": idx.copy(),
+                  "T": None if teacher is None else np.asarray(teacher, dtype=np.float32)[:, :, idx, :].copy()}
+        foot = replay_sample_bytes(B, H, N, D, K.dtype.itemsize, idx.size, teacher is not None)
+        if foot > self.budget:
+            return None
+        while self.samples and self.used + foot > self.budget:
+            self.samples.pop(0)
+            self.evicted += 1
+        sid = self.next_id
+        self.next_id += 1
+        self.samples.append((sid, foot, sample))
+        return sid
+
+    def fetch(self, sid: int):
+        for i, _, smp in self.samples:
+            if i == sid:
+                return smp
+        raise KeyError(sid)
 
 
 def normwise_err(got, ref, axes=(-2, -1)) -> float:

@@ -703,6 +703,91 @@ def test_gate_non_finite_distance_fails_closed():
     assert g.update(0.0) and not g.update(float("nan")) and g.updates == 1
 
 
+# ---------------------------------------------------------------- replay buffer
+
+def test_replay_footprint_hand_worked():
+    # bf16 [1,2,10,64]: K and V 2560 B each; 3 query rows 768 B; fp32 teacher
+    # rows 1536 B; 3 int32 indices 12 B -> one 256-byte unit
+    assert O.replay_sample_bytes(1, 2, 10, 64, 2, 3, True) == 2560 + 2560 + 768 + 1536 + 256
+    # fp32 [2,3,5,64], every token kept, no teacher: 3 x 7680 + 256
+    assert O.replay_sample_bytes(2, 3, 5, 64, 4, 5, False) == 23296
+    assert O.replay_part_bytes(0) == 0 and O.replay_part_bytes(1) == 256 and O.replay_part_bytes(257) == 512
+
+
+def _replay_sample(rng, N, Nq, D=64, B=1, H=2, teacher=True):
+    Q, K, V = (rng.standard_normal((B, H, N, D)).astype(np.float32) for _ in range(3))
+    T = rng.standard_normal((B, H, N, D)).astype(np.float32) if teacher else None
+    idx = np.sort(rng.choice(N, size=Nq, replace=False)).astype(np.int32)
+    return Q, K, V, idx, T
+
+
+def _longest_fitting_suffix(history, budget):
+    """Brute force: the most recent pushes whose footprints fit, longest first."""
+    for k in range(len(history), -1, -1):
+        tail = history[len(history) - k:]
+        if sum(f for _, f in tail) <= budget:
+            return [i for i, _ in tail]
+    return []
+
+
+def test_replay_holds_longest_fitting_suffix():
+    rng = np.random.default_rng(31)
+    budget = 200_000
+    rb = O.ReplayBuffer(budget)
+    history = []
+    for _ in range(40):
+        N = int(rng.integers(8, 120))
+        Nq = int(rng.integers(1, N + 1))
+        Q, K, V, idx, T = _replay_sample(rng, N, Nq, teacher=bool(rng.integers(0, 2)))
+        foot = O.replay_sample_bytes(1, 2, N, 64, 4, Nq, T is not None)
+        sid = rb.push(Q, K, V, idx, T)
+        if foot > budget:
+            assert sid is None
+            continue
+        history.append((sid, foot))
+        assert rb.ids() == _longest_fitting_suffix(history, budget)
+        assert rb.used <= budget and rb.ids()[-1] == sid
+    assert rb.evicted > 0 and len(history) > len(rb.ids())
+
+
+def test_replay_stores_gathered_query_rows():
+    rng = np.random.default_rng(5)
+    Q, K, V, idx, T = _replay_sample(rng, 37, 9)
+    rb = O.ReplayBuffer(1 << 20)
+    sid = rb.push(Q, K, V, idx, T)
+    Q0, K0 = Q.copy(), K.copy()
+    Q[...] = 0.0                                 # the sample is a copy taken at push time
+    K[...] = 0.0
+    smp = rb.fetch(sid)
+    for b in range(Q.shape[0]):
+        for h in range(Q.shape[1]):
+            for j, n in enumerate(idx):
+                assert np.array_equal(smp["Q"][b, h, j], Q0[b, h, n])
+                assert np.array_equal(smp["T"][b, h, j], T[b, h, n])
+    assert np.array_equal(smp["K"], K0) and np.array_equal(smp["V"], V) and np.array_equal(smp["idx"], idx)
+
+
+def test_replay_refuses_sample_above_budget():
+    rng = np.random.default_rng(2)
+    Q, K, V, idx, T = _replay_sample(rng, 16, 4)
+    foot = O.replay_sample_bytes(1, 2, 16, 64, 4, 4, True)
+    rb = O.ReplayBuffer(foot)                    # exactly one sample fits
+    assert rb.push(Q, K, V, idx, T) == 0
+    assert rb.push(Q, K, V, idx, T) == 1 and rb.ids() == [1] and rb.evicted == 1
+    small = O.ReplayBuffer(foot - 1)
+    assert small.push(Q, K, V, idx, T) is None and small.ids() == [] and small.next_id == 0
+    with pytest.raises(KeyError):
+        small.fetch(0)
+
+
+@pytest.mark.parametrize("bad", [[3, 3], [5, 2], [-1, 4], [0, 16]])
+def test_replay_rejects_bad_indices(bad):
+    rng = np.random.default_rng(3)
+    Q, K, V, _, T = _replay_sample(rng, 16, 4)
+    with pytest.raises(ValueError):
+        O.ReplayBuffer(1 << 20).push(Q, K, V, np.array(bad), T)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_linear():
@@ -904,3 +989,25 @@ def test_planted_gate_without_hysteresis_is_caught(monkeypatch):
     monkeypatch.setattr(O.ReadinessGate, "update", _mut_gate_no_hysteresis_update)
     with pytest.raises(AssertionError):
         _pins_gate()
+
+
+def _mut_replay_lifo_push(self, Q, K, V, idx, teacher=None):
+    """Planted mistake: evicts the newest sample instead of the oldest."""
+    idx = np.asarray(idx, dtype=np.int32)
+    B, H, N, D = np.asarray(K).shape
+    foot = O.replay_sample_bytes(B, H, N, D, np.asarray(K).dtype.itemsize, idx.size, teacher is not None)
+    if foot > self.budget:
+        return None
+    while self.samples and self.used + foot > self.budget:
+        self.samples.pop()
+        self.evicted += 1
+    sid = self.next_id
+    self.next_id += 1
+    self.samples.append((sid, foot, {"K": K, "V": V, "Q": np.asarray(Q)[:, :, idx], "idx": idx, "T": teacher}))
+    return sid
+
+
+def test_planted_replay_lifo_eviction_is_caught(monkeypatch):
+    monkeypatch.setattr(O.ReplayBuffer, "push", _mut_replay_lifo_push)
+    with pytest.raises(AssertionError):
+        test_replay_holds_longest_fitting_suffix()
