@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--lr", type=float, default=1e-4, help="Adam learning rate of the distillation step")
     ap.add_argument("--cosine", action="store_true",
                     help="time the student/teacher cosine distance of the readiness gate instead")
+    ap.add_argument("--replay", action="store_true",
+                    help="time the replay buffer's offload (push), fetch and a push overlapped with a distillation "
+                         "step instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
@@ -636,6 +639,121 @@ def main_cosine(args):
     print(json.dumps(res), flush=True)
 
 
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def main_replay(args):
+    """Replay-buffer offload of one layer call of the workload (K, V whole, a
+    quarter of the query rows, fp32 teacher rows there) into the default
+    768 MiB pinned ring: push throughput (device -> host), fetch throughput
+    (host -> device), and a push issued beside a distillation step."""
+    import numpy as np
+    import torch
+    import linear_hybrid_attention_amd as ttr
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    if w.causal or not w.proj:
+        print("--replay needs a non-causal workload with a projection", file=sys.stderr)
+        sys.exit(2)
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def io(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x[name]).to(dev)
+
+    Q, K, V = io("Q"), io("K"), io("V")
+    T = torch.from_numpy(np.random.default_rng(w.seed + 7).standard_normal((w.B, w.H, w.N, w.D),
+                                                                           dtype=np.float32)).to(dev)
+    Nq = max(1, w.N // 4)
+    idx = workloads.query_subsample(w.N, Nq, w.seed)
+    io_b = 2 if w.dtype == "bf16" else 4
+    slices = w.B * w.H
+    payload = 2 * slices * w.N * w.D * io_b + slices * Nq * w.D * (io_b + 4) + Nq * 4
+    rb = ttr.ReplayBuffer(768 << 20, 128 << 20)
+    for _ in range(args.warmup):
+        rb.push(Q, K, V, idx, T)
+    rb.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rb.push(Q, K, V, idx, T)
+    rb.synchronize()
+    push_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    held = rb.ids()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rb.fetch(held[0])
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        rb.fetch(held[i % len(held)])
+    end.record(stream)
+    torch.cuda.synchronize()
+    fetch_ms = start.elapsed_time(end) / args.steps
+
+    # a push beside each distillation step (both read Q, K, V only)
+    b = x["b"] if x["b"] is not None else np.zeros((w.H, w.F), np.float32)
+    state = ttr.DistillState(torch.from_numpy(x["W"]).to(dev), torch.from_numpy(b).to(dev),
+                             torch.from_numpy(x["g"]).to(dev))
+    lib = ttr.load_library()
+    d = ttr.Dims(w.B, w.H, w.N, w.D, w.F, 1 if w.dtype == "bf16" else 0, 0)
+    ws = torch.empty(lib.ttr_distill_workspace_bytes(d, w.L, 1), dtype=torch.uint8, device=dev)
+    eps = float(x["eps"])
+    nov = max(5, args.steps // 4)
+    for _ in range(3):
+        ttr.distill_step(state, Q, K, V, w.L, args.lr, eps, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(nov):
+        ttr.distill_step(state, Q, K, V, w.L, args.lr, eps, ws=ws)
+    torch.cuda.synchronize()
+    alone_ms = (time.perf_counter() - t0) * 1e3 / nov
+    t0 = time.perf_counter()
+    for _ in range(nov):
+        rb.push(Q, K, V, idx, T)
+        ttr.distill_step(state, Q, K, V, w.L, args.lr, eps, ws=ws)
+    torch.cuda.synchronize()
+    rb.synchronize()
+    both_ms = (time.perf_counter() - t0) * 1e3 / nov
+    st = rb.stats()
+    push_gbs = payload / (push_ms * 1e-3) / 1e9
+    res = {"metric": f"replay-buffer offload GB/s ({w.name}: B={w.B}, H={w.H}, N={w.N}, D={w.D}, Nq={Nq}, "
+                     "K/V whole + query and fp32 teacher rows, 768 MiB pinned ring)",
+           "value": push_gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": push_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+           "config": {"workload": w.name, "mode": "replay", "B": w.B, "H": w.H, "N": w.N, "D": w.D, "Nq": Nq,
+                      "sample_payload_bytes": payload, "budget_bytes": 768 << 20},
+           "roofline": {"kernel": "push: K/V DMA + gather_rows_kernel into the pinned ring", "bound": "pcie",
+                        "achieved": push_gbs, "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": push_gbs / PCIE_PEAK_GBS,
+                        "traffic": None, "algorithmic_bytes_per_launch": payload, "avg_launch_ms": push_ms},
+           "fetch": {"ms": fetch_ms, "GB/s": payload / (fetch_ms * 1e-3) / 1e9},
+           "overlap": {"distill_step_ms": alone_ms, "push_ms": push_ms, "push_plus_distill_ms": both_ms},
+           "held": {"count": st.count, "bytes_used": st.bytes_used, "evicted": st.evicted},
+           "cpu_baseline": None}
+    rb.close()
+    if not args.no_cpu_baseline:
+        import oracle.ttr_oracle as O
+        hq = x["Q_bits"] if w.dtype == "bf16" else x["Q"]
+        hk = x["K_bits"] if w.dtype == "bf16" else x["K"]
+        hv = x["V_bits"] if w.dtype == "bf16" else x["V"]
+        ht = T.cpu().numpy()
+        ref = O.ReplayBuffer(768 << 20)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) or reps == 0:
+            ref.push(hq, hk, hv, idx, ht)
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": payload / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} pushes of the {w.name} sample into the oracle's model (host copies)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -659,6 +777,9 @@ def main():
         return
     if args.distill:
         main_distill(args)
+        return
+    if args.replay:
+        main_replay(args)
         return
     if args.cosine:
         main_cosine(args)

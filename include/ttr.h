@@ -66,7 +66,10 @@ typedef enum {
   TTR_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than ttr_workspace_bytes */
   TTR_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                   */
   TTR_ERR_HIP = 7,         /* a HIP launch failed, see ttr_last_hip_error()      */
-  TTR_ERR_ALIAS = 8        /* an output overlaps an input                        */
+  TTR_ERR_ALIAS = 8,       /* an output overlaps an input                        */
+  TTR_ERR_BUDGET = 9,      /* a replay sample larger than the budget or max size */
+  TTR_ERR_NOT_FOUND = 10,  /* a replay sample id that is not (or no longer) held */
+  TTR_ERR_DEVICE = 11      /* called with another device current than at create  */
 } ttr_status;
 
 typedef enum { TTR_FP32 = 0, TTR_BF16 = 1 } ttr_dtype;
@@ -252,6 +255,90 @@ size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk)
 
 /* Static, never-NULL description of a status code. */
 const char* ttr_status_string(ttr_status st);
+
+/* ------------------------------------------------------------------------
+ * Replay buffer ("Flux2TTRTrainer", "How the distillation works": samples keep
+ * full keys and values but subsampled queries, offloaded to CPU memory within
+ * a budget, 768 MB by default; "The honest gotchas": replay offloads to the CPU
+ * by default).
+ *
+ * Unlike the stateless calls above, a ttr_replay object owns memory: a ring of
+ * pinned host memory (hipHostMalloc) of budget_bytes + max_sample_bytes, and
+ * one side stream of the device current at ttr_replay_create (default
+ * priority, non-blocking). Every later call must be made with that device
+ * current (else TTR_ERR_DEVICE). Calls on one object are serialised by a
+ * lock; calls on different objects are independent.
+ *
+ * A sample of one layer call holds K, V [B,H,N,D] whole, the query rows
+ * Q[:, :, q_index] [B,H,Nq,D] (IO dtype), optionally the teacher's fp32
+ * output rows at the same q_index [B,H,Nq,D], and q_index itself (int32 [Nq],
+ * strictly increasing in [0, N)). Each of these arrays takes its size rounded
+ * up to 256 bytes from the budget (ttr_replay_sample_bytes). A push that would
+ * exceed the budget first evicts the oldest samples (FIFO) until the new one
+ * fits, so the samples held are always the longest run of most recent pushes
+ * that fits the budget; the extra max_sample_bytes of the ring are slack that
+ * lets a contiguous placement always be found, so placement never evicts
+ * more. Sample ids count accepted pushes from 0.
+ * ------------------------------------------------------------------------ */
+typedef struct ttr_replay ttr_replay;
+
+typedef struct {
+  int32_t count;      /* samples held */
+  int64_t first_id;   /* id of the oldest sample held (-1 when empty) */
+  int64_t pushed;     /* accepted pushes so far */
+  int64_t evicted;    /* samples evicted so far */
+  size_t bytes_used;  /* sum of the held samples' footprints (<= budget_bytes) */
+  size_t budget_bytes, max_sample_bytes, ring_bytes;
+} ttr_replay_stats;
+
+/* Budget footprint in bytes of one sample (0 if the shape is invalid): dims
+ * d (F ignored, taken as D), Nq query rows, with or without teacher rows. */
+size_t ttr_replay_sample_bytes(ttr_dims d, int32_t Nq, int32_t with_teacher);
+
+/* Create a replay buffer on the current device. budget_bytes >= 256;
+ * 256 <= max_sample_bytes <= budget_bytes bounds every later push. *out
+ * receives the object (NULL on failure). TTR_ERR_HIP when the pinned ring or
+ * the stream cannot be created. */
+ttr_status ttr_replay_create(size_t budget_bytes, size_t max_sample_bytes, ttr_replay** out);
+
+/* Wait for every copy the object enqueued, then free its ring, events and
+ * stream. NULL is a no-op. */
+void ttr_replay_destroy(ttr_replay* rb);
+
+/* Push one sample. Q, K, V: device [B,H,N,D] in the IO dtype; teacher: device
+ * fp32 [B,H,N,D] or NULL; q_index: HOST int32 [Nq] (copied before returning).
+ * The copies run on the object's side stream after the work already enqueued
+ * on `stream`: K and V by DMA into the ring, the Q and teacher rows by a
+ * gather kernel that writes straight into the pinned ring. The caller must
+ * not modify Q, K, V or teacher until ttr_replay_wait_pushed (or
+ * ttr_replay_synchronize) has ordered its later work after the copies.
+ * *id_out receives the sample's id. TTR_ERR_BUDGET when the footprint exceeds
+ * budget_bytes or max_sample_bytes (nothing changes); TTR_ERR_SHAPE for Nq
+ * outside [1, N] or an index list that is not strictly increasing in [0, N). */
+ttr_status ttr_replay_push(ttr_replay* rb, ttr_dims d, int32_t Nq, const void* Q, const void* K, const void* V,
+                           const float* teacher, const int32_t* q_index, void* stream, int64_t* id_out);
+
+/* Make `stream` wait for the copies of every push enqueued so far (after
+ * which the pushed inputs may be reused by work on that stream). */
+ttr_status ttr_replay_wait_pushed(ttr_replay* rb, void* stream);
+
+/* Block the host until every push's copies have finished. */
+ttr_status ttr_replay_synchronize(ttr_replay* rb);
+
+/* Copy sample `id` back to device memory on `stream` (which first waits for
+ * the sample's own push): Qs [B,H,Nq,D] and K, V [B,H,N,D] in the IO dtype,
+ * teacher rows fp32 [B,H,Nq,D] (NULL to skip; a non-NULL pointer for a sample
+ * without teacher rows is TTR_ERR_SHAPE), q_index host int32 [Nq] (NULL to
+ * skip; filled before returning). The sample's ring space is not reused
+ * until these copies have finished. TTR_ERR_NOT_FOUND for an id not held. */
+ttr_status ttr_replay_fetch(ttr_replay* rb, int64_t id, void* Qs, void* K, void* V, float* teacher_rows,
+                            int32_t* q_index, void* stream);
+
+/* Shape of sample `id`: *d (F = D), *Nq, *has_teacher (each pointer may be NULL). */
+ttr_status ttr_replay_info(ttr_replay* rb, int64_t id, ttr_dims* d, int32_t* Nq, int32_t* has_teacher);
+
+/* Counters of the object (see ttr_replay_stats). */
+ttr_status ttr_replay_get_stats(ttr_replay* rb, ttr_replay_stats* out);
 
 /* hipError_t of the last TTR_ERR_HIP returned on the calling thread (0 if none). */
 int ttr_last_hip_error(void);

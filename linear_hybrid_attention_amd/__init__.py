@@ -58,6 +58,12 @@ class LayerDims(ctypes.Structure):
                 ("H", ctypes.c_int32), ("dtype", ctypes.c_int32), ("fmap", ctypes.c_int32)]
 
 
+class ReplayStats(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("first_id", ctypes.c_int64), ("pushed", ctypes.c_int64),
+                ("evicted", ctypes.c_int64), ("bytes_used", ctypes.c_size_t), ("budget_bytes", ctypes.c_size_t),
+                ("max_sample_bytes", ctypes.c_size_t), ("ring_bytes", ctypes.c_size_t)]
+
+
 class GateConfig(ctypes.Structure):
     _fields_ = [("ema_rate", ctypes.c_double), ("threshold_on", ctypes.c_double),
                 ("threshold_off", ctypes.c_double), ("min_updates", ctypes.c_int32)]
@@ -127,6 +133,25 @@ def load_library() -> ctypes.CDLL:
     lib.ttr_gate_update.restype = ctypes.c_int
     lib.ttr_landmark_count.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_int32, ctypes.c_int32]
     lib.ttr_landmark_count.restype = ctypes.c_int32
+    lib.ttr_replay_sample_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32]
+    lib.ttr_replay_sample_bytes.restype = ctypes.c_size_t
+    lib.ttr_replay_create.argtypes = [ctypes.c_size_t, ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]
+    lib.ttr_replay_create.restype = ctypes.c_int
+    lib.ttr_replay_destroy.argtypes = [_P]
+    lib.ttr_replay_destroy.restype = None
+    lib.ttr_replay_push.argtypes = [_P, Dims, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.POINTER(ctypes.c_int64)]
+    lib.ttr_replay_push.restype = ctypes.c_int
+    lib.ttr_replay_wait_pushed.argtypes = [_P, _P]
+    lib.ttr_replay_wait_pushed.restype = ctypes.c_int
+    lib.ttr_replay_synchronize.argtypes = [_P]
+    lib.ttr_replay_synchronize.restype = ctypes.c_int
+    lib.ttr_replay_fetch.argtypes = [_P, ctypes.c_int64, _P, _P, _P, _P, _P, _P]
+    lib.ttr_replay_fetch.restype = ctypes.c_int
+    lib.ttr_replay_info.argtypes = [_P, ctypes.c_int64, ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int32)]
+    lib.ttr_replay_info.restype = ctypes.c_int
+    lib.ttr_replay_get_stats.argtypes = [_P, ctypes.POINTER(ReplayStats)]
+    lib.ttr_replay_get_stats.restype = ctypes.c_int
     lib.ttr_status_string.argtypes = [ctypes.c_int]
     lib.ttr_status_string.restype = ctypes.c_char_p
     lib.ttr_last_hip_error.argtypes = []
@@ -457,3 +482,108 @@ def landmark_count(N: int, fraction: float, lmin: int, lmax: int) -> int:
     if L < 0:
         raise ValueError("landmark_count: need N >= 0, fraction >= 0 and 0 <= lmin <= lmax")
     return int(L)
+
+
+def replay_sample_bytes(B: int, H: int, N: int, D: int, dtype: torch.dtype, Nq: int, teacher: bool) -> int:
+    """Budget footprint of one replay sample (ttr_replay_sample_bytes); 0 for an invalid shape."""
+    d = Dims(B, H, N, D, D, _IO[dtype], 0)
+    return int(load_library().ttr_replay_sample_bytes(d, int(Nq), 1 if teacher else 0))
+
+
+class ReplayBuffer:
+    """FIFO replay buffer in pinned host memory (ttr_replay_*): full K/V, the query
+    rows at a strictly increasing index subset and, optionally, the teacher's fp32
+    rows there. Pushes copy on the library's side stream; the pushed tensors are
+    kept referenced here until wait_pushed() or synchronize() orders the current
+    stream after the copies."""
+
+    DEFAULT_BUDGET = 768 << 20
+
+    def __init__(self, budget_bytes: int = DEFAULT_BUDGET, max_sample_bytes: Optional[int] = None):
+        lib = load_library()
+        if max_sample_bytes is None:
+            max_sample_bytes = min(int(budget_bytes), 256 << 20)
+        h = ctypes.c_void_p()
+        _check(lib.ttr_replay_create(int(budget_bytes), int(max_sample_bytes), ctypes.byref(h)), "ttr_replay_create")
+        self._h = h
+        self._pending = []
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value is not None:
+            load_library().ttr_replay_destroy(self._h)
+            self._h = None
+            self._pending = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def push(self, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_index,
+             teacher: Optional[torch.Tensor] = None) -> int:
+        """Push one sample (Q, K, V [B,H,N,D] IO dtype, teacher fp32 [B,H,N,D] or None,
+        q_index host int32 indices); returns its id."""
+        import numpy as np
+        lib = load_library()
+        d = _dims(K, int(K.shape[3]))
+        idx = np.ascontiguousarray(np.asarray(q_index, dtype=np.int32).reshape(-1))
+        if idx.size < 1:
+            raise ValueError("q_index must hold at least one index")
+        sid = ctypes.c_int64(-1)
+        st = lib.ttr_replay_push(self._h, d, int(idx.size), _dev(Q, "Q", K.dtype), _dev(K, "K"), _dev(V, "V", K.dtype),
+                                 _dev(teacher, "teacher", torch.float32), idx.ctypes.data, _stream(K),
+                                 ctypes.byref(sid))
+        _check(st, "ttr_replay_push")
+        self._pending.extend(t for t in (Q, K, V, teacher) if t is not None)
+        return int(sid.value)
+
+    def wait_pushed(self) -> None:
+        """Order the current stream's later work after every push's copies."""
+        dev = torch.cuda.current_device()
+        _check(load_library().ttr_replay_wait_pushed(self._h, torch.cuda.current_stream(dev).cuda_stream),
+               "ttr_replay_wait_pushed")
+        self._pending = []
+
+    def synchronize(self) -> None:
+        _check(load_library().ttr_replay_synchronize(self._h), "ttr_replay_synchronize")
+        self._pending = []
+
+    def info(self, sid: int):
+        d, nq, ht = Dims(), ctypes.c_int32(), ctypes.c_int32()
+        _check(load_library().ttr_replay_info(self._h, int(sid), ctypes.byref(d), ctypes.byref(nq), ctypes.byref(ht)),
+               "ttr_replay_info")
+        return d, int(nq.value), bool(ht.value)
+
+    def fetch(self, sid: int, teacher: bool = True):
+        """Copy sample ``sid`` back to the GPU on the current stream: returns
+        (Q rows [B,H,Nq,D], K, V [B,H,N,D], teacher rows fp32 or None, q_index numpy int32)."""
+        import numpy as np
+        d, nq, has_t = self.info(sid)
+        dt = torch.bfloat16 if d.dtype == TTR_BF16 else torch.float32
+        dev = torch.device("cuda", torch.cuda.current_device())
+        Qs = torch.empty(d.B, d.H, nq, d.D, dtype=dt, device=dev)
+        K = torch.empty(d.B, d.H, d.N, d.D, dtype=dt, device=dev)
+        V = torch.empty_like(K)
+        T = torch.empty(d.B, d.H, nq, d.D, dtype=torch.float32, device=dev) if (teacher and has_t) else None
+        idx = np.empty(nq, dtype=np.int32)
+        st = load_library().ttr_replay_fetch(self._h, int(sid), Qs.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                             None if T is None else T.data_ptr(), idx.ctypes.data,
+                                             torch.cuda.current_stream(dev).cuda_stream)
+        _check(st, "ttr_replay_fetch")
+        return Qs, K, V, T, idx
+
+    def stats(self) -> ReplayStats:
+        out = ReplayStats()
+        _check(load_library().ttr_replay_get_stats(self._h, ctypes.byref(out)), "ttr_replay_get_stats")
+        return out
+
+    def ids(self):
+        st = self.stats()
+        return list(range(st.first_id, st.first_id + st.count)) if st.count else []

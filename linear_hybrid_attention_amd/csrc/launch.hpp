@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/ttr.h"
+
 namespace ttr {
 
 struct Problem {
@@ -115,5 +117,15 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
 size_t cosine_workspace_bytes(const Problem& p);
 hipError_t launch_cosine_distance(const Problem& p, const void* student, const void* teacher, float* out, void* ws,
                                   hipStream_t s, StageTimer* t);
+
+// k_replay.hip: rows q_index[0..Nq) of every (batch, head) slice of Q (and T
+// when non-NULL) copied to [slices, Nq, row]; q_index and the destinations
+// may be device-mapped pinned host memory.
+hipError_t launch_replay_gather(const void* Q, void* q_dst, int q_row_bytes, const float* T, void* t_dst,
+                                int t_row_bytes, const int32_t* q_index, int slices, int N, int Nq, hipStream_t s);
+
+// Records a failed HIP call's error for ttr_last_hip_error (calling thread)
+// and maps it to a status.
+ttr_status report_hip(hipError_t e);
 
 }  // namespace ttr

@@ -69,6 +69,8 @@ size_t hybrid_ws(const ttr_dims& d, bool proj, int32_t L) {
 
 }  // namespace
 
+ttr_status ttr::report_hip(hipError_t e) { return hip_status(e); }
+
 extern "C" {
 
 const char* ttr_status_string(ttr_status st) {
@@ -82,6 +84,9 @@ const char* ttr_status_string(ttr_status st) {
     case TTR_ERR_ALIGN: return "pointer not 16-byte aligned";
     case TTR_ERR_HIP: return "HIP launch failed";
     case TTR_ERR_ALIAS: return "an output overlaps an input";
+    case TTR_ERR_BUDGET: return "replay sample larger than the budget or the maximum sample size";
+    case TTR_ERR_NOT_FOUND: return "replay sample id not held";
+    case TTR_ERR_DEVICE: return "called with another device current than at create";
   }
   return "unknown status";
 }

@@ -41,7 +41,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "bf16_round_bits", "bf16_bits_to_f32",
-           "LayerWorkload", "LAYER_WORKLOADS", "make_layer_inputs", "make_grad_output"]
+           "LayerWorkload", "LAYER_WORKLOADS", "make_layer_inputs", "make_grad_output", "query_subsample"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -186,3 +186,12 @@ def make_layer_inputs(w: LayerWorkload, seed: Optional[int] = None, bias: bool =
 def make_grad_output(w: Workload, seed: int) -> np.ndarray:
     """A seeded upstream gradient dLoss/dout for workload ``w``: fp32 [B,H,N,D] ~ N(0, 1)."""
     return np.random.default_rng(seed).standard_normal((w.B, w.H, w.N, w.D), dtype=np.float32)
+
+
+def query_subsample(N: int, Nq: int, seed: int) -> np.ndarray:
+    """Seeded subset of Nq of the N token positions, strictly increasing int32
+    (the query rows a replay sample keeps)."""
+    if not 1 <= Nq <= N:
+        raise ValueError("need 1 <= Nq <= N")
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(N, size=Nq, replace=False)).astype(np.int32)
