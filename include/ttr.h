@@ -263,8 +263,8 @@ const char* ttr_status_string(ttr_status st);
  * by default).
  *
  * Unlike the stateless calls above, a ttr_replay object owns memory: a ring of
- * pinned host memory (hipHostMalloc) of budget_bytes + max_sample_bytes, and
- * one side stream of the device current at ttr_replay_create (default
+ * pinned host memory (hipHostMalloc) of budget_bytes + max_sample_bytes, a
+ * device staging area of max_sample_bytes, and one side stream of the device current at ttr_replay_create (default
  * priority, non-blocking). Every later call must be made with that device
  * current (else TTR_ERR_DEVICE). Calls on one object are serialised by a
  * lock; calls on different objects are independent.
@@ -308,8 +308,9 @@ void ttr_replay_destroy(ttr_replay* rb);
 /* Push one sample. Q, K, V: device [B,H,N,D] in the IO dtype; teacher: device
  * fp32 [B,H,N,D] or NULL; q_index: HOST int32 [Nq] (copied before returning).
  * The copies run on the object's side stream after the work already enqueued
- * on `stream`: K and V by DMA into the ring, the Q and teacher rows by a
- * gather kernel that writes straight into the pinned ring. The caller must
+ * on `stream`: a kernel gathers the Q and teacher rows into the object's
+ * device staging area, then DMA copies move them, K and V into the ring. The
+ * caller must
  * not modify Q, K, V or teacher until ttr_replay_wait_pushed (or
  * ttr_replay_synchronize) has ordered its later work after the copies.
  * *id_out receives the sample's id. TTR_ERR_BUDGET when the footprint exceeds
@@ -345,8 +346,8 @@ int ttr_last_hip_error(void);
 
 /* Per-kernel timing for profilers and benchmarks. After this call, the
  * calling thread's next ttr_hybrid_forward, ttr_causal_scan,
- * ttr_nnt_layer_forward, ttr_hybrid_backward, ttr_distill_step or
- * ttr_cosine_distance records
+ * ttr_nnt_layer_forward, ttr_hybrid_backward, ttr_distill_step,
+ * ttr_cosine_distance or ttr_replay_push records
  * events[0] on its stream before its first kernel and events[1], events[2],
  * ... after each kernel (or stage) it launches, as long as events remain:
  *   bf16 hybrid: key/value partial sums, operand pack, fused query kernel;
@@ -360,7 +361,9 @@ int ttr_last_hip_error(void);
  *   distillation step: W to bf16 (bf16 IO), teacher (when computed), the
  *     backward's forward stages, loss rows, loss total, the backward's
  *     gradient stages, Adam;
- *   cosine distance: per-workgroup partial sums, total.
+ *   cosine distance: per-workgroup partial sums, total;
+ *   replay push (on the replay object's side stream): the row gather, the
+ *     rows' copy, K's copy, V's copy.
  * Events left over are recorded after the last kernel. The registration is
  * consumed by that one call. events holds n hipEvent_t handles created by the
  * caller; NULL clears the registration. The events only observe: the enqueued

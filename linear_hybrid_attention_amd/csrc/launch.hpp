@@ -118,11 +118,15 @@ size_t cosine_workspace_bytes(const Problem& p);
 hipError_t launch_cosine_distance(const Problem& p, const void* student, const void* teacher, float* out, void* ws,
                                   hipStream_t s, StageTimer* t);
 
-// k_replay.hip: rows q_index[0..Nq) of every (batch, head) slice of Q (and T
-// when non-NULL) copied to [slices, Nq, row]; q_index and the destinations
-// may be device-mapped pinned host memory.
+// k_replay.hip: rows q_index[0..Nq) (device-readable, e.g. mapped pinned
+// memory) of every (batch, head) slice of Q, and of T when non-NULL, copied
+// to [slices, Nq, row] (device).
 hipError_t launch_replay_gather(const void* Q, void* q_dst, int q_row_bytes, const float* T, void* t_dst,
                                 int t_row_bytes, const int32_t* q_index, int slices, int N, int Nq, hipStream_t s);
+
+// The calling thread's registered stage events (ttr_set_stage_events), taken
+// and cleared; the first is recorded on s at once.
+StageTimer take_stage_timer(hipStream_t s);
 
 // Records a failed HIP call's error for ttr_last_hip_error (calling thread)
 // and maps it to a status.

@@ -15,9 +15,11 @@
 // Hence the samples held are exactly the longest run of recent pushes that
 // fits the budget, and placement never evicts beyond the budget rule.
 //
-// Device->host copies run on the object's own side stream: K and V by DMA,
-// the query and teacher rows by a gather kernel writing through the ring's
-// device mapping. Host->device copies (fetch) run on the caller's stream.
+// Device->host copies run on the object's own side stream: a gather kernel
+// packs the query and teacher rows into a device staging area (reading the
+// indices from the ring through its device mapping), then DMA copies move
+// the rows, K and V into the ring. Host->device copies (fetch) are DMA
+// on the caller's stream.
 // Per sample, one event marks its push complete and one its last fetch; ring
 // space is reused only after both have completed.
 #include <hip/hip_runtime.h>
@@ -25,6 +27,7 @@
 #include <cstring>
 #include <deque>
 #include <mutex>
+#include <vector>
 
 #include "../../include/ttr.h"
 #include "launch.hpp"
@@ -86,11 +89,13 @@ struct ttr_replay {
   std::mutex mu;
   int device = 0;
   size_t budget = 0, max_sample = 0, ring = 0;
-  uint8_t* host = nullptr;     // pinned ring (host address)
-  uint8_t* mapped = nullptr;   // the same ring's device address
+  uint8_t* host = nullptr;     // pinned ring
+  uint8_t* mapped = nullptr;   // the ring's device address
+  uint8_t* staging = nullptr;  // device, max_sample bytes: a push's gathered rows
   hipStream_t side = nullptr;
   hipEvent_t inputs_ready = nullptr;  // caller stream -> side stream
   hipEvent_t last_push = nullptr;     // side stream, after the latest push
+  std::vector<hipEvent_t> events;     // pool of per-sample events not in use
   bool any_push = false;
   std::deque<Sample> live;
   size_t used = 0;
@@ -105,12 +110,21 @@ ttr_status check_device(const ttr_replay* rb) {
   return TTR_OK;
 }
 
-// Wait until no copy touches the sample's ring bytes, then release its events.
-hipError_t retire(Sample& s) {
+hipError_t take_event(ttr_replay* rb, hipEvent_t* ev) {
+  if (!rb->events.empty()) {
+    *ev = rb->events.back();
+    rb->events.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreateWithFlags(ev, hipEventDisableTiming);
+}
+
+// Wait until no copy touches the sample's ring bytes, then return its events to the pool.
+hipError_t retire(ttr_replay* rb, Sample& s) {
   hipError_t e = hipEventSynchronize(s.done);
   if (e == hipSuccess && s.read_recorded) e = hipEventSynchronize(s.read);
-  (void)hipEventDestroy(s.done);
-  (void)hipEventDestroy(s.read);
+  rb->events.push_back(s.done);
+  rb->events.push_back(s.read);
   return e;
 }
 
@@ -164,6 +178,9 @@ ttr_status ttr_replay_create(size_t budget_bytes, size_t max_sample_bytes, ttr_r
   void* mapped = nullptr;
   if (e == hipSuccess) e = hipHostGetDevicePointer(&mapped, host, 0);
   rb->mapped = static_cast<uint8_t*>(mapped);
+  void* staging = nullptr;
+  if (e == hipSuccess) e = hipMalloc(&staging, rb->max_sample);
+  rb->staging = static_cast<uint8_t*>(staging);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&rb->side, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&rb->inputs_ready, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&rb->last_push, hipEventDisableTiming);
@@ -178,12 +195,14 @@ ttr_status ttr_replay_create(size_t budget_bytes, size_t max_sample_bytes, ttr_r
 void ttr_replay_destroy(ttr_replay* rb) {
   if (rb == nullptr) return;
   if (rb->side != nullptr) (void)hipStreamSynchronize(rb->side);
-  for (Sample& s : rb->live) (void)retire(s);
+  for (Sample& s : rb->live) (void)retire(rb, s);
   rb->live.clear();
+  for (hipEvent_t ev : rb->events) (void)hipEventDestroy(ev);
   if (rb->inputs_ready != nullptr) (void)hipEventDestroy(rb->inputs_ready);
   if (rb->last_push != nullptr) (void)hipEventDestroy(rb->last_push);
   if (rb->side != nullptr) (void)hipStreamDestroy(rb->side);
   if (rb->host != nullptr) (void)hipHostFree(rb->host);
+  if (rb->staging != nullptr) (void)hipFree(rb->staging);
   delete rb;
 }
 
@@ -211,7 +230,7 @@ ttr_status ttr_replay_push(ttr_replay* rb, ttr_dims d, int32_t Nq, const void* Q
   if (foot > rb->budget || foot > rb->max_sample) return TTR_ERR_BUDGET;
   while (!rb->live.empty() && rb->used + foot > rb->budget) {
     Sample& old = rb->live.front();
-    const hipError_t e = retire(old);
+    const hipError_t e = retire(rb, old);
     rb->used -= old.foot;
     rb->live.pop_front();
     ++rb->evicted;
@@ -228,25 +247,34 @@ ttr_status ttr_replay_push(ttr_replay* rb, ttr_dims d, int32_t Nq, const void* Q
   std::memcpy(rb->host + s.off_i(), q_index, parts.idx);
 
   hipStream_t caller = static_cast<hipStream_t>(stream);
-  hipError_t e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&s.read, hipEventDisableTiming);
+  hipError_t e = take_event(rb, &s.done);
+  if (e == hipSuccess) e = take_event(rb, &s.read);
   if (e == hipSuccess) e = hipEventRecord(rb->inputs_ready, caller);
   if (e == hipSuccess) e = hipStreamWaitEvent(rb->side, rb->inputs_ready, 0);
+  StageTimer timer = take_stage_timer(rb->side);  // optional events around the copies
+  // staging (device): [Q rows | T rows], laid out like the sample's rows in the ring; the
+  // kernel reads the indices from the ring through its device mapping (a few KB)
+  uint8_t* st_q = rb->staging;
+  uint8_t* st_t = st_q + round_up(parts.q);
+  const size_t rows_bytes = teacher != nullptr ? round_up(parts.q) + parts.t : parts.q;
+  if (e == hipSuccess)
+    e = launch_replay_gather(Q, st_q, d.D * (int)dtype_bytes(d.dtype), teacher, st_t, d.D * (int)sizeof(float),
+                             reinterpret_cast<const int32_t*>(rb->mapped + s.off_i()), d.B * d.H, d.N, Nq,
+                             rb->side);
+  timer.mark();
+  if (e == hipSuccess) e = hipMemcpyAsync(rb->host + s.off_q(), st_q, rows_bytes, hipMemcpyDeviceToHost, rb->side);
+  timer.mark();
   if (e == hipSuccess) e = hipMemcpyAsync(rb->host + s.off_k(), K, parts.kv, hipMemcpyDeviceToHost, rb->side);
+  timer.mark();
   if (e == hipSuccess) e = hipMemcpyAsync(rb->host + s.off_v(), V, parts.kv, hipMemcpyDeviceToHost, rb->side);
-  if (e == hipSuccess) {
-    const int io_row = d.D * (int)dtype_bytes(d.dtype);
-    e = launch_replay_gather(Q, rb->mapped + s.off_q(), io_row, teacher, rb->mapped + s.off_t(),
-                             d.D * (int)sizeof(float), reinterpret_cast<const int32_t*>(rb->mapped + s.off_i()),
-                             d.B * d.H, d.N, Nq, rb->side);
-  }
+  timer.finish();
   if (e == hipSuccess) e = hipEventRecord(s.done, rb->side);
   if (e == hipSuccess) e = hipEventRecord(rb->last_push, rb->side);
   if (e != hipSuccess) {
     // the sample is not kept; copies already enqueued finish before its bytes are reused
     (void)hipStreamSynchronize(rb->side);
-    if (s.done != nullptr) (void)hipEventDestroy(s.done);
-    if (s.read != nullptr) (void)hipEventDestroy(s.read);
+    if (s.done != nullptr) rb->events.push_back(s.done);
+    if (s.read != nullptr) rb->events.push_back(s.read);
     return report_hip(e);
   }
   rb->any_push = true;

@@ -14,8 +14,10 @@ thread_local int g_last_hip_error = 0;
 thread_local void* const* g_stage_events = nullptr;
 thread_local int g_stage_n = 0;
 
+}  // namespace
+
 // Take (and clear) the calling thread's registered stage events; record the first.
-StageTimer take_stage_timer(hipStream_t s) {
+StageTimer ttr::take_stage_timer(hipStream_t s) {
   StageTimer t;
   t.ev = g_stage_events;
   t.n = g_stage_n;
@@ -25,6 +27,8 @@ StageTimer take_stage_timer(hipStream_t s) {
   t.mark();
   return t;
 }
+
+namespace {
 
 ttr_status hip_status(hipError_t e) {
   if (e == hipSuccess) return TTR_OK;
