@@ -416,7 +416,9 @@ def distill_plan(w):
     plan = []
     if w.dtype == "bf16":
         plan.append(("to_bf16_kernel (W)", 0, 0))
-    plan.append(("teacher softmax attention (hybrid_kernel, L = N)", 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
+    teacher = ("teacher softmax attention (kv2 + fused query kernel, every token a landmark, alpha 0)"
+               if w.dtype == "bf16" else "teacher softmax attention (hybrid_kernel, L = N)")
+    plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
     plan += [("bgemm z_q = Q W + b", gemm_nd, 0), ("bgemm z_k = K W + b", gemm_nd, 0),
              ("colsum ksum", 0, 0), ("bgemm KV = phi_k^T V", gemm_nd, 0), ("bgemm num = phi_q KV", gemm_nd, 0),
              ("den_lin_kernel", 2 * Z * N * F, 0)]
