@@ -57,6 +57,14 @@ bias-corrected, no weight decay) updates W, b, g and s. The backward gives
 the gradients of the trainable parameters W, b, g (Q, K, V are the frozen
 model's activations).
 
+A replay sample (below) keeps every key and value but only some query rows,
+and the student is trained on it ("Flux2TTRTrainer", section "How the
+distillation works"). Every function here therefore takes Q with Nq rows and
+K, V with N rows: the linear branch and the landmarks (strided over the N
+keys) come from K and V, and each query row's output depends on that row
+only. Trained on a sample, the loss averages over the sample's rows, and its
+teacher is the teacher's output at those rows.
+
 Readiness gating and the landmark count ("Flux2TTRTrainer", section "How the
 distillation works": a layer serves the student only after enough updates and
 once its EMA cosine distance to the teacher is low, with hysteresis, failing
@@ -89,6 +97,9 @@ linearity, convex hull, alpha limits, last causal token equals the non-causal
 result), and a hand-worked example under tests/golden/. The NNT layer is pinned by
 the layer restated in torch with heads as column slices and the N x N form,
 the zero query/key projection closed form, and head-permutation invariance.
+Sampled query rows are pinned by the forward on a subset of rows equal to
+those rows of the full forward, and the backward on them equal to the full
+backward with a zero upstream gradient on every other row.
 The replay buffer is pinned by the brute-force longest-fitting-suffix rule over
 a random push sequence, hand-worked footprints, row-by-row gathering and the
 refusal of a sample larger than the budget.
@@ -233,7 +244,7 @@ def landmark_attn(Q, K, V, L: int) -> np.ndarray:
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, H, N, D = Q.shape
-    idx = landmark_indices(N, L)
+    idx = landmark_indices(K.shape[2], L)  # landmarks stride over the keys (N keys may differ from Q's rows)
     out = np.empty((B, H, N, D))
     scale = 1.0 / math.sqrt(D)
     for bi in range(B):

@@ -788,6 +788,40 @@ def test_replay_rejects_bad_indices(bad):
         O.ReplayBuffer(1 << 20).push(Q, K, V, np.array(bad), T)
 
 
+# ---------------------------------------------------------------- sampled query rows
+
+def _sampled_case(seed=91, B=2, H=2, N=40, D=6, F=9, L=7, Nq=13):
+    r = np.random.default_rng(seed)
+    Q, K, V = (r.standard_normal((B, H, N, D)) for _ in range(3))
+    W = r.standard_normal((H, D, F)) / math.sqrt(D)
+    b = r.standard_normal((H, F)) * 0.1
+    g = r.standard_normal(H)
+    idx = np.sort(r.choice(N, size=Nq, replace=False))
+    return Q, K, V, W, b, g, L, idx
+
+
+def test_sampled_rows_forward_equals_rows_of_full_forward():
+    Q, K, V, W, b, g, L, idx = _sampled_case()
+    full = O.hybrid_forward(Q, K, V, W, b, g, EPS, L)
+    rows = O.hybrid_forward(Q[:, :, idx], K, V, W, b, g, EPS, L)
+    assert np.abs(rows - full[:, :, idx]).max() < 1e-12
+    assert np.abs(O.full_softmax_attention(Q[:, :, idx], K, V) - O.full_softmax_attention(Q, K, V)[:, :, idx]).max() < 1e-12
+
+
+def test_sampled_rows_backward_equals_full_backward_with_zero_rows():
+    # rows outside the sample get a zero upstream gradient: nothing of theirs reaches W, b or g
+    Q, K, V, W, b, g, L, idx = _sampled_case(92)
+    r = np.random.default_rng(5)
+    dout_s = r.standard_normal((Q.shape[0], Q.shape[1], idx.size, Q.shape[3]))
+    dout = np.zeros_like(Q)
+    dout[:, :, idx] = dout_s
+    for LL in (L, 0):
+        got = O.hybrid_backward(Q[:, :, idx], K, V, W, b, g, EPS, LL, dout_s)
+        ref = O.hybrid_backward(Q, K, V, W, b, g, EPS, LL, dout)
+        for a, c in zip(got, ref):
+            assert np.abs(a - c).max() < 1e-10 * max(1.0, np.abs(c).max())
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_linear():
@@ -1011,3 +1045,23 @@ def test_planted_replay_lifo_eviction_is_caught(monkeypatch):
     monkeypatch.setattr(O.ReplayBuffer, "push", _mut_replay_lifo_push)
     with pytest.raises(AssertionError):
         test_replay_holds_longest_fitting_suffix()
+
+
+def _mut_landmarks_over_queries(Q, K, V, L):
+    """Planted mistake: the landmark stride taken from the query rows."""
+    Q, K, V = np.asarray(Q, float), np.asarray(K, float), np.asarray(V, float)
+    B, H, N, D = Q.shape
+    idx = O.landmark_indices(N, L)
+    out = np.empty((B, H, N, D))
+    for bi in range(B):
+        for h in range(H):
+            s_ = (Q[bi, h] @ K[bi, h][idx].T) / math.sqrt(D)
+            p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
+            out[bi, h] = (p_ @ V[bi, h][idx]) / p_.sum(axis=1, keepdims=True)
+    return out
+
+
+def test_planted_landmarks_over_queries_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "landmark_attn", _mut_landmarks_over_queries)
+    with pytest.raises(AssertionError):
+        test_sampled_rows_forward_equals_rows_of_full_forward()
