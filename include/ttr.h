@@ -183,6 +183,22 @@ ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void
 /* Workspace size in bytes of ttr_distill_step (0 if the shape is invalid). */
 size_t ttr_distill_workspace_bytes(ttr_dims d, int32_t L, int32_t compute_teacher);
 
+/* The distillation step on a replay sample ("Flux2TTRTrainer", "How the
+ * distillation works": the student is trained on replay samples, which keep
+ * every key and value but only some query rows): as ttr_distill_step, with
+ * Q [B,H,Nq,D] the sample's query rows (1 <= Nq <= d.N) over K, V [B,H,N,D]
+ * (N = d.N keys; the landmarks stride over the keys), teacher [B,H,Nq,D] fp32
+ * the teacher's output at those rows or NULL (then computed: softmax attention
+ * of the Nq queries over all N keys). The loss averages over the B*H*Nq rows.
+ * With Nq == d.N this is ttr_distill_step. */
+ttr_status ttr_distill_step_rows(ttr_dims d, int32_t Nq, const void* Q, const void* K, const void* V,
+                                 const float* teacher, float* W, float* b, float* g, float* s, float* moments,
+                                 int32_t step, float lr, float eps, int32_t L, float* loss, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Workspace size in bytes of ttr_distill_step_rows (0 if the shape is invalid). */
+size_t ttr_distill_rows_workspace_bytes(ttr_dims d, int32_t Nq, int32_t L, int32_t compute_teacher);
+
 /* Cosine distance of a student's attention output to a teacher's: the mean
  * over the B*H*N rows of 1 - o.t / max(|o| |t|, 1e-8) (rows of D values),
  * written to out (one fp32 device value). student, teacher [B,H,N,D] in the
@@ -346,7 +362,7 @@ int ttr_last_hip_error(void);
 
 /* Per-kernel timing for profilers and benchmarks. After this call, the
  * calling thread's next ttr_hybrid_forward, ttr_causal_scan,
- * ttr_nnt_layer_forward, ttr_hybrid_backward, ttr_distill_step,
+ * ttr_nnt_layer_forward, ttr_hybrid_backward, ttr_distill_step (or _rows),
  * ttr_cosine_distance or ttr_replay_push records
  * events[0] on its stream before its first kernel and events[1], events[2],
  * ... after each kernel (or stage) it launches, as long as events remain:

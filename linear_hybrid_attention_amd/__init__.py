@@ -97,6 +97,8 @@ _SIGS = {
                             ctypes.c_size_t, _P],
     "ttr_distill_step": [Dims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
                          ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
+    "ttr_distill_step_rows": [Dims, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                              ctypes.c_float, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
     "ttr_cosine_distance": [Dims, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "ttr_nnt_layer_forward": [LayerDims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
                               _P, _P, ctypes.c_size_t, _P],
@@ -123,6 +125,8 @@ def load_library() -> ctypes.CDLL:
     lib.ttr_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_distill_workspace_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32]
     lib.ttr_distill_workspace_bytes.restype = ctypes.c_size_t
+    lib.ttr_distill_rows_workspace_bytes.argtypes = [Dims, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.ttr_distill_rows_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_backward_workspace_bytes.argtypes = [Dims, ctypes.c_int32]
     lib.ttr_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.ttr_nnt_layer_workspace_bytes.argtypes = [LayerDims, ctypes.c_int32]
@@ -413,24 +417,33 @@ class DistillState:
 
 def distill_step(state: DistillState, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, L: int, lr: float,
                  eps: float = 1e-6, teacher: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
-    """One distillation step (ttr_distill_step); updates ``state`` in place and
-    returns the device tensor [loss, huber, 1 - cos] before the update."""
+    """One distillation step; updates ``state`` in place and returns the device
+    tensor [loss, huber, 1 - cos] before the update. Q may hold fewer query
+    rows than K and V (a replay sample): then ttr_distill_step_rows, with
+    ``teacher`` (if given) the teacher's rows for those queries; otherwise
+    ttr_distill_step."""
     lib = load_library()
-    d = _dims(Q, int(state.W.shape[2]))
-    need = lib.ttr_distill_workspace_bytes(d, int(L), int(teacher is None))
+    if Q.dim() != 4 or K.dim() != 4 or Q.shape[:2] != K.shape[:2] or Q.shape[3] != K.shape[3]:
+        raise ValueError("Q must be [B, H, Nq, D] with K, V [B, H, N, D]")
+    d = _dims(K, int(state.W.shape[2]))
+    nq = int(Q.shape[2])
+    rows = nq != d.N
+    need = (lib.ttr_distill_rows_workspace_bytes(d, nq, int(L), int(teacher is None)) if rows else
+            lib.ttr_distill_workspace_bytes(d, int(L), int(teacher is None)))
+    where = "ttr_distill_step_rows" if rows else "ttr_distill_step"
     if need == 0:
-        raise TTRError(2, "ttr_distill_step", "invalid shape for the distillation step")
+        raise TTRError(2, where, "invalid shape for the distillation step")
     ws, wsb = _workspace(d, need, Q, ws)
     loss = torch.empty(3, dtype=torch.float32, device=Q.device)
     state.step += 1
-    st = lib.ttr_distill_step(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype),
-                              _dev(teacher, "teacher", torch.float32), _dev(state.W, "W"), _dev(state.b, "b"),
-                              _dev(state.g, "g"), _dev(state.s, "s"), _dev(state.moments, "moments"), state.step,
-                              float(lr), float(eps), int(L), _dev(loss, "loss"), None if ws is None else ws.data_ptr(),
-                              wsb, _stream(Q))
+    args = (_dev(Q, "Q", K.dtype), _dev(K, "K"), _dev(V, "V", K.dtype), _dev(teacher, "teacher", torch.float32),
+            _dev(state.W, "W"), _dev(state.b, "b"), _dev(state.g, "g"), _dev(state.s, "s"),
+            _dev(state.moments, "moments"), state.step, float(lr), float(eps), int(L), _dev(loss, "loss"),
+            None if ws is None else ws.data_ptr(), wsb, _stream(Q))
+    st = lib.ttr_distill_step_rows(d, nq, *args) if rows else lib.ttr_distill_step(d, *args)
     if st != 0:
         state.step -= 1
-    _check(st, "ttr_distill_step")
+    _check(st, where)
     return loss
 
 

@@ -316,6 +316,12 @@ __global__ void colsum_final_kernel(const float* part, int Z, int F, float* out)
   out[i] = s;
 }
 
+// a[i] += b[i]
+__global__ void add_into_kernel(float* a, const float* b, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] += b[i];
+}
+
 // Per row (z, n), one wave: den = phi(z_q) . ks + eps; lin = num / den (in place).
 __global__ void den_lin_kernel(const float* zq, const float* ks, float* num, float* den, int Z, int N, int F, int D,
                                float eps) {
@@ -416,27 +422,27 @@ static hipError_t launch_dz(float* dphi, const float* zv, const float* r, const 
 // ---------------------------------------------------------------- host side
 BackwardLayout backward_layout(const Problem& p) {
   BackwardLayout l;
-  const size_t Z = (size_t)p.B * p.H, N = p.N, F = p.F, D = p.D;
+  const size_t Z = (size_t)p.B * p.H, N = p.N, NQ = query_rows(p), F = p.F, D = p.D;
   size_t o = 0;
   auto take = [&](size_t n) {
     const size_t at = o;
     o += (n * 4 + 255) & ~(size_t)255;
     return at;
   };
-  l.zq = take(Z * N * F);
+  l.zq = take(Z * NQ * F);
   l.zk = take(Z * N * F);
-  l.dzq = take(Z * N * F);
+  l.dzq = take(Z * NQ * F);
   l.dzk = take(Z * N * F);
-  l.lin = take(Z * N * D);
-  l.lm = take(Z * N * D);
-  l.dnum = take(Z * N * D);
+  l.lin = take(Z * NQ * D);
+  l.lm = take(Z * NQ * D);
+  l.dnum = take(Z * NQ * D);
   l.kv = take(Z * F * D);
   l.dkv = take(Z * F * D);
   l.ks = take(Z * F);
   l.dks = take(Z * F);
-  l.den = take(Z * N);
-  l.dden = take(Z * N);
-  l.rpart = take(Z * N);
+  l.den = take(Z * NQ);
+  l.dden = take(Z * NQ);
+  l.rpart = take(Z * NQ);
   l.colpart = take(Z * kColSplit * F);
   l.splitk = take(splitk_elems(p));
   l.bytes = o;
@@ -469,19 +475,21 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
                                         const float* bias, float eps, int L, const BwBufs& t, hipStream_t s,
                                         StageTimer* tm) {
   float *zq = t.zq, *zk = t.zk, *lin = t.lin, *lm = t.lm, *kv = t.kv, *ks = t.ks, *den = t.den;
-  const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H, dt = p.dtype;
+  const int B = p.B, H = p.H, N = p.N, NQ = query_rows(p), D = p.D, F = p.F, Z = B * H, dt = p.dtype;
   const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
-  // z_q = Q W + b, z_k = K W + b: per (b, h), [N x D] . [D x F]; the bias in a second pass
-  auto proj = [&](const void* X, float* Zout) {
+  const long long QF = (long long)NQ * F, QD = (long long)NQ * D;
+  // z_q = Q W + b, z_k = K W + b: per (b, h), [rows x D] . [D x F], the bias in the epilogue
+  auto proj = [&](const void* X, float* Zout, int rows) {
+    const long long RD = (long long)rows * D, RF = (long long)rows * F;
     BgemmArgs a{};
     a.A = X;
     a.B = W;
     a.C = Zout;
-    a.M = N;
+    a.M = rows;
     a.N = F;
     a.K = D;
     a.KB = 1;
-    a.sAz = ND;
+    a.sAz = RD;
     a.sAm = D;
     a.sAk = 1;
     // W[h] for z = b*H + h: z-stride cannot express "z % H", so launch per batch
@@ -492,19 +500,19 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     a.beta = 0;
     for (int b = 0; b < B; ++b) {
       BgemmArgs ab = a;
-      ab.A = static_cast<const unsigned char*>(X) + (size_t)b * H * ND * (dt == 1 ? 2 : 4);
-      ab.C = Zout + (size_t)b * H * NF;
+      ab.A = static_cast<const unsigned char*>(X) + (size_t)b * H * RD * (dt == 1 ? 2 : 4);
+      ab.C = Zout + (size_t)b * H * RF;
       ab.sBz = (long long)D * F;
-      ab.sCz = NF;
+      ab.sCz = RF;
       ab.bias_n = bias;  // z = h within one batch row
       ab.sbz = F;
       TTR_HIP(launch_bgemm(dt, true, true, false, ab, H, s));
     }
     return hipSuccess;
   };
-  TTR_HIP(proj(Q, zq));
+  TTR_HIP(proj(Q, zq, NQ));
   tm->mark();
-  TTR_HIP(proj(K, zk));
+  TTR_HIP(proj(K, zk, N));
   tm->mark();
 
   // ks = sum_n phi(z_k); KV = phi(z_k)^T V
@@ -537,23 +545,23 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     a.A = zq;
     a.B = kv;
     a.C = lin;
-    a.M = N;
+    a.M = NQ;
     a.N = D;
     a.K = F;
     a.KB = 1;
-    a.sAz = NF;
+    a.sAz = QF;
     a.sAm = F;
     a.sAk = 1;
     a.sBz = FD;
     a.sBk = D;
     a.sBn = 1;
-    a.sCz = ND;
+    a.sCz = QD;
     a.sCm = D;
     a.sCn = 1;
     TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s));
     tm->mark();
   }
-  TTR_HIP(launch_den_lin(zq, ks, lin, den, Z, N, F, D, eps, s));
+  TTR_HIP(launch_den_lin(zq, ks, lin, den, Z, NQ, F, D, eps, s));
   tm->mark();
   // landmark branch output (fp32), for dalpha
   if (L > 0) {
@@ -563,6 +571,7 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     ha.V = V;
     ha.H = H;
     ha.N = N;
+    ha.Nq = NQ;
     ha.L = L;
     ha.out = lm;
     Problem pl = p;
@@ -580,10 +589,11 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
                                      hipStream_t s, StageTimer* tm) {
   float *zq = t.zq, *zk = t.zk, *dzq = t.dzq, *dzk = t.dzk, *lin = t.lin, *lm = t.lm, *dnum = t.dnum, *kv = t.kv;
   float *dkv = t.dkv, *ks = t.ks, *dks = t.dks, *den = t.den, *dden = t.dden, *rpart = t.rpart;
-  const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H, dt = p.dtype;
+  const int B = p.B, H = p.H, N = p.N, NQ = query_rows(p), D = p.D, F = p.F, Z = B * H, dt = p.dtype;
   const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
-  // dnum, dden, dalpha row shares
-  TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, N, D, Z, L > 0, dnum, dden, rpart, s));
+  const long long QF = (long long)NQ * F, QD = (long long)NQ * D;
+  // dnum, dden, dalpha row shares (one per query row)
+  TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, NQ, D, Z, L > 0, dnum, dden, rpart, s));
   tm->mark();
   // dphi_q = dnum KV^T (+ dden ks^T in dz): [N x D] . [D x F]
   {
@@ -591,17 +601,17 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.A = dnum;
     a.B = kv;  // B(k = d, n = f) = KV[f][d]
     a.C = dzq;
-    a.M = N;
+    a.M = NQ;
     a.N = F;
     a.K = D;
     a.KB = 1;
-    a.sAz = ND;
+    a.sAz = QD;
     a.sAm = D;
     a.sAk = 1;
     a.sBz = FD;
     a.sBk = 1;
     a.sBn = D;
-    a.sCz = NF;
+    a.sCz = QF;
     a.sCm = F;
     a.sCn = 1;
     TTR_HIP(launch_bgemm(dt, false, false, false, a, Z, s));
@@ -615,12 +625,12 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.C = dkv;
     a.M = F;
     a.N = D;
-    a.K = N;
+    a.K = NQ;
     a.KB = 1;
-    a.sAz = NF;
+    a.sAz = QF;
     a.sAm = 1;
     a.sAk = F;
-    a.sBz = ND;
+    a.sBz = QD;
     a.sBk = D;
     a.sBn = 1;
     a.sCz = FD;
@@ -629,10 +639,10 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s, t.splitk, t.splitk_n));
     tm->mark();
   }
-  TTR_HIP(launch_colsum<1>(zq, nullptr, dden, NF, N, 0, N, Z, F, t.colpart, dks, s));
+  TTR_HIP(launch_colsum<1>(zq, nullptr, dden, QF, NQ, 0, NQ, Z, F, t.colpart, dks, s));
   tm->mark();
   // dz_q = (dphi_q + dden ks^T) phi'(z_q)
-  TTR_HIP(launch_dz(dzq, zq, dden, ks, Z, N, F, s));
+  TTR_HIP(launch_dz(dzq, zq, dden, ks, Z, NQ, F, s));
   tm->mark();
   // dphi_k = V dKV^T (+ dks in dz): [N x D] . [D x F]
   {
@@ -659,21 +669,22 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
   TTR_HIP(launch_dz(dzk, zk, nullptr, dks, Z, N, F, s));
   tm->mark();
   // dW[h] = sum_b Q[b,h]^T dz_q[b,h] + K[b,h]^T dz_k[b,h]: the batch is the outer K loop
-  auto dw = [&](const void* X, const float* dzv, int beta) {
+  auto dw = [&](const void* X, const float* dzv, int rows, int beta) {
+    const long long RD = (long long)rows * D, RF = (long long)rows * F;
     BgemmArgs a{};
     a.A = X;  // A(m = d, k = n) = X[n][d]
     a.B = dzv;
     a.C = dW;
     a.M = D;
     a.N = F;
-    a.K = N;
+    a.K = rows;
     a.KB = B;
-    a.sAz = ND;
-    a.sAkb = (long long)H * ND;
+    a.sAz = RD;
+    a.sAkb = (long long)H * RD;
     a.sAm = 1;
     a.sAk = D;
-    a.sBz = NF;
-    a.sBkb = (long long)H * NF;
+    a.sBz = RF;
+    a.sBkb = (long long)H * RF;
     a.sBk = F;
     a.sBn = 1;
     a.sCz = (long long)D * F;
@@ -682,13 +693,20 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.beta = beta;
     return launch_bgemm(dt, true, false, false, a, H, s, t.splitk, t.splitk_n);
   };
-  TTR_HIP(dw(Q, dzq, 0));
+  TTR_HIP(dw(Q, dzq, NQ, 0));
   tm->mark();
-  TTR_HIP(dw(K, dzk, 1));
+  TTR_HIP(dw(K, dzk, N, 1));
   tm->mark();
   // db[h] over rows (b, n) of slice h; dg[h] from the row shares of dalpha
-  TTR_HIP(launch_colsum<2>(dzq, dzk, nullptr, NF, N, (long long)H * NF, B * N, H, F, t.colpart, db, s));
-  TTR_HIP(launch_colsum<3>(rpart, nullptr, nullptr, N, N, (long long)H * N, B * N, H, 1, t.colpart, dg, s));
+  if (NQ == N) {
+    TTR_HIP(launch_colsum<2>(dzq, dzk, nullptr, NF, N, (long long)H * NF, B * N, H, F, t.colpart, db, s));
+  } else {  // query and key rows differ in number: two sums (dks, no longer needed, holds the second)
+    TTR_HIP(launch_colsum<3>(dzq, nullptr, nullptr, QF, NQ, (long long)H * QF, B * NQ, H, F, t.colpart, db, s));
+    TTR_HIP(launch_colsum<3>(dzk, nullptr, nullptr, NF, N, (long long)H * NF, B * N, H, F, t.colpart, dks, s));
+    hipLaunchKernelGGL(add_into_kernel, dim3(blocks((size_t)H * F, 256)), dim3(256), 0, s, db, dks, H * F);
+    TTR_HIP(hipGetLastError());
+  }
+  TTR_HIP(launch_colsum<3>(rpart, nullptr, nullptr, NQ, NQ, (long long)H * NQ, B * NQ, H, 1, t.colpart, dg, s));
   hipLaunchKernelGGL(dg_scale_kernel, dim3(blocks(H, 64)), dim3(64), 0, s, dg, g, H, L > 0 ? 1 : 0);
   TTR_HIP(hipGetLastError());
   tm->mark();
@@ -851,7 +869,7 @@ __global__ void to_bf16_kernel(const float* x, uint16_t* y, size_t n) {
 
 DistillLayout distill_layout(const Problem& p, bool need_teacher) {
   DistillLayout l;
-  const size_t Z = (size_t)p.B * p.H, N = p.N, D = p.D, F = p.F, H = p.H;
+  const size_t Z = (size_t)p.B * p.H, N = query_rows(p), D = p.D, F = p.F, H = p.H;  // N: query rows here
   auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
   size_t o = al(backward_layout(p).bytes);
   l.w_io = o;
@@ -885,7 +903,7 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
                                float eps, int L, float* loss_out, void* ws, hipStream_t s, StageTimer* tm) {
   const DistillLayout l = distill_layout(p, teacher == nullptr);
   unsigned char* w8 = static_cast<unsigned char*>(ws);
-  const int B = p.B, H = p.H, N = p.N, D = p.D, F = p.F, Z = B * H;
+  const int B = p.B, H = p.H, N = p.N, NQ = query_rows(p), D = p.D, F = p.F, Z = B * H;
   const size_t nW = (size_t)H * D * F, nb = (size_t)H * F;
   // weights in the IO dtype for the forward and backward
   const void* Wio = W;
@@ -909,8 +927,10 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
       TTR_HIP(hipGetLastError());
       FusedPack pk;
       StageTimer none;
-      TTR_HIP(launch_kv2(p, K, V, Wio, bias, N, w8 + l.tws, &pk, s, &none));
-      TTR_HIP(launch_fused_query(p, Q, pk, gneg, eps, N, tb, s));
+      TTR_HIP(launch_kv2(p, K, V, Wio, bias, N, w8 + l.tws, &pk, s, &none));  // over the N keys
+      Problem pq = p;  // the query kernel tiles the query rows
+      pq.N = NQ;
+      TTR_HIP(launch_fused_query(pq, Q, pk, gneg, eps, N, tb, s));
       Tb = tb;
     } else {
       float* tw = reinterpret_cast<float*>(w8 + l.teacher);
@@ -920,6 +940,7 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
       ha.V = V;
       ha.H = H;
       ha.N = N;
+      ha.Nq = NQ;
       ha.L = N;
       ha.out = tw;
       Problem pl = p;
@@ -937,15 +958,15 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
   float* crw = reinterpret_cast<float*>(w8 + l.crow);
   float* gr = reinterpret_cast<float*>(w8 + l.grads);
   float *dW = gr, *db = gr + nW, *dg = db + nb, *ds = dg + H;
-  hipLaunchKernelGGL(distill_loss_rows_kernel, dim3(blocks((size_t)Z * N, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
-                     g, sv, H, N, D, Z, L > 0 ? 1 : 0, dout, hrow, crw);
+  hipLaunchKernelGGL(distill_loss_rows_kernel, dim3(blocks((size_t)Z * NQ, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
+                     g, sv, H, NQ, D, Z, L > 0 ? 1 : 0, dout, hrow, crw);
   TTR_HIP(hipGetLastError());
   tm->mark();
   float* lpart = reinterpret_cast<float*>(w8 + l.lpart);
-  const int nparts = (Z * N + kLossRows - 1) / kLossRows;
-  hipLaunchKernelGGL(distill_loss_part_kernel, dim3(nparts), dim3(256), 0, s, hrow, crw, Z * N, lpart);
+  const int nparts = (Z * NQ + kLossRows - 1) / kLossRows;
+  hipLaunchKernelGGL(distill_loss_part_kernel, dim3(nparts), dim3(256), 0, s, hrow, crw, Z * NQ, lpart);
   TTR_HIP(hipGetLastError());
-  hipLaunchKernelGGL(distill_loss_total_kernel, dim3(1), dim3(64), 0, s, lpart, nparts, Z * N, D, sv, loss_out, ds);
+  hipLaunchKernelGGL(distill_loss_total_kernel, dim3(1), dim3(64), 0, s, lpart, nparts, Z * NQ, D, sv, loss_out, ds);
   TTR_HIP(hipGetLastError());
   tm->mark();
   TTR_HIP(backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s, tm));

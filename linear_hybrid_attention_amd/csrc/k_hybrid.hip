@@ -72,10 +72,10 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int bh = blockIdx.y, h = bh % a.H;
-  const int N = a.N;
+  const int N = a.N, NQ = a.Nq > 0 ? a.Nq : a.N;  // keys, query rows
   const int tok = blockIdx.x * 128 + 32 * w + c;
-  const bool tok_ok = tok < N;
-  const T* Q = static_cast<const T*>(a.Q) + (size_t)bh * N * D;
+  const bool tok_ok = tok < NQ;
+  const T* Q = static_cast<const T*>(a.Q) + (size_t)bh * NQ * D;
 
   // Q^T as B operand: lane = token, k-slots = 8 consecutive features of Q.
   Frag<T> qf[D / 16];
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
 
       if constexpr ((MODE & M_PHI) != 0) {
         if (tok_ok) {
-          OutT* o = static_cast<OutT*>(a.out) + ((size_t)bh * N + tok) * F + fc * 32 + 4 * g;
+          OutT* o = static_cast<OutT*>(a.out) + ((size_t)bh * NQ + tok) * F + fc * 32 + 4 * g;
 #pragma unroll
           for (int q = 0; q < 4; ++q) st4(o + 8 * q, p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
         }
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
 
   if constexpr (MODE != M_PHI) {
     if (tok_ok) {
-      OutT* o = static_cast<OutT*>(a.out) + ((size_t)bh * N + tok) * D + 4 * g;
+      OutT* o = static_cast<OutT*>(a.out) + ((size_t)bh * NQ + tok) * D + 4 * g;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
 template <typename T, int D, bool PROJ, int MAP>
 static hipError_t launch_hybrid_t(int mode, bool out_io, const HybridArgs& a, int B, hipStream_t s) {
   constexpr int F = PROJ ? 256 : D;
-  const dim3 grid((a.N + 127) / 128, B * a.H), block(256);
+  const dim3 grid(((a.Nq > 0 ? a.Nq : a.N) + 127) / 128, B * a.H), block(256);
   switch (mode) {
     case M_PHI:
       hipLaunchKernelGGL((hybrid_kernel<T, D, F, PROJ, M_PHI, T, MAP>), grid, block, 0, s, a);

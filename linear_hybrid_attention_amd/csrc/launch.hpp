@@ -14,7 +14,11 @@ struct Problem {
   int dtype;  // 0 = fp32, 1 = bf16
   bool proj;  // W present (F == 256) or identity map (F == D)
   int fmap;   // feature map: kElu1, kRelu or kSoftmax (the last two only without W)
+  int Nq;     // query rows (a replay sample keeps fewer queries than keys); 0 means N
 };
+
+// Query rows of a problem: N unless the queries are a subsample of the N keys.
+inline int query_rows(const Problem& p) { return p.Nq > 0 ? p.Nq : p.N; }
 
 enum { M_PHI = 1, M_LIN = 2, M_LM = 4 };
 
@@ -42,8 +46,9 @@ struct HybridArgs {
   const float* ksum;  // fp32 [B,H,F]
   const float* g;     // fp32 [H]
   float eps;
-  int H, N, L;
+  int H, N, L;  // N keys (and queries unless Nq is set)
   void* out;
+  int Nq;       // query rows when they differ from the keys' N (0: N)
 };
 
 // k_hybrid.hip: feature map / apply / landmark / fused apply+landmark+blend.

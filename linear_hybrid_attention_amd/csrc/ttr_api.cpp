@@ -46,6 +46,7 @@ Problem make_problem(const ttr_dims& d, bool proj) {
   p.dtype = d.dtype;
   p.proj = proj;
   p.fmap = d.fmap;
+  p.Nq = d.N;
   return p;
 }
 
@@ -461,14 +462,22 @@ ttr_status ttr_hybrid_backward(ttr_dims d, const void* Q, const void* K, const v
 }
 
 size_t ttr_distill_workspace_bytes(ttr_dims d, int32_t L, int32_t compute_teacher) {
-  if (check_backward(d, L) != TTR_OK) return 0;
-  return distill_layout(make_problem(d, true), compute_teacher != 0).bytes;
+  return ttr_distill_rows_workspace_bytes(d, d.N, L, compute_teacher);
 }
 
-ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void* V, const float* teacher, float* W,
-                            float* b, float* g, float* s, float* moments, int32_t step, float lr, float eps, int32_t L,
-                            float* loss, void* ws, size_t ws_bytes, void* stream) {
+size_t ttr_distill_rows_workspace_bytes(ttr_dims d, int32_t Nq, int32_t L, int32_t compute_teacher) {
+  if (check_backward(d, L) != TTR_OK || Nq < 1 || Nq > d.N) return 0;
+  Problem p = make_problem(d, true);
+  p.Nq = Nq;
+  return distill_layout(p, compute_teacher != 0).bytes;
+}
+
+ttr_status ttr_distill_step_rows(ttr_dims d, int32_t Nq, const void* Q, const void* K, const void* V,
+                                 const float* teacher, float* W, float* b, float* g, float* s, float* moments,
+                                 int32_t step, float lr, float eps, int32_t L, float* loss, void* ws, size_t ws_bytes,
+                                 void* stream) {
   TTR_TRY(check_backward(d, L));
+  if (Nq < 1 || Nq > d.N) return TTR_ERR_SHAPE;
   if (step < 1 || !(lr > 0.f) || !(lr < 1e30f)) return TTR_ERR_SHAPE;
   TTR_TRY(check_ptr(Q));
   TTR_TRY(check_ptr(K));
@@ -477,15 +486,16 @@ ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void
   for (const void* ptr : {(const void*)W, (const void*)b, (const void*)g, (const void*)s, (const void*)moments,
                           (const void*)loss})
     TTR_TRY(check_ptr(ptr));
-  const Problem p = make_problem(d, true);
+  Problem p = make_problem(d, true);
+  p.Nq = Nq;
   const size_t need = distill_layout(p, teacher == nullptr).bytes;
   if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
   TTR_TRY(check_ptr(ws));
   const size_t nW = (size_t)d.H * d.D * d.F * 4, nb = (size_t)d.H * d.F * 4, ng = (size_t)d.H * 4;
   const size_t nm = 2 * (nW + nb + ng + 8);
+  const size_t q_bytes = (size_t)d.B * d.H * Nq * d.D * io(d), rows_f32 = (size_t)d.B * d.H * Nq * d.D * 4;
   const Range outs[] = {{W, nW}, {b, nb}, {g, ng}, {s, 8}, {moments, nm}, {loss, 12}, {ws, need}};
-  const Range ins[] = {{Q, qkv_bytes(d)}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)},
-                       {teacher, teacher ? f32_out_bytes(d) : 0}};
+  const Range ins[] = {{Q, q_bytes}, {K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {teacher, teacher ? rows_f32 : 0}};
   TTR_TRY(check_no_alias(outs, 7, ins, 4));
   hipStream_t st = (hipStream_t)stream;
   StageTimer t = take_stage_timer(st);
@@ -493,6 +503,13 @@ ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void
       launch_distill_step(p, Q, K, V, teacher, W, b, g, s, moments, step, lr, eps, L, loss, ws, st, &t));
   t.finish();
   return r;
+}
+
+ttr_status ttr_distill_step(ttr_dims d, const void* Q, const void* K, const void* V, const float* teacher, float* W,
+                            float* b, float* g, float* s, float* moments, int32_t step, float lr, float eps, int32_t L,
+                            float* loss, void* ws, size_t ws_bytes, void* stream) {
+  return ttr_distill_step_rows(d, d.N, Q, K, V, teacher, W, b, g, s, moments, step, lr, eps, L, loss, ws, ws_bytes,
+                               stream);
 }
 
 size_t ttr_cosine_workspace_bytes(ttr_dims d) {

@@ -49,18 +49,27 @@ def _nerr(got, ref):
     return float(np.abs(got - ref).max() / scale) if scale > 0 else float(np.abs(got).max())
 
 
-def _one_step(w, teacher_given=False):
-    print(f"[distill] {w.name} {w.dtype} B={w.B} H={w.H} N={w.N} L={w.L} teacher_given={teacher_given}", flush=True)
+def _one_step(w, teacher_given=False, nq=None):
+    """One step on every query row, or (nq) on a seeded subsample of nq query
+    rows over all keys and values, as for a replay sample."""
+    print(f"[distill] {w.name} {w.dtype} B={w.B} H={w.H} N={w.N} L={w.L} teacher_given={teacher_given} nq={nq}",
+          flush=True)
     x, b, st, Q, K, V = _setup(w)
     eps = float(x["eps"])
-    T = O.full_softmax_attention(x["Q"], x["K"], x["V"])
-    Tt = torch.from_numpy(T.astype(np.float32)).to(DEV) if teacher_given else None
+    xq = x["Q"]
+    if nq is not None:
+        idx = workloads.query_subsample(w.N, nq, w.seed + 11)
+        xq = x["Q"][:, :, idx]
+        Q = (torch.from_numpy(np.ascontiguousarray(x["Q_bits"][:, :, idx]).view(np.int16)).view(torch.bfloat16)
+             if w.dtype == "bf16" else torch.from_numpy(np.ascontiguousarray(xq))).to(DEV)
+    T = O.full_softmax_attention(xq, x["K"], x["V"])
+    Tt = torch.from_numpy(np.ascontiguousarray(T, dtype=np.float32)).to(DEV) if teacher_given else None
     loss = ttr.distill_step(st, Q, K, V, w.L, LR, eps, teacher=Tt).cpu().numpy()
     torch.cuda.synchronize()
     s0 = np.zeros(2)
-    W2, b2, g2, s2, rs, rloss = O.distill_step(x["Q"], x["K"], x["V"], x["W"], b, x["g"], s0,
+    W2, b2, g2, s2, rs, rloss = O.distill_step(xq, x["K"], x["V"], x["W"], b, x["g"], s0,
                                                _ref_state(x["W"], b, x["g"], s0), 1, LR, eps, w.L, T)
-    out = O.hybrid_forward(x["Q"], x["K"], x["V"], x["W"], b, x["g"], eps, w.L)
+    out = O.hybrid_forward(xq, x["K"], x["V"], x["W"], b, x["g"], eps, w.L)
     _, _, _, rH, rC = O.distill_loss(out, T, s0)
     tol = TOL[w.dtype]
     errs = {"loss": abs(loss[0] - rloss) / abs(rloss), "huber": abs(loss[1] - rH) / abs(rH),
@@ -99,6 +108,38 @@ def test_distill_step_bf16():
 
 def test_distill_step_bf16_no_landmarks():
     _one_step(workloads.WORKLOADS["flux_512"].with_(name="ds_bf16_l0", B=1, H=2, N=200, L=0))
+
+
+@pytest.mark.parametrize("dtype,teacher_given,L,N,nq", [
+    ("fp32", True, 10, 100, 23), ("fp32", False, 10, 100, 37), ("bf16", True, 20, 300, 77),
+    ("bf16", False, 20, 300, 130), ("bf16", True, 0, 257, 65)])
+def test_distill_step_on_sampled_query_rows(dtype, teacher_given, L, N, nq):
+    base = workloads.WORKLOADS["tiny_fp32"] if dtype == "fp32" else workloads.WORKLOADS["flux_512"]
+    w = base.with_(name=f"ds_rows_{dtype}", B=1, H=2, N=N, L=L, b_std=0.1)
+    _one_step(w, teacher_given=teacher_given, nq=nq)
+
+
+def test_phase1_chain_through_the_replay_buffer():
+    # teacher on every query, push (K, V whole, a quarter of the queries, the teacher's rows),
+    # fetch, and one student step on the fetched sample: the oracle's step on the same rows
+    w = workloads.WORKLOADS["flux_512"].with_(name="ds_replay", B=1, H=3, N=600, L=24)
+    x, b, st, Q, K, V = _setup(w)
+    eps = float(x["eps"])
+    idx = workloads.query_subsample(w.N, w.N // 4, 7)
+    T = O.full_softmax_attention(x["Q"], x["K"], x["V"])
+    with ttr.ReplayBuffer(64 << 20, 32 << 20) as rb:
+        sid = rb.push(Q, K, V, idx, torch.from_numpy(np.ascontiguousarray(T, dtype=np.float32)).to(DEV))
+        Qs, Ks, Vs, Ts, got_idx = rb.fetch(sid)
+        assert np.array_equal(got_idx, idx)
+        loss = ttr.distill_step(st, Qs, Ks, Vs, w.L, LR, eps, teacher=Ts).cpu().numpy()
+    s0 = np.zeros(2)
+    Tr = T[:, :, idx].astype(np.float32).astype(np.float64)  # the rows as stored (fp32)
+    W2, b2, g2, s2, rs, rloss = O.distill_step(x["Q"][:, :, idx], x["K"], x["V"], x["W"], b, x["g"], s0,
+                                               _ref_state(x["W"], b, x["g"], s0), 1, LR, eps, w.L, Tr)
+    print(f"[distill] replay chain loss {loss[0]:.6f} vs {rloss:.6f}", flush=True)
+    assert abs(loss[0] - rloss) <= TOL["bf16"] * abs(rloss)
+    m_got = st.moments.cpu().numpy()[:x["W"].size].reshape(x["W"].shape)
+    assert _nerr(m_got, rs["mW"]) <= TOL["bf16"]
 
 
 def test_distill_trajectory_matches_oracle_fp32():
