@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--distill", action="store_true",
                     help="time one Phase-1 distillation step (teacher, student, loss, backward, Adam) instead")
     ap.add_argument("--lr", type=float, default=1e-4, help="Adam learning rate of the distillation step")
+    ap.add_argument("--nq", type=int, default=0,
+                    help="with --distill: train on a replay sample of NQ query rows (teacher rows given)")
     ap.add_argument("--cosine", action="store_true",
                     help="time the student/teacher cosine distance of the readiness gate instead")
     ap.add_argument("--replay", action="store_true",
@@ -223,6 +225,7 @@ def cpu_baseline(w, x, target_s):
     """
     import numpy as np
     import oracle.ttr_oracle as O
+    import workloads
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -407,35 +410,40 @@ def main_layer(args):
     print(json.dumps(res), flush=True)
 
 
-def distill_plan(w):
-    """Launches of one distillation step (teacher computed, bias present), in
-    order: (name, algorithmic flops, algorithmic bytes)."""
-    Z, N, D, F, L, B, H = w.B * w.H, w.N, w.D, w.F, w.L, w.B, w.H
+def distill_plan(w, nq=None):
+    """Launches of one distillation step, in order: (name, algorithmic flops,
+    algorithmic bytes). nq: a replay sample's query rows (the teacher's rows
+    given, so no teacher stage); else every query row and the teacher computed."""
+    Z, N, D, F, L = w.B * w.H, w.N, w.D, w.F, w.L
+    NQ = N if nq is None else nq
     io = 2 if w.dtype == "bf16" else 4
-    gemm_nd = 2 * Z * N * D * F  # every product of the layer is N x D x F per (b, h)
+    gq, gk = 2 * Z * NQ * D * F, 2 * Z * N * D * F  # a product over the query rows / the key rows
     plan = []
     if w.dtype == "bf16":
         plan.append(("to_bf16_kernel (W)", 0, 0))
-    teacher = ("teacher softmax attention (kv2 + fused query kernel, every token a landmark, alpha 0)"
-               if w.dtype == "bf16" else "teacher softmax attention (hybrid_kernel, L = N)")
-    plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
-    plan += [("bgemm z_q = Q W + b", gemm_nd, 0), ("bgemm z_k = K W + b", gemm_nd, 0),
-             ("colsum ksum", 0, 0), ("bgemm KV = phi_k^T V", gemm_nd, 0), ("bgemm num = phi_q KV", gemm_nd, 0),
-             ("den_lin_kernel", 2 * Z * N * F, 0)]
+    if nq is None:
+        teacher = ("teacher softmax attention (kv2 + fused query kernel, every token a landmark, alpha 0)"
+                   if w.dtype == "bf16" else "teacher softmax attention (hybrid_kernel, L = N)")
+        plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
+    plan += [("bgemm z_q = Q W + b", gq, 0), ("bgemm z_k = K W + b", gk, 0),
+             ("colsum ksum", 0, 0), ("bgemm KV = phi_k^T V", gk, 0), ("bgemm num = phi_q KV", gq, 0),
+             ("den_lin_kernel", 2 * Z * NQ * F, 0)]
     if L > 0:
-        plan.append(("landmark branch (hybrid_kernel)", 4 * Z * N * L * D, 0))
+        plan.append(("landmark branch (hybrid_kernel)", 4 * Z * NQ * L * D, 0))
     plan += [("distill_loss_rows_kernel", 0, 0), ("distill_loss_total_kernel", 0, 0), ("dlin_kernel", 0, 0),
-             ("bgemm dphi_q = dnum KV^T", gemm_nd, 0), ("bgemm dKV = phi_q^T dnum", gemm_nd, 0),
-             ("colsum dks", 2 * Z * N * F, 0), ("dz_kernel (q)", 0, 0), ("bgemm dphi_k = V dKV^T", gemm_nd, 0),
-             ("dz_kernel (k)", 0, 0), ("bgemm dW += Q^T dz_q", gemm_nd, 0), ("bgemm dW += K^T dz_k", gemm_nd, 0),
+             ("bgemm dz_q = (dnum KV^T + dden ks^T) phi'(z_q)", gq, 0), ("bgemm dKV = phi_q^T dnum", gq, 0),
+             ("colsum dks", 2 * Z * NQ * F, 0), ("bgemm dz_k = (V dKV^T + dks) phi'(z_k)", gk, 0),
+             ("bgemm dW += Q^T dz_q", gq, 0), ("bgemm dW += K^T dz_k", gk, 0),
              ("colsum db, dg", 0, 0), ("adam_kernel", 0, 0)]
     return plan
 
 
-def cpu_baseline_distill(w, x, target_s, lr):
-    """The oracle's distillation step on the first heads of the same inputs, scaled to all heads."""
+def cpu_baseline_distill(w, x, target_s, lr, nq=None):
+    """The oracle's distillation step on the first heads of the same inputs, scaled to all heads
+    (nq: on the replay sample's query rows, with its teacher rows given)."""
     import numpy as np
     import oracle.ttr_oracle as O
+    import workloads
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -448,8 +456,13 @@ def cpu_baseline_distill(w, x, target_s, lr):
         st = {k: np.zeros_like(v) for k, v in (("mW", W), ("vW", W), ("mb", b), ("vb", b), ("mg", g), ("vg", g))}
         st["ms"] = np.zeros(2)
         st["vs"] = np.zeros(2)
+        Qh = x["Q"][:, sl]
+        T = None
+        if nq is not None:
+            Qh = Qh[:, :, workloads.query_subsample(w.N, nq, w.seed)]
+            T = np.random.default_rng(w.seed + 5).standard_normal((w.B, w.H, nq, w.D), dtype=np.float32)[:, sl]
         t0 = time.perf_counter()
-        O.distill_step(x["Q"][:, sl], x["K"][:, sl], x["V"][:, sl], W, b, g, np.zeros(2), st, 1, lr, x["eps"], w.L)
+        O.distill_step(Qh, x["K"][:, sl], x["V"][:, sl], W, b, g, np.zeros(2), st, 1, lr, x["eps"], w.L, T)
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -461,8 +474,13 @@ def cpu_baseline_distill(w, x, target_s, lr):
         reps += 1
     t = total / reps
     sec_full = t * w.H / heads
-    sample = (f"{heads} of {w.H} heads (all {w.B} batch rows) of the {w.name} workload (N={w.N}), fp64 numpy oracle "
-              f"distillation step, {reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all heads")
+    rows = "" if nq is None else f", {nq} sampled query rows"
+    sample = (f"{heads} of {w.H} heads (all {w.B} batch rows) of the {w.name} workload (N={w.N}{rows}), fp64 numpy "
+              f"oracle distillation step, {reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all "
+              "heads")
+    if nq is not None:
+        return {"value": w.B / sec_full, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+                "sample": sample, "seconds_full_estimate": sec_full}
     return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": sample, "seconds_full_estimate": sec_full}
 
@@ -493,15 +511,26 @@ def main_distill(args):
                              torch.from_numpy(x["g"]).to(dev))
     lib = ttr.load_library()
     d = ttr.Dims(w.B, w.H, w.N, w.D, w.F, 1 if w.dtype == "bf16" else 0, 0)
-    ws = torch.empty(lib.ttr_distill_workspace_bytes(d, w.L, 1), dtype=torch.uint8, device=dev)
+    nq = args.nq if args.nq else None
+    teacher = None
+    if nq is not None:  # a replay sample: nq query rows over every key, the teacher's rows given
+        idx = workloads.query_subsample(w.N, nq, w.seed)
+        qsel = x["Q_bits" if w.dtype == "bf16" else "Q"][:, :, idx]
+        Q = torch.from_numpy(np.ascontiguousarray(qsel).view(np.int16 if w.dtype == "bf16" else np.float32))
+        Q = (Q.view(torch.bfloat16) if w.dtype == "bf16" else Q).to(dev)
+        teacher = torch.from_numpy(np.random.default_rng(w.seed + 5).standard_normal(
+            (w.B, w.H, nq, w.D), dtype=np.float32)).to(dev)
+        ws = torch.empty(lib.ttr_distill_rows_workspace_bytes(d, nq, w.L, 0), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(lib.ttr_distill_workspace_bytes(d, w.L, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    plan = distill_plan(w)
+    plan = distill_plan(w, nq)
     eps = float(x["eps"])
 
     def step(events=None):
         if events is not None:
             lib.ttr_set_stage_events(events, len(plan) + 1)
-        return ttr.distill_step(state, Q, K, V, w.L, args.lr, eps, ws=ws)
+        return ttr.distill_step(state, Q, K, V, w.L, args.lr, eps, teacher=teacher, ws=ws)
 
     for _ in range(args.warmup):
         step()
@@ -536,13 +565,21 @@ def main_distill(args):
         kernels[kn] = {"ms": kern_ms[kn], "flops": kf, "bytes": kb, "bound": r["bound"], "frac": r["frac"]}
     total_flops = sum(p[1] for p in plan)
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    if nq is None:
+        metric = (f"TTR distillation step tokens/sec ({w.name}: B={w.B}, H={w.H}, N={w.N}, L={w.L}; teacher, "
+                  "student, loss, backward and Adam)")
+        value, unit = w.B * w.N / (ms * 1e-3), "tokens/s"
+    else:
+        metric = (f"TTR distillation step on a replay sample, samples/sec ({w.name}: B={w.B}, H={w.H}, N={w.N} keys, "
+                  f"Nq={nq} query rows, L={w.L}; teacher rows given; student, loss, backward and Adam)")
+        value, unit = w.B / (ms * 1e-3), "samples/s"
     res = {
-        "metric": f"TTR distillation step tokens/sec ({w.name}: B={w.B}, H={w.H}, N={w.N}, L={w.L}; teacher, "
-                  "student, loss, backward and Adam)",
-        "value": w.B * w.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric,
+        "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "mode": "distill", "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F, "L": w.L,
+        "config": {"workload": w.name, "mode": "distill" if nq is None else "distill_sample", "B": w.B, "H": w.H,
+                   "N": w.N, "Nq": w.N if nq is None else nq, "D": w.D, "F": w.F, "L": w.L,
                    "lr": args.lr, "global_batch": w.B, "seq_len": w.N},
         "roofline": {"kernel": name, "bound": rl["bound"], "achieved": rl["achieved"], "peak": rl["peak"],
                      "unit": rl["unit"], "frac": rl["frac"], "traffic": None,
@@ -554,7 +591,7 @@ def main_distill(args):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_distill(w, x, args.cpu_seconds, args.lr)
+        res["cpu_baseline"] = cpu_baseline_distill(w, x, args.cpu_seconds, args.lr, nq)
     print(json.dumps(res), flush=True)
 
 

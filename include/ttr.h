@@ -373,7 +373,8 @@ int ttr_last_hip_error(void);
  *     as above, out projection;
  *   backward: Q projection, K projection (one stage each, whatever the batch),
  *     ksum, KV, num, normaliser, landmark branch (L > 0), then dnum/dden,
- *     dphi_q, dKV, dks, dz_q, dphi_k, dz_k, dW from Q, dW from K, db/dg;
+ *     dz_q (its product with the phi' factor in the epilogue), dKV, dks, dz_k
+ *     (likewise), dW from Q, dW from K, db/dg;
  *   distillation step: W to bf16 (bf16 IO), teacher (when computed), the
  *     backward's forward stages, loss rows, loss total, the backward's
  *     gradient stages, Adam;

@@ -37,6 +37,12 @@ struct BgemmArgs {
   long long sbz;
   int ksplit;           // > 1: blockIdx.z = z * ksplit + split; partial sums go to part
   float* part;          // [Z][ksplit][M][N]
+  // optional dz epilogue (no split-K): C(m, n) = (acc + r(m) s(n)) phi'(x(m, n)), phi = elu + 1,
+  // x = dz_x laid out like C, r = dz_r[z * dz_srz + m] (1 when NULL), s = dz_s[z * dz_ssz + n]
+  const float* dz_x;
+  const float* dz_r;
+  const float* dz_s;
+  long long dz_srz, dz_ssz;
 };
 
 template <typename CT> struct BgTile {
@@ -191,24 +197,49 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
     }
   }
   // lane (c, g) holds, per tile (i, j), column n0 + wn*64 + j*32 + c and rows crow(lane, r)
+  const bool dz = a.ksplit == 1 && a.dz_s != nullptr;
+  const float* __restrict__ dzx = a.dz_x;
+  float* __restrict__ Cz = a.C + z * a.sCz;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn * 64 + j * 32 + c;
     if (n >= a.N) continue;
     const float bn = (a.ksplit == 1 && a.bias_n) ? a.bias_n[z * a.sbz + n] : 0.f;
+    const float sn = dz ? a.dz_s[z * a.dz_ssz + n] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int mb = m0 + wm * 64 + i * 32;
+      if (a.ksplit > 1) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + crow(lane, r);
-        if (m >= a.M) continue;
-        if (a.ksplit > 1) {
-          a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[i][j][r];
-        } else {
-          float* p = a.C + z * a.sCz + (long long)m * a.sCm + (long long)n * a.sCn;
-          *p = (a.beta ? *p + acc[i][j][r] : acc[i][j][r]) + bn;
+        for (int r = 0; r < 16; ++r) {
+          const int m = mb + crow(lane, r);
+          if (m < a.M) a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[i][j][r];
+        }
+        continue;
+      }
+      // the dz operands of the 16 rows are loaded before any store
+      float xv[16], rv[16];
+      if (dz) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = min(mb + crow(lane, r), a.M - 1);
+          xv[r] = dzx[z * a.sCz + (long long)m * a.sCm + (long long)n * a.sCn];
+          rv[r] = a.dz_r ? a.dz_r[z * a.dz_srz + m] : 1.f;
         }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + crow(lane, r);
+        if (m >= a.M) continue;
+        float* p = Cz + (long long)m * a.sCm + (long long)n * a.sCn;
+        float v = (a.beta ? *p + acc[i][j][r] : acc[i][j][r]) + bn;
+        if (dz) {  // dz = (dphi + r s) phi'(x), phi'(x) = 1 for x > 0, exp(x) otherwise
+          const float dp = v + rv[r] * sn;
+          v = xv[r] > 0.f ? dp : dp * __expf(xv[r]);
+        }
+        *p = v;
+      }
+    }
   }
 }
 
@@ -250,6 +281,7 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   BgemmArgs a = a0;
   a.ksplit = 1;
   a.part = nullptr;
+  if (a.dz_s != nullptr) scratch = nullptr;  // the dz epilogue runs in the GEMM itself (no split-K)
   const int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128) * Z;
   const int steps = a.KB * ((a.K + 31) / 32);
   if (scratch != nullptr && tiles < 512 && steps >= 32) {
@@ -367,19 +399,6 @@ __global__ void dlin_kernel(const float* dout, const float* lin, const float* lm
   }
 }
 
-// dz[z][n][f] = (dphi[z][n][f] + r[z][n] s[z][f]) phi'(zv[z][n][f]), in place on dphi;
-// r == NULL means r = 1.
-__global__ void dz_kernel(float* dphi, const float* zv, const float* r, const float* sv, int Z, int N, int F) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (size_t)Z * N * F) return;
-  const int f = (int)(i % F);
-  const size_t row = i / F;
-  const int z = (int)(row / N);
-  const float x = zv[i];
-  const float dp = dphi[i] + (r ? r[row] : 1.f) * sv[(size_t)z * F + f];
-  dphi[i] = x > 0.f ? dp : dp * __expf(x);
-}
-
 // dg[h] *= alpha (1 - alpha) (or 0 without the landmark branch)
 __global__ void dg_scale_kernel(float* dg, const float* g, int H, int has_lm) {
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
@@ -412,11 +431,6 @@ static hipError_t launch_dlin(const float* dout, const float* lin, const float* 
                               hipStream_t s) {
   hipLaunchKernelGGL(dlin_kernel, dim3(blocks((size_t)Z * N, 4)), dim3(256), 0, s, dout, lin, lm, den, g, H, N, D, Z,
                      has_lm ? 1 : 0, dnum, dden, rpart);
-  return hipGetLastError();
-}
-static hipError_t launch_dz(float* dphi, const float* zv, const float* r, const float* sv, int Z, int N, int F,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(dz_kernel, dim3(blocks((size_t)Z * N * F, 256)), dim3(256), 0, s, dphi, zv, r, sv, Z, N, F);
   return hipGetLastError();
 }
 // ---------------------------------------------------------------- host side
@@ -595,12 +609,17 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
   // dnum, dden, dalpha row shares (one per query row)
   TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, NQ, D, Z, L > 0, dnum, dden, rpart, s));
   tm->mark();
-  // dphi_q = dnum KV^T (+ dden ks^T in dz): [N x D] . [D x F]
+  // dz_q = (dnum KV^T + dden ks^T) phi'(z_q): [Nq x D] . [D x F], the rest in the epilogue
   {
     BgemmArgs a{};
     a.A = dnum;
     a.B = kv;  // B(k = d, n = f) = KV[f][d]
     a.C = dzq;
+    a.dz_x = zq;
+    a.dz_r = dden;
+    a.dz_s = ks;
+    a.dz_srz = NQ;
+    a.dz_ssz = F;
     a.M = NQ;
     a.N = F;
     a.K = D;
@@ -641,15 +660,15 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
   }
   TTR_HIP(launch_colsum<1>(zq, nullptr, dden, QF, NQ, 0, NQ, Z, F, t.colpart, dks, s));
   tm->mark();
-  // dz_q = (dphi_q + dden ks^T) phi'(z_q)
-  TTR_HIP(launch_dz(dzq, zq, dden, ks, Z, NQ, F, s));
-  tm->mark();
-  // dphi_k = V dKV^T (+ dks in dz): [N x D] . [D x F]
+  // dz_k = (V dKV^T + 1 dks^T) phi'(z_k): [N x D] . [D x F], the rest in the epilogue
   {
     BgemmArgs a{};
     a.A = V;
     a.B = dkv;  // B(k = d, n = f) = dKV[f][d]
     a.C = dzk;
+    a.dz_x = zk;
+    a.dz_s = dks;
+    a.dz_ssz = F;
     a.M = N;
     a.N = F;
     a.K = D;
@@ -666,8 +685,6 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     TTR_HIP(launch_bgemm(dt, true, false, false, a, Z, s));
     tm->mark();
   }
-  TTR_HIP(launch_dz(dzk, zk, nullptr, dks, Z, N, F, s));
-  tm->mark();
   // dW[h] = sum_b Q[b,h]^T dz_q[b,h] + K[b,h]^T dz_k[b,h]: the batch is the outer K loop
   auto dw = [&](const void* X, const float* dzv, int rows, int beta) {
     const long long RD = (long long)rows * D, RF = (long long)rows * F;
