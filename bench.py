@@ -426,15 +426,15 @@ def distill_plan(w, nq=None):
                    if w.dtype == "bf16" else "teacher softmax attention (hybrid_kernel, L = N)")
         plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
     plan += [("bgemm z_q = Q W + b", gq, 0), ("bgemm z_k = K W + b", gk, 0),
-             ("colsum ksum", 0, 0), ("bgemm KV = phi_k^T V", gk, 0), ("bgemm num = phi_q KV", gq, 0),
+             ("ksum (tile sums of the z_k epilogue)", 0, 0), ("bgemm KV = phi_k^T V", gk, 0), ("bgemm num = phi_q KV", gq, 0),
              ("den_lin_kernel", 2 * Z * NQ * F, 0)]
     if L > 0:
         plan.append(("landmark branch (hybrid_kernel)", 4 * Z * NQ * L * D, 0))
     plan += [("distill_loss_rows_kernel", 0, 0), ("distill_loss_total_kernel", 0, 0), ("dlin_kernel", 0, 0),
              ("bgemm dz_q = (dnum KV^T + dden ks^T) phi'(z_q)", gq, 0), ("bgemm dKV = phi_q^T dnum", gq, 0),
-             ("colsum dks", 2 * Z * NQ * F, 0), ("bgemm dz_k = (V dKV^T + dks) phi'(z_k)", gk, 0),
+             ("dks (tile sums of the dz_q epilogue)", 0, 0), ("bgemm dz_k = (V dKV^T + dks) phi'(z_k)", gk, 0),
              ("bgemm dW += Q^T dz_q", gq, 0), ("bgemm dW += K^T dz_k", gk, 0),
-             ("colsum db, dg", 0, 0), ("adam_kernel", 0, 0)]
+             ("db (tile sums of the dz epilogues), dg", 0, 0), ("adam_kernel", 0, 0)]
     return plan
 
 

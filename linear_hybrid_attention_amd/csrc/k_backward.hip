@@ -43,6 +43,12 @@ struct BgemmArgs {
   const float* dz_r;
   const float* dz_s;
   long long dz_srz, dz_ssz;
+  // optional column sums of the epilogue (no split-K), as partials per (z, 64-row half
+  // tile): [z][2 ceil(M / 128)][N], of the written values (cs_val), of elu1(dz_x) dz_r
+  // (cs_phir) or of elu1 of the written values (cs_phi)
+  float* cs_val;
+  float* cs_phir;
+  float* cs_phi;
 };
 
 template <typename CT> struct BgTile {
@@ -198,14 +204,16 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
   }
   // lane (c, g) holds, per tile (i, j), column n0 + wn*64 + j*32 + c and rows crow(lane, r)
   const bool dz = a.ksplit == 1 && a.dz_s != nullptr;
+  const bool cs = a.ksplit == 1 && (a.cs_val || a.cs_phir || a.cs_phi);
   const float* __restrict__ dzx = a.dz_x;
   float* __restrict__ Cz = a.C + z * a.sCz;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn * 64 + j * 32 + c;
-    if (n >= a.N) continue;
+    if (n >= a.N) continue;  // (lanes c and c + 32 share n: both skip or both go on)
     const float bn = (a.ksplit == 1 && a.bias_n) ? a.bias_n[z * a.sbz + n] : 0.f;
     const float sn = dz ? a.dz_s[z * a.dz_ssz + n] : 0.f;
+    float cv = 0.f, cp = 0.f, cq = 0.f;  // this lane's column sums over its rows of the half tile
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int mb = m0 + wm * 64 + i * 32;
@@ -236,8 +244,22 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
         if (dz) {  // dz = (dphi + r s) phi'(x), phi'(x) = 1 for x > 0, exp(x) otherwise
           const float dp = v + rv[r] * sn;
           v = xv[r] > 0.f ? dp : dp * __expf(xv[r]);
+          if (a.cs_phir) cp += elu1(xv[r]) * rv[r];
         }
+        if (a.cs_val) cv += v;
+        if (a.cs_phi) cq += elu1(v);
         *p = v;
+      }
+    }
+    if (cs) {  // the column's two lanes (rows 4g..) combine; one partial per (z, half tile)
+      cv += __shfl_xor(cv, 32);
+      cp += __shfl_xor(cp, 32);
+      cq += __shfl_xor(cq, 32);
+      if (g == 0) {
+        const size_t at = ((size_t)z * (2 * gridDim.x) + 2 * blockIdx.x + wm) * a.N + n;
+        if (a.cs_val) a.cs_val[at] = cv;
+        if (a.cs_phir) a.cs_phir[at] = cp;
+        if (a.cs_phi) a.cs_phi[at] = cq;
       }
     }
   }
@@ -281,7 +303,7 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   BgemmArgs a = a0;
   a.ksplit = 1;
   a.part = nullptr;
-  if (a.dz_s != nullptr) scratch = nullptr;  // the dz epilogue runs in the GEMM itself (no split-K)
+  if (a.dz_s != nullptr || a.cs_val || a.cs_phir || a.cs_phi) scratch = nullptr;  // epilogue work: no split-K
   const int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128) * Z;
   const int steps = a.KB * ((a.K + 31) / 32);
   if (scratch != nullptr && tiles < 512 && steps >= 32) {
@@ -348,10 +370,28 @@ __global__ void colsum_final_kernel(const float* part, int Z, int F, float* out)
   out[i] = s;
 }
 
-// a[i] += b[i]
-__global__ void add_into_kernel(float* a, const float* b, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) a[i] += b[i];
+// Column sums from the GEMM epilogues' half-tile partials, in a fixed order:
+// out[o][n] = sum_{b < nb} (sum_{t < t1} p1[(b zs + o)][t][n] + sum_{t < t2} p2[(b zs + o)][t][n])
+// (p2 may be NULL). Workgroup (x, o): columns 64 x .. 64 x + 63 of output row o;
+// thread group q (0..3) adds the partials t = q, q + 4, ... in order, and the
+// four group sums are added in order.
+__global__ __launch_bounds__(256) void tile_colsum_kernel(const float* p1, int t1, const float* p2, int t2, int nb,
+                                                          int zs, int ncol, float* out) {
+  __shared__ float sh[4][64];
+  const int n = blockIdx.x * 64 + (threadIdx.x & 63), q = threadIdx.x >> 6, o = blockIdx.y;
+  float s = 0.f;
+  if (n < ncol) {
+    for (int b = 0; b < nb; ++b) {
+      const size_t zz = (size_t)b * zs + o;
+      for (int t = q; t < t1; t += 4) s += p1[(zz * t1 + t) * ncol + n];
+      if (p2 != nullptr)
+        for (int t = q; t < t2; t += 4) s += p2[(zz * t2 + t) * ncol + n];
+    }
+  }
+  sh[q][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (q == 0 && n < ncol) out[(size_t)o * ncol + n] = ((sh[0][threadIdx.x] + sh[1][threadIdx.x]) + sh[2][threadIdx.x]) +
+                                                      sh[3][threadIdx.x];
 }
 
 // Per row (z, n), one wave: den = phi(z_q) . ks + eps; lin = num / den (in place).
@@ -409,6 +449,13 @@ __global__ void dg_scale_kernel(float* dg, const float* g, int H, int has_lm) {
 
 // ---------------------------------------------------------------- launches
 static unsigned blocks(size_t n, unsigned t) { return (unsigned)((n + t - 1) / t); }
+static int half_tiles(int rows) { return 2 * ((rows + 127) / 128); }
+static hipError_t launch_tile_colsum(const float* p1, int t1, const float* p2, int t2, int nb, int zs, int ncol,
+                                     int nout, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(tile_colsum_kernel, dim3((ncol + 63) / 64, nout), dim3(256), 0, s, p1, t1, p2, t2, nb, zs, ncol,
+                     out);
+  return hipGetLastError();
+}
 
 template <int MODE>
 static hipError_t launch_colsum(const float* src, const float* src2, const float* wv, long long sz, int rb,
@@ -458,6 +505,11 @@ BackwardLayout backward_layout(const Problem& p) {
   l.dden = take(Z * NQ);
   l.rpart = take(Z * NQ);
   l.colpart = take(Z * kColSplit * F);
+  // half-tile column partials of the GEMM epilogues: ksum then db (query rows), dks, db (key rows)
+  const size_t cs = Z * (size_t)half_tiles((int)(N > NQ ? N : NQ)) * F;
+  l.cs1 = take(cs);
+  l.cs2 = take(cs);
+  l.cs3 = take(cs);
   l.splitk = take(splitk_elems(p));
   l.bytes = o;
   return l;
@@ -471,7 +523,8 @@ BackwardLayout backward_layout(const Problem& p) {
 
 // Workspace views of the backward's fp32 intermediates.
 struct BwBufs {
-  float *zq, *zk, *dzq, *dzk, *lin, *lm, *dnum, *kv, *dkv, *ks, *dks, *den, *dden, *rpart, *colpart, *splitk;
+  float *zq, *zk, *dzq, *dzk, *lin, *lm, *dnum, *kv, *dkv, *ks, *dks, *den, *dden, *rpart, *colpart, *cs1, *cs2, *cs3,
+      *splitk;
   size_t splitk_n;
 };
 static BwBufs bw_bufs(const Problem& p, void* ws) {
@@ -480,7 +533,8 @@ static BwBufs bw_bufs(const Problem& p, void* ws) {
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w8 + off); };
   return BwBufs{F32(l.zq),  F32(l.zk),  F32(l.dzq),  F32(l.dzk),   F32(l.lin),     F32(l.lm),
                 F32(l.dnum), F32(l.kv),  F32(l.dkv),  F32(l.ks),    F32(l.dks),     F32(l.den),
-                F32(l.dden), F32(l.rpart), F32(l.colpart), F32(l.splitk), splitk_elems(p)};
+                F32(l.dden), F32(l.rpart), F32(l.colpart), F32(l.cs1), F32(l.cs2), F32(l.cs3),
+                F32(l.splitk), splitk_elems(p)};
 }
 
 // Forward pass with the intermediates the gradients need: z_q, z_k (biased),
@@ -493,7 +547,7 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
   const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
   const long long QF = (long long)NQ * F, QD = (long long)NQ * D;
   // z_q = Q W + b, z_k = K W + b: per (b, h), [rows x D] . [D x F], the bias in the epilogue
-  auto proj = [&](const void* X, float* Zout, int rows) {
+  auto proj = [&](const void* X, float* Zout, int rows, float* phi_part) {
     const long long RD = (long long)rows * D, RF = (long long)rows * F;
     BgemmArgs a{};
     a.A = X;
@@ -520,17 +574,18 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
       ab.sCz = RF;
       ab.bias_n = bias;  // z = h within one batch row
       ab.sbz = F;
+      if (phi_part) ab.cs_phi = phi_part + (size_t)b * H * half_tiles(rows) * F;  // sum of phi(z) per half tile
       TTR_HIP(launch_bgemm(dt, true, true, false, ab, H, s));
     }
     return hipSuccess;
   };
-  TTR_HIP(proj(Q, zq, NQ));
+  TTR_HIP(proj(Q, zq, NQ, nullptr));
   tm->mark();
-  TTR_HIP(proj(K, zk, N));
+  TTR_HIP(proj(K, zk, N, t.cs1));
   tm->mark();
 
-  // ks = sum_n phi(z_k); KV = phi(z_k)^T V
-  TTR_HIP(launch_colsum<0>(zk, nullptr, nullptr, NF, N, 0, N, Z, F, t.colpart, ks, s));
+  // ks = sum_n phi(z_k) from the z_k products' half-tile sums; KV = phi(z_k)^T V
+  TTR_HIP(launch_tile_colsum(t.cs1, half_tiles(N), nullptr, 0, 1, 0, F, Z, ks, s));
   tm->mark();
   {
     BgemmArgs a{};
@@ -620,6 +675,8 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.dz_s = ks;
     a.dz_srz = NQ;
     a.dz_ssz = F;
+    a.cs_val = t.cs1;   // db, query rows
+    a.cs_phir = t.cs2;  // dks = sum_n phi(z_q) dden
     a.M = NQ;
     a.N = F;
     a.K = D;
@@ -658,7 +715,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s, t.splitk, t.splitk_n));
     tm->mark();
   }
-  TTR_HIP(launch_colsum<1>(zq, nullptr, dden, QF, NQ, 0, NQ, Z, F, t.colpart, dks, s));
+  TTR_HIP(launch_tile_colsum(t.cs2, half_tiles(NQ), nullptr, 0, 1, 0, F, Z, dks, s));
   tm->mark();
   // dz_k = (V dKV^T + 1 dks^T) phi'(z_k): [N x D] . [D x F], the rest in the epilogue
   {
@@ -669,6 +726,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.dz_x = zk;
     a.dz_s = dks;
     a.dz_ssz = F;
+    a.cs_val = t.cs3;  // db, key rows
     a.M = N;
     a.N = F;
     a.K = D;
@@ -715,14 +773,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
   TTR_HIP(dw(K, dzk, N, 1));
   tm->mark();
   // db[h] over rows (b, n) of slice h; dg[h] from the row shares of dalpha
-  if (NQ == N) {
-    TTR_HIP(launch_colsum<2>(dzq, dzk, nullptr, NF, N, (long long)H * NF, B * N, H, F, t.colpart, db, s));
-  } else {  // query and key rows differ in number: two sums (dks, no longer needed, holds the second)
-    TTR_HIP(launch_colsum<3>(dzq, nullptr, nullptr, QF, NQ, (long long)H * QF, B * NQ, H, F, t.colpart, db, s));
-    TTR_HIP(launch_colsum<3>(dzk, nullptr, nullptr, NF, N, (long long)H * NF, B * N, H, F, t.colpart, dks, s));
-    hipLaunchKernelGGL(add_into_kernel, dim3(blocks((size_t)H * F, 256)), dim3(256), 0, s, db, dks, H * F);
-    TTR_HIP(hipGetLastError());
-  }
+  TTR_HIP(launch_tile_colsum(t.cs1, half_tiles(NQ), t.cs3, half_tiles(N), B, H, F, H, db, s));
   TTR_HIP(launch_colsum<3>(rpart, nullptr, nullptr, NQ, NQ, (long long)H * NQ, B * NQ, H, 1, t.colpart, dg, s));
   hipLaunchKernelGGL(dg_scale_kernel, dim3(blocks(H, 64)), dim3(64), 0, s, dg, g, H, L > 0 ? 1 : 0);
   TTR_HIP(hipGetLastError());
