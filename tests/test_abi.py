@@ -179,6 +179,30 @@ def test_staged_validation(lib):
     assert lib.ttr_kv_reduce(D(N=4096), big, 2 * big, 3 * big, None, 4 * big, 5 * big, None, 0, None) == WS
 
 
+def test_distillation_validation(lib):
+    # host-side checks of the distillation steps (no launch: every call fails before enqueueing)
+    big = 1 << 40
+    d = D(B=1, H=2, N=256, Dm=64, F=256, dt=0)
+    P9 = [big * (i + 1) for i in range(9)]
+    Q, K, V, T, W, b, g, s_, m = P9
+    loss, ws = 10 * big, 11 * big
+
+    def rows(nq, step=1, lr=1e-3, L=16, wsb=1 << 40, teacher=T):
+        return lib.ttr_distill_step_rows(d, nq, Q, K, V, teacher, W, b, g, s_, m, step, lr, 1e-6, L, loss, ws, wsb,
+                                         None)
+
+    assert rows(0) == SHAPE and rows(257) == SHAPE         # 1 <= Nq <= N
+    assert rows(64, step=0) == SHAPE and rows(64, lr=0.0) == SHAPE
+    assert rows(64, L=257) == SHAPE
+    assert rows(64, wsb=16) == WS
+    assert lib.ttr_distill_rows_workspace_bytes(d, 0, 16, 0) == 0
+    assert lib.ttr_distill_rows_workspace_bytes(d, 257, 16, 0) == 0
+    full = lib.ttr_distill_rows_workspace_bytes(d, 256, 16, 1)
+    assert full == lib.ttr_distill_workspace_bytes(d, 16, 1) > 0
+    assert 0 < lib.ttr_distill_rows_workspace_bytes(d, 64, 16, 1) < full
+    assert lib.ttr_distill_step(d, Q, K, V, T, W, b, g, s_, m, 1, 1e-3, 1e-6, 16, loss, ws, 16, None) == WS
+
+
 def test_workspace_bytes(lib):
     assert lib.ttr_workspace_bytes(D(Dm=96), 0, 0, 0) == 0
     assert lib.ttr_workspace_bytes(D(), 300, 0, 0) == 0
