@@ -175,11 +175,11 @@ def kernel_plan(w):
         state = 2 * D * D + D  # P += phi(k)^T v, z += phi(k) per token
         plan = []
         if nseg > 1:
-            plan.append((f"causal2_kernel<{chunk}, false>", BH * seg_tokens * state, 2 * BH * seg_tokens * D * io))
+            plan.append((f"causal2_kernel<{chunk}, false, 0>", BH * seg_tokens * state, 2 * BH * seg_tokens * D * io))
         # per token: its share of the causal score and value tiles (C/2 keys on
         # average, plus the diagonal), the inter-chunk product and the state update
         walk = BH * N * (2 * 2 * D * (chunk // 2 + 16) + 2 * D * D + state)
-        plan.append((f"causal2_kernel<{chunk}, true>", walk, 4 * tok))
+        plan.append((f"causal2_kernel<{chunk}, true, 0>", walk, 4 * tok))
         return plan
     proj = 2 * N * D * F  # X W_h
     kv = 2 * N * F * D + N * F  # phi(K)^T V and ksum
