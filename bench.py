@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--replay", action="store_true",
                     help="time the replay buffer's offload (push), fetch and a push overlapped with a distillation "
                          "step instead")
+    ap.add_argument("--staged", action="store_true",
+                    help="time each staged entry point (feature map, key/value reduction, apply, landmark branch, "
+                         "blend) with its own roofline instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
@@ -678,6 +681,85 @@ def main_cosine(args):
     print(json.dumps(res), flush=True)
 
 
+def main_staged(args):
+    """The staged entry points on the workload, one call each: ttr_feature_map (of Q), ttr_kv_reduce,
+    ttr_apply, ttr_landmark_attn and ttr_blend, each timed by HIP events around the call while a spin
+    kernel keeps the GPU behind the host (so the events see the kernels, not the launch latency), each
+    with the roofline of its algorithmic flops and bytes (its fp32 intermediates are part of its
+    interface: they are counted)."""
+    import numpy as np
+    import torch
+    import linear_hybrid_attention_amd as ttr
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    if w.causal or not w.proj or w.L == 0:
+        print("--staged needs a non-causal workload with a projection and landmarks", file=sys.stderr)
+        sys.exit(2)
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def io(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x[name]).to(dev)
+
+    Q, K, V, W = io("Q"), io("K"), io("V"), io("W")
+    b, g = torch.from_numpy(x["b"]).to(dev), torch.from_numpy(x["g"]).to(dev)
+    eps = float(x["eps"])
+    iot = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    KV, ksum = ttr.kv_reduce(K, V, W, b)
+    out_lin = ttr.apply(Q, W, b, KV, ksum, eps)
+    out_lm = ttr.landmark_attn(Q, K, V, w.L)
+    Z, N, D, F, L = w.B * w.H, w.N, w.D, w.F, w.L
+    ib = 2 if w.dtype == "bf16" else 4
+    stages = [
+        ("ttr_feature_map (phi of Q)", lambda: ttr.feature_map(Q, W, b), 2 * Z * N * D * F, Z * N * (D + F) * ib),
+        ("ttr_kv_reduce", lambda: ttr.kv_reduce(K, V, W, b), 4 * Z * N * D * F,
+         2 * Z * N * D * ib + Z * F * (D + 1) * 4),
+        ("ttr_apply", lambda: ttr.apply(Q, W, b, KV, ksum, eps), 4 * Z * N * D * F,
+         Z * N * D * (ib + 4) + Z * F * (D + 1) * 4),
+        ("ttr_landmark_attn", lambda: ttr.landmark_attn(Q, K, V, L), 4 * Z * N * L * D,
+         Z * N * D * (ib + 4) + 2 * Z * L * D * ib),
+        ("ttr_blend", lambda: ttr.blend(out_lin, out_lm, g, iot), 0, Z * N * D * (8 + ib)),
+    ]
+    stream = torch.cuda.current_stream(dev)
+    res_st = {}
+    for name, fn, fl, nb in stages:
+        for _ in range(max(3, args.warmup // 4)):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda._sleep(50_000_000)  # the GPU spins while the host enqueues every timed call
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+        r = roofline(w, fl, nb, ms)
+        res_st[name] = {"ms": ms, "flops": fl, "bytes": nb, "bound": r["bound"], "achieved": r["achieved"],
+                        "peak": r["peak"], "unit": r["unit"], "frac": r["frac"]}
+    total = sum(v["ms"] for v in res_st.values())
+    top = max(res_st, key=lambda k: res_st[k]["ms"])
+    t = res_st[top]
+    res = {"metric": f"staged TTR hybrid attention tokens/sec ({w.name}: B={w.B}, H={w.H}, N={w.N}, L={w.L}; five "
+                     "entry points with fp32 intermediates)",
+           "value": w.B * w.N / (total * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": total, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+           "config": {"workload": w.name, "mode": "staged", "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F,
+                      "L": w.L},
+           "roofline": {"kernel": top, "bound": t["bound"], "achieved": t["achieved"],
+                        "peak": t["peak"],
+                        "unit": t["unit"], "frac": t["frac"], "traffic": None,
+                        "algorithmic_flops_per_launch": t["flops"], "algorithmic_bytes_per_launch": t["bytes"],
+                        "avg_launch_ms": t["ms"]},
+           "stages": res_st, "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+
+
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
 
 
@@ -838,6 +920,9 @@ def main():
         return
     if args.replay:
         main_replay(args)
+        return
+    if args.staged:
+        main_staged(args)
         return
     if args.cosine:
         main_cosine(args)
