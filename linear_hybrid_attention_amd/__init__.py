@@ -263,8 +263,7 @@ def kv_reduce(K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor] = None
     d = _dims(K, F, fmap)
     KV = torch.empty((d.B, d.H, F, d.D), dtype=torch.float32, device=K.device)
     ksum = torch.empty((d.B, d.H, F), dtype=torch.float32, device=K.device)
-    need = lib.ttr_workspace_bytes(d, 0, 0, 0) - KV.numel() * 4 - ksum.numel() * 4
-    ws, wsb = _workspace(d, max(0, need), K, ws)
+    ws, wsb = _workspace(d, lib.ttr_workspace_bytes(d, 0, 0, 0), K, ws)  # the documented bound
     st = lib.ttr_kv_reduce(d, _dev(K, "K"), _dev(V, "V", K.dtype), _dev(W, "W", K.dtype),
                            _dev(b, "b", torch.float32), KV.data_ptr(), ksum.data_ptr(),
                            None if ws is None else ws.data_ptr(), wsb, _stream(K))

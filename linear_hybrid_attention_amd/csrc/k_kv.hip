@@ -326,4 +326,12 @@ hipError_t launch_kv_reduce(const Problem& p, const void* K, const void* V, cons
   return hipGetLastError();
 }
 
+hipError_t launch_kv_finalize(const Problem& p, const float* part, int nsplit, float* KV, float* ksum,
+                              hipStream_t s) {
+  const int FD = p.F * p.D;
+  const int blocks = (FD + p.F + 1023) / 1024;
+  hipLaunchKernelGGL(kv_finalize_kernel, dim3(blocks, p.B * p.H), dim3(256), 0, s, part, nsplit, FD, p.F, KV, ksum);
+  return hipGetLastError();
+}
+
 }  // namespace ttr

@@ -493,4 +493,52 @@ hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void
   return hipErrorInvalidValue;
 }
 
+// The key/value reduction on its own (ttr_kv_reduce, bf16 IO): the partial
+// kernel into the workspace, then the fixed-order sum of the split partials into
+// fp32 KV [F][D] and ksum [F] (the partials' own layout). Workspace: the
+// partials, then room for the W^T chunks the partial kernel also writes.
+size_t kv2_reduce_workspace_bytes(const Problem& p) {
+  int ns, ch;
+  kv2_plan(p, &ns, &ch);
+  return (size_t)p.B * p.H * ns * (size_t)(p.F * p.D + p.F) * 4 + (size_t)p.H * p.F * p.D * 2;
+}
+
+template <int D, int F, bool PROJ, int MAP>
+static void launch_kv2_partial_t(const Problem& p, const Kv2Args& ka, hipStream_t s) {
+  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit, p.B * p.H), dim3(512), 0, s, ka);
+}
+
+hipError_t launch_kv2_reduce(const Problem& p, const void* K, const void* V, const void* W, const float* bias,
+                             float* KV, float* ksum, void* ws, hipStream_t s) {
+  if (p.dtype != 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
+  int nsplit, chunk;
+  kv2_plan(p, &nsplit, &chunk);
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  Kv2Args ka;
+  ka.K = static_cast<const uint16_t*>(K);
+  ka.V = static_cast<const uint16_t*>(V);
+  ka.W = static_cast<const uint16_t*>(W);
+  ka.bias = bias;
+  ka.H = p.H;
+  ka.N = p.N;
+  ka.chunk = chunk;
+  ka.nsplit = nsplit;
+  ka.part = reinterpret_cast<float*>(w8);
+  ka.pack_w = w8 + (size_t)p.B * p.H * nsplit * (size_t)(p.F * p.D + p.F) * 4;
+  if (p.D == 128) {
+    if (p.proj) launch_kv2_partial_t<128, 256, true, kElu1>(p, ka, s);
+    else if (p.fmap == kRelu) launch_kv2_partial_t<128, 128, false, kRelu>(p, ka, s);
+    else if (p.fmap == kSoftmax) launch_kv2_partial_t<128, 128, false, kSoftmax>(p, ka, s);
+    else launch_kv2_partial_t<128, 128, false, kElu1>(p, ka, s);
+  } else {
+    if (p.proj) launch_kv2_partial_t<64, 256, true, kElu1>(p, ka, s);
+    else if (p.fmap == kRelu) launch_kv2_partial_t<64, 64, false, kRelu>(p, ka, s);
+    else if (p.fmap == kSoftmax) launch_kv2_partial_t<64, 64, false, kSoftmax>(p, ka, s);
+    else launch_kv2_partial_t<64, 64, false, kElu1>(p, ka, s);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_kv_finalize(p, ka.part, nsplit, KV, ksum, s);
+}
+
 }  // namespace ttr

@@ -61,6 +61,9 @@ int kv_nsplit(const Problem& p);
 size_t kv_workspace_bytes(const Problem& p);
 hipError_t launch_kv_reduce(const Problem& p, const void* K, const void* V, const void* W,
                             const float* bias, float* KV, float* ksum, void* ws, hipStream_t s);
+// Fixed-order sum of split partials [B*H][nsplit][F*D + F] into KV and ksum.
+hipError_t launch_kv_finalize(const Problem& p, const float* part, int nsplit, float* KV, float* ksum,
+                              hipStream_t s);
 
 // k_kv2.hip + k_fused.hip: the bf16 hot path. launch_kv2 runs the split-N
 // key/value reduction and writes the per-head operand pack into ws; then
@@ -75,6 +78,11 @@ hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void
                       void* ws, FusedPack* pk, hipStream_t s, StageTimer* t);
 hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& pk, const float* g, float eps,
                               int L, void* out, hipStream_t s);
+// The key/value reduction alone on the bf16 path (ttr_kv_reduce): the partial
+// kernel of the fused path, then the fixed-order sum into fp32 KV and ksum.
+size_t kv2_reduce_workspace_bytes(const Problem& p);
+hipError_t launch_kv2_reduce(const Problem& p, const void* K, const void* V, const void* W, const float* bias,
+                             float* KV, float* ksum, void* ws, hipStream_t s);
 
 // k_blend.hip
 hipError_t launch_blend(const Problem& p, const float* lin, const float* lm, const float* g, void* out,

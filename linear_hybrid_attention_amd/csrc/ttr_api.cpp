@@ -149,7 +149,9 @@ ttr_status ttr_kv_reduce(ttr_dims d, const void* K, const void* V, const void* W
   TTR_TRY(check_opt_ptr(W));
   TTR_TRY(check_opt_ptr(b));
   const Problem p = make_problem(d, proj);
-  const size_t need = kv_workspace_bytes(p);
+  // bf16: the fused path's partial kernel, then a fixed-order sum; fp32: the generic kernels
+  const bool fast = d.dtype == TTR_BF16;
+  const size_t need = fast ? kv2_reduce_workspace_bytes(p) : kv_workspace_bytes(p);
   if (need > 0) {
     if (ws == nullptr || ws_bytes < need) return TTR_ERR_WORKSPACE;
     TTR_TRY(check_ptr(ws));
@@ -157,6 +159,7 @@ ttr_status ttr_kv_reduce(ttr_dims d, const void* K, const void* V, const void* W
   const Range outs[] = {{KV, kv_bytes(d)}, {ksum, ks_bytes(d)}, {ws, need}};
   const Range ins[] = {{K, qkv_bytes(d)}, {V, qkv_bytes(d)}, {W, proj ? w_bytes(d) : 0}, {b, b ? b_bytes(d) : 0}};
   TTR_TRY(check_no_alias(outs, 3, ins, 4));
+  if (fast) return hip_status(launch_kv2_reduce(p, K, V, W, b, KV, ksum, ws, (hipStream_t)stream));
   return hip_status(launch_kv_reduce(p, K, V, W, b, KV, ksum, ws, (hipStream_t)stream));
 }
 
