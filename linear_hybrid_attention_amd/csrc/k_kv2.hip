@@ -80,6 +80,15 @@ struct Kv2Shape {
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
+// Work item of workgroup i in a one-dimensional grid of n: the hardware places
+// workgroup i on XCD i % 8, so items are renumbered such that consecutive ones
+// (the splits or jobs of one (batch, head)) run on one XCD and share its L2
+// copy of that head's W and partials.
+__device__ __forceinline__ int xcd_item(int i, int n) {
+  const int per = n / 8;
+  return i < per * 8 ? (i % 8) * per + i / 8 : i;
+}
+
 template <int D, int F, bool PROJ, int MAP>
 __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
   using S = Kv2Shape<D, F>;
@@ -89,7 +98,8 @@ __global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
-  const int split = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int split = item % a.nsplit, bh = item / a.nsplit, h = bh % a.H;
   const int fs = w % NFS, tw = w / NFS, f0 = 32 * fs;
   const int N = a.N;
   const int t_begin = split * a.chunk;
@@ -299,7 +309,7 @@ struct PackArgs {
   unsigned char* pack_w;   // [H][w_bytes]
 };
 
-// Jobs of one (batch, head), by blockIdx.x:
+// Jobs of one (batch, head), by job index:
 //   [0, KVJ)            KV^T rows: FJ features x D (sum of partials), ksum, bias
 //   then one per 32-landmark chunk (K_L and V_L^T)
 // (The W^T chunks are written by the partial kernel, which holds W in registers.)
@@ -308,15 +318,16 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
   constexpr int FJ = 2048 / D > F ? F : 2048 / D;  // features per KV job: (FJ/2)*(D/4) = 256 threads
   constexpr int KVJ = F / FJ;
   const int tid = threadIdx.x;
-  const int bh = blockIdx.y, h = bh % a.H;
   const int nlb = (a.L + 31) / 32;
+  const int item = xcd_item(blockIdx.x, gridDim.x), njobs = KVJ + nlb;
+  const int bh = item / njobs, h = bh % a.H;
   PackLayout pl{D, F, a.L, nlb};
   unsigned char* base = a.pack_bh + (size_t)bh * pl.bh_bytes();
   float* biasP = reinterpret_cast<float*>(base);
   float* ksumP = biasP + F;
   uint16_t* kvc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes());
   uint16_t* lmc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes() + pl.kv_bytes());
-  const int job = blockIdx.x;
+  const int job = item % njobs;
 
   if (job < KVJ) {
     // FJ features f0.. x D values: thread -> (feature pair, 4 consecutive d).
@@ -428,13 +439,13 @@ size_t fused_workspace_bytes(const Problem& p, int L) {
 template <int D, int F, bool PROJ, int MAP>
 static hipError_t launch_kv2_t(const Problem& p, const Kv2Args& ka, const PackArgs& pa, hipStream_t s,
                                StageTimer* t) {
-  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit, p.B * p.H), dim3(512), 0, s, ka);
+  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit * p.B * p.H), dim3(512), 0, s, ka);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   t->mark();
   constexpr int FJ = 2048 / D > F ? F : 2048 / D;
   const int jobs = F / FJ + (pa.L + 31) / 32;
-  hipLaunchKernelGGL((kv2_pack_kernel<D, F, PROJ>), dim3(jobs, p.B * p.H), dim3(256), 0, s, pa);
+  hipLaunchKernelGGL((kv2_pack_kernel<D, F, PROJ>), dim3(jobs * p.B * p.H), dim3(256), 0, s, pa);
   e = hipGetLastError();
   t->mark();
   return e;
@@ -505,7 +516,7 @@ size_t kv2_reduce_workspace_bytes(const Problem& p) {
 
 template <int D, int F, bool PROJ, int MAP>
 static void launch_kv2_partial_t(const Problem& p, const Kv2Args& ka, hipStream_t s) {
-  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit, p.B * p.H), dim3(512), 0, s, ka);
+  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit * p.B * p.H), dim3(512), 0, s, ka);
 }
 
 hipError_t launch_kv2_reduce(const Problem& p, const void* K, const void* V, const void* W, const float* bias,
