@@ -428,9 +428,12 @@ def distill_plan(w, nq=None):
         teacher = ("teacher softmax attention (kv2 + fused query kernel, every token a landmark, alpha 0)"
                    if w.dtype == "bf16" else "teacher softmax attention (hybrid_kernel, L = N)")
         plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
-    plan += [("bgemm z_q = Q W + b", gq, 0), ("bgemm z_k = K W + b", gk, 0),
-             ("ksum (tile sums of the z_k epilogue)", 0, 0), ("bgemm KV = phi_k^T V", gk, 0), ("bgemm num = phi_q KV", gq, 0),
-             ("den_lin_kernel", 2 * Z * NQ * F, 0)]
+    plan += [("bgemm z_q = Q W + b", gq, 0), ("bgemm z_k = K W + b", gk, 0)]
+    if w.dtype == "bf16":  # KV and ksum from K and V by the key/value kernel
+        plan.append(("KV, ksum = phi(K W + b)^T V, colsum (kv2_partial_kernel + kv_finalize_kernel)", gk, 0))
+    else:
+        plan += [("ksum (tile sums of the z_k epilogue)", 0, 0), ("bgemm KV = phi_k^T V", gk, 0)]
+    plan += [("bgemm num = phi_q KV", gq, 0), ("den_lin_kernel", 2 * Z * NQ * F, 0)]
     if L > 0:
         plan.append(("landmark branch (hybrid_kernel)", 4 * Z * NQ * L * D, 0))
     plan += [("distill_loss_rows_kernel", 0, 0), ("distill_loss_total_kernel", 0, 0), ("dlin_kernel", 0, 0),

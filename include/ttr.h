@@ -372,7 +372,8 @@ int ttr_last_hip_error(void);
  *   layer: the weight transposes, Q/K/V projection, the attention's stages
  *     as above, out projection;
  *   backward: Q projection, K projection (one stage each, whatever the batch),
- *     ksum, KV, num, normaliser, landmark branch (L > 0), then dnum/dden,
+ *     KV and ksum (bf16: one stage, from K and V; fp32: ksum, then KV), num,
+ *     normaliser, landmark branch (L > 0), then dnum/dden,
  *     dz_q (its product with the phi' factor in the epilogue), dKV, dks, dz_k
  *     (likewise), dW from Q, dW from K, db/dg;
  *   distillation step: W to bf16 (bf16 IO), teacher (when computed), the

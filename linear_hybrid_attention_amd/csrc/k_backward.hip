@@ -35,7 +35,7 @@ struct BgemmArgs {
   int beta;
   const float* bias_n;  // optional: C(m, n) += bias_n[z * sbz + n]
   long long sbz;
-  int ksplit;           // > 1: blockIdx.z = z * ksplit + split; partial sums go to part
+  int ksplit;           // > 1: item z * ksplit + split per tile; partial sums go to part
   float* part;          // [Z][ksplit][M][N]
   // optional dz epilogue (no split-K): C(m, n) = (acc + r(m) s(n)) phi'(x(m, n)), phi = elu + 1,
   // x = dz_x laid out like C, r = dz_r[z * dz_srz + m] (1 when NULL), s = dz_s[z * dz_ssz + n]
@@ -52,7 +52,8 @@ struct BgemmArgs {
 };
 
 template <typename CT> struct BgTile {
-  static constexpr int TM = 128;                          // rows of each operand tile (m or n)
+  static constexpr int TM = 128;                          // output rows per workgroup (operand A tile rows)
+  static constexpr int TN = 64;                           // output columns per workgroup (operand B tile rows)
   static constexpr int KT = 32;                           // K per step
   static constexpr int LD = KT + 16 / (int)sizeof(CT);    // padded row (16-byte multiple)
 };
@@ -65,47 +66,58 @@ template <typename CT> __device__ __forceinline__ CT to_ct(float x);
 template <> __device__ __forceinline__ float to_ct<float>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t to_ct<uint16_t>(float x) { return f2bf(x); }
 
-// 16 consecutive elements at p (16-byte aligned) as floats
-template <typename T> __device__ __forceinline__ void ld16(const T* p, float (&v)[16]);
-template <> __device__ __forceinline__ void ld16<float>(const float* p, float (&v)[16]) {
+// NE consecutive elements at p (16-byte aligned) as floats
+template <typename T, int NE> __device__ __forceinline__ void ld_run(const T* p, float (&v)[NE]) {
+  if constexpr (sizeof(T) == 4) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 x = reinterpret_cast<const f32x4*>(p)[q];
+    for (int q = 0; q < NE / 4; ++q) {
+      const f32x4 x = reinterpret_cast<const f32x4*>(p)[q];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[4 * q + j] = x[j];
-  }
-}
-template <> __device__ __forceinline__ void ld16<uint16_t>(const uint16_t* p, float (&v)[16]) {
+      for (int j = 0; j < 4; ++j) v[4 * q + j] = x[j];
+    }
+  } else {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const u32x4 x = reinterpret_cast<const u32x4*>(p)[q];
+    for (int q = 0; q < NE / 8; ++q) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(p)[q];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * q + 2 * j] = __uint_as_float(x[j] << 16);
-      v[8 * q + 2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = __uint_as_float(x[j] << 16);
+        v[8 * q + 2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+      }
     }
   }
 }
 
-// One operand tile [128 rows][KT] of one K-step into registers: 16 elements
-// per thread along the operand's contiguous dimension. k_contig: thread t
-// takes row t / 2, k (t % 2) * 16 .. + 15; else k t / 8 and rows
-// (t % 8) * 16 .. + 15. Whole runs inside the matrix and 16-byte aligned use
-// vector loads; others load element by element with bounds (zeros outside).
-// phi = elu + 1 applies to loaded elements only (outside stays 0).
-template <typename T, bool ELU>
-__device__ __forceinline__ void bg_load(float (&v)[16], const T* base, long long s_row, long long s_k, int row0,
+// Operand tile geometry: ROWS rows x KT k of one K-step, NE = ROWS / 8
+// elements per thread (256 threads) along the operand's contiguous dimension.
+// k_contig: thread t takes row t / TPR and k (t % TPR) NE .. + NE - 1 (TPR =
+// KT / NE threads per row); else k t / 8 and rows (t % 8) NE .. + NE - 1.
+// Whole runs inside the matrix and 16-byte aligned use vector loads; others
+// load element by element with bounds (zeros outside). phi = elu + 1 applies
+// to loaded elements only (outside stays 0).
+template <int ROWS> struct BgGeo {
+  static constexpr int NE = ROWS / 8, TPR = 32 / NE;
+  __device__ static int kc_row(int t) { return t / TPR; }
+  __device__ static int kc_k(int t) { return (t % TPR) * NE; }
+  __device__ static int nk_k(int t) { return t / 8; }
+  __device__ static int nk_row(int t) { return (t % 8) * NE; }
+};
+
+template <typename T, bool ELU, int ROWS>
+__device__ __forceinline__ void bg_load(float (&v)[ROWS / 8], const T* base, long long s_row, long long s_k, int row0,
                                         int nrows, int k0, int K, bool k_contig, bool vec, int tid) {
+  using G = BgGeo<ROWS>;
+  constexpr int NE = G::NE;
   if (k_contig) {
-    const int gr = row0 + tid / 2, gk = k0 + (tid % 2) * 16;
-    if (vec && gr < nrows && gk + 16 <= K) {
-      ld16<T>(base + (long long)gr * s_row + gk, v);  // s_k == 1 here
+    const int gr = row0 + G::kc_row(tid), gk = k0 + G::kc_k(tid);
+    if (vec && gr < nrows && gk + NE <= K) {
+      ld_run<T, NE>(base + (long long)gr * s_row + gk, v);  // s_k == 1 here
       if (ELU)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = elu1(v[i]);
+        for (int i = 0; i < NE; ++i) v[i] = elu1(v[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < NE; ++i) {
         float x = 0.f;
         if (gr < nrows && gk + i < K) {
           x = ld_elem<T>(base, (long long)gr * s_row + (long long)(gk + i) * s_k);
@@ -115,15 +127,15 @@ __device__ __forceinline__ void bg_load(float (&v)[16], const T* base, long long
       }
     }
   } else {
-    const int gk = k0 + tid / 8, gr = row0 + (tid % 8) * 16;
-    if (vec && gk < K && gr + 16 <= nrows) {
-      ld16<T>(base + (long long)gk * s_k + gr, v);  // s_row == 1 here
+    const int gk = k0 + G::nk_k(tid), gr = row0 + G::nk_row(tid);
+    if (vec && gk < K && gr + NE <= nrows) {
+      ld_run<T, NE>(base + (long long)gk * s_k + gr, v);  // s_row == 1 here
       if (ELU)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = elu1(v[i]);
+        for (int i = 0; i < NE; ++i) v[i] = elu1(v[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < NE; ++i) {
         float x = 0.f;
         if (gr + i < nrows && gk < K) {
           x = ld_elem<T>(base, (long long)(gr + i) * s_row + (long long)gk * s_k);
@@ -134,30 +146,120 @@ __device__ __forceinline__ void bg_load(float (&v)[16], const T* base, long long
     }
   }
 }
-template <typename CT>
-__device__ __forceinline__ void bg_store(CT* tile, const float (&v)[16], bool k_contig, int tid) {
-  constexpr int LD = BgTile<CT>::LD;
+template <typename CT, int ROWS>
+__device__ __forceinline__ void bg_store(CT* tile, const float (&v)[ROWS / 8], bool k_contig, int tid) {
+  using G = BgGeo<ROWS>;
+  constexpr int LD = BgTile<CT>::LD, NE = G::NE;
   if (k_contig) {
-    CT* p = tile + (tid / 2) * LD + (tid % 2) * 16;
+    CT* p = tile + G::kc_row(tid) * LD + G::kc_k(tid);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = to_ct<CT>(v[i]);
+    for (int i = 0; i < NE; ++i) p[i] = to_ct<CT>(v[i]);
   } else {
-    CT* p = tile + ((tid % 8) * 16) * LD + tid / 8;
+    CT* p = tile + G::nk_row(tid) * LD + G::nk_k(tid);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i * LD] = to_ct<CT>(v[i]);
+    for (int i = 0; i < NE; ++i) p[i * LD] = to_ct<CT>(v[i]);
   }
 }
 
-// 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (2 x 2 MFMA tiles).
-template <typename CT, typename TA, typename TB, bool A_ELU>
-__global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
-  constexpr int TM = BgTile<CT>::TM, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
+// The same tile move for a 16-bit operand going to a 16-bit tile unchanged:
+// the elements stay packed (NE / 2 registers) and are stored as they came.
+template <int ROWS>
+__device__ __forceinline__ void bg_load_raw(u32x4 (&v)[ROWS / 64], const uint16_t* base, long long s_row,
+                                            long long s_k, int row0, int nrows, int k0, int K, bool k_contig,
+                                            bool vec, int tid) {
+  using G = BgGeo<ROWS>;
+  constexpr int NE = G::NE;
+  uint16_t e[NE];
+  if (k_contig) {
+    const int gr = row0 + G::kc_row(tid), gk = k0 + G::kc_k(tid);
+    if (vec && gr < nrows && gk + NE <= K) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(base + (long long)gr * s_row + gk);
+#pragma unroll
+      for (int u = 0; u < NE / 8; ++u) v[u] = q[u];
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      e[i] = (gr < nrows && gk + i < K) ? base[(long long)gr * s_row + (long long)(gk + i) * s_k] : (uint16_t)0;
+  } else {
+    const int gk = k0 + G::nk_k(tid), gr = row0 + G::nk_row(tid);
+    if (vec && gk < K && gr + NE <= nrows) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(base + (long long)gk * s_k + gr);
+#pragma unroll
+      for (int u = 0; u < NE / 8; ++u) v[u] = q[u];
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      e[i] = (gr + i < nrows && gk < K) ? base[(long long)(gr + i) * s_row + (long long)gk * s_k] : (uint16_t)0;
+  }
+#pragma unroll
+  for (int u = 0; u < NE / 8; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[u][j] = (uint32_t)e[8 * u + 2 * j] | ((uint32_t)e[8 * u + 2 * j + 1] << 16);
+}
+template <int ROWS>
+__device__ __forceinline__ void bg_store_raw(uint16_t* tile, const u32x4 (&v)[ROWS / 64], bool k_contig, int tid) {
+  using G = BgGeo<ROWS>;
+  constexpr int LD = BgTile<uint16_t>::LD, NE = G::NE;
+  if (k_contig) {
+    u32x4* p = reinterpret_cast<u32x4*>(tile + G::kc_row(tid) * LD + G::kc_k(tid));
+#pragma unroll
+    for (int u = 0; u < NE / 8; ++u) p[u] = v[u];
+  } else {
+    uint16_t* p = tile + G::nk_row(tid) * LD + G::nk_k(tid);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) p[i * LD] = (uint16_t)(v[i >> 3][(i & 7) >> 1] >> (16 * (i & 1)));
+  }
+}
+
+// One operand's staging registers for a K-step: packed 16-bit elements when
+// they go to the tile unchanged, else floats (converted or mapped on the way).
+template <typename CT, typename T, bool ELU, int ROWS>
+struct BgStage {
+  float v[ROWS / 8];
+  __device__ __forceinline__ void load(const T* base, long long s_row, long long s_k, int row0, int nrows, int k0,
+                                       int K, bool kc, bool vec, int tid) {
+    bg_load<T, ELU, ROWS>(v, base, s_row, s_k, row0, nrows, k0, K, kc, vec, tid);
+  }
+  __device__ __forceinline__ void store(CT* tile, bool kc, int tid) const { bg_store<CT, ROWS>(tile, v, kc, tid); }
+};
+template <int ROWS>
+struct BgStage<uint16_t, uint16_t, false, ROWS> {
+  u32x4 v[ROWS / 64];
+  __device__ __forceinline__ void load(const uint16_t* base, long long s_row, long long s_k, int row0, int nrows,
+                                       int k0, int K, bool kc, bool vec, int tid) {
+    bg_load_raw<ROWS>(v, base, s_row, s_k, row0, nrows, k0, K, kc, vec, tid);
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, bool kc, int tid) const {
+    bg_store_raw<ROWS>(tile, v, kc, tid);
+  }
+};
+
+// Work item of workgroup i in a one-dimensional grid of n: the hardware places
+// workgroup i on XCD i % 8, so items are renumbered such that consecutive ones
+// run on one XCD (the N tiles of one M tile share that XCD's L2 copy of A).
+__device__ __forceinline__ int bg_item(int i, int n) {
+  const int per = n / 8;
+  return i < per * 8 ? (i % 8) * per + i / 8 : i;
+}
+
+// 128 x 64 output tile per workgroup, 4 waves of 32 x 64 (1 x 2 MFMA tiles):
+// a small accumulator, so that four workgroups share a compute unit and their
+// memory phases overlap. Workgroup items run N tile fastest, then M tile, then
+// z * ksplit + split. EPI: the dz or column-sum epilogue is compiled in (never
+// with split-K).
+template <typename CT, typename TA, typename TB, bool A_ELU, bool EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void bgemm_kernel(BgemmArgs a) {
+  constexpr int TM = BgTile<CT>::TM, TN = BgTile<CT>::TN, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
   __shared__ __attribute__((aligned(16))) CT As[TM * LD];
-  __shared__ __attribute__((aligned(16))) CT Bs[TM * LD];  // B^T: [128 n][KT]
+  __shared__ __attribute__((aligned(16))) CT Bs[TN * LD];  // B^T: [64 n][KT]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
-  const int wm = w & 1, wn = w >> 1;
-  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TM, z = blockIdx.z / a.ksplit, split = blockIdx.z % a.ksplit;
+  const int mtiles = (a.M + TM - 1) / TM, ntiles = (a.N + TN - 1) / TN;
+  const int item = bg_item(blockIdx.x, gridDim.x), rest = item / ntiles;
+  const int ntile = item % ntiles, mtile = rest % mtiles, zs = rest / mtiles;
+  const int m0 = mtile * TM, n0 = ntile * TN, z = zs / a.ksplit, split = zs % a.ksplit;
   const TA* A = static_cast<const TA*>(a.A) + z * a.sAz;
   const TB* B = static_cast<const TB*>(a.B) + z * a.sBz;
   const bool a_kc = a.sAk == 1, b_kc = a.sBk == 1;
@@ -169,62 +271,74 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
   const bool b_vec = (b_kc || a.sBn == 1) && ((b_kc ? a.sBn : a.sBk) % PB == 0) && (a.sBz % PB == 0) &&
                      (a.sBkb % PB == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
 
-  f32x16 acc[2][2];
+  f32x16 acc[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  float va[16], vb[16];
+  for (int j = 0; j < 2; ++j) acc[j] = f32x16{};
+  BgStage<CT, TA, A_ELU, TM> va;
+  BgStage<CT, TB, false, TN> vb;
   const int nks = (a.K + KT - 1) / KT, steps = a.KB * nks;
   const int per = (steps + a.ksplit - 1) / a.ksplit, s_begin = split * per, total = min(steps, s_begin + per);
   auto load = [&](int s) {
     const int kb = s / nks, k0 = (s % nks) * KT;
-    bg_load<TA, A_ELU>(va, A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a.K, a_kc, a_vec, tid);
-    bg_load<TB, false>(vb, B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, a.K, b_kc, b_vec, tid);
+    va.load(A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a.K, a_kc, a_vec, tid);
+    vb.load(B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, a.K, b_kc, b_vec, tid);
   };
   if (s_begin < total) load(s_begin);
   for (int s = s_begin; s < total; ++s) {
     __syncthreads();  // every wave is done with the previous tile
-    bg_store<CT>(As, va, a_kc, tid);
-    bg_store<CT>(Bs, vb, b_kc, tid);
+    va.store(As, a_kc, tid);
+    vb.store(Bs, b_kc, tid);
     __syncthreads();
     if (s + 1 < total) load(s + 1);  // in flight during the products
 #pragma unroll
     for (int kb = 0; kb < KT / 16; ++kb) {
-      Frag<CT> fa[2], fb[2];
+      const Frag<CT> fa = ld_frag<CT>(As + (w * 32 + c) * LD + kb * 16 + 8 * g);
+      Frag<CT> fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = ld_frag<CT>(As + (wm * 64 + i * 32 + c) * LD + kb * 16 + 8 * g);
+      for (int j = 0; j < 2; ++j) fb[j] = ld_frag<CT>(Bs + (j * 32 + c) * LD + kb * 16 + 8 * g);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = ld_frag<CT>(Bs + (wn * 64 + j * 32 + c) * LD + kb * 16 + 8 * g);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc[i][j], fa[i], fb[j]);
+      for (int j = 0; j < 2; ++j) mma(acc[j], fa, fb[j]);
     }
   }
-  // lane (c, g) holds, per tile (i, j), column n0 + wn*64 + j*32 + c and rows crow(lane, r)
-  const bool dz = a.ksplit == 1 && a.dz_s != nullptr;
-  const bool cs = a.ksplit == 1 && (a.cs_val || a.cs_phir || a.cs_phi);
-  const float* __restrict__ dzx = a.dz_x;
-  float* __restrict__ Cz = a.C + z * a.sCz;
+  // lane (c, g) holds, per tile j, column n0 + j*32 + c and rows m0 + w*32 + crow(lane, r)
+  const int mb = m0 + w * 32;
+  if (!EPI) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + c;
-    if (n >= a.N) continue;  // (lanes c and c + 32 share n: both skip or both go on)
-    const float bn = (a.ksplit == 1 && a.bias_n) ? a.bias_n[z * a.sbz + n] : 0.f;
-    const float sn = dz ? a.dz_s[z * a.dz_ssz + n] : 0.f;
-    float cv = 0.f, cp = 0.f, cq = 0.f;  // this lane's column sums over its rows of the half tile
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int mb = m0 + wm * 64 + i * 32;
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + j * 32 + c;
+      if (n >= a.N) continue;  // (lanes c and c + 32 share n: both skip or both go on)
       if (a.ksplit > 1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = mb + crow(lane, r);
-          if (m < a.M) a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[i][j][r];
+          if (m < a.M) a.part[((size_t)zs * a.M + m) * a.N + n] = acc[j][r];
         }
         continue;
       }
+      const float bn = a.bias_n ? a.bias_n[z * a.sbz + n] : 0.f;
+      float* __restrict__ Cz = a.C + z * a.sCz;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + crow(lane, r);
+        if (m >= a.M) continue;
+        float* p = Cz + (long long)m * a.sCm + (long long)n * a.sCn;
+        *p = (a.beta ? *p + acc[j][r] : acc[j][r]) + bn;
+      }
+    }
+    return;
+  }
+  // Epilogue with the dz products and column sums (no split-K).
+  const bool dz = a.dz_s != nullptr;
+  const float* __restrict__ dzx = a.dz_x;
+  float* __restrict__ Cz = a.C + z * a.sCz;
+  __shared__ float csw[3][4][64];  // per wave: its 32 rows' column sums
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + j * 32 + c;
+    float cv = 0.f, cp = 0.f, cq = 0.f;  // this lane's column sums over its rows
+    if (n < a.N) {  // (lanes c and c + 32 share n: both skip or both go on)
+      const float bn = a.bias_n ? a.bias_n[z * a.sbz + n] : 0.f;
+      const float sn = dz ? a.dz_s[z * a.dz_ssz + n] : 0.f;
       // the dz operands of the 16 rows are loaded before any store
       float xv[16], rv[16];
       if (dz) {
@@ -240,7 +354,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
         const int m = mb + crow(lane, r);
         if (m >= a.M) continue;
         float* p = Cz + (long long)m * a.sCm + (long long)n * a.sCn;
-        float v = (a.beta ? *p + acc[i][j][r] : acc[i][j][r]) + bn;
+        float v = (a.beta ? *p + acc[j][r] : acc[j][r]) + bn;
         if (dz) {  // dz = (dphi + r s) phi'(x), phi'(x) = 1 for x > 0, exp(x) otherwise
           const float dp = v + rv[r] * sn;
           v = xv[r] > 0.f ? dp : dp * __expf(xv[r]);
@@ -251,16 +365,25 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BgemmArgs a) {
         *p = v;
       }
     }
-    if (cs) {  // the column's two lanes (rows 4g..) combine; one partial per (z, half tile)
-      cv += __shfl_xor(cv, 32);
-      cp += __shfl_xor(cp, 32);
-      cq += __shfl_xor(cq, 32);
-      if (g == 0) {
-        const size_t at = ((size_t)z * (2 * gridDim.x) + 2 * blockIdx.x + wm) * a.N + n;
-        if (a.cs_val) a.cs_val[at] = cv;
-        if (a.cs_phir) a.cs_phir[at] = cp;
-        if (a.cs_phi) a.cs_phi[at] = cq;
-      }
+    // the column's two lanes (rows 4g..) combine; the wave's sums go to LDS
+    cv += __shfl_xor(cv, 32);
+    cp += __shfl_xor(cp, 32);
+    cq += __shfl_xor(cq, 32);
+    if (g == 0) {
+      csw[0][w][j * 32 + c] = cv;
+      csw[1][w][j * 32 + c] = cp;
+      csw[2][w][j * 32 + c] = cq;
+    }
+  }
+  __syncthreads();
+  // one partial per (z, 64-row half tile): waves 2h and 2h + 1, added in that order
+  if (tid < 128) {
+    const int h = tid >> 6, col = tid & 63, n = n0 + col;
+    if (n < a.N) {
+      const size_t at = ((size_t)z * (2 * mtiles) + 2 * mtile + h) * a.N + n;
+      if (a.cs_val) a.cs_val[at] = csw[0][2 * h][col] + csw[0][2 * h + 1][col];
+      if (a.cs_phir) a.cs_phir[at] = csw[1][2 * h][col] + csw[1][2 * h + 1][col];
+      if (a.cs_phi) a.cs_phi[at] = csw[2][2 * h][col] + csw[2][2 * h + 1][col];
     }
   }
 }
@@ -274,15 +397,21 @@ __global__ void bgemm_reduce_kernel(BgemmArgs a, int Z) {
   float* p = a.C + z * a.sCz + (long long)m * a.sCm + (long long)n * a.sCn;
   float v = a.beta ? *p : 0.f;
   const float* P = a.part + (size_t)z * a.ksplit * mn + (size_t)m * a.N + n;
-  for (int sp = 0; sp < a.ksplit; ++sp) v += P[(size_t)sp * mn];
+  // every split's load issued before the first add (ksplit <= 16), added in order
+  float x[16];
+#pragma unroll
+  for (int sp = 0; sp < 16; ++sp) x[sp] = sp < a.ksplit ? P[(size_t)sp * mn] : 0.f;
+#pragma unroll
+  for (int sp = 0; sp < 16; ++sp)
+    if (sp < a.ksplit) v += x[sp];
   if (a.bias_n) v += a.bias_n[z * a.sbz + n];
   *p = v;
 }
 
-template <typename CT, typename TA, typename TB, bool ELU>
+template <typename CT, typename TA, typename TB, bool ELU, bool EPI = false>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
-  const dim3 grid((a.M + 127) / 128, (a.N + 127) / 128, Z * a.ksplit);
-  hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU>), grid, dim3(256), 0, s, a);
+  const dim3 grid((unsigned)(((a.M + 127) / 128) * ((a.N + 63) / 64) * Z * a.ksplit));
+  hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   const size_t n = (size_t)Z * a.M * a.N;
@@ -304,7 +433,7 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   a.ksplit = 1;
   a.part = nullptr;
   if (a.dz_s != nullptr || a.cs_val || a.cs_phir || a.cs_phi) scratch = nullptr;  // epilogue work: no split-K
-  const int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128) * Z;
+  const int tiles = ((a.M + 127) / 128) * ((a.N + 63) / 64) * Z;
   const int steps = a.KB * ((a.K + 31) / 32);
   if (scratch != nullptr && tiles < 512 && steps >= 32) {
     int ks = min(16, max(1, 2048 / tiles));
@@ -315,17 +444,28 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
       a.part = scratch;
     }
   }
+  // the epilogue variants exist for the operand kinds the products use
+  const bool epi = a.dz_s != nullptr || a.cs_val || a.cs_phir || a.cs_phi;
+  if (epi && a_elu) return hipErrorInvalidValue;
   if (dtype == 1) {
-    if (a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false>(a, Z, s);
-    if (a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false>(a, Z, s);
+    if (a_io && b_io)
+      return epi ? launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, true>(a, Z, s)
+                 : launch_bgemm_t<uint16_t, uint16_t, uint16_t, false>(a, Z, s);
+    if (a_io && !b_io)
+      return epi ? launch_bgemm_t<uint16_t, uint16_t, float, false, true>(a, Z, s)
+                 : launch_bgemm_t<uint16_t, uint16_t, float, false>(a, Z, s);
     if (!a_io && b_io) {
+      if (epi) return hipErrorInvalidValue;
       return a_elu ? launch_bgemm_t<uint16_t, float, uint16_t, true>(a, Z, s)
                    : launch_bgemm_t<uint16_t, float, uint16_t, false>(a, Z, s);
     }
-    return a_elu ? launch_bgemm_t<uint16_t, float, float, true>(a, Z, s)
-                 : launch_bgemm_t<uint16_t, float, float, false>(a, Z, s);
+    if (a_elu) return launch_bgemm_t<uint16_t, float, float, true>(a, Z, s);
+    return epi ? launch_bgemm_t<uint16_t, float, float, false, true>(a, Z, s)
+               : launch_bgemm_t<uint16_t, float, float, false>(a, Z, s);
   }
-  return a_elu ? launch_bgemm_t<float, float, float, true>(a, Z, s) : launch_bgemm_t<float, float, float, false>(a, Z, s);
+  if (a_elu) return launch_bgemm_t<float, float, float, true>(a, Z, s);
+  return epi ? launch_bgemm_t<float, float, float, false, true>(a, Z, s)
+             : launch_bgemm_t<float, float, float, false>(a, Z, s);
 }
 
 // ---------------------------------------------------------------- small kernels
@@ -481,6 +621,12 @@ static hipError_t launch_dlin(const float* dout, const float* lin, const float* 
   return hipGetLastError();
 }
 // ---------------------------------------------------------------- host side
+// bf16 with the elu + 1 projection at D = 64 or 128: KV and ksum come from the
+// forward's key/value kernel (split partials over the keys, a fixed-order sum).
+static bool kv_from_keys(const Problem& p) {
+  return p.dtype == 1 && p.proj && p.fmap == kElu1 && (p.D == 64 || p.D == 128) && p.F == 256;
+}
+
 BackwardLayout backward_layout(const Problem& p) {
   BackwardLayout l;
   const size_t Z = (size_t)p.B * p.H, N = p.N, NQ = query_rows(p), F = p.F, D = p.D;
@@ -510,7 +656,10 @@ BackwardLayout backward_layout(const Problem& p) {
   l.cs1 = take(cs);
   l.cs2 = take(cs);
   l.cs3 = take(cs);
-  l.splitk = take(splitk_elems(p));
+  // split-K partials, or (bf16 with the projection) the key/value kernel's split partials and W^T chunks
+  size_t sk = splitk_elems(p);
+  if (kv_from_keys(p)) sk = std::max(sk, (kv2_reduce_workspace_bytes(p) + 3) / 4);
+  l.splitk = take(sk);
   l.bytes = o;
   return l;
 }
@@ -579,34 +728,42 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     }
     return hipSuccess;
   };
+  // bf16: KV = phi(z_k)^T V and ks = sum_n phi(z_k) straight from K and V by the
+  // forward's key/value kernel (it forms z_k = K W + b in registers), which
+  // reads K and V instead of the fp32 z_k
+  const bool kv_direct = kv_from_keys(p);
   TTR_HIP(proj(Q, zq, NQ, nullptr));
   tm->mark();
-  TTR_HIP(proj(K, zk, N, t.cs1));
+  TTR_HIP(proj(K, zk, N, kv_direct ? nullptr : t.cs1));
   tm->mark();
-
-  // ks = sum_n phi(z_k) from the z_k products' half-tile sums; KV = phi(z_k)^T V
-  TTR_HIP(launch_tile_colsum(t.cs1, half_tiles(N), nullptr, 0, 1, 0, F, Z, ks, s));
-  tm->mark();
-  {
-    BgemmArgs a{};
-    a.A = zk;  // A(m = f, k = n) = phi(z_k[n][f])
-    a.B = V;
-    a.C = kv;
-    a.M = F;
-    a.N = D;
-    a.K = N;
-    a.KB = 1;
-    a.sAz = NF;
-    a.sAm = 1;
-    a.sAk = F;
-    a.sBz = ND;
-    a.sBk = D;
-    a.sBn = 1;
-    a.sCz = FD;
-    a.sCm = D;
-    a.sCn = 1;
-    TTR_HIP(launch_bgemm(dt, false, true, true, a, Z, s, t.splitk, t.splitk_n));
+  if (kv_direct) {
+    TTR_HIP(launch_kv2_reduce(p, K, V, W, bias, kv, ks, t.splitk, s));
     tm->mark();
+  } else {
+    // ks = sum_n phi(z_k) from the z_k products' half-tile sums; KV = phi(z_k)^T V
+    TTR_HIP(launch_tile_colsum(t.cs1, half_tiles(N), nullptr, 0, 1, 0, F, Z, ks, s));
+    tm->mark();
+    {
+      BgemmArgs a{};
+      a.A = zk;  // A(m = f, k = n) = phi(z_k[n][f])
+      a.B = V;
+      a.C = kv;
+      a.M = F;
+      a.N = D;
+      a.K = N;
+      a.KB = 1;
+      a.sAz = NF;
+      a.sAm = 1;
+      a.sAk = F;
+      a.sBz = ND;
+      a.sBk = D;
+      a.sBn = 1;
+      a.sCz = FD;
+      a.sCm = D;
+      a.sCn = 1;
+      TTR_HIP(launch_bgemm(dt, false, true, true, a, Z, s, t.splitk, t.splitk_n));
+      tm->mark();
+    }
   }
   // num = phi(z_q) KV -> lin (in place after den)
   {
