@@ -436,7 +436,7 @@ def distill_plan(w, nq=None):
     plan += [("bgemm num = phi_q KV", gq, 0), ("den_lin_kernel", 2 * Z * NQ * F, 0)]
     if L > 0:
         plan.append(("landmark branch (hybrid_kernel)", 4 * Z * NQ * L * D, 0))
-    plan += [("distill_loss_rows_kernel", 0, 0), ("distill_loss_total_kernel", 0, 0), ("dlin_kernel", 0, 0),
+    plan += [("loss rows and dnum, dden (distill_loss_dlin_kernel)", 0, 0), ("distill_loss_total_kernel", 0, 0),
              ("bgemm dz_q = (dnum KV^T + dden ks^T) phi'(z_q)", gq, 0), ("bgemm dKV = phi_q^T dnum", gq, 0),
              ("dks (tile sums of the dz_q epilogue)", 0, 0), ("bgemm dz_k = (V dKV^T + dks) phi'(z_k)", gk, 0),
              ("bgemm dW += Q^T dz_q", gq, 0), ("bgemm dW += K^T dz_k", gk, 0),

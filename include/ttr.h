@@ -377,8 +377,8 @@ int ttr_last_hip_error(void);
  *     dz_q (its product with the phi' factor in the epilogue), dKV, dks, dz_k
  *     (likewise), dW from Q, dW from K, db/dg;
  *   distillation step: W to bf16 (bf16 IO), teacher (when computed), the
- *     backward's forward stages, loss rows, loss total, the backward's
- *     gradient stages, Adam;
+ *     backward's forward stages, loss rows with dnum/dden, loss total, the
+ *     backward's gradient stages after dnum/dden, Adam;
  *   cosine distance: per-workgroup partial sums, total;
  *   replay push (on the replay object's side stream): the row gather, the
  *     rows' copy, K's copy, V's copy.

@@ -809,7 +809,8 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
   return hipSuccess;
 }
 
-// Gradients from dout, after backward_forward_pass filled t.
+// Gradients from dout, after backward_forward_pass filled t (dout NULL: dnum,
+// dden and rpart are already in t).
 static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void* K, const void* V, const float* g,
                                      int L, const float* dout, float* dW, float* db, float* dg, const BwBufs& t,
                                      hipStream_t s, StageTimer* tm) {
@@ -819,8 +820,10 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
   const long long NF = (long long)N * F, ND = (long long)N * D, FD = (long long)F * D;
   const long long QF = (long long)NQ * F, QD = (long long)NQ * D;
   // dnum, dden, dalpha row shares (one per query row)
-  TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, NQ, D, Z, L > 0, dnum, dden, rpart, s));
-  tm->mark();
+  if (dout != nullptr) {  // (NULL: the caller has formed them)
+    TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, NQ, D, Z, L > 0, dnum, dden, rpart, s));
+    tm->mark();
+  }
   // dz_q = (dnum KV^T + dden ks^T) phi'(z_q): [Nq x D] . [D x F], the rest in the epilogue
   {
     BgemmArgs a{};
@@ -948,32 +951,38 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
 
 // ---------------------------------------------------------------- distillation step
 // Per row (z, n), one wave: o = alpha lin + (1 - alpha) lm (lin alone when L == 0),
-// t = the teacher row; writes dout = w1 clip(o - t, -1, 1) / numel - w2 dcos / rows,
-// the row's huber sum and 1 - cos. w = exp(-s).
-__global__ void distill_loss_rows_kernel(const float* lin, const float* lm, const float* teacher,
-                                         const uint16_t* teacher_bf16, const float* g, const float* sv, int H, int N,
-                                         int D, int Z, int has_lm, float* dout, float* hrow, float* crow_) {
+// t = the teacher row; dout = w1 clip(o - t, -1, 1) / numel - w2 dcos / rows (the
+// loss's gradient with respect to o, kept in registers), the row's huber sum
+// and 1 - cos; then the linear branch's row gradients from dout: dlin = alpha
+// dout, dnum = dlin / den, dden = -sum_d dlin lin / den, and the row's share of
+// dalpha, sum_d dout (lin - lm). w = exp(-s).
+__global__ void distill_loss_dlin_kernel(const float* lin, const float* lm, const float* teacher,
+                                         const uint16_t* teacher_bf16, const float* g, const float* sv,
+                                         const float* den_row, int H, int N, int D, int Z, int has_lm, float* hrow,
+                                         float* crow_, float* dnum, float* dden, float* rpart) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= Z * N) return;
   const int h = (row / N) % H;
   const float alpha = has_lm ? 1.f / (1.f + expf(-g[h])) : 1.f;
   const float w1 = expf(-sv[0]), w2 = expf(-sv[1]);
   const float inv_numel = 1.f / ((float)Z * N * D), inv_rows = 1.f / ((float)Z * N);
-  const float* li = lin + (size_t)row * D;
-  const float* lr = lm + (size_t)row * D;
-  const size_t trow = (size_t)row * D;
-  float ov[4], tv[4];  // D <= 256: up to 4 elements per lane
+  const size_t rb = (size_t)row * D;
+  float lv[4], mv[4], ov[4], tv[4];  // D <= 256: up to 4 elements per lane
   float hs = 0.f, dot = 0.f, oo = 0.f, tt = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int d = lane + 64 * j;
-    float o = 0.f, t = 0.f;
+    float l = 0.f, m = 0.f, o = 0.f, t = 0.f;
     if (d < D) {
-      o = has_lm ? alpha * li[d] + (1.f - alpha) * lr[d] : li[d];
-      t = teacher_bf16 ? bf2f(teacher_bf16[trow + d]) : teacher[trow + d];
+      l = lin[rb + d];
+      m = has_lm ? lm[rb + d] : 0.f;
+      o = has_lm ? alpha * l + (1.f - alpha) * m : l;
+      t = teacher_bf16 ? bf2f(teacher_bf16[rb + d]) : teacher[rb + d];
       const float r = o - t, ar = fabsf(r);
       hs += ar <= 1.f ? 0.5f * r * r : ar - 0.5f;
     }
+    lv[j] = l;
+    mv[j] = m;
     ov[j] = o;
     tv[j] = t;
     dot += o * t;
@@ -987,22 +996,34 @@ __global__ void distill_loss_rows_kernel(const float* lin, const float* lm, cons
     tt += __shfl_xor(tt, off);
   }
   const float no = sqrtf(oo), nt = sqrtf(tt);
-  const float den = fmaxf(no * nt, 1e-8f);
-  const float cosv = dot / den;
+  const float cden = fmaxf(no * nt, 1e-8f);
+  const float cosv = dot / cden;
   const bool live = no * nt > 1e-8f;
-  const float co = live ? dot * nt / (no * den * den) : 0.f;
+  const float co = live ? dot * nt / (no * cden * cden) : 0.f;
+  const float inv = 1.f / den_row[row];
+  float sd = 0.f, sa = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int d = lane + 64 * j;
     if (d < D) {
       const float r = ov[j] - tv[j];
-      const float dcos = tv[j] / den - co * ov[j];
-      dout[(size_t)row * D + d] = w1 * fminf(fmaxf(r, -1.f), 1.f) * inv_numel - w2 * dcos * inv_rows;
+      const float dcos = tv[j] / cden - co * ov[j];
+      const float G = w1 * fminf(fmaxf(r, -1.f), 1.f) * inv_numel - w2 * dcos * inv_rows;
+      const float dl = alpha * G;
+      dnum[rb + d] = dl * inv;
+      sd += dl * lv[j];
+      if (has_lm) sa += G * (lv[j] - mv[j]);
     }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    sd += __shfl_xor(sd, off);
+    sa += __shfl_xor(sa, off);
   }
   if (lane == 0) {
     hrow[row] = hs;
     crow_[row] = 1.f - cosv;
+    dden[row] = -sd * inv;
+    rpart[row] = sa;
   }
 }
 
@@ -1109,8 +1130,6 @@ DistillLayout distill_layout(const Problem& p, bool need_teacher) {
       o += al(Z * N * D * 4);
     }
   }
-  l.dout = o;
-  o += al(Z * N * D * 4);
   l.hrow = o;
   o += al(Z * N * 4);
   l.crow = o;
@@ -1178,13 +1197,12 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
   }
   const BwBufs t = bw_bufs(p, ws);
   TTR_HIP(backward_forward_pass(p, Q, K, V, Wio, bias, eps, L, t, s, tm));
-  float* dout = reinterpret_cast<float*>(w8 + l.dout);
   float* hrow = reinterpret_cast<float*>(w8 + l.hrow);
   float* crw = reinterpret_cast<float*>(w8 + l.crow);
   float* gr = reinterpret_cast<float*>(w8 + l.grads);
   float *dW = gr, *db = gr + nW, *dg = db + nb, *ds = dg + H;
-  hipLaunchKernelGGL(distill_loss_rows_kernel, dim3(blocks((size_t)Z * NQ, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
-                     g, sv, H, NQ, D, Z, L > 0 ? 1 : 0, dout, hrow, crw);
+  hipLaunchKernelGGL(distill_loss_dlin_kernel, dim3(blocks((size_t)Z * NQ, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
+                     g, sv, t.den, H, NQ, D, Z, L > 0 ? 1 : 0, hrow, crw, t.dnum, t.dden, t.rpart);
   TTR_HIP(hipGetLastError());
   tm->mark();
   float* lpart = reinterpret_cast<float*>(w8 + l.lpart);
@@ -1194,7 +1212,7 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
   hipLaunchKernelGGL(distill_loss_total_kernel, dim3(1), dim3(64), 0, s, lpart, nparts, Z * NQ, D, sv, loss_out, ds);
   TTR_HIP(hipGetLastError());
   tm->mark();
-  TTR_HIP(backward_grad_pass(p, Q, K, V, g, L, dout, dW, db, dg, t, s, tm));
+  TTR_HIP(backward_grad_pass(p, Q, K, V, g, L, nullptr, dW, db, dg, t, s, tm));  // dnum, dden, rpart are in place
   AdamArgs a;
   a.p[0] = W;
   a.p[1] = bias;

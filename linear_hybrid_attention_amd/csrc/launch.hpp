@@ -119,7 +119,7 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
 
 // Phase-1 distillation step (k_backward.hip): workspace after the backward's
 struct DistillLayout {
-  size_t w_io, teacher, gneg, tws, dout, hrow, crow, grads, lpart, bytes;
+  size_t w_io, teacher, gneg, tws, hrow, crow, grads, lpart, bytes;
 };
 DistillLayout distill_layout(const Problem& p, bool need_teacher);
 hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, const void* V, const float* teacher,
