@@ -433,7 +433,7 @@ def distill_plan(w, nq=None):
         plan.append(("KV, ksum = phi(K W + b)^T V, colsum (kv2_partial_kernel + kv_finalize_kernel)", gk, 0))
     else:
         plan += [("ksum (tile sums of the z_k epilogue)", 0, 0), ("bgemm KV = phi_k^T V", gk, 0)]
-    plan += [("bgemm num = phi_q KV", gq, 0), ("den_lin_kernel", 2 * Z * NQ * F, 0)]
+    plan += [("bgemm lin = phi_q KV / den, den = phi_q . ks + eps (normaliser formed from the staged rows)", gq, 0)]
     if L > 0:
         plan.append(("landmark branch (hybrid_kernel)", 4 * Z * NQ * L * D, 0))
     plan += [("loss rows and dnum, dden (distill_loss_dlin_kernel)", 0, 0), ("distill_loss_total_kernel", 0, 0),

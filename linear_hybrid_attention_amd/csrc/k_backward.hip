@@ -49,6 +49,13 @@ struct BgemmArgs {
   float* cs_val;
   float* cs_phir;
   float* cs_phi;
+  // optional normaliser (no split-K; A = phi(x) rows, k contiguous): den(m) = sum_k A(m, k)
+  // den_ks[z * den_ksz + k] + den_eps, written to den_out[z * den_oz + m] by the first N
+  // tile, and C(m, n) = acc / den(m)
+  const float* den_ks;
+  long long den_ksz, den_oz;
+  float* den_out;
+  float den_eps;
 };
 
 template <typename CT> struct BgTile {
@@ -248,9 +255,12 @@ __device__ __forceinline__ int bg_item(int i, int n) {
 // a small accumulator, so that four workgroups share a compute unit and their
 // memory phases overlap. Workgroup items run N tile fastest, then M tile, then
 // z * ksplit + split. EPI: the dz or column-sum epilogue is compiled in (never
-// with split-K).
-template <typename CT, typename TA, typename TB, bool A_ELU, bool EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void bgemm_kernel(BgemmArgs a) {
+// with split-K). DEN: the normaliser of each row is formed from the staged A
+// rows (thread pair t, t + 1 holds one row's k run of a step) and divides the
+// row (never with split-K).
+constexpr int kDenMaxK = 512;  // the normaliser's K (the feature count) at most
+template <typename CT, typename TA, typename TB, bool A_ELU, bool EPI, bool DEN = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4))) void bgemm_kernel(BgemmArgs a) {
   constexpr int TM = BgTile<CT>::TM, TN = BgTile<CT>::TN, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
   __shared__ __attribute__((aligned(16))) CT As[TM * LD];
   __shared__ __attribute__((aligned(16))) CT Bs[TN * LD];  // B^T: [64 n][KT]
@@ -283,9 +293,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     va.load(A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a.K, a_kc, a_vec, tid);
     vb.load(B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, a.K, b_kc, b_vec, tid);
   };
+  float dpart = 0.f;  // DEN: this thread's share of its row's phi(A) . ks
+  __shared__ __attribute__((aligned(16))) float ksh[DEN ? kDenMaxK : 1];  // DEN: ks, zero past K
+  if constexpr (DEN)
+    for (int k = tid; k < kDenMaxK; k += 256) ksh[k] = k < a.K ? a.den_ks[z * a.den_ksz + k] : 0.f;
   if (s_begin < total) load(s_begin);
   for (int s = s_begin; s < total; ++s) {
-    __syncthreads();  // every wave is done with the previous tile
+    __syncthreads();  // every wave is done with the previous tile (and, DEN, ksh is written)
+    if constexpr (DEN) {  // (A is k-contiguous: the thread's 16 values are k0 + (tid % 2) 16 ..)
+      const f32x4* kp = reinterpret_cast<const f32x4*>(ksh + (s % nks) * KT + (tid % 2) * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 kv = kp[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dpart += va.v[4 * q + i] * kv[i];
+      }
+    }
     va.store(As, a_kc, tid);
     vb.store(Bs, b_kc, tid);
     __syncthreads();
@@ -302,6 +325,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
   }
   // lane (c, g) holds, per tile j, column n0 + j*32 + c and rows m0 + w*32 + crow(lane, r)
   const int mb = m0 + w * 32;
+  if constexpr (DEN) {
+    __shared__ float dsh[TM];
+    dpart += __shfl_xor(dpart, 1);
+    if ((tid & 1) == 0) dsh[tid >> 1] = dpart + a.den_eps;
+    __syncthreads();
+    if (ntile == 0 && tid < TM && m0 + tid < a.M) a.den_out[z * a.den_oz + m0 + tid] = dsh[tid];
+    float* __restrict__ Cz = a.C + z * a.sCz;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + j * 32 + c;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = w * 32 + crow(lane, r), m = m0 + ml;
+        if (m < a.M) Cz[(long long)m * a.sCm + (long long)n * a.sCn] = acc[j][r] / dsh[ml];
+      }
+    }
+    return;
+  }
   if (!EPI) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -408,10 +450,10 @@ __global__ void bgemm_reduce_kernel(BgemmArgs a, int Z) {
   *p = v;
 }
 
-template <typename CT, typename TA, typename TB, bool ELU, bool EPI = false>
+template <typename CT, typename TA, typename TB, bool ELU, bool EPI = false, bool DEN = false>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
   const dim3 grid((unsigned)(((a.M + 127) / 128) * ((a.N + 63) / 64) * Z * a.ksplit));
-  hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   const size_t n = (size_t)Z * a.M * a.N;
@@ -432,7 +474,7 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   BgemmArgs a = a0;
   a.ksplit = 1;
   a.part = nullptr;
-  if (a.dz_s != nullptr || a.cs_val || a.cs_phir || a.cs_phi) scratch = nullptr;  // epilogue work: no split-K
+  if (a.dz_s != nullptr || a.cs_val || a.cs_phir || a.cs_phi || a.den_ks) scratch = nullptr;  // epilogue work: no split-K
   const int tiles = ((a.M + 127) / 128) * ((a.N + 63) / 64) * Z;
   const int steps = a.KB * ((a.K + 31) / 32);
   if (scratch != nullptr && tiles < 512 && steps >= 32) {
@@ -447,6 +489,11 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   // the epilogue variants exist for the operand kinds the products use
   const bool epi = a.dz_s != nullptr || a.cs_val || a.cs_phir || a.cs_phi;
   if (epi && a_elu) return hipErrorInvalidValue;
+  if (a.den_ks != nullptr) {  // phi(fp32 A) rows, k contiguous, fp32 B
+    if (epi || !a_elu || a_io || b_io || a.sAk != 1 || a.K > kDenMaxK || a.KB != 1) return hipErrorInvalidValue;
+    return dtype == 1 ? launch_bgemm_t<uint16_t, float, float, true, false, true>(a, Z, s)
+                      : launch_bgemm_t<float, float, float, true, false, true>(a, Z, s);
+  }
   if (dtype == 1) {
     if (a_io && b_io)
       return epi ? launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, true>(a, Z, s)
@@ -534,23 +581,6 @@ __global__ __launch_bounds__(256) void tile_colsum_kernel(const float* p1, int t
                                                       sh[3][threadIdx.x];
 }
 
-// Per row (z, n), one wave: den = phi(z_q) . ks + eps; lin = num / den (in place).
-__global__ void den_lin_kernel(const float* zq, const float* ks, float* num, float* den, int Z, int N, int F, int D,
-                               float eps) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= Z * N) return;
-  const int z = row / N;
-  const float* zr = zq + (size_t)row * F;
-  const float* k = ks + (size_t)z * F;
-  float s = 0.f;
-  for (int f = lane; f < F; f += 64) s += elu1(zr[f]) * k[f];
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  const float dn = s + eps;
-  if (lane == 0) den[row] = dn;
-  float* nr = num + (size_t)row * D;
-  for (int d = lane; d < D; d += 64) nr[d] = nr[d] / dn;
-}
-
 // Per row: dlin = alpha dout; dnum = dlin / den; dden = -sum_d dlin lin / den;
 // and the row's share of dalpha: sum_d dout (lin - lm) (into rpart[row]).
 __global__ void dlin_kernel(const float* dout, const float* lin, const float* lm, const float* den, const float* g,
@@ -605,12 +635,6 @@ static hipError_t launch_colsum(const float* src, const float* src2, const float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(colsum_final_kernel, dim3(blocks((size_t)Z * F, 256)), dim3(256), 0, s, part, Z, F, out);
-  return hipGetLastError();
-}
-static hipError_t launch_den_lin(const float* zq, const float* ks, float* num, float* den, int Z, int N, int F, int D,
-                                 float eps, hipStream_t s) {
-  hipLaunchKernelGGL(den_lin_kernel, dim3(blocks((size_t)Z * N, 4)), dim3(256), 0, s, zq, ks, num, den, Z, N, F, D,
-                     eps);
   return hipGetLastError();
 }
 static hipError_t launch_dlin(const float* dout, const float* lin, const float* lm, const float* den, const float* g,
@@ -765,7 +789,7 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
       tm->mark();
     }
   }
-  // num = phi(z_q) KV -> lin (in place after den)
+  // lin = phi(z_q) KV / den, den = phi(z_q) . ks + eps
   {
     BgemmArgs a{};
     a.A = zq;
@@ -784,11 +808,14 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     a.sCz = QD;
     a.sCm = D;
     a.sCn = 1;
+    a.den_ks = ks;  // den = phi(z_q) . ks + eps, and lin = num / den, in the same pass
+    a.den_ksz = F;
+    a.den_out = den;
+    a.den_oz = NQ;
+    a.den_eps = eps;
     TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s));
     tm->mark();
   }
-  TTR_HIP(launch_den_lin(zq, ks, lin, den, Z, NQ, F, D, eps, s));
-  tm->mark();
   // landmark branch output (fp32), for dalpha
   if (L > 0) {
     HybridArgs ha = {};
