@@ -425,7 +425,7 @@ def distill_plan(w, nq=None):
     if w.dtype == "bf16":
         plan.append(("to_bf16_kernel (W)", 0, 0))
     if nq is None:
-        teacher = ("teacher softmax attention (kv2 + fused query kernel, every token a landmark, alpha 0)"
+        teacher = ("teacher softmax attention (landmark pack + fused query kernel without its linear branch, every key a landmark)"
                    if w.dtype == "bf16" else "teacher softmax attention (hybrid_kernel, L = N)")
         plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
     plan += [("bgemm z_q = Q W + b", gq, 0), ("bgemm z_k = K W + b", gk, 0)]

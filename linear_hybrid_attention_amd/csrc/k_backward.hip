@@ -1129,10 +1129,6 @@ __global__ void adam_kernel(AdamArgs a) {
   }
 }
 
-__global__ void fill_kernel(float* x, float v, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) x[i] = v;
-}
 
 // fp32 -> bf16 (round to nearest even)
 __global__ void to_bf16_kernel(const float* x, uint16_t* y, size_t n) {
@@ -1147,12 +1143,11 @@ DistillLayout distill_layout(const Problem& p, bool need_teacher) {
   size_t o = al(backward_layout(p).bytes);
   l.w_io = o;
   o += al(p.dtype == 1 ? H * D * F * 2 : 0);
-  l.teacher = o;  // fp32 teacher (fp32 IO), or bf16 teacher, -inf gates and the fused path's workspace (bf16 IO)
+  l.teacher = o;  // fp32 teacher (fp32 IO), or bf16 teacher and its landmark pack (bf16 IO)
   if (need_teacher) {
     if (p.dtype == 1) {
-      l.gneg = o + al(Z * N * D * 2);
-      l.tws = l.gneg + al(H * 4);
-      o = l.tws + al(fused_workspace_bytes(p, p.N));
+      l.tws = o + al(Z * N * D * 2);
+      o = l.tws + al(lm_pack_bytes(p, p.N));
     } else {
       o += al(Z * N * D * 4);
     }
@@ -1185,23 +1180,19 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
     tm->mark();
     Wio = wb;
   }
-  // Teacher: softmax over every token. bf16: the fused hybrid path with every
-  // token a landmark and alpha = sigmoid(-inf) = 0 exactly (the linear branch
-  // is multiplied by 0), output in bf16; fp32: the landmark branch with L = N.
+  // Teacher: softmax over every token. bf16: the fused query kernel without its
+  // linear branch over a pack in which every key is a landmark, output in
+  // bf16; fp32: the landmark branch with L = N.
   const float* T = teacher;
   const uint16_t* Tb = nullptr;
   if (teacher == nullptr) {
     if (p.dtype == 1) {
       uint16_t* tb = reinterpret_cast<uint16_t*>(w8 + l.teacher);
-      float* gneg = reinterpret_cast<float*>(w8 + l.gneg);
-      hipLaunchKernelGGL(fill_kernel, dim3(blocks(H, 64)), dim3(64), 0, s, gneg, -INFINITY, H);
-      TTR_HIP(hipGetLastError());
       FusedPack pk;
-      StageTimer none;
-      TTR_HIP(launch_kv2(p, K, V, Wio, bias, N, w8 + l.tws, &pk, s, &none));  // over the N keys
+      TTR_HIP(launch_lm_pack(p, K, V, N, w8 + l.tws, &pk, s));  // every one of the N keys
       Problem pq = p;  // the query kernel tiles the query rows
       pq.N = NQ;
-      TTR_HIP(launch_fused_query(pq, Q, pk, gneg, eps, N, tb, s));
+      TTR_HIP(launch_softmax_query(pq, Q, pk, N, tb, s));
       Tb = tb;
     } else {
       float* tw = reinterpret_cast<float*>(w8 + l.teacher);

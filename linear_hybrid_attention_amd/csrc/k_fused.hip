@@ -42,7 +42,9 @@ struct FusedArgs {
   uint16_t* out;
 };
 
-template <int D, int F, int MAP>
+// LIN = false: softmax attention over the landmarks alone, out = o / l (the
+// pack then holds only the landmark chunks; no linear branch, no blend).
+template <int D, int F, int MAP, bool LIN = true>
 __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   constexpr int CH = 64 * D;  // elements per chunk (every chunk kind)
   constexpr int NFC = F / 64;
@@ -67,20 +69,22 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
 
   const unsigned char* pbh = a.pack_bh + (size_t)bh * a.bh_bytes;
   const uint16_t* wpk = reinterpret_cast<const uint16_t*>(a.pack_w + (size_t)h * a.w_bytes);
-  const uint16_t* kvpk = reinterpret_cast<const uint16_t*>(pbh + 2 * F * 4);
+  constexpr int VEC = LIN ? 2 * F * 4 : 0;  // bias and ksum ahead of the chunks
+  constexpr int LB = LIN ? 2 * NFC : 0;     // index of the first landmark chunk
+  const uint16_t* kvpk = reinterpret_cast<const uint16_t*>(pbh + VEC);
   const int nlc = (L + 31) / 32;  // landmark chunks
-  const int nch = 2 * NFC + nlc;
+  const int nch = LB + nlc;
 
   // Chunk ci is copied global -> LDS slot ci % 4 asynchronously at the start
   // of the step before the one that first reads it; every step ends by
   // waiting for its copies and a barrier. A step reads at most two chunks
   // (consecutive), so the two it reads and the two in flight never share a slot.
   const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wpk, (uint32_t)a.w_bytes);                     // W^T chunks
-  const __amdgpu_buffer_rsrc_t rkv = buffer_rsrc(kvpk, (uint32_t)(a.bh_bytes - 2 * F * 4));   // KV^T, then landmark chunks
+  const __amdgpu_buffer_rsrc_t rkv = buffer_rsrc(kvpk, (uint32_t)(a.bh_bytes - VEC));   // KV^T, then landmark chunks
   auto issue = [&](int ci) {
     if (ci >= nch) return;  // workgroup-uniform
-    const bool wchunk = ci < 2 * NFC && !(ci & 1);
-    const uint32_t soff = (uint32_t)(ci < 2 * NFC ? (ci >> 1) : NFC + ci - 2 * NFC) * (CH * 2);
+    const bool wchunk = LIN && ci < 2 * NFC && !(ci & 1);
+    const uint32_t soff = (uint32_t)(!LIN ? ci : ci < 2 * NFC ? (ci >> 1) : NFC + ci - 2 * NFC) * (CH * 2);
     uint16_t* dst = slots + (ci % NSLOT) * CH;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i)
@@ -97,8 +101,8 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   // (from HBM), so that one wait covers all their latencies.
   issue(0);
   issue(1);
-  issue(2);
-  {
+  if constexpr (LIN) {  // (landmarks alone: step lc starts chunk lc + 2)
+    issue(2);
     const __amdgpu_buffer_rsrc_t rvec = buffer_rsrc(pbh, 2 * F * 4);
     if (tid < 2 * F * 4 / 16) copy16_async(rvec, (uint32_t)tid * 16, 0, smem + w * 64 * 16);
   }
@@ -106,14 +110,14 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   const uint16_t* Qp = a.Q + ((size_t)bh * N + (tok_ok ? tok : 0)) * D + 8 * g;
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) qf[kb] = ld_frag<uint16_t>(Qp + kb * 16);  // rows past N: row 0, not stored
-  const float gh = L > 0 ? a.g[h] : 0.f;
-  end_step();  // chunks 0..2, bias and ksum in LDS; Q in registers
+  const float gh = LIN && L > 0 ? a.g[h] : 0.f;
+  end_step();  // chunks 0..2, bias and ksum in LDS (landmarks alone: chunks 0, 1); Q in registers
 
   // softmax map (identity projection, F == D): the token's feature maximum
   // and inverse sum, from its Q row (half in this lane, half in lane ^ 32)
   // plus the bias (stored in MFMA row order: feature f at kperm(f))
   float qm = 0.f, qinv = 1.f;
-  if constexpr (MAP == kSoftmax) {
+  if constexpr (LIN && MAP == kSoftmax) {
     float z[D / 2];
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) {
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   // GEMM1 result while the GEMM2 MFMAs are still executing. Step k reads
   // chunks 2k - 1 (KV^T) and 2k (W^T).
   Frag<uint16_t> pb[4];
-  {  // (chunks 1 and 2 are already in flight)
+  if constexpr (LIN) {  // (chunks 1 and 2 are already in flight)
     f32x16 acc[2];
     gemm1(0, acc);
     map_den(0, acc, pb);
@@ -197,9 +201,11 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
     }
   };
   f32x16 accb[2];  // the next step's accumulators, holding its bias
-  if (NFC > 1) load_bias(1, accb);
-  pin_before(accb[0]);
-  pin_before(accb[1]);
+  if constexpr (LIN) {
+    if (NFC > 1) load_bias(1, accb);
+    pin_before(accb[0]);
+    pin_before(accb[1]);
+  }
   // Step k reads KV^T chunk 2k - 1 and W^T chunk 2k: slots 1 and 2 for odd
   // k, 3 and 0 for even k. Both call sites pass the parity as a literal and
   // the step is inlined, so every operand address folds to a lane base plus
@@ -262,10 +268,12 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
     pin_before(accb[1]);
     end_step();
   };
+  if constexpr (LIN) {
 #pragma clang loop unroll(disable)
-  for (int k = 1; k < NFC; k += 2) {
-    lin_step(k, true);
-    if (k + 1 < NFC) lin_step(k + 1, false);  // workgroup-uniform
+    for (int k = 1; k < NFC; k += 2) {
+      lin_step(k, true);
+      if (k + 1 < NFC) lin_step(k + 1, false);  // workgroup-uniform
+    }
   }
   // landmark branch state
   f32x16 o[D / 32];
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   const float sl2 = kLog2e * rsqrtf((float)D);
   // S^T of landmark chunk lc = K_L . Q^T
   auto scores = [&](int lc, f32x16& s) {
-    const uint16_t* kl = slot_of(2 * NFC + lc);
+    const uint16_t* kl = slot_of(LB + lc);
     s = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) mma(s, ld_frag<uint16_t>(kl + toff<D, kRowRead>(c, kb * 16 + 8 * g)), qf[kb]);
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   };
   // o^T += V_L^T . P^T of chunk lc
   auto pv = [&](int lc, const Frag<uint16_t> (&pf)[2]) {
-    const uint16_t* vlt = slot_of(2 * NFC + lc) + 32 * D;
+    const uint16_t* vlt = slot_of(LB + lc) + 32 * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       mma(o[db], ld_frag<uint16_t>(vlt + toff32(db * 32 + c, 8 * g)), pf[0]);
@@ -325,10 +333,14 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   };
 
   // last linear step: GEMM2 of the last feature chunk, with the scores of
-  // landmark chunk 0 (chunk 2 NFC) beside it
+  // landmark chunk 0 (chunk 2 NFC) beside it (landmarks alone: the scores and
+  // softmax of chunk 0, already in LDS with chunk 1)
   f32x16 s;
   Frag<uint16_t> pf[2];
-  {
+  if constexpr (!LIN) {
+    scores(0, s);  // (the launch has L >= 1)
+    softmax(0, s, pf);
+  } else {
     issue(2 * NFC + 1);
     if (nlc > 0) scores(0, s);  // workgroup-uniform
     gemm2(NFC - 1, pb);
@@ -346,11 +358,11 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
 
   // ---- landmark branch, software-pipelined: step lc issues the scores of
   // chunk lc + 1 and the PV product of chunk lc, then runs the softmax of
-  // chunk lc + 1 while the PV MFMAs execute. Step lc reads chunks 2 NFC + lc
-  // (V_L^T) and 2 NFC + lc + 1 (K_L).
+  // chunk lc + 1 while the PV MFMAs execute. Step lc reads chunks LB + lc
+  // (V_L^T) and LB + lc + 1 (K_L), LB = 2 NFC (0 for landmarks alone).
 #pragma clang loop unroll(disable)
   for (int lc = 0; lc < nlc; ++lc) {
-    issue(2 * NFC + lc + 2);
+    issue(LB + lc + 2);
     const bool more = lc + 1 < nlc;  // workgroup-uniform
     if (more) scores(lc + 1, s);
     pv(lc, pf);
@@ -362,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   // Epilogue: the wave's 32 x D output tile goes through LDS (the slots are
   // free after the last barrier) so that the global stores are whole 16-byte
   // pieces, four full rows per store instruction.
-  const float cb = L > 0 ? (1.f - 1.f / (1.f + expf(-gh))) / l : 0.f;
+  const float cb = !LIN ? 1.f / l : L > 0 ? (1.f - 1.f / (1.f + expf(-gh))) / l : 0.f;
   uint16_t* ot = slots + w * 32 * D;  // [32 tokens][D], kRowRead swizzle
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -370,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
     for (int q = 0; q < 4; ++q) {
       float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = num[db][4 * q + j] + cb * o[db][4 * q + j];
+      for (int j = 0; j < 4; ++j) v[j] = (LIN ? num[db][4 * q + j] : 0.f) + cb * o[db][4 * q + j];
       st4(ot + toff<D, kRowRead>(c, db * 32 + 8 * q + 4 * g), v[0], v[1], v[2], v[3]);
     }
   wave_lds_order();
@@ -395,10 +407,27 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   }
 }
 
-template <int D, int F, int MAP>
+template <int D, int F, int MAP, bool LIN = true>
 static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((fused_query_kernel<D, F, MAP>), dim3(a.nwg), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fused_query_kernel<D, F, MAP, LIN>), dim3(a.nwg), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_softmax_query(const Problem& p, const void* Q, const FusedPack& pk, int L, void* out,
+                                hipStream_t s) {
+  if (p.dtype != 1 || L < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
+  FusedArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.pack_bh = pk.pack_bh;
+  a.bh_bytes = pk.bh_bytes;
+  a.H = p.H;
+  a.N = p.N;
+  a.L = L;
+  a.ntiles = (p.N + 127) / 128;
+  a.nwg = a.ntiles * p.B * p.H;
+  a.out = static_cast<uint16_t*>(out);
+  // (F and the map do not enter the landmark-only variant)
+  return p.D == 128 ? launch_fused_t<128, 64, kElu1, false>(a, s) : launch_fused_t<64, 64, kElu1, false>(a, s);
 }
 
 hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& pk, const float* g, float eps,

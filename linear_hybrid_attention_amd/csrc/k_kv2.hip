@@ -307,6 +307,7 @@ struct PackArgs {
   int H, N, L;
   unsigned char* pack_bh;  // [BH][bh_bytes]
   unsigned char* pack_w;   // [H][w_bytes]
+  int lm_only;             // 1: the landmark jobs alone, into a pack of landmark chunks only
 };
 
 // Jobs of one (batch, head), by job index:
@@ -319,15 +320,15 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
   constexpr int KVJ = F / FJ;
   const int tid = threadIdx.x;
   const int nlb = (a.L + 31) / 32;
-  const int item = xcd_item(blockIdx.x, gridDim.x), njobs = KVJ + nlb;
+  const int item = xcd_item(blockIdx.x, gridDim.x), njobs = a.lm_only ? nlb : KVJ + nlb;
   const int bh = item / njobs, h = bh % a.H;
-  PackLayout pl{D, F, a.L, nlb};
+  PackLayout pl{D, a.lm_only ? 0 : F, a.L, nlb};
   unsigned char* base = a.pack_bh + (size_t)bh * pl.bh_bytes();
   float* biasP = reinterpret_cast<float*>(base);
   float* ksumP = biasP + F;
   uint16_t* kvc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes());
   uint16_t* lmc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes() + pl.kv_bytes());
-  const int job = item % njobs;
+  const int job = item % njobs + (a.lm_only ? KVJ : 0);
 
   if (job < KVJ) {
     // FJ features f0.. x D values: thread -> (feature pair, 4 consecutive d).
@@ -488,6 +489,7 @@ hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void
   pa.L = L;
   pa.pack_bh = pbh;
   pa.pack_w = pw;
+  pa.lm_only = 0;
   if (p.dtype != 1) return hipErrorInvalidValue;
   if (p.D == 128) {
     if (p.proj) return launch_kv2_t<128, 256, true, kElu1>(p, ka, pa, s, t);
@@ -550,6 +552,36 @@ hipError_t launch_kv2_reduce(const Problem& p, const void* K, const void* V, con
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_kv_finalize(p, ka.part, nsplit, KV, ksum, s);
+}
+
+// Every key j < L of a landmark pack alone (the chunks of the softmax-only query
+// kernel): K_L and V_L^T chunks per (batch, head), nothing else.
+size_t lm_pack_bytes(const Problem& p, int L) {
+  const PackLayout pl{p.D, 0, L, (L + 31) / 32};
+  return (size_t)p.B * p.H * pl.bh_bytes();
+}
+
+hipError_t launch_lm_pack(const Problem& p, const void* K, const void* V, int L, void* ws, FusedPack* pk,
+                          hipStream_t s) {
+  if (p.dtype != 1 || L < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
+  const PackLayout pl{p.D, 0, L, (L + 31) / 32};
+  PackArgs pa{};
+  pa.K = static_cast<const uint16_t*>(K);
+  pa.V = static_cast<const uint16_t*>(V);
+  pa.H = p.H;
+  pa.N = p.N;
+  pa.L = L;
+  pa.pack_bh = static_cast<unsigned char*>(ws);
+  pa.lm_only = 1;
+  pk->pack_bh = pa.pack_bh;
+  pk->pack_w = nullptr;
+  pk->bh_bytes = pl.bh_bytes();
+  pk->w_bytes = 0;
+  const dim3 grid((unsigned)(pl.nlb * p.B * p.H));
+  // (the landmark jobs do not depend on the feature count: any instantiation serves)
+  if (p.D == 128) hipLaunchKernelGGL((kv2_pack_kernel<128, 256, true>), grid, dim3(256), 0, s, pa);
+  else hipLaunchKernelGGL((kv2_pack_kernel<64, 256, true>), grid, dim3(256), 0, s, pa);
+  return hipGetLastError();
 }
 
 }  // namespace ttr

@@ -76,6 +76,14 @@ struct FusedPack {
 size_t fused_workspace_bytes(const Problem& p, int L);
 hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void* W, const float* bias, int L,
                       void* ws, FusedPack* pk, hipStream_t s, StageTimer* t);
+// Softmax attention of the query rows over landmarks j < L alone (keys at
+// (j N) / L): a pack of landmark chunks (lm_pack_bytes of workspace), then the
+// fused query kernel without its linear branch; bf16, D = 64 or 128.
+size_t lm_pack_bytes(const Problem& p, int L);
+hipError_t launch_lm_pack(const Problem& p, const void* K, const void* V, int L, void* ws, FusedPack* pk,
+                          hipStream_t s);
+hipError_t launch_softmax_query(const Problem& p, const void* Q, const FusedPack& pk, int L, void* out,
+                                hipStream_t s);
 hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& pk, const float* g, float eps,
                               int L, void* out, hipStream_t s);
 // The key/value reduction alone on the bf16 path (ttr_kv_reduce): the partial
@@ -119,7 +127,7 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
 
 // Phase-1 distillation step (k_backward.hip): workspace after the backward's
 struct DistillLayout {
-  size_t w_io, teacher, gneg, tws, hrow, crow, grads, lpart, bytes;
+  size_t w_io, teacher, tws, hrow, crow, grads, lpart, bytes;
 };
 DistillLayout distill_layout(const Problem& p, bool need_teacher);
 hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, const void* V, const float* teacher,
