@@ -49,6 +49,8 @@ struct BgemmArgs {
   float* cs_val;
   float* cs_phir;
   float* cs_phi;
+  // optional (epilogue variants, beta = 0): the output rounded to bf16 here instead of C
+  uint16_t* C16;
   // optional normaliser (no split-K; A = phi(x) rows, k contiguous): den(m) = sum_k A(m, k)
   // den_ks[z * den_ksz + k] + den_eps, written to den_out[z * den_oz + m] by the first N
   // tile, and C(m, n) = acc / den(m)
@@ -254,12 +256,12 @@ __device__ __forceinline__ int bg_item(int i, int n) {
 // 128 x 64 output tile per workgroup, 4 waves of 32 x 64 (1 x 2 MFMA tiles):
 // a small accumulator, so that four workgroups share a compute unit and their
 // memory phases overlap. Workgroup items run N tile fastest, then M tile, then
-// z * ksplit + split. EPI: the dz or column-sum epilogue is compiled in (never
-// with split-K). DEN: the normaliser of each row is formed from the staged A
-// rows (thread pair t, t + 1 holds one row's k run of a step) and divides the
-// row (never with split-K).
+// z * ksplit + split. EPI: the epilogue's dz and column-sum terms (0: none;
+// never with split-K); O16: that epilogue's output in bf16. DEN: the normaliser
+// of each row is formed from the staged A rows (thread pair t, t + 1 holds one
+// row's k run of a step) and divides the row (never with split-K).
 constexpr int kDenMaxK = 512;  // the normaliser's K (the feature count) at most
-template <typename CT, typename TA, typename TB, bool A_ELU, bool EPI, bool DEN = false>
+template <typename CT, typename TA, typename TB, bool A_ELU, int EPI, bool DEN = false, bool O16 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4))) void bgemm_kernel(BgemmArgs a) {
   constexpr int TM = BgTile<CT>::TM, TN = BgTile<CT>::TN, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
   __shared__ __attribute__((aligned(16))) CT As[TM * LD];
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
     }
     return;
   }
-  if (!EPI) {
+  if constexpr (EPI == 0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + j * 32 + c;
@@ -369,10 +371,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
     }
     return;
   }
-  // Epilogue with the dz products and column sums (no split-K).
-  const bool dz = a.dz_s != nullptr;
-  const float* __restrict__ dzx = a.dz_x;
-  float* __restrict__ Cz = a.C + z * a.sCz;
+  // Epilogue with the dz products and column sums (no split-K, beta = 0), its
+  // terms fixed by EPI: 1: dz with the row factor r = dz_r, the column sums of
+  // dz (cs_val) and of phi(x) r (cs_phir); 2: dz with r = 1 and the column sums
+  // of dz; 3: the column sums of phi of the output (cs_phi). O16: the output
+  // rounded to bf16 into C16. Offsets within a z slice are 32-bit (the host
+  // checks the slice's extent); full tiles store without row checks.
+  constexpr bool DZ = EPI == 1 || EPI == 2, HAS_R = EPI == 1, CSV = DZ, CSR = EPI == 1, CSQ = EPI == 3;
+  const long long zo = (long long)z * a.sCz;
+  const float* __restrict__ dzx = DZ ? a.dz_x + zo : nullptr;
+  float* __restrict__ Cz = O16 ? nullptr : a.C + zo;
+  uint16_t* __restrict__ Cz16 = O16 ? a.C16 + zo : nullptr;
+  const int sCm = (int)a.sCm, sCn = (int)a.sCn;
+  const bool full = m0 + TM <= a.M;  // every row of the tile exists (workgroup-uniform)
   __shared__ float csw[3][4][64];  // per wave: its 32 rows' column sums
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -380,31 +391,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
     float cv = 0.f, cp = 0.f, cq = 0.f;  // this lane's column sums over its rows
     if (n < a.N) {  // (lanes c and c + 32 share n: both skip or both go on)
       const float bn = a.bias_n ? a.bias_n[z * a.sbz + n] : 0.f;
-      const float sn = dz ? a.dz_s[z * a.dz_ssz + n] : 0.f;
+      const float sn = DZ ? a.dz_s[z * a.dz_ssz + n] : 0.f;
       // the dz operands of the 16 rows are loaded before any store
       float xv[16], rv[16];
-      if (dz) {
+      if constexpr (DZ) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = min(mb + crow(lane, r), a.M - 1);
-          xv[r] = dzx[z * a.sCz + (long long)m * a.sCm + (long long)n * a.sCn];
-          rv[r] = a.dz_r ? a.dz_r[z * a.dz_srz + m] : 1.f;
+          xv[r] = dzx[m * sCm + n * sCn];
+          rv[r] = HAS_R ? a.dz_r[z * a.dz_srz + m] : 1.f;
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mb + crow(lane, r);
-        if (m >= a.M) continue;
-        float* p = Cz + (long long)m * a.sCm + (long long)n * a.sCn;
-        float v = (a.beta ? *p + acc[j][r] : acc[j][r]) + bn;
-        if (dz) {  // dz = (dphi + r s) phi'(x), phi'(x) = 1 for x > 0, exp(x) otherwise
+      auto emit = [&](int r, int m) __attribute__((always_inline)) {
+        const int off = m * sCm + n * sCn;
+        float v = acc[j][r] + bn;
+        if constexpr (DZ) {  // dz = (dphi + r s) phi'(x), phi'(x) = 1 for x > 0, exp(x) otherwise
           const float dp = v + rv[r] * sn;
           v = xv[r] > 0.f ? dp : dp * __expf(xv[r]);
-          if (a.cs_phir) cp += elu1(xv[r]) * rv[r];
+          if constexpr (CSR) cp += elu1(xv[r]) * rv[r];
         }
-        if (a.cs_val) cv += v;
-        if (a.cs_phi) cq += elu1(v);
-        *p = v;
+        if constexpr (CSV) cv += v;
+        if constexpr (CSQ) cq += elu1(v);
+        if constexpr (O16) Cz16[off] = f2bf(v);  // (the column sums above use the fp32 value)
+        else Cz[off] = v;
+      };
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) emit(r, mb + crow(lane, r));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mb + crow(lane, r);
+          if (m < a.M) emit(r, m);
+        }
       }
     }
     // the column's two lanes (rows 4g..) combine; the wave's sums go to LDS
@@ -423,9 +442,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
     const int h = tid >> 6, col = tid & 63, n = n0 + col;
     if (n < a.N) {
       const size_t at = ((size_t)z * (2 * mtiles) + 2 * mtile + h) * a.N + n;
-      if (a.cs_val) a.cs_val[at] = csw[0][2 * h][col] + csw[0][2 * h + 1][col];
-      if (a.cs_phir) a.cs_phir[at] = csw[1][2 * h][col] + csw[1][2 * h + 1][col];
-      if (a.cs_phi) a.cs_phi[at] = csw[2][2 * h][col] + csw[2][2 * h + 1][col];
+      if constexpr (CSV) a.cs_val[at] = csw[0][2 * h][col] + csw[0][2 * h + 1][col];
+      if constexpr (CSR) a.cs_phir[at] = csw[1][2 * h][col] + csw[1][2 * h + 1][col];
+      if constexpr (CSQ) a.cs_phi[at] = csw[2][2 * h][col] + csw[2][2 * h + 1][col];
     }
   }
 }
@@ -450,10 +469,10 @@ __global__ void bgemm_reduce_kernel(BgemmArgs a, int Z) {
   *p = v;
 }
 
-template <typename CT, typename TA, typename TB, bool ELU, bool EPI = false, bool DEN = false>
+template <typename CT, typename TA, typename TB, bool ELU, int EPI = 0, bool DEN = false, bool O16 = false>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
   const dim3 grid((unsigned)(((a.M + 127) / 128) * ((a.N + 63) / 64) * Z * a.ksplit));
-  hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   const size_t n = (size_t)Z * a.M * a.N;
@@ -486,33 +505,54 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
       a.part = scratch;
     }
   }
-  // the epilogue variants exist for the operand kinds the products use
-  const bool epi = a.dz_s != nullptr || a.cs_val || a.cs_phir || a.cs_phi;
-  if (epi && a_elu) return hipErrorInvalidValue;
+  // The epilogue's terms select its variant (EPI 1: dz with a row factor, with
+  // the column sums of dz and of phi(x) r; 2: dz, with the column sums of dz; 3:
+  // the column sums of phi of the output); the variants exist for the operand
+  // kinds the products use, other combinations are refused.
+  int epi = 0;
+  if (a.dz_s != nullptr) {
+    if (!a.cs_val || a.cs_phi || (a.dz_r != nullptr) != (a.cs_phir != nullptr)) return hipErrorInvalidValue;
+    epi = a.dz_r ? 1 : 2;
+  } else if (a.cs_val || a.cs_phir) {
+    return hipErrorInvalidValue;
+  } else if (a.cs_phi) {
+    epi = 3;
+  }
+  if (epi != 0) {
+    if (a_elu || a.beta) return hipErrorInvalidValue;
+    // offsets within a slice are 32-bit
+    const long long ext = (long long)(a.M - 1) * a.sCm + (long long)(a.N - 1) * a.sCn;
+    if (ext > 0x7fffffffLL || a.sCm > 0x7fffffffLL || a.sCn > 0x7fffffffLL) return hipErrorInvalidValue;
+  }
+  const bool o16 = a.C16 != nullptr;
+  if (o16 && ((epi != 1 && epi != 2) || dtype != 1)) return hipErrorInvalidValue;
   if (a.den_ks != nullptr) {  // phi(fp32 A) rows, k contiguous, fp32 B
-    if (epi || !a_elu || a_io || b_io || a.sAk != 1 || a.K > kDenMaxK || a.KB != 1) return hipErrorInvalidValue;
-    return dtype == 1 ? launch_bgemm_t<uint16_t, float, float, true, false, true>(a, Z, s)
-                      : launch_bgemm_t<float, float, float, true, false, true>(a, Z, s);
+    if (epi != 0 || !a_elu || a_io || b_io || a.sAk != 1 || a.K > kDenMaxK || a.KB != 1) return hipErrorInvalidValue;
+    return dtype == 1 ? launch_bgemm_t<uint16_t, float, float, true, 0, true>(a, Z, s)
+                      : launch_bgemm_t<float, float, float, true, 0, true>(a, Z, s);
+  }
+  if (epi != 0) {
+    if (dtype == 1) {
+      if (epi == 1 && o16 && !a_io && !b_io) return launch_bgemm_t<uint16_t, float, float, false, 1, false, true>(a, Z, s);
+      if (epi == 2 && o16 && a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false, 2, false, true>(a, Z, s);
+      if (epi == 3 && a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 3>(a, Z, s);
+      return hipErrorInvalidValue;
+    }
+    if (epi == 1) return launch_bgemm_t<float, float, float, false, 1>(a, Z, s);
+    if (epi == 2) return launch_bgemm_t<float, float, float, false, 2>(a, Z, s);
+    return launch_bgemm_t<float, float, float, false, 3>(a, Z, s);
   }
   if (dtype == 1) {
-    if (a_io && b_io)
-      return epi ? launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, true>(a, Z, s)
-                 : launch_bgemm_t<uint16_t, uint16_t, uint16_t, false>(a, Z, s);
-    if (a_io && !b_io)
-      return epi ? launch_bgemm_t<uint16_t, uint16_t, float, false, true>(a, Z, s)
-                 : launch_bgemm_t<uint16_t, uint16_t, float, false>(a, Z, s);
+    if (a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false>(a, Z, s);
+    if (a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false>(a, Z, s);
     if (!a_io && b_io) {
-      if (epi) return hipErrorInvalidValue;
       return a_elu ? launch_bgemm_t<uint16_t, float, uint16_t, true>(a, Z, s)
                    : launch_bgemm_t<uint16_t, float, uint16_t, false>(a, Z, s);
     }
-    if (a_elu) return launch_bgemm_t<uint16_t, float, float, true>(a, Z, s);
-    return epi ? launch_bgemm_t<uint16_t, float, float, false, true>(a, Z, s)
-               : launch_bgemm_t<uint16_t, float, float, false>(a, Z, s);
+    return a_elu ? launch_bgemm_t<uint16_t, float, float, true>(a, Z, s)
+                 : launch_bgemm_t<uint16_t, float, float, false>(a, Z, s);
   }
-  if (a_elu) return launch_bgemm_t<float, float, float, true>(a, Z, s);
-  return epi ? launch_bgemm_t<float, float, float, false, true>(a, Z, s)
-             : launch_bgemm_t<float, float, float, false>(a, Z, s);
+  return a_elu ? launch_bgemm_t<float, float, float, true>(a, Z, s) : launch_bgemm_t<float, float, float, false>(a, Z, s);
 }
 
 // ---------------------------------------------------------------- small kernels
@@ -662,8 +702,11 @@ BackwardLayout backward_layout(const Problem& p) {
   };
   l.zq = take(Z * NQ * F);
   l.zk = take(Z * N * F);
-  l.dzq = take(Z * NQ * F);
-  l.dzk = take(Z * N * F);
+  // dz_q, dz_k: bf16 on the bf16 path (their only reader, the dW products,
+  // stages them as bf16 operands), else fp32
+  const size_t dz_el = p.dtype == 1 ? 2 : 4;
+  l.dzq = take((Z * NQ * F * dz_el + 3) / 4);
+  l.dzk = take((Z * N * F * dz_el + 3) / 4);
   l.lin = take(Z * NQ * D);
   l.lm = take(Z * NQ * D);
   l.dnum = take(Z * NQ * D);
@@ -856,7 +899,8 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     BgemmArgs a{};
     a.A = dnum;
     a.B = kv;  // B(k = d, n = f) = KV[f][d]
-    a.C = dzq;
+    if (dt == 1) a.C16 = reinterpret_cast<uint16_t*>(dzq);
+    else a.C = dzq;
     a.dz_x = zq;
     a.dz_r = dden;
     a.dz_s = ks;
@@ -909,7 +953,8 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     BgemmArgs a{};
     a.A = V;
     a.B = dkv;  // B(k = d, n = f) = dKV[f][d]
-    a.C = dzk;
+    if (dt == 1) a.C16 = reinterpret_cast<uint16_t*>(dzk);
+    else a.C = dzk;
     a.dz_x = zk;
     a.dz_s = dks;
     a.dz_ssz = F;
@@ -931,7 +976,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     tm->mark();
   }
   // dW[h] = sum_b Q[b,h]^T dz_q[b,h] + K[b,h]^T dz_k[b,h]: the batch is the outer K loop
-  auto dw = [&](const void* X, const float* dzv, int rows, int beta) {
+  auto dw = [&](const void* X, const void* dzv, int rows, int beta) {  // dz in the IO dtype
     const long long RD = (long long)rows * D, RF = (long long)rows * F;
     BgemmArgs a{};
     a.A = X;  // A(m = d, k = n) = X[n][d]
@@ -953,7 +998,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCm = F;
     a.sCn = 1;
     a.beta = beta;
-    return launch_bgemm(dt, true, false, false, a, H, s, t.splitk, t.splitk_n);
+    return launch_bgemm(dt, true, dt == 1, false, a, H, s, t.splitk, t.splitk_n);
   };
   TTR_HIP(dw(Q, dzq, NQ, 0));
   tm->mark();
