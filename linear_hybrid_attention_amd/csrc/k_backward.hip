@@ -222,6 +222,18 @@ __device__ __forceinline__ void bg_store_raw(uint16_t* tile, const u32x4 (&v)[RO
   }
 }
 
+// The thread's run for unconditional vector loads (the host has checked the
+// alignment, K % KT == 0 and, for row-strided operands, whole row groups): a
+// row past nrows reads a valid row instead; it only feeds output rows or
+// columns that are never stored.
+template <typename T, int ROWS>
+__device__ __forceinline__ const T* bg_fast_ptr(const T* base, long long s_row, long long s_k, int row0, int nrows,
+                                                int k0, bool k_contig, int tid) {
+  using G = BgGeo<ROWS>;
+  if (k_contig) return base + (long long)min(row0 + G::kc_row(tid), nrows - 1) * s_row + (k0 + G::kc_k(tid));
+  return base + (long long)(k0 + G::nk_k(tid)) * s_k + min(row0 + G::nk_row(tid), nrows - G::NE);
+}
+
 // One operand's staging registers for a K-step: packed 16-bit elements when
 // they go to the tile unchanged, else floats (converted or mapped on the way).
 template <typename CT, typename T, bool ELU, int ROWS>
@@ -231,6 +243,13 @@ struct BgStage {
                                        int K, bool kc, bool vec, int tid) {
     bg_load<T, ELU, ROWS>(v, base, s_row, s_k, row0, nrows, k0, K, kc, vec, tid);
   }
+  __device__ __forceinline__ void load_fast(const T* base, long long s_row, long long s_k, int row0, int nrows,
+                                            int k0, bool kc, int tid) {
+    ld_run<T, ROWS / 8>(bg_fast_ptr<T, ROWS>(base, s_row, s_k, row0, nrows, k0, kc, tid), v);
+    if (ELU)
+#pragma unroll
+      for (int i = 0; i < ROWS / 8; ++i) v[i] = elu1(v[i]);
+  }
   __device__ __forceinline__ void store(CT* tile, bool kc, int tid) const { bg_store<CT, ROWS>(tile, v, kc, tid); }
 };
 template <int ROWS>
@@ -239,6 +258,12 @@ struct BgStage<uint16_t, uint16_t, false, ROWS> {
   __device__ __forceinline__ void load(const uint16_t* base, long long s_row, long long s_k, int row0, int nrows,
                                        int k0, int K, bool kc, bool vec, int tid) {
     bg_load_raw<ROWS>(v, base, s_row, s_k, row0, nrows, k0, K, kc, vec, tid);
+  }
+  __device__ __forceinline__ void load_fast(const uint16_t* base, long long s_row, long long s_k, int row0,
+                                            int nrows, int k0, bool kc, int tid) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(bg_fast_ptr<uint16_t, ROWS>(base, s_row, s_k, row0, nrows, k0, kc, tid));
+#pragma unroll
+    for (int u = 0; u < ROWS / 64; ++u) v[u] = q[u];
   }
   __device__ __forceinline__ void store(uint16_t* tile, bool kc, int tid) const {
     bg_store_raw<ROWS>(tile, v, kc, tid);
@@ -261,7 +286,8 @@ __device__ __forceinline__ int bg_item(int i, int n) {
 // of each row is formed from the staged A rows (thread pair t, t + 1 holds one
 // row's k run of a step) and divides the row (never with split-K).
 constexpr int kDenMaxK = 512;  // the normaliser's K (the feature count) at most
-template <typename CT, typename TA, typename TB, bool A_ELU, int EPI, bool DEN = false, bool O16 = false>
+template <typename CT, typename TA, typename TB, bool A_ELU, int EPI, bool DEN = false, bool O16 = false,
+          bool FAST = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4))) void bgemm_kernel(BgemmArgs a) {
   constexpr int TM = BgTile<CT>::TM, TN = BgTile<CT>::TN, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
   __shared__ __attribute__((aligned(16))) CT As[TM * LD];
@@ -292,8 +318,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
   const int per = (steps + a.ksplit - 1) / a.ksplit, s_begin = split * per, total = min(steps, s_begin + per);
   auto load = [&](int s) {
     const int kb = s / nks, k0 = (s % nks) * KT;
-    va.load(A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a.K, a_kc, a_vec, tid);
-    vb.load(B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, a.K, b_kc, b_vec, tid);
+    if constexpr (FAST) {
+      va.load_fast(A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a_kc, tid);
+      vb.load_fast(B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, b_kc, tid);
+    } else {
+      va.load(A + kb * a.sAkb, a.sAm, a.sAk, m0, a.M, k0, a.K, a_kc, a_vec, tid);
+      vb.load(B + kb * a.sBkb, a.sBn, a.sBk, n0, a.N, k0, a.K, b_kc, b_vec, tid);
+    }
   };
   float dpart = 0.f;  // DEN: this thread's share of its row's phi(A) . ks
   __shared__ __attribute__((aligned(16))) float ksh[DEN ? kDenMaxK : 1];  // DEN: ks, zero past K
@@ -360,12 +391,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
         continue;
       }
       const float bn = a.bias_n ? a.bias_n[z * a.sbz + n] : 0.f;
-      float* __restrict__ Cz = a.C + z * a.sCz;
+      float* __restrict__ Cz = a.C + z * a.sCz + (long long)n * a.sCn;
+      if (m0 + TM <= a.M && !a.beta) {  // a full tile, written over: no row checks
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Cz[(long long)(mb + crow(lane, r)) * a.sCm] = acc[j][r] + bn;
+        continue;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = mb + crow(lane, r);
         if (m >= a.M) continue;
-        float* p = Cz + (long long)m * a.sCm + (long long)n * a.sCn;
+        float* p = Cz + (long long)m * a.sCm;
         *p = (a.beta ? *p + acc[j][r] : acc[j][r]) + bn;
       }
     }
@@ -469,10 +505,28 @@ __global__ void bgemm_reduce_kernel(BgemmArgs a, int Z) {
   *p = v;
 }
 
+// The unconditional-load variant's conditions: both operands 16-byte aligned
+// with whole runs (as the kernel's vector path requires), K a multiple of the
+// K-step, and whole row groups for an operand whose rows are contiguous.
+template <typename TA, typename TB>
+static bool bg_fast(const BgemmArgs& a) {
+  const long long PA = 16 / sizeof(TA), PB = 16 / sizeof(TB);
+  const bool a_kc = a.sAk == 1, b_kc = a.sBk == 1;
+  const bool a_vec = (a_kc || a.sAm == 1) && ((a_kc ? a.sAm : a.sAk) % PA == 0) && (a.sAz % PA == 0) &&
+                     (a.sAkb % PA == 0) && ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0);
+  const bool b_vec = (b_kc || a.sBn == 1) && ((b_kc ? a.sBn : a.sBk) % PB == 0) && (a.sBz % PB == 0) &&
+                     (a.sBkb % PB == 0) && ((reinterpret_cast<uintptr_t>(a.B) & 15) == 0);
+  return a_vec && b_vec && a.K % 32 == 0 && (a_kc || (a.M >= 16 && a.M % 16 == 0)) &&
+         (b_kc || (a.N >= 8 && a.N % 8 == 0));
+}
+
 template <typename CT, typename TA, typename TB, bool ELU, int EPI = 0, bool DEN = false, bool O16 = false>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
   const dim3 grid((unsigned)(((a.M + 127) / 128) * ((a.N + 63) / 64) * Z * a.ksplit));
-  hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16>), grid, dim3(256), 0, s, a);
+  if (bg_fast<TA, TB>(a))
+    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   const size_t n = (size_t)Z * a.M * a.N;

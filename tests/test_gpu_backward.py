@@ -59,6 +59,9 @@ BASE = workloads.WORKLOADS
     BASE["flux_512"].with_(name="bw_bf16", B=2, H=3, N=300, L=20),
     BASE["flux_512"].with_(name="bw_bf16_d64", B=1, H=2, N=257, D=64, L=7, w_std=0.125),
     BASE["flux_512"].with_(name="bw_bf16_l0", B=1, H=2, N=190, L=0),
+    # whole row groups and K-steps (the products' unconditional-load variant) with a partial last tile
+    BASE["flux_512"].with_(name="bw_bf16_rows16", B=1, H=2, N=272, L=16),
+    BASE["tiny_fp32"].with_(name="bw_fp32_rows32", N=160, L=8),
 ], ids=lambda w: w.name)
 def test_backward_matches_oracle(w):
     _check(w)
