@@ -1076,46 +1076,57 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
 }
 
 // ---------------------------------------------------------------- distillation step
-// Per row (z, n), one wave: o = alpha lin + (1 - alpha) lm (lin alone when L == 0),
+// Per row (z, n), D / 4 lanes: o = alpha lin + (1 - alpha) lm (lin alone when L == 0),
 // t = the teacher row; dout = w1 clip(o - t, -1, 1) / numel - w2 dcos / rows (the
 // loss's gradient with respect to o, kept in registers), the row's huber sum
 // and 1 - cos; then the linear branch's row gradients from dout: dlin = alpha
 // dout, dnum = dlin / den, dden = -sum_d dlin lin / den, and the row's share of
 // dalpha, sum_d dout (lin - lm). w = exp(-s).
-__global__ void distill_loss_dlin_kernel(const float* lin, const float* lm, const float* teacher,
-                                         const uint16_t* teacher_bf16, const float* g, const float* sv,
-                                         const float* den_row, int H, int N, int D, int Z, int has_lm, float* hrow,
-                                         float* crow_, float* dnum, float* dden, float* rpart) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= Z * N) return;
+template <int D>
+__global__ __launch_bounds__(256) void distill_loss_dlin_kernel(const float* lin, const float* lm, const float* teacher,
+                                                                const uint16_t* teacher_bf16, const float* g,
+                                                                const float* sv, const float* den_row, int H, int N,
+                                                                int Z, int has_lm, float* hrow, float* crow_,
+                                                                float* dnum, float* dden, float* rpart) {
+  // A row is LPR lanes of 4 consecutive elements (16-byte loads and stores);
+  // a wave holds 64 / LPR rows, and the row sums stay within a row's lanes.
+  constexpr int LPR = D / 4, RPW = 64 / LPR;
+  static_assert(D % 4 == 0 && 64 % LPR == 0, "row layout");
+  const int lane = threadIdx.x & 63, l4 = lane % LPR;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int rows = Z * N;
+  const bool ok = row0 < rows;
+  const int row = ok ? row0 : rows - 1;  // (every lane takes part in the shuffles)
   const int h = (row / N) % H;
   const float alpha = has_lm ? 1.f / (1.f + expf(-g[h])) : 1.f;
   const float w1 = expf(-sv[0]), w2 = expf(-sv[1]);
-  const float inv_numel = 1.f / ((float)Z * N * D), inv_rows = 1.f / ((float)Z * N);
-  const size_t rb = (size_t)row * D;
-  float lv[4], mv[4], ov[4], tv[4];  // D <= 256: up to 4 elements per lane
+  const float inv_numel = 1.f / ((float)rows * D), inv_rows = 1.f / (float)rows;
+  const size_t at = (size_t)row * D + 4 * l4;
+  const f32x4 lv = *reinterpret_cast<const f32x4*>(lin + at);
+  const f32x4 mv = has_lm ? *reinterpret_cast<const f32x4*>(lm + at) : f32x4{};
+  f32x4 tv;
+  if (teacher_bf16) {
+    const uint2 b = *reinterpret_cast<const uint2*>(teacher_bf16 + at);
+    tv[0] = __uint_as_float(b.x << 16);
+    tv[1] = __uint_as_float(b.x & 0xffff0000u);
+    tv[2] = __uint_as_float(b.y << 16);
+    tv[3] = __uint_as_float(b.y & 0xffff0000u);
+  } else {
+    tv = *reinterpret_cast<const f32x4*>(teacher + at);
+  }
+  float ov[4];
   float hs = 0.f, dot = 0.f, oo = 0.f, tt = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = lane + 64 * j;
-    float l = 0.f, m = 0.f, o = 0.f, t = 0.f;
-    if (d < D) {
-      l = lin[rb + d];
-      m = has_lm ? lm[rb + d] : 0.f;
-      o = has_lm ? alpha * l + (1.f - alpha) * m : l;
-      t = teacher_bf16 ? bf2f(teacher_bf16[rb + d]) : teacher[rb + d];
-      const float r = o - t, ar = fabsf(r);
-      hs += ar <= 1.f ? 0.5f * r * r : ar - 0.5f;
-    }
-    lv[j] = l;
-    mv[j] = m;
-    ov[j] = o;
-    tv[j] = t;
-    dot += o * t;
+  for (int e = 0; e < 4; ++e) {
+    const float o = has_lm ? alpha * lv[e] + (1.f - alpha) * mv[e] : lv[e];
+    const float r = o - tv[e], ar = fabsf(r);
+    hs += ar <= 1.f ? 0.5f * r * r : ar - 0.5f;
+    ov[e] = o;
+    dot += o * tv[e];
     oo += o * o;
-    tt += t * t;
+    tt += tv[e] * tv[e];
   }
-  for (int off = 32; off > 0; off >>= 1) {
+  for (int off = LPR / 2; off > 0; off >>= 1) {
     hs += __shfl_xor(hs, off);
     dot += __shfl_xor(dot, off);
     oo += __shfl_xor(oo, off);
@@ -1128,24 +1139,23 @@ __global__ void distill_loss_dlin_kernel(const float* lin, const float* lm, cons
   const float co = live ? dot * nt / (no * cden * cden) : 0.f;
   const float inv = 1.f / den_row[row];
   float sd = 0.f, sa = 0.f;
+  f32x4 dn;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = lane + 64 * j;
-    if (d < D) {
-      const float r = ov[j] - tv[j];
-      const float dcos = tv[j] / cden - co * ov[j];
-      const float G = w1 * fminf(fmaxf(r, -1.f), 1.f) * inv_numel - w2 * dcos * inv_rows;
-      const float dl = alpha * G;
-      dnum[rb + d] = dl * inv;
-      sd += dl * lv[j];
-      if (has_lm) sa += G * (lv[j] - mv[j]);
-    }
+  for (int e = 0; e < 4; ++e) {
+    const float r = ov[e] - tv[e];
+    const float dcos = tv[e] / cden - co * ov[e];
+    const float G = w1 * fminf(fmaxf(r, -1.f), 1.f) * inv_numel - w2 * dcos * inv_rows;
+    const float dl = alpha * G;
+    dn[e] = dl * inv;
+    sd += dl * lv[e];
+    if (has_lm) sa += G * (lv[e] - mv[e]);
   }
-  for (int off = 32; off > 0; off >>= 1) {
+  if (ok) *reinterpret_cast<f32x4*>(dnum + at) = dn;
+  for (int off = LPR / 2; off > 0; off >>= 1) {
     sd += __shfl_xor(sd, off);
     sa += __shfl_xor(sa, off);
   }
-  if (lane == 0) {
+  if (ok && l4 == 0) {
     hrow[row] = hs;
     crow_[row] = 1.f - cosv;
     dden[row] = -sd * inv;
@@ -1318,8 +1328,17 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
   float* crw = reinterpret_cast<float*>(w8 + l.crow);
   float* gr = reinterpret_cast<float*>(w8 + l.grads);
   float *dW = gr, *db = gr + nW, *dg = db + nb, *ds = dg + H;
-  hipLaunchKernelGGL(distill_loss_dlin_kernel, dim3(blocks((size_t)Z * NQ, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
-                     g, sv, t.den, H, NQ, D, Z, L > 0 ? 1 : 0, hrow, crw, t.dnum, t.dden, t.rpart);
+  {
+    const size_t waves = ((size_t)Z * NQ + (256 / D) - 1) / (256 / D);  // 256 / D rows per wave
+    if (D == 128)
+      hipLaunchKernelGGL(distill_loss_dlin_kernel<128>, dim3(blocks(waves, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
+                         g, sv, t.den, H, NQ, Z, L > 0 ? 1 : 0, hrow, crw, t.dnum, t.dden, t.rpart);
+    else if (D == 64)
+      hipLaunchKernelGGL(distill_loss_dlin_kernel<64>, dim3(blocks(waves, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
+                         g, sv, t.den, H, NQ, Z, L > 0 ? 1 : 0, hrow, crw, t.dnum, t.dden, t.rpart);
+    else
+      return hipErrorInvalidValue;
+  }
   TTR_HIP(hipGetLastError());
   tm->mark();
   float* lpart = reinterpret_cast<float*>(w8 + l.lpart);
