@@ -610,47 +610,6 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
 }
 
 // ---------------------------------------------------------------- small kernels
-// Column sums with a fixed order, in two passes:
-//   out[z][f] = sum_{r < R} val(z, r, f)
-// row r of slice z at src + z * sz + (r / rb) * sblk + (r % rb) * F;
-//   MODE 0: val = phi(x); 1: phi(x) * wv[z * R + r]; 2: x + src2[same]; 3: x.
-// Pass 1 (grid Z x F/64 x NSPLIT): 64 columns by 4 row groups per workgroup,
-// each group a strided run of its split's rows, combined in group order.
-// Pass 2 adds the splits in order.
-constexpr int kColSplit = 32;
-template <int MODE>
-__global__ __launch_bounds__(256) void colsum_part_kernel(const float* src, const float* src2, const float* wv,
-                                                          long long sz, int rb, long long sblk, int R, int F,
-                                                          float* part) {
-  __shared__ float sh[4][64];
-  const int z = blockIdx.x, f = blockIdx.y * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6, sp = blockIdx.z;
-  const int per = (R + kColSplit - 1) / kColSplit, r0 = sp * per, r1 = min(R, r0 + per);
-  float acc = 0.f;
-  if (f < F) {
-    for (int r = r0 + grp; r < r1; r += 4) {
-      const size_t off = (size_t)z * sz + (size_t)(r / rb) * sblk + (size_t)(r % rb) * F + f;
-      const float x = src[off];
-      if constexpr (MODE == 0) acc += elu1(x);
-      else if constexpr (MODE == 1) acc += elu1(x) * wv[(size_t)z * R + r];
-      else if constexpr (MODE == 2) acc += x + src2[off];
-      else acc += x;
-    }
-  }
-  sh[grp][threadIdx.x & 63] = acc;
-  __syncthreads();
-  if (grp == 0 && f < F)
-    part[((size_t)z * kColSplit + sp) * F + f] = ((sh[0][threadIdx.x] + sh[1][threadIdx.x]) + sh[2][threadIdx.x]) +
-                                                 sh[3][threadIdx.x];
-}
-__global__ void colsum_final_kernel(const float* part, int Z, int F, float* out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= Z * F) return;
-  const int z = i / F, f = i % F;
-  float s = 0.f;
-  for (int sp = 0; sp < kColSplit; ++sp) s += part[((size_t)z * kColSplit + sp) * F + f];
-  out[i] = s;
-}
-
 // Column sums from the GEMM epilogues' half-tile partials, in a fixed order:
 // out[o][n] = sum_{b < nb} (sum_{t < t1} p1[(b zs + o)][t][n] + sum_{t < t2} p2[(b zs + o)][t][n])
 // (p2 may be NULL). Workgroup (x, o): columns 64 x .. 64 x + 63 of output row o;
@@ -664,8 +623,10 @@ __global__ __launch_bounds__(256) void tile_colsum_kernel(const float* p1, int t
   if (n < ncol) {
     for (int b = 0; b < nb; ++b) {
       const size_t zz = (size_t)b * zs + o;
+#pragma unroll 8
       for (int t = q; t < t1; t += 4) s += p1[(zz * t1 + t) * ncol + n];
       if (p2 != nullptr)
+#pragma unroll 8
         for (int t = q; t < t2; t += 4) s += p2[(zz * t2 + t) * ncol + n];
     }
   }
@@ -703,12 +664,29 @@ __global__ void dlin_kernel(const float* dout, const float* lin, const float* lm
   }
 }
 
-// dg[h] *= alpha (1 - alpha) (or 0 without the landmark branch)
-__global__ void dg_scale_kernel(float* dg, const float* g, int H, int has_lm) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
-  const float al = has_lm ? 1.f / (1.f + expf(-g[h])) : 0.f;
-  dg[h] = has_lm ? dg[h] * al * (1.f - al) : 0.f;
+// dg[h] = alpha (1 - alpha) sum_{b, n} rpart[(b H + h) NQ + n] (0 without
+// landmarks): one workgroup per head, each thread adds a strided run of the
+// rows in order, then a fixed-order tree over the threads.
+__global__ __launch_bounds__(256) void dg_kernel(const float* rpart, const float* g, int B, int H, int NQ,
+                                                 int has_lm, float* dg) {
+  __shared__ float sh[256];
+  const int h = blockIdx.x, t = threadIdx.x;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float* r = rpart + ((size_t)b * H + h) * NQ;
+#pragma unroll 8
+    for (int n = t; n < NQ; n += 256) s += r[n];
+  }
+  sh[t] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) sh[t] += sh[t + o];
+    __syncthreads();
+  }
+  if (t == 0) {
+    const float al = has_lm ? 1.f / (1.f + expf(-g[h])) : 0.f;
+    dg[h] = has_lm ? sh[0] * al * (1.f - al) : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------- launches
@@ -721,16 +699,6 @@ static hipError_t launch_tile_colsum(const float* p1, int t1, const float* p2, i
   return hipGetLastError();
 }
 
-template <int MODE>
-static hipError_t launch_colsum(const float* src, const float* src2, const float* wv, long long sz, int rb,
-                                long long sblk, int R, int Z, int F, float* part, float* out, hipStream_t s) {
-  hipLaunchKernelGGL((colsum_part_kernel<MODE>), dim3(Z, (F + 63) / 64, kColSplit), dim3(256), 0, s, src, src2, wv, sz,
-                     rb, sblk, R, F, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3(blocks((size_t)Z * F, 256)), dim3(256), 0, s, part, Z, F, out);
-  return hipGetLastError();
-}
 static hipError_t launch_dlin(const float* dout, const float* lin, const float* lm, const float* den, const float* g,
                               int H, int N, int D, int Z, bool has_lm, float* dnum, float* dden, float* rpart,
                               hipStream_t s) {
@@ -771,7 +739,6 @@ BackwardLayout backward_layout(const Problem& p) {
   l.den = take(Z * NQ);
   l.dden = take(Z * NQ);
   l.rpart = take(Z * NQ);
-  l.colpart = take(Z * kColSplit * F);
   // half-tile column partials of the GEMM epilogues: ksum then db (query rows), dks, db (key rows)
   const size_t cs = Z * (size_t)half_tiles((int)(N > NQ ? N : NQ)) * F;
   l.cs1 = take(cs);
@@ -793,7 +760,7 @@ BackwardLayout backward_layout(const Problem& p) {
 
 // Workspace views of the backward's fp32 intermediates.
 struct BwBufs {
-  float *zq, *zk, *dzq, *dzk, *lin, *lm, *dnum, *kv, *dkv, *ks, *dks, *den, *dden, *rpart, *colpart, *cs1, *cs2, *cs3,
+  float *zq, *zk, *dzq, *dzk, *lin, *lm, *dnum, *kv, *dkv, *ks, *dks, *den, *dden, *rpart, *cs1, *cs2, *cs3,
       *splitk;
   size_t splitk_n;
 };
@@ -803,7 +770,7 @@ static BwBufs bw_bufs(const Problem& p, void* ws) {
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w8 + off); };
   return BwBufs{F32(l.zq),  F32(l.zk),  F32(l.dzq),  F32(l.dzk),   F32(l.lin),     F32(l.lm),
                 F32(l.dnum), F32(l.kv),  F32(l.dkv),  F32(l.ks),    F32(l.dks),     F32(l.den),
-                F32(l.dden), F32(l.rpart), F32(l.colpart), F32(l.cs1), F32(l.cs2), F32(l.cs3),
+                F32(l.dden), F32(l.rpart), F32(l.cs1), F32(l.cs2), F32(l.cs3),
                 F32(l.splitk), splitk_elems(p)};
 }
 
@@ -1060,8 +1027,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
   tm->mark();
   // db[h] over rows (b, n) of slice h; dg[h] from the row shares of dalpha
   TTR_HIP(launch_tile_colsum(t.cs1, half_tiles(NQ), t.cs3, half_tiles(N), B, H, F, H, db, s));
-  TTR_HIP(launch_colsum<3>(rpart, nullptr, nullptr, NQ, NQ, (long long)H * NQ, B * NQ, H, 1, t.colpart, dg, s));
-  hipLaunchKernelGGL(dg_scale_kernel, dim3(blocks(H, 64)), dim3(64), 0, s, dg, g, H, L > 0 ? 1 : 0);
+  hipLaunchKernelGGL(dg_kernel, dim3(H), dim3(256), 0, s, rpart, g, B, H, NQ, L > 0 ? 1 : 0, dg);
   TTR_HIP(hipGetLastError());
   tm->mark();
   return hipSuccess;

@@ -118,7 +118,7 @@ hipError_t launch_proj_gemm(int dtype, bool a_heads, bool c_qkv, const void* A, 
 // k_backward.hip: gradients of the hybrid forward for W, b, g (fp32
 // intermediates in the workspace, byte offsets below).
 struct BackwardLayout {
-  size_t zq, zk, dzq, dzk, lin, lm, dnum, kv, dkv, ks, dks, den, dden, rpart, colpart, cs1, cs2, cs3, splitk, bytes;
+  size_t zq, zk, dzq, dzk, lin, lm, dnum, kv, dkv, ks, dks, den, dden, rpart, cs1, cs2, cs3, splitk, bytes;
 };
 BackwardLayout backward_layout(const Problem& p);
 hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K, const void* V, const void* W,
