@@ -435,7 +435,8 @@ def distill_plan(w, nq=None):
         plan += [("ksum (tile sums of the z_k epilogue)", 0, 0), ("bgemm KV = phi_k^T V", gk, 0)]
     plan += [("bgemm lin = phi_q KV / den, den = phi_q . ks + eps (normaliser formed from the staged rows)", gq, 0)]
     if L > 0:
-        plan.append(("landmark branch (hybrid_kernel)", 4 * Z * NQ * L * D, 0))
+        plan.append(("landmark branch (landmark pack + fused query kernel's landmark loop, fp32 out)"
+                     if w.dtype == "bf16" else "landmark branch (hybrid_kernel)", 4 * Z * NQ * L * D, 0))
     plan += [("loss rows and dnum, dden (distill_loss_dlin_kernel)", 0, 0), ("distill_loss_total_kernel", 0, 0),
              ("bgemm dz_q = (dnum KV^T + dden ks^T) phi'(z_q)", gq, 0), ("bgemm dKV = phi_q^T dnum", gq, 0),
              ("dks (tile sums of the dz_q epilogue)", 0, 0), ("bgemm dz_k = (V dKV^T + dks) phi'(z_k)", gk, 0),

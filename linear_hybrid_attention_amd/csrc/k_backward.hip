@@ -707,6 +707,14 @@ static hipError_t launch_dlin(const float* dout, const float* lin, const float* 
   return hipGetLastError();
 }
 // ---------------------------------------------------------------- host side
+// bf16 at D = 64 or 128 with L <= N: the student's landmark branch runs the
+// fused query kernel's landmark loop (fp32 output; the store resource covers a
+// slice; the workspace holds a pack of up to N landmarks).
+static bool lm_fused(const Problem& p, int L) {
+  return p.dtype == 1 && (p.D == 64 || p.D == 128) && L >= 1 && L <= p.N &&
+         (size_t)query_rows(p) * p.D * 4 < ((size_t)1 << 32);
+}
+
 // bf16 with the elu + 1 projection at D = 64 or 128: KV and ksum come from the
 // forward's key/value kernel (split partials over the keys, a fixed-order sum).
 static bool kv_from_keys(const Problem& p) {
@@ -747,6 +755,8 @@ BackwardLayout backward_layout(const Problem& p) {
   // split-K partials, or (bf16 with the projection) the key/value kernel's split partials and W^T chunks
   size_t sk = splitk_elems(p);
   if (kv_from_keys(p)) sk = std::max(sk, (kv2_reduce_workspace_bytes(p) + 3) / 4);
+  // (and the landmark pack of the student's landmark branch; the largest L is N)
+  if (lm_fused(p, p.N)) sk = std::max(sk, (lm_pack_bytes(p, p.N) + 3) / 4);
   l.splitk = take(sk);
   l.bytes = o;
   return l;
@@ -880,8 +890,17 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s));
     tm->mark();
   }
-  // landmark branch output (fp32), for dalpha
-  if (L > 0) {
+  // landmark branch output (fp32), for dalpha. bf16: a pack of the L landmarks
+  // (strided over the N keys) in the split-K scratch, free at this point, and
+  // the fused query kernel's landmark loop alone with an fp32 output.
+  if (L > 0 && lm_fused(p, L)) {
+    FusedPack pk;
+    TTR_HIP(launch_lm_pack(p, K, V, L, t.splitk, &pk, s));
+    Problem pq = p;
+    pq.N = NQ;
+    TTR_HIP(launch_softmax_query_f32(pq, Q, pk, L, lm, s));
+    tm->mark();
+  } else if (L > 0) {
     HybridArgs ha = {};
     ha.Q = Q;
     ha.K = K;

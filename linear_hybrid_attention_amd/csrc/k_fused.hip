@@ -40,11 +40,13 @@ struct FusedArgs {
   float eps;
   int H, N, L, ntiles, nwg;
   uint16_t* out;
+  float* out32;  // OUT32: the output in fp32 instead
 };
 
 // LIN = false: softmax attention over the landmarks alone, out = o / l (the
 // pack then holds only the landmark chunks; no linear branch, no blend).
-template <int D, int F, int MAP, bool LIN = true>
+// OUT32: the output in fp32 (out32).
+template <int D, int F, int MAP, bool LIN = true, bool OUT32 = false>
 __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   constexpr int CH = 64 * D;  // elements per chunk (every chunk kind)
   constexpr int NFC = F / 64;
@@ -375,6 +377,37 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   // free after the last barrier) so that the global stores are whole 16-byte
   // pieces, four full rows per store instruction.
   const float cb = !LIN ? 1.f / l : L > 0 ? (1.f - 1.f / (1.f + expf(-gh))) / l : 0.f;
+  if constexpr (OUT32) {
+    // the wave's [32 tokens][D] fp32 tile: rows of 4 D bytes swizzled as bf16
+    // rows of 2 D columns (a 16-byte piece is 4 floats), 16-byte stores
+    uint16_t* ot = slots + w * 32 * 2 * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (LIN ? num[db][4 * q + j] : 0.f) + cb * o[db][4 * q + j];
+        *reinterpret_cast<f32x4*>(ot + toff<2 * D, kRowRead>(c, 2 * (db * 32 + 8 * q + 4 * g))) = v;
+      }
+    wave_lds_order();
+    constexpr int PPR = D / 4, NP32 = 32 * PPR / 64;  // pieces per row, per lane
+    const uint32_t bytes32 = (uint32_t)((size_t)N * D * 4);  // (the launch checks it fits 32 bits)
+    const __amdgpu_buffer_rsrc_t r32 = buffer_rsrc(a.out32 + (size_t)bh * N * D, bytes32);
+    u32x4 v32[NP32];
+#pragma unroll
+    for (int i = 0; i < NP32; ++i) {
+      const int P = 64 * i + lane, row = P / PPR, pc = P % PPR;
+      v32[i] = *reinterpret_cast<const u32x4*>(ot + toff<2 * D, kRowRead>(row, pc * 8));
+    }
+#pragma unroll
+    for (int i = 0; i < NP32; ++i) {
+      const int P = 64 * i + lane, row = P / PPR, pc = P % PPR;
+      const int n = tile * 128 + 32 * w + row;
+      store16(r32, n < N ? (uint32_t)(n * D + pc * 4) * 4 : bytes32, v32[i]);
+    }
+    return;
+  }
   uint16_t* ot = slots + w * 32 * D;  // [32 tokens][D], kRowRead swizzle
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -407,9 +440,9 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   }
 }
 
-template <int D, int F, int MAP, bool LIN = true>
+template <int D, int F, int MAP, bool LIN = true, bool OUT32 = false>
 static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((fused_query_kernel<D, F, MAP, LIN>), dim3(a.nwg), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fused_query_kernel<D, F, MAP, LIN, OUT32>), dim3(a.nwg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -428,6 +461,23 @@ hipError_t launch_softmax_query(const Problem& p, const void* Q, const FusedPack
   a.out = static_cast<uint16_t*>(out);
   // (F and the map do not enter the landmark-only variant)
   return p.D == 128 ? launch_fused_t<128, 64, kElu1, false>(a, s) : launch_fused_t<64, 64, kElu1, false>(a, s);
+}
+
+hipError_t launch_softmax_query_f32(const Problem& p, const void* Q, const FusedPack& pk, int L, float* out,
+                                    hipStream_t s) {
+  if (p.dtype != 1 || L < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
+  if ((size_t)p.N * p.D * 4 >= ((size_t)1 << 32)) return hipErrorInvalidValue;  // the store resource's size
+  FusedArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.pack_bh = pk.pack_bh;
+  a.bh_bytes = pk.bh_bytes;
+  a.H = p.H;
+  a.N = p.N;
+  a.L = L;
+  a.ntiles = (p.N + 127) / 128;
+  a.nwg = a.ntiles * p.B * p.H;
+  a.out32 = out;
+  return p.D == 128 ? launch_fused_t<128, 64, kElu1, false, true>(a, s) : launch_fused_t<64, 64, kElu1, false, true>(a, s);
 }
 
 hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& pk, const float* g, float eps,

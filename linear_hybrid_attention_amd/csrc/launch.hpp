@@ -84,6 +84,9 @@ hipError_t launch_lm_pack(const Problem& p, const void* K, const void* V, int L,
                           hipStream_t s);
 hipError_t launch_softmax_query(const Problem& p, const void* Q, const FusedPack& pk, int L, void* out,
                                 hipStream_t s);
+// The same with an fp32 output (N D 4 bytes per slice must fit 32 bits).
+hipError_t launch_softmax_query_f32(const Problem& p, const void* Q, const FusedPack& pk, int L, float* out,
+                                    hipStream_t s);
 hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& pk, const float* g, float eps,
                               int L, void* out, hipStream_t s);
 // The key/value reduction alone on the bf16 path (ttr_kv_reduce): the partial
