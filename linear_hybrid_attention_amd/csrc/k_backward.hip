@@ -251,6 +251,18 @@ struct BgStage {
       for (int i = 0; i < ROWS / 8; ++i) v[i] = elu1(v[i]);
   }
   __device__ __forceinline__ void store(CT* tile, bool kc, int tid) const { bg_store<CT, ROWS>(tile, v, kc, tid); }
+  // (a row-strided operand into a bf16 tile stored [k][row], kTrRead layout:
+  // the thread's NE consecutive rows at its k are whole 16-byte pieces)
+  __device__ __forceinline__ void store_tr(uint16_t* tile, int tid) const {
+    using G = BgGeo<ROWS>;
+#pragma unroll
+    for (int u = 0; u < G::NE / 8; ++u) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(v[8 * u + 2 * j], v[8 * u + 2 * j + 1]);
+      *reinterpret_cast<u32x4*>(tile + toff<ROWS, kTrRead>(G::nk_k(tid), G::nk_row(tid) + 8 * u)) = w;
+    }
+  }
 };
 template <int ROWS>
 struct BgStage<uint16_t, uint16_t, false, ROWS> {
@@ -267,6 +279,12 @@ struct BgStage<uint16_t, uint16_t, false, ROWS> {
   }
   __device__ __forceinline__ void store(uint16_t* tile, bool kc, int tid) const {
     bg_store_raw<ROWS>(tile, v, kc, tid);
+  }
+  __device__ __forceinline__ void store_tr(uint16_t* tile, int tid) const {
+    using G = BgGeo<ROWS>;
+#pragma unroll
+    for (int u = 0; u < G::NE / 8; ++u)
+      *reinterpret_cast<u32x4*>(tile + toff<ROWS, kTrRead>(G::nk_k(tid), G::nk_row(tid) + 8 * u)) = v[u];
   }
 };
 
@@ -287,7 +305,7 @@ __device__ __forceinline__ int bg_item(int i, int n) {
 // row's k run of a step) and divides the row (never with split-K).
 constexpr int kDenMaxK = 512;  // the normaliser's K (the feature count) at most
 template <typename CT, typename TA, typename TB, bool A_ELU, int EPI, bool DEN = false, bool O16 = false,
-          bool FAST = false>
+          bool FAST = false, bool TT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4))) void bgemm_kernel(BgemmArgs a) {
   constexpr int TM = BgTile<CT>::TM, TN = BgTile<CT>::TN, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
   __shared__ __attribute__((aligned(16))) CT As[TM * LD];
@@ -342,16 +360,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
         for (int i = 0; i < 4; ++i) dpart += va.v[4 * q + i] * kv[i];
       }
     }
-    va.store(As, a_kc, tid);
-    vb.store(Bs, b_kc, tid);
+    if constexpr (TT) {  // both operands row-strided: [k][row] tiles
+      va.store_tr(As, tid);
+      vb.store_tr(Bs, tid);
+    } else {
+      va.store(As, a_kc, tid);
+      vb.store(Bs, b_kc, tid);
+    }
     __syncthreads();
     if (s + 1 < total) load(s + 1);  // in flight during the products
 #pragma unroll
     for (int kb = 0; kb < KT / 16; ++kb) {
-      const Frag<CT> fa = ld_frag<CT>(As + (w * 32 + c) * LD + kb * 16 + 8 * g);
-      Frag<CT> fb[2];
+      Frag<CT> fa, fb[2];
+      if constexpr (TT) {  // transposed reads: both fragments hold k in the same (C-row) order
+        fa = tr_frag<TM>(As, kb * 16, w * 32, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = ld_frag<CT>(Bs + (j * 32 + c) * LD + kb * 16 + 8 * g);
+        for (int j = 0; j < 2; ++j) fb[j] = tr_frag<TN>(Bs, kb * 16, j * 32, lane);
+      } else {
+        fa = ld_frag<CT>(As + (w * 32 + c) * LD + kb * 16 + 8 * g);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = ld_frag<CT>(Bs + (j * 32 + c) * LD + kb * 16 + 8 * g);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) mma(acc[j], fa, fb[j]);
     }
@@ -520,13 +549,14 @@ static bool bg_fast(const BgemmArgs& a) {
          (b_kc || (a.N >= 8 && a.N % 8 == 0));
 }
 
-template <typename CT, typename TA, typename TB, bool ELU, int EPI = 0, bool DEN = false, bool O16 = false>
+template <typename CT, typename TA, typename TB, bool ELU, int EPI = 0, bool DEN = false, bool O16 = false,
+          bool TT = false>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
   const dim3 grid((unsigned)(((a.M + 127) / 128) * ((a.N + 63) / 64) * Z * a.ksplit));
   if (bg_fast<TA, TB>(a))
-    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, true, TT>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, false, TT>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   const size_t n = (size_t)Z * a.M * a.N;
@@ -540,7 +570,7 @@ static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
 static size_t splitk_elems(const Problem& p) { return (size_t)16 * p.B * p.H * p.F * p.D; }
 
 // A grid of few tiles with a long reduction splits K (at most 16 ways, at
-// least 8 steps each, aiming at about 2048 workgroups), when `scratch` holds
+// least 8 steps each, aiming at about 1024 workgroups), when `scratch` holds
 // the partial products.
 static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, const BgemmArgs& a0, int Z, hipStream_t s,
                                float* scratch = nullptr, size_t scratch_elems = 0) {
@@ -551,7 +581,7 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   const int tiles = ((a.M + 127) / 128) * ((a.N + 63) / 64) * Z;
   const int steps = a.KB * ((a.K + 31) / 32);
   if (scratch != nullptr && tiles < 512 && steps >= 32) {
-    int ks = min(16, max(1, 2048 / tiles));
+    int ks = min(16, max(1, 1024 / tiles));
     ks = min(ks, steps / 8);
     while (ks > 1 && (size_t)ks * Z * a.M * a.N > scratch_elems) --ks;
     if (ks > 1) {
@@ -596,6 +626,12 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
     if (epi == 2) return launch_bgemm_t<float, float, float, false, 2>(a, Z, s);
     return launch_bgemm_t<float, float, float, false, 3>(a, Z, s);
   }
+  // bf16 products whose operands are both row-strided (dW, dKV) stage them as
+  // [k][row] tiles read by transposing LDS reads: whole 16-byte stores instead
+  // of scattered 2-byte ones
+  const bool tt = a.sAk != 1 && a.sBk != 1;
+  if (dtype == 1 && tt && a_io && b_io && !a_elu) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 0, false, false, true>(a, Z, s);
+  if (dtype == 1 && tt && !a_io && !b_io && a_elu) return launch_bgemm_t<uint16_t, float, float, true, 0, false, false, true>(a, Z, s);
   if (dtype == 1) {
     if (a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false>(a, Z, s);
     if (a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false>(a, Z, s);
