@@ -305,7 +305,7 @@ __device__ __forceinline__ int bg_item(int i, int n) {
 // row's k run of a step) and divides the row (never with split-K).
 constexpr int kDenMaxK = 512;  // the normaliser's K (the feature count) at most
 template <typename CT, typename TA, typename TB, bool A_ELU, int EPI, bool DEN = false, bool O16 = false,
-          bool FAST = false, bool TT = false>
+          bool FAST = false, bool TT = false, bool BT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4))) void bgemm_kernel(BgemmArgs a) {
   constexpr int TM = BgTile<CT>::TM, TN = BgTile<CT>::TN, KT = BgTile<CT>::KT, LD = BgTile<CT>::LD;
   __shared__ __attribute__((aligned(16))) CT As[TM * LD];
@@ -363,6 +363,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
     if constexpr (TT) {  // both operands row-strided: [k][row] tiles
       va.store_tr(As, tid);
       vb.store_tr(Bs, tid);
+    } else if constexpr (BT) {  // B row-strided: its tile [k][row]; A's as usual
+      va.store(As, true, tid);
+      vb.store_tr(Bs, tid);
     } else {
       va.store(As, a_kc, tid);
       vb.store(Bs, b_kc, tid);
@@ -374,6 +377,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
       Frag<CT> fa, fb[2];
       if constexpr (TT) {  // transposed reads: both fragments hold k in the same (C-row) order
         fa = tr_frag<TM>(As, kb * 16, w * 32, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = tr_frag<TN>(Bs, kb * 16, j * 32, lane);
+      } else if constexpr (BT) {  // A's k values in that order: k0 + 4g .. + 3, then k0 + 8 + 4g .. + 3
+        const uint16_t* ap = As + (w * 32 + c) * LD + kb * 16 + 4 * g;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(ap), hi = *reinterpret_cast<const u32x2*>(ap + 8);
+        fa = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int j = 0; j < 2; ++j) fb[j] = tr_frag<TN>(Bs, kb * 16, j * 32, lane);
       } else {
@@ -550,13 +559,13 @@ static bool bg_fast(const BgemmArgs& a) {
 }
 
 template <typename CT, typename TA, typename TB, bool ELU, int EPI = 0, bool DEN = false, bool O16 = false,
-          bool TT = false>
+          bool TT = false, bool BT = false>
 static hipError_t launch_bgemm_t(const BgemmArgs& a, int Z, hipStream_t s) {
   const dim3 grid((unsigned)(((a.M + 127) / 128) * ((a.N + 63) / 64) * Z * a.ksplit));
   if (bg_fast<TA, TB>(a))
-    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, true, TT>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, true, TT, BT>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, false, TT>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bgemm_kernel<CT, TA, TB, ELU, EPI, DEN, O16, false, TT, BT>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   const size_t n = (size_t)Z * a.M * a.N;
@@ -612,6 +621,8 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   if (o16 && ((epi != 1 && epi != 2) || dtype != 1)) return hipErrorInvalidValue;
   if (a.den_ks != nullptr) {  // phi(fp32 A) rows, k contiguous, fp32 B
     if (epi != 0 || !a_elu || a_io || b_io || a.sAk != 1 || a.K > kDenMaxK || a.KB != 1) return hipErrorInvalidValue;
+    if (dtype == 1 && a.sBk != 1)  // B row-strided (lin: KV)
+      return launch_bgemm_t<uint16_t, float, float, true, 0, true, false, false, true>(a, Z, s);
     return dtype == 1 ? launch_bgemm_t<uint16_t, float, float, true, 0, true>(a, Z, s)
                       : launch_bgemm_t<float, float, float, true, 0, true>(a, Z, s);
   }
@@ -632,6 +643,9 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   const bool tt = a.sAk != 1 && a.sBk != 1;
   if (dtype == 1 && tt && a_io && b_io && !a_elu) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 0, false, false, true>(a, Z, s);
   if (dtype == 1 && tt && !a_io && !b_io && a_elu) return launch_bgemm_t<uint16_t, float, float, true, 0, false, false, true>(a, Z, s);
+  // B alone row-strided (z = X W + b): its tile [k][row], A's fragments read in the same k order
+  if (dtype == 1 && epi == 0 && a.sAk == 1 && a.sBk != 1 && a_io && b_io && !a_elu)
+    return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 0, false, false, false, true>(a, Z, s);
   if (dtype == 1) {
     if (a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false>(a, Z, s);
     if (a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false>(a, Z, s);
