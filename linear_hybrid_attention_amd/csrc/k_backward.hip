@@ -629,6 +629,7 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   if (epi != 0) {
     if (dtype == 1) {
       if (epi == 1 && o16 && !a_io && !b_io) return launch_bgemm_t<uint16_t, float, float, false, 1, false, true>(a, Z, s);
+      if (epi == 1 && o16 && a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false, 1, false, true>(a, Z, s);
       if (epi == 2 && o16 && a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false, 2, false, true>(a, Z, s);
       if (epi == 3 && a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 3>(a, Z, s);
       return hipErrorInvalidValue;
@@ -643,6 +644,7 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   const bool tt = a.sAk != 1 && a.sBk != 1;
   if (dtype == 1 && tt && a_io && b_io && !a_elu) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 0, false, false, true>(a, Z, s);
   if (dtype == 1 && tt && !a_io && !b_io && a_elu) return launch_bgemm_t<uint16_t, float, float, true, 0, false, false, true>(a, Z, s);
+  if (dtype == 1 && tt && !a_io && b_io && a_elu) return launch_bgemm_t<uint16_t, float, uint16_t, true, 0, false, false, true>(a, Z, s);
   // B alone row-strided (z = X W + b): its tile [k][row], A's fragments read in the same k order
   if (dtype == 1 && epi == 0 && a.sAk == 1 && a.sBk != 1 && a_io && b_io && !a_elu)
     return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 0, false, false, false, true>(a, Z, s);
@@ -689,7 +691,8 @@ __global__ __launch_bounds__(256) void tile_colsum_kernel(const float* p1, int t
 // Per row: dlin = alpha dout; dnum = dlin / den; dden = -sum_d dlin lin / den;
 // and the row's share of dalpha: sum_d dout (lin - lm) (into rpart[row]).
 __global__ void dlin_kernel(const float* dout, const float* lin, const float* lm, const float* den, const float* g,
-                            int H, int N, int D, int Z, int has_lm, float* dnum, float* dden, float* rpart) {
+                            int H, int N, int D, int Z, int has_lm, float* dnum, uint16_t* dnum16, float* dden,
+                            float* rpart) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= Z * N) return;
   const int h = (row / N) % H;
@@ -700,7 +703,8 @@ __global__ void dlin_kernel(const float* dout, const float* lin, const float* lm
   float sd = 0.f, sa = 0.f;
   for (int d = lane; d < D; d += 64) {
     const float dl = alpha * G[d];
-    dnum[(size_t)row * D + d] = dl * inv;
+    if (dnum16) dnum16[(size_t)row * D + d] = f2bf(dl * inv);
+    else dnum[(size_t)row * D + d] = dl * inv;
     sd += dl * li[d];
     if (has_lm) sa += G[d] * (li[d] - lm[(size_t)row * D + d]);
   }
@@ -750,10 +754,11 @@ static hipError_t launch_tile_colsum(const float* p1, int t1, const float* p2, i
 }
 
 static hipError_t launch_dlin(const float* dout, const float* lin, const float* lm, const float* den, const float* g,
-                              int H, int N, int D, int Z, bool has_lm, float* dnum, float* dden, float* rpart,
+                              int H, int N, int D, int Z, bool has_lm, float* dnum, uint16_t* dnum16, float* dden,
+                              float* rpart,
                               hipStream_t s) {
   hipLaunchKernelGGL(dlin_kernel, dim3(blocks((size_t)Z * N, 4)), dim3(256), 0, s, dout, lin, lm, den, g, H, N, D, Z,
-                     has_lm ? 1 : 0, dnum, dden, rpart);
+                     has_lm ? 1 : 0, dnum, dnum16, dden, rpart);
   return hipGetLastError();
 }
 // ---------------------------------------------------------------- host side
@@ -789,7 +794,9 @@ BackwardLayout backward_layout(const Problem& p) {
   l.dzk = take((Z * N * F * dz_el + 3) / 4);
   l.lin = take(Z * NQ * D);
   l.lm = take(Z * NQ * D);
-  l.dnum = take(Z * NQ * D);
+  // dnum: bf16 on the bf16 path (its readers, the dz_q and dKV products, stage
+  // it as a bf16 operand), else fp32
+  l.dnum = take((Z * NQ * D * (p.dtype == 1 ? 2 : 4) + 3) / 4);
   l.kv = take(Z * F * D);
   l.dkv = take(Z * F * D);
   l.ks = take(Z * F);
@@ -981,7 +988,8 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
   const long long QF = (long long)NQ * F, QD = (long long)NQ * D;
   // dnum, dden, dalpha row shares (one per query row)
   if (dout != nullptr) {  // (NULL: the caller has formed them)
-    TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, NQ, D, Z, L > 0, dnum, dden, rpart, s));
+    TTR_HIP(launch_dlin(dout, lin, lm, den, g, H, NQ, D, Z, L > 0, dt == 1 ? nullptr : dnum,
+                        dt == 1 ? reinterpret_cast<uint16_t*>(dnum) : nullptr, dden, rpart, s));
     tm->mark();
   }
   // dz_q = (dnum KV^T + dden ks^T) phi'(z_q): [Nq x D] . [D x F], the rest in the epilogue
@@ -1011,7 +1019,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCz = QF;
     a.sCm = F;
     a.sCn = 1;
-    TTR_HIP(launch_bgemm(dt, false, false, false, a, Z, s));
+    TTR_HIP(launch_bgemm(dt, dt == 1, false, false, a, Z, s));  // dnum in the IO dtype
     tm->mark();
   }
   // dKV = phi(z_q)^T dnum: [F x N] . [N x D]; dks = phi(z_q)^T dden
@@ -1033,7 +1041,7 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCz = FD;
     a.sCm = D;
     a.sCn = 1;
-    TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s, t.splitk, t.splitk_n));
+    TTR_HIP(launch_bgemm(dt, false, dt == 1, true, a, Z, s, t.splitk, t.splitk_n));  // dnum in the IO dtype
     tm->mark();
   }
   TTR_HIP(launch_tile_colsum(t.cs2, half_tiles(NQ), nullptr, 0, 1, 0, F, Z, dks, s));
@@ -1117,7 +1125,7 @@ hipError_t launch_hybrid_backward(const Problem& p, const void* Q, const void* K
 // and 1 - cos; then the linear branch's row gradients from dout: dlin = alpha
 // dout, dnum = dlin / den, dden = -sum_d dlin lin / den, and the row's share of
 // dalpha, sum_d dout (lin - lm). w = exp(-s).
-template <int D>
+template <int D, bool DN16>
 __global__ __launch_bounds__(256) void distill_loss_dlin_kernel(const float* lin, const float* lm, const float* teacher,
                                                                 const uint16_t* teacher_bf16, const float* g,
                                                                 const float* sv, const float* den_row, int H, int N,
@@ -1185,7 +1193,16 @@ __global__ __launch_bounds__(256) void distill_loss_dlin_kernel(const float* lin
     sd += dl * lv[e];
     if (has_lm) sa += G * (lv[e] - mv[e]);
   }
-  if (ok) *reinterpret_cast<f32x4*>(dnum + at) = dn;
+  if (ok) {
+    if constexpr (DN16) {  // the bf16 path keeps dnum in bf16
+      uint2 b;
+      b.x = pack_bf16x2(dn[0], dn[1]);
+      b.y = pack_bf16x2(dn[2], dn[3]);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dnum) + at) = b;
+    } else {
+      *reinterpret_cast<f32x4*>(dnum + at) = dn;
+    }
+  }
   for (int off = LPR / 2; off > 0; off >>= 1) {
     sd += __shfl_xor(sd, off);
     sa += __shfl_xor(sa, off);
@@ -1365,14 +1382,15 @@ hipError_t launch_distill_step(const Problem& p, const void* Q, const void* K, c
   float *dW = gr, *db = gr + nW, *dg = db + nb, *ds = dg + H;
   {
     const size_t waves = ((size_t)Z * NQ + (256 / D) - 1) / (256 / D);  // 256 / D rows per wave
-    if (D == 128)
-      hipLaunchKernelGGL(distill_loss_dlin_kernel<128>, dim3(blocks(waves, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
-                         g, sv, t.den, H, NQ, Z, L > 0 ? 1 : 0, hrow, crw, t.dnum, t.dden, t.rpart);
-    else if (D == 64)
-      hipLaunchKernelGGL(distill_loss_dlin_kernel<64>, dim3(blocks(waves, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb,
-                         g, sv, t.den, H, NQ, Z, L > 0 ? 1 : 0, hrow, crw, t.dnum, t.dden, t.rpart);
-    else
-      return hipErrorInvalidValue;
+    // (dnum in the IO dtype: bf16 on the bf16 path)
+    auto launch = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(blocks(waves, 4)), dim3(256), 0, s, t.lin, t.lm, T, Tb, g, sv, t.den, H, NQ, Z,
+                         L > 0 ? 1 : 0, hrow, crw, t.dnum, t.dden, t.rpart);
+    };
+    const bool b16 = p.dtype == 1;
+    if (D == 128) b16 ? launch(distill_loss_dlin_kernel<128, true>) : launch(distill_loss_dlin_kernel<128, false>);
+    else if (D == 64) b16 ? launch(distill_loss_dlin_kernel<64, true>) : launch(distill_loss_dlin_kernel<64, false>);
+    else return hipErrorInvalidValue;
   }
   TTR_HIP(hipGetLastError());
   tm->mark();
