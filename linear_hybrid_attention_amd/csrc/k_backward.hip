@@ -40,6 +40,7 @@ struct BgemmArgs {
   // optional dz epilogue (no split-K): C(m, n) = (acc + r(m) s(n)) phi'(x(m, n)), phi = elu + 1,
   // x = dz_x laid out like C, r = dz_r[z * dz_srz + m] (1 when NULL), s = dz_s[z * dz_ssz + n]
   const float* dz_x;
+  const uint16_t* dz_phi;  // (EPI 5, 6) instead of dz_x: phi(x) in bf16; phi'(x) = min(phi(x), 1)
   const float* dz_r;
   const float* dz_s;
   long long dz_srz, dz_ssz;
@@ -51,6 +52,7 @@ struct BgemmArgs {
   float* cs_phi;
   // optional (epilogue variants, beta = 0): the output rounded to bf16 here instead of C
   uint16_t* C16;
+  int phi_out;  // (epilogue variant 4) the output is phi(acc + bias) in bf16, into C16
   // optional normaliser (no split-K; A = phi(x) rows, k contiguous): den(m) = sum_k A(m, k)
   // den_ks[z * den_ksz + k] + den_eps, written to den_out[z * den_oz + m] by the first N
   // tile, and C(m, n) = acc / den(m)
@@ -239,6 +241,7 @@ __device__ __forceinline__ const T* bg_fast_ptr(const T* base, long long s_row, 
 template <typename CT, typename T, bool ELU, int ROWS>
 struct BgStage {
   float v[ROWS / 8];
+  __device__ __forceinline__ float val(int i) const { return v[i]; }
   __device__ __forceinline__ void load(const T* base, long long s_row, long long s_k, int row0, int nrows, int k0,
                                        int K, bool kc, bool vec, int tid) {
     bg_load<T, ELU, ROWS>(v, base, s_row, s_k, row0, nrows, k0, K, kc, vec, tid);
@@ -267,6 +270,10 @@ struct BgStage {
 template <int ROWS>
 struct BgStage<uint16_t, uint16_t, false, ROWS> {
   u32x4 v[ROWS / 64];
+  __device__ __forceinline__ float val(int i) const {
+    const uint32_t w = v[i >> 3][(i & 7) >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
   __device__ __forceinline__ void load(const uint16_t* base, long long s_row, long long s_k, int row0, int nrows,
                                        int k0, int K, bool kc, bool vec, int tid) {
     bg_load_raw<ROWS>(v, base, s_row, s_k, row0, nrows, k0, K, kc, vec, tid);
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
       for (int q = 0; q < 4; ++q) {
         const f32x4 kv = kp[q];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dpart += va.v[4 * q + i] * kv[i];
+        for (int i = 0; i < 4; ++i) dpart += va.val(4 * q + i) * kv[i];
       }
     }
     if constexpr (TT) {  // both operands row-strided: [k][row] tiles
@@ -448,12 +455,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
   // Epilogue with the dz products and column sums (no split-K, beta = 0), its
   // terms fixed by EPI: 1: dz with the row factor r = dz_r, the column sums of
   // dz (cs_val) and of phi(x) r (cs_phir); 2: dz with r = 1 and the column sums
-  // of dz; 3: the column sums of phi of the output (cs_phi). O16: the output
-  // rounded to bf16 into C16. Offsets within a z slice are 32-bit (the host
+  // of dz; 3: the column sums of phi of the output (cs_phi); 4: phi of the
+  // output (with O16); 5, 6: as 1, 2 with the dz operand given as phi(x) in
+  // bf16 (dz_phi). O16: the output rounded to bf16 into C16. Offsets within a z slice are 32-bit (the host
   // checks the slice's extent); full tiles store without row checks.
-  constexpr bool DZ = EPI == 1 || EPI == 2, HAS_R = EPI == 1, CSV = DZ, CSR = EPI == 1, CSQ = EPI == 3;
+  constexpr bool XP = EPI == 5 || EPI == 6;  // the dz operand is phi(x) in bf16
+  constexpr bool DZ = EPI == 1 || EPI == 2 || XP, HAS_R = EPI == 1 || EPI == 5, CSV = DZ,
+                 CSR = HAS_R, CSQ = EPI == 3, PHI_OUT = EPI == 4;
   const long long zo = (long long)z * a.sCz;
-  const float* __restrict__ dzx = DZ ? a.dz_x + zo : nullptr;
+  const float* __restrict__ dzx = DZ && !XP ? a.dz_x + zo : nullptr;
+  const uint16_t* __restrict__ dzp = XP ? a.dz_phi + zo : nullptr;
   float* __restrict__ Cz = O16 ? nullptr : a.C + zo;
   uint16_t* __restrict__ Cz16 = O16 ? a.C16 + zo : nullptr;
   const int sCm = (int)a.sCm, sCn = (int)a.sCn;
@@ -472,7 +483,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = min(mb + crow(lane, r), a.M - 1);
-          xv[r] = dzx[m * sCm + n * sCn];
+          xv[r] = XP ? bf2f(dzp[m * sCm + n * sCn]) : dzx[m * sCm + n * sCn];
           rv[r] = HAS_R ? a.dz_r[z * a.dz_srz + m] : 1.f;
         }
       }
@@ -481,9 +492,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEN ? 3 : 4
         float v = acc[j][r] + bn;
         if constexpr (DZ) {  // dz = (dphi + r s) phi'(x), phi'(x) = 1 for x > 0, exp(x) otherwise
           const float dp = v + rv[r] * sn;
-          v = xv[r] > 0.f ? dp : dp * __expf(xv[r]);
-          if constexpr (CSR) cp += elu1(xv[r]) * rv[r];
+          if constexpr (XP) v = dp * fminf(xv[r], 1.f);  // (phi(x) = exp(x) <= 1 for x <= 0, x + 1 > 1 else)
+          else v = xv[r] > 0.f ? dp : dp * __expf(xv[r]);
+          if constexpr (CSR) cp += (XP ? xv[r] : elu1(xv[r])) * rv[r];
         }
+        if constexpr (PHI_OUT) v = elu1(v);
         if constexpr (CSV) cv += v;
         if constexpr (CSQ) cq += elu1(v);
         if constexpr (O16) Cz16[off] = f2bf(v);  // (the column sums above use the fp32 value)
@@ -602,14 +615,20 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
   // the column sums of dz and of phi(x) r; 2: dz, with the column sums of dz; 3:
   // the column sums of phi of the output); the variants exist for the operand
   // kinds the products use, other combinations are refused.
+  // (4: phi of the output in bf16; 5, 6: as 1, 2 with the dz operand given as
+  // phi(x) in bf16)
   int epi = 0;
   if (a.dz_s != nullptr) {
-    if (!a.cs_val || a.cs_phi || (a.dz_r != nullptr) != (a.cs_phir != nullptr)) return hipErrorInvalidValue;
-    epi = a.dz_r ? 1 : 2;
+    if (!a.cs_val || a.cs_phi || a.phi_out || (a.dz_r != nullptr) != (a.cs_phir != nullptr)) return hipErrorInvalidValue;
+    if ((a.dz_x != nullptr) == (a.dz_phi != nullptr)) return hipErrorInvalidValue;
+    epi = a.dz_phi ? (a.dz_r ? 5 : 6) : (a.dz_r ? 1 : 2);
   } else if (a.cs_val || a.cs_phir) {
     return hipErrorInvalidValue;
   } else if (a.cs_phi) {
+    if (a.phi_out) return hipErrorInvalidValue;
     epi = 3;
+  } else if (a.phi_out) {
+    epi = 4;
   }
   if (epi != 0) {
     if (a_elu || a.beta) return hipErrorInvalidValue;
@@ -618,9 +637,13 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
     if (ext > 0x7fffffffLL || a.sCm > 0x7fffffffLL || a.sCn > 0x7fffffffLL) return hipErrorInvalidValue;
   }
   const bool o16 = a.C16 != nullptr;
-  if (o16 && ((epi != 1 && epi != 2) || dtype != 1)) return hipErrorInvalidValue;
-  if (a.den_ks != nullptr) {  // phi(fp32 A) rows, k contiguous, fp32 B
-    if (epi != 0 || !a_elu || a_io || b_io || a.sAk != 1 || a.K > kDenMaxK || a.KB != 1) return hipErrorInvalidValue;
+  if (o16 && (epi == 0 || epi == 3 || dtype != 1)) return hipErrorInvalidValue;
+  if (epi >= 4 && (!o16 || dtype != 1)) return hipErrorInvalidValue;  // (bf16 outputs of the bf16 path)
+  if (a.den_ks != nullptr) {  // phi rows as A (fp32 mapped on staging, or bf16 phi), k contiguous, fp32 B
+    if (epi != 0 || b_io || a.sAk != 1 || a.K > kDenMaxK || a.KB != 1) return hipErrorInvalidValue;
+    if (dtype == 1 && a_io && !a_elu && a.sBk != 1)
+      return launch_bgemm_t<uint16_t, uint16_t, float, false, 0, true, false, false, true>(a, Z, s);
+    if (!a_elu || a_io) return hipErrorInvalidValue;
     if (dtype == 1 && a.sBk != 1)  // B row-strided (lin: KV)
       return launch_bgemm_t<uint16_t, float, float, true, 0, true, false, false, true>(a, Z, s);
     return dtype == 1 ? launch_bgemm_t<uint16_t, float, float, true, 0, true>(a, Z, s)
@@ -630,6 +653,10 @@ static hipError_t launch_bgemm(int dtype, bool a_io, bool b_io, bool a_elu, cons
     if (dtype == 1) {
       if (epi == 1 && o16 && !a_io && !b_io) return launch_bgemm_t<uint16_t, float, float, false, 1, false, true>(a, Z, s);
       if (epi == 1 && o16 && a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false, 1, false, true>(a, Z, s);
+      if (epi == 5 && o16 && a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false, 5, false, true>(a, Z, s);
+      if (epi == 6 && o16 && a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false, 6, false, true>(a, Z, s);
+      if (epi == 4 && o16 && a_io && b_io && a.sAk == 1 && a.sBk != 1)
+        return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 4, false, true, false, true>(a, Z, s);
       if (epi == 2 && o16 && a_io && !b_io) return launch_bgemm_t<uint16_t, uint16_t, float, false, 2, false, true>(a, Z, s);
       if (epi == 3 && a_io && b_io) return launch_bgemm_t<uint16_t, uint16_t, uint16_t, false, 3>(a, Z, s);
       return hipErrorInvalidValue;
@@ -785,8 +812,11 @@ BackwardLayout backward_layout(const Problem& p) {
     o += (n * 4 + 255) & ~(size_t)255;
     return at;
   };
-  l.zq = take(Z * NQ * F);
-  l.zk = take(Z * N * F);
+  // z_q, z_k: fp32 pre-activations, or on the bf16 path phi(z) in bf16 (every
+  // reader takes phi; phi'(z) = min(phi(z), 1))
+  const size_t z_el = p.dtype == 1 ? 2 : 4;
+  l.zq = take((Z * NQ * F * z_el + 3) / 4);
+  l.zk = take((Z * N * F * z_el + 3) / 4);
   // dz_q, dz_k: bf16 on the bf16 path (their only reader, the dW products,
   // stages them as bf16 operands), else fp32
   const size_t dz_el = p.dtype == 1 ? 2 : 4;
@@ -873,7 +903,12 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     for (int b = 0; b < B; ++b) {
       BgemmArgs ab = a;
       ab.A = static_cast<const unsigned char*>(X) + (size_t)b * H * RD * (dt == 1 ? 2 : 4);
-      ab.C = Zout + (size_t)b * H * RF;
+      if (dt == 1) {  // bf16: phi(z) in bf16, what every later reader takes
+        ab.C16 = reinterpret_cast<uint16_t*>(Zout) + (size_t)b * H * RF;
+        ab.phi_out = 1;
+      } else {
+        ab.C = Zout + (size_t)b * H * RF;
+      }
       ab.sBz = (long long)D * F;
       ab.sCz = RF;
       ab.bias_n = bias;  // z = h within one batch row
@@ -944,7 +979,7 @@ static hipError_t backward_forward_pass(const Problem& p, const void* Q, const v
     a.den_out = den;
     a.den_oz = NQ;
     a.den_eps = eps;
-    TTR_HIP(launch_bgemm(dt, false, false, true, a, Z, s));
+    TTR_HIP(launch_bgemm(dt, dt == 1, false, dt != 1, a, Z, s));  // bf16: A is phi(z_q) in bf16
     tm->mark();
   }
   // landmark branch output (fp32), for dalpha. bf16: a pack of the L landmarks
@@ -999,7 +1034,8 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.B = kv;  // B(k = d, n = f) = KV[f][d]
     if (dt == 1) a.C16 = reinterpret_cast<uint16_t*>(dzq);
     else a.C = dzq;
-    a.dz_x = zq;
+    if (dt == 1) a.dz_phi = reinterpret_cast<const uint16_t*>(zq);  // phi(z_q), bf16
+    else a.dz_x = zq;
     a.dz_r = dden;
     a.dz_s = ks;
     a.dz_srz = NQ;
@@ -1041,7 +1077,8 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.sCz = FD;
     a.sCm = D;
     a.sCn = 1;
-    TTR_HIP(launch_bgemm(dt, false, dt == 1, true, a, Z, s, t.splitk, t.splitk_n));  // dnum in the IO dtype
+    // dnum in the IO dtype; bf16: A is phi(z_q) in bf16 already
+    TTR_HIP(launch_bgemm(dt, dt == 1, dt == 1, dt != 1, a, Z, s, t.splitk, t.splitk_n));
     tm->mark();
   }
   TTR_HIP(launch_tile_colsum(t.cs2, half_tiles(NQ), nullptr, 0, 1, 0, F, Z, dks, s));
@@ -1053,7 +1090,8 @@ static hipError_t backward_grad_pass(const Problem& p, const void* Q, const void
     a.B = dkv;  // B(k = d, n = f) = dKV[f][d]
     if (dt == 1) a.C16 = reinterpret_cast<uint16_t*>(dzk);
     else a.C = dzk;
-    a.dz_x = zk;
+    if (dt == 1) a.dz_phi = reinterpret_cast<const uint16_t*>(zk);  // phi(z_k), bf16
+    else a.dz_x = zk;
     a.dz_s = dks;
     a.dz_ssz = F;
     a.cs_val = t.cs3;  // db, key rows
