@@ -149,7 +149,8 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
  * "Flux2TTRTrainer", "How the distillation works" (the student layer that
  * Phase 1 trains); "NNT Define Linear Attention", "How it works" (the linear branch).
  * b may be NULL (zero bias; db is still written). g is needed when L > 0.
- * ws: at least ttr_backward_workspace_bytes(d, L) bytes (fp32 intermediates). */
+ * ws: at least ttr_backward_workspace_bytes(d, L) bytes (the intermediates: fp32,
+ * with phi(z), dz and dnum in bf16 on the bf16 path). */
 ttr_status ttr_hybrid_backward(ttr_dims d, const void* Q, const void* K, const void* V, const void* W,
                                const float* b, const float* g, float eps, int32_t L, const float* dout,
                                float* dW, float* db, float* dg, void* ws, size_t ws_bytes, void* stream);
