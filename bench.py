@@ -52,6 +52,9 @@ def parse():
                     help="time each staged entry point (feature map, key/value reduction, apply, landmark branch, "
                          "blend) with its own roofline instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--cold", action="store_true",
+                    help="cold caches: write a 1 GiB scratch buffer before every timed forward (flushes the L2s "
+                         "and the 256 MB MALL) and time each forward on its own")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     ap.add_argument("--write-traffic", default=None, metavar="DIR",
@@ -170,15 +173,16 @@ def kernel_plan(w):
     io = 2 if w.dtype == "bf16" else 4
     tok = BH * N * D * io  # one [B, H, N, D] tensor
     if w.causal:
-        chunk = 128  # the chunk the hybrid entry point uses for the causal route
+        chunk = w.chunk
         nseg, cps = causal_plan(w, chunk)
-        # segment totals read K and V of every segment but the last; the walk
-        # reads Q, K, V and writes out once
+        # segment totals read K and V of every segment but the last: a re-read
+        # the method does not need, so it carries no algorithmic bytes; the
+        # walk reads Q, K, V and writes out once
         seg_tokens = min(N, (nseg - 1) * cps * chunk)
         state = 2 * D * D + D  # P += phi(k)^T v, z += phi(k) per token
         plan = []
         if nseg > 1:
-            plan.append((f"causal2_kernel<{chunk}, false, 0>", BH * seg_tokens * state, 2 * BH * seg_tokens * D * io))
+            plan.append((f"causal2_kernel<{chunk}, false, 0>", BH * seg_tokens * state, 0))
         # per token: its share of the causal score and value tiles (C/2 keys on
         # average, plus the diagonal), the inter-chunk product and the state update
         walk = BH * N * (2 * 2 * D * (chunk // 2 + 16) + 2 * D * D + state)
@@ -217,6 +221,41 @@ def causal_plan(w, chunk):
 def algorithmic_bytes(w):
     io = 2 if w.dtype == "bf16" else 4
     return 4 * w.B * w.H * w.N * w.D * io  # Q, K, V read once, out written once
+
+
+def host_info():
+    """The host's CPU model and physical core count (from /proc/cpuinfo), and the BLAS threads numpy uses."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    return {"host_cpu": model, "host_physical_cores": len(cores) or None, "host_logical_cpus": os.cpu_count(),
+            "usable_cpus": affinity, "blas_threads": int(threads)}
 
 
 def cpu_baseline(w, x, target_s):
@@ -259,7 +298,7 @@ def cpu_baseline(w, x, target_s):
     sec_full = t * total_seqs / seqs
     sample = (f"{seqs} of {total_seqs} (batch, head) slices of the {w.name} workload (N={w.N}), fp64 numpy "
               f"oracle, {reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all slices")
-    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", **host_info(),
             "sample": sample, "seconds_full_estimate": sec_full}
 
 
@@ -311,7 +350,7 @@ def cpu_baseline_layer(w, x, target_s):
     sec_full = t * w.B / nb
     sample = (f"{nb} of {w.B} sequences of the {w.name} workload (N={w.N}, E={w.E}), fp64 numpy oracle, "
               f"{reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all sequences")
-    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", **host_info(),
             "sample": sample, "seconds_full_estimate": sec_full}
 
 
@@ -486,9 +525,9 @@ def cpu_baseline_distill(w, x, target_s, lr, nq=None):
               f"oracle distillation step, {reps} pass(es) totalling {total:.1f} s, {t:.3f} s per pass, scaled to all "
               "heads")
     if nq is not None:
-        return {"value": w.B / sec_full, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+        return {"value": w.B / sec_full, "unit": "samples/s", "cores": int(threads), "kind": "oracle", **host_info(),
                 "sample": sample, "seconds_full_estimate": sec_full}
-    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": w.B * w.N / sec_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", **host_info(),
             "sample": sample, "seconds_full_estimate": sec_full}
 
 
@@ -681,7 +720,7 @@ def main_cosine(args):
             reps += 1
         sec = (time.perf_counter() - t0) / reps
         res["cpu_baseline"] = {"value": w.B * w.H * w.N / sec, "unit": "rows/s", "cores": os.cpu_count() or 1,
-                               "kind": "oracle", "sample": f"the whole {w.name} pair, {reps} pass(es)"}
+                               "kind": "oracle", **host_info(), "sample": f"the whole {w.name} pair, {reps} pass(es)"}
     print(json.dumps(res), flush=True)
 
 
@@ -893,7 +932,7 @@ def main_replay(args):
             ref.push(hq, hk, hv, idx, ht)
             reps += 1
         sec = (time.perf_counter() - t0) / reps
-        res["cpu_baseline"] = {"value": payload / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        res["cpu_baseline"] = {"value": payload / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", **host_info(),
                                "sample": f"{reps} pushes of the {w.name} sample into the oracle's model (host copies)"}
     print(json.dumps(res), flush=True)
 
@@ -950,14 +989,16 @@ def main():
     out = torch.empty_like(Q)
     lib = ttr.load_library()
     F = w.F
-    nbytes = ttr.workspace_bytes(w.B, w.H, w.N, w.D, F, 1 if w.dtype == "bf16" else 0, w.L, w.causal, 0)
+    nbytes = ttr.workspace_bytes(w.B, w.H, w.N, w.D, F, 1 if w.dtype == "bf16" else 0, w.L, w.causal,
+                                 w.chunk if w.causal else 0)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
         if events is not None:
             lib.ttr_set_stage_events(events, len(plan) + 1)
-        ttr.hybrid_forward(Q, K, V, W, b, g, eps, w.L, causal=w.causal, out=out, ws=ws)
+        ttr.hybrid_forward(Q, K, V, W, b, g, eps, w.L, causal=w.causal, out=out, ws=ws,
+                           chunk=w.chunk if w.causal else 0)
 
     plan = kernel_plan(w)
     for _ in range(args.warmup):
@@ -975,19 +1016,35 @@ def main():
     torch.cuda.synchronize()
 
     # Headline: K forwards back to back, nothing recorded between kernels.
+    # Cold: before each forward a 1 GiB buffer is written (every L2 line and
+    # the MALL now hold other data) and each forward is timed on its own.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
+    if flush is None:
+        start.record(stream)
+        for i in range(args.steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+    else:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            pairs[i][0].record(stream)
+            step()
+            pairs[i][1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = sum(a.elapsed_time(b) for a, b in pairs)
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
     # Per-kernel durations: another K forwards with an event between kernels.
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
         step(handles[i])
     torch.cuda.synchronize()
     kern_ms = {}
@@ -1012,8 +1069,10 @@ def main():
     peak_fwd = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     if w.causal:
         metric = f"causal linear-attention tokens/sec (B={w.B}, H={w.H}, N={w.N}, D={w.D})"
-    else:
+    elif w.name == "flux_1024":
         metric = "hybrid-attention tokens/sec at Flux 1024^2 (24 heads) + % bf16 MFMA peak"
+    else:
+        metric = f"hybrid-attention tokens/sec ({w.name}: B={w.B}, H={w.H}, N={w.N}, D={w.D}, L={w.L})"
     res = {
         "metric": metric,
         "value": w.B * w.N / (ms * 1e-3),
@@ -1028,7 +1087,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F, "L": w.L,
-                   "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
+                   "causal": w.causal, **({"chunk": w.chunk} if w.causal else {}),
+                   "caches": "cold" if args.cold else "hot", "global_batch": w.B, "seq_len": w.N},
         "roofline": {"kernel": name, "bound": rl["bound"], "achieved": rl["achieved"], "peak": rl["peak"],
                      "unit": rl["unit"], "frac": rl["frac"], "traffic": traffic,
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,

@@ -129,9 +129,11 @@ ttr_status ttr_causal_scan(ttr_dims d, const void* Q, const void* K, const void*
 
 /* The whole hybrid forward (kv_reduce, then apply + landmark + blend in one
  * fused kernel), out [B,H,N,D] in the IO dtype. L == 0: out = out_lin.
- * causal != 0 routes to ttr_causal_scan with chunk 128 (the largest supported
- * chunk <= 128 for the dtype and D) and needs L == 0 and W == NULL
- * (the pages define no causal landmark branch: TTR_ERR_UNSUPPORTED otherwise).
+ * causal != 0 routes to ttr_causal_scan and needs L == 0 and W == NULL (the
+ * pages define no causal landmark branch: TTR_ERR_UNSUPPORTED otherwise).
+ * The value names the chunk: 64, 128 or 256 runs that chunk; 1 runs the
+ * default one (128, or the largest supported chunk below it for the dtype and
+ * D); any other value is TTR_ERR_SHAPE.
  * ws: at least ttr_workspace_bytes(d, L, causal, 0) bytes. */
 ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const void* V,
                               const void* W, const float* b, const float* g, float eps,
@@ -267,7 +269,9 @@ ttr_status ttr_nnt_layer_forward(ttr_layer_dims d, const void* x, const void* Wq
 /* Workspace size in bytes of ttr_nnt_layer_forward (0 if the shape is invalid). */
 size_t ttr_nnt_layer_workspace_bytes(ttr_layer_dims d, int32_t causal);
 
-/* Workspace size in bytes for the given call shape (0 if the shape is invalid). */
+/* Workspace size in bytes for the given call shape (0 if the shape is invalid).
+ * causal takes the values ttr_hybrid_forward accepts; chunk, when non-zero,
+ * names the causal chunk instead (ttr_causal_scan's argument). */
 size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk);
 
 /* Static, never-NULL description of a status code. */

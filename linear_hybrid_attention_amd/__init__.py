@@ -327,13 +327,15 @@ def causal_scan(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, b: Optional[t
 def hybrid_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor],
                    b: Optional[torch.Tensor], g: Optional[torch.Tensor], eps: float = 1e-6, L: int = 0,
                    causal: bool = False, out: Optional[torch.Tensor] = None,
-                   ws: Optional[torch.Tensor] = None, fmap: str = "elu1") -> torch.Tensor:
-    """The whole TTR forward, [B,H,N,D] in Q's dtype (ttr_hybrid_forward)."""
+                   ws: Optional[torch.Tensor] = None, fmap: str = "elu1", chunk: int = 0) -> torch.Tensor:
+    """The whole TTR forward, [B,H,N,D] in Q's dtype (ttr_hybrid_forward).
+    With causal, chunk (64, 128 or 256) names the scan's chunk; 0 takes the default."""
     lib = load_library()
     d = _dims(Q, _feat_dim(Q, W), fmap)
     if out is None:
         out = torch.empty_like(Q)
-    need = lib.ttr_workspace_bytes(d, int(L), int(causal), 0)
+    causal = (int(chunk) if chunk else 1) if causal else 0
+    need = lib.ttr_workspace_bytes(d, int(L), causal, 0)
     ws, wsb = _workspace(d, need, Q, ws)
     st = lib.ttr_hybrid_forward(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype),
                                 _dev(W, "W", Q.dtype), _dev(b, "b", torch.float32), _dev(g, "g", torch.float32),

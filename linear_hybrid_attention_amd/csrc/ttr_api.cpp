@@ -105,10 +105,18 @@ void ttr_set_stage_events(void* const* events, int32_t n) {
   g_stage_n = g_stage_events ? n : 0;
 }
 
+// The causal chunk a `causal` argument of ttr_hybrid_forward names: 1 is the
+// default chunk, 64 / 128 / 256 that chunk; 0 for any other value.
+static int32_t causal_chunk_of(const ttr_dims& d, int32_t causal) {
+  if (causal == 1) return causal_default_chunk(d.dtype, d.D);
+  if (causal == 64 || causal == 128 || causal == 256) return causal;
+  return 0;
+}
+
 size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk) {
   if (causal) {
     if (d.F != d.D || check_dims(d, false) != TTR_OK) return 0;
-    if (chunk == 0) chunk = causal_default_chunk(d.dtype, d.D);
+    if (chunk == 0) chunk = causal_chunk_of(d, causal);
     if (!causal_chunk_ok(d.dtype, d.D, chunk)) return 0;
     return causal_workspace_bytes(make_problem(d, false), chunk);
   }
@@ -269,7 +277,8 @@ static ttr_status hybrid_forward_impl(ttr_dims d, const void* Q, const void* K, 
     if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
     if (W != nullptr || L != 0) return TTR_ERR_UNSUPPORTED;
     TTR_TRY(check_dims(d, false));
-    const int32_t chunk = causal_default_chunk(d.dtype, d.D);
+    if (causal != 1 && causal != 64 && causal != 128 && causal != 256) return TTR_ERR_SHAPE;
+    const int32_t chunk = causal_chunk_of(d, causal);
     if (chunk == 0) return TTR_ERR_UNSUPPORTED;
     return causal_scan_impl(d, Q, K, V, W, b, eps, chunk, out, ws, ws_bytes, s, outer);
   }

@@ -477,12 +477,19 @@ def hybrid_backward(Q, K, V, W, b, g, eps, L: int, dout):
 
 
 def full_softmax_attention(Q, K, V) -> np.ndarray:
-    """softmax(Q K^T / sqrt(D)) V per (batch, head): native attention, the teacher."""
+    """softmax(Q K^T / sqrt(D)) V per (batch, head): native attention, the teacher.
+    One (batch, head) slice at a time, with matrix products (queries may be
+    fewer than keys: Q [B,H,Nq,D], K and V [B,H,N,D])."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
-    S = np.einsum("bhnd,bhmd->bhnm", Q, K) / math.sqrt(Q.shape[3])
-    S -= S.max(axis=-1, keepdims=True)
-    P = np.exp(S)
-    return np.einsum("bhnm,bhmd->bhnd", P, V) / P.sum(axis=-1)[..., None]
+    B, H, Nq, D = Q.shape
+    out = np.empty((B, H, Nq, V.shape[3]))
+    for bi in range(B):
+        for h in range(H):
+            S = (Q[bi, h] @ K[bi, h].T) / math.sqrt(D)
+            S -= S.max(axis=-1, keepdims=True)
+            P = np.exp(S)
+            out[bi, h] = (P @ V[bi, h]) / P.sum(axis=-1)[:, None]
+    return out
 
 
 def distill_loss(out, teacher, s, delta: float = 1.0):

@@ -119,6 +119,20 @@ def test_distill_step_on_sampled_query_rows(dtype, teacher_given, L, N, nq):
     _one_step(w, teacher_given=teacher_given, nq=nq)
 
 
+@pytest.mark.timeout(600)
+def test_distill_step_flux_1024_full_size():
+    # the measured workload: every query row, the teacher (softmax attention
+    # over all 4608 keys) computed by the step itself
+    _one_step(workloads.WORKLOADS["flux_1024"])
+
+
+@pytest.mark.timeout(600)
+def test_distill_step_flux_1024_replay_sample():
+    # a replay sample of the measured workload: 1152 of the 4608 query rows over
+    # every key and value, the teacher's rows given
+    _one_step(workloads.WORKLOADS["flux_1024"], teacher_given=True, nq=1152)
+
+
 def test_phase1_chain_through_the_replay_buffer():
     # teacher on every query, push (K, V whole, a quarter of the queries, the teacher's rows),
     # fetch, and one student step on the fetched sample: the oracle's step on the same rows

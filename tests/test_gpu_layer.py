@@ -83,12 +83,15 @@ def test_layer_repeated_calls_are_bitwise_equal():
     assert np.array_equal(_run(w, x), _run(w, x))
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("name", ["nnt_layer", "nnt_layer_causal"])
-def test_layer_full_size_sampled_batches(name):
-    # the full workload on the GPU; the oracle on batches 0 and B - 1 (sequences are independent)
+def test_layer_full_size_all_sequences(name):
+    # the full workload on the GPU, every element of all B sequences against the oracle
     w = workloads.LAYER_WORKLOADS[name]
     print(f"[layer] full size {name}", flush=True)
     x = workloads.make_layer_inputs(w)
     got = _run(w, x)
-    ref = _ref(w, x, [0, w.B - 1])
-    assert _err(got[[0, w.B - 1]], ref) <= TOL[w.dtype]
+    ref = _ref(w, x, list(range(w.B)))
+    e = _err(got, ref)
+    print(f"[layer] {name} normwise error {e:.3e}", flush=True)
+    assert e <= TOL[w.dtype]

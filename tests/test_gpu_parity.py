@@ -40,23 +40,32 @@ def test_hybrid_forward_full_workloads(name):
     assert err <= TOL[w.dtype], err
 
 
-def test_causal_full_size_sampled_rows():
+@pytest.mark.timeout(600)
+def test_causal_full_size_whole_output():
+    # the causal configuration as stated (chunk 256) through the metric entry
+    # point, every element of all 64 (batch, head) slices against the oracle's
+    # per-token prefix recurrence; chunks 128 and 64 of the scan on the same inputs
     w = workloads.WORKLOADS["causal"]
     x = workloads.make_inputs(w)
-    print(f"[causal] B={w.B} H={w.H} N={w.N} D={w.D} chunk={w.chunk}", flush=True)
-    out = ttr.causal_scan(*(to_device(w, x)[k] for k in ("Q", "K", "V")), eps=float(np.float32(w.eps)),
-                          chunk=w.chunk)
+    d = to_device(w, x)
+    eps = float(np.float32(w.eps))
+    print(f"[causal] B={w.B} H={w.H} N={w.N} D={w.D} chunk={w.chunk} (hybrid entry point)", flush=True)
+    assert w.chunk == 256
+    outs = {256: host(ttr.hybrid_forward(d["Q"], d["K"], d["V"], None, None, None, eps, 0, causal=True,
+                                         chunk=w.chunk))}
+    for c in (128, 64):
+        print(f"[causal] chunk {c} (scan entry point)", flush=True)
+        outs[c] = host(ttr.causal_scan(d["Q"], d["K"], d["V"], eps=eps, chunk=c))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    rows = [(0, 0, 0), (0, 0, 255), (0, 0, 256), (7, 7, w.N - 1), (3, 5, 2047), (3, 5, 2048),
-            (1, 2, w.N // 2)]
-    rows += [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.N))) for _ in range(57)]
-    ref = O.causal_rows(x["Q"], x["K"], x["V"], None, None, x["eps"], rows)
-    got = np.stack([host(out[b, h, n]) for b, h, n in rows])
-    # row-normwise error: |gpu - ref| / max|ref| per sampled row
-    err = float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
-    print(f"[causal] sampled-row err {err:.3e}", flush=True)
-    assert err <= TOL["bf16"], err
+    print("[causal] oracle (per-token recurrence over 32768 tokens)", flush=True)
+    ref = O.causal_forward(x["Q"], x["K"], x["V"], None, None, x["eps"])
+    for c, out in outs.items():
+        assert np.isfinite(out).all()
+        err = normwise(out, ref)
+        # per-row normwise error, a diagnostic: |gpu - ref| / max|ref| within each row
+        row = float((np.abs(out - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
+        print(f"[causal] chunk {c}: slice normwise err {err:.3e}, worst row {row:.3e}", flush=True)
+        assert err <= TOL["bf16"], (c, err)
 
 
 @pytest.mark.parametrize("dtype,D,chunk", [("bf16", 64, 256), ("bf16", 64, 128), ("bf16", 64, 64),

@@ -14,6 +14,8 @@ TTR trainer page targets -- "Flux2TTRTrainer", sections "Why this exists" and
   flux_1024   B=1 H=24 N=4608  D=128 F=256 bf16, L=128  (4096 image + 512 text)
   flux_2048   B=1 H=24 N=16896 D=128 F=256 bf16, L=256  (16384 image + 512 text)
   causal      B=8 H=8  N=32768 D=64  (identity map, F=D) bf16, causal, chunk 256
+  flux_1024_h3  flux_1024 at H=3: one GPU's share when the 24 heads are spread
+                over 8 GPUs (its own seed)
 
 Distributions: Q, K, V ~ N(0, 1); W_h ~ N(0, 1/D) (variance notation, so the
 standard deviation is 1/sqrt(D)); b_h ~ N(0, 0.01) (std 0.1) except the tiny
@@ -79,8 +81,11 @@ WORKLOADS = {
                           1 / np.sqrt(128.0), 0.1, 1002),
     "flux_2048": Workload("flux_2048", 1, 24, 16896, 128, 256, "bf16", 256, False, True,
                           1 / np.sqrt(128.0), 0.1, 1003),
+    # one GPU's share of flux_1024 when its 24 heads are spread over 8 GPUs
+    "flux_1024_h3": Workload("flux_1024_h3", 1, 3, 4608, 128, 256, "bf16", 128, False, True,
+                             1 / np.sqrt(128.0), 0.1, 1007),
     "causal": Workload("causal", 8, 8, 32768, 64, 64, "bf16", 0, True, False,
-                       0.0, 0.0, 1004),
+                       0.0, 0.0, 1004, chunk=256),
 }
 
 
