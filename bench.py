@@ -145,7 +145,7 @@ def kernel_sources(name):
     common = ["common.hpp", "tiles.hpp", "launch.hpp"]
     if name.startswith("proj_gemm") or name.startswith("wt_transpose"):
         return ["k_proj.hip"] + common
-    if name.startswith("kv2_"):
+    if name.startswith("kv_stage"):
         return ["k_kv2.hip"] + common
     if name.startswith("fused_"):
         return ["k_fused.hip"] + common
@@ -193,8 +193,8 @@ def kernel_plan(w):
     apply = 2 * N * F * D + 2 * N * F  # phi(Q) KV and phi(Q) . ksum
     lm = 4 * N * L * D  # Q K_L^T and P V_L
     if w.dtype == "bf16":
-        return [("kv2_partial_kernel", BH * (proj + kv), 2 * tok),
-                ("kv2_pack_kernel", 0, 0),
+        return [("kv_stage_reset_kernel", 0, 0),
+                ("kv_stage_kernel", BH * (proj + kv), 2 * tok),
                 ("fused_query_kernel", BH * (proj + apply + lm), 2 * tok)]
     return [("kv_partial_kernel (+ kv_finalize_kernel)", BH * (proj + kv), 2 * tok),
             ("hybrid_kernel", BH * (proj + apply + lm), 2 * tok)]
@@ -315,7 +315,7 @@ def layer_plan(w):
     plan = [("wt_transpose_kernel", 0, 0),
             ("proj_gemm_kernel (qkv)", 2 * M * E * 3 * E, M * E * io)]
     for name, fl, by in kernel_plan(core):
-        if name.startswith("kv2_partial"):  # identity map: the method has no projection flops here
+        if name.startswith("kv_stage_kernel"):  # identity map: the method has no projection flops here
             fl = core.B * core.H * (2 * core.N * core.D * core.D + core.N * core.D)
         if name.startswith("fused_query"):
             fl = core.B * core.H * (2 * core.N * core.D * core.D + 2 * core.N * core.D)
@@ -469,7 +469,7 @@ def distill_plan(w, nq=None):
         plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
     plan += [("bgemm z_q = Q W + b", gq, 0), ("bgemm z_k = K W + b", gk, 0)]
     if w.dtype == "bf16":  # KV and ksum from K and V by the key/value kernel
-        plan.append(("KV, ksum = phi(K W + b)^T V, colsum (kv2_partial_kernel + kv_finalize_kernel)", gk, 0))
+        plan.append(("KV, ksum = phi(K W + b)^T V, colsum (kv_stage_reset_kernel + kv_stage_kernel)", gk, 0))
     else:
         plan += [("ksum (tile sums of the z_k epilogue)", 0, 0), ("bgemm KV = phi_k^T V", gk, 0)]
     plan += [("bgemm lin = phi_q KV / den, den = phi_q . ks + eps (normaliser formed from the staged rows)", gq, 0)]

@@ -1,29 +1,49 @@
-// bf16 hot path, stage 1: key/value reduction and the per-head operand pack.
+// bf16 hot path, stage 1: the key/value reduction and the per-head operand
+// pack of the fused query kernel, in one launch.
 //
-// kv2_partial_kernel: KV = phi(K)^T V and ksum over one token range of one
-// (batch, head) ("NNT Define Linear Attention", section "How it works":
-// K'^T V first, sum(K') for the normaliser; phi(x) = elu(x W_h + b_h) + 1 per
+// KV = phi(K)^T V and ksum = sum over tokens of phi(K), per (batch, head)
+// ("NNT Define Linear Attention", section "How it works": K'^T V first,
+// sum(K') for the normaliser; phi(x) = elu(x W_h + b_h) + 1 per
 // "Flux2TTRTrainer", section "Inputs worth setting", and the elu(x) + 1 map of
 // the linear-attention page, section "The inputs").
-//   8 waves, two per SIMD. Wave w owns features f0 = 32 (w % NFS) ..
-//   f0 + 31 and keeps that slice of W in registers. Per step of 32 tokens:
-//     phi[tok x 32]  = K[tok x D] . W[:, slice]     (A = K rows from LDS)
-//     KV[32 x D]    += phi^T . V                    (B = V read transposed
-//                                                    from LDS, ds_read_b64_tr_b16)
-//   K and V rows of 128-token super-steps are loaded into registers one
-//   super-step ahead and written to a double LDS buffer; one barrier per
-//   super-step.
 //
-// kv2_pack_kernel: adds the split partials in split order (deterministic) and
-// writes the operands of the fused query kernel as bf16 "chunks" that are
-// exact images of its LDS tiles (swizzled, feature order matched to the MFMA
-// register layout), so that kernel stages them with straight 16-byte copies:
-//   per head h:         W^T chunks  [64 f][D]        (F / 64 of them)
-//   per (batch, head):  bias, ksum  [F] fp32 each, in kperm order
-//                       KV^T chunks [D][64 f]        (F / 64)
-//                       per 32 landmarks: K_L [32 j][D], V_L^T [D][32 j]
-//   with landmarks idx_j = floor(j N / L) ("Flux2TTRTrainer", section "How the
-//   distillation works": exact softmax over strided landmark tokens).
+// kv_stage_kernel. A workgroup owns FG = min(F, 128) features of one (batch,
+// head) and one token range ("split"); its four waves (one per SIMD, up to
+// 512 registers each) own 64 features each, the group's features covered by
+// NFW = FG / 64 waves and the tokens of a step by the NTG = 4 / NFW token
+// groups of 32. Per step a wave computes, for its 32 tokens:
+//   phi[tok x 64]  = map(K[tok x D] . W[:, 64 features] + b)   (A = K rows straight
+//                     from global memory into registers, B = W held in registers)
+//   KV[64 x D]    += phi^T . V                                  (A = the C tile of the
+//                     first product, B = V read transposed from LDS)
+// V of a step is staged in LDS once for the workgroup (through registers: the
+// compiler serialises transposing LDS reads behind any LDS DMA copy in
+// flight). The steps are software-pipelined: iteration j issues the first
+// product of step j + 1 and the second of step j - 1 and maps step j in
+// between, so the map's vector work overlaps the matrix core.
+//
+// The splits of a (batch, head, feature group) then meet: each writes its
+// fp32 partial (its waves' token groups added through LDS first), counts
+// itself in at the group's counter and waits for the others (a bounded spin;
+// every workgroup of the launch is resident, the grid is at most one
+// workgroup per compute unit), and each reduces a share of the group's
+// outputs over the splits in split order -- deterministic -- straight into
+// the fused query kernel's pack (bf16 KV^T chunks, ksum and bias) or into
+// fp32 KV and ksum. Partials are written and read with agent-coherent
+// (sc1) accesses, so the splits may run on different XCDs.
+//
+// The pack, per (batch, head): bias, ksum [F] fp32 in kperm order; F / 64
+// KV^T chunks [D][64 f]; one K_L + V_L^T chunk per 32 landmarks
+// idx_j = floor(j N / L) ("Flux2TTRTrainer", section "How the distillation
+// works": exact softmax over strided landmark tokens); per head the W^T
+// chunks [64 f][D]. Every chunk is an exact image of the query kernel's LDS
+// tile (swizzled, features in MFMA C-row order).
+//
+// lm_pack_kernel: the landmark chunks alone (every key a landmark for the
+// distillation's teacher, or the student's landmark branch).
+#include <atomic>
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"
@@ -47,355 +67,28 @@ struct PackLayout {
   __host__ __device__ size_t w_bytes() const { return (size_t)F * D * 2; }
 };
 
-// ---------------------------------------------------------------- kv2 partial kernel
-struct Kv2Args {
-  const uint16_t* K;
-  const uint16_t* V;
-  const uint16_t* W;  // [H][D][F] or NULL (identity)
-  const float* bias;  // [H][F] or NULL
-  int H, N, chunk, nsplit;
-  float* part;             // [BH][nsplit][F*D + F]
-  unsigned char* pack_w;   // [H][F*D bf16]: W^T chunks, written by split 0 of batch 0
-};
-
-template <int D, int F>
-struct Kv2Shape {
-  static constexpr int NW = 8;
-  static constexpr int NFS = F / 32;
-  static constexpr int NTW = NW / NFS;
-  static constexpr int STEP = 32 * NTW;           // tokens all waves consume per MFMA step
-  static constexpr int SS = 128;                  // tokens per staged super-step
-  static_assert(SS % STEP == 0, "whole steps per super-step");
-  static constexpr int TILE = SS * D;             // elements of the K (or V) tile of a super-step
-  static constexpr int BUF = 2 * TILE;            // K tile, then V tile
-  static constexpr int PER_T = BUF / 8 / 512;     // 16-byte pieces per thread per super-step
-  static_assert(PER_T * 512 * 8 == BUF && (TILE / 8) % 512 == 0, "whole pieces, K/V split per piece index");
-  using WR = LdsRow<uint16_t, D>;                 // W^T [F][D] staging (prologue)
-  static constexpr int w_bytes = F * WR::bytes_per_row;
-  static constexpr int ring_bytes = 2 * BUF * 2 + 2 * SS * 8;  // K/V double buffer, then per-token softmax stats
-  static constexpr int red_floats = (D / 32) * 16 * 64 + 64;  // one wave's KV slice + ksum
-  static constexpr int r_bytes = (NTW - 1) * NFS * red_floats * 4;
-  static constexpr int m1 = w_bytes > ring_bytes ? w_bytes : ring_bytes;
-  static constexpr int bytes = m1 > r_bytes ? m1 : r_bytes;
-  static_assert(bytes <= 160 * 1024, "LDS budget");
-};
-
 // Work item of workgroup i in a one-dimensional grid of n: the hardware places
 // workgroup i on XCD i % 8, so items are renumbered such that consecutive ones
-// (the splits or jobs of one (batch, head)) run on one XCD and share its L2
-// copy of that head's W and partials.
+// (the splits or jobs of one (batch, head)) run on one XCD.
 __device__ __forceinline__ int xcd_item(int i, int n) {
   const int per = n / 8;
   return i < per * 8 ? (i % 8) * per + i / 8 : i;
 }
 
-template <int D, int F, bool PROJ, int MAP>
-__global__ __launch_bounds__(512, 1) void kv2_partial_kernel(Kv2Args a) {
-  using S = Kv2Shape<D, F>;
-  constexpr int NFS = S::NFS, NTW = S::NTW, STEP = S::STEP, SS = S::SS, PER_T = S::PER_T;
-  using WR = typename S::WR;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 5, c = lane & 31;
-  const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int split = item % a.nsplit, bh = item / a.nsplit, h = bh % a.H;
-  const int fs = w % NFS, tw = w / NFS, f0 = 32 * fs;
-  const int N = a.N;
-  const int t_begin = split * a.chunk;
-  const int t_end = min(N, t_begin + a.chunk);
-  const int nss = (t_end - t_begin + SS - 1) / SS;
-  const uint16_t* K = a.K + (size_t)bh * N * D;
-  const uint16_t* V = a.V + (size_t)bh * N * D;
-
-  // K/V staging through registers: piece i of thread tid is piece tid + 512 i
-  // of the super-step (K pieces first). Rows past the range repeat the last
-  // valid token; their phi is masked to zero below, so they add nothing.
-  // (Direct global -> LDS copies are not used: the compiler waits for every
-  // such copy in flight before a transposed LDS read, which would serialise
-  // the prefetch.)
-  u32x4 stg[PER_T];
-  auto load_stg = [&](int ss) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const bool isv = i >= PER_T / 2;
-      const int Pl = tid + 512 * (isv ? i - PER_T / 2 : i);
-      const int row = Pl / (D / 8), p = Pl % (D / 8);
-      const int t = min(t_begin + ss * SS + row, t_end - 1);
-      stg[i] = *reinterpret_cast<const u32x4*>((isv ? V : K) + (size_t)t * D + p * 8);
-    }
-  };
-  uint16_t* const ring = reinterpret_cast<uint16_t*>(smem);
-  float2* const stats = reinterpret_cast<float2*>(smem + 2 * S::BUF * 2);  // [2][SS] (max, 1 / sum)
-  // softmax map (identity projection, F == D): a thread's K pieces are all
-  // logical piece tid % (D / 8) of their rows, so its 8 bias values are fixed
-  float kbias[8];
-  if constexpr (MAP == kSoftmax) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) kbias[j] = a.bias ? a.bias[(size_t)h * F + (tid % (D / 8)) * 8 + j] : 0.f;
-  }
-  auto store_stg = [&](int buf) {
-    uint16_t* kt = ring + buf * S::BUF;
-    uint16_t* vt = kt + S::TILE;
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const bool isv = i >= PER_T / 2;
-      const int Pl = tid + 512 * (isv ? i - PER_T / 2 : i);
-      const int row = Pl / (D / 8), p = Pl % (D / 8);
-      if (isv) {
-        *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = stg[i];
-      } else {
-        *reinterpret_cast<u32x4*>(kt + toff<D, kRowRead>(row, p * 8)) = stg[i];
-        if constexpr (MAP == kSoftmax) {  // the row's D / 8 pieces: D / 8 consecutive lanes
-          const Vec8<uint16_t> kv8 = __builtin_bit_cast(Vec8<uint16_t>, stg[i]);
-          float z[8], m, inv;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) z[j] = bf2f(kv8.v[j]) + kbias[j];
-          softmax_stats<8, D / 8 - 1>(z, m, inv);
-          if (p == 0) stats[buf * SS + row] = float2{m, inv};
-        }
-      }
-    }
-  };
-  load_stg(0);  // in flight during the W staging below
-
-  // W slice as B operand (lane = feature column f0 + c, k = D), via a transposed LDS image.
-  Frag<uint16_t> wf[D / 16];
-  {
-    uint16_t* Wt = reinterpret_cast<uint16_t*>(smem);
-    if constexpr (PROJ) {
-      const uint16_t* W = a.W + (size_t)h * D * F;
-      static_assert((D / 2) * (F / 8) % 512 == 0, "whole rounds");
-#pragma unroll
-      for (int u = tid; u < (D / 2) * (F / 8); u += 512) {
-        const int d = 2 * (u % (D / 2)), fo = (u / (D / 2)) * 8;
-        const Vec8<uint16_t> w0 = ld8(W + (size_t)d * F + fo);
-        const Vec8<uint16_t> w1 = ld8(W + (size_t)(d + 1) * F + fo);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st_pair(Wt + (fo + j) * WR::stride + d, w0.v[j], w1.v[j]);
-      }
-    } else {
-      for (int u = tid; u < F * D; u += 512) {
-        const int f = u / D, d = u % D;
-        Wt[f * WR::stride + d] = f == d ? (uint16_t)0x3f80 : (uint16_t)0;  // bf16 1.0 / 0.0
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) wf[kb] = ld_frag<uint16_t>(Wt + (f0 + c) * WR::stride + kb * 16 + 8 * g);
-    __syncthreads();  // the region becomes the K/V double buffer
-    // The fused query kernel's W^T chunks [64 f][D] (kRowRead) are per head:
-    // one workgroup per head writes them, each lane its row f0 + c in 16-byte pieces.
-    if (split == 0 && bh < a.H && tw == 0) {
-      uint16_t* wc = reinterpret_cast<uint16_t*>(a.pack_w + (size_t)h * F * D * 2) + (size_t)((f0 + c) / 64) * 64 * D;
-#pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb)
-        *reinterpret_cast<u32x4*>(wc + toff<D, kRowRead>((f0 + c) & 63, kb * 16 + 8 * g)) = __builtin_bit_cast(u32x4, wf[kb]);
-    }
-  }
-  const float bcol = a.bias ? a.bias[(size_t)h * F + f0 + c] : 0.f;
-  f32x16 bias16;  // GEMM1 starts from the bias (MFMA C operand, only read)
-#pragma unroll
-  for (int r = 0; r < 16; ++r) bias16[r] = bcol;
-
-  f32x16 kv[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) kv[db] = f32x16{};
-  float ks = 0.f;
-
-  store_stg(0);
-  if (nss > 1) load_stg(1);
-  for (int ss = 0; ss < nss; ++ss) {
-    barrier_lds();  // super-step ss is in buffer ss & 1; every wave is done with the other buffer
-    const uint16_t* kt = ring + (ss & 1) * S::BUF;
-    const uint16_t* vt = kt + S::TILE;
-#pragma unroll
-    for (int j = 0; j < SS / STEP; ++j) {
-      const int r0 = j * STEP + 32 * tw;  // this wave's 32 rows of the super-step
-      const int t0 = t_begin + ss * SS + r0;
-      if (t0 >= t_end) break;  // wave-uniform
-      // two independent chains over alternate k-blocks, added at the end
-      f32x16 acc = mma_from(bias16, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, 8 * g)), wf[0]);
-      f32x16 acc2 = mma_from(f32x16{}, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, 16 + 8 * g)), wf[1]);
-#pragma unroll
-      for (int kb = 2; kb < D / 16; kb += 2) {
-        mma(acc, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, kb * 16 + 8 * g)), wf[kb]);
-        mma(acc2, ld_frag<uint16_t>(kt + toff<D, kRowRead>(r0 + c, kb * 16 + 16 + 8 * g)), wf[kb + 1]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
-      float p[16];
-      // softmax: (max, 1 / sum) of the row's token, from the staging pass
-      auto st = [&](int r) {
-        if constexpr (MAP == kSoftmax) return stats[(ss & 1) * SS + r0 + crow(lane, r)];
-        else return float2{0.f, 1.f};
-      };
-      if (t0 + 32 <= t_end) {  // wave-uniform: only the range's last step has rows past it
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float2 sr = st(r);
-          p[r] = phi_of<MAP>(acc[r], sr.x, sr.y);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float2 sr = st(r);
-          p[r] = t0 + crow(lane, r) < t_end ? phi_of<MAP>(acc[r], sr.x, sr.y) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ks += p[r];
-      const Frag<uint16_t> pa0 = to_frag<uint16_t>(p), pa1 = to_frag<uint16_t>(p + 8);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        mma(kv[db], pa0, tr_frag<D>(vt, r0, 32 * db, lane));
-        mma(kv[db], pa1, tr_frag<D>(vt, r0 + 16, 32 * db, lane));
-      }
-    }
-    // The only global loads in flight are the staged super-step's, so this
-    // wait (issued one super-step ago) is the full count.
-    if (ss + 1 < nss) {
-      store_stg((ss + 1) & 1);
-      if (ss + 2 < nss) load_stg(ss + 2);
-    }
-  }
-  ks += shfl_xor32(ks);
-  __syncthreads();  // K/V buffers no longer read
-
-  if constexpr (NTW > 1) {
-    float* red = reinterpret_cast<float*>(smem);
-    if (tw > 0) {
-      float* rb = red + ((tw - 1) * NFS + fs) * S::red_floats;
-      int i = 0;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rb[(i++) * 64 + lane] = kv[db][r];
-      rb[i * 64 + lane] = ks;
-    }
-    __syncthreads();
-    if (tw == 0) {
-      for (int t2 = 1; t2 < NTW; ++t2) {
-        const float* rb = red + ((t2 - 1) * NFS + fs) * S::red_floats;
-        int i = 0;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) kv[db][r] += rb[(i++) * 64 + lane];
-        ks += rb[i * 64 + lane];
-      }
-    }
-  }
-  if (tw == 0) {
-    float* kvo = a.part + ((size_t)bh * a.nsplit + split) * (size_t)(F * D + F);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) kvo[(size_t)(f0 + crow(lane, r)) * D + db * 32 + c] = kv[db][r];
-    if (g == 0) kvo[F * D + f0 + c] = ks;
-  }
-}
-
-// ---------------------------------------------------------------- pack kernel
-struct PackArgs {
-  const float* part;  // [BH][nsplit][F*D + F]
-  int nsplit;
-  const uint16_t* K;
-  const uint16_t* V;
-  const uint16_t* W;
-  const float* bias;
-  int H, N, L;
-  unsigned char* pack_bh;  // [BH][bh_bytes]
-  unsigned char* pack_w;   // [H][w_bytes]
-  int lm_only;             // 1: the landmark jobs alone, into a pack of landmark chunks only
-};
-
-// Jobs of one (batch, head), by job index:
-//   [0, KVJ)            KV^T rows: FJ features x D (sum of partials), ksum, bias
-//   then one per 32-landmark chunk (K_L and V_L^T)
-// (The W^T chunks are written by the partial kernel, which holds W in registers.)
-template <int D, int F, bool PROJ>
-__global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
-  constexpr int FJ = 2048 / D > F ? F : 2048 / D;  // features per KV job: (FJ/2)*(D/4) = 256 threads
-  constexpr int KVJ = F / FJ;
-  const int tid = threadIdx.x;
-  const int nlb = (a.L + 31) / 32;
-  const int item = xcd_item(blockIdx.x, gridDim.x), njobs = a.lm_only ? nlb : KVJ + nlb;
-  const int bh = item / njobs, h = bh % a.H;
-  PackLayout pl{D, a.lm_only ? 0 : F, a.L, nlb};
-  unsigned char* base = a.pack_bh + (size_t)bh * pl.bh_bytes();
-  float* biasP = reinterpret_cast<float*>(base);
-  float* ksumP = biasP + F;
-  uint16_t* kvc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes());
-  uint16_t* lmc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes() + pl.kv_bytes());
-  const int job = item % njobs + (a.lm_only ? KVJ : 0);
-
-  if (job < KVJ) {
-    // FJ features f0.. x D values: thread -> (feature pair, 4 consecutive d).
-    // Partials are loaded 8 splits at a time and added in split order.
-    const int f0 = job * FJ;
-    const size_t stride = (size_t)F * D + F;
-    const float* p0 = a.part + (size_t)bh * a.nsplit * stride;
-    for (int u = tid; u < (FJ / 2) * (D / 4); u += 256) {
-      const int fp = u / (D / 4), d0 = (u % (D / 4)) * 4, f = f0 + 2 * fp;
-      f32x4 s0 = f32x4{}, s1 = f32x4{};
-      for (int s = 0; s < a.nsplit; s += 8) {
-        f32x4 v0[8], v1[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int sk = min(s + k, a.nsplit - 1);
-          v0[k] = *reinterpret_cast<const f32x4*>(p0 + sk * stride + (size_t)f * D + d0);
-          v1[k] = *reinterpret_cast<const f32x4*>(p0 + sk * stride + (size_t)(f + 1) * D + d0);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (s + k < a.nsplit) {
-            s0 += v0[k];
-            s1 += v1[k];
-          }
-      }
-      // KV^T chunk f / 64, column q = (f & 32) + kperm(f & 31); f even so q + 1 holds f + 1
-      uint16_t* ch = kvc + (size_t)(f / 64) * 64 * D;
-      const int q = (f & 32) + kperm(f & 31);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = d0 + j;
-        *reinterpret_cast<uint32_t*>(ch + toff<64, kRowRead>(d, q)) = pack_bf16x2(s0[j], s1[j]);
-      }
-    }
-    if (tid < FJ) {
-      const int f = f0 + tid;
-      float s = 0.f;
-      for (int sp = 0; sp < a.nsplit; sp += 8) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = p0[min(sp + k, a.nsplit - 1) * stride + (size_t)F * D + f];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (sp + k < a.nsplit) s += v[k];
-      }
-      ksumP[kperm(f)] = s;
-      biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
-    }
-    return;
-  }
-  const int jb = job - KVJ;  // landmark chunk of 32
-  if (jb >= nlb) return;
-  const uint16_t* K = a.K + (size_t)bh * a.N * D;
-  const uint16_t* V = a.V + (size_t)bh * a.N * D;
-  uint16_t* kl = lmc + (size_t)jb * pl.chunk_elems();
+// Landmark chunk jb of one (batch, head): K_L [32 j][D] straight to the chunk,
+// V_L rows through LDS (vrows, 32 x (D + 8) bf16) so that V_L^T [D][32 j]
+// (landmark jl in column kperm(jl)) is written in 16-byte pieces. Landmarks
+// past L are zero. All 256 threads of the workgroup take part.
+template <int D>
+__device__ __forceinline__ void landmark_chunk(const uint16_t* K, const uint16_t* V, int N, int L, int jb,
+                                               uint16_t* kl, uint16_t (*vrows)[D + 8], int tid) {
   uint16_t* vl = kl + 32 * D;
-  // K_L [32 j][D] straight to the chunk; V_L rows through LDS so that V_L^T
-  // [D][32 j] (landmark jl in column kperm(jl)) is written in 16-byte pieces.
-  // Landmarks past L are zero.
-  __shared__ uint16_t vrows[32][D + 8];
   for (int u = tid; u < 2 * 32 * (D / 8); u += 256) {
     const int isv = u >= 32 * (D / 8);
     const int uu = u - isv * 32 * (D / 8);
     const int jl = uu / (D / 8), d0 = (uu % (D / 8)) * 8, j = jb * 32 + jl;
     const uint16_t* src = isv ? V : K;
-    const Vec8<uint16_t> v =
-        j < a.L ? ld8(src + (size_t)(((long long)j * a.N) / a.L) * D + d0) : zero8<uint16_t>();
+    const Vec8<uint16_t> v = j < L ? ld8(src + (size_t)(((long long)j * N) / L) * D + d0) : zero8<uint16_t>();
     if (isv) *reinterpret_cast<Vec8<uint16_t>*>(&vrows[jl][d0]) = v;
     else st8(kl + toff<D, kRowRead>(jl, d0), v);
   }
@@ -407,21 +100,641 @@ __global__ __launch_bounds__(256) void kv2_pack_kernel(PackArgs a) {
     for (int e = 0; e < 8; ++e) v.v[e] = vrows[kperm(8 * q + e)][d];  // kperm is its own inverse
     st8(vl + toff32(d, 8 * q), v);
   }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- key/value stage
+struct KvsArgs {
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* W;  // [H][D][F] or NULL (identity)
+  const float* bias;  // [H][F] or NULL
+  int H, N, L;
+  int nsplit, chunk;     // token splits of a group and the tokens of each (a multiple of the step)
+  float* part;           // [groups][nsplit][FG * D + FG] fp32 partials
+  unsigned* counters;    // [groups] arrivals, zero on entry (kv_stage_reset_kernel)
+  unsigned spin_limit;   // polls of a waiting workgroup before it gives up
+  unsigned char* pack_bh;  // pack mode: [BH][bh_bytes]
+  unsigned long long bh_bytes;
+  unsigned char* pack_w;   // pack mode: [H][F D bf16] W^T chunks (written by batch 0)
+  float* kv_out;           // fp32 mode: KV [BH][F][D]
+  float* ks_out;           // fp32 mode: ksum [BH][F]
+};
+
+template <int D, int F>
+struct KvsShape {
+  static constexpr int FG = F < 128 ? F : 128;  // features of a workgroup
+  static constexpr int NG = F / FG;             // feature groups of a head
+  static constexpr int NFW = FG / 64;           // waves across the group's features
+  static constexpr int NTG = 4 / NFW;           // token groups of 32 per step
+  static constexpr int STEP = 32 * NTG;         // tokens of a workgroup step
+  static constexpr int NKB = D / 16;            // k-blocks of a K row
+  static constexpr int NDB = D / 32;            // 32-column blocks of V
+  static constexpr int VP = STEP * D / 8 / 256;  // 16-byte V pieces per thread per step
+  static constexpr int PART = FG * D + FG;       // floats of one split's partial
+  static_assert(F == 64 || F % 128 == 0, "feature count");
+  static_assert(VP * 256 * 8 == STEP * D && VP >= 1, "whole V pieces");
+  static constexpr int vbuf_bytes = 2 * STEP * D * 2;            // V double buffer
+  static constexpr int wtile_bytes = D * FG * 2;                 // W tile (prologue)
+  static constexpr int stats_bytes = 4 * 2 * 32 * 8;             // softmax (max, 1 / sum) per wave and step parity
+  static constexpr int main_bytes = vbuf_bytes + wtile_bytes + stats_bytes;
+  static constexpr int red_bytes = (NTG - 1) * NFW * (64 * D + 64) * 4;  // token-group partials
+  static constexpr int lm_bytes = 32 * (D + 8) * 2;
+  static constexpr int bytes = main_bytes > red_bytes ? (main_bytes > lm_bytes ? main_bytes : lm_bytes)
+                                                      : (red_bytes > lm_bytes ? red_bytes : lm_bytes);
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+// (a quiet NaN by its bits: the file is built without NaN semantics)
+#define kQNaN __uint_as_float(0x7fc00000u)
+
+__global__ void kv_stage_reset_kernel(unsigned* counters, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    __hip_atomic_store(counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-byte load / store that are coherent at agent scope (sc1): they reach the
+// point where every XCD sees the same data, whatever L2 holds.
+__device__ __forceinline__ u32x4 ld16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
+}
+__device__ __forceinline__ void st16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
+}
+
+template <int D, int F, bool PROJ, int MAP, bool PACK>
+__global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
+  using S = KvsShape<D, F>;
+  constexpr int FG = S::FG, NG = S::NG, NFW = S::NFW, NTG = S::NTG, STEP = S::STEP, NKB = S::NKB,
+                NDB = S::NDB, VP = S::VP;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
+  uint16_t* const vbuf = reinterpret_cast<uint16_t*>(smem);                       // [2][STEP][D] kTrRead
+  uint16_t* const wt = reinterpret_cast<uint16_t*>(smem + S::vbuf_bytes);         // [D][FG] kTrRead, rows kperm'd
+  float2* const stats = reinterpret_cast<float2*>(smem + S::vbuf_bytes + S::wtile_bytes);  // [4][2][32]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  const int fw = w % NFW, tg = w / NFW;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int split = item % a.nsplit, group = item / a.nsplit;
+  const int bh = group / NG, fgi = group % NG, h = bh % a.H;
+  const int fg0 = fgi * FG;         // first feature of the group
+  const int fw0 = fg0 + 64 * fw;    // first of this wave's 64 features
+  const int N = a.N;
+  const int t_begin = split * a.chunk;
+  const int t_end = min(N, t_begin + a.chunk);
+  const int nsteps = (t_end - t_begin + STEP - 1) / STEP;
+  const uint16_t* Kp = a.K + (size_t)bh * N * D;
+  const uint16_t* Vp = a.V + (size_t)bh * N * D;
+
+  // ---- operand streams, through buffer resources that end at the range's
+  // last token: a row past it reads as zeros (so it adds nothing to KV, and
+  // a fixed phi(0 W + b) to ksum, taken out after the loop). K rows of step j
+  // for this wave's 32 tokens, as the A operand (lane = token c, k-slots =
+  // columns 16 kb + 8 g ..); V rows of step j: piece tid + 256 i of the step.
+  const uint32_t range_bytes = (uint32_t)((size_t)t_end * D * 2);
+  const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(Kp, range_bytes);
+  const __amdgpu_buffer_rsrc_t rV = buffer_rsrc(Vp, range_bytes);
+  auto load_k = [&](int j, Frag<uint16_t> (&kf)[NKB]) {
+    const uint32_t off = (uint32_t)(t_begin + j * STEP + 32 * tg + c) * (D * 2) + 16 * g;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      kf[kb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rK, (int)(off + 32 * kb), 0, 0));
+  };
+  auto load_v = [&](int j, u32x4 (&vs)[VP]) {
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int P = tid + 256 * i, row = P / (D / 8), p = P % (D / 8);
+      vs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rV, (int)((uint32_t)(t_begin + j * STEP + row) * (D * 2) + p * 16), 0, 0));
+    }
+  };
+  auto store_v = [&](int buf, const u32x4 (&vs)[VP]) {
+    uint16_t* vt = vbuf + buf * STEP * D;
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int P = tid + 256 * i, row = P / (D / 8), p = P % (D / 8);
+      *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = vs[i];
+    }
+  };
+
+  // Every load is issued unconditionally (steps past the range read zeros),
+  // so the compiler's count of loads in flight is exact on every path and
+  // each wait covers only the loads it needs.
+  Frag<uint16_t> kf0[NKB], kf1[NKB];
+  u32x4 vs0[VP], vs1[VP];
+  load_k(0, kf0);
+  load_k(1, kf1);
+  load_v(0, vs0);
+  load_v(1, vs1);
+
+  // ---- W slice as the B operand (lane = feature fw0 + 32 fb + c, k-slots =
+  // rows 16 kb + 8 g ..): the group's W columns are staged as a [D][FG] tile
+  // whose rows are permuted by kperm within each block of 16, so that the
+  // transposing read (which hands a lane its k-rows in C-row order) returns
+  // them in natural order, the order of the K fragments.
+  Frag<uint16_t> wf[2][NKB];
+  if constexpr (PROJ) {
+    const uint16_t* W = a.W + (size_t)h * D * F + fg0;
+    constexpr int WP = D * FG / 8 / 256;
+    static_assert(WP * 256 * 8 == D * FG, "whole W pieces");
+    u32x4 wv[WP];
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int P = tid + 256 * i, d = P / (FG / 8), p = P % (FG / 8);
+      wv[i] = *reinterpret_cast<const u32x4*>(W + (size_t)d * F + p * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int P = tid + 256 * i, d = P / (FG / 8), p = P % (FG / 8);
+      *reinterpret_cast<u32x4*>(wt + toff<FG, kTrRead>((d & ~15) | kperm(d & 15), p * 8)) = wv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) wf[fb][kb] = tr_frag<FG>(wt, 16 * kb, 64 * fw + 32 * fb, lane);
+  } else {
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int f = fw0 + 32 * fb + c;
+        u32x4 u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d0 = 16 * kb + 8 * g + 2 * q;
+          u[q] = (d0 == f ? 0x3f80u : 0u) | (d0 + 1 == f ? 0x3f800000u : 0u);  // bf16 1.0 on the diagonal
+        }
+        wf[fb][kb] = __builtin_bit_cast(bf16x8, u);
+      }
+  }
+  // The fused query kernel's W^T chunks [64 f][D] (kRowRead) are per head:
+  // batch 0's first split writes them, each lane the 16-byte row pieces of
+  // the W slice it holds.
+  if constexpr (PACK) {  // (the identity map too: the query kernel multiplies by it to transpose Q)
+    if (split == 0 && bh < a.H && tg == 0) {
+      uint16_t* wc = reinterpret_cast<uint16_t*>(a.pack_w + (size_t)h * F * D * 2) + (size_t)(fw0 / 64) * 64 * D;
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          *reinterpret_cast<u32x4*>(wc + toff<D, kRowRead>(32 * fb + c, 16 * kb + 8 * g)) =
+              __builtin_bit_cast(u32x4, wf[fb][kb]);
+    }
+  }
+
+  // The bias enters the map, not the product: for elu + 1,
+  // phi = max(x + (b + 1), min(exp2(x log2e + b log2e), 1)) costs what the map
+  // without a bias does (an fma in place of the multiply, an add either way).
+  float bcol[2], bl2[2];  // per lane (its feature column): b + 1 (elu + 1) or b, and b log2e
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb) {
+    const float bc = a.bias ? a.bias[(size_t)h * F + fw0 + 32 * fb + c] : 0.f;
+    bcol[fb] = MAP == kElu1 ? bc + 1.f : bc;
+    bl2[fb] = bc * kLog2e;
+  }
+  auto phi_b = [&](float x, int fb, float2 st) -> float {
+    if constexpr (MAP == kElu1) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, bl2[fb]));
+      return fmaxf(x + bcol[fb], fminf(fmaxf(e, 0.f), 1.f));
+    } else {
+      return phi_of<MAP>(x + bcol[fb], st.x, st.y);
+    }
+  };
+  // softmax map (identity projection, F == D): each lane's bias values for the
+  // columns its K fragments hold, for the token statistics
+  float kbias[MAP == kSoftmax ? NKB * 8 : 1];
+  if constexpr (MAP == kSoftmax) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kbias[8 * kb + i] = a.bias ? a.bias[(size_t)h * F + 16 * kb + 8 * g + i] : 0.f;
+  }
+  float2* const wstats = stats + w * 64;  // [2 parities][32 tokens]
+  // the softmax statistics (max, 1 / sum) of this wave's 32 tokens of a step,
+  // from their K rows (half in this lane, half in lane ^ 32)
+  auto token_stats = [&](const Frag<uint16_t> (&kf)[NKB], int par) {
+    if constexpr (MAP == kSoftmax) {
+      float z[NKB * 8], m, inv;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        frag_to_f32(kf[kb], z + 8 * kb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[8 * kb + i] += kbias[8 * kb + i];
+      }
+      softmax_stats<NKB * 8, 32>(z, m, inv);
+      if (g == 0) wstats[par * 32 + c] = float2{m, inv};
+    }
+  };
+
+  f32x16 kv[2][NDB];
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) kv[fb][db] = f32x16{};
+  float ks[2] = {0.f, 0.f};
+  f32x16 c1a[2], c1b[2];               // first products of even / odd steps
+  Frag<uint16_t> pba[2][2], pbb[2][2];  // mapped phi of even / odd steps, as A operands
+
+  auto gemm1 = [&](const Frag<uint16_t> (&kf)[NKB], f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) acc[fb] = mma_from(f32x16{}, kf[0], wf[fb][0]);
+#pragma unroll
+    for (int kb = 1; kb < NKB; ++kb)
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) mma(acc[fb], kf[kb], wf[fb][kb]);
+  };
+  // phi of one step and feature block fb as the second product's A operands;
+  // ksum from the rounded pairs (the values that product uses), two per v_dot2.
+  const uint32_t ones2 = 0x3f803f80u;  // bf16 (1, 1)
+  auto map_fb = [&](int par, int fb, const f32x16& acc, Frag<uint16_t> (&pb)[2]) {
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float2 st = float2{0.f, 1.f};
+      if constexpr (MAP == kSoftmax) st = wstats[par * 32 + crow(lane, r)];
+      p[r] = phi_b(acc[r], fb, st);
+    }
+    uint32_t u[16 / 2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x2 pr = {(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
+      ks[fb] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, ones2), ks[fb], false);
+      u[i] = __builtin_bit_cast(uint32_t, pr);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const u32x4 v = {u[4 * hh], u[4 * hh + 1], u[4 * hh + 2], u[4 * hh + 3]};
+      pb[hh] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+  auto gemm2 = [&](int buf, const Frag<uint16_t> (&pb)[2][2]) {
+    const uint16_t* vt = vbuf + buf * STEP * D;
+    Frag<uint16_t> vf[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) vf[db][hh] = tr_frag<D>(vt, 32 * tg + 16 * hh, 32 * db, lane);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) mma(kv[fb][db], pb[fb][hh], vf[db][hh]);
+  };
+  // one MFMA, then N vector instructions, for the region's MFMAs
+  auto interleave = [&](auto n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sched_group<kSchedMfma, 1>();
+      sched_group<kSchedAnyValu, decltype(n)::value>();
+    }
+  };
+
+  // ---- prologue: the first product of step 0
+  token_stats(kf0, 0);
+  gemm1(kf0, c1a);
+  load_k(2, kf0);
+
+  // ---- iteration j: the first product of step j + 1, the map of step j, the
+  // second product of step j - 1; V of step j into LDS buffer j & 1 (read in
+  // iteration j + 1); loads of K for step j + 3 and V for step j + 2. Every
+  // operation is unconditional (steps past the range compute on zero rows
+  // whose results are never used), so an iteration is one basic block: its
+  // two regions each pair 16 MFMAs with half of the map's vector work, and
+  // the compiler's count of loads in flight is exact. Even and odd iterations
+  // hold their operands in separate registers, so the loop is unrolled by
+  // two; iteration 0 has no second product.
+  auto iteration = [&](int j, auto odd, auto with2) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd)::value;
+    constexpr bool W2 = decltype(with2)::value;
+    Frag<uint16_t>(&kn)[NKB] = ODD ? kf0 : kf1;  // K of step j + 1
+    f32x16(&cn)[2] = ODD ? c1a : c1b;            // its first product
+    f32x16(&cc)[2] = ODD ? c1b : c1a;            // step j's first product
+    Frag<uint16_t>(&pc)[2][2] = ODD ? pbb : pba;  // step j's mapped phi
+    Frag<uint16_t>(&pp)[2][2] = ODD ? pba : pbb;  // step j - 1's
+    u32x4(&vs)[VP] = ODD ? vs1 : vs0;            // V of step j
+    if constexpr (W2) barrier_lds();  // V of step j - 1 is in LDS; step j - 2's buffer is free
+    token_stats(kn, (j + 1) & 1);
+    // region A: the second product of step j - 1 (its V fragments one
+    // 32-column block ahead of their MFMAs) beside the map of step j's first feature block
+    if constexpr (W2) gemm2((j - 1) & 1, pp);
+    map_fb(j & 1, 0, cc[0], pc[0]);
+    if constexpr (W2) {  // the reads first, part of the map over their latency, then the MFMAs interleaved
+      sched_group<kSchedDsRead, 4 * NDB>();
+      sched_group<kSchedAnyValu, 40>();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedAnyValu, 5>();
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // region B: the first product of step j + 1 beside the map of the second block
+    gemm1(kn, cn);
+    map_fb(j & 1, 1, cc[1], pc[1]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sched_group<kSchedMfma, 1>();
+      sched_group<kSchedAnyValu, 7>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(j + 3, kn);
+    store_v(j & 1, vs);
+    load_v(j + 2, vs);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  iteration(0, F_{}, F_{});
+  // (every trip of the loop runs both iterations, so the loads in flight at
+  // its head are the same on every path into it)
+  int j2 = 1;
+  for (; j2 + 1 <= nsteps; j2 += 2) {
+    iteration(j2, T_{}, T_{});
+    iteration(j2 + 1, F_{}, T_{});
+  }
+  if (j2 <= nsteps) iteration(j2, T_{}, T_{});
+  // Rows past the range: the maps of steps nfull .. nsteps saw K = 0 there,
+  // i.e. phi(0 W + b), the same bits each time; take them out of ksum.
+  {
+    const int nfull = (t_end - t_begin) / STEP;
+    float2 st0 = float2{0.f, 1.f};
+    if constexpr (MAP == kSoftmax) {
+      float z[NKB * 8], m, inv;
+#pragma unroll
+      for (int i = 0; i < NKB * 8; ++i) z[i] = kbias[i];
+      softmax_stats<NKB * 8, 32>(z, m, inv);
+      st0 = float2{m, inv};
+    }
+    int nzero = 0;  // rows past the range among this lane's 16 rows of each map
+    for (int jj = nfull; jj <= nsteps; ++jj) {
+      const int lim = t_end - (t_begin + jj * STEP + 32 * tg);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nzero += crow(lane, r) >= lim;
+    }
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) {
+      const float z0 = bf2f(f2bf(phi_b(0.f, fb, st0)));
+      ks[fb] -= (float)nzero * z0;
+    }
+  }
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb) ks[fb] += shfl_xor32(ks[fb]);
+  __syncthreads();  // LDS free
+
+  // ---- the token groups' sums, added in order into token group 0
+  constexpr int RF = 64 * D + 64;  // floats of one wave's KV and ksum
+  float* red = reinterpret_cast<float*>(smem);
+  if constexpr (NTG > 1) {
+    if (tg > 0) {
+      float* rb = red + ((tg - 1) * NFW + fw) * RF;
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v = {kv[fb][db][4 * q], kv[fb][db][4 * q + 1], kv[fb][db][4 * q + 2], kv[fb][db][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4) = v;
+          }
+      if (g == 0) {
+        rb[64 * D + c] = ks[0];
+        rb[64 * D + 32 + c] = ks[1];
+      }
+    }
+    __syncthreads();
+    if (tg == 0) {
+      for (int t2 = 1; t2 < NTG; ++t2) {
+        const float* rb = red + ((t2 - 1) * NFW + fw) * RF;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) kv[fb][db][4 * q + e] += v[e];
+            }
+        ks[0] += rb[64 * D + c];
+        ks[1] += rb[64 * D + 32 + c];
+      }
+    }
+  }
+  // ---- this split's partial: [fw][fb][db][q][lane][4] (the accumulators'
+  // register image: element e of piece q of lane l is KV[f][d] with
+  // f = fg0 + 64 fw + 32 fb + crow(l, 4 q + e), d = 32 db + (l & 31)), then ksum [FG]
+  const size_t pstride = (size_t)S::PART * 4;
+  const __amdgpu_buffer_rsrc_t rpart = buffer_rsrc(a.part + (size_t)group * a.nsplit * S::PART,
+                                                   (uint32_t)(a.nsplit * pstride));
+  if (tg == 0) {
+    const uint32_t base = (uint32_t)(split * pstride);
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v = {kv[fb][db][4 * q], kv[fb][db][4 * q + 1], kv[fb][db][4 * q + 2], kv[fb][db][4 * q + 3]};
+          st16_agent(rpart, base + (uint32_t)((((fw * 2 + fb) * NDB + db) * 4 + q) * 64 + lane) * 16,
+                     __builtin_bit_cast(u32x4, v));
+        }
+    // ksum in 16-byte pieces: lane c (c % 4 == 0) stores those of lanes c .. c + 3
+    float k4[2][4];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k4[fb][e] = __shfl(ks[fb], (lane & ~3) + e, 64);
+    if (g == 0 && (c & 3) == 0) {
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) {
+        f32x4 v = {k4[fb][0], k4[fb][1], k4[fb][2], k4[fb][3]};
+        st16_agent(rpart, base + (uint32_t)(FG * D + 64 * fw + 32 * fb + c) * 4, __builtin_bit_cast(u32x4, v));
+      }
+    }
+  }
+
+  // ---- landmark chunks of this (batch, head), spread over its workgroups
+  // (they need no partial: done while the other splits finish)
+  if constexpr (PACK) {
+    const int nlb = (a.L + 31) / 32;
+    if (nlb > 0) {
+      const PackLayout pl{D, F, a.L, nlb};
+      uint16_t* lmc = reinterpret_cast<uint16_t*>(a.pack_bh + (size_t)bh * a.bh_bytes + pl.vec_bytes() + pl.kv_bytes());
+      auto vrows = reinterpret_cast<uint16_t(*)[D + 8]>(smem);
+      const int nwg = NG * a.nsplit, me = fgi * a.nsplit + split;
+      __syncthreads();  // the token-group sums are read
+      for (int jb = me; jb < nlb; jb += nwg)
+        landmark_chunk<D>(Kp, Vp, N, a.L, jb, lmc + (size_t)jb * pl.chunk_elems(), vrows, tid);
+    }
+  }
+
+  // ---- meet the group's other splits. The partial stores are complete
+  // (acknowledged at the agent's coherence point) before the count.
+  wait_vmcnt<0>();
+  __syncthreads();
+  __shared__ unsigned ok_s;
+  if (tid == 0) {
+    __hip_atomic_fetch_add(a.counters + group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned n = 0;
+    while (__hip_atomic_load(a.counters + group, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.nsplit &&
+           ++n < a.spin_limit)
+      __builtin_amdgcn_s_sleep(2);
+    ok_s = n < a.spin_limit;
+  }
+  __syncthreads();
+  // A workgroup that gave up writes NaN into its share of the outputs (the
+  // call's result is then undefined, and visibly so).
+  const bool ok = ok_s != 0;
+
+  // ---- this split's share of the reduction, summed over the splits in order
+  if constexpr (PACK) {
+    const PackLayout pl{D, F, a.L, (a.L + 31) / 32};
+    unsigned char* base = a.pack_bh + (size_t)bh * a.bh_bytes;
+    float* biasP = reinterpret_cast<float*>(base);
+    float* ksumP = biasP + F;
+    uint16_t* kvc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes());
+    // task: (fw, fb, db, k, lane) -> the bf16 piece of KV^T chunk fw at row
+    // d = 32 db + (lane & 31), columns 32 fb + 16 k + 8 (lane >> 5) .. + 7,
+    // from pieces q = 2 k and 2 k + 1 of the partials
+    constexpr int TASKS = NFW * 2 * NDB * 2 * 64;
+    const int per = (TASKS + a.nsplit - 1) / a.nsplit;
+    for (int t = split * per + tid; t < min(TASKS, (split + 1) * per); t += 256) {
+      const int ln = t & 63, k = (t >> 6) & 1, db = (t >> 7) % NDB, fb = (t / (128 * NDB)) & 1,
+                fwt = t / (256 * NDB);
+      const uint32_t o0 = (uint32_t)((((fwt * 2 + fb) * NDB + db) * 4 + 2 * k) * 64 + ln) * 16;
+      const uint32_t o1 = o0 + 64 * 16;
+      f32x4 s0 = f32x4{}, s1 = f32x4{};
+      for (int sp = 0; sp < a.nsplit; sp += 4) {
+        u32x4 v0[4], v1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t so = (uint32_t)(min(sp + u, a.nsplit - 1) * pstride);
+          v0[u] = ld16_agent(rpart, so + o0);
+          v1[u] = ld16_agent(rpart, so + o1);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (sp + u < a.nsplit) {
+            s0 += __builtin_bit_cast(f32x4, v0[u]);
+            s1 += __builtin_bit_cast(f32x4, v1[u]);
+          }
+      }
+      if (!ok) s0 = s1 = f32x4{kQNaN, kQNaN, kQNaN, kQNaN};
+      u32x4 o;
+      o[0] = pack_bf16x2(s0[0], s0[1]);
+      o[1] = pack_bf16x2(s0[2], s0[3]);
+      o[2] = pack_bf16x2(s1[0], s1[1]);
+      o[3] = pack_bf16x2(s1[2], s1[3]);
+      uint16_t* ch = kvc + (size_t)((fg0 + 64 * fwt) / 64) * 64 * D;
+      *reinterpret_cast<u32x4*>(ch + toff<64, kRowRead>(32 * db + (ln & 31), 32 * fb + 16 * k + 8 * (ln >> 5))) = o;
+    }
+    if (split == 0 && tid < FG) {  // ksum and bias of the group's features, in kperm order
+      float s = 0.f;
+      for (int sp = 0; sp < a.nsplit; ++sp)
+        s += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 16));
+      const int f = fg0 + tid;
+      ksumP[kperm(f)] = ok ? s : kQNaN;
+      biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
+    }
+  } else {
+    // task: (fw, fb, db, q, g, lane quad) -> KV rows f = .. crow(l, 4 q + e) (e = 0..3),
+    // columns d = 32 db + 4 cq .. + 3: four lanes' pieces, transposed
+    constexpr int TASKS = NFW * 2 * NDB * 4 * 2 * 8;
+    const int per = (TASKS + a.nsplit - 1) / a.nsplit;
+    for (int t = split * per + tid; t < min(TASKS, (split + 1) * per); t += 256) {
+      const int cq = t & 7, gg = (t >> 3) & 1, q = (t >> 4) & 3, db = (t >> 6) % NDB, fb = (t / (64 * NDB)) & 1,
+                fwt = t / (128 * NDB);
+      f32x4 sum[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};  // [lane i][element e]
+      for (int sp = 0; sp < a.nsplit; ++sp) {
+        u32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ln = 32 * gg + 4 * cq + i;
+          v[i] = ld16_agent(rpart, (uint32_t)(sp * pstride) +
+                                       (uint32_t)((((fwt * 2 + fb) * NDB + db) * 4 + q) * 64 + ln) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] += __builtin_bit_cast(f32x4, v[i]);
+      }
+      float* kvo = a.kv_out + (size_t)bh * F * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = fg0 + 64 * fwt + 32 * fb + 8 * q + 4 * gg + e;  // crow(lane of half gg, 4 q + e)
+        f32x4 o = {sum[0][e], sum[1][e], sum[2][e], sum[3][e]};
+        if (!ok) o = f32x4{kQNaN, kQNaN, kQNaN, kQNaN};
+        *reinterpret_cast<f32x4*>(kvo + (size_t)f * D + 32 * db + 4 * cq) = o;
+      }
+    }
+    if (split == 0 && tid < FG) {
+      float s = 0.f;
+      for (int sp = 0; sp < a.nsplit; ++sp)
+        s += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 16));
+      a.ks_out[(size_t)bh * F + fg0 + tid] = ok ? s : kQNaN;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- landmark-only pack
+struct LmPackArgs {
+  const uint16_t* K;
+  const uint16_t* V;
+  int N, L;
+  unsigned char* pack_bh;  // [BH][nlb chunks]
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void lm_pack_kernel(LmPackArgs a) {
+  __shared__ uint16_t vrows[32][D + 8];
+  const int nlb = (a.L + 31) / 32;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int bh = item / nlb, jb = item % nlb;
+  const PackLayout pl{D, 0, a.L, nlb};
+  uint16_t* kl = reinterpret_cast<uint16_t*>(a.pack_bh + (size_t)bh * pl.bh_bytes()) + (size_t)jb * pl.chunk_elems();
+  landmark_chunk<D>(a.K + (size_t)bh * a.N * D, a.V + (size_t)bh * a.N * D, a.N, a.L, jb, kl, vrows, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- host side
-static void kv2_plan(const Problem& p, int* nsplit, int* chunk) {
-  const int step = 32 * (8 / (p.F / 32));
-  const int bh = p.B * p.H;
-  const int nsteps = (p.N + step - 1) / step;
-  int want = 256 / bh;
-  if (want < 1) want = 1;
-  int maxs = nsteps / 2;
-  if (maxs < 1) maxs = 1;
-  if (want > maxs) want = maxs;
-  const int steps_per = (nsteps + want - 1) / want;
-  *chunk = steps_per * step;
-  *nsplit = (p.N + *chunk - 1) / *chunk;
+// Compute units the grid may fill (one workgroup each), for the device that is
+// current: the workspace is sized for at most 256, the MI355X count.
+static int kvs_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    v = n < 256 ? n : 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+struct KvsPlan {
+  int FG, NG, groups, nsplit, chunk;
+  size_t part_bytes, cnt_bytes;  // fp32 partials; counters (256-byte aligned)
+};
+
+static KvsPlan kvs_plan(const Problem& p, int cus) {
+  KvsPlan k;
+  k.FG = p.F < 128 ? p.F : 128;
+  k.NG = p.F / k.FG;
+  const int step = k.FG >= 128 ? 64 : 128;
+  k.groups = p.B * p.H * k.NG;
+  int ns = cus / k.groups;
+  const int maxs = (p.N + 2 * step - 1) / (2 * step);  // at least two steps per split
+  if (ns > maxs) ns = maxs;
+  if (ns < 1) ns = 1;
+  const int per = (p.N + ns - 1) / ns;
+  k.chunk = (per + step - 1) / step * step;
+  k.nsplit = (p.N + k.chunk - 1) / k.chunk;  // every split non-empty
+  k.part_bytes = (size_t)k.groups * k.nsplit * (size_t)(k.FG * p.D + k.FG) * 4;
+  k.cnt_bytes = ((size_t)k.groups * 4 + 255) / 256 * 256;
+  return k;
 }
 
 static PackLayout pack_layout(const Problem& p, int L) {
@@ -429,129 +742,107 @@ static PackLayout pack_layout(const Problem& p, int L) {
   return pl;
 }
 
-size_t fused_workspace_bytes(const Problem& p, int L) {
-  int ns, ch;
-  kv2_plan(p, &ns, &ch);
-  const PackLayout pl = pack_layout(p, L);
-  return (size_t)p.B * p.H * ns * (size_t)(p.F * p.D + p.F) * 4 + (size_t)p.B * p.H * pl.bh_bytes() +
-         (size_t)p.H * pl.w_bytes();
+static bool kvs_supported(const Problem& p) {
+  if (p.dtype != 1 || (p.D != 64 && p.D != 128)) return false;
+  if (p.proj) return p.fmap == kElu1 && p.F % 128 == 0;
+  return p.F == p.D;
 }
 
-template <int D, int F, bool PROJ, int MAP>
-static hipError_t launch_kv2_t(const Problem& p, const Kv2Args& ka, const PackArgs& pa, hipStream_t s,
-                               StageTimer* t) {
-  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit * p.B * p.H), dim3(512), 0, s, ka);
+size_t fused_workspace_bytes(const Problem& p, int L) {
+  const KvsPlan k = kvs_plan(p, 256);
+  const PackLayout pl = pack_layout(p, L);
+  return k.part_bytes + k.cnt_bytes + (size_t)p.B * p.H * pl.bh_bytes() + (size_t)p.H * pl.w_bytes();
+}
+
+size_t kv2_reduce_workspace_bytes(const Problem& p) {
+  const KvsPlan k = kvs_plan(p, 256);
+  return k.part_bytes + k.cnt_bytes;
+}
+
+template <int D, int F, bool PROJ, int MAP, bool PACK>
+static hipError_t launch_kvs_t(const KvsArgs& a, int groups, hipStream_t s, StageTimer* t) {
+  hipLaunchKernelGGL(kv_stage_reset_kernel, dim3(1), dim3(256), 0, s, a.counters, groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  t->mark();
-  constexpr int FJ = 2048 / D > F ? F : 2048 / D;
-  const int jobs = F / FJ + (pa.L + 31) / 32;
-  hipLaunchKernelGGL((kv2_pack_kernel<D, F, PROJ>), dim3(jobs * p.B * p.H), dim3(256), 0, s, pa);
+  if (t) t->mark();
+  hipLaunchKernelGGL((kv_stage_kernel<D, F, PROJ, MAP, PACK>), dim3(groups * a.nsplit), dim3(256), 0, s, a);
   e = hipGetLastError();
-  t->mark();
+  if (t) t->mark();
   return e;
+}
+
+template <bool PACK>
+static hipError_t launch_kvs(const Problem& p, const KvsArgs& a, int groups, hipStream_t s, StageTimer* t) {
+  if (p.D == 128) {
+    if (p.proj) {
+      if (p.F == 256) return launch_kvs_t<128, 256, true, kElu1, PACK>(a, groups, s, t);
+      if (p.F == 512) return launch_kvs_t<128, 512, true, kElu1, PACK>(a, groups, s, t);
+      return hipErrorInvalidValue;
+    }
+    if (p.fmap == kRelu) return launch_kvs_t<128, 128, false, kRelu, PACK>(a, groups, s, t);
+    if (p.fmap == kSoftmax) return launch_kvs_t<128, 128, false, kSoftmax, PACK>(a, groups, s, t);
+    return launch_kvs_t<128, 128, false, kElu1, PACK>(a, groups, s, t);
+  }
+  if (p.proj) {
+    if (p.F == 256) return launch_kvs_t<64, 256, true, kElu1, PACK>(a, groups, s, t);
+    if (p.F == 512) return launch_kvs_t<64, 512, true, kElu1, PACK>(a, groups, s, t);
+    return hipErrorInvalidValue;
+  }
+  if (p.fmap == kRelu) return launch_kvs_t<64, 64, false, kRelu, PACK>(a, groups, s, t);
+  if (p.fmap == kSoftmax) return launch_kvs_t<64, 64, false, kSoftmax, PACK>(a, groups, s, t);
+  return launch_kvs_t<64, 64, false, kElu1, PACK>(a, groups, s, t);
+}
+
+static KvsArgs kvs_args(const Problem& p, const KvsPlan& k, const void* K, const void* V, const void* W,
+                        const float* bias, int L, unsigned char* ws) {
+  KvsArgs a{};
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.W = static_cast<const uint16_t*>(W);
+  a.bias = bias;
+  a.H = p.H;
+  a.N = p.N;
+  a.L = L;
+  a.nsplit = k.nsplit;
+  a.chunk = k.chunk;
+  a.part = reinterpret_cast<float*>(ws);
+  a.counters = reinterpret_cast<unsigned*>(ws + k.part_bytes);
+  a.spin_limit = 1u << 20;  // about a second of polling
+  return a;
 }
 
 hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void* W, const float* bias, int L,
                       void* ws, FusedPack* pk, hipStream_t s, StageTimer* t) {
-  int nsplit, chunk;
-  kv2_plan(p, &nsplit, &chunk);
+  if (!kvs_supported(p)) return hipErrorInvalidValue;
+  const KvsPlan k = kvs_plan(p, kvs_cus());
+  const KvsPlan kw = kvs_plan(p, 256);  // the workspace's layout
   const PackLayout pl = pack_layout(p, L);
   unsigned char* w8 = static_cast<unsigned char*>(ws);
-  float* part = reinterpret_cast<float*>(w8);
-  unsigned char* pbh = w8 + (size_t)p.B * p.H * nsplit * (size_t)(p.F * p.D + p.F) * 4;
+  unsigned char* pbh = w8 + kw.part_bytes + kw.cnt_bytes;
   unsigned char* pw = pbh + (size_t)p.B * p.H * pl.bh_bytes();
   pk->pack_bh = pbh;
   pk->pack_w = pw;
   pk->bh_bytes = pl.bh_bytes();
   pk->w_bytes = pl.w_bytes();
-
-  Kv2Args ka;
-  ka.K = static_cast<const uint16_t*>(K);
-  ka.V = static_cast<const uint16_t*>(V);
-  ka.W = static_cast<const uint16_t*>(W);
-  ka.bias = bias;
-  ka.H = p.H;
-  ka.N = p.N;
-  ka.chunk = chunk;
-  ka.nsplit = nsplit;
-  ka.part = part;
-  ka.pack_w = pw;
-  PackArgs pa;
-  pa.part = part;
-  pa.nsplit = nsplit;
-  pa.K = ka.K;
-  pa.V = ka.V;
-  pa.W = ka.W;
-  pa.bias = bias;
-  pa.H = p.H;
-  pa.N = p.N;
-  pa.L = L;
-  pa.pack_bh = pbh;
-  pa.pack_w = pw;
-  pa.lm_only = 0;
-  if (p.dtype != 1) return hipErrorInvalidValue;
-  if (p.D == 128) {
-    if (p.proj) return launch_kv2_t<128, 256, true, kElu1>(p, ka, pa, s, t);
-    if (p.fmap == kRelu) return launch_kv2_t<128, 128, false, kRelu>(p, ka, pa, s, t);
-    if (p.fmap == kSoftmax) return launch_kv2_t<128, 128, false, kSoftmax>(p, ka, pa, s, t);
-    return launch_kv2_t<128, 128, false, kElu1>(p, ka, pa, s, t);
-  }
-  if (p.D == 64) {
-    if (p.proj) return launch_kv2_t<64, 256, true, kElu1>(p, ka, pa, s, t);
-    if (p.fmap == kRelu) return launch_kv2_t<64, 64, false, kRelu>(p, ka, pa, s, t);
-    if (p.fmap == kSoftmax) return launch_kv2_t<64, 64, false, kSoftmax>(p, ka, pa, s, t);
-    return launch_kv2_t<64, 64, false, kElu1>(p, ka, pa, s, t);
-  }
-  return hipErrorInvalidValue;
-}
-
-// The key/value reduction on its own (ttr_kv_reduce, bf16 IO): the partial
-// kernel into the workspace, then the fixed-order sum of the split partials into
-// fp32 KV [F][D] and ksum [F] (the partials' own layout). Workspace: the
-// partials, then room for the W^T chunks the partial kernel also writes.
-size_t kv2_reduce_workspace_bytes(const Problem& p) {
-  int ns, ch;
-  kv2_plan(p, &ns, &ch);
-  return (size_t)p.B * p.H * ns * (size_t)(p.F * p.D + p.F) * 4 + (size_t)p.H * p.F * p.D * 2;
-}
-
-template <int D, int F, bool PROJ, int MAP>
-static void launch_kv2_partial_t(const Problem& p, const Kv2Args& ka, hipStream_t s) {
-  hipLaunchKernelGGL((kv2_partial_kernel<D, F, PROJ, MAP>), dim3(ka.nsplit * p.B * p.H), dim3(512), 0, s, ka);
+  KvsArgs a = kvs_args(p, k, K, V, W, bias, L, w8);
+  a.counters = reinterpret_cast<unsigned*>(w8 + kw.part_bytes);
+  a.pack_bh = pbh;
+  a.bh_bytes = pl.bh_bytes();
+  a.pack_w = pw;
+  return launch_kvs<true>(p, a, k.groups, s, t);
 }
 
 hipError_t launch_kv2_reduce(const Problem& p, const void* K, const void* V, const void* W, const float* bias,
                              float* KV, float* ksum, void* ws, hipStream_t s) {
-  if (p.dtype != 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
-  int nsplit, chunk;
-  kv2_plan(p, &nsplit, &chunk);
+  if (!kvs_supported(p)) return hipErrorInvalidValue;
+  const KvsPlan k = kvs_plan(p, kvs_cus());
+  const KvsPlan kw = kvs_plan(p, 256);
   unsigned char* w8 = static_cast<unsigned char*>(ws);
-  Kv2Args ka;
-  ka.K = static_cast<const uint16_t*>(K);
-  ka.V = static_cast<const uint16_t*>(V);
-  ka.W = static_cast<const uint16_t*>(W);
-  ka.bias = bias;
-  ka.H = p.H;
-  ka.N = p.N;
-  ka.chunk = chunk;
-  ka.nsplit = nsplit;
-  ka.part = reinterpret_cast<float*>(w8);
-  ka.pack_w = w8 + (size_t)p.B * p.H * nsplit * (size_t)(p.F * p.D + p.F) * 4;
-  if (p.D == 128) {
-    if (p.proj) launch_kv2_partial_t<128, 256, true, kElu1>(p, ka, s);
-    else if (p.fmap == kRelu) launch_kv2_partial_t<128, 128, false, kRelu>(p, ka, s);
-    else if (p.fmap == kSoftmax) launch_kv2_partial_t<128, 128, false, kSoftmax>(p, ka, s);
-    else launch_kv2_partial_t<128, 128, false, kElu1>(p, ka, s);
-  } else {
-    if (p.proj) launch_kv2_partial_t<64, 256, true, kElu1>(p, ka, s);
-    else if (p.fmap == kRelu) launch_kv2_partial_t<64, 64, false, kRelu>(p, ka, s);
-    else if (p.fmap == kSoftmax) launch_kv2_partial_t<64, 64, false, kSoftmax>(p, ka, s);
-    else launch_kv2_partial_t<64, 64, false, kElu1>(p, ka, s);
-  }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_kv_finalize(p, ka.part, nsplit, KV, ksum, s);
+  KvsArgs a = kvs_args(p, k, K, V, W, bias, 0, w8);
+  a.counters = reinterpret_cast<unsigned*>(w8 + kw.part_bytes);
+  a.kv_out = KV;
+  a.ks_out = ksum;
+  return launch_kvs<false>(p, a, k.groups, s, nullptr);
 }
 
 // Every key j < L of a landmark pack alone (the chunks of the softmax-only query
@@ -565,22 +856,19 @@ hipError_t launch_lm_pack(const Problem& p, const void* K, const void* V, int L,
                           hipStream_t s) {
   if (p.dtype != 1 || L < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
   const PackLayout pl{p.D, 0, L, (L + 31) / 32};
-  PackArgs pa{};
-  pa.K = static_cast<const uint16_t*>(K);
-  pa.V = static_cast<const uint16_t*>(V);
-  pa.H = p.H;
-  pa.N = p.N;
-  pa.L = L;
-  pa.pack_bh = static_cast<unsigned char*>(ws);
-  pa.lm_only = 1;
-  pk->pack_bh = pa.pack_bh;
+  LmPackArgs a{};
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.N = p.N;
+  a.L = L;
+  a.pack_bh = static_cast<unsigned char*>(ws);
+  pk->pack_bh = a.pack_bh;
   pk->pack_w = nullptr;
   pk->bh_bytes = pl.bh_bytes();
   pk->w_bytes = 0;
   const dim3 grid((unsigned)(pl.nlb * p.B * p.H));
-  // (the landmark jobs do not depend on the feature count: any instantiation serves)
-  if (p.D == 128) hipLaunchKernelGGL((kv2_pack_kernel<128, 256, true>), grid, dim3(256), 0, s, pa);
-  else hipLaunchKernelGGL((kv2_pack_kernel<64, 256, true>), grid, dim3(256), 0, s, pa);
+  if (p.D == 128) hipLaunchKernelGGL((lm_pack_kernel<128>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((lm_pack_kernel<64>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
