@@ -79,11 +79,11 @@ __device__ __forceinline__ int xcd_item(int i, int n) {
 // V_L rows through LDS (vrows, 32 x (D + 8) bf16) so that V_L^T [D][32 j]
 // (landmark jl in column kperm(jl)) is written in 16-byte pieces. Landmarks
 // past L are zero. All 256 threads of the workgroup take part.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void landmark_chunk(const uint16_t* K, const uint16_t* V, int N, int L, int jb,
                                                uint16_t* kl, uint16_t (*vrows)[D + 8], int tid) {
   uint16_t* vl = kl + 32 * D;
-  for (int u = tid; u < 2 * 32 * (D / 8); u += 256) {
+  for (int u = tid; u < 2 * 32 * (D / 8); u += NT) {
     const int isv = u >= 32 * (D / 8);
     const int uu = u - isv * 32 * (D / 8);
     const int jl = uu / (D / 8), d0 = (uu % (D / 8)) * 8, j = jb * 32 + jl;
@@ -92,15 +92,15 @@ __device__ __forceinline__ void landmark_chunk(const uint16_t* K, const uint16_t
     if (isv) *reinterpret_cast<Vec8<uint16_t>*>(&vrows[jl][d0]) = v;
     else st8(kl + toff<D, kRowRead>(jl, d0), v);
   }
-  __syncthreads();
-  for (int u = tid; u < D * 4; u += 256) {  // piece (row d, columns 8q .. 8q + 7)
+  barrier_lds();
+  for (int u = tid; u < D * 4; u += NT) {  // piece (row d, columns 8q .. 8q + 7)
     const int d = u / 4, q = u % 4;
     Vec8<uint16_t> v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v.v[e] = vrows[kperm(8 * q + e)][d];  // kperm is its own inverse
     st8(vl + toff32(d, 8 * q), v);
   }
-  __syncthreads();
+  barrier_lds();
 }
 
 // ---------------------------------------------------------------- key/value stage
@@ -125,23 +125,23 @@ template <int D, int F>
 struct KvsShape {
   static constexpr int FG = F < 128 ? F : 128;  // features of a workgroup
   static constexpr int NG = F / FG;             // feature groups of a head
-  static constexpr int NFW = FG / 64;           // waves across the group's features
-  static constexpr int NTG = 4 / NFW;           // token groups of 32 per step
+  static constexpr int NPW = FG / 64;           // producer (and consumer) waves across the group's features
+  static constexpr int NTG = 4 / NPW;           // token groups of 32 per step
   static constexpr int STEP = 32 * NTG;         // tokens of a workgroup step
   static constexpr int NKB = D / 16;            // k-blocks of a K row
   static constexpr int NDB = D / 32;            // 32-column blocks of V
-  static constexpr int VP = STEP * D / 8 / 256;  // 16-byte V pieces per thread per step
+  static constexpr int VP = STEP * D / 8 / 256;  // 16-byte V pieces per consumer thread per step
   static constexpr int PART = FG * D + FG;       // floats of one split's partial
   static_assert(F == 64 || F % 128 == 0, "feature count");
   static_assert(VP * 256 * 8 == STEP * D && VP >= 1, "whole V pieces");
-  static constexpr int vbuf_bytes = 2 * STEP * D * 2;            // V double buffer
-  static constexpr int wtile_bytes = D * FG * 2;                 // W tile (prologue)
-  static constexpr int stats_bytes = 4 * 2 * 32 * 8;             // softmax (max, 1 / sum) per wave and step parity
-  static constexpr int main_bytes = vbuf_bytes + wtile_bytes + stats_bytes;
-  static constexpr int red_bytes = (NTG - 1) * NFW * (64 * D + 64) * 4;  // token-group partials
-  static constexpr int lm_bytes = 32 * (D + 8) * 2;
-  static constexpr int bytes = main_bytes > red_bytes ? (main_bytes > lm_bytes ? main_bytes : lm_bytes)
-                                                      : (red_bytes > lm_bytes ? red_bytes : lm_bytes);
+  static constexpr int vbuf_bytes = 2 * STEP * D * 2;        // V double buffer [2][STEP][D]
+  static constexpr int pbuf_bytes = 2 * 4 * 64 * 32 * 2;     // phi^T double buffer [2][4 producers][64 f][32 tok]
+  static constexpr int wtile_bytes = D * FG * 2;             // W tile (prologue)
+  static constexpr int stats_bytes = 4 * 2 * 32 * 8;         // softmax (max, 1 / sum) per producer and step parity
+  static constexpr int lm_bytes = 32 * (D + 8) * 2;          // landmark V rows (prologue)
+  static constexpr int main_bytes = vbuf_bytes + pbuf_bytes + wtile_bytes + stats_bytes + lm_bytes;
+  static constexpr int red_bytes = (NTG - 1) * NPW * (64 * D + 64) * 4;  // token-group partials
+  static constexpr int bytes = main_bytes > red_bytes ? main_bytes : red_bytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -162,24 +162,39 @@ __device__ __forceinline__ void st16_agent(__amdgpu_buffer_rsrc_t r, uint32_t of
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
 }
 
+// Eight waves, two per SIMD: waves 0-3 are producers, 4-7 consumers (wave w
+// and w + 4 share a SIMD, so one's vector work runs beside the other's
+// matrix products). Producer (fp, tg) computes, for the 32 tokens of token
+// group tg of a step and its 64 features fp:
+//   phi[tok x 64] = map(K[tok x D] . W[:, 64 features] + b)     (A = K rows straight
+//                    from global memory into registers, B = W in registers)
+// and writes phi^T [64 f][32 tok] to LDS; consumer (fc = fp, tg) accumulates
+//   KV[64 x D] += phi^T . V                                       (A = phi^T from LDS,
+//                    B = V read transposed from LDS)
+// Iteration t: producers map step t, consumers take step t - 1; one barrier.
 template <int D, int F, bool PROJ, int MAP, bool PACK>
-__global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
+__global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   using S = KvsShape<D, F>;
-  constexpr int FG = S::FG, NG = S::NG, NFW = S::NFW, NTG = S::NTG, STEP = S::STEP, NKB = S::NKB,
+  constexpr int FG = S::FG, NG = S::NG, NPW = S::NPW, NTG = S::NTG, STEP = S::STEP, NKB = S::NKB,
                 NDB = S::NDB, VP = S::VP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
   uint16_t* const vbuf = reinterpret_cast<uint16_t*>(smem);                       // [2][STEP][D] kTrRead
-  uint16_t* const wt = reinterpret_cast<uint16_t*>(smem + S::vbuf_bytes);         // [D][FG] kTrRead, rows kperm'd
-  float2* const stats = reinterpret_cast<float2*>(smem + S::vbuf_bytes + S::wtile_bytes);  // [4][2][32]
+  uint16_t* const pbuf = reinterpret_cast<uint16_t*>(smem + S::vbuf_bytes);       // [2][4][64][32] toff32
+  uint16_t* const wt = reinterpret_cast<uint16_t*>(smem + S::vbuf_bytes + S::pbuf_bytes);  // [D][FG], rows kperm'd
+  float2* const stats = reinterpret_cast<float2*>(smem + S::vbuf_bytes + S::pbuf_bytes + S::wtile_bytes);
+  auto lmrows = reinterpret_cast<uint16_t(*)[D + 8]>(smem + S::vbuf_bytes + S::pbuf_bytes + S::wtile_bytes +
+                                                     S::stats_bytes);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
-  const int fw = w % NFW, tg = w / NFW;
+  const bool producer = w < 4;
+  const int pw = w & 3;                   // index among the producers (or the consumers)
+  const int fs = pw % NPW, tg = pw / NPW;  // feature slice, token group
   const int item = xcd_item(blockIdx.x, gridDim.x);
   const int split = item % a.nsplit, group = item / a.nsplit;
   const int bh = group / NG, fgi = group % NG, h = bh % a.H;
   const int fg0 = fgi * FG;         // first feature of the group
-  const int fw0 = fg0 + 64 * fw;    // first of this wave's 64 features
+  const int fs0 = fg0 + 64 * fs;    // first of this wave's 64 features
   const int N = a.N;
   const int t_begin = split * a.chunk;
   const int t_end = min(N, t_begin + a.chunk);
@@ -190,8 +205,9 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
   // ---- operand streams, through buffer resources that end at the range's
   // last token: a row past it reads as zeros (so it adds nothing to KV, and
   // a fixed phi(0 W + b) to ksum, taken out after the loop). K rows of step j
-  // for this wave's 32 tokens, as the A operand (lane = token c, k-slots =
-  // columns 16 kb + 8 g ..); V rows of step j: piece tid + 256 i of the step.
+  // for a producer's 32 tokens, as the A operand (lane = token c, k-slots =
+  // columns 16 kb + 8 g ..); V rows of step j: piece ct + 256 i of the step
+  // for consumer thread ct.
   const uint32_t range_bytes = (uint32_t)((size_t)t_end * D * 2);
   const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(Kp, range_bytes);
   const __amdgpu_buffer_rsrc_t rV = buffer_rsrc(Vp, range_bytes);
@@ -201,10 +217,11 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
     for (int kb = 0; kb < NKB; ++kb)
       kf[kb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rK, (int)(off + 32 * kb), 0, 0));
   };
+  const int ct = tid - 256;  // consumer thread
   auto load_v = [&](int j, u32x4 (&vs)[VP]) {
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
-      const int P = tid + 256 * i, row = P / (D / 8), p = P % (D / 8);
+      const int P = ct + 256 * i, row = P / (D / 8), p = P % (D / 8);
       vs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rV, (int)((uint32_t)(t_begin + j * STEP + row) * (D * 2) + p * 16), 0, 0));
     }
@@ -213,282 +230,324 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
     uint16_t* vt = vbuf + buf * STEP * D;
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
-      const int P = tid + 256 * i, row = P / (D / 8), p = P % (D / 8);
+      const int P = ct + 256 * i, row = P / (D / 8), p = P % (D / 8);
       *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = vs[i];
     }
   };
-
-  // Every load is issued unconditionally (steps past the range read zeros),
-  // so the compiler's count of loads in flight is exact on every path and
-  // each wait covers only the loads it needs.
-  Frag<uint16_t> kf0[NKB], kf1[NKB];
-  u32x4 vs0[VP], vs1[VP];
-  load_k(0, kf0);
-  load_k(1, kf1);
-  load_v(0, vs0);
-  load_v(1, vs1);
-
-  // ---- W slice as the B operand (lane = feature fw0 + 32 fb + c, k-slots =
-  // rows 16 kb + 8 g ..): the group's W columns are staged as a [D][FG] tile
-  // whose rows are permuted by kperm within each block of 16, so that the
-  // transposing read (which hands a lane its k-rows in C-row order) returns
-  // them in natural order, the order of the K fragments.
-  Frag<uint16_t> wf[2][NKB];
+  // ---- landmark chunks of this (batch, head), spread over its workgroups
+  // (they need no partial: done first, beside the W loads)
+  if constexpr (PACK) {
+    const int nlb = (a.L + 31) / 32;
+    if (nlb > 0) {
+      const PackLayout pl{D, F, a.L, nlb};
+      uint16_t* lmc = reinterpret_cast<uint16_t*>(a.pack_bh + (size_t)bh * a.bh_bytes + pl.vec_bytes() + pl.kv_bytes());
+      const int nwg = NG * a.nsplit, me = fgi * a.nsplit + split;
+      for (int jb = me; jb < nlb; jb += nwg)
+        landmark_chunk<D, 512>(Kp, Vp, N, a.L, jb, lmc + (size_t)jb * pl.chunk_elems(), lmrows, tid);
+    }
+  }
+  // ---- the group's W columns as a [D][FG] tile whose rows are permuted by
+  // kperm within each block of 16, so that the transposing read (which hands
+  // a lane its k-rows in C-row order) returns them in natural order, the
+  // order of the K fragments
   if constexpr (PROJ) {
     const uint16_t* W = a.W + (size_t)h * D * F + fg0;
-    constexpr int WP = D * FG / 8 / 256;
-    static_assert(WP * 256 * 8 == D * FG, "whole W pieces");
+    constexpr int WP = D * FG / 8 / 512;
+    static_assert(WP * 512 * 8 == D * FG, "whole W pieces");
     u32x4 wv[WP];
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
-      const int P = tid + 256 * i, d = P / (FG / 8), p = P % (FG / 8);
+      const int P = tid + 512 * i, d = P / (FG / 8), p = P % (FG / 8);
       wv[i] = *reinterpret_cast<const u32x4*>(W + (size_t)d * F + p * 8);
     }
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
-      const int P = tid + 256 * i, d = P / (FG / 8), p = P % (FG / 8);
+      const int P = tid + 512 * i, d = P / (FG / 8), p = P % (FG / 8);
       *reinterpret_cast<u32x4*>(wt + toff<FG, kTrRead>((d & ~15) | kperm(d & 15), p * 8)) = wv[i];
     }
-    __syncthreads();
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) wf[fb][kb] = tr_frag<FG>(wt, 16 * kb, 64 * fw + 32 * fb, lane);
-  } else {
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int f = fw0 + 32 * fb + c;
-        u32x4 u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int d0 = 16 * kb + 8 * g + 2 * q;
-          u[q] = (d0 == f ? 0x3f80u : 0u) | (d0 + 1 == f ? 0x3f800000u : 0u);  // bf16 1.0 on the diagonal
-        }
-        wf[fb][kb] = __builtin_bit_cast(bf16x8, u);
-      }
+    barrier_lds();
   }
-  // The fused query kernel's W^T chunks [64 f][D] (kRowRead) are per head:
-  // batch 0's first split writes them, each lane the 16-byte row pieces of
-  // the W slice it holds.
-  if constexpr (PACK) {  // (the identity map too: the query kernel multiplies by it to transpose Q)
-    if (split == 0 && bh < a.H && tg == 0) {
-      uint16_t* wc = reinterpret_cast<uint16_t*>(a.pack_w + (size_t)h * F * D * 2) + (size_t)(fw0 / 64) * 64 * D;
+  const size_t pstride = (size_t)S::PART * 4;
+  const __amdgpu_buffer_rsrc_t rpart = buffer_rsrc(a.part + (size_t)group * a.nsplit * S::PART,
+                                                   (uint32_t)(a.nsplit * pstride));
+  constexpr int RF = 64 * D + 64;  // floats of one wave slice's KV and ksum (token-group sums)
+  float* red = reinterpret_cast<float*>(smem);
+  // phi^T of a producer: [64 f][32 tok] in the toff32 layout, tokens of each
+  // half in kperm column order, so that a consumer's plain 16-byte row read
+  // hands it the tokens in the C-row order of the transposed V fragments
+  auto ptile = [&](int buf, int p) -> uint16_t* { return pbuf + (buf * 4 + p) * 64 * 32; };
+  // Both roles run nsteps + 1 iterations with one barrier each (but the
+  // first), then the same barriers of the token-group sums: their s_barrier
+  // counts match. Each role's state lives in its own branch.
+  if (producer) {
+    // ---- producer: W slice as the B operand (lane = feature fs0 + 32 fb + c,
+    // k-slots = rows 16 kb + 8 g ..)
+    Frag<uint16_t> wf[2][NKB];
+    if constexpr (PROJ) {
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          *reinterpret_cast<u32x4*>(wc + toff<D, kRowRead>(32 * fb + c, 16 * kb + 8 * g)) =
-              __builtin_bit_cast(u32x4, wf[fb][kb]);
-    }
-  }
-
-  // The bias enters the map, not the product: for elu + 1,
-  // phi = max(x + (b + 1), min(exp2(x log2e + b log2e), 1)) costs what the map
-  // without a bias does (an fma in place of the multiply, an add either way).
-  float bcol[2], bl2[2];  // per lane (its feature column): b + 1 (elu + 1) or b, and b log2e
-#pragma unroll
-  for (int fb = 0; fb < 2; ++fb) {
-    const float bc = a.bias ? a.bias[(size_t)h * F + fw0 + 32 * fb + c] : 0.f;
-    bcol[fb] = MAP == kElu1 ? bc + 1.f : bc;
-    bl2[fb] = bc * kLog2e;
-  }
-  auto phi_b = [&](float x, int fb, float2 st) -> float {
-    if constexpr (MAP == kElu1) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, bl2[fb]));
-      return fmaxf(x + bcol[fb], fminf(fmaxf(e, 0.f), 1.f));
+        for (int kb = 0; kb < NKB; ++kb) wf[fb][kb] = tr_frag<FG>(wt, 16 * kb, 64 * fs + 32 * fb, lane);
     } else {
-      return phi_of<MAP>(x + bcol[fb], st.x, st.y);
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int f = fs0 + 32 * fb + c;
+          u32x4 u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d0 = 16 * kb + 8 * g + 2 * q;
+            u[q] = (d0 == f ? 0x3f80u : 0u) | (d0 + 1 == f ? 0x3f800000u : 0u);  // bf16 1.0 on the diagonal
+          }
+          wf[fb][kb] = __builtin_bit_cast(bf16x8, u);
+        }
     }
-  };
-  // softmax map (identity projection, F == D): each lane's bias values for the
-  // columns its K fragments hold, for the token statistics
-  float kbias[MAP == kSoftmax ? NKB * 8 : 1];
-  if constexpr (MAP == kSoftmax) {
+    // The fused query kernel's W^T chunks [64 f][D] (kRowRead) are per head:
+    // batch 0's first split writes them, each producer lane the 16-byte row
+    // pieces of the W slice it holds (the identity map too: the query kernel
+    // multiplies by it to transpose Q).
+    if constexpr (PACK) {
+      if (split == 0 && bh < a.H && tg == 0) {
+        uint16_t* wc = reinterpret_cast<uint16_t*>(a.pack_w + (size_t)h * F * D * 2) + (size_t)(fs0 / 64) * 64 * D;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kbias[8 * kb + i] = a.bias ? a.bias[(size_t)h * F + 16 * kb + 8 * g + i] : 0.f;
-  }
-  float2* const wstats = stats + w * 64;  // [2 parities][32 tokens]
-  // the softmax statistics (max, 1 / sum) of this wave's 32 tokens of a step,
-  // from their K rows (half in this lane, half in lane ^ 32)
-  auto token_stats = [&](const Frag<uint16_t> (&kf)[NKB], int par) {
-    if constexpr (MAP == kSoftmax) {
-      float z[NKB * 8], m, inv;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        frag_to_f32(kf[kb], z + 8 * kb);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) z[8 * kb + i] += kbias[8 * kb + i];
-      }
-      softmax_stats<NKB * 8, 32>(z, m, inv);
-      if (g == 0) wstats[par * 32 + c] = float2{m, inv};
-    }
-  };
-
-  f32x16 kv[2][NDB];
-#pragma unroll
-  for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) kv[fb][db] = f32x16{};
-  float ks[2] = {0.f, 0.f};
-  f32x16 c1a[2], c1b[2];               // first products of even / odd steps
-  Frag<uint16_t> pba[2][2], pbb[2][2];  // mapped phi of even / odd steps, as A operands
-
-  auto gemm1 = [&](const Frag<uint16_t> (&kf)[NKB], f32x16 (&acc)[2]) {
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb) acc[fb] = mma_from(f32x16{}, kf[0], wf[fb][0]);
-#pragma unroll
-    for (int kb = 1; kb < NKB; ++kb)
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb) mma(acc[fb], kf[kb], wf[fb][kb]);
-  };
-  // phi of one step and feature block fb as the second product's A operands;
-  // ksum from the rounded pairs (the values that product uses), two per v_dot2.
-  const uint32_t ones2 = 0x3f803f80u;  // bf16 (1, 1)
-  auto map_fb = [&](int par, int fb, const f32x16& acc, Frag<uint16_t> (&pb)[2]) {
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float2 st = float2{0.f, 1.f};
-      if constexpr (MAP == kSoftmax) st = wstats[par * 32 + crow(lane, r)];
-      p[r] = phi_b(acc[r], fb, st);
-    }
-    uint32_t u[16 / 2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x2 pr = {(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
-      ks[fb] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, ones2), ks[fb], false);
-      u[i] = __builtin_bit_cast(uint32_t, pr);
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const u32x4 v = {u[4 * hh], u[4 * hh + 1], u[4 * hh + 2], u[4 * hh + 3]};
-      pb[hh] = __builtin_bit_cast(bf16x8, v);
-    }
-  };
-  auto gemm2 = [&](int buf, const Frag<uint16_t> (&pb)[2][2]) {
-    const uint16_t* vt = vbuf + buf * STEP * D;
-    Frag<uint16_t> vf[NDB][2];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) vf[db][hh] = tr_frag<D>(vt, 32 * tg + 16 * hh, 32 * db, lane);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb) mma(kv[fb][db], pb[fb][hh], vf[db][hh]);
-  };
-  // one MFMA, then N vector instructions, for the region's MFMAs
-  auto interleave = [&](auto n) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sched_group<kSchedMfma, 1>();
-      sched_group<kSchedAnyValu, decltype(n)::value>();
-    }
-  };
-
-  // ---- prologue: the first product of step 0
-  token_stats(kf0, 0);
-  gemm1(kf0, c1a);
-  load_k(2, kf0);
-
-  // ---- iteration j: the first product of step j + 1, the map of step j, the
-  // second product of step j - 1; V of step j into LDS buffer j & 1 (read in
-  // iteration j + 1); loads of K for step j + 3 and V for step j + 2. Every
-  // operation is unconditional (steps past the range compute on zero rows
-  // whose results are never used), so an iteration is one basic block: its
-  // two regions each pair 16 MFMAs with half of the map's vector work, and
-  // the compiler's count of loads in flight is exact. Even and odd iterations
-  // hold their operands in separate registers, so the loop is unrolled by
-  // two; iteration 0 has no second product.
-  auto iteration = [&](int j, auto odd, auto with2) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(odd)::value;
-    constexpr bool W2 = decltype(with2)::value;
-    Frag<uint16_t>(&kn)[NKB] = ODD ? kf0 : kf1;  // K of step j + 1
-    f32x16(&cn)[2] = ODD ? c1a : c1b;            // its first product
-    f32x16(&cc)[2] = ODD ? c1b : c1a;            // step j's first product
-    Frag<uint16_t>(&pc)[2][2] = ODD ? pbb : pba;  // step j's mapped phi
-    Frag<uint16_t>(&pp)[2][2] = ODD ? pba : pbb;  // step j - 1's
-    u32x4(&vs)[VP] = ODD ? vs1 : vs0;            // V of step j
-    if constexpr (W2) barrier_lds();  // V of step j - 1 is in LDS; step j - 2's buffer is free
-    token_stats(kn, (j + 1) & 1);
-    // region A: the second product of step j - 1 (its V fragments one
-    // 32-column block ahead of their MFMAs) beside the map of step j's first feature block
-    if constexpr (W2) gemm2((j - 1) & 1, pp);
-    map_fb(j & 1, 0, cc[0], pc[0]);
-    if constexpr (W2) {  // the reads first, part of the map over their latency, then the MFMAs interleaved
-      sched_group<kSchedDsRead, 4 * NDB>();
-      sched_group<kSchedAnyValu, 40>();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sched_group<kSchedMfma, 1>();
-        sched_group<kSchedAnyValu, 5>();
+          for (int kb = 0; kb < NKB; ++kb)
+            *reinterpret_cast<u32x4*>(wc + toff<D, kRowRead>(32 * fb + c, 16 * kb + 8 * g)) =
+                __builtin_bit_cast(u32x4, wf[fb][kb]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // region B: the first product of step j + 1 beside the map of the second block
-    gemm1(kn, cn);
-    map_fb(j & 1, 1, cc[1], pc[1]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sched_group<kSchedMfma, 1>();
-      sched_group<kSchedAnyValu, 7>();
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(j + 3, kn);
-    store_v(j & 1, vs);
-    load_v(j + 2, vs);
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  iteration(0, F_{}, F_{});
-  // (every trip of the loop runs both iterations, so the loads in flight at
-  // its head are the same on every path into it)
-  int j2 = 1;
-  for (; j2 + 1 <= nsteps; j2 += 2) {
-    iteration(j2, T_{}, T_{});
-    iteration(j2 + 1, F_{}, T_{});
-  }
-  if (j2 <= nsteps) iteration(j2, T_{}, T_{});
-  // Rows past the range: the maps of steps nfull .. nsteps saw K = 0 there,
-  // i.e. phi(0 W + b), the same bits each time; take them out of ksum.
-  {
-    const int nfull = (t_end - t_begin) / STEP;
-    float2 st0 = float2{0.f, 1.f};
-    if constexpr (MAP == kSoftmax) {
-      float z[NKB * 8], m, inv;
-#pragma unroll
-      for (int i = 0; i < NKB * 8; ++i) z[i] = kbias[i];
-      softmax_stats<NKB * 8, 32>(z, m, inv);
-      st0 = float2{m, inv};
-    }
-    int nzero = 0;  // rows past the range among this lane's 16 rows of each map
-    for (int jj = nfull; jj <= nsteps; ++jj) {
-      const int lim = t_end - (t_begin + jj * STEP + 32 * tg);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) nzero += crow(lane, r) >= lim;
-    }
+    // The bias enters the map, not the product: for elu + 1,
+    // phi = max(x + (b + 1), min(exp2(x log2e + b log2e), 1)) costs what the
+    // map without a bias does (an fma in place of the multiply, an add either way).
+    float bcol[2], bl2[2];  // per lane (its feature column): b + 1 (elu + 1) or b, and b log2e
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb) {
-      const float z0 = bf2f(f2bf(phi_b(0.f, fb, st0)));
-      ks[fb] -= (float)nzero * z0;
+      const float bc = a.bias ? a.bias[(size_t)h * F + fs0 + 32 * fb + c] : 0.f;
+      bcol[fb] = MAP == kElu1 ? bc + 1.f : bc;
+      bl2[fb] = bc * kLog2e;
     }
-  }
+    auto phi_b = [&](float x, int fb, float2 st) -> float {
+      if constexpr (MAP == kElu1) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, bl2[fb]));
+        return fmaxf(x + bcol[fb], fminf(fmaxf(e, 0.f), 1.f));
+      } else {
+        return phi_of<MAP>(x + bcol[fb], st.x, st.y);
+      }
+    };
+    // softmax map (identity projection, F == D): each lane's bias values for
+    // the columns its K fragments hold, for the token statistics
+    float kbias[MAP == kSoftmax ? NKB * 8 : 1];
+    if constexpr (MAP == kSoftmax) {
 #pragma unroll
-  for (int fb = 0; fb < 2; ++fb) ks[fb] += shfl_xor32(ks[fb]);
-  __syncthreads();  // LDS free
-
-  // ---- the token groups' sums, added in order into token group 0
-  constexpr int RF = 64 * D + 64;  // floats of one wave's KV and ksum
-  float* red = reinterpret_cast<float*>(smem);
-  if constexpr (NTG > 1) {
-    if (tg > 0) {
-      float* rb = red + ((tg - 1) * NFW + fw) * RF;
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kbias[8 * kb + i] = a.bias ? a.bias[(size_t)h * F + 16 * kb + 8 * g + i] : 0.f;
+    }
+    float2* const wstats = stats + pw * 64;  // [2 parities][32 tokens]
+    auto token_stats = [&](const Frag<uint16_t> (&kf)[NKB], int par) {
+      if constexpr (MAP == kSoftmax) {
+        float z[NKB * 8], m, inv;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          frag_to_f32(kf[kb], z + 8 * kb);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) z[8 * kb + i] += kbias[8 * kb + i];
+        }
+        softmax_stats<NKB * 8, 32>(z, m, inv);
+        if (g == 0) wstats[par * 32 + c] = float2{m, inv};
+      }
+    };
+    float ks[2] = {0.f, 0.f};
+    const uint32_t ones2 = 0x3f803f80u;  // bf16 (1, 1)
+    // step j: the first product, the map, phi^T into LDS, ksum from the
+    // rounded pairs (two per v_dot2)
+    auto produce = [&](int j, const Frag<uint16_t> (&kf)[NKB]) __attribute__((always_inline)) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) acc[fb] = mma_from(f32x16{}, kf[0], wf[fb][0]);
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb)
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) mma(acc[fb], kf[kb], wf[fb][kb]);
+      uint16_t* pt = ptile(j & 1, pw);
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) {
+        uint32_t u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float2 s0 = float2{0.f, 1.f}, s1 = float2{0.f, 1.f};
+          if constexpr (MAP == kSoftmax) {
+            s0 = wstats[(j & 1) * 32 + crow(lane, 2 * i)];
+            s1 = wstats[(j & 1) * 32 + crow(lane, 2 * i + 1)];
+          }
+          const bf16x2 pr = {(__bf16)phi_b(acc[fb][2 * i], fb, s0), (__bf16)phi_b(acc[fb][2 * i + 1], fb, s1)};
+          ks[fb] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, ones2), ks[fb], false);
+          u[i] = __builtin_bit_cast(uint32_t, pr);
+        }
+        // registers 0-7 are tokens kperm(8 g .. 8 g + 7), 8-15 kperm(16 + 8 g ..)
+        const u32x4 lo = {u[0], u[1], u[2], u[3]}, hi = {u[4], u[5], u[6], u[7]};
+        *reinterpret_cast<u32x4*>(pt + toff32(32 * fb + c, 8 * g)) = lo;
+        *reinterpret_cast<u32x4*>(pt + toff32(32 * fb + c, 16 + 8 * g)) = hi;
+      }
+    };
+    // K of step j into registers, two steps ahead: every load unconditional
+    // (steps past the range read zeros), so the compiler's count of loads in
+    // flight is exact on every path
+    Frag<uint16_t> kf0[NKB], kf1[NKB];
+    load_k(0, kf0);
+    load_k(1, kf1);
+    auto iteration = [&](int t, auto odd) __attribute__((always_inline)) {
+      Frag<uint16_t>(&kf)[NKB] = decltype(odd)::value ? kf1 : kf0;
+      if (t > 0) barrier_lds();  // phi^T of step t - 2's buffer is consumed
+      if constexpr (MAP == kSoftmax) {
+        token_stats(kf, t & 1);
+        wave_lds_order();
+      }
+      produce(t, kf);
+      load_k(t + 2, kf);
+    };
+    int t2 = 0;
+    for (; t2 + 1 <= nsteps; t2 += 2) {
+      iteration(t2, std::false_type{});
+      iteration(t2 + 1, std::true_type{});
+    }
+    if (t2 <= nsteps) iteration(t2, std::false_type{});
+    // Rows past the range: the maps of steps nfull .. nsteps saw K = 0 there,
+    // i.e. phi(0 W + b), the same bits each time; take them out of ksum.
+    {
+      const int nfull = (t_end - t_begin) / STEP;
+      float2 st0 = float2{0.f, 1.f};
+      if constexpr (MAP == kSoftmax) {
+        float z[NKB * 8], m, inv;
+#pragma unroll
+        for (int i = 0; i < NKB * 8; ++i) z[i] = kbias[i];
+        softmax_stats<NKB * 8, 32>(z, m, inv);
+        st0 = float2{m, inv};
+      }
+      int nzero = 0;  // rows past the range among this lane's 16 rows of each map
+      for (int jj = nfull; jj <= nsteps; ++jj) {
+        const int lim = t_end - (t_begin + jj * STEP + 32 * tg);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nzero += crow(lane, r) >= lim;
+      }
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) {
+        const float z0 = bf2f(f2bf(phi_b(0.f, fb, st0)));
+        ks[fb] -= (float)nzero * z0;
+        ks[fb] += shfl_xor32(ks[fb]);
+      }
+    }
+    __syncthreads();  // LDS free
+    if constexpr (NTG > 1) {  // the token groups' ksum, added in order into token group 0
+      if (tg > 0 && g == 0) {
+        float* rb = red + ((tg - 1) * NPW + fs) * RF;
+        rb[64 * D + c] = ks[0];
+        rb[64 * D + 32 + c] = ks[1];
+      }
+      __syncthreads();
+      if (tg == 0)
+        for (int t3 = 1; t3 < NTG; ++t3) {
+          const float* rb = red + ((t3 - 1) * NPW + fs) * RF;
+          ks[0] += rb[64 * D + c];
+          ks[1] += rb[64 * D + 32 + c];
+        }
+    }
+    if (tg == 0) {  // this split's ksum [FG] after its KV, in 16-byte pieces (lane c % 4 == 0: lanes c .. c + 3)
+      float k4[2][4];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k4[fb][e] = __shfl(ks[fb], (lane & ~3) + e, 64);
+      if (g == 0 && (c & 3) == 0) {
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+          f32x4 v = {k4[fb][0], k4[fb][1], k4[fb][2], k4[fb][3]};
+          st16_agent(rpart, (uint32_t)(split * pstride) + (uint32_t)(FG * D + 64 * fs + 32 * fb + c) * 4,
+                     __builtin_bit_cast(u32x4, v));
+        }
+      }
+    }
+  } else {
+    // ---- consumer: KV[64 x D] += phi^T . V per step
+    f32x16 kv[2][NDB];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) kv[fb][db] = f32x16{};
+    auto consume = [&](int j) __attribute__((always_inline)) {
+      const uint16_t* pt = ptile(j & 1, pw);
+      const uint16_t* vt = vbuf + (j & 1) * STEP * D;
+      Frag<uint16_t> pa[2][2], vf[NDB][2];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) pa[fb][hh] = ld_frag<uint16_t>(pt + toff32(32 * fb + c, 16 * hh + 8 * g));
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) vf[db][hh] = tr_frag<D>(vt, 32 * tg + 16 * hh, 32 * db, lane);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int fb = 0; fb < 2; ++fb) mma(kv[fb][db], pa[fb][hh], vf[db][hh]);
+    };
+    u32x4 vs0[VP], vs1[VP];
+    load_v(0, vs0);
+    load_v(1, vs1);
+    auto iteration = [&](int t, auto odd) __attribute__((always_inline)) {
+      u32x4(&vs)[VP] = decltype(odd)::value ? vs1 : vs0;
+      if (t > 0) {
+        barrier_lds();  // phi^T and V of step t - 1 are in LDS
+        consume(t - 1);
+      }
+      store_v(t & 1, vs);
+      load_v(t + 2, vs);
+    };
+    int t2 = 0;
+    for (; t2 + 1 <= nsteps; t2 += 2) {
+      iteration(t2, std::false_type{});
+      iteration(t2 + 1, std::true_type{});
+    }
+    if (t2 <= nsteps) iteration(t2, std::false_type{});
+    __syncthreads();  // LDS free
+    if constexpr (NTG > 1) {  // the token groups' KV, added in order into token group 0
+      if (tg > 0) {
+        float* rb = red + ((tg - 1) * NPW + fs) * RF;
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              f32x4 v = {kv[fb][db][4 * q], kv[fb][db][4 * q + 1], kv[fb][db][4 * q + 2], kv[fb][db][4 * q + 3]};
+              *reinterpret_cast<f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4) = v;
+            }
+      }
+      __syncthreads();
+      if (tg == 0)
+        for (int t3 = 1; t3 < NTG; ++t3) {
+          const float* rb = red + ((t3 - 1) * NPW + fs) * RF;
+#pragma unroll
+          for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kv[fb][db][4 * q + e] += v[e];
+              }
+        }
+    }
+    // this split's partial: [fs][fb][db][q][lane][4] (the accumulators'
+    // register image: element e of piece q of lane l is KV[f][d] with
+    // f = fg0 + 64 fs + 32 fb + crow(l, 4 q + e), d = 32 db + (l & 31)), then ksum [FG]
+    if (tg == 0) {
+      const uint32_t base = (uint32_t)(split * pstride);
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
@@ -496,77 +555,9 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             f32x4 v = {kv[fb][db][4 * q], kv[fb][db][4 * q + 1], kv[fb][db][4 * q + 2], kv[fb][db][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4) = v;
+            st16_agent(rpart, base + (uint32_t)((((fs * 2 + fb) * NDB + db) * 4 + q) * 64 + lane) * 16,
+                       __builtin_bit_cast(u32x4, v));
           }
-      if (g == 0) {
-        rb[64 * D + c] = ks[0];
-        rb[64 * D + 32 + c] = ks[1];
-      }
-    }
-    __syncthreads();
-    if (tg == 0) {
-      for (int t2 = 1; t2 < NTG; ++t2) {
-        const float* rb = red + ((t2 - 1) * NFW + fw) * RF;
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 v = *reinterpret_cast<const f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) kv[fb][db][4 * q + e] += v[e];
-            }
-        ks[0] += rb[64 * D + c];
-        ks[1] += rb[64 * D + 32 + c];
-      }
-    }
-  }
-  // ---- this split's partial: [fw][fb][db][q][lane][4] (the accumulators'
-  // register image: element e of piece q of lane l is KV[f][d] with
-  // f = fg0 + 64 fw + 32 fb + crow(l, 4 q + e), d = 32 db + (l & 31)), then ksum [FG]
-  const size_t pstride = (size_t)S::PART * 4;
-  const __amdgpu_buffer_rsrc_t rpart = buffer_rsrc(a.part + (size_t)group * a.nsplit * S::PART,
-                                                   (uint32_t)(a.nsplit * pstride));
-  if (tg == 0) {
-    const uint32_t base = (uint32_t)(split * pstride);
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v = {kv[fb][db][4 * q], kv[fb][db][4 * q + 1], kv[fb][db][4 * q + 2], kv[fb][db][4 * q + 3]};
-          st16_agent(rpart, base + (uint32_t)((((fw * 2 + fb) * NDB + db) * 4 + q) * 64 + lane) * 16,
-                     __builtin_bit_cast(u32x4, v));
-        }
-    // ksum in 16-byte pieces: lane c (c % 4 == 0) stores those of lanes c .. c + 3
-    float k4[2][4];
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) k4[fb][e] = __shfl(ks[fb], (lane & ~3) + e, 64);
-    if (g == 0 && (c & 3) == 0) {
-#pragma unroll
-      for (int fb = 0; fb < 2; ++fb) {
-        f32x4 v = {k4[fb][0], k4[fb][1], k4[fb][2], k4[fb][3]};
-        st16_agent(rpart, base + (uint32_t)(FG * D + 64 * fw + 32 * fb + c) * 4, __builtin_bit_cast(u32x4, v));
-      }
-    }
-  }
-
-  // ---- landmark chunks of this (batch, head), spread over its workgroups
-  // (they need no partial: done while the other splits finish)
-  if constexpr (PACK) {
-    const int nlb = (a.L + 31) / 32;
-    if (nlb > 0) {
-      const PackLayout pl{D, F, a.L, nlb};
-      uint16_t* lmc = reinterpret_cast<uint16_t*>(a.pack_bh + (size_t)bh * a.bh_bytes + pl.vec_bytes() + pl.kv_bytes());
-      auto vrows = reinterpret_cast<uint16_t(*)[D + 8]>(smem);
-      const int nwg = NG * a.nsplit, me = fgi * a.nsplit + split;
-      __syncthreads();  // the token-group sums are read
-      for (int jb = me; jb < nlb; jb += nwg)
-        landmark_chunk<D>(Kp, Vp, N, a.L, jb, lmc + (size_t)jb * pl.chunk_elems(), vrows, tid);
     }
   }
 
@@ -589,33 +580,34 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
   const bool ok = ok_s != 0;
 
   // ---- this split's share of the reduction, summed over the splits in order
+  // (each thread's loads for up to eight splits issued before its adds)
   if constexpr (PACK) {
     const PackLayout pl{D, F, a.L, (a.L + 31) / 32};
     unsigned char* base = a.pack_bh + (size_t)bh * a.bh_bytes;
     float* biasP = reinterpret_cast<float*>(base);
     float* ksumP = biasP + F;
     uint16_t* kvc = reinterpret_cast<uint16_t*>(base + pl.vec_bytes());
-    // task: (fw, fb, db, k, lane) -> the bf16 piece of KV^T chunk fw at row
+    // task: (fs, fb, db, k, lane) -> the bf16 piece of KV^T chunk fs at row
     // d = 32 db + (lane & 31), columns 32 fb + 16 k + 8 (lane >> 5) .. + 7,
     // from pieces q = 2 k and 2 k + 1 of the partials
-    constexpr int TASKS = NFW * 2 * NDB * 2 * 64;
+    constexpr int TASKS = NPW * 2 * NDB * 2 * 64;
     const int per = (TASKS + a.nsplit - 1) / a.nsplit;
-    for (int t = split * per + tid; t < min(TASKS, (split + 1) * per); t += 256) {
+    for (int t = split * per + tid; t < min(TASKS, (split + 1) * per); t += 512) {
       const int ln = t & 63, k = (t >> 6) & 1, db = (t >> 7) % NDB, fb = (t / (128 * NDB)) & 1,
-                fwt = t / (256 * NDB);
-      const uint32_t o0 = (uint32_t)((((fwt * 2 + fb) * NDB + db) * 4 + 2 * k) * 64 + ln) * 16;
+                fst = t / (256 * NDB);
+      const uint32_t o0 = (uint32_t)((((fst * 2 + fb) * NDB + db) * 4 + 2 * k) * 64 + ln) * 16;
       const uint32_t o1 = o0 + 64 * 16;
       f32x4 s0 = f32x4{}, s1 = f32x4{};
-      for (int sp = 0; sp < a.nsplit; sp += 4) {
-        u32x4 v0[4], v1[4];
+      for (int sp = 0; sp < a.nsplit; sp += 8) {
+        u32x4 v0[8], v1[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           const uint32_t so = (uint32_t)(min(sp + u, a.nsplit - 1) * pstride);
           v0[u] = ld16_agent(rpart, so + o0);
           v1[u] = ld16_agent(rpart, so + o1);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
           if (sp + u < a.nsplit) {
             s0 += __builtin_bit_cast(f32x4, v0[u]);
             s1 += __builtin_bit_cast(f32x4, v1[u]);
@@ -627,7 +619,7 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
       o[1] = pack_bf16x2(s0[2], s0[3]);
       o[2] = pack_bf16x2(s1[0], s1[1]);
       o[3] = pack_bf16x2(s1[2], s1[3]);
-      uint16_t* ch = kvc + (size_t)((fg0 + 64 * fwt) / 64) * 64 * D;
+      uint16_t* ch = kvc + (size_t)((fg0 + 64 * fst) / 64) * 64 * D;
       *reinterpret_cast<u32x4*>(ch + toff<64, kRowRead>(32 * db + (ln & 31), 32 * fb + 16 * k + 8 * (ln >> 5))) = o;
     }
     if (split == 0 && tid < FG) {  // ksum and bias of the group's features, in kperm order
@@ -640,13 +632,13 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
       biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
     }
   } else {
-    // task: (fw, fb, db, q, g, lane quad) -> KV rows f = .. crow(l, 4 q + e) (e = 0..3),
+    // task: (fs, fb, db, q, g, lane quad) -> KV rows f = .. crow(l, 4 q + e) (e = 0..3),
     // columns d = 32 db + 4 cq .. + 3: four lanes' pieces, transposed
-    constexpr int TASKS = NFW * 2 * NDB * 4 * 2 * 8;
+    constexpr int TASKS = NPW * 2 * NDB * 4 * 2 * 8;
     const int per = (TASKS + a.nsplit - 1) / a.nsplit;
-    for (int t = split * per + tid; t < min(TASKS, (split + 1) * per); t += 256) {
+    for (int t = split * per + tid; t < min(TASKS, (split + 1) * per); t += 512) {
       const int cq = t & 7, gg = (t >> 3) & 1, q = (t >> 4) & 3, db = (t >> 6) % NDB, fb = (t / (64 * NDB)) & 1,
-                fwt = t / (128 * NDB);
+                fst = t / (128 * NDB);
       f32x4 sum[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};  // [lane i][element e]
       for (int sp = 0; sp < a.nsplit; ++sp) {
         u32x4 v[4];
@@ -654,7 +646,7 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int ln = 32 * gg + 4 * cq + i;
           v[i] = ld16_agent(rpart, (uint32_t)(sp * pstride) +
-                                       (uint32_t)((((fwt * 2 + fb) * NDB + db) * 4 + q) * 64 + ln) * 16);
+                                       (uint32_t)((((fst * 2 + fb) * NDB + db) * 4 + q) * 64 + ln) * 16);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) sum[i] += __builtin_bit_cast(f32x4, v[i]);
@@ -662,7 +654,7 @@ __global__ __launch_bounds__(256, 1) void kv_stage_kernel(KvsArgs a) {
       float* kvo = a.kv_out + (size_t)bh * F * D;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int f = fg0 + 64 * fwt + 32 * fb + 8 * q + 4 * gg + e;  // crow(lane of half gg, 4 q + e)
+        const int f = fg0 + 64 * fst + 32 * fb + 8 * q + 4 * gg + e;  // crow(lane of half gg, 4 q + e)
         f32x4 o = {sum[0][e], sum[1][e], sum[2][e], sum[3][e]};
         if (!ok) o = f32x4{kQNaN, kQNaN, kQNaN, kQNaN};
         *reinterpret_cast<f32x4*>(kvo + (size_t)f * D + 32 * db + 4 * cq) = o;
@@ -694,7 +686,7 @@ __global__ __launch_bounds__(256) void lm_pack_kernel(LmPackArgs a) {
   const int bh = item / nlb, jb = item % nlb;
   const PackLayout pl{D, 0, a.L, nlb};
   uint16_t* kl = reinterpret_cast<uint16_t*>(a.pack_bh + (size_t)bh * pl.bh_bytes()) + (size_t)jb * pl.chunk_elems();
-  landmark_chunk<D>(a.K + (size_t)bh * a.N * D, a.V + (size_t)bh * a.N * D, a.N, a.L, jb, kl, vrows, threadIdx.x);
+  landmark_chunk<D, 256>(a.K + (size_t)bh * a.N * D, a.V + (size_t)bh * a.N * D, a.N, a.L, jb, kl, vrows, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- host side
@@ -723,7 +715,7 @@ static KvsPlan kvs_plan(const Problem& p, int cus) {
   KvsPlan k;
   k.FG = p.F < 128 ? p.F : 128;
   k.NG = p.F / k.FG;
-  const int step = k.FG >= 128 ? 64 : 128;
+  const int step = 32 * (4 / (k.FG / 64));
   k.groups = p.B * p.H * k.NG;
   int ns = cus / k.groups;
   const int maxs = (p.N + 2 * step - 1) / (2 * step);  // at least two steps per split
@@ -765,7 +757,7 @@ static hipError_t launch_kvs_t(const KvsArgs& a, int groups, hipStream_t s, Stag
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (t) t->mark();
-  hipLaunchKernelGGL((kv_stage_kernel<D, F, PROJ, MAP, PACK>), dim3(groups * a.nsplit), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((kv_stage_kernel<D, F, PROJ, MAP, PACK>), dim3(groups * a.nsplit), dim3(512), 0, s, a);
   e = hipGetLastError();
   if (t) t->mark();
   return e;
