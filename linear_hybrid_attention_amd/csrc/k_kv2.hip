@@ -12,15 +12,16 @@
 // 512 registers each) own 64 features each, the group's features covered by
 // NFW = FG / 64 waves and the tokens of a step by the NTG = 4 / NFW token
 // groups of 32. Per step a wave computes, for its 32 tokens:
-//   phi[tok x 64]  = map(K[tok x D] . W[:, 64 features] + b)   (A = K rows straight
-//                     from global memory into registers, B = W held in registers)
-//   KV[64 x D]    += phi^T . V                                  (A = the C tile of the
-//                     first product, B = V read transposed from LDS)
-// V of a step is staged in LDS once for the workgroup (through registers: the
-// compiler serialises transposing LDS reads behind any LDS DMA copy in
-// flight). The steps are software-pipelined: iteration j issues the first
-// product of step j + 1 and the second of step j - 1 and maps step j in
-// between, so the map's vector work overlaps the matrix core.
+//   phi[tok x 64]  = map(K[tok x D] . W[:, 64 features] + b)   (A = K rows read from
+//                     LDS, B = W held in registers)
+//   KV[64 x D]    += phi^T . V                                  (A = phi^T from LDS,
+//                     B = V read transposed from LDS)
+// The K and V rows of a step reach LDS by asynchronous copies (global -> LDS,
+// whole 128-byte lines per 16 lanes, pieces placed in the swizzled layout the
+// operand reads want), issued two steps ahead by the waves that map, into
+// three-slot rings. The waves of the second product issue no copies: the
+// compiler makes transposing LDS reads wait for every copy the reading wave
+// has in flight.
 //
 // The splits of a (batch, head, feature group) then meet: each writes its
 // fp32 partial (its waves' token groups added through LDS first), counts
@@ -29,8 +30,13 @@
 // workgroup per compute unit), and each reduces a share of the group's
 // outputs over the splits in split order -- deterministic -- straight into
 // the fused query kernel's pack (bf16 KV^T chunks, ksum and bias) or into
-// fp32 KV and ksum. Partials are written and read with agent-coherent
-// (sc1) accesses, so the splits may run on different XCDs.
+// fp32 KV and ksum. The grid is numbered so that the splits of a group run on
+// one XCD: their partials then stay in that XCD's L2 (plain stores and loads,
+// no trip to memory before the reduction). Each workgroup counts itself in
+// under its XCD's id; a group found spread over several XCDs takes a second
+// round in which every split first writes its L2 back to memory and then
+// drops stale lines, so the result never depends on where the hardware put
+// the workgroups.
 //
 // The pack, per (batch, head): bias, ksum [F] fp32 in kperm order; F / 64
 // KV^T chunks [D][64 f]; one K_L + V_L^T chunk per 32 landmarks
@@ -112,7 +118,8 @@ struct KvsArgs {
   int H, N, L;
   int nsplit, chunk;     // token splits of a group and the tokens of each (a multiple of the step)
   float* part;           // [groups][nsplit][FG * D + FG] fp32 partials
-  unsigned* counters;    // [groups] arrivals, zero on entry (kv_stage_reset_kernel)
+  unsigned* counters;    // [groups][4]: arrivals per XCD (8 byte fields), second-round arrivals, unused;
+                         // zero on entry (kv_stage_reset_kernel)
   unsigned spin_limit;   // polls of a waiting workgroup before it gives up
   unsigned char* pack_bh;  // pack mode: [BH][bh_bytes]
   unsigned long long bh_bytes;
@@ -130,19 +137,29 @@ struct KvsShape {
   static constexpr int STEP = 32 * NTG;         // tokens of a workgroup step
   static constexpr int NKB = D / 16;            // k-blocks of a K row
   static constexpr int NDB = D / 32;            // 32-column blocks of V
-  static constexpr int VP = STEP * D / 8 / 256;  // 16-byte V pieces per consumer thread per step
+  static constexpr int NI = STEP * D / 8 / 64 / 4;  // copies (16 bytes per lane) per producer wave per tile
   static constexpr int PART = FG * D + FG;       // floats of one split's partial
   static_assert(F == 64 || F % 128 == 0, "feature count");
-  static_assert(VP * 256 * 8 == STEP * D && VP >= 1, "whole V pieces");
-  static constexpr int vbuf_bytes = 2 * STEP * D * 2;        // V double buffer [2][STEP][D]
-  static constexpr int pbuf_bytes = 2 * 4 * 64 * 32 * 2;     // phi^T double buffer [2][4 producers][64 f][32 tok]
+  static_assert(NI * 4 * 64 * 8 == STEP * D && NI >= 1, "whole copies");
+  // consumer wave: features fs, CW_DB of the NDB 32-column blocks of V (part
+  // dp of NDP), CW_TG of the NTG token groups (part tp of NTP)
+  static constexpr int CW_DB = FG == 128 ? NDB / 2 : 1;
+  static constexpr int NDP = NDB / CW_DB;
+  static constexpr int NTP = 4 / NPW / NDP;
+  static constexpr int CW_TG = NTG / NTP;
+  static_assert(NPW * NDP * NTP == 4 && CW_TG * NTP == NTG && CW_DB * NDP == NDB, "consumer split");
+  static_assert(NTG > 1, "both roles take the same barriers after the loop");
+  static constexpr int tile_elems = STEP * D;                // one step of K (or V) rows, one ring slot
+  static constexpr int pbuf_bytes = 3 * 4 * 64 * 32 * 2;     // phi^T ring [3][4 producers][64 f][32 tok]
   static constexpr int wtile_bytes = D * FG * 2;             // W tile (prologue)
-  static constexpr int stats_bytes = 4 * 2 * 32 * 8;         // softmax (max, 1 / sum) per producer and step parity
+  static constexpr int stats_bytes = 4 * 3 * 32 * 8;         // softmax (max, 1 / sum) per producer and ring slot
   static constexpr int lm_bytes = 32 * (D + 8) * 2;          // landmark V rows (prologue)
-  static constexpr int main_bytes = vbuf_bytes + pbuf_bytes + wtile_bytes + stats_bytes + lm_bytes;
-  static constexpr int red_bytes = (NTG - 1) * NPW * (64 * D + 64) * 4;  // token-group partials
-  static constexpr int bytes = main_bytes > red_bytes ? main_bytes : red_bytes;
-  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static constexpr int CIMG = 2 * CW_DB * 16 * 64;           // floats of a consumer wave's accumulators
+  static constexpr int KSOFF = (NTP - 1) * NPW * NDP * CIMG;  // producer ksum sums after the consumer images
+  static constexpr int red_bytes = (KSOFF + (NTG - 1) * NPW * 64) * 4;
+  static constexpr int max2(int x, int y) { return x > y ? x : y; }
+  static constexpr int bytes = max2(max2(pbuf_bytes + stats_bytes, wtile_bytes), max2(lm_bytes, red_bytes));
+  static_assert(bytes + 6 * tile_elems * 2 <= 160 * 1024, "LDS budget");
 };
 
 // (a quiet NaN by its bits: the file is built without NaN semantics)
@@ -153,13 +170,30 @@ __global__ void kv_stage_reset_kernel(unsigned* counters, int n) {
     __hip_atomic_store(counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 16-byte load / store that are coherent at agent scope (sc1): they reach the
-// point where every XCD sees the same data, whatever L2 holds.
-__device__ __forceinline__ u32x4 ld16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
+// Partial loads and stores: plain, through the XCD's L2 (see the meeting of
+// the splits for when that is coherent).
+__device__ __forceinline__ u32x4 ld16_part(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
-__device__ __forceinline__ void st16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4& v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
+__device__ __forceinline__ void st16_part(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// Id of the XCD the calling wave runs on (hardware register XCC_ID, bits 0-3;
+// gfx950 parts have at most eight XCDs).
+__device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 7u; }
+
+// Arrivals of a group: byte x of the word counts the splits on XCD x.
+__device__ __forceinline__ unsigned arrivals(unsigned long long v, unsigned& xcds) {
+  unsigned n = 0;
+  xcds = 0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const unsigned b = (unsigned)(v >> (8 * x)) & 255u;
+    n += b;
+    xcds += b != 0;
+  }
+  return n;
 }
 
 // Eight waves, two per SIMD: waves 0-3 are producers, 4-7 consumers (wave w
@@ -176,14 +210,28 @@ template <int D, int F, bool PROJ, int MAP, bool PACK>
 __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   using S = KvsShape<D, F>;
   constexpr int FG = S::FG, NG = S::NG, NPW = S::NPW, NTG = S::NTG, STEP = S::STEP, NKB = S::NKB,
-                NDB = S::NDB, VP = S::VP;
+                NDB = S::NDB, NI = S::NI;
+  // Ring slots of K ([STEP][D] kRowRead) and V ([STEP][D] kTrRead), each its
+  // own LDS object: the compiler then keeps a wave's LDS reads from waiting
+  // on copies into other slots. smem: the phi^T ring and the softmax stats;
+  // before the loop the W tile and landmark rows, after it the reductions.
+  __shared__ __attribute__((aligned(16))) uint16_t kr0[S::tile_elems], kr1[S::tile_elems], kr2[S::tile_elems];
+  __shared__ __attribute__((aligned(16))) uint16_t vr0[S::tile_elems], vr1[S::tile_elems], vr2[S::tile_elems];
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
-  uint16_t* const vbuf = reinterpret_cast<uint16_t*>(smem);                       // [2][STEP][D] kTrRead
-  uint16_t* const pbuf = reinterpret_cast<uint16_t*>(smem + S::vbuf_bytes);       // [2][4][64][32] toff32
-  uint16_t* const wt = reinterpret_cast<uint16_t*>(smem + S::vbuf_bytes + S::pbuf_bytes);  // [D][FG], rows kperm'd
-  float2* const stats = reinterpret_cast<float2*>(smem + S::vbuf_bytes + S::pbuf_bytes + S::wtile_bytes);
-  auto lmrows = reinterpret_cast<uint16_t(*)[D + 8]>(smem + S::vbuf_bytes + S::pbuf_bytes + S::wtile_bytes +
-                                                     S::stats_bytes);
+  uint16_t* const pbuf = reinterpret_cast<uint16_t*>(smem);                      // [3][4][64][32] toff32
+  float2* const stats = reinterpret_cast<float2*>(smem + S::pbuf_bytes);
+  uint16_t* const wt = reinterpret_cast<uint16_t*>(smem);                        // [D][FG], rows kperm'd
+  auto lmrows = reinterpret_cast<uint16_t(*)[D + 8]>(smem);
+  auto kslot = [&](auto sl) -> uint16_t* {
+    if constexpr (decltype(sl)::value == 0) return kr0;
+    else if constexpr (decltype(sl)::value == 1) return kr1;
+    else return kr2;
+  };
+  auto vslot = [&](auto sl) -> uint16_t* {
+    if constexpr (decltype(sl)::value == 0) return vr0;
+    else if constexpr (decltype(sl)::value == 1) return vr1;
+    else return vr2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
@@ -204,36 +252,41 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
 
   // ---- operand streams, through buffer resources that end at the range's
   // last token: a row past it reads as zeros (so it adds nothing to KV, and
-  // a fixed phi(0 W + b) to ksum, taken out after the loop). K rows of step j
-  // for a producer's 32 tokens, as the A operand (lane = token c, k-slots =
-  // columns 16 kb + 8 g ..); V rows of step j: piece ct + 256 i of the step
-  // for consumer thread ct.
+  // a fixed phi(0 W + b) to ksum, taken out after the loop). Producer wave pw
+  // copies pieces 64 (NI pw + i) + lane of a step's tile: row r = piece / (D / 8),
+  // physical piece q' = piece % (D / 8), which holds the row's piece q' ^ tswz(r).
   const uint32_t range_bytes = (uint32_t)((size_t)t_end * D * 2);
   const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(Kp, range_bytes);
   const __amdgpu_buffer_rsrc_t rV = buffer_rsrc(Vp, range_bytes);
-  auto load_k = [&](int j, Frag<uint16_t> (&kf)[NKB]) {
-    const uint32_t off = (uint32_t)(t_begin + j * STEP + 32 * tg + c) * (D * 2) + 16 * g;
+  uint32_t koff[NI], voff[NI];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      kf[kb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rK, (int)(off + 32 * kb), 0, 0));
-  };
-  const int ct = tid - 256;  // consumer thread
-  auto load_v = [&](int j, u32x4 (&vs)[VP]) {
+  for (int i = 0; i < NI; ++i) {
+    const int P = 64 * (NI * pw + i) + lane, r = P / (D / 8), qp = P % (D / 8);
+    koff[i] = (uint32_t)(t_begin + r) * (D * 2) + (uint32_t)(qp ^ tswz<D, kRowRead>(r)) * 16;
+    voff[i] = (uint32_t)(t_begin + r) * (D * 2) + (uint32_t)(qp ^ tswz<D, kTrRead>(r)) * 16;
+  }
+  // Step j goes to ring slot j % 3, given as a constant: LDS offsets the
+  // compiler can see apart keep it from making the wave's LDS reads wait for
+  // copies into other slots.
+  auto copy_k = [&](int j, auto slot) {
+    uint16_t* dst = kslot(slot);
 #pragma unroll
-    for (int i = 0; i < VP; ++i) {
-      const int P = ct + 256 * i, row = P / (D / 8), p = P % (D / 8);
-      vs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rV, (int)((uint32_t)(t_begin + j * STEP + row) * (D * 2) + p * 16), 0, 0));
-    }
+    for (int i = 0; i < NI; ++i) copy16_async(rK, koff[i] + (uint32_t)(j * STEP * D * 2), 0, dst + (NI * pw + i) * 512);
   };
-  auto store_v = [&](int buf, const u32x4 (&vs)[VP]) {
-    uint16_t* vt = vbuf + buf * STEP * D;
+  auto copy_v = [&](int j, auto slot) {
+    uint16_t* dst = vslot(slot);
 #pragma unroll
-    for (int i = 0; i < VP; ++i) {
-      const int P = ct + 256 * i, row = P / (D / 8), p = P % (D / 8);
-      *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = vs[i];
-    }
+    for (int i = 0; i < NI; ++i) copy16_async(rV, voff[i] + (uint32_t)(j * STEP * D * 2), 0, dst + (NI * pw + i) * 512);
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  // K(0), V(0) and K(1) first: they land while the prologue runs
+  if (producer) {
+    copy_k(0, C0{});
+    copy_v(0, C0{});
+    copy_k(1, C1{});
+  }
   // ---- landmark chunks of this (batch, head), spread over its workgroups
   // (they need no partial: done first, beside the W loads)
   if constexpr (PACK) {
@@ -270,12 +323,11 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   const size_t pstride = (size_t)S::PART * 4;
   const __amdgpu_buffer_rsrc_t rpart = buffer_rsrc(a.part + (size_t)group * a.nsplit * S::PART,
                                                    (uint32_t)(a.nsplit * pstride));
-  constexpr int RF = 64 * D + 64;  // floats of one wave slice's KV and ksum (token-group sums)
   float* red = reinterpret_cast<float*>(smem);
   // phi^T of a producer: [64 f][32 tok] in the toff32 layout, tokens of each
   // half in kperm column order, so that a consumer's plain 16-byte row read
   // hands it the tokens in the C-row order of the transposed V fragments
-  auto ptile = [&](int buf, int p) -> uint16_t* { return pbuf + (buf * 4 + p) * 64 * 32; };
+  auto ptile = [&](int slot, int p) -> uint16_t* { return pbuf + (slot * 4 + p) * 64 * 32; };
   // Both roles run nsteps + 1 iterations with one barrier each (but the
   // first), then the same barriers of the token-group sums: their s_barrier
   // counts match. Each role's state lives in its own branch.
@@ -345,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) kbias[8 * kb + i] = a.bias ? a.bias[(size_t)h * F + 16 * kb + 8 * g + i] : 0.f;
     }
-    float2* const wstats = stats + pw * 64;  // [2 parities][32 tokens]
+    float2* const wstats = stats + pw * 96;  // [3 slots][32 tokens]
     auto token_stats = [&](const Frag<uint16_t> (&kf)[NKB], int par) {
       if constexpr (MAP == kSoftmax) {
         float z[NKB * 8], m, inv;
@@ -363,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
     const uint32_t ones2 = 0x3f803f80u;  // bf16 (1, 1)
     // step j: the first product, the map, phi^T into LDS, ksum from the
     // rounded pairs (two per v_dot2)
-    auto produce = [&](int j, const Frag<uint16_t> (&kf)[NKB]) __attribute__((always_inline)) {
+    auto produce = [&](int slot, const Frag<uint16_t> (&kf)[NKB]) __attribute__((always_inline)) {
       f32x16 acc[2];
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) acc[fb] = mma_from(f32x16{}, kf[0], wf[fb][0]);
@@ -371,7 +423,8 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       for (int kb = 1; kb < NKB; ++kb)
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) mma(acc[fb], kf[kb], wf[fb][kb]);
-      uint16_t* pt = ptile(j & 1, pw);
+      __builtin_amdgcn_s_setprio(0);  // the map's vector work runs beside the consumer's products
+      uint16_t* pt = ptile(slot, pw);
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) {
         uint32_t u[8];
@@ -379,8 +432,8 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
         for (int i = 0; i < 8; ++i) {
           float2 s0 = float2{0.f, 1.f}, s1 = float2{0.f, 1.f};
           if constexpr (MAP == kSoftmax) {
-            s0 = wstats[(j & 1) * 32 + crow(lane, 2 * i)];
-            s1 = wstats[(j & 1) * 32 + crow(lane, 2 * i + 1)];
+            s0 = wstats[slot * 32 + crow(lane, 2 * i)];
+            s1 = wstats[slot * 32 + crow(lane, 2 * i + 1)];
           }
           const bf16x2 pr = {(__bf16)phi_b(acc[fb][2 * i], fb, s0), (__bf16)phi_b(acc[fb][2 * i + 1], fb, s1)};
           ks[fb] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, ones2), ks[fb], false);
@@ -392,28 +445,40 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
         *reinterpret_cast<u32x4*>(pt + toff32(32 * fb + c, 16 + 8 * g)) = hi;
       }
     };
-    // K of step j into registers, two steps ahead: every load unconditional
-    // (steps past the range read zeros), so the compiler's count of loads in
-    // flight is exact on every path
-    Frag<uint16_t> kf0[NKB], kf1[NKB];
-    load_k(0, kf0);
-    load_k(1, kf1);
-    auto iteration = [&](int t, auto odd) __attribute__((always_inline)) {
-      Frag<uint16_t>(&kf)[NKB] = decltype(odd)::value ? kf1 : kf0;
-      if (t > 0) barrier_lds();  // phi^T of step t - 2's buffer is consumed
+    // Iteration t: this wave's copies of K(t) and V(t - 1) (issued two
+    // iterations back) have landed when at most the 2 NI copies of the last
+    // iteration are in flight; after the barrier everyone's have, phi^T
+    // buffer t & 1 is free, and so are the ring slots of K(t - 1) and V(t - 2),
+    // which take K(t + 2) and V(t + 1). Copies past the range read zeros.
+    // (t % 3 == slot)
+    auto iteration = [&](int t, auto slot) __attribute__((always_inline)) {
+      constexpr int sl = decltype(slot)::value;
+      wait_vmcnt<2 * NI>();
+      barrier_lds();
+      // this wave's products first on the SIMD's matrix core (the consumer
+      // wave beside it waits for them anyway one step later)
+      __builtin_amdgcn_s_setprio(1);
+      copy_k(t + 2, std::integral_constant<int, (sl + 2) % 3>{});
+      copy_v(t + 1, std::integral_constant<int, (sl + 1) % 3>{});
+      const uint16_t* kt = kslot(slot);
+      Frag<uint16_t> kf[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kf[kb] = ld_frag<uint16_t>(kt + toff<D, kRowRead>(32 * tg + c, 16 * kb + 8 * g));
       if constexpr (MAP == kSoftmax) {
-        token_stats(kf, t & 1);
+        token_stats(kf, sl);
         wave_lds_order();
       }
-      produce(t, kf);
-      load_k(t + 2, kf);
+      produce(sl, kf);
     };
-    int t2 = 0;
-    for (; t2 + 1 <= nsteps; t2 += 2) {
-      iteration(t2, std::false_type{});
-      iteration(t2 + 1, std::true_type{});
+    int t3 = 0;
+    for (; t3 + 2 <= nsteps; t3 += 3) {
+      iteration(t3, C0{});
+      iteration(t3 + 1, C1{});
+      iteration(t3 + 2, C2{});
     }
-    if (t2 <= nsteps) iteration(t2, std::false_type{});
+    if (t3 <= nsteps) iteration(t3, C0{});
+    if (t3 + 1 <= nsteps) iteration(t3 + 1, C1{});
+    wait_vmcnt<0>();  // the last (zero) copies have landed before LDS is reused
     // Rows past the range: the maps of steps nfull .. nsteps saw K = 0 there,
     // i.e. phi(0 W + b), the same bits each time; take them out of ksum.
     {
@@ -442,16 +507,16 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
     __syncthreads();  // LDS free
     if constexpr (NTG > 1) {  // the token groups' ksum, added in order into token group 0
       if (tg > 0 && g == 0) {
-        float* rb = red + ((tg - 1) * NPW + fs) * RF;
-        rb[64 * D + c] = ks[0];
-        rb[64 * D + 32 + c] = ks[1];
+        float* rb = red + S::KSOFF + ((tg - 1) * NPW + fs) * 64;
+        rb[c] = ks[0];
+        rb[32 + c] = ks[1];
       }
       __syncthreads();
       if (tg == 0)
-        for (int t3 = 1; t3 < NTG; ++t3) {
-          const float* rb = red + ((t3 - 1) * NPW + fs) * RF;
-          ks[0] += rb[64 * D + c];
-          ks[1] += rb[64 * D + 32 + c];
+        for (int u = 1; u < NTG; ++u) {
+          const float* rb = red + S::KSOFF + ((u - 1) * NPW + fs) * 64;
+          ks[0] += rb[c];
+          ks[1] += rb[32 + c];
         }
     }
     if (tg == 0) {  // this split's ksum [FG] after its KV, in 16-byte pieces (lane c % 4 == 0: lanes c .. c + 3)
@@ -464,114 +529,128 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
           f32x4 v = {k4[fb][0], k4[fb][1], k4[fb][2], k4[fb][3]};
-          st16_agent(rpart, (uint32_t)(split * pstride) + (uint32_t)(FG * D + 64 * fs + 32 * fb + c) * 4,
+          st16_part(rpart, (uint32_t)(split * pstride) + (uint32_t)(FG * D + 64 * fs + 32 * fb + c) * 4,
                      __builtin_bit_cast(u32x4, v));
         }
       }
     }
   } else {
-    // ---- consumer: KV[64 x D] += phi^T . V per step
-    f32x16 kv[2][NDB];
+    // ---- consumer: KV[64 features x the wave's CW_DB column blocks] += phi^T . V
+    // over the tokens of its CW_TG token groups, per step
+    constexpr int CW_DB = S::CW_DB, CW_TG = S::CW_TG, NDP = S::NDP, NTP = S::NTP;
+    const int dp = (pw / NPW) % NDP, tp = pw / NPW / NDP;
+    f32x16 kv[2][CW_DB];
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) kv[fb][db] = f32x16{};
+      for (int i = 0; i < CW_DB; ++i) kv[fb][i] = f32x16{};
     auto consume = [&](int j) __attribute__((always_inline)) {
-      const uint16_t* pt = ptile(j & 1, pw);
-      const uint16_t* vt = vbuf + (j & 1) * STEP * D;
-      Frag<uint16_t> pa[2][2], vf[NDB][2];
+      const int sl = j % 3;
+      const uint16_t* vt = sl == 0 ? vr0 : sl == 1 ? vr1 : vr2;
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) pa[fb][hh] = ld_frag<uint16_t>(pt + toff32(32 * fb + c, 16 * hh + 8 * g));
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) vf[db][hh] = tr_frag<D>(vt, 32 * tg + 16 * hh, 32 * db, lane);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int fb = 0; fb < 2; ++fb) mma(kv[fb][db], pa[fb][hh], vf[db][hh]);
-    };
-    u32x4 vs0[VP], vs1[VP];
-    load_v(0, vs0);
-    load_v(1, vs1);
-    auto iteration = [&](int t, auto odd) __attribute__((always_inline)) {
-      u32x4(&vs)[VP] = decltype(odd)::value ? vs1 : vs0;
-      if (t > 0) {
-        barrier_lds();  // phi^T and V of step t - 1 are in LDS
-        consume(t - 1);
-      }
-      store_v(t & 1, vs);
-      load_v(t + 2, vs);
-    };
-    int t2 = 0;
-    for (; t2 + 1 <= nsteps; t2 += 2) {
-      iteration(t2, std::false_type{});
-      iteration(t2 + 1, std::true_type{});
-    }
-    if (t2 <= nsteps) iteration(t2, std::false_type{});
-    __syncthreads();  // LDS free
-    if constexpr (NTG > 1) {  // the token groups' KV, added in order into token group 0
-      if (tg > 0) {
-        float* rb = red + ((tg - 1) * NPW + fs) * RF;
+      for (int u = 0; u < CW_TG; ++u) {
+        const int tgx = tp * CW_TG + u;
+        const uint16_t* pt = ptile(sl, tgx * NPW + fs);  // the producer (fs, tgx)
+        Frag<uint16_t> pa[2][2], vf[CW_DB][2];
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+          for (int hh = 0; hh < 2; ++hh) pa[fb][hh] = ld_frag<uint16_t>(pt + toff32(32 * fb + c, 16 * hh + 8 * g));
+#pragma unroll
+        for (int i = 0; i < CW_DB; ++i)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) vf[i][hh] = tr_frag<D>(vt, 32 * tgx + 16 * hh, 32 * (dp * CW_DB + i), lane);
+#pragma unroll
+        for (int i = 0; i < CW_DB; ++i)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb) mma(kv[fb][i], pa[fb][hh], vf[i][hh]);
+      }
+    };
+    for (int t = 0; t <= nsteps; ++t) {
+      barrier_lds();  // phi^T and V of step t - 1 are in LDS
+      if (t > 0) consume(t - 1);
+    }
+    __syncthreads();  // LDS free
+    // the token parts' KV (more than one only when a feature group is one
+    // wave wide), added in order into part 0; the same barriers as the
+    // producers' ksum sums
+    float* const img = red + (((tp > 0 ? tp : 1) - 1) * NPW + fs) * NDP * S::CIMG + dp * S::CIMG;
+    if constexpr (NTP > 1) {
+      if (tp > 0) {
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+          for (int i = 0; i < CW_DB; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              f32x4 v = {kv[fb][db][4 * q], kv[fb][db][4 * q + 1], kv[fb][db][4 * q + 2], kv[fb][db][4 * q + 3]};
-              *reinterpret_cast<f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4) = v;
+              f32x4 v = {kv[fb][i][4 * q], kv[fb][i][4 * q + 1], kv[fb][i][4 * q + 2], kv[fb][i][4 * q + 3]};
+              *reinterpret_cast<f32x4*>(img + (((fb * CW_DB + i) * 4 + q) * 64 + lane) * 4) = v;
             }
       }
-      __syncthreads();
-      if (tg == 0)
-        for (int t3 = 1; t3 < NTG; ++t3) {
-          const float* rb = red + ((t3 - 1) * NPW + fs) * RF;
+    }
+    __syncthreads();
+    if constexpr (NTP > 1) {
+      if (tp == 0)
+        for (int u = 1; u < NTP; ++u) {
+          const float* rb = red + ((u - 1) * NPW + fs) * NDP * S::CIMG + dp * S::CIMG;
 #pragma unroll
           for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int i = 0; i < CW_DB; ++i)
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(rb + (((fb * NDB + db) * 4 + q) * 64 + lane) * 4);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(rb + (((fb * CW_DB + i) * 4 + q) * 64 + lane) * 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kv[fb][db][4 * q + e] += v[e];
+                for (int e = 0; e < 4; ++e) kv[fb][i][4 * q + e] += v[e];
               }
         }
     }
     // this split's partial: [fs][fb][db][q][lane][4] (the accumulators'
     // register image: element e of piece q of lane l is KV[f][d] with
     // f = fg0 + 64 fs + 32 fb + crow(l, 4 q + e), d = 32 db + (l & 31)), then ksum [FG]
-    if (tg == 0) {
+    if (tp == 0) {
       const uint32_t base = (uint32_t)(split * pstride);
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int i = 0; i < CW_DB; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            f32x4 v = {kv[fb][db][4 * q], kv[fb][db][4 * q + 1], kv[fb][db][4 * q + 2], kv[fb][db][4 * q + 3]};
-            st16_agent(rpart, base + (uint32_t)((((fs * 2 + fb) * NDB + db) * 4 + q) * 64 + lane) * 16,
-                       __builtin_bit_cast(u32x4, v));
+            const int db = dp * CW_DB + i;
+            f32x4 v = {kv[fb][i][4 * q], kv[fb][i][4 * q + 1], kv[fb][i][4 * q + 2], kv[fb][i][4 * q + 3]};
+            st16_part(rpart, base + (uint32_t)((((fs * 2 + fb) * NDB + db) * 4 + q) * 64 + lane) * 16,
+                      __builtin_bit_cast(u32x4, v));
           }
     }
   }
 
-  // ---- meet the group's other splits. The partial stores are complete
-  // (acknowledged at the agent's coherence point) before the count.
+  // ---- meet the group's other splits. The partial stores are complete (in
+  // this XCD's L2) before the count. If every split of the group runs on one
+  // XCD, that L2 is the one place all of them read the partials from. If not,
+  // each split writes its L2 back (an agent-scope release) and counts itself
+  // in again, and after the second count drops stale lines (an agent-scope
+  // acquire), so its loads see memory.
   wait_vmcnt<0>();
   __syncthreads();
   __shared__ unsigned ok_s;
   if (tid == 0) {
-    __hip_atomic_fetch_add(a.counters + group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned n = 0;
-    while (__hip_atomic_load(a.counters + group, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.nsplit &&
+    unsigned long long* cw = reinterpret_cast<unsigned long long*>(a.counters + 4 * group);
+    unsigned* c2 = a.counters + 4 * group + 2;
+    __hip_atomic_fetch_add(cw, 1ull << (8 * xcd_id()), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned n = 0, xcds = 0;
+    while (arrivals(__hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), xcds) < (unsigned)a.nsplit &&
            ++n < a.spin_limit)
       __builtin_amdgcn_s_sleep(2);
+    if (n < a.spin_limit && xcds > 1) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(c2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      while (__hip_atomic_load(c2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.nsplit &&
+             ++n < a.spin_limit)
+        __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
     ok_s = n < a.spin_limit;
   }
   __syncthreads();
@@ -603,8 +682,8 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const uint32_t so = (uint32_t)(min(sp + u, a.nsplit - 1) * pstride);
-          v0[u] = ld16_agent(rpart, so + o0);
-          v1[u] = ld16_agent(rpart, so + o1);
+          v0[u] = ld16_part(rpart, so + o0);
+          v1[u] = ld16_part(rpart, so + o1);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -626,7 +705,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       float s = 0.f;
       for (int sp = 0; sp < a.nsplit; ++sp)
         s += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 16));
+                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 0));
       const int f = fg0 + tid;
       ksumP[kperm(f)] = ok ? s : kQNaN;
       biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
@@ -645,7 +724,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ln = 32 * gg + 4 * cq + i;
-          v[i] = ld16_agent(rpart, (uint32_t)(sp * pstride) +
+          v[i] = ld16_part(rpart, (uint32_t)(sp * pstride) +
                                        (uint32_t)((((fst * 2 + fb) * NDB + db) * 4 + q) * 64 + ln) * 16);
         }
 #pragma unroll
@@ -664,7 +743,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       float s = 0.f;
       for (int sp = 0; sp < a.nsplit; ++sp)
         s += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 16));
+                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 0));
       a.ks_out[(size_t)bh * F + fg0 + tid] = ok ? s : kQNaN;
     }
   }
@@ -720,12 +799,13 @@ static KvsPlan kvs_plan(const Problem& p, int cus) {
   int ns = cus / k.groups;
   const int maxs = (p.N + 2 * step - 1) / (2 * step);  // at least two steps per split
   if (ns > maxs) ns = maxs;
+  if (ns > 255) ns = 255;  // the arrivals of one XCD fit a byte
   if (ns < 1) ns = 1;
   const int per = (p.N + ns - 1) / ns;
   k.chunk = (per + step - 1) / step * step;
   k.nsplit = (p.N + k.chunk - 1) / k.chunk;  // every split non-empty
   k.part_bytes = (size_t)k.groups * k.nsplit * (size_t)(k.FG * p.D + k.FG) * 4;
-  k.cnt_bytes = ((size_t)k.groups * 4 + 255) / 256 * 256;
+  k.cnt_bytes = ((size_t)k.groups * 16 + 255) / 256 * 256;
   return k;
 }
 
@@ -753,7 +833,7 @@ size_t kv2_reduce_workspace_bytes(const Problem& p) {
 
 template <int D, int F, bool PROJ, int MAP, bool PACK>
 static hipError_t launch_kvs_t(const KvsArgs& a, int groups, hipStream_t s, StageTimer* t) {
-  hipLaunchKernelGGL(kv_stage_reset_kernel, dim3(1), dim3(256), 0, s, a.counters, groups);
+  hipLaunchKernelGGL(kv_stage_reset_kernel, dim3(1), dim3(256), 0, s, a.counters, 4 * groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (t) t->mark();
