@@ -140,6 +140,21 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
                               int32_t L, int32_t causal, void* out, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* ttr_hybrid_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a fixed array of
+ * TTR_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs
+ * on until the process ends; the call itself allocates nothing. Arguments,
+ * layouts and results are those of ttr_hybrid_forward. TTR_ERR_WORKSPACE when
+ * ttr_workspace_bytes(d, L, causal, 0) exceeds TTR_NOALLOC_SCRATCH_BYTES.
+ * Every call on one GPU uses that GPU's one array (the kernels clear what must
+ * start at zero): calls that overlap on one GPU (other streams, other host
+ * threads) race and give undefined results; calls in one stream are safe. */
+#define TTR_NOALLOC_SCRATCH_BYTES (32u << 20)
+ttr_status ttr_hybrid_forward_noalloc(ttr_dims d, const void* Q, const void* K, const void* V,
+                                      const void* W, const float* b, const float* g, float eps,
+                                      int32_t L, int32_t causal, void* out, void* stream);
+
 /* Gradients of the hybrid forward (non-causal, elu + 1 map, projection W
  * required, 0 <= L <= N) for its trainable parameters, given
  * dout = dLoss/dout fp32 [B,H,N,D]:

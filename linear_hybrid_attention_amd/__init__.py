@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "TTRError", "load_library", "library_path", "exported_symbols", "Dims", "FMAPS",
     "feature_map", "kv_reduce", "apply", "landmark_attn", "blend", "causal_scan",
-    "hybrid_forward", "workspace_bytes", "status_string", "version",
+    "hybrid_forward", "hybrid_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "workspace_bytes", "status_string", "version",
     "TTR_FP32", "TTR_BF16",
 ]
 
@@ -93,6 +93,8 @@ _SIGS = {
     "ttr_causal_scan": [Dims, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
     "ttr_hybrid_forward": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                            _P, _P, ctypes.c_size_t, _P],
+    "ttr_hybrid_forward_noalloc": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                   _P, _P],
     "ttr_hybrid_backward": [Dims, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P, _P, _P, _P, _P,
                             ctypes.c_size_t, _P],
     "ttr_distill_step": [Dims, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
@@ -343,6 +345,29 @@ def hybrid_forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: Optiona
                                 None if ws is None else ws.data_ptr(), wsb, _stream(Q))
     _check(st, "ttr_hybrid_forward")
     return out
+
+
+def hybrid_forward_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W: Optional[torch.Tensor],
+                           b: Optional[torch.Tensor], g: Optional[torch.Tensor], eps: float = 1e-6, L: int = 0,
+                           causal: bool = False, out: Optional[torch.Tensor] = None, fmap: str = "elu1",
+                           chunk: int = 0) -> torch.Tensor:
+    """hybrid_forward with the library's fixed per-GPU workspace
+    (ttr_hybrid_forward_noalloc): no workspace argument, no allocation by the
+    call (out, when given, is written in place)."""
+    lib = load_library()
+    d = _dims(Q, _feat_dim(Q, W), fmap)
+    if out is None:
+        out = torch.empty_like(Q)
+    causal = (int(chunk) if chunk else 1) if causal else 0
+    st = lib.ttr_hybrid_forward_noalloc(d, _dev(Q, "Q"), _dev(K, "K", Q.dtype), _dev(V, "V", Q.dtype),
+                                        _dev(W, "W", Q.dtype), _dev(b, "b", torch.float32),
+                                        _dev(g, "g", torch.float32), float(eps), int(L), int(causal),
+                                        _dev(out, "out", Q.dtype), _stream(Q))
+    _check(st, "ttr_hybrid_forward_noalloc")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TTR_NOALLOC_SCRATCH_BYTES
 
 
 def nnt_layer_workspace_bytes(B: int, N: int, E: int, H: int, dtype: int, causal: bool = False,
