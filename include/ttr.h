@@ -32,7 +32,9 @@
  *     and out_lm are always fp32.
  *   - Every pointer must be 16-byte aligned. Outputs must not overlap inputs.
  *   - The caller owns all memory, including the workspace; the library never
- *     allocates, frees, synchronises or keeps a pointer after returning.
+ *     allocates, frees, synchronises or keeps a pointer after returning (the
+ *     replay buffer object and the fixed workspace array of
+ *     ttr_hybrid_forward_noalloc are the library's own, see there).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream). Calls are stateless and thread-safe.
  *   - Arguments are validated on the host before anything is enqueued; on a
@@ -40,9 +42,12 @@
  *     nothing. A failed launch returns TTR_ERR_HIP; ttr_last_hip_error()
  *     gives the hipError_t (per calling thread).
  *   - Results are bitwise deterministic run to run (no floating-point atomics).
- *   - Shape rules: B, H, N >= 1; D in {64, 128}; with W, F == 256; without W,
- *     F == D. fp32 IO needs D == 64. 0 <= L <= N. Ragged N (not a multiple of
- *     any tile size) is supported.
+ *   - Shape rules: B, H, N >= 1; D in {64, 128}; with W, F a multiple of 256
+ *     (else TTR_ERR_SHAPE), of which F == 256 is implemented by every entry
+ *     point and F == 512 by the bf16 ttr_hybrid_forward (and its _noalloc
+ *     form); other multiples return TTR_ERR_UNSUPPORTED. Without W, F == D.
+ *     fp32 IO needs D == 64. 0 <= L <= N. Ragged N (not a multiple of any
+ *     tile size) is supported.
  *   - The relu and softmax feature maps are those of the NNT linear attention,
  *     applied to already projected features: they need W == NULL and no
  *     landmark branch (L == 0); otherwise TTR_ERR_UNSUPPORTED.
@@ -76,7 +81,7 @@ typedef enum { TTR_FP32 = 0, TTR_BF16 = 1 } ttr_dtype;
 
 typedef enum { TTR_FMAP_ELU1 = 0, TTR_FMAP_RELU = 1, TTR_FMAP_SOFTMAX = 2 } ttr_fmap;
 
-/* Problem sizes. F is the feature dimension (256 with a projection W, D without). */
+/* Problem sizes. F is the feature dimension (a multiple of 256 with a projection W, D without). */
 typedef struct {
   int32_t B, H, N, D, F;
   int32_t dtype; /* ttr_dtype of the IO tensors */

@@ -497,14 +497,15 @@ hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& 
   a.nwg = a.ntiles * p.B * p.H;
   a.out = static_cast<uint16_t*>(out);
   if (p.dtype != 1) return hipErrorInvalidValue;
+  if (p.proj && p.F != 256 && p.F != 512) return hipErrorInvalidValue;
   if (p.D == 128) {
-    if (p.proj) return launch_fused_t<128, 256, kElu1>(a, s);
+    if (p.proj) return p.F == 512 ? launch_fused_t<128, 512, kElu1>(a, s) : launch_fused_t<128, 256, kElu1>(a, s);
     if (p.fmap == kRelu) return launch_fused_t<128, 128, kRelu>(a, s);
     if (p.fmap == kSoftmax) return launch_fused_t<128, 128, kSoftmax>(a, s);
     return launch_fused_t<128, 128, kElu1>(a, s);
   }
   if (p.D == 64) {
-    if (p.proj) return launch_fused_t<64, 256, kElu1>(a, s);
+    if (p.proj) return p.F == 512 ? launch_fused_t<64, 512, kElu1>(a, s) : launch_fused_t<64, 256, kElu1>(a, s);
     if (p.fmap == kRelu) return launch_fused_t<64, 64, kRelu>(a, s);
     if (p.fmap == kSoftmax) return launch_fused_t<64, 64, kSoftmax>(a, s);
     return launch_fused_t<64, 64, kElu1>(a, s);

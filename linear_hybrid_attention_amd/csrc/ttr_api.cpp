@@ -121,7 +121,7 @@ size_t ttr_workspace_bytes(ttr_dims d, int32_t L, int32_t causal, int32_t chunk)
     return causal_workspace_bytes(make_problem(d, false), chunk);
   }
   const bool proj = d.F != d.D;
-  if (check_dims(d, proj) != TTR_OK || L < 0 || L > d.N) return 0;
+  if (check_dims(d, proj, forward_max_f(d)) != TTR_OK || L < 0 || L > d.N) return 0;
   return hybrid_ws(d, proj, L);
 }
 
@@ -283,7 +283,7 @@ static ttr_status hybrid_forward_impl(ttr_dims d, const void* Q, const void* K, 
     return causal_scan_impl(d, Q, K, V, W, b, eps, chunk, out, ws, ws_bytes, s, outer);
   }
   const bool proj = W != nullptr;
-  TTR_TRY(check_dims(d, proj));
+  TTR_TRY(check_dims(d, proj, forward_max_f(d)));
   if (L < 0 || L > d.N) return TTR_ERR_SHAPE;
   if (d.fmap != TTR_FMAP_ELU1 && L > 0) return TTR_ERR_UNSUPPORTED;  // landmarks belong to the elu+1 TTR layer
   TTR_TRY(check_ptr(Q));

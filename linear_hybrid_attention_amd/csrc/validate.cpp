@@ -1,6 +1,7 @@
 // Host-only argument validation for the C ABI. Shape rules follow the
 // method's pages: "Flux2TTRTrainer", section "Inputs worth setting"
-// (feature_dim is a multiple of 256; this library implements 256), and
+// (feature_dim is a multiple of 256; this library implements 256, and 512 on
+// the bf16 hybrid forward), and
 // "NNT Define Linear Attention", section "The inputs" (causal flag, eps).
 #include "validate.hpp"
 
@@ -14,7 +15,7 @@ size_t dtype_bytes(int32_t dtype) {
   }
 }
 
-ttr_status check_dims(const ttr_dims& d, bool has_w) {
+ttr_status check_dims(const ttr_dims& d, bool has_w, int32_t max_f) {
   if (dtype_bytes(d.dtype) == 0) return TTR_ERR_DTYPE;
   if (d.fmap < TTR_FMAP_ELU1 || d.fmap > TTR_FMAP_SOFTMAX) return TTR_ERR_SHAPE;
   // relu / softmax: the NNT linear attention's maps on projected features
@@ -23,7 +24,7 @@ ttr_status check_dims(const ttr_dims& d, bool has_w) {
   if (d.D != 64 && d.D != 128) return TTR_ERR_SHAPE;
   if (has_w) {
     if (d.F < 256 || d.F % 256 != 0) return TTR_ERR_SHAPE;
-    if (d.F != 256) return TTR_ERR_UNSUPPORTED;
+    if (d.F > max_f) return TTR_ERR_UNSUPPORTED;
   } else if (d.F != d.D) {
     return TTR_ERR_SHAPE;
   }

@@ -14,7 +14,13 @@ size_t dtype_bytes(int32_t dtype);
 
 // Rules on B, H, N, D, F, dtype shared by every entry point.
 // has_w: a projection W is given (F must be 256) or not (F must equal D).
-ttr_status check_dims(const ttr_dims& d, bool has_w);
+// max_f: the largest projected feature dimension the calling entry point
+// implements (a multiple of 256 above it is TTR_ERR_UNSUPPORTED).
+ttr_status check_dims(const ttr_dims& d, bool has_w, int32_t max_f = 256);
+
+// Projected feature dimensions of the bf16 hybrid forward: 256 and 512.
+constexpr int32_t kMaxFeatureDimBf16Forward = 512;
+inline int32_t forward_max_f(const ttr_dims& d) { return d.dtype == TTR_BF16 ? kMaxFeatureDimBf16Forward : 256; }
 
 // NULL and 16-byte alignment of a required pointer (NULL -> TTR_ERR_NULL).
 ttr_status check_ptr(const void* p);

@@ -40,6 +40,23 @@ def test_hybrid_forward_full_workloads(name):
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("shape", [dict(), dict(B=2, H=2, N=777, L=33), dict(H=2, N=1500, D=64, L=48),
+                                   dict(H=2, N=1000, L=0)])
+def test_hybrid_forward_feature_dim_512(shape):
+    # feature_dim 512 ("Flux2TTRTrainer", "Inputs worth setting": a multiple of
+    # 256): the flux_1024 shape at F = 512, every element, and ragged shapes
+    w = small("flux_1024", F=512, seed=40 + len(shape), **shape)
+    x = workloads.make_inputs(w)
+    print(f"[hybrid-f512] B={w.B} H={w.H} N={w.N} D={w.D} F={w.F} L={w.L}", flush=True)
+    out = run_hybrid(w, to_device(w, x))
+    torch.cuda.synchronize()
+    ref = oracle_hybrid(w, x)
+    err = normwise(host(out), ref)
+    print(f"[hybrid-f512] normwise err {err:.3e}", flush=True)
+    assert np.isfinite(host(out)).all()
+    assert err <= TOL[w.dtype], err
+
+
 @pytest.mark.timeout(600)
 def test_causal_full_size_whole_output():
     # the causal configuration as stated (chunk 256) through the metric entry
