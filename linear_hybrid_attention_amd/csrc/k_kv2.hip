@@ -117,6 +117,7 @@ struct KvsArgs {
   const float* bias;  // [H][F] or NULL
   int H, N, L;
   int nsplit, chunk;     // token splits of a group and the tokens of each (a multiple of the step)
+  int groups, per_xcd;   // (batch, head, feature group) groups; grid slots per XCD (grid = 8 per_xcd)
   float* part;           // [groups][nsplit][FG * D + FG] fp32 partials
   unsigned* counters;    // [groups][4]: arrivals per XCD (8 byte fields), second-round arrivals, unused;
                          // zero on entry (kv_stage_reset_kernel)
@@ -238,7 +239,12 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   const bool producer = w < 4;
   const int pw = w & 3;                   // index among the producers (or the consumers)
   const int fs = pw % NPW, tg = pw / NPW;  // feature slice, token group
-  const int item = xcd_item(blockIdx.x, gridDim.x);
+  // Workgroup i runs on XCD i % 8 and takes slot i / 8 of that XCD's per_xcd
+  // slots; the slots of one XCD hold whole groups (per_xcd is a multiple of
+  // nsplit), so all splits of a group share an L2. Slots past the last group
+  // have no work.
+  const int item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+  if (item >= a.groups * a.nsplit) return;
   const int split = item % a.nsplit, group = item / a.nsplit;
   const int bh = group / NG, fgi = group % NG, h = bh % a.H;
   const int fg0 = fgi * FG;         // first feature of the group
@@ -658,6 +664,24 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   // call's result is then undefined, and visibly so).
   const bool ok = ok_s != 0;
 
+  // ksum of feature fg0 + f summed over the splits in split order (loads
+  // issued eight at a time, ahead of their adds)
+  auto ksum_over_splits = [&](int f) -> float {
+    float s = 0.f;
+    for (int sp = 0; sp < a.nsplit; sp += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rpart, (int)((uint32_t)(min(sp + u, a.nsplit - 1) * pstride) + (FG * D + f) * 4),
+                                             0, 0));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp + u < a.nsplit) s += v[u];
+    }
+    return s;
+  };
+
   // ---- this split's share of the reduction, summed over the splits in order
   // (each thread's loads for up to eight splits issued before its adds)
   if constexpr (PACK) {
@@ -702,10 +726,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       *reinterpret_cast<u32x4*>(ch + toff<64, kRowRead>(32 * db + (ln & 31), 32 * fb + 16 * k + 8 * (ln >> 5))) = o;
     }
     if (split == 0 && tid < FG) {  // ksum and bias of the group's features, in kperm order
-      float s = 0.f;
-      for (int sp = 0; sp < a.nsplit; ++sp)
-        s += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 0));
+      const float s = ksum_over_splits(tid);
       const int f = fg0 + tid;
       ksumP[kperm(f)] = ok ? s : kQNaN;
       biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
@@ -740,10 +761,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       }
     }
     if (split == 0 && tid < FG) {
-      float s = 0.f;
-      for (int sp = 0; sp < a.nsplit; ++sp)
-        s += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rpart, (int)((uint32_t)(sp * pstride) + (FG * D + tid) * 4), 0, 0));
+      const float s = ksum_over_splits(tid);
       a.ks_out[(size_t)bh * F + fg0 + tid] = ok ? s : kQNaN;
     }
   }
@@ -786,7 +804,7 @@ static int kvs_cus() {
 }
 
 struct KvsPlan {
-  int FG, NG, groups, nsplit, chunk;
+  int FG, NG, groups, nsplit, chunk, per_xcd;
   size_t part_bytes, cnt_bytes;  // fp32 partials; counters (256-byte aligned)
 };
 
@@ -796,7 +814,10 @@ static KvsPlan kvs_plan(const Problem& p, int cus) {
   k.NG = p.F / k.FG;
   const int step = 32 * (4 / (k.FG / 64));
   k.groups = p.B * p.H * k.NG;
-  int ns = cus / k.groups;
+  // Groups are spread over the 8 XCDs, gx per XCD, each with its splits on
+  // that XCD's compute units (one workgroup per unit).
+  const int gx = (k.groups + 7) / 8;
+  int ns = (cus / 8) / gx;
   const int maxs = (p.N + 2 * step - 1) / (2 * step);  // at least two steps per split
   if (ns > maxs) ns = maxs;
   if (ns > 255) ns = 255;  // the arrivals of one XCD fit a byte
@@ -804,6 +825,7 @@ static KvsPlan kvs_plan(const Problem& p, int cus) {
   const int per = (p.N + ns - 1) / ns;
   k.chunk = (per + step - 1) / step * step;
   k.nsplit = (p.N + k.chunk - 1) / k.chunk;  // every split non-empty
+  k.per_xcd = gx * k.nsplit;
   k.part_bytes = (size_t)k.groups * k.nsplit * (size_t)(k.FG * p.D + k.FG) * 4;
   k.cnt_bytes = ((size_t)k.groups * 16 + 255) / 256 * 256;
   return k;
@@ -837,7 +859,7 @@ static hipError_t launch_kvs_t(const KvsArgs& a, int groups, hipStream_t s, Stag
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (t) t->mark();
-  hipLaunchKernelGGL((kv_stage_kernel<D, F, PROJ, MAP, PACK>), dim3(groups * a.nsplit), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((kv_stage_kernel<D, F, PROJ, MAP, PACK>), dim3(8 * a.per_xcd), dim3(512), 0, s, a);
   e = hipGetLastError();
   if (t) t->mark();
   return e;
@@ -877,6 +899,8 @@ static KvsArgs kvs_args(const Problem& p, const KvsPlan& k, const void* K, const
   a.L = L;
   a.nsplit = k.nsplit;
   a.chunk = k.chunk;
+  a.groups = k.groups;
+  a.per_xcd = k.per_xcd;
   a.part = reinterpret_cast<float*>(ws);
   a.counters = reinterpret_cast<unsigned*>(ws + k.part_bytes);
   a.spin_limit = 1u << 20;  // about a second of polling
