@@ -52,6 +52,8 @@ def parse():
                     help="time each staged entry point (feature map, key/value reduction, apply, landmark branch, "
                          "blend) with its own roofline instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="causal workloads: run this chunk (64, 128 or 256) instead of the workload's own")
     ap.add_argument("--cold", action="store_true",
                     help="cold caches: write a 1 GiB scratch buffer before every timed forward (flushes the L2s "
                          "and the 256 MB MALL) and time each forward on its own")
@@ -149,7 +151,7 @@ def kernel_sources(name):
         return ["k_kv2.hip"] + common
     if name.startswith("fused_"):
         return ["k_fused.hip"] + common
-    if name.startswith("causal2_"):
+    if name.startswith("causal1_"):
         return ["k_causal2.hip"] + common
     return ["k_hybrid.hip", "k_kv.hip", "k_causal.hip"] + common
 
@@ -175,19 +177,17 @@ def kernel_plan(w):
     if w.causal:
         chunk = w.chunk
         nseg, cps = causal_plan(w, chunk)
-        # segment totals read K and V of every segment but the last: a re-read
-        # the method does not need, so it carries no algorithmic bytes; the
-        # walk reads Q, K, V and writes out once
+        # one pass: each segment's state from its K and V (all but the last
+        # segment), then the walk; the state pass's reading of K and V again
+        # is the design's (its second read comes from cache), so the method's
+        # bytes are Q, K, V read once and out written once
         seg_tokens = min(N, (nseg - 1) * cps * chunk)
         state = 2 * D * D + D  # P += phi(k)^T v, z += phi(k) per token
-        plan = []
-        if nseg > 1:
-            plan.append((f"causal2_kernel<{chunk}, false, 0>", BH * seg_tokens * state, 0))
         # per token: its share of the causal score and value tiles (C/2 keys on
         # average, plus the diagonal), the inter-chunk product and the state update
         walk = BH * N * (2 * 2 * D * (chunk // 2 + 16) + 2 * D * D + state)
-        plan.append((f"causal2_kernel<{chunk}, true, 0>", walk, 4 * tok))
-        return plan
+        return [("causal1_reset_kernel", 0, 0),
+                (f"causal1_kernel<{chunk}, 0>", BH * seg_tokens * state + walk, 4 * tok)]
     proj = 2 * N * D * F  # X W_h
     kv = 2 * N * F * D + N * F  # phi(K)^T V and ksum
     apply = 2 * N * F * D + 2 * N * F  # phi(Q) KV and phi(Q) . ksum
@@ -211,9 +211,10 @@ def roofline(w, flops, nbytes, ms):
 
 
 def causal_plan(w, chunk):
-    """Segments of the chunked scan: about 1024 workgroups over the (batch, head) slices."""
+    """Segments of the single-pass scan: about 1024 tokens each, shorter when that gives fewer than 512 workgroups."""
     nchunks = -(-w.N // chunk)
-    want = min(max(-(-1024 // (w.B * w.H)), 1), nchunks)
+    want = max(-(-w.N // 1024), -(-512 // (w.B * w.H)))
+    want = max(min(want, nchunks), 1)
     cps = -(-nchunks // want)
     return -(-nchunks // cps), cps
 
@@ -971,6 +972,8 @@ def main():
         main_cosine(args)
         return
     w = workloads.WORKLOADS[args.workload]
+    if args.chunk and w.causal:
+        w = w.with_(chunk=args.chunk)
     x = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

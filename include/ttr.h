@@ -393,7 +393,8 @@ int ttr_last_hip_error(void);
  * ... after each kernel (or stage) it launches, as long as events remain:
  *   bf16 hybrid: key/value partial sums, operand pack, fused query kernel;
  *   fp32 hybrid: key/value reduction, query kernel;
- *   causal: segment totals (when the sequence has several segments), chunk walk;
+ *   causal, bf16 with D = 64: the reset of its segment flags, the single-pass scan;
+ *   other causal: segment totals (when the sequence has several segments), chunk walk;
  *   layer: the weight transposes, Q/K/V projection, the attention's stages
  *     as above, out projection;
  *   backward: Q projection, K projection (one stage each, whatever the batch),

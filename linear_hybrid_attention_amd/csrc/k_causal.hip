@@ -327,8 +327,8 @@ size_t causal_seg_bytes(const Problem& p, int chunk) {
 }
 
 size_t causal_workspace_bytes(const Problem& p, int chunk) {
-  // segment totals, then (streamed kernel only) the store sink
-  return causal_seg_bytes(p, chunk) + (causal2_supported(p, chunk) ? CAUSAL2_SINK_BYTES : 0);
+  // the streamed single-pass kernel's prefixes, flags and store sink; else segment totals
+  return causal2_supported(p, chunk) ? causal1_workspace_bytes(p, chunk) : causal_seg_bytes(p, chunk);
 }
 
 template <typename T, int D, int C, int MAP>

@@ -18,7 +18,10 @@
 //  * the next chunk's query rows are loaded during the current chunk;
 //  * each wave's 32 x 64 output block goes through LDS so the global stores
 //    are whole 16-byte pieces.
-// Pass 1 (segment totals) and pass 2 (walk) are the same kernel, WALK = false / true.
+// One launch (after a one-workgroup reset of its flags): each workgroup sums
+// its segment's state, takes the inclusive prefix of the segment before from
+// the workgroup that had it (a chained scan over segments, waits bounded),
+// publishes its own, then walks the segment (causal1_kernel below).
 #include "common.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"
@@ -31,8 +34,12 @@ struct Causal2Args {
   const uint16_t* V;
   const float* bias;  // [H][64] or NULL
   float eps;
-  int H, N, cps, nseg;
-  float* seg;  // [BH][nseg][64*64 + 64]: segment totals P^T (row d, column f), then z
+  int H, N, cps, nseg, nbh;
+  float* seg;        // [BH][nseg][64*64 + 64]: inclusive prefixes P^T (row d, column f), then z
+  unsigned* flags;   // [BH][nseg]: prefix published (zero on entry, causal1_reset_kernel)
+  unsigned* ticket;  // next segment to take (zero on entry)
+  unsigned* err;     // set when a wait gave up (zero on entry)
+  unsigned spin_limit;
   uint16_t* sink;  // CAUSAL2_SINK_BYTES of workspace that absorb the stores of rows past N
   uint16_t* out;
 };
@@ -57,11 +64,15 @@ struct Causal2Shape {
   static constexpr int WG_PER_CU = (160 * 1024) / bytes >= 2 ? 2 : 1;
 };
 
+// Chunks [cbeg, cend) of (batch, head) bh. WALK = false: the segment's
+// state only (P and zr summed from the values they hold on entry); WALK = true:
+// the outputs, starting from the state P, zr of the tokens before the
+// segment. smem is laid out for the walk (the state pass uses its first two tiles).
 template <int C, bool WALK, int MAP>
-__global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causal2_kernel(Causal2Args a) {
-  using S = Causal2Shape<C, WALK>;
+__device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned char* smem, int bh, int cbeg, int cend,
+                                               f32x16& P, float& zr) {
+  using S = Causal2Shape<C, true>;
   constexpr int D = 64, NB = S::NB, QB = S::QB, PER_T = S::PER_T;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::bytes];
   uint16_t* ktt = reinterpret_cast<uint16_t*>(smem);  // phi(K) rows, kTrRead (state update)
   uint16_t* vt = ktt + S::TILE;                        // V rows, kTrRead
   uint16_t* kt = vt + S::TILE;                         // phi(K) rows, kRowRead (walk: scores)
@@ -70,8 +81,7 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
   uint16_t* Pt = reinterpret_cast<uint16_t*>(smem + S::kv_bytes);
   uint16_t* ostage = reinterpret_cast<uint16_t*>(smem + S::kv_bytes + S::pt_bytes + S::zb_bytes);
 
-  const int s = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
-  if (!WALK && s >= a.nseg - 1) return;  // the last segment's total is never read
+  const int h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;  // wave-uniform, kept in a scalar register
   const int N = a.N;
@@ -79,23 +89,11 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
   const uint16_t* Qg = a.Q + base;
   const uint16_t* Kg = a.K + base;
   const uint16_t* Vg = a.V + base;
-  const int nchunks = (N + C - 1) / C;
-  const int cbeg = s * a.cps, cend = min(nchunks, cbeg + a.cps);
-  if (cbeg >= cend) return;
 
   const Frag<uint16_t> ones = __builtin_bit_cast(Frag<uint16_t>, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   // P^T tile owned by this wave: rows dt*32.., columns ft*32.. (dt = w >> 1, ft = w & 1).
   const int dt = w >> 1, ft = w & 1;
-  f32x16 P = f32x16{};
-  float zr = 0.f;  // z[ft*32 + c], kept by the waves with dt == 0
-  if constexpr (WALK) {
-    for (int s2 = 0; s2 < s; ++s2) {
-      const float* sp = a.seg + ((size_t)bh * a.nseg + s2) * (size_t)(D * D + D);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) P[r] += sp[(dt * 32 + crow(lane, r)) * D + ft * 32 + c];
-      zr += sp[D * D + ft * 32 + c];
-    }
-  }
+  // (zr: z[ft*32 + c]; the waves with dt == 0 write it to LDS)
   // A thread's K pieces are all logical piece tid % 8 of their rows: 8 fixed columns.
   const int kcol = (tid & 7) * 8;
   float kb[8];
@@ -329,27 +327,118 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, WALK>::WG_PER_CU)) void causa
     if constexpr (WALK) store_out(ch);
   }
 
-  if constexpr (!WALK) {
-    float* o = a.seg + ((size_t)bh * a.nseg + s) * (size_t)(D * D + D);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[(dt * 32 + crow(lane, r)) * D + ft * 32 + c] = P[r];
-    if (dt == 0 && lane < 32) o[D * D + ft * 32 + c] = zr;
+}
+
+
+// Single pass: workgroups take segments in the order of an atomic ticket
+// (ticket t: segment t / BH of (batch, head) t % BH), sum the segment's
+// state, wait for the inclusive prefix of the segment before (published by a
+// workgroup with a smaller ticket, so one that is already running), publish
+// their own inclusive prefix (the one before plus this segment's, in that
+// order: the result is the same whatever the timing), then walk the segment.
+// Prefixes are written and read with agent-coherent accesses; a wait that
+// exceeds spin_limit polls sets *err and makes the outputs NaN.
+template <int C, int MAP>
+__global__ __launch_bounds__(256, (Causal2Shape<C, true>::WG_PER_CU)) void causal1_kernel(Causal2Args a) {
+  constexpr int D = 64, E = D * D + D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Causal2Shape<C, true>::bytes];
+  __shared__ unsigned tk_s, ok_s;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3, dt = w >> 1, ft = w & 1;
+  if (tid == 0) tk_s = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int t = (int)tk_s;
+  const int s = t / a.nbh, bh = t % a.nbh;
+  const int nchunks = (a.N + C - 1) / C;
+  const int cbeg = s * a.cps, cend = min(nchunks, cbeg + a.cps);  // non-empty by the plan
+  const bool last = s == a.nseg - 1;  // no segment reads its prefix
+
+  f32x16 PA = f32x16{};
+  float zA = 0.f;
+  if (!last) {
+    causal_segment<C, false, MAP>(a, smem, bh, cbeg, cend, PA, zA);
+    __syncthreads();  // LDS free for the walk
   }
+  f32x16 P = f32x16{};
+  float zr = 0.f;
+  if (s > 0) {
+    if (tid == 0) {
+      const unsigned* fl = a.flags + (size_t)bh * a.nseg + (s - 1);
+      unsigned n = 0;
+      while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u && ++n < a.spin_limit)
+        __builtin_amdgcn_s_sleep(2);
+      ok_s = n < a.spin_limit;
+      if (!ok_s) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const float* ip = a.seg + ((size_t)bh * a.nseg + (s - 1)) * E;
+    const bool ok = ok_s != 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      P[r] = ok ? __hip_atomic_load(ip + (dt * 32 + crow(lane, r)) * D + ft * 32 + c, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT)
+                : __uint_as_float(0x7fc00000u);
+    zr = ok ? __hip_atomic_load(ip + D * D + ft * 32 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+            : __uint_as_float(0x7fc00000u);
+  }
+  if (!last) {
+    float* op = a.seg + ((size_t)bh * a.nseg + s) * E;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      __hip_atomic_store(op + (dt * 32 + crow(lane, r)) * D + ft * 32 + c, P[r] + PA[r], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    if (dt == 0 && lane < 32)
+      __hip_atomic_store(op + D * D + ft * 32 + c, zr + zA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmcnt<0>();  // the prefix is at the agent's coherence point before its flag
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(a.flags + (size_t)bh * a.nseg + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  causal_segment<C, true, MAP>(a, smem, bh, cbeg, cend, P, zr);
+}
+
+__global__ void causal1_reset_kernel(unsigned* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) __hip_atomic_store(p + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int C, int MAP>
 static hipError_t launch_causal2_t(const Causal2Args& a, int B, hipStream_t s, StageTimer* t) {
-  const dim3 grid(a.nseg, B * a.H), block(256);
-  if (a.nseg > 1) {
-    hipLaunchKernelGGL((causal2_kernel<C, false, MAP>), grid, block, 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    t->mark();
-  }
-  hipLaunchKernelGGL((causal2_kernel<C, true, MAP>), grid, block, 0, s, a);
-  const hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(causal1_reset_kernel, dim3(1), dim3(256), 0, s, a.flags, a.nbh * a.nseg + 2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  t->mark();
+  hipLaunchKernelGGL((causal1_kernel<C, MAP>), dim3(a.nseg * a.nbh), dim3(256), 0, s, a);
+  e = hipGetLastError();
   t->mark();
   return e;
+}
+
+// Segments of the single pass: about 1024 tokens each (so the K and V rows a
+// segment reads twice are still in the last-level cache the second time),
+// shorter when that gives fewer than 512 workgroups; every segment non-empty.
+void causal1_plan(const Problem& p, int chunk, int* nseg, int* cps) {
+  const int nchunks = (p.N + chunk - 1) / chunk;
+  const int bh = p.B * p.H;
+  int want = (p.N + 1023) / 1024;
+  const int fill = (512 + bh - 1) / bh;
+  if (want < fill) want = fill;
+  if (want > nchunks) want = nchunks;
+  if (want < 1) want = 1;
+  *cps = (nchunks + want - 1) / want;
+  *nseg = (nchunks + *cps - 1) / *cps;
+}
+
+// Workspace: prefixes [BH][nseg][D D + D] fp32 | flags [BH][nseg], ticket, err
+// (256-byte aligned) | the store sink.
+static size_t causal1_prefix_bytes(const Problem& p, int nseg) {
+  return (size_t)p.B * p.H * nseg * (size_t)(64 * 64 + 64) * sizeof(float);
+}
+static size_t causal1_flag_bytes(const Problem& p, int nseg) {
+  return ((size_t)p.B * p.H * nseg * 4 + 8 + 255) / 256 * 256;
+}
+size_t causal1_workspace_bytes(const Problem& p, int chunk) {
+  int nseg, cps;
+  causal1_plan(p, chunk, &nseg, &cps);
+  return causal1_prefix_bytes(p, nseg) + causal1_flag_bytes(p, nseg) + CAUSAL2_SINK_BYTES;
 }
 
 bool causal2_supported(const Problem& p, int chunk) {
@@ -374,9 +463,15 @@ hipError_t launch_causal2(const Problem& p, const void* Q, const void* K, const 
   a.eps = eps;
   a.H = p.H;
   a.N = p.N;
-  causal_plan(p, chunk, &a.nseg, &a.cps);
-  a.seg = static_cast<float*>(ws);
-  a.sink = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + causal_seg_bytes(p, chunk));
+  causal1_plan(p, chunk, &a.nseg, &a.cps);
+  a.nbh = p.B * p.H;
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  a.seg = reinterpret_cast<float*>(w8);
+  a.flags = reinterpret_cast<unsigned*>(w8 + causal1_prefix_bytes(p, a.nseg));
+  a.ticket = a.flags + (size_t)a.nbh * a.nseg;
+  a.err = a.ticket + 1;
+  a.spin_limit = 1u << 20;  // a tenth of a second or so of polling
+  a.sink = reinterpret_cast<uint16_t*>(w8 + causal1_prefix_bytes(p, a.nseg) + causal1_flag_bytes(p, a.nseg));
   static_assert(CAUSAL2_SINK_BYTES >= 2 * 4 * 64 * 16, "one 16-byte slot per store of a wave (QB <= 2)");
   a.out = static_cast<uint16_t*>(out);
   if (p.fmap == kRelu) return launch_causal2_m<kRelu>(a, p.B, chunk, s, t);

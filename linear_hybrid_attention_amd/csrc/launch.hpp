@@ -103,6 +103,7 @@ hipError_t launch_blend(const Problem& p, const float* lin, const float* lm, con
 void causal_plan(const Problem& p, int chunk, int* nseg, int* chunks_per_seg);
 size_t causal_workspace_bytes(const Problem& p, int chunk);
 size_t causal_seg_bytes(const Problem& p, int chunk);  // the segment-totals part of the workspace
+size_t causal1_workspace_bytes(const Problem& p, int chunk);  // the single-pass bf16 D = 64 kernel's
 // k_causal2.hip: the bf16, D = 64 scan with streamed chunk tiles (same plan; the
 // workspace adds a sink for the stores of rows past N after the segment totals).
 constexpr size_t CAUSAL2_SINK_BYTES = 8192;
