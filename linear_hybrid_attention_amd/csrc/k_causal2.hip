@@ -47,9 +47,13 @@ struct Causal2Args {
 template <int C, bool WALK>
 struct Causal2Shape {
   static constexpr int D = 64;
+  // waves: four own the 32 x 32 tiles of the state P^T; at C = 256 four more
+  // take query blocks, so that every wave holds one block (two waves per SIMD)
+  static constexpr int NW = C == 256 ? 8 : 4;
+  static constexpr int NT = 64 * NW;
   static constexpr int TILE = C * D;               // elements of the K (or V) tile
-  static constexpr int PER_T = 2 * TILE / 8 / 256;  // 16-byte pieces per thread per chunk (K then V)
-  static_assert(PER_T * 256 * 8 == 2 * TILE && (TILE / 8) % 256 == 0, "whole pieces, K/V split per piece index");
+  static constexpr int PER_T = 2 * TILE / 8 / NT;  // 16-byte pieces per thread per chunk (K then V)
+  static_assert(PER_T * NT * 8 == 2 * TILE && (TILE / 8) % NT == 0, "whole pieces, K/V split per piece index");
   // phi(K) is read transposed by the state update and, in the walk, also as
   // rows by the score product: the walk keeps it twice, once per swizzle.
   static constexpr int nk = WALK ? 2 : 1;
@@ -57,8 +61,8 @@ struct Causal2Shape {
   static constexpr int pt_bytes = WALK ? D * D * 2 : 0;  // P^T as MFMA operand, [d][f] kRowRead
   static constexpr int zb_bytes = 2 * D * 4;             // z, then the bias (zeros without one)
   static constexpr int NB = C / 32;                // 32-token blocks per chunk
-  static constexpr int QB = (NB + 3) / 4;          // query blocks per wave
-  static constexpr int o_bytes = WALK ? 4 * QB * 32 * D * 2 : 0;  // per-wave output staging
+  static constexpr int QB = (NB + NW - 1) / NW;    // query blocks per wave
+  static constexpr int o_bytes = WALK ? NW * QB * 32 * D * 2 : 0;  // per-wave output staging
   static constexpr int bytes = kv_bytes + pt_bytes + zb_bytes + o_bytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static constexpr int WG_PER_CU = (160 * 1024) / bytes >= 2 ? 2 : 1;
@@ -72,7 +76,7 @@ template <int C, bool WALK, int MAP>
 __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned char* smem, int bh, int cbeg, int cend,
                                                f32x16& P, float& zr) {
   using S = Causal2Shape<C, true>;
-  constexpr int D = 64, NB = S::NB, QB = S::QB, PER_T = S::PER_T;
+  constexpr int D = 64, NB = S::NB, QB = S::QB, PER_T = S::PER_T, NW = S::NW, NT = S::NT;
   uint16_t* ktt = reinterpret_cast<uint16_t*>(smem);  // phi(K) rows, kTrRead (state update)
   uint16_t* vt = ktt + S::TILE;                        // V rows, kTrRead
   uint16_t* kt = vt + S::TILE;                         // phi(K) rows, kRowRead (walk: scores)
@@ -83,7 +87,8 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
 
   const int h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;  // wave-uniform, kept in a scalar register
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);  // wave-uniform, kept in a scalar register
+  const bool owner = w < 4;  // owns a tile of the state
   const int N = a.N;
   const size_t base = (size_t)bh * N * D;
   const uint16_t* Qg = a.Q + base;
@@ -91,8 +96,8 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
   const uint16_t* Vg = a.V + base;
 
   const Frag<uint16_t> ones = __builtin_bit_cast(Frag<uint16_t>, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-  // P^T tile owned by this wave: rows dt*32.., columns ft*32.. (dt = w >> 1, ft = w & 1).
-  const int dt = w >> 1, ft = w & 1;
+  // P^T tile owned by waves 0-3: rows dt*32.., columns ft*32.. (dt = w >> 1, ft = w & 1).
+  const int dt = (w >> 1) & 1, ft = w & 1;
   // (zr: z[ft*32 + c]; the waves with dt == 0 write it to LDS)
   // A thread's K pieces are all logical piece tid % 8 of their rows: 8 fixed columns.
   const int kcol = (tid & 7) * 8;
@@ -101,7 +106,7 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
   for (int j = 0; j < 8; ++j) kb[j] = a.bias ? a.bias[(size_t)h * D + kcol + j] : 0.f;
   if (tid < D) bS[tid] = a.bias ? a.bias[(size_t)h * D + tid] : 0.f;
 
-  // K/V staging: piece i of thread tid is piece tid + 256 i of the chunk
+  // K/V staging: piece i of thread tid is piece tid + NT i of the chunk
   // (K pieces first); rows past N repeat row N - 1 and are zeroed (K) when
   // stored, so they contribute nothing.
   u32x4 stg[PER_T];
@@ -110,7 +115,7 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const bool isv = i >= PER_T / 2;
-      const int Pl = tid + 256 * (isv ? i - PER_T / 2 : i);
+      const int Pl = tid + NT * (isv ? i - PER_T / 2 : i);
       const int row = Pl / (D / 8), p = Pl % (D / 8);
       const int t = min(c0 + row, N - 1);
       stg[i] = *reinterpret_cast<const u32x4*>((isv ? Vg : Kg) + (size_t)t * D + p * 8);
@@ -121,7 +126,7 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const bool isv = i >= PER_T / 2;
-      const int Pl = tid + 256 * (isv ? i - PER_T / 2 : i);
+      const int Pl = tid + NT * (isv ? i - PER_T / 2 : i);
       const int row = Pl / (D / 8), p = Pl % (D / 8);
       if (isv) {
         *reinterpret_cast<u32x4*>(vt + toff<D, kTrRead>(row, p * 8)) = stg[i];
@@ -140,6 +145,7 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
     }
   };
   auto write_state = [&]() {
+    if (!owner) return;
 #pragma unroll
     for (int r = 0; r < 16; ++r) Pt[toff<D, kRowRead>(dt * 32 + crow(lane, r), ft * 32 + c)] = f2bf(P[r]);
     if (dt == 0 && g == 0) zS[ft * 32 + c] = zr;
@@ -151,7 +157,7 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
   auto load_q = [&](int ch) {
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
-      const int qb = (i & 1) ? (4 * i + 3 - w) : (4 * i + w);
+      const int qb = (i & 1) ? (NW * i + NW - 1 - w) : (NW * i + w);
       // Rows past N repeat row N - 1 and blocks past the chunk (waves without
       // a block when C = 64) load the last block: their outputs are not stored.
       const int q = min(ch * C + min(qb, NB - 1) * 32 + c, N - 1);
@@ -169,7 +175,7 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
     wave_lds_order();
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
-      const int qb = (i & 1) ? (4 * i + 3 - w) : (4 * i + w);
+      const int qb = (i & 1) ? (NW * i + NW - 1 - w) : (NW * i + w);
       const uint16_t* ot = ostage + (w * QB + i) * 32 * D;
       const int t0 = max(ch, 0) * C + qb * 32;
       uint16_t* og = a.out + base + (size_t)t0 * D;
@@ -235,7 +241,9 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
     // every row of Z holds the sums), in registers (the LDS copy is updated after
     // every wave has read the current one).
     // (The walk, short of registers, sums z on the VALU instead.)
-    if constexpr (!WALK) {
+    if (!owner) {
+      // (no state tile: waves 4-7 at C = 256)
+    } else if constexpr (!WALK) {
       f32x16 Z = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < C / 16; ++kk) {
@@ -263,7 +271,7 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
     if constexpr (WALK) {
 #pragma unroll
       for (int i = 0; i < QB; ++i) {
-        const int qb = (i & 1) ? (4 * i + 3 - w) : (4 * i + w);
+        const int qb = (i & 1) ? (NW * i + NW - 1 - w) : (NW * i + w);
         if (qb >= NB) continue;  // wave-uniform (C = 64 only)
         float den = den0[i];
         f32x16 num[D / 32];
@@ -339,12 +347,13 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
 // Prefixes are written and read with agent-coherent accesses; a wait that
 // exceeds spin_limit polls sets *err and makes the outputs NaN.
 template <int C, int MAP>
-__global__ __launch_bounds__(256, (Causal2Shape<C, true>::WG_PER_CU)) void causal1_kernel(Causal2Args a) {
+__global__ __launch_bounds__((Causal2Shape<C, true>::NT), (Causal2Shape<C, true>::WG_PER_CU)) void causal1_kernel(Causal2Args a) {
   constexpr int D = 64, E = D * D + D;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Causal2Shape<C, true>::bytes];
   __shared__ unsigned tk_s, ok_s;
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3, dt = w >> 1, ft = w & 1;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), dt = (w >> 1) & 1, ft = w & 1;
+  const bool owner = w < 4;  // the waves that hold a tile of the state
   if (tid == 0) tk_s = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int t = (int)tk_s;
@@ -373,6 +382,7 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, true>::WG_PER_CU)) void causa
     __syncthreads();
     const float* ip = a.seg + ((size_t)bh * a.nseg + (s - 1)) * E;
     const bool ok = ok_s != 0;
+    if (owner) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       P[r] = ok ? __hip_atomic_load(ip + (dt * 32 + crow(lane, r)) * D + ft * 32 + c, __ATOMIC_RELAXED,
@@ -380,15 +390,18 @@ __global__ __launch_bounds__(256, (Causal2Shape<C, true>::WG_PER_CU)) void causa
                 : __uint_as_float(0x7fc00000u);
     zr = ok ? __hip_atomic_load(ip + D * D + ft * 32 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
             : __uint_as_float(0x7fc00000u);
+    }
   }
   if (!last) {
     float* op = a.seg + ((size_t)bh * a.nseg + s) * E;
+    if (owner) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       __hip_atomic_store(op + (dt * 32 + crow(lane, r)) * D + ft * 32 + c, P[r] + PA[r], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     if (dt == 0 && lane < 32)
       __hip_atomic_store(op + D * D + ft * 32 + c, zr + zA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     wait_vmcnt<0>();  // the prefix is at the agent's coherence point before its flag
     __syncthreads();
     if (tid == 0) __hip_atomic_store(a.flags + (size_t)bh * a.nseg + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -406,7 +419,7 @@ static hipError_t launch_causal2_t(const Causal2Args& a, int B, hipStream_t s, S
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   t->mark();
-  hipLaunchKernelGGL((causal1_kernel<C, MAP>), dim3(a.nseg * a.nbh), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((causal1_kernel<C, MAP>), dim3(a.nseg * a.nbh), dim3(Causal2Shape<C, true>::NT), 0, s, a);
   e = hipGetLastError();
   t->mark();
   return e;
