@@ -329,6 +329,11 @@ ttr_status ttr_replay_fetch(ttr_replay* rb, int64_t id, void* Qs, void* K, void*
   if (e == hipSuccess) e = hipMemcpyAsync(Qs, rb->host + s->off_q(), s->parts.q, hipMemcpyHostToDevice, st);
   if (e == hipSuccess && teacher_rows != nullptr)
     e = hipMemcpyAsync(teacher_rows, rb->host + s->off_t(), s->parts.t, hipMemcpyHostToDevice, st);
+  // The sample keeps one read event. A fetch on another stream than the last
+  // one's would otherwise replace it: the stream first waits for the earlier
+  // record (after its own copies are enqueued, so they are not delayed), and
+  // the new record then stands for every fetch so far.
+  if (e == hipSuccess && s->read_recorded) e = hipStreamWaitEvent(st, s->read, 0);
   // recorded even after a failed copy so that reuse of the ring space waits for what was enqueued
   const hipError_t er = hipEventRecord(s->read, st);
   if (er == hipSuccess) s->read_recorded = true;

@@ -151,3 +151,28 @@ def test_replay_refusals_and_evicted_ids():
                                   torch.cuda.current_stream().cuda_stream)
         assert st == 2
         rb.synchronize()
+
+
+def test_replay_fetch_on_two_streams_then_evict():
+    # a sample fetched on two streams, then evicted at once by the next pushes:
+    # the ring bytes are reused only after both fetches' copies have read them
+    host, dev = _sample(21, 1, 8, 4096, 128, "bf16", 512, True)
+    foot = O.replay_sample_bytes(1, 8, 4096, 128, 2, 512, True)
+    ref = O.ReplayBuffer(2 * foot)
+    with ttr.ReplayBuffer(2 * foot, foot) as rb:
+        sid = _push_both(rb, ref, host, dev)
+        smp = ref.fetch(sid)
+        sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+        with torch.cuda.stream(sa):
+            got_a = rb.fetch(sid)
+        with torch.cuda.stream(sb):
+            got_b = rb.fetch(sid)
+        other, odev = _sample(22, 1, 8, 4096, 128, "bf16", 512, True)
+        for _ in range(2):                        # the second push evicts the fetched sample
+            _push_both(rb, ref, other, odev)
+        assert sid not in rb.ids()
+        torch.cuda.synchronize()
+        for Qs, K, V, T, idx in (got_a, got_b):
+            assert _same(_bits(K), smp["K"]) and _same(_bits(V), smp["V"])
+            assert _same(_bits(Qs), smp["Q"]) and _same(_bits(T), smp["T"])
+            assert np.array_equal(idx, smp["idx"])
