@@ -155,7 +155,7 @@ ttr_status ttr_hybrid_forward(ttr_dims d, const void* Q, const void* K, const vo
  * Every call on one GPU uses that GPU's one array (the kernels clear what must
  * start at zero): calls that overlap on one GPU (other streams, other host
  * threads) race and give undefined results; calls in one stream are safe. */
-#define TTR_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define TTR_NOALLOC_SCRATCH_BYTES (64u << 20)
 ttr_status ttr_hybrid_forward_noalloc(ttr_dims d, const void* Q, const void* K, const void* V,
                                       const void* W, const float* b, const float* g, float eps,
                                       int32_t L, int32_t causal, void* out, void* stream);

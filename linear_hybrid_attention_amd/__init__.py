@@ -367,7 +367,7 @@ def hybrid_forward_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W:
     return out
 
 
-NOALLOC_SCRATCH_BYTES = 32 << 20  # TTR_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TTR_NOALLOC_SCRATCH_BYTES
 
 
 def nnt_layer_workspace_bytes(B: int, N: int, E: int, H: int, dtype: int, causal: bool = False,

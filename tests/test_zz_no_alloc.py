@@ -51,9 +51,18 @@ def test_noalloc_causal():
     assert np.array_equal(got, ref)
 
 
+def test_noalloc_full_size_causal():
+    # the causal configuration at its stated chunk: the largest workspace of the workloads
+    w = workloads.WORKLOADS["causal"]
+    need = ttr.workspace_bytes(w.B, w.H, w.N, w.D, w.F, 1, 0, True, w.chunk)
+    assert need <= ttr.NOALLOC_SCRATCH_BYTES
+    got, ref = _pair(w, causal=True, chunk=w.chunk)
+    assert np.array_equal(got, ref)
+
+
 def test_noalloc_rejects_beyond_the_array():
     # host-side check: the call needs more than the array holds, nothing runs
-    w = small("flux_1024", B=4, H=64, N=4096, L=0, seed=34)
+    w = small("flux_1024", B=8, H=64, N=4096, L=0, seed=34)
     need = ttr.workspace_bytes(w.B, w.H, w.N, w.D, w.F, 1, w.L, False, 0)
     assert need > ttr.NOALLOC_SCRATCH_BYTES
     dev = torch.device("cuda:0")
