@@ -2,9 +2,9 @@
  * ttr.h -- C ABI of the MI355X (gfx950) TTR hybrid-attention library (libttr.so).
  *
  * The method (web pages it is described on, by title and section):
- *   "Flux2TTRTrainer", "How the distillation works": a TTR layer fuses a
- *     linear-time kernel branch with a small exact-softmax branch over
- *     landmark tokens, blended by a bounded weight; "Inputs worth setting":
+ *   "Flux2TTRTrainer", "How the distillation works": a TTR layer combines a
+ *     kernel branch whose cost grows linearly with the tokens and an exact
+ *     softmax over a few landmark tokens, mixed by a weight kept in (0, 1); "Inputs worth setting":
  *     feature_dim F defaults to 256 and must be a multiple of 256.
  *   "NNT Define Linear Attention", "The inputs": feature map elu(x) + 1
  *     (also relu or softmax), eps = 1e-6 in the denominator, causal flag;
@@ -182,8 +182,8 @@ size_t ttr_backward_workspace_bytes(ttr_dims d, int32_t L);
 
 /* One Phase-1 distillation step of a TTR layer on one batch of Q, K, V
  * ("Flux2TTRTrainer", "How the distillation works": the student TTR layer
- * regresses native softmax attention; the loss is a Kendall-style
- * uncertainty-weighted blend of huber and cosine; optimizer state persists):
+ * regresses native softmax attention; huber and cosine terms weighed by
+ * learned uncertainties after Kendall; optimizer state persists):
  *   teacher = softmax(Q K^T / sqrt(D)) V per (b, h) (computed when teacher is NULL)
  *   out     = the hybrid forward with W, b, g (W rounded to the IO dtype for it)
  *   loss    = exp(-s1) huber + s1 + exp(-s2) (1 - cos) + s2
@@ -226,7 +226,7 @@ size_t ttr_distill_rows_workspace_bytes(ttr_dims d, int32_t Nq, int32_t L, int32
  * over the B*H*N rows of 1 - o.t / max(|o| |t|, 1e-8) (rows of D values),
  * written to out (one fp32 device value). student, teacher [B,H,N,D] in the
  * IO dtype. The quantity the readiness gate tracks ("Flux2TTRTrainer", "How
- * the distillation works": EMA cosine distance to the teacher).
+ * the distillation works": a moving average of the cosine distance to the teacher).
  * ws: at least ttr_cosine_workspace_bytes(d) bytes. */
 ttr_status ttr_cosine_distance(ttr_dims d, const void* student, const void* teacher, float* out, void* ws,
                                size_t ws_bytes, void* stream);

@@ -1,7 +1,7 @@
 // Backward of the hybrid forward for the trainable parameters W_h, b_h, g_h,
 // and the Phase-1 distillation step around it ("Flux2TTRTrainer", section "How
 // the distillation works": the TTR student regresses native softmax attention;
-// the loss is an uncertainty-weighted blend of huber and cosine; per-layer
+// huber and cosine terms weighed by learned uncertainties; per-layer
 // optimizer state). The chain rule (dout -> dW, db, dg):
 //   dlin   = alpha dout,   dalpha = sum dout (lin - lm),   dg = dalpha alpha (1 - alpha)
 //   dnum   = dlin / den,   dden = -sum_d dlin lin / den

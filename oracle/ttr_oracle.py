@@ -8,9 +8,9 @@ nothing from it.
 Sources (page titles and sections of the method's web pages):
 
 * "Flux2TTRTrainer", section "How the distillation works": the TTR layer
-  fuses a linear-time kernel branch with a small exact-softmax branch over
-  landmark tokens, blended by a bounded weight. Section "Why this exists":
-  the branch is a kernel-regression replacement for attention. Section
+  combines a kernel branch whose cost grows linearly with the tokens and an
+  exact softmax over a few landmark tokens, mixed by a weight kept in (0, 1). Section "Why this exists":
+  the branch stands in for a layer's attention as a kernel regression. Section
   "Inputs worth setting": feature_dim defaults to 256 and is a multiple of 256.
 * "NNT Define Linear Attention", section "The inputs": the elu feature map is
   elu(x) + 1; eps (default 1e-6) sits in the denominator; causal masks so a
@@ -46,8 +46,8 @@ identity (an inference forward).
 
 The distillation step ("Flux2TTRTrainer", section "How the distillation
 works": the teacher is native softmax attention, the student is the TTR
-layer, the loss is a Kendall-style uncertainty-weighted blend of huber and
-cosine, optimizer state persists per layer) is read as: teacher =
+layer, the huber and cosine terms of the loss are weighed by learned
+uncertainties after Kendall, optimizer state persists per layer) is read as: teacher =
 softmax(Q K^T / sqrt(D)) V on the same inputs; loss = exp(-s1) huber + s1 +
 exp(-s2) (1 - cos) + s2 with learnable log-variances s = (s1, s2) (Kendall,
 Gal and Cipolla's homoscedastic weighting), huber with delta = 1 averaged over
@@ -67,8 +67,8 @@ teacher is the teacher's output at those rows.
 
 Readiness gating and the landmark count ("Flux2TTRTrainer", section "How the
 distillation works": a layer serves the student only after enough updates and
-once its EMA cosine distance to the teacher is low, with hysteresis, failing
-closed to the teacher; section "Inputs worth setting": landmark
+once the moving average of its cosine distance to the teacher has dropped far
+enough, with separate on and off thresholds, and serves the teacher otherwise; section "Inputs worth setting": landmark
 fraction/min/max and a readiness threshold) are read as: distance = mean over
 (batch, head, token) rows of 1 - cos(student_row, teacher_row); ema = d on
 the first update, then rate * ema + (1 - rate) * d; a gate that is not ready
