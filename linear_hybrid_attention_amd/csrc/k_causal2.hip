@@ -25,6 +25,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"
+#include "validate.hpp"
 
 namespace ttr {
 
@@ -483,7 +484,7 @@ hipError_t launch_causal2(const Problem& p, const void* Q, const void* K, const 
   a.flags = reinterpret_cast<unsigned*>(w8 + causal1_prefix_bytes(p, a.nseg));
   a.ticket = a.flags + (size_t)a.nbh * a.nseg;
   a.err = a.ticket + 1;
-  a.spin_limit = 1u << 20;  // a tenth of a second or so of polling
+  a.spin_limit = env_spin_limit(1u << 20);  // a tenth of a second or so of polling
   a.sink = reinterpret_cast<uint16_t*>(w8 + causal1_prefix_bytes(p, a.nseg) + causal1_flag_bytes(p, a.nseg));
   static_assert(CAUSAL2_SINK_BYTES >= 2 * 4 * 64 * 16, "one 16-byte slot per store of a wave (QB <= 2)");
   a.out = static_cast<uint16_t*>(out);

@@ -53,6 +53,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"
+#include "validate.hpp"
 
 namespace ttr {
 
@@ -122,6 +123,7 @@ struct KvsArgs {
   unsigned* counters;    // [groups][4]: arrivals per XCD (8 byte fields), second-round arrivals, unused;
                          // zero on entry (kv_stage_reset_kernel)
   unsigned spin_limit;   // polls of a waiting workgroup before it gives up
+  unsigned force_round2;  // take the cross-XCD round whatever the placement (a test hook)
   unsigned char* pack_bh;  // pack mode: [BH][bh_bytes]
   unsigned long long bh_bytes;
   unsigned char* pack_w;   // pack mode: [H][F D bf16] W^T chunks (written by batch 0)
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
     while (arrivals(__hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), xcds) < (unsigned)a.nsplit &&
            ++n < a.spin_limit)
       __builtin_amdgcn_s_sleep(2);
-    if (n < a.spin_limit && xcds > 1) {
+    if (n < a.spin_limit && (xcds > 1 || a.force_round2 != 0)) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __hip_atomic_fetch_add(c2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       while (__hip_atomic_load(c2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.nsplit &&
@@ -903,7 +905,8 @@ static KvsArgs kvs_args(const Problem& p, const KvsPlan& k, const void* K, const
   a.per_xcd = k.per_xcd;
   a.part = reinterpret_cast<float*>(ws);
   a.counters = reinterpret_cast<unsigned*>(ws + k.part_bytes);
-  a.spin_limit = 1u << 20;  // about a second of polling
+  a.spin_limit = env_spin_limit(1u << 20);  // about a second of polling
+  a.force_round2 = env_flag("TTR_KVS_CROSS_XCD_ROUND") ? 1u : 0u;
   return a;
 }
 

@@ -5,7 +5,21 @@
 // "NNT Define Linear Attention", section "The inputs" (causal flag, eps).
 #include "validate.hpp"
 
+#include <cstdlib>
+
 namespace ttr {
+
+unsigned env_spin_limit(unsigned deflt) {
+  const char* v = std::getenv("TTR_SPIN_LIMIT");
+  if (v == nullptr || *v == 0) return deflt;
+  const unsigned long n = std::strtoul(v, nullptr, 10);
+  return n >= 1 && n <= 0xFFFFFFFFul ? (unsigned)n : deflt;
+}
+
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v != nullptr && v[0] == '1' && v[1] == 0;
+}
 
 size_t dtype_bytes(int32_t dtype) {
   switch (dtype) {

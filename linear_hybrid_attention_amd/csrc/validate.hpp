@@ -14,6 +14,15 @@ size_t dtype_bytes(int32_t dtype);
 
 // Rules on B, H, N, D, F, dtype shared by every entry point.
 // has_w: a projection W is given (F must be 256) or not (F must equal D).
+// Test hooks read at every launch (no effect unless set): TTR_SPIN_LIMIT
+// replaces the poll limit of the kernels' bounded waits (a tiny value makes
+// them give up, so a test can check that they fail visibly and finish);
+// TTR_KVS_CROSS_XCD_ROUND=1 makes the key/value stage take its cross-XCD round
+// (write-back, second count, invalidate) even when a group's splits share an
+// XCD, so the round is exercised on hardware that never needs it.
+unsigned env_spin_limit(unsigned deflt);
+bool env_flag(const char* name);
+
 // max_f: the largest projected feature dimension the calling entry point
 // implements (a multiple of 256 above it is TTR_ERR_UNSUPPORTED).
 ttr_status check_dims(const ttr_dims& d, bool has_w, int32_t max_f = 256);
