@@ -42,6 +42,14 @@
  *     nothing. A failed launch returns TTR_ERR_HIP; ttr_last_hip_error()
  *     gives the hipError_t (per calling thread).
  *   - Results are bitwise deterministic run to run (no floating-point atomics).
+ *   - Kernels that wait for one another's results (the key/value stage's
+ *     splits, the causal scan's segments) poll a bounded number of times
+ *     (about 2^20). A wait that gives up makes the outputs it feeds NaN, and
+ *     the causal scan also sets the error word of its workspace. Two
+ *     environment variables, read at every launch, exist for tests:
+ *     TTR_SPIN_LIMIT=n sets the poll limit (n >= 1), and
+ *     TTR_KVS_CROSS_XCD_ROUND=1 makes the key/value stage take the coherent
+ *     round it otherwise takes only when a group's workgroups span XCDs.
  *   - Shape rules: B, H, N >= 1; D in {64, 128}; with W, F a multiple of 256
  *     (else TTR_ERR_SHAPE), of which F == 256 is implemented by every entry
  *     point and F == 512 by the bf16 ttr_hybrid_forward (and its _noalloc
