@@ -336,9 +336,10 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   // half in kperm column order, so that a consumer's plain 16-byte row read
   // hands it the tokens in the C-row order of the transposed V fragments
   auto ptile = [&](int slot, int p) -> uint16_t* { return pbuf + (slot * 4 + p) * 64 * 32; };
-  // Both roles run nsteps + 1 iterations with one barrier each (but the
-  // first), then the same barriers of the token-group sums: their s_barrier
-  // counts match. Each role's state lives in its own branch.
+  // Both roles take nsteps + 1 loop barriers (the producers map steps
+  // 0 .. nsteps - 1, the consumers take them one iteration later), then the
+  // same barriers after the loop: their s_barrier counts match. Each role's
+  // state lives in its own branch.
   if (producer) {
     // ---- producer: W slice as the B operand (lane = feature fs0 + 32 fb + c,
     // k-slots = rows 16 kb + 8 g ..)
@@ -478,16 +479,19 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       }
       produce(sl, kf);
     };
+    // steps 0 .. nsteps - 1, then one more barrier while the consumers take
+    // the last step (no map of a step nobody reads: the matrix core is theirs)
     int t3 = 0;
-    for (; t3 + 2 <= nsteps; t3 += 3) {
+    for (; t3 + 3 <= nsteps; t3 += 3) {
       iteration(t3, C0{});
       iteration(t3 + 1, C1{});
       iteration(t3 + 2, C2{});
     }
-    if (t3 <= nsteps) iteration(t3, C0{});
-    if (t3 + 1 <= nsteps) iteration(t3 + 1, C1{});
+    if (t3 < nsteps) iteration(t3, C0{});
+    if (t3 + 1 < nsteps) iteration(t3 + 1, C1{});
     wait_vmcnt<0>();  // the last (zero) copies have landed before LDS is reused
-    // Rows past the range: the maps of steps nfull .. nsteps saw K = 0 there,
+    barrier_lds();
+    // Rows past the range: the maps of steps nfull .. nsteps - 1 saw K = 0 there,
     // i.e. phi(0 W + b), the same bits each time; take them out of ksum.
     {
       const int nfull = (t_end - t_begin) / STEP;
@@ -500,7 +504,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
         st0 = float2{m, inv};
       }
       int nzero = 0;  // rows past the range among this lane's 16 rows of each map
-      for (int jj = nfull; jj <= nsteps; ++jj) {
+      for (int jj = nfull; jj < nsteps; ++jj) {
         const int lim = t_end - (t_begin + jj * STEP + 32 * tg);
 #pragma unroll
         for (int r = 0; r < 16; ++r) nzero += crow(lane, r) >= lim;
