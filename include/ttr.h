@@ -399,7 +399,9 @@ int ttr_last_hip_error(void);
  * ttr_cosine_distance or ttr_replay_push records
  * events[0] on its stream before its first kernel and events[1], events[2],
  * ... after each kernel (or stage) it launches, as long as events remain:
- *   bf16 hybrid: key/value partial sums, operand pack, fused query kernel;
+ *   bf16 hybrid: the reset of the key/value stage's counters, the key/value
+ *     stage (partials, split reduction and operand pack in one launch), the
+ *     fused query kernel;
  *   fp32 hybrid: key/value reduction, query kernel;
  *   causal, bf16 with D = 64: the reset of its segment flags, the single-pass scan;
  *   other causal: segment totals (when the sequence has several segments), chunk walk;
