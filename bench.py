@@ -193,8 +193,7 @@ def kernel_plan(w):
     apply = 2 * N * F * D + 2 * N * F  # phi(Q) KV and phi(Q) . ksum
     lm = 4 * N * L * D  # Q K_L^T and P V_L
     if w.dtype == "bf16":
-        return [("kv_stage_reset_kernel", 0, 0),
-                ("kv_stage_kernel", BH * (proj + kv), 2 * tok),
+        return [("kv_stage_kernel", BH * (proj + kv), 2 * tok),
                 ("fused_query_kernel", BH * (proj + apply + lm), 2 * tok)]
     return [("kv_partial_kernel (+ kv_finalize_kernel)", BH * (proj + kv), 2 * tok),
             ("hybrid_kernel", BH * (proj + apply + lm), 2 * tok)]
@@ -470,7 +469,7 @@ def distill_plan(w, nq=None):
         plan.append((teacher, 4 * Z * N * N * D, 3 * Z * N * D * io + Z * N * D * 4))
     plan += [("bgemm z_q = Q W + b", gq, 0), ("bgemm z_k = K W + b", gk, 0)]
     if w.dtype == "bf16":  # KV and ksum from K and V by the key/value kernel
-        plan.append(("KV, ksum = phi(K W + b)^T V, colsum (kv_stage_reset_kernel + kv_stage_kernel)", gk, 0))
+        plan.append(("KV, ksum = phi(K W + b)^T V, colsum (kv_stage_kernel)", gk, 0))
     else:
         plan += [("ksum (tile sums of the z_k epilogue)", 0, 0), ("bgemm KV = phi_k^T V", gk, 0)]
     plan += [("bgemm lin = phi_q KV / den, den = phi_q . ks + eps (normaliser formed from the staged rows)", gq, 0)]

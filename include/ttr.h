@@ -50,6 +50,11 @@
  *     TTR_SPIN_LIMIT=n sets the poll limit (n >= 1), and
  *     TTR_KVS_CROSS_XCD_ROUND=1 makes the key/value stage take the coherent
  *     round it otherwise takes only when a group's workgroups span XCDs.
+ *   - The key/value stage's meeting counters live in the workspace and need
+ *     no reset launch: each launch carries a number (a process-wide count)
+ *     that tags them, so their contents on entry do not matter, and the last
+ *     workgroup of a group to leave clears them, so a launch captured in a
+ *     graph can be replayed. Concurrent calls must not share a workspace.
  *   - Shape rules: B, H, N >= 1; D in {64, 128}; with W, F a multiple of 256
  *     (else TTR_ERR_SHAPE), of which F == 256 is implemented by every entry
  *     point and F == 512 by the bf16 ttr_hybrid_forward (and its _noalloc
@@ -399,9 +404,8 @@ int ttr_last_hip_error(void);
  * ttr_cosine_distance or ttr_replay_push records
  * events[0] on its stream before its first kernel and events[1], events[2],
  * ... after each kernel (or stage) it launches, as long as events remain:
- *   bf16 hybrid: the reset of the key/value stage's counters, the key/value
- *     stage (partials, split reduction and operand pack in one launch), the
- *     fused query kernel;
+ *   bf16 hybrid: the key/value stage (partials, split reduction and operand
+ *     pack in one launch), the fused query kernel;
  *   fp32 hybrid: key/value reduction, query kernel;
  *   causal, bf16 with D = 64: the reset of its segment flags, the single-pass scan;
  *   other causal: segment totals (when the sequence has several segments), chunk walk;

@@ -120,8 +120,8 @@ struct KvsArgs {
   int nsplit, chunk;     // token splits of a group and the tokens of each (a multiple of the step)
   int groups, per_xcd;   // (batch, head, feature group) groups; grid slots per XCD (grid = 8 per_xcd)
   float* part;           // [groups][nsplit][FG * D + FG] fp32 partials
-  unsigned* counters;    // [groups][4]: arrivals per XCD (8 byte fields), second-round arrivals, unused;
-                         // zero on entry (kv_stage_reset_kernel)
+  unsigned long long* counters;  // [groups][4] meeting words: arrivals, second round, departures, unused
+  unsigned long long call;        // this launch's number (45 bits, never 0), which tags the meeting words
   unsigned spin_limit;   // polls of a waiting workgroup before it gives up
   unsigned force_round2;  // take the cross-XCD round whatever the placement (a test hook)
   unsigned char* pack_bh;  // pack mode: [BH][bh_bytes]
@@ -168,11 +168,6 @@ struct KvsShape {
 // (a quiet NaN by its bits: the file is built without NaN semantics)
 #define kQNaN __uint_as_float(0x7fc00000u)
 
-__global__ void kv_stage_reset_kernel(unsigned* counters, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x)
-    __hip_atomic_store(counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Partial loads and stores: plain, through the XCD's L2 (see the meeting of
 // the splits for when that is coherent).
 __device__ __forceinline__ u32x4 ld16_part(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -186,17 +181,36 @@ __device__ __forceinline__ void st16_part(__amdgpu_buffer_rsrc_t r, uint32_t off
 // gfx950 parts have at most eight XCDs).
 __device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 7u; }
 
-// Arrivals of a group: byte x of the word counts the splits on XCD x.
-__device__ __forceinline__ unsigned arrivals(unsigned long long v, unsigned& xcds) {
-  unsigned n = 0;
-  xcds = 0;
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const unsigned b = (unsigned)(v >> (8 * x)) & 255u;
-    n += b;
-    xcds += b != 0;
-  }
-  return n;
+// Meeting words of a group (arrivals, second round, departures): bits 0-7
+// count the splits, bits 8-15 (arrivals) count those that run on another XCD
+// than split 0, bits 16-18 (arrivals) hold split 0's XCD, bits 19-63 the
+// number of the launch the word belongs to. Split 0 writes the three words
+// afresh when it starts; the others add themselves to a word only once they
+// have seen it carry this launch's number (a load and an atomic add on one
+// location, so the add lands after split 0's write), so the words' contents
+// on entry do not matter and no reset launch is needed. The last split to
+// leave clears them, so a replay of a captured launch (the same number
+// again) waits for split 0 as well.
+constexpr int kMeetTag = 19;
+__device__ __forceinline__ unsigned long long meet_load(const unsigned long long* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Polls w until it carries this launch's number (true) or the limit runs out;
+// n counts the polls, v receives the word.
+__device__ __forceinline__ bool meet_tagged(const unsigned long long* w, unsigned long long call, unsigned limit,
+                                            unsigned& n, unsigned long long& v) {
+  while (((v = meet_load(w)) >> kMeetTag) != call)
+    if (++n >= limit) return false;
+    else __builtin_amdgcn_s_sleep(2);
+  return true;
+}
+// Polls w until its count reaches ns (true) or the limit runs out.
+__device__ __forceinline__ bool meet_all(const unsigned long long* w, unsigned ns, unsigned limit, unsigned& n,
+                                         unsigned long long& v) {
+  while (((v = meet_load(w)) & 255u) < ns)
+    if (++n >= limit) return false;
+    else __builtin_amdgcn_s_sleep(2);
+  return true;
 }
 
 // Eight waves, two per SIMD: waves 0-3 are producers, 4-7 consumers (wave w
@@ -248,6 +262,13 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   const int item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
   if (item >= a.groups * a.nsplit) return;
   const int split = item % a.nsplit, group = item / a.nsplit;
+  unsigned long long* const mw = a.counters + 4 * group;  // the group's meeting words
+  if (split == 0 && tid == 0) {
+    const unsigned long long t = a.call << kMeetTag;
+    __hip_atomic_store(mw, t | ((unsigned long long)xcd_id() << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mw + 1, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mw + 2, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   const int bh = group / NG, fgi = group % NG, h = bh % a.H;
   const int fg0 = fgi * FG;         // first feature of the group
   const int fs0 = fg0 + 64 * fs;    // first of this wave's 64 features
@@ -340,6 +361,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   // 0 .. nsteps - 1, the consumers take them one iteration later), then the
   // same barriers after the loop: their s_barrier counts match. Each role's
   // state lives in its own branch.
+  unsigned long long pre = 0;  // (tid 0) the arrivals word, read early: split 0 wrote it at its start
   if (producer) {
     // ---- producer: W slice as the B operand (lane = feature fs0 + 32 fb + c,
     // k-slots = rows 16 kb + 8 g ..)
@@ -491,6 +513,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
     if (t3 + 1 < nsteps) iteration(t3 + 1, C1{});
     wait_vmcnt<0>();  // the last (zero) copies have landed before LDS is reused
     barrier_lds();
+    if (tid == 0) pre = meet_load(mw);  // (its latency hides behind the partial stores)
     // Rows past the range: the maps of steps nfull .. nsteps - 1 saw K = 0 there,
     // i.e. phi(0 W + b), the same bits each time; take them out of ksum.
     {
@@ -648,22 +671,37 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   __syncthreads();
   __shared__ unsigned ok_s;
   if (tid == 0) {
-    unsigned long long* cw = reinterpret_cast<unsigned long long*>(a.counters + 4 * group);
-    unsigned* c2 = a.counters + 4 * group + 2;
-    __hip_atomic_fetch_add(cw, 1ull << (8 * xcd_id()), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned n = 0, xcds = 0;
-    while (arrivals(__hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), xcds) < (unsigned)a.nsplit &&
-           ++n < a.spin_limit)
-      __builtin_amdgcn_s_sleep(2);
-    if (n < a.spin_limit && (xcds > 1 || a.force_round2 != 0)) {
+    const unsigned ns = (unsigned)a.nsplit;
+    unsigned n = 0;
+    unsigned long long v = 0;
+    bool ok = (pre >> kMeetTag) == a.call ? (v = pre, true) : meet_tagged(mw, a.call, a.spin_limit, n, v);
+    if (ok) {
+      const bool away = (unsigned)((v >> 16) & 7u) != xcd_id();
+      __hip_atomic_fetch_add(mw, away ? 257ull : 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = meet_all(mw, ns, a.spin_limit, n, v);
+    }
+    // (every split that got here saw the same, final, arrivals word)
+    if (ok && (((v >> 8) & 255u) != 0 || a.force_round2 != 0)) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(c2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      while (__hip_atomic_load(c2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.nsplit &&
-             ++n < a.spin_limit)
-        __builtin_amdgcn_s_sleep(2);
+      unsigned long long v2;
+      ok = meet_tagged(mw + 1, a.call, a.spin_limit, n, v2);
+      if (ok) {
+        __hip_atomic_fetch_add(mw + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = meet_all(mw + 1, ns, a.spin_limit, n, v2);
+      }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    ok_s = n < a.spin_limit;
+    ok_s = ok;
+    // leave: after the last split's departure nobody reads the group's words
+    // again in this launch, and that split clears them
+    unsigned m = 0;
+    unsigned long long d;
+    if (meet_tagged(mw + 2, a.call, a.spin_limit, m, d) &&
+        (__hip_atomic_fetch_add(mw + 2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 255u) + 1 == ns) {
+      __hip_atomic_store(mw, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mw + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mw + 2, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
   // A workgroup that gave up writes NaN into its share of the outputs (the
@@ -826,14 +864,14 @@ static KvsPlan kvs_plan(const Problem& p, int cus) {
   int ns = (cus / 8) / gx;
   const int maxs = (p.N + 2 * step - 1) / (2 * step);  // at least two steps per split
   if (ns > maxs) ns = maxs;
-  if (ns > 255) ns = 255;  // the arrivals of one XCD fit a byte
+  if (ns > 255) ns = 255;  // the count of a meeting word is a byte
   if (ns < 1) ns = 1;
   const int per = (p.N + ns - 1) / ns;
   k.chunk = (per + step - 1) / step * step;
   k.nsplit = (p.N + k.chunk - 1) / k.chunk;  // every split non-empty
   k.per_xcd = gx * k.nsplit;
   k.part_bytes = (size_t)k.groups * k.nsplit * (size_t)(k.FG * p.D + k.FG) * 4;
-  k.cnt_bytes = ((size_t)k.groups * 16 + 255) / 256 * 256;
+  k.cnt_bytes = ((size_t)k.groups * 32 + 255) / 256 * 256;
   return k;
 }
 
@@ -859,14 +897,23 @@ size_t kv2_reduce_workspace_bytes(const Problem& p) {
   return k.part_bytes + k.cnt_bytes;
 }
 
+// Launch numbers tag the meeting words (45 bits; 0, the number of a cleared
+// word, is skipped).
+static unsigned long long next_launch_number() {
+  static std::atomic<unsigned long long> counter{0};
+  unsigned long long v;
+  do v = (counter.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << (64 - kMeetTag)) - 1);
+  while (v == 0);
+  return v;
+}
+
 template <int D, int F, bool PROJ, int MAP, bool PACK>
-static hipError_t launch_kvs_t(const KvsArgs& a, int groups, hipStream_t s, StageTimer* t) {
-  hipLaunchKernelGGL(kv_stage_reset_kernel, dim3(1), dim3(256), 0, s, a.counters, 4 * groups);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (t) t->mark();
+static hipError_t launch_kvs_t(const KvsArgs& a0, int groups, hipStream_t s, StageTimer* t) {
+  (void)groups;
+  KvsArgs a = a0;
+  a.call = next_launch_number();
   hipLaunchKernelGGL((kv_stage_kernel<D, F, PROJ, MAP, PACK>), dim3(8 * a.per_xcd), dim3(512), 0, s, a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (t) t->mark();
   return e;
 }
@@ -908,7 +955,7 @@ static KvsArgs kvs_args(const Problem& p, const KvsPlan& k, const void* K, const
   a.groups = k.groups;
   a.per_xcd = k.per_xcd;
   a.part = reinterpret_cast<float*>(ws);
-  a.counters = reinterpret_cast<unsigned*>(ws + k.part_bytes);
+  a.counters = reinterpret_cast<unsigned long long*>(ws + k.part_bytes);
   a.spin_limit = env_spin_limit(1u << 20);  // about a second of polling
   a.force_round2 = env_flag("TTR_KVS_CROSS_XCD_ROUND") ? 1u : 0u;
   return a;
@@ -928,7 +975,7 @@ hipError_t launch_kv2(const Problem& p, const void* K, const void* V, const void
   pk->bh_bytes = pl.bh_bytes();
   pk->w_bytes = pl.w_bytes();
   KvsArgs a = kvs_args(p, k, K, V, W, bias, L, w8);
-  a.counters = reinterpret_cast<unsigned*>(w8 + kw.part_bytes);
+  a.counters = reinterpret_cast<unsigned long long*>(w8 + kw.part_bytes);
   a.pack_bh = pbh;
   a.bh_bytes = pl.bh_bytes();
   a.pack_w = pw;
@@ -942,7 +989,7 @@ hipError_t launch_kv2_reduce(const Problem& p, const void* K, const void* V, con
   const KvsPlan kw = kvs_plan(p, 256);
   unsigned char* w8 = static_cast<unsigned char*>(ws);
   KvsArgs a = kvs_args(p, k, K, V, W, bias, 0, w8);
-  a.counters = reinterpret_cast<unsigned*>(w8 + kw.part_bytes);
+  a.counters = reinterpret_cast<unsigned long long*>(w8 + kw.part_bytes);
   a.kv_out = KV;
   a.ks_out = ksum;
   return launch_kvs<false>(p, a, k.groups, s, nullptr);

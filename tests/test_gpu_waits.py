@@ -8,8 +8,13 @@ library's test hooks (environment variables read at every launch):
 * TTR_SPIN_LIMIT=1: every bounded wait gives up after one poll. The kernels
   must still finish, and a result is either the usual one bit for bit or
   visibly poisoned (NaN), never silently different; the causal scan also sets
-  its error word. Without the hook the next call is clean again (the reset
-  launch of every call clears counters, flags and the error word).
+  its error word. Without the hook the next call is clean again (the causal
+  scan's reset launch clears its flags and error word; the key/value stage's
+  meeting words carry the launch's number and are cleared by the group's last
+  workgroup).
+* The key/value stage needs no reset: a workspace full of arbitrary bytes
+  gives the usual result bit for bit, and so do replays of a captured forward
+  (each replay carries the same launch number).
 
 Every kernel exits normally in all of these runs: only the waits are cut short."""
 import numpy as np
@@ -54,6 +59,54 @@ def test_kv_stage_wait_timeout_is_visible(monkeypatch):
         assert np.array_equal(got, ref) or np.isnan(got).any()
     monkeypatch.delenv("TTR_SPIN_LIMIT")
     assert np.array_equal(_forward(w, d), ref)
+
+
+@pytest.mark.parametrize("fill", ["ones", "random"])
+def test_kv_stage_any_workspace_contents(fill):
+    w = small("flux_1024", H=5, N=3000, L=64, seed=54)
+    d = to_device(w, workloads.make_inputs(w))
+    eps = float(np.float32(w.eps))
+    need = ttr.workspace_bytes(w.B, w.H, w.N, w.D, w.F, 1, w.L, False, 0)
+    ref = host(ttr.hybrid_forward(d["Q"], d["K"], d["V"], d["W"], d["b"], d["g"], eps, w.L))
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for i in range(3):
+        if fill == "ones":
+            ws = torch.full((need,), 255, dtype=torch.uint8, device=d["Q"].device)
+        else:
+            ws = torch.randint(0, 256, (need,), generator=gen, dtype=torch.uint8).to(d["Q"].device)
+        got = host(ttr.hybrid_forward(d["Q"], d["K"], d["V"], d["W"], d["b"], d["g"], eps, w.L, ws=ws))
+        torch.cuda.synchronize()
+        print(f"[waits] workspace filled with {fill} bytes, call {i}", flush=True)
+        assert np.array_equal(got, ref)
+
+
+def test_kv_stage_graph_replays():
+    w = small("flux_1024", H=4, N=2500, L=64, seed=55)
+    d = to_device(w, workloads.make_inputs(w))
+    eps = float(np.float32(w.eps))
+    need = ttr.workspace_bytes(w.B, w.H, w.N, w.D, w.F, 1, w.L, False, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=d["Q"].device)
+    out = torch.empty_like(d["Q"])
+    ref = host(ttr.hybrid_forward(d["Q"], d["K"], d["V"], d["W"], d["b"], d["g"], eps, w.L, ws=ws))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # (a warm-up on the capture stream)
+        ttr.hybrid_forward(d["Q"], d["K"], d["V"], d["W"], d["b"], d["g"], eps, w.L, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ttr.hybrid_forward(d["Q"], d["K"], d["V"], d["W"], d["b"], d["g"], eps, w.L, out=out, ws=ws)
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[waits] graph replay {i}", flush=True)
+        assert np.array_equal(host(out), ref)
+        # eager calls between replays use new launch numbers on the same workspace
+        again = host(ttr.hybrid_forward(d["Q"], d["K"], d["V"], d["W"], d["b"], d["g"], eps, w.L, ws=ws))
+        assert np.array_equal(again, ref)
 
 
 def _causal_plan(B, H, N, chunk):
