@@ -48,6 +48,8 @@
 // lm_pack_kernel: the landmark chunks alone (every key a landmark for the
 // distillation's teacher, or the student's landmark branch).
 #include <atomic>
+#include <chrono>
+#include <random>
 #include <type_traits>
 
 #include "common.hpp"
@@ -898,9 +900,16 @@ size_t kv2_reduce_workspace_bytes(const Problem& p) {
 }
 
 // Launch numbers tag the meeting words (45 bits; 0, the number of a cleared
-// word, is skipped).
+// word, is skipped). Each process starts the count at a random point, so
+// words another process left in reused memory (only a launch whose splits
+// never all left does so) are not taken for this process's.
+static unsigned long long first_launch_number() {
+  std::random_device rd;
+  return ((unsigned long long)rd() << 32) ^ (unsigned long long)rd() ^
+         (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+}
 static unsigned long long next_launch_number() {
-  static std::atomic<unsigned long long> counter{0};
+  static std::atomic<unsigned long long> counter{first_launch_number()};
   unsigned long long v;
   do v = (counter.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << (64 - kMeetTag)) - 1);
   while (v == 0);
