@@ -169,7 +169,7 @@ def _phi_slice(x: np.ndarray, W: Optional[np.ndarray], b: Optional[np.ndarray], 
 def feature_map(X, W=None, b=None, kind: str = "elu1") -> np.ndarray:
     """phi(X) = map(X W_h + b_h) per (batch, head).  X [B,H,N,D] -> [B,H,N,F].
 
-    map is elu(z) + 1 by default (north-star feature map; "Flux2TTRTrainer"
+    map is elu(z) + 1 by default (the hybrid forward's map; "Flux2TTRTrainer"
     section "Inputs worth setting" for feature_dim F; "NNT Define Linear
     Attention" section "The inputs" for elu + 1), or relu / softmax over the
     features (the other options of that section).
