@@ -224,7 +224,8 @@ __device__ __forceinline__ bool meet_all(const unsigned long long* w, unsigned n
 // and writes phi^T [64 f][32 tok] to LDS; consumer (fc = fp, tg) accumulates
 //   KV[64 x D] += phi^T . V                                       (A = phi^T from LDS,
 //                    B = V read transposed from LDS)
-// Iteration t: producers map step t, consumers take step t - 1; one barrier.
+// Iteration t: producers form the products of step t and map step t - 1,
+// consumers take step t - 2; one barrier.
 template <int D, int F, bool PROJ, int MAP, bool PACK>
 __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   using S = KvsShape<D, F>;
@@ -312,10 +313,9 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
-  // K(0), V(0) and K(1) first: they land while the prologue runs
+  // K(0) and K(1) first: they land while the prologue runs
   if (producer) {
     copy_k(0, C0{});
-    copy_v(0, C0{});
     copy_k(1, C1{});
   }
   // ---- landmark chunks of this (batch, head), spread over its workgroups
@@ -359,10 +359,10 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   // half in kperm column order, so that a consumer's plain 16-byte row read
   // hands it the tokens in the C-row order of the transposed V fragments
   auto ptile = [&](int slot, int p) -> uint16_t* { return pbuf + (slot * 4 + p) * 64 * 32; };
-  // Both roles take nsteps + 1 loop barriers (the producers map steps
-  // 0 .. nsteps - 1, the consumers take them one iteration later), then the
-  // same barriers after the loop: their s_barrier counts match. Each role's
-  // state lives in its own branch.
+  // Both roles take nsteps + 2 loop barriers (the producers' iteration t
+  // forms the products of step t and maps step t - 1, the consumers take
+  // step t - 2), then the same barriers after the loop: their s_barrier
+  // counts match. Each role's state lives in its own branch.
   unsigned long long pre = 0;  // (tid 0) the arrivals word, read early: split 0 wrote it at its start
   if (producer) {
     // ---- producer: W slice as the B operand (lane = feature fs0 + 32 fb + c,
@@ -446,17 +446,18 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
     };
     float ks[2] = {0.f, 0.f};
     const uint32_t ones2 = 0x3f803f80u;  // bf16 (1, 1)
-    // step j: the first product, the map, phi^T into LDS, ksum from the
-    // rounded pairs (two per v_dot2)
-    auto produce = [&](int slot, const Frag<uint16_t> (&kf)[NKB]) __attribute__((always_inline)) {
-      f32x16 acc[2];
+    // a step's first product: acc = K rows . W slice
+    auto products = [&](const Frag<uint16_t> (&kf)[NKB], f32x16 (&acc)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) acc[fb] = mma_from(f32x16{}, kf[0], wf[fb][0]);
 #pragma unroll
       for (int kb = 1; kb < NKB; ++kb)
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) mma(acc[fb], kf[kb], wf[fb][kb]);
-      __builtin_amdgcn_s_setprio(0);  // the map's vector work runs beside the consumer's products
+    };
+    // the map of a step's products, phi^T into LDS slot `slot`, ksum from the
+    // rounded pairs (two per v_dot2)
+    auto map_store = [&](int slot, const f32x16 (&acc)[2]) __attribute__((always_inline)) {
       uint16_t* pt = ptile(slot, pw);
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) {
@@ -478,41 +479,66 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
         *reinterpret_cast<u32x4*>(pt + toff32(32 * fb + c, 16 + 8 * g)) = hi;
       }
     };
-    // Iteration t: this wave's copies of K(t) and V(t - 1) (issued two
-    // iterations back) have landed when at most the 2 NI copies of the last
-    // iteration are in flight; after the barrier everyone's have, phi^T
-    // buffer t & 1 is free, and so are the ring slots of K(t - 1) and V(t - 2),
-    // which take K(t + 2) and V(t + 1). Copies past the range read zeros.
-    // (t % 3 == slot)
-    auto iteration = [&](int t, auto slot) __attribute__((always_inline)) {
-      constexpr int sl = decltype(slot)::value;
-      wait_vmcnt<2 * NI>();
+    // Iteration t (0 .. nsteps) forms the products of step t (t < nsteps)
+    // and, beside them, maps step t - 1 (t >= 1) from the products the
+    // previous iteration left in acc, so the map no longer waits for its own
+    // step's products. Copies: K(t + 2) into ring slot (t + 2) % 3 and V(t)
+    // into slot t % 3 (the consumers take V(t - 2) from slot (t + 1) % 3).
+    // At the start of iteration t this wave's copies of K(t) and V(t - 2)
+    // have landed once at most the 2 NI copies of iteration t - 1 are in
+    // flight (iteration 0: at most NI, K(1)); after the barrier everyone's
+    // have, and phi^T slot (t - 1) % 3 is free (the consumers read step t - 4
+    // there last, in iteration t - 2). Copies past the range read zeros.
+    // (t % 3 == slot; kind 0: products only, 1: both, 2: the last map only)
+    f32x16 acc[2];
+    auto iteration = [&](int t, auto slot, auto waitn, auto kind) __attribute__((always_inline)) {
+      constexpr int sl = decltype(slot)::value, KIND = decltype(kind)::value;
+      wait_vmcnt<decltype(waitn)::value>();
       barrier_lds();
-      // this wave's products first on the SIMD's matrix core (the consumer
-      // wave beside it waits for them anyway one step later)
+      // this wave's work first on the SIMD (the consumer wave beside it
+      // fills the matrix core's gaps)
       __builtin_amdgcn_s_setprio(1);
       copy_k(t + 2, std::integral_constant<int, (sl + 2) % 3>{});
-      copy_v(t + 1, std::integral_constant<int, (sl + 1) % 3>{});
-      const uint16_t* kt = kslot(slot);
-      Frag<uint16_t> kf[NKB];
+      copy_v(t, std::integral_constant<int, sl>{});
+      f32x16 nacc[2];
+      if constexpr (KIND != 2) {
+        const uint16_t* kt = kslot(slot);
+        Frag<uint16_t> kf[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kf[kb] = ld_frag<uint16_t>(kt + toff<D, kRowRead>(32 * tg + c, 16 * kb + 8 * g));
-      if constexpr (MAP == kSoftmax) {
-        token_stats(kf, sl);
-        wave_lds_order();
+        for (int kb = 0; kb < NKB; ++kb) kf[kb] = ld_frag<uint16_t>(kt + toff<D, kRowRead>(32 * tg + c, 16 * kb + 8 * g));
+        if constexpr (MAP == kSoftmax) {
+          token_stats(kf, sl);
+          wave_lds_order();
+        }
+        products(kf, nacc);
       }
-      produce(sl, kf);
+      if constexpr (KIND != 0) map_store((sl + 2) % 3, acc);
+      __builtin_amdgcn_s_setprio(0);
+      if constexpr (KIND != 2) {
+        acc[0] = nacc[0];
+        acc[1] = nacc[1];
+      }
     };
-    // steps 0 .. nsteps - 1, then one more barrier while the consumers take
-    // the last step (no map of a step nobody reads: the matrix core is theirs)
-    int t3 = 0;
+    using W1 = std::integral_constant<int, NI>;
+    using W2 = std::integral_constant<int, 2 * NI>;
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    iteration(0, C0{}, W1{}, K0{});  // (every split has at least one step)
+    int t3 = 1;
     for (; t3 + 3 <= nsteps; t3 += 3) {
-      iteration(t3, C0{});
-      iteration(t3 + 1, C1{});
-      iteration(t3 + 2, C2{});
+      iteration(t3, C1{}, W2{}, K1{});
+      iteration(t3 + 1, C2{}, W2{}, K1{});
+      iteration(t3 + 2, C0{}, W2{}, K1{});
     }
-    if (t3 < nsteps) iteration(t3, C0{});
-    if (t3 + 1 < nsteps) iteration(t3 + 1, C1{});
+    if (t3 < nsteps) iteration(t3, C1{}, W2{}, K1{});
+    if (t3 + 1 < nsteps) iteration(t3 + 1, C2{}, W2{}, K1{});
+    // iteration nsteps: the map of the last step, then one more barrier while
+    // the consumers take it (no products of a step nobody reads)
+    const int rl = nsteps % 3;
+    if (rl == 0) iteration(nsteps, C0{}, W2{}, K2{});
+    else if (rl == 1) iteration(nsteps, C1{}, W2{}, K2{});
+    else iteration(nsteps, C2{}, W2{}, K2{});
     wait_vmcnt<0>();  // the last (zero) copies have landed before LDS is reused
     barrier_lds();
     if (tid == 0) pre = meet_load(mw);  // (its latency hides behind the partial stores)
@@ -605,9 +631,9 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
             for (int fb = 0; fb < 2; ++fb) mma(kv[fb][i], pa[fb][hh], vf[i][hh]);
       }
     };
-    for (int t = 0; t <= nsteps; ++t) {
-      barrier_lds();  // phi^T and V of step t - 1 are in LDS
-      if (t > 0) consume(t - 1);
+    for (int t = 0; t <= nsteps + 1; ++t) {
+      barrier_lds();  // phi^T and V of step t - 2 are in LDS
+      if (t > 1) consume(t - 2);
     }
     __syncthreads();  // LDS free
     // the token parts' KV (more than one only when a feature group is one
