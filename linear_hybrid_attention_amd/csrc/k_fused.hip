@@ -46,6 +46,16 @@ struct FusedArgs {
 // LIN = false: softmax attention over the landmarks alone, out = o / l (the
 // pack then holds only the landmark chunks; no linear branch, no blend).
 // OUT32: the output in fp32 (out32).
+// The map of the linear branch on a product that already holds the pack's
+// bias: for elu + 1 the pack stores b + 1, so x = z + b + 1 and
+// elu(z + b) + 1 = max(x, min(exp(x - 1), 1)) (an fma, the exponential with
+// its clamp, a max); relu and softmax take x = z + b.
+template <int MAP>
+__device__ __forceinline__ float phi_q(float x, float m, float inv_s) {
+  if constexpr (MAP == kElu1) return fmaxf(x, fminf(fmaxf(__builtin_amdgcn_exp2f(fmaf(x, kLog2e, -kLog2e)), 0.f), 1.f));
+  else return phi_of<MAP>(x, m, inv_s);
+}
+
 template <int D, int F, int MAP, bool LIN = true, bool OUT32 = false>
 __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   constexpr int CH = 64 * D;  // elements per chunk (every chunk kind)
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       const float* kp = vecS + F + fc * 64 + fb * 32 + 8 * g;
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = phi_of<MAP>(acc[fb][r], qm, qinv);
+      for (int r = 0; r < 16; ++r) p[r] = phi_q<MAP>(acc[fb][r], qm, qinv);
 #pragma unroll
       for (int r = 0; r < 8; ++r) den += p[r] * kp[r] + p[8 + r] * kp[16 + r];
       pb[2 * fb] = to_frag<uint16_t>(p);
@@ -251,8 +261,8 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
 #pragma unroll
         for (int u = 0; u < PPS; ++u) {
           const int t = (j - N1) * PPS + u, fb = t >> 3, q = t & 7;
-          const float p0 = phi_of<MAP>(acc[fb][2 * q], qm, qinv);
-          const float p1 = phi_of<MAP>(acc[fb][2 * q + 1], qm, qinv);
+          const float p0 = phi_q<MAP>(acc[fb][2 * q], qm, qinv);
+          const float p1 = phi_q<MAP>(acc[fb][2 * q + 1], qm, qinv);
           den = fmaf(p0, __uint_as_float(kq[t >> 1][2 * (t & 1)]), den);
           den = fmaf(p1, __uint_as_float(kq[t >> 1][2 * (t & 1) + 1]), den);
           pw[2 * fb + (q >> 2)][q & 3] = pack_bf16x2(p0, p1);

@@ -38,7 +38,8 @@
 // drops stale lines, so the result never depends on where the hardware put
 // the workgroups.
 //
-// The pack, per (batch, head): bias, ksum [F] fp32 in kperm order; F / 64
+// The pack, per (batch, head): bias (b + 1 for the elu + 1 map, which then
+// takes x = z + b + 1 straight from the products), ksum [F] fp32 in kperm order; F / 64
 // KV^T chunks [D][64 f]; one K_L + V_L^T chunk per 32 landmarks
 // idx_j = floor(j N / L) ("Flux2TTRTrainer", section "How the distillation
 // works": exact softmax over strided landmark tokens); per head the W^T
@@ -253,7 +254,9 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
     else return vr2;
   };
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // (the wave index is read into a scalar register, so LDS copy destinations
+  // derived from it are computed with scalar instructions)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
   const bool producer = w < 4;
   const int pw = w & 3;                   // index among the producers (or the consumers)
@@ -288,8 +291,6 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   // copies pieces 64 (NI pw + i) + lane of a step's tile: row r = piece / (D / 8),
   // physical piece q' = piece % (D / 8), which holds the row's piece q' ^ tswz(r).
   const uint32_t range_bytes = (uint32_t)((size_t)t_end * D * 2);
-  const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(Kp, range_bytes);
-  const __amdgpu_buffer_rsrc_t rV = buffer_rsrc(Vp, range_bytes);
   uint32_t koff[NI], voff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -299,16 +300,26 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
   }
   // Step j goes to ring slot j % 3, given as a constant: LDS offsets the
   // compiler can see apart keep it from making the wave's LDS reads wait for
-  // copies into other slots.
+  // copies into other slots. Step j's copies go through a resource whose base
+  // is moved j steps on and whose size shrinks by as much (never below zero),
+  // built with scalar instructions: the lane offsets stay as they are, and
+  // the bounds check still ends at the range's last token.
+  auto step_rsrc = [&](const uint16_t* base, int j) {
+    const uint32_t off = (uint32_t)__builtin_amdgcn_readfirstlane(j * STEP * D * 2);
+    const uint32_t left = range_bytes > off ? range_bytes - off : 0u;
+    return buffer_rsrc(reinterpret_cast<const unsigned char*>(base) + off, __builtin_amdgcn_readfirstlane(left));
+  };
   auto copy_k = [&](int j, auto slot) {
     uint16_t* dst = kslot(slot);
+    const __amdgpu_buffer_rsrc_t r = step_rsrc(Kp, j);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) copy16_async(rK, koff[i] + (uint32_t)(j * STEP * D * 2), 0, dst + (NI * pw + i) * 512);
+    for (int i = 0; i < NI; ++i) copy16_async(r, koff[i], 0, dst + (NI * pw + i) * 512);
   };
   auto copy_v = [&](int j, auto slot) {
     uint16_t* dst = vslot(slot);
+    const __amdgpu_buffer_rsrc_t r = step_rsrc(Vp, j);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) copy16_async(rV, voff[i] + (uint32_t)(j * STEP * D * 2), 0, dst + (NI * pw + i) * 512);
+    for (int i = 0; i < NI; ++i) copy16_async(r, voff[i], 0, dst + (NI * pw + i) * 512);
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
@@ -403,22 +414,26 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
                 __builtin_bit_cast(u32x4, wf[fb][kb]);
       }
     }
-    // The bias enters the map, not the product: for elu + 1,
-    // phi = max(x + (b + 1), min(exp2(x log2e + b log2e), 1)) costs what the
-    // map without a bias does (an fma in place of the multiply, an add either way).
-    float bcol[2], bl2[2];  // per lane (its feature column): b + 1 (elu + 1) or b, and b log2e
+    // The bias enters the product: the first MFMA of a step takes as its C
+    // input a tile holding each lane's bias (lane = feature column), b + 1
+    // for elu + 1, so the products come out as x = z + b + 1 and the map is
+    // phi = max(x, min(exp2(x log2e - log2e), 1)) (three instructions: an
+    // fma, the exponential with its clamp, a max; the relu and softmax maps
+    // take x = z + b as it is).
+    f32x16 bsplat[2];
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb) {
       const float bc = a.bias ? a.bias[(size_t)h * F + fs0 + 32 * fb + c] : 0.f;
-      bcol[fb] = MAP == kElu1 ? bc + 1.f : bc;
-      bl2[fb] = bc * kLog2e;
+      const float b1 = MAP == kElu1 ? bc + 1.f : bc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bsplat[fb][r] = b1;
     }
-    auto phi_b = [&](float x, int fb, float2 st) -> float {
+    auto phi_b = [&](float x, float2 st) -> float {
       if constexpr (MAP == kElu1) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, bl2[fb]));
-        return fmaxf(x + bcol[fb], fminf(fmaxf(e, 0.f), 1.f));
+        const float e = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -kLog2e));
+        return fmaxf(x, fminf(fmaxf(e, 0.f), 1.f));
       } else {
-        return phi_of<MAP>(x + bcol[fb], st.x, st.y);
+        return phi_of<MAP>(x, st.x, st.y);
       }
     };
     // softmax map (identity projection, F == D): each lane's bias values for
@@ -449,7 +464,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
     // a step's first product: acc = K rows . W slice
     auto products = [&](const Frag<uint16_t> (&kf)[NKB], f32x16 (&acc)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb) acc[fb] = mma_from(f32x16{}, kf[0], wf[fb][0]);
+      for (int fb = 0; fb < 2; ++fb) acc[fb] = mma_from(bsplat[fb], kf[0], wf[fb][0]);
 #pragma unroll
       for (int kb = 1; kb < NKB; ++kb)
 #pragma unroll
@@ -469,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
             s0 = wstats[slot * 32 + crow(lane, 2 * i)];
             s1 = wstats[slot * 32 + crow(lane, 2 * i + 1)];
           }
-          const bf16x2 pr = {(__bf16)phi_b(acc[fb][2 * i], fb, s0), (__bf16)phi_b(acc[fb][2 * i + 1], fb, s1)};
+          const bf16x2 pr = {(__bf16)phi_b(acc[fb][2 * i], s0), (__bf16)phi_b(acc[fb][2 * i + 1], s1)};
           ks[fb] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, ones2), ks[fb], false);
           u[i] = __builtin_bit_cast(uint32_t, pr);
         }
@@ -562,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       }
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) {
-        const float z0 = bf2f(f2bf(phi_b(0.f, fb, st0)));
+        const float z0 = bf2f(f2bf(phi_b(bsplat[fb][0], st0)));  // a zero row's products are the bias tile
         ks[fb] -= (float)nzero * z0;
         ks[fb] += shfl_xor32(ks[fb]);
       }
@@ -801,7 +816,7 @@ __global__ __launch_bounds__(512, 1) void kv_stage_kernel(KvsArgs a) {
       const float s = ksum_over_splits(tid);
       const int f = fg0 + tid;
       ksumP[kperm(f)] = ok ? s : kQNaN;
-      biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
+      biasP[kperm(f)] = (a.bias ? a.bias[(size_t)h * F + f] : 0.f) + (MAP == kElu1 ? 1.f : 0.f);
     }
   } else {
     // task: (fs, fb, db, q, g, lane quad) -> KV rows f = .. crow(l, 4 q + e) (e = 0..3),
