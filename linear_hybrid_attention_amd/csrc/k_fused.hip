@@ -372,14 +372,41 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   // chunk lc + 1 and the PV product of chunk lc, then runs the softmax of
   // chunk lc + 1 while the PV MFMAs execute. Step lc reads chunks LB + lc
   // (V_L^T) and LB + lc + 1 (K_L), LB = 2 NFC (0 for landmarks alone).
+  // The two products alternate one MFMA per slot (the scores are a single
+  // accumulation chain; a PV MFMA between two of its links covers the
+  // chain's latency), and every operand is read from LDS LEAD slots ahead.
+  constexpr int NPV = 2 * (D / 32), NSC = D / 16, NL = NPV + NSC;
+  static_assert(NPV == NSC, "one scores MFMA after each PV MFMA");
+  auto lm_step = [&](int lc) __attribute__((always_inline)) {
+    const uint16_t* kl = slot_of(LB + lc + 1);
+    const uint16_t* vlt = slot_of(LB + lc) + 32 * D;
+    auto a_ptr = [&](int j) -> const uint16_t* {
+      const int i = j >> 1;
+      if (j & 1) return kl + toff<D, kRowRead>(c, i * 16 + 8 * g);
+      return vlt + toff32((i >> 1) * 32 + c, (i & 1) * 16 + 8 * g);
+    };
+    Frag<uint16_t> fa[NL];
+#pragma unroll
+    for (int j = 0; j < LEAD; ++j) fa[j] = ld_frag<uint16_t>(a_ptr(j));
+    s = f32x16{};
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      if (j + LEAD < NL) fa[j + LEAD] = ld_frag<uint16_t>(a_ptr(j + LEAD));
+      const int i = j >> 1;
+      if (j & 1) mma(s, fa[j], qf[i]);
+      else mma(o[i >> 1], fa[j], pf[i & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 #pragma clang loop unroll(disable)
-  for (int lc = 0; lc < nlc; ++lc) {
+  for (int lc = 0; lc + 1 < nlc; ++lc) {
     issue(LB + lc + 2);
-    const bool more = lc + 1 < nlc;  // workgroup-uniform
-    if (more) scores(lc + 1, s);
-    pv(lc, pf);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) softmax(lc + 1, s, pf);
+    lm_step(lc);
+    softmax(lc + 1, s, pf);
+    end_step();
+  }
+  if (nlc > 0) {  // the last chunk: its PV product alone
+    pv(nlc - 1, pf);
     end_step();
   }
 

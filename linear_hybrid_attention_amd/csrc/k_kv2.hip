@@ -171,13 +171,18 @@ struct KvsShape {
 // (a quiet NaN by its bits: the file is built without NaN semantics)
 #define kQNaN __uint_as_float(0x7fc00000u)
 
-// Partial loads and stores: plain, through the XCD's L2 (see the meeting of
-// the splits for when that is coherent).
+// Partial loads and stores through the XCD's L2 (see the meeting of the
+// splits for when that is coherent). The stores are system-scope (sc0 sc1):
+// the L2 writes them through to memory while the kernel runs, so no partial
+// is still dirty in L2 when the kernel ends and the end-of-kernel write-back
+// covers only the pack (about 1 us less between this kernel and the query
+// kernel at flux_1024, where the partials are 15.7 MB).
 __device__ __forceinline__ u32x4 ld16_part(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 __device__ __forceinline__ void st16_part(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4& v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+  constexpr int kSc0Sc1 = 1 | 16;  // cache-policy bits: sc0 (1), sc1 (16)
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kSc0Sc1);
 }
 
 // Id of the XCD the calling wave runs on (hardware register XCC_ID, bits 0-3;
