@@ -458,7 +458,9 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   wave_lds_order();
   // The stores go through a buffer resource over this (batch, head)'s output
   // rows: a row past N gets offset N D 2 bytes, the resource's size, which
-  // the hardware drops. No branch, so all the LDS reads are in flight at once.
+  // the hardware drops. They write through the L2 (the output is not read
+  // again by this forward), so the L2 holds no dirty output lines when the
+  // kernel ends and its end-of-kernel write-back is short. No branch, so all the LDS reads are in flight at once.
   // (The validated N D < 2^31 keeps every offset within 32 bits.)
   constexpr int PIECES_PER_ROW = D / 8, NP = 32 * PIECES_PER_ROW / 64;
   const uint32_t out_bytes = (uint32_t)((size_t)N * D * 2);
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   for (int i = 0; i < NP; ++i) {
     const int P = 64 * i + lane, row = P / PIECES_PER_ROW, pc = P % PIECES_PER_ROW;
     const int n = tile * 128 + 32 * w + row;
-    store16(rout, n < N ? (uint32_t)(n * D + pc * 8) * 2 : out_bytes, v[i]);
+    store16_wt(rout, n < N ? (uint32_t)(n * D + pc * 8) * 2 : out_bytes, v[i]);
   }
 }
 

@@ -89,6 +89,14 @@ __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, 
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
 
+// The same store at system scope (cache-policy bits sc0 and sc1): the L2
+// writes it through to memory at once instead of holding a dirty line until
+// the end-of-kernel write-back.
+__device__ __forceinline__ void store16_wt(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4& v) {
+  constexpr int kSc0Sc1 = 1 | 16;
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kSc0Sc1);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
 template <int N>
