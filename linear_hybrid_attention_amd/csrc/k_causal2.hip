@@ -188,7 +188,10 @@ __device__ __forceinline__ void causal_segment(const Causal2Args& a, unsigned ch
         const bool ok = qb < NB && ch >= 0 && t0 + row < N;
         // one sink slot per store, so that none of them is merged away
         uint16_t* sk = a.sink + ((i * (32 * D / 8 / 64) + k) * 64 + lane) * 8;
-        *reinterpret_cast<u32x4*>(ok ? og + (size_t)row * D + pc * 8 : sk) = v;
+        // nontemporal: the output streams past the caches (it is not read
+        // again here), leaving the L2 and the last-level cache to the K and
+        // V rows that the walk reads a second time
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(ok ? og + (size_t)row * D + pc * 8 : sk));
       }
     }
   };
