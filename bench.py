@@ -52,6 +52,9 @@ def parse():
                     help="time each staged entry point (feature map, key/value reduction, apply, landmark branch, "
                          "blend) with its own roofline instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="untimed forwards for this many milliseconds before the warm-up steps, so that the GPU "
+                         "has reached its steady clock (see settle())")
     ap.add_argument("--chunk", type=int, default=0,
                     help="causal workloads: run this chunk (64, 128 or 256) instead of the workload's own")
     ap.add_argument("--cold", action="store_true",
@@ -65,6 +68,34 @@ def parse():
                          "profiles/traffic_counters.json")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy in the counter runs")
     return ap.parse_args()
+
+
+def settle(step, ms):
+    """Untimed calls of step() for about ms milliseconds of wall time. After an
+    idle period the GPU runs the forward up to 8% slower until it has been
+    under load for a while (the first 200 flux_1024 forwards after a pause run
+    at 64 us, the next at 60 us; on a fresh process 200-500 ms of load did not
+    always suffice, 1000 ms did in every run), which a handful of warm-up steps
+    does not cover. Returns the calls."""
+    import torch
+    n = 0
+    t_end = time.perf_counter() + ms / 1000.0
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+    return n
+
+
+def host_lead(steps):
+    """Before the start event of a back-to-back timed region: a spin kernel of
+    about 40 us per timed step, so that the host has enqueued the timed calls
+    before the GPU reaches the start event. The region then holds the GPU's
+    time for the calls and not the host's launch latency (about 14 us of Python
+    per call, which otherwise leaves the GPU idle after the start event)."""
+    import torch
+    torch.cuda._sleep(int(steps) * 80_000)  # cycles; about 40 us each at the measured 2 GHz
 
 
 def copy_calibration(mib):
@@ -386,6 +417,7 @@ def main_layer(args):
         ttr.nnt_layer_forward(X, Wq, bq, Wk, bk, Wv, bv, Wo, bo, w.H, float(x["eps"]), w.causal, w.fmap,
                               out=out, ws=ws)
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -398,6 +430,7 @@ def main_layer(args):
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    host_lead(args.steps)
     start.record(stream)
     for _ in range(args.steps):
         step()
@@ -435,7 +468,8 @@ def main_layer(args):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "E": w.E, "H": w.H, "D": w.E // w.H,
-                   "feature_map": w.fmap, "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
+                   "feature_map": w.fmap, "causal": w.causal, "global_batch": w.B, "seq_len": w.N,
+                   "clock_settle_ms": args.settle_ms, "clock_settle_calls": settled},
         "roofline": {"kernel": name, "bound": rl["bound"], "achieved": rl["achieved"], "peak": rl["peak"],
                      "unit": rl["unit"], "frac": rl["frac"], "traffic": traffic,
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nb,
@@ -1003,6 +1037,7 @@ def main():
                            chunk=w.chunk if w.causal else 0)
 
     plan = kernel_plan(w)
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -1025,6 +1060,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if flush is None:
+        host_lead(args.steps)
         start.record(stream)
         for i in range(args.steps):
             step()
@@ -1090,7 +1126,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "F": w.F, "L": w.L,
                    "causal": w.causal, **({"chunk": w.chunk} if w.causal else {}),
-                   "caches": "cold" if args.cold else "hot", "global_batch": w.B, "seq_len": w.N},
+                   "caches": "cold" if args.cold else "hot", "global_batch": w.B, "seq_len": w.N,
+                   "clock_settle_ms": args.settle_ms, "clock_settle_calls": settled},
         "roofline": {"kernel": name, "bound": rl["bound"], "achieved": rl["achieved"], "peak": rl["peak"],
                      "unit": rl["unit"], "frac": rl["frac"], "traffic": traffic,
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
