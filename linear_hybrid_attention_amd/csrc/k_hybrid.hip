@@ -25,12 +25,18 @@ namespace ttr {
 
 template <typename T, int D, int F, int MODE>
 struct HybridSmem {
-  using WR = LdsRow<T, D>;   // W^T   [F][D]
-  using KR = LdsRow<T, F>;   // KV^T  [D][F]  (columns in kperm order)
+  // Features staged at a time: all F when W^T and KV^T fit in LDS together,
+  // else blocks of 64 (fp32 with D = 128: 128 KB each in full)
+  static constexpr int full_bytes = F * LdsRow<T, D>::bytes_per_row +
+                                    ((MODE & M_LIN) ? D * LdsRow<T, F>::bytes_per_row : 0) + 2 * F * 4;
+  static constexpr int FB = full_bytes <= 160 * 1024 ? F : 64;
+  static_assert(F % FB == 0, "whole feature blocks");
+  using WR = LdsRow<T, D>;   // W^T   [FB][D]
+  using KR = LdsRow<T, FB>;  // KV^T  [D][FB]  (columns in kperm order)
   static constexpr int LB = 64;  // landmarks per LDS block
   using LR = LdsRow<T, D>;   // K_L   [LB][D]
   using VR = LdsRow<T, LB>;  // V_L^T [D][LB] (columns in kperm order)
-  static constexpr int w_bytes = F * WR::bytes_per_row;
+  static constexpr int w_bytes = FB * WR::bytes_per_row;
   static constexpr int kv_bytes = (MODE & M_LIN) ? D * KR::bytes_per_row : 0;
   static constexpr int lin_bytes = (MODE & (M_PHI | M_LIN)) ? w_bytes + kv_bytes + 2 * F * 4 : 0;
   static constexpr int lm_bytes = (MODE & M_LM) ? LB * LR::bytes_per_row + D * VR::bytes_per_row : 0;
@@ -42,24 +48,25 @@ __device__ __forceinline__ int landmark_index(int j, int N, int L) {
   return (int)(((long long)j * (long long)N) / (long long)L);
 }
 
-// Stage W^T (or the identity when there is no projection) into LDS.
-template <typename T, int D, int F, bool PROJ>
-__device__ __forceinline__ void stage_wt(T* Wt, const T* W, int tid) {
+// Stage rows f0 .. f0 + FB - 1 of W^T (or of the identity when there is no
+// projection) into LDS; W is [D][F].
+template <typename T, int D, int F, int FB, bool PROJ>
+__device__ __forceinline__ void stage_wt(T* Wt, const T* W, int f0, int tid) {
   using WR = LdsRow<T, D>;
   if constexpr (PROJ) {
     // consecutive threads take consecutive d pairs: conflict-free LDS writes
-    for (int u = tid; u < (D / 2) * (F / 8); u += 256) {
+    for (int u = tid; u < (D / 2) * (FB / 8); u += 256) {
       const int d = 2 * (u % (D / 2));
       const int fo = (u / (D / 2)) * 8;
-      const Vec8<T> w0 = ld8(W + (size_t)d * F + fo);
-      const Vec8<T> w1 = ld8(W + (size_t)(d + 1) * F + fo);
+      const Vec8<T> w0 = ld8(W + (size_t)d * F + f0 + fo);
+      const Vec8<T> w1 = ld8(W + (size_t)(d + 1) * F + f0 + fo);
 #pragma unroll
       for (int j = 0; j < 8; ++j) st_pair(Wt + (fo + j) * WR::stride + d, w0.v[j], w1.v[j]);
     }
   } else {
-    for (int u = tid; u < F * D; u += 256) {
+    for (int u = tid; u < FB * D; u += 256) {
       const int f = u / D, d = u % D;
-      Wt[f * WR::stride + d] = from_f32<T>(f == d ? 1.f : 0.f);
+      Wt[f * WR::stride + d] = from_f32<T>(f0 + f == d ? 1.f : 0.f);
     }
   }
 }
@@ -94,22 +101,29 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
     float* biasP = reinterpret_cast<float*>(smem + S::w_bytes + S::kv_bytes);
     float* ksumP = biasP + F;
 
-    stage_wt<T, D, F, PROJ>(Wt, static_cast<const T*>(a.W) + (size_t)h * D * F, tid);
-    for (int f = tid; f < F; f += 256) biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
-    if constexpr ((MODE & M_LIN) != 0) {
-      const float* KV = a.KV + (size_t)bh * F * D;
-      for (int u = tid; u < (F / 2) * (D / 4); u += 256) {
-        const int f = 2 * (u % (F / 2));
-        const int d0 = (u / (F / 2)) * 4;
-        const f32x4 k0 = *reinterpret_cast<const f32x4*>(KV + (size_t)f * D + d0);
-        const f32x4 k1 = *reinterpret_cast<const f32x4*>(KV + (size_t)(f + 1) * D + d0);
-        const int pos = kperm(f);  // f even: kperm(f + 1) == pos + 1
+    constexpr int FB = S::FB;
+    // W^T rows and KV^T columns of features f0 .. f0 + FB - 1 (kperm order
+    // within each aligned 16: the same in the block as in the whole)
+    auto stage_block = [&](int f0) {
+      stage_wt<T, D, F, FB, PROJ>(Wt, static_cast<const T*>(a.W) + (size_t)h * D * F, f0, tid);
+      if constexpr ((MODE & M_LIN) != 0) {
+        const float* KV = a.KV + (size_t)bh * F * D;
+        for (int u = tid; u < (FB / 2) * (D / 4); u += 256) {
+          const int f = 2 * (u % (FB / 2));
+          const int d0 = (u / (FB / 2)) * 4;
+          const f32x4 k0 = *reinterpret_cast<const f32x4*>(KV + (size_t)(f0 + f) * D + d0);
+          const f32x4 k1 = *reinterpret_cast<const f32x4*>(KV + (size_t)(f0 + f + 1) * D + d0);
+          const int pos = kperm(f);  // f even: kperm(f + 1) == pos + 1
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          st_pair(KVt + (d0 + j) * KR::stride + pos, from_f32<T>(k0[j]), from_f32<T>(k1[j]));
+          for (int j = 0; j < 4; ++j)
+            st_pair(KVt + (d0 + j) * KR::stride + pos, from_f32<T>(k0[j]), from_f32<T>(k1[j]));
+        }
       }
+    };
+    stage_block(0);
+    for (int f = tid; f < F; f += 256) biasP[kperm(f)] = a.bias ? a.bias[(size_t)h * F + f] : 0.f;
+    if constexpr ((MODE & M_LIN) != 0)
       for (int f = tid; f < F; f += 256) ksumP[kperm(f)] = a.ksum[(size_t)bh * F + f];
-    }
     __syncthreads();
 
     // softmax map (identity projection, F == D): the token's feature maximum
@@ -133,6 +147,12 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
     float den = 0.f;
 
     for (int fc = 0; fc < F / 32; ++fc) {
+      if (FB < F && fc > 0 && fc % (FB / 32) == 0) {  // next feature block (workgroup-uniform)
+        __syncthreads();
+        stage_block(fc * 32);
+        __syncthreads();
+      }
+      const int fl = fc % (FB / 32);  // chunk within the staged block
       // phi^T chunk [32 features x 32 tokens]; the bias is preloaded into the accumulator.
       f32x16 acc;
       {
@@ -142,7 +162,7 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
       }
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb)
-        mma(acc, ld_frag<T>(Wt + (fc * 32 + c) * WR::stride + kb * 16 + 8 * g), qf[kb]);
+        mma(acc, ld_frag<T>(Wt + (fl * 32 + c) * WR::stride + kb * 16 + 8 * g), qf[kb]);
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] = phi_of<MAP>(acc[r], qm, qinv);
@@ -161,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void hybrid_kernel(HybridArgs a) {
         const Frag<T> pb0 = to_frag<T>(p), pb1 = to_frag<T>(p + 8);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const T* ap = KVt + (db * 32 + c) * KR::stride + fc * 32 + 8 * g;
+          const T* ap = KVt + (db * 32 + c) * KR::stride + fl * 32 + 8 * g;
           mma(num[db], ld_frag<T>(ap), pb0);
           mma(num[db], ld_frag<T>(ap + 16), pb1);
         }
@@ -314,8 +334,9 @@ hipError_t launch_hybrid(const Problem& p, int mode, bool out_io, const HybridAr
   if (p.dtype == 1) {
     if (p.D == 64) return launch_hybrid_d<uint16_t, 64>(p, mode, out_io, a, s);
     if (p.D == 128) return launch_hybrid_d<uint16_t, 128>(p, mode, out_io, a, s);
-  } else if (p.dtype == 0 && p.D == 64) {
-    return launch_hybrid_d<float, 64>(p, mode, out_io, a, s);
+  } else if (p.dtype == 0) {
+    if (p.D == 64) return launch_hybrid_d<float, 64>(p, mode, out_io, a, s);
+    if (p.D == 128) return launch_hybrid_d<float, 128>(p, mode, out_io, a, s);
   }
   return hipErrorInvalidValue;
 }

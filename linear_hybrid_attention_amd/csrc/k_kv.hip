@@ -314,6 +314,8 @@ hipError_t launch_kv_reduce(const Problem& p, const void* K, const void* V, cons
     launch_kv_d<uint16_t, 64>(p, a, s);
   } else if (p.dtype == 0 && p.D == 64) {
     launch_kv_d<float, 64>(p, a, s);
+  } else if (p.dtype == 0 && p.D == 128) {
+    launch_kv_d<float, 128>(p, a, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -42,7 +42,6 @@ ttr_status check_dims(const ttr_dims& d, bool has_w, int32_t max_f) {
   } else if (d.F != d.D) {
     return TTR_ERR_SHAPE;
   }
-  if (d.dtype == TTR_FP32 && d.D != 64) return TTR_ERR_UNSUPPORTED;
   // grid limits: (batch, head) pairs run on grid.y
   if ((int64_t)d.B * d.H > 65535) return TTR_ERR_UNSUPPORTED;
   if ((int64_t)d.N * d.D >= ((int64_t)1 << 31)) return TTR_ERR_UNSUPPORTED;

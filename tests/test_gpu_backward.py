@@ -62,6 +62,7 @@ BASE = workloads.WORKLOADS
     # whole row groups and K-steps (the products' unconditional-load variant) with a partial last tile
     BASE["flux_512"].with_(name="bw_bf16_rows16", B=1, H=2, N=272, L=16),
     BASE["tiny_fp32"].with_(name="bw_fp32_rows32", N=160, L=8),
+    BASE["tiny_fp32"].with_(name="bw_fp32_d128", N=120, D=128, L=6, w_std=1 / np.sqrt(128.0)),
 ], ids=lambda w: w.name)
 def test_backward_matches_oracle(w):
     _check(w)

@@ -102,6 +102,11 @@ def test_distill_step_fp32_given_teacher():
     _one_step(workloads.WORKLOADS["tiny_fp32"].with_(name="ds_fp32_t", N=96, L=12, b_std=0.1), teacher_given=True)
 
 
+def test_distill_step_fp32_d128():
+    _one_step(workloads.WORKLOADS["tiny_fp32"].with_(name="ds_fp32_d128", N=90, D=128, L=9, b_std=0.1,
+                                                     w_std=1 / np.sqrt(128.0)))
+
+
 def test_distill_step_bf16():
     _one_step(workloads.WORKLOADS["flux_512"].with_(name="ds_bf16", B=1, H=2, N=300, L=20))
 

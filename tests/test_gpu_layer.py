@@ -56,6 +56,7 @@ CASES = [
     ("fp32", 1, 150, 128, 2, True, "elu1"),
     ("fp32", 2, 64, 256, 4, False, "relu"),
     ("fp32", 1, 129, 256, 4, True, "softmax"),
+    ("fp32", 2, 100, 256, 2, False, "elu1"),      # D = 128
 ]
 
 

@@ -57,6 +57,22 @@ def test_hybrid_forward_feature_dim_512(shape):
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("shape", [dict(N=256, D=128, L=16), dict(B=2, H=3, N=333, D=128, L=7),
+                                   dict(N=200, D=128, L=0), dict(N=100, D=128, F=128, proj=False, L=5)])
+def test_hybrid_forward_fp32_d128(shape):
+    # fp32 IO with D = 128: W^T and KV^T are staged 64 features at a time
+    # (together they would fill 256 KB of LDS); identity map: F = D = 128
+    w = small("tiny_fp32", seed=60 + len(shape) + shape["N"], **shape)
+    x = workloads.make_inputs(w)
+    print(f"[hybrid-fp32-d128] B={w.B} H={w.H} N={w.N} D={w.D} F={w.F} L={w.L}", flush=True)
+    out = run_hybrid(w, to_device(w, x))
+    torch.cuda.synchronize()
+    err = normwise(host(out), oracle_hybrid(w, x))
+    print(f"[hybrid-fp32-d128] normwise err {err:.3e}", flush=True)
+    assert np.isfinite(host(out)).all()
+    assert err <= TOL["fp32"], err
+
+
 @pytest.mark.timeout(600)
 def test_causal_full_size_whole_output():
     # the causal configuration as stated (chunk 256) through the metric entry
@@ -157,7 +173,8 @@ def test_hybrid_causal_route():
 
 STAGED = [("tiny_fp32", {}), ("flux_512", dict(H=3, N=1000, L=7, seed=21)),
           ("flux_512", dict(H=2, N=333, D=64, L=33, seed=22)),
-          ("tiny_fp32", dict(N=257, L=5, seed=23))]
+          ("tiny_fp32", dict(N=257, L=5, seed=23)),
+          ("tiny_fp32", dict(H=3, N=300, D=128, L=9, seed=26))]  # fp32 with D = 128
 
 
 @pytest.mark.parametrize("name,kw", STAGED)

@@ -35,7 +35,10 @@ def test_sample_bytes_invalid_shape(lib):
     assert ttr.replay_sample_bytes(1, 2, 10, 64, torch.bfloat16, 0, True) == 0
     assert ttr.replay_sample_bytes(1, 2, 10, 64, torch.bfloat16, 11, True) == 0
     assert ttr.replay_sample_bytes(1, 2, 10, 96, torch.bfloat16, 3, True) == 0
-    assert ttr.replay_sample_bytes(1, 2, 10, 128, torch.float32, 3, True) == 0
+    # fp32 with D = 128 is a valid sample shape (the fp32 forward, backward and
+    # distillation step take D = 128)
+    assert ttr.replay_sample_bytes(1, 2, 10, 128, torch.float32, 3, True) == \
+        O.replay_sample_bytes(1, 2, 10, 128, 4, 3, True)
     assert lib.ttr_replay_sample_bytes(ttr.Dims(1, 2, 10, 64, 64, 7, 0), 3, 0) == 0
 
 
