@@ -59,7 +59,8 @@
  *     (else TTR_ERR_SHAPE), of which F == 256 is implemented by every entry
  *     point and F == 512 by the bf16 ttr_hybrid_forward (and its _noalloc
  *     form); other multiples return TTR_ERR_UNSUPPORTED. Without W, F == D.
- *     The causal scan with fp32 IO needs D == 64 (D == 128: TTR_ERR_UNSUPPORTED).
+ *     The causal scan with fp32 IO and D == 128 takes chunk 64 only (others:
+ *     TTR_ERR_UNSUPPORTED); its default chunk is then 64.
  *     0 <= L <= N. Ragged N (not a multiple of any tile size) is supported.
  *   - The relu and softmax feature maps are those of the NNT linear attention,
  *     applied to already projected features: they need W == NULL and no
@@ -290,7 +291,7 @@ typedef struct {
  * feature_map, eps, causal, batch_first) and "How it works" (project Q/K/V,
  * feature map, K'^T V first, normalise, project back out).
  * Shape rules: B, N, H >= 1; E % 128 == 0; E % H == 0; D = E / H in {64, 128}
- * (64 for the causal layer with fp32 IO); B*N*E < 2^31; B*H <= 65535.
+ * B*N*E < 2^31; B*H <= 65535.
  * ws: at least ttr_nnt_layer_workspace_bytes(d, causal) bytes (transposed
  * weights, Q/K/V and the attention output in [B,H,N,D], and the attention's
  * own workspace); its contents on entry do not matter. */

@@ -44,9 +44,12 @@ struct CausalShape {
   using TR = LdsRow<T, C>;  // phi(K)^T and V^T [D][C], tokens in kperm order
   using PR = LdsRow<T, D>;  // P^T [D][D]
   static constexpr int NTPW = (D / 32) * (D / 32) / 4;  // state tiles per wave
-  static constexpr int phik_bytes = C * KR::bytes_per_row;
   static constexpr int t_bytes = D * TR::bytes_per_row;
   static constexpr int p_bytes = D * PR::bytes_per_row;
+  // phi(K) also as rows (the score product's operand) when it fits; else
+  // (fp32 with D = 128) the score operand is gathered from phi(K)^T
+  static constexpr bool ROWS = C * KR::bytes_per_row + 2 * t_bytes + p_bytes + D * 4 <= 160 * 1024;
+  static constexpr int phik_bytes = ROWS ? C * KR::bytes_per_row : 0;
   static constexpr int off_phikt = phik_bytes;
   static constexpr int off_vt = off_phikt + t_bytes;
   static constexpr int off_pt = off_vt + t_bytes;
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void causal_scan_kernel(CausalArgs a) {
   for (int ch = cbeg; ch < cend; ++ch) {
     const int c0 = ch * C;
     __syncthreads();  // state written; previous chunk fully consumed
-    stage_chunk<T, D, C, true, MAP>(K, V, bias, c0, N, phiK, phiKt, Vt, tid);
+    stage_chunk<T, D, C, S::ROWS, MAP>(K, V, bias, c0, N, phiK, phiKt, Vt, tid);
     __syncthreads();
 
     for (int i = 0; i < (NB + 3) / 4; ++i) {
@@ -269,8 +272,17 @@ __global__ __launch_bounds__(256, 1) void causal_scan_kernel(CausalArgs a) {
       for (int kb2 = 0; kb2 <= qb; ++kb2) {
         f32x16 sc = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb)
-          mma(sc, ld_frag<T>(phiK + (kb2 * 32 + c) * KR::stride + kb * 16 + 8 * g), qf[kb]);
+        for (int kb = 0; kb < D / 16; ++kb) {
+          if constexpr (S::ROWS) {
+            mma(sc, ld_frag<T>(phiK + (kb2 * 32 + c) * KR::stride + kb * 16 + 8 * g), qf[kb]);
+          } else {  // key kb2 * 32 + c, features kb * 16 + 8 g + j: column kperm(key) of phi(K)^T
+            Frag<T> kf;
+            const T* col = phiKt + kperm(kb2 * 32 + c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kf[j] = col[(kb * 16 + 8 * g + j) * TR::stride];
+            mma(sc, kf, qf[kb]);
+          }
+        }
         float sv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -347,7 +359,7 @@ static hipError_t launch_causal_t(const CausalArgs& a, int B, hipStream_t s, Sta
 }
 
 // bf16 with D = 64 runs the streamed kernels of k_causal2.hip; these cover
-// fp32 (D = 64) and bf16 with D = 128.
+// fp32 (D = 64, and D = 128 at chunk 64) and bf16 with D = 128.
 template <int MAP>
 static hipError_t launch_causal_m(const Problem& p, const CausalArgs& a, int chunk, hipStream_t s, StageTimer* t) {
   if (p.dtype == 1 && p.D == 128) {
@@ -356,6 +368,8 @@ static hipError_t launch_causal_m(const Problem& p, const CausalArgs& a, int chu
   } else if (p.dtype == 0 && p.D == 64) {
     if (chunk == 64) return launch_causal_t<float, 64, 64, MAP>(a, p.B, s, t);
     if (chunk == 128) return launch_causal_t<float, 64, 128, MAP>(a, p.B, s, t);
+  } else if (p.dtype == 0 && p.D == 128) {
+    if (chunk == 64) return launch_causal_t<float, 128, 64, MAP>(a, p.B, s, t);
   }
   return hipErrorInvalidValue;
 }

@@ -81,6 +81,7 @@ bool causal_chunk_ok(int32_t dtype, int32_t D, int32_t chunk) {
   if (dtype == TTR_BF16 && D == 64) return true;
   if (dtype == TTR_BF16 && D == 128) return chunk <= 128;
   if (dtype == TTR_FP32 && D == 64) return chunk <= 128;
+  if (dtype == TTR_FP32 && D == 128) return chunk == 64;
   return false;
 }
 

@@ -69,7 +69,8 @@ def test_hybrid_forward_validation(lib):
     assert hyb(lib, D(Dm=128, F=256, dt=0), wsb=16, **kw) == WS  # fp32 IO with D = 128: valid
     kw2 = dict(kw)
     kw2["W"] = None
-    assert hyb(lib, D(Dm=128, F=128, dt=0), causal=1, L=0, **kw2) == UNSUP  # (the fp32 causal scan needs D == 64)
+    assert hyb(lib, D(Dm=128, F=128, dt=0), causal=128, L=0, **kw2) == UNSUP  # fp32, D = 128: chunk 64 only
+    assert hyb(lib, D(Dm=128, F=128, dt=0), causal=64, L=0, wsb=16, **kw2) == WS
     assert hyb(lib, D(), L=257, **kw) == SHAPE
     assert hyb(lib, D(), L=-1, **kw) == SHAPE
     kw2 = dict(kw)
@@ -141,7 +142,7 @@ def test_nnt_layer_validation(lib):
     assert layer(LD(E=192, H=3)) == UNSUP          # E not a multiple of 128
     assert layer(LD(E=512, H=16)) == UNSUP         # D = 32
     assert layer(LD(E=512, H=4, dt=0), wsb=16) == WS  # fp32 with D = 128: valid, reaches the workspace check
-    assert layer(LD(E=512, H=4, dt=0), causal=1) == UNSUP  # the fp32 causal scan needs D = 64
+    assert layer(LD(E=512, H=4, dt=0), causal=1, wsb=16) == WS  # fp32 causal with D = 128: chunk 64
     assert layer(LD(), x=None) == NULL
     assert layer(LD(), Wo=None) == NULL
     assert layer(LD(), Wq=big + 8) == ALIGN

@@ -57,6 +57,7 @@ CASES = [
     ("fp32", 2, 64, 256, 4, False, "relu"),
     ("fp32", 1, 129, 256, 4, True, "softmax"),
     ("fp32", 2, 100, 256, 2, False, "elu1"),      # D = 128
+    ("fp32", 1, 150, 256, 2, True, "elu1"),       # D = 128, causal (chunk 64)
 ]
 
 

@@ -103,7 +103,7 @@ def test_causal_full_size_whole_output():
 
 @pytest.mark.parametrize("dtype,D,chunk", [("bf16", 64, 256), ("bf16", 64, 128), ("bf16", 64, 64),
                                            ("bf16", 128, 128), ("bf16", 128, 64), ("fp32", 64, 128),
-                                           ("fp32", 64, 64)])
+                                           ("fp32", 64, 64), ("fp32", 128, 64)])
 def test_causal_small_full(dtype, D, chunk):
     w = small("causal", B=2, H=3, N=1000, D=D, F=D, dtype=dtype, seed=11)
     x = workloads.make_inputs(w)
