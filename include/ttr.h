@@ -57,8 +57,8 @@
  *     graph can be replayed. Concurrent calls must not share a workspace.
  *   - Shape rules: B, H, N >= 1; D in {64, 128}; with W, F a multiple of 256
  *     (else TTR_ERR_SHAPE), of which F == 256 is implemented by every entry
- *     point and F == 512 by the bf16 ttr_hybrid_forward (and its _noalloc
- *     form); other multiples return TTR_ERR_UNSUPPORTED. Without W, F == D.
+ *     point and F == 512, 768 and 1024 by the bf16 ttr_hybrid_forward (and its
+ *     _noalloc form); other multiples return TTR_ERR_UNSUPPORTED. Without W, F == D.
  *     The causal scan with fp32 IO and D == 128 takes chunk 64 only (others:
  *     TTR_ERR_UNSUPPORTED); its default chunk is then 64.
  *     0 <= L <= N. Ragged N (not a multiple of any tile size) is supported.

@@ -116,7 +116,11 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
   if constexpr (LIN) {  // (landmarks alone: step lc starts chunk lc + 2)
     issue(2);
     const __amdgpu_buffer_rsrc_t rvec = buffer_rsrc(pbh, 2 * F * 4);
-    if (tid < 2 * F * 4 / 16) copy16_async(rvec, (uint32_t)tid * 16, 0, smem + w * 64 * 16);
+    constexpr int NVP = 2 * F * 4 / 16;  // 16-byte pieces of the two vectors (a multiple of 64)
+#pragma unroll
+    for (int r = 0; r < (NVP + 255) / 256; ++r)
+      if (tid + 256 * r < NVP)  // wave-uniform
+        copy16_async(rvec, (uint32_t)(tid + 256 * r) * 16, 0, smem + (256 * r + w * 64) * 16);
   }
   Frag<uint16_t> qf[D / 16];
   const uint16_t* Qp = a.Q + ((size_t)bh * N + (tok_ok ? tok : 0)) * D + 8 * g;
@@ -536,15 +540,23 @@ hipError_t launch_fused_query(const Problem& p, const void* Q, const FusedPack& 
   a.nwg = a.ntiles * p.B * p.H;
   a.out = static_cast<uint16_t*>(out);
   if (p.dtype != 1) return hipErrorInvalidValue;
-  if (p.proj && p.F != 256 && p.F != 512) return hipErrorInvalidValue;
+  if (p.proj && p.F != 256 && p.F != 512 && p.F != 768 && p.F != 1024) return hipErrorInvalidValue;
   if (p.D == 128) {
-    if (p.proj) return p.F == 512 ? launch_fused_t<128, 512, kElu1>(a, s) : launch_fused_t<128, 256, kElu1>(a, s);
+    if (p.proj) {
+      if (p.F == 1024) return launch_fused_t<128, 1024, kElu1>(a, s);
+      if (p.F == 768) return launch_fused_t<128, 768, kElu1>(a, s);
+      return p.F == 512 ? launch_fused_t<128, 512, kElu1>(a, s) : launch_fused_t<128, 256, kElu1>(a, s);
+    }
     if (p.fmap == kRelu) return launch_fused_t<128, 128, kRelu>(a, s);
     if (p.fmap == kSoftmax) return launch_fused_t<128, 128, kSoftmax>(a, s);
     return launch_fused_t<128, 128, kElu1>(a, s);
   }
   if (p.D == 64) {
-    if (p.proj) return p.F == 512 ? launch_fused_t<64, 512, kElu1>(a, s) : launch_fused_t<64, 256, kElu1>(a, s);
+    if (p.proj) {
+      if (p.F == 1024) return launch_fused_t<64, 1024, kElu1>(a, s);
+      if (p.F == 768) return launch_fused_t<64, 768, kElu1>(a, s);
+      return p.F == 512 ? launch_fused_t<64, 512, kElu1>(a, s) : launch_fused_t<64, 256, kElu1>(a, s);
+    }
     if (p.fmap == kRelu) return launch_fused_t<64, 64, kRelu>(a, s);
     if (p.fmap == kSoftmax) return launch_fused_t<64, 64, kSoftmax>(a, s);
     return launch_fused_t<64, 64, kElu1>(a, s);

@@ -979,6 +979,8 @@ static hipError_t launch_kvs(const Problem& p, const KvsArgs& a, int groups, hip
     if (p.proj) {
       if (p.F == 256) return launch_kvs_t<128, 256, true, kElu1, PACK>(a, groups, s, t);
       if (p.F == 512) return launch_kvs_t<128, 512, true, kElu1, PACK>(a, groups, s, t);
+      if (p.F == 768) return launch_kvs_t<128, 768, true, kElu1, PACK>(a, groups, s, t);
+      if (p.F == 1024) return launch_kvs_t<128, 1024, true, kElu1, PACK>(a, groups, s, t);
       return hipErrorInvalidValue;
     }
     if (p.fmap == kRelu) return launch_kvs_t<128, 128, false, kRelu, PACK>(a, groups, s, t);
@@ -988,6 +990,8 @@ static hipError_t launch_kvs(const Problem& p, const KvsArgs& a, int groups, hip
   if (p.proj) {
     if (p.F == 256) return launch_kvs_t<64, 256, true, kElu1, PACK>(a, groups, s, t);
     if (p.F == 512) return launch_kvs_t<64, 512, true, kElu1, PACK>(a, groups, s, t);
+    if (p.F == 768) return launch_kvs_t<64, 768, true, kElu1, PACK>(a, groups, s, t);
+    if (p.F == 1024) return launch_kvs_t<64, 1024, true, kElu1, PACK>(a, groups, s, t);
     return hipErrorInvalidValue;
   }
   if (p.fmap == kRelu) return launch_kvs_t<64, 64, false, kRelu, PACK>(a, groups, s, t);

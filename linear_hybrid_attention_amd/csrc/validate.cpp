@@ -1,7 +1,7 @@
 // Host-only argument validation for the C ABI. Shape rules follow the
 // method's pages: "Flux2TTRTrainer", section "Inputs worth setting"
-// (feature_dim is a multiple of 256; this library implements 256, and 512 on
-// the bf16 hybrid forward), and
+// (feature_dim is a multiple of 256; this library implements 256, and 512,
+// 768 and 1024 on the bf16 hybrid forward), and
 // "NNT Define Linear Attention", section "The inputs" (causal flag, eps).
 #include "validate.hpp"
 

@@ -27,8 +27,8 @@ bool env_flag(const char* name);
 // implements (a multiple of 256 above it is TTR_ERR_UNSUPPORTED).
 ttr_status check_dims(const ttr_dims& d, bool has_w, int32_t max_f = 256);
 
-// Projected feature dimensions of the bf16 hybrid forward: 256 and 512.
-constexpr int32_t kMaxFeatureDimBf16Forward = 512;
+// Projected feature dimensions of the bf16 hybrid forward: 256, 512, 768 and 1024.
+constexpr int32_t kMaxFeatureDimBf16Forward = 1024;
 inline int32_t forward_max_f(const ttr_dims& d) { return d.dtype == TTR_BF16 ? kMaxFeatureDimBf16Forward : 256; }
 
 // NULL and 16-byte alignment of a required pointer (NULL -> TTR_ERR_NULL).

@@ -63,9 +63,10 @@ def test_hybrid_forward_validation(lib):
     assert hyb(lib, D(F=200), **kw) == SHAPE          # feature_dim must be a multiple of 256
     assert hyb(lib, D(F=384), **kw) == SHAPE          # not a multiple of 256
     assert hyb(lib, D(F=512), **kw) == UNSUP          # fp32 IO: F == 256 only
-    assert hyb(lib, D(F=768, dt=1), **kw) == UNSUP    # bf16: 256 and 512 are implemented
+    assert hyb(lib, D(F=768, dt=1), wsb=16, **kw) == WS  # bf16: 256, 512, 768 and 1024 are implemented
     assert hyb(lib, D(F=512, dt=1), wsb=16, **kw) == WS  # bf16 F = 512: valid, reaches the workspace check
-    assert hyb(lib, D(F=1024, dt=1), **kw) == UNSUP
+    assert hyb(lib, D(F=1024, dt=1), wsb=16, **kw) == WS
+    assert hyb(lib, D(F=1280, dt=1), **kw) == UNSUP
     assert hyb(lib, D(Dm=128, F=256, dt=0), wsb=16, **kw) == WS  # fp32 IO with D = 128: valid
     kw2 = dict(kw)
     kw2["W"] = None
@@ -219,11 +220,14 @@ def test_workspace_bytes(lib):
     # at least KV and ksum in fp32
     assert c2 >= 24 * (256 * 128 + 256) * 4
     assert lib.ttr_workspace_bytes(ttr.Dims(8, 8, 32768, 64, 64, 1), 0, 1, 256) > 0
-    # feature dimension: bf16 F = 512 has a workspace (larger than F = 256), F = 384 / 768 none
+    # feature dimension: bf16 F = 512, 768, 1024 have growing workspaces, F = 384 (not a multiple
+    # of 256) and 1280 (beyond the implemented) none
     c4 = lib.ttr_workspace_bytes(ttr.Dims(1, 24, 4608, 128, 512, 1), 128, 0, 0)
-    assert c4 > c2
+    c6 = lib.ttr_workspace_bytes(ttr.Dims(1, 24, 4608, 128, 768, 1), 128, 0, 0)
+    c8 = lib.ttr_workspace_bytes(ttr.Dims(1, 24, 4608, 128, 1024, 1), 128, 0, 0)
+    assert c8 > c6 > c4 > c2
     assert lib.ttr_workspace_bytes(ttr.Dims(1, 24, 4608, 128, 384, 1), 128, 0, 0) == 0
-    assert lib.ttr_workspace_bytes(ttr.Dims(1, 24, 4608, 128, 768, 1), 128, 0, 0) == 0
+    assert lib.ttr_workspace_bytes(ttr.Dims(1, 24, 4608, 128, 1280, 1), 128, 0, 0) == 0
     assert lib.ttr_workspace_bytes(ttr.Dims(1, 2, 256, 64, 512, 0), 16, 0, 0) == 0  # fp32: 256 only
 
 

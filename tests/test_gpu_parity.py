@@ -57,6 +57,22 @@ def test_hybrid_forward_feature_dim_512(shape):
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("F,shape", [(768, dict()), (1024, dict()), (768, dict(B=2, H=2, N=777, L=33)),
+                                     (1024, dict(H=2, N=1500, D=64, L=48)), (1024, dict(H=2, N=300, L=0))])
+def test_hybrid_forward_feature_dim_768_1024(F, shape):
+    # feature_dim 768 and 1024 (a multiple of 256, "Flux2TTRTrainer", "Inputs
+    # worth setting"): the flux_1024 shape, every element, and ragged shapes
+    w = small("flux_1024", F=F, seed=70 + F // 256 + len(shape), **shape)
+    x = workloads.make_inputs(w)
+    print(f"[hybrid-f{F}] B={w.B} H={w.H} N={w.N} D={w.D} F={w.F} L={w.L}", flush=True)
+    out = run_hybrid(w, to_device(w, x))
+    torch.cuda.synchronize()
+    err = normwise(host(out), oracle_hybrid(w, x))
+    print(f"[hybrid-f{F}] normwise err {err:.3e}", flush=True)
+    assert np.isfinite(host(out)).all()
+    assert err <= TOL[w.dtype], err
+
+
 @pytest.mark.parametrize("shape", [dict(N=256, D=128, L=16), dict(B=2, H=3, N=333, D=128, L=7),
                                    dict(N=200, D=128, L=0), dict(N=100, D=128, F=128, proj=False, L=5)])
 def test_hybrid_forward_fp32_d128(shape):
