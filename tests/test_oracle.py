@@ -638,6 +638,31 @@ def test_distill_step_self_teacher_moves_only_log_variances():
     assert np.all(s2 < 0)  # d loss / d s = 1 - exp(-s) * 0 = 1 > 0 pushes s down
 
 
+def test_distill_step_matches_torch_autograd_and_adam():
+    # three whole steps against an independent composition: the forward restated
+    # in torch, the teacher from SDPA, huber and cosine from torch, gradients by
+    # autograd and the update by torch.optim.Adam (one optimiser over W, b, g, s)
+    Q, K, V, W, b, g, L, _ = _bw_small(88, B=1, H=2, N=24, D=6, F=8, L=6)
+    s = np.array([0.1, -0.2])
+    lr = 5e-3
+    Wt, bt, gt, stt = (torch.tensor(a.copy(), requires_grad=True) for a in (W, b, g, s))
+    opt = torch.optim.Adam([Wt, bt, gt, stt], lr=lr, betas=(0.9, 0.999), eps=1e-8)
+    T = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(a) for a in (Q, K, V)))
+    st = _adam_state(W, b, g, s)
+    for k in range(1, 4):
+        W, b, g, s, st, loss = O.distill_step(Q, K, V, W, b, g, s, st, k, lr, EPS, L)
+        opt.zero_grad()
+        out = _torch_hybrid(Q, K, V, Wt, bt, gt, EPS, L)
+        Ht = torch.nn.functional.huber_loss(out, T, delta=1.0)
+        Ct = (1 - torch.nn.functional.cosine_similarity(out, T, dim=-1, eps=1e-8)).mean()
+        Lt = torch.exp(-stt[0]) * Ht + stt[0] + torch.exp(-stt[1]) * Ct + stt[1]
+        Lt.backward()
+        opt.step()
+        assert abs(loss - Lt.item()) < 1e-10 * max(1.0, abs(Lt.item()))
+        for mine, ref in ((W, Wt), (b, bt), (g, gt), (s, stt)):
+            assert np.abs(mine - ref.detach().numpy()).max() < 1e-10
+
+
 def test_distill_steps_reduce_the_loss():
     Q, K, V, W, b, g, L, _ = _bw_small(87, B=1, H=2, N=32, D=8, F=16, L=8)
     s = np.zeros(2)
