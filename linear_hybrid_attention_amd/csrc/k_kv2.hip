@@ -912,7 +912,11 @@ static KvsPlan kvs_plan(const Problem& p, int cus) {
   int ns = (cus / 8) / gx;
   const int maxs = (p.N + 2 * step - 1) / (2 * step);  // at least two steps per split
   if (ns > maxs) ns = maxs;
-  if (ns > 255) ns = 255;  // the count of a meeting word is a byte
+  // At most 16 splits: with fewer groups than XCDs (the 3-head share shape)
+  // more splits only add meeting and reduction work (16: 27.7 against 28.7 us
+  // with 24 at [1,3,4608,128]; 8 and 12 gave no gain). (The count of a
+  // meeting word is a byte: at most 255 splits in any case.)
+  if (ns > 16) ns = 16;
   if (ns < 1) ns = 1;
   const int per = (p.N + ns - 1) / ns;
   k.chunk = (per + step - 1) / step * step;
