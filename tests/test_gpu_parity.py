@@ -58,10 +58,12 @@ def test_hybrid_forward_feature_dim_512(shape):
 
 
 @pytest.mark.parametrize("F,shape", [(768, dict()), (1024, dict()), (768, dict(B=2, H=2, N=777, L=33)),
-                                     (1024, dict(H=2, N=1500, D=64, L=48)), (1024, dict(H=2, N=300, L=0))])
+                                     (1024, dict(H=2, N=1500, D=64, L=48)), (1024, dict(H=2, N=300, L=0)),
+                                     (768, dict(H=3, N=999, D=64, L=20)), (256, dict(B=2))])
 def test_hybrid_forward_feature_dim_768_1024(F, shape):
     # feature_dim 768 and 1024 (a multiple of 256, "Flux2TTRTrainer", "Inputs
-    # worth setting"): the flux_1024 shape, every element, and ragged shapes
+    # worth setting"): the flux_1024 shape, every element, and ragged shapes;
+    # last, the flux_1024 shape with two batches (F = 256)
     w = small("flux_1024", F=F, seed=70 + F // 256 + len(shape), **shape)
     x = workloads.make_inputs(w)
     print(f"[hybrid-f{F}] B={w.B} H={w.H} N={w.N} D={w.D} F={w.F} L={w.L}", flush=True)
