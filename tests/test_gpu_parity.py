@@ -26,7 +26,7 @@ def run_hybrid(w, d):
 
 # ------------------------------------------------------------------ whole forward, all workloads
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "flux_512", "flux_1024", "flux_2048"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "flux_512", "flux_1024", "flux_2048", "flux_1024_h3"])
 def test_hybrid_forward_full_workloads(name):
     w = workloads.WORKLOADS[name]
     x = workloads.make_inputs(w)
