@@ -192,7 +192,8 @@ def test_hybrid_causal_route():
 STAGED = [("tiny_fp32", {}), ("flux_512", dict(H=3, N=1000, L=7, seed=21)),
           ("flux_512", dict(H=2, N=333, D=64, L=33, seed=22)),
           ("tiny_fp32", dict(N=257, L=5, seed=23)),
-          ("tiny_fp32", dict(H=3, N=300, D=128, L=9, seed=26))]  # fp32 with D = 128
+          ("tiny_fp32", dict(H=3, N=300, D=128, L=9, seed=26)),  # fp32 with D = 128
+          ("flux_1024", {})]  # the staged calls at the size their bench line times
 
 
 @pytest.mark.parametrize("name,kw", STAGED)
