@@ -244,12 +244,16 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       const int fb = t >> 3, q = t & 7;
       return *reinterpret_cast<const u32x4*>(kbase + fb * 32 + (q < 4 ? 2 * q : 16 + 2 * (q - 4)));
     };
+    // (The slots run at raised wave priority: of the SIMD's two waves, the
+    // one in its slots issues first, the other fills in with its map,
+    // softmax or step end.)
     f32x16 acc[2] = {accb[0], accb[1]};
     Frag<uint16_t> fa[NJ];
     u32x4 kq[8];
     u32x4 pw[4];
 #pragma unroll
     for (int j = 0; j < LEAD; ++j) fa[j] = ld_frag<uint16_t>(a_ptr(j));
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (j + LEAD < NJ) fa[j + LEAD] = ld_frag<uint16_t>(a_ptr(j + LEAD));
@@ -274,6 +278,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(bf16x8, pw[i]);
     load_bias(min(k + 1, NFC - 1), accb);  // unconditional: a branch here would let the map sink past the slots
@@ -393,6 +398,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
 #pragma unroll
     for (int j = 0; j < LEAD; ++j) fa[j] = ld_frag<uint16_t>(a_ptr(j));
     s = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       if (j + LEAD < NL) fa[j + LEAD] = ld_frag<uint16_t>(a_ptr(j + LEAD));
@@ -401,6 +407,7 @@ __global__ __launch_bounds__(256, 2) void fused_query_kernel(FusedArgs a) {
       else mma(o[i >> 1], fa[j], pf[i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 #pragma clang loop unroll(disable)
   for (int lc = 0; lc + 1 < nlc; ++lc) {
